@@ -1,0 +1,340 @@
+"""fp64 CPU oracle of the decoder attention block.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  The product path (the HIP library and its Python binding) never
+calls it, and it imports nothing from the product path.
+
+It is the plain definition of what one decoder attention block of a
+Qwen3-ASR-style text decoder computes, written out in fp64 NumPy with no
+blocking, fusion or reordering:
+
+* input RMSNorm, then one fused q/k/v projection, then per-head RMSNorm of q
+  and k, then rotary position embedding in full precision, then the KV-cache
+  update, then grouped-query attention over the cache with a full-precision
+  softmax, then the output projection.  The operation list is the one
+  "Qwen3-ASR -- Latency & Bottleneck Analysis" gives for decoder attention in
+  section 07 ("Why attention is 48.6% of decode": q/k/v projections, GQA
+  repeat_kv, QK^T, softmax in fp32, AV, o_proj), with the norms of "Norms are
+  real money at this size" (same section) and the rotary of section 03's
+  module table ("rotary (MRoPE, fp32)").
+* k-token verification scores k candidate positions in one causal pass over
+  the committed cache; position i sees the committed prefix and the
+  candidates up to and including i ("Can CTC make Qwen3-ASR faster?",
+  section 03, "Speculative decoding: what work actually disappears?").
+* cropping returns the cache to a committed prefix (same page, section 03
+  "Greedy exactness" and section 11 Phase D, transactional commit/crop).
+
+Readings taken where the pages are silent (each one is listed with its reason
+in the design notes): rotate-half rotary pairing (t, t + d/2); one scalar
+position per token, so the multi-section rotary reduces to the 1-D form; the
+new token sits at position ``lens`` and attends to itself; attention reads the
+appended K/V as stored (rounded once to the cache's 16-bit type); scale
+1/sqrt(d); q head i uses kv head i // (nq / nkv); RMSNorm is
+x * g / sqrt(mean(x^2) + eps) with the same eps for all norms; no biases.
+
+Inputs are 16-bit bit patterns (``uint16``) widened exactly to fp64; every
+intermediate stays in fp64, and the only rounding is the one into the cache.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+STATUS_CAPACITY = 1   # an append would pass the cache capacity: rows skipped, output NaN
+STATUS_CROP_GROW = 2  # a crop asked for a length above the current one: ignored
+
+
+# ----------------------------------------------------------------------------
+# 16-bit formats, from their bit patterns
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of 16-bit bit patterns."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == F16:
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == BF16:
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+_TABLES: dict = {}
+
+
+def _magnitude_table(dtype: str):
+    """Non-negative finite patterns in ascending order, then the infinity pattern.
+
+    For IEEE-style formats the non-negative patterns 0 .. max-finite are
+    ordered by value.  Infinity is placed where the next pattern would be,
+    with the value max + ulp(max), so that round-to-nearest-even overflows to
+    infinity exactly when IEEE 754 says it does.
+    """
+    if dtype not in _TABLES:
+        if dtype == F16:
+            max_pat, inf_pat, inf_val = 0x7BFF, 0x7C00, 65536.0
+        elif dtype == BF16:
+            max_pat, inf_pat, inf_val = 0x7F7F, 0x7F80, 2.0 ** 128
+        else:
+            raise ValueError(dtype)
+        pats = np.arange(0, max_pat + 1, dtype=np.uint32).astype(np.uint16)
+        vals = np.append(widen(pats, dtype), inf_val)
+        pats = np.append(pats, np.uint16(inf_pat))
+        _TABLES[dtype] = (vals, pats)
+    return _TABLES[dtype]
+
+
+def rne16(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values to the nearest 16-bit value, ties to the even pattern.
+
+    Works from the table of representable magnitudes: find the two
+    neighbours, keep the nearer, and on an exact tie keep the one whose
+    pattern is even.  The sign bit is copied (so -0.0 stays -0.0).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    vals, pats = _magnitude_table(dtype)
+    mag = np.abs(a)
+    hi = np.clip(np.searchsorted(vals, mag, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_lo = mag - vals[lo]
+    d_hi = vals[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (pats[hi] % 2 == 0))
+    out = np.where(pick_hi, pats[hi], pats[lo]).astype(np.uint16)
+    out = np.where(mag >= vals[-1], pats[-1], out)          # at or past infinity
+    out = np.where(np.signbit(a), out | np.uint16(0x8000), out).astype(np.uint16)
+    nan_pat = np.uint16(0x7E00 if dtype == F16 else 0x7FC0)
+    return np.where(np.isnan(a), nan_pat, out).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# configuration, weights, cache
+
+@dataclass(frozen=True)
+class BlockConfig:
+    hidden: int = 1024
+    n_q_heads: int = 16
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    rms_eps: float = 1e-6
+    rope_theta: float = 1e6
+    dtype: str = F16
+
+
+@dataclass
+class LayerWeights:
+    """One layer's weights widened to fp64 (inputs are 16-bit patterns)."""
+    input_norm_w: np.ndarray   # [H]
+    w_qkv: np.ndarray          # [(nq + 2 nkv) d][H], rows q | k | v, head-major
+    q_norm_w: np.ndarray       # [d]
+    k_norm_w: np.ndarray       # [d]
+    w_o: np.ndarray            # [H][nq d]
+
+    @classmethod
+    def from_bits(cls, bits: dict, dtype: str) -> "LayerWeights":
+        return cls(**{name: widen(bits[name], dtype) for name in
+                      ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o")})
+
+
+@dataclass
+class KVCache:
+    """One layer's cache: K and V as 16-bit patterns [batch_cap][nkv][capacity][d]."""
+    k: np.ndarray
+    v: np.ndarray
+    lens: np.ndarray           # [batch_cap] committed lengths
+    dtype: str
+    status: int = 0
+
+    @classmethod
+    def empty(cls, batch_cap, n_kv_heads, capacity, head_dim, dtype):
+        shape = (batch_cap, n_kv_heads, capacity, head_dim)
+        return cls(np.zeros(shape, np.uint16), np.zeros(shape, np.uint16),
+                   np.zeros(batch_cap, np.int64), dtype)
+
+    @property
+    def capacity(self) -> int:
+        return self.k.shape[2]
+
+    def copy(self) -> "KVCache":
+        return KVCache(self.k.copy(), self.v.copy(), self.lens.copy(), self.dtype, self.status)
+
+
+# ----------------------------------------------------------------------------
+# the steps of the block
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """x * gain / sqrt(mean(x^2) + eps), over the last axis."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x * gain / np.sqrt(ms + eps)
+
+
+def rope_frequencies(head_dim: int, theta: float) -> np.ndarray:
+    """omega_t = theta^(-2t/d), t = 0 .. d/2 - 1 (a geometric ladder from 1)."""
+    t = np.arange(head_dim // 2, dtype=np.float64)
+    return theta ** (-2.0 * t / head_dim)
+
+
+def rope(u: np.ndarray, pos, theta: float) -> np.ndarray:
+    """Rotate pairs (t, t + d/2) of the last axis by the angle pos * omega_t.
+
+    ``pos`` broadcasts against ``u.shape[:-1]``.
+    """
+    d = u.shape[-1]
+    half = d // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_frequencies(d, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = u[..., :half], u[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def _split_qkv(qkv: np.ndarray, cfg: BlockConfig):
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    q = qkv[..., : nq * d].reshape(qkv.shape[:-1] + (nq, d))
+    k = qkv[..., nq * d: (nq + nkv) * d].reshape(qkv.shape[:-1] + (nkv, d))
+    v = qkv[..., (nq + nkv) * d:].reshape(qkv.shape[:-1] + (nkv, d))
+    return q, k, v
+
+
+def _softmax(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def decode(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray,
+           slots=None, positions=None, residual_bits=None) -> np.ndarray:
+    """One-token decode for B rows (each row a distinct sequence slot).
+
+    Row i works on slot ``slots[i]`` (default i) at position
+    ``positions[i]`` (default the slot's length): it computes q, k, v, appends
+    k and v at index lens[slot], attends over lens[slot] + 1 positions and
+    returns out[i] = W_o a (+ residual).  lens[slot] grows by one.  A row whose
+    append would pass the capacity is skipped: NaN output, the capacity status
+    bit set, its length unchanged.  Rows are handled one at a time here, as a
+    sequence of single-row computations.
+    """
+    x = widen(x_bits, cfg.dtype)
+    B = x.shape[0]
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    group = nq // nkv
+    res = widen(residual_bits, cfg.dtype) if residual_bits is not None else None
+    out = np.empty((B, cfg.hidden), np.float64)
+    for i in range(B):
+        s = int(slots[i]) if slots is not None else i
+        L = int(cache.lens[s])
+        h = rms_norm(x[i], w.input_norm_w, cfg.rms_eps)
+        q, k, v = _split_qkv(w.w_qkv @ h, cfg)
+        q = rms_norm(q, w.q_norm_w, cfg.rms_eps)
+        k = rms_norm(k, w.k_norm_w, cfg.rms_eps)
+        p = int(positions[i]) if positions is not None else L
+        q = rope(q, p, cfg.rope_theta)
+        k = rope(k, p, cfg.rope_theta)
+        if L + 1 > cache.capacity:
+            cache.status |= STATUS_CAPACITY
+            out[i] = np.nan
+            continue
+        cache.k[s, :, L, :] = rne16(k, cache.dtype)
+        cache.v[s, :, L, :] = rne16(v, cache.dtype)
+        n_vis = L + 1
+        a = np.empty((nq, d))
+        for head in range(nq):
+            g = head // group
+            K = widen(cache.k[s, g, :n_vis, :], cache.dtype)
+            V = widen(cache.v[s, g, :n_vis, :], cache.dtype)
+            wts = _softmax(K @ q[head] / math.sqrt(d))
+            a[head] = wts @ V
+        out[i] = w.w_o @ a.reshape(nq * d)
+        if res is not None:
+            out[i] += res[i]
+        cache.lens[s] = n_vis
+    return out
+
+
+def verify(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray,
+           slots=None, positions=None, residual_bits=None) -> np.ndarray:
+    """k-token causal verification block for B sequences: x is [B][k][H].
+
+    For each sequence the k rows are processed as one block: one [k x H]
+    projection, k appends at lens .. lens + k - 1, and a causally masked
+    [k x (lens + k)] score matrix per query head, where row r sees positions
+    0 .. lens + r.  Rotary positions are ``positions[b] + r`` (default
+    lens + r).  lens grows by k.
+    """
+    x = widen(x_bits, cfg.dtype)
+    B, kk, _ = x.shape
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    group = nq // nkv
+    res = widen(residual_bits, cfg.dtype) if residual_bits is not None else None
+    out = np.empty((B, kk, cfg.hidden), np.float64)
+    for b in range(B):
+        s = int(slots[b]) if slots is not None else b
+        L = int(cache.lens[s])
+        Hn = rms_norm(x[b], w.input_norm_w, cfg.rms_eps)                # [k][H]
+        Q, K_new, V_new = _split_qkv(Hn @ w.w_qkv.T, cfg)               # [k][heads][d]
+        Q = rms_norm(Q, w.q_norm_w, cfg.rms_eps)
+        K_new = rms_norm(K_new, w.k_norm_w, cfg.rms_eps)
+        p0 = int(positions[b]) if positions is not None else L
+        pos = p0 + np.arange(kk)
+        Q = rope(Q, pos[:, None], cfg.rope_theta)
+        K_new = rope(K_new, pos[:, None], cfg.rope_theta)
+        if L + kk > cache.capacity:
+            cache.status |= STATUS_CAPACITY
+            out[b] = np.nan
+            continue
+        cache.k[s, :, L:L + kk, :] = rne16(K_new.transpose(1, 0, 2), cache.dtype)
+        cache.v[s, :, L:L + kk, :] = rne16(V_new.transpose(1, 0, 2), cache.dtype)
+        n_all = L + kk
+        visible = np.arange(n_all)[None, :] <= (L + np.arange(kk))[:, None]   # [k][L + k]
+        A = np.empty((kk, nq, d))
+        for head in range(nq):
+            g = head // group
+            K = widen(cache.k[s, g, :n_all, :], cache.dtype)
+            V = widen(cache.v[s, g, :n_all, :], cache.dtype)
+            S = (Q[:, head, :] @ K.T) / math.sqrt(d)
+            S = np.where(visible, S, -np.inf)
+            A[:, head, :] = _softmax(S) @ V
+        out[b] = A.reshape(kk, nq * d) @ w.w_o.T
+        if res is not None:
+            out[b] += res[b]
+        cache.lens[s] = n_all
+    return out
+
+
+def kv_append(cache: KVCache, k_bits: np.ndarray, v_bits: np.ndarray, slots=None) -> None:
+    """Copy given 16-bit rows into the cache: k_bits, v_bits are [B][n][nkv][d].
+
+    Rows of sequence b go to positions lens .. lens + n - 1 of slot
+    ``slots[b]``; lens grows by n.  A sequence whose rows would pass the
+    capacity is skipped and the capacity status bit set.
+    """
+    k_bits = np.asarray(k_bits, np.uint16)
+    v_bits = np.asarray(v_bits, np.uint16)
+    B, n = k_bits.shape[:2]
+    for b in range(B):
+        s = int(slots[b]) if slots is not None else b
+        L = int(cache.lens[s])
+        if L + n > cache.capacity:
+            cache.status |= STATUS_CAPACITY
+            continue
+        cache.k[s, :, L:L + n, :] = k_bits[b].transpose(1, 0, 2)
+        cache.v[s, :, L:L + n, :] = v_bits[b].transpose(1, 0, 2)
+        cache.lens[s] = L + n
+
+
+def kv_crop(caches, new_lens) -> None:
+    """Set every layer's lens to new_lens; cached data is left as it is.
+
+    Only shrinking (or keeping) is allowed: a slot whose new length is
+    negative or above its current one keeps its length and the layer's
+    crop-grow status bit is set.
+    """
+    new_lens = np.asarray(new_lens)
+    for c in caches:
+        for b in range(len(c.lens)):
+            nl = int(new_lens[b])
+            if 0 <= nl <= c.lens[b]:
+                c.lens[b] = nl
+            else:
+                c.status |= STATUS_CROP_GROW

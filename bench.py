@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the decoder attention block on one MI355X.
+
+Headline workload: the 28-layer attention stack of Qwen3-ASR-0.6B decoding
+at batch 1 in fp16 (hidden 1024, 16 q / 8 kv heads, head_dim 128), with a
+795-token prefilled cache and 130 generated tokens (KV 795 -> 925), the clip
+of "Qwen3-ASR -- Latency & Bottleneck Analysis" section 01.  One step = one
+generated token = 28 layer calls; step s of a 130-step round uses cache
+length 795 + s, and a crop returns the cache to 795 after step 129.  Each
+step is one captured HIP graph (replayed), so host overhead is out of the
+timed region, as the pages' static one-token step suggests (section 08,
+step 2).
+
+Also timed (``--batched``, default on): ragged batched decode, 64 sequences,
+bf16, lengths U{200..1500} (one step = 28 layer calls + the crop back to
+the committed lengths), reported as tokens/s.
+
+Prints ONE JSON line.  `value` = microseconds per generated token for the
+28-layer block at batch 1 (lower is better).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+CAP_BS1 = 928                  # cache capacity of the bs1 workload (>= 925, multiple of 16)
+CAP_B64 = 1536                 # cache capacity of the batch-64 workload (>= 1501)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=130)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-batched", action="store_true", help="skip the batch-64 leg")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    p.add_argument("--dispatch", type=int, default=0, help="0 auto, 1 one kernel per phase, 2 fused")
+    p.add_argument("--profile-steps", type=int, default=0,
+                   help="run only this many bs1 steps eagerly (for profilers) and exit")
+    return p.parse_args()
+
+
+def layer_bytes(H, nq, nkv, d, committed, rows, e_in=2, e_out=4):
+    """Algorithmic HBM bytes of one layer call: weights once, committed K/V read once,
+    new K/V rows written, x read and out written.  Workspace traffic is not counted."""
+    w = ((nq + 2 * nkv) * d * H + H * nq * d + H + 2 * d) * 2
+    kv_read = sum(committed) * 2 * nkv * d * 2
+    kv_write = rows * 2 * nkv * d * 2
+    return w + kv_read + kv_write + rows * H * (e_in + e_out)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every sequence's work is independent: see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gqa_decode_attention_amd as ga
+    from synth import inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(torch.float16 if dtype == si.F16 else torch.bfloat16).to(dev)
+
+    # ------------------------------------------------------------ bs1 workload
+    c2 = si.CONFIGS[2]
+    H, NL, dtype = c2["hidden"], c2["layers"], c2["dtype"]
+    P0, NSTEP = 795, 130
+    cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch)
+    t0 = time.time()
+    weights, kvs = [], []
+    for l in range(NL):
+        wb = si.layer_weights(2, l, H, dtype)
+        weights.append(ga.Weights(*(to_dev(wb[n], dtype) for n in
+                                    ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o"))))
+        kb, vb = si.kv_rows(2, l, 0, P0, dtype)
+        kv = ga.KVLayer.empty(1, 8, CAP_BS1, dtype=torch.float16, device=dev)
+        ga.kv_append(kv, to_dev(kb.transpose(1, 0, 2)[None], dtype), to_dev(vb.transpose(1, 0, 2)[None], dtype))
+        kvs.append(kv)
+    xs = torch.stack([torch.stack([to_dev(si.activations(2, l, s, 1, H, dtype), dtype) for l in range(NL)])
+                      for s in range(NSTEP)])                      # [step][layer][1][H]
+    outs = torch.empty((NL, 1, H), dtype=torch.float32, device=dev)
+    ws = ga.alloc_workspace(cfg, 1, CAP_BS1, device=dev)
+    base_lens = torch.full((1,), P0, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] bs1 inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def step_calls(s):
+        for l in range(NL):
+            ga.layer_decode(cfg, weights[l], kvs[l], xs[s, l], outs[l], ws, host_lens=[P0 + s])
+
+    if args.profile_steps:
+        for s in range(args.profile_steps):
+            step_calls(s % NSTEP)
+            if s % NSTEP == NSTEP - 1:
+                ga.kv_crop(kvs, base_lens)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps}))
+        return
+
+    graphs = []
+    for s in range(NSTEP):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_calls(s)
+        graphs.append(g)
+    crop_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(crop_graph):
+        ga.kv_crop(kvs, base_lens)
+    # capture only records: reset the lengths that eager work may have touched
+    ga.kv_crop(kvs, base_lens)
+    torch.cuda.synchronize()
+
+    def run_steps(n, start=0):
+        for i in range(start, start + n):
+            s = i % NSTEP
+            graphs[s].replay()
+            if s == NSTEP - 1:
+                crop_graph.replay()
+
+    run_steps(args.warmup)
+    # restart the round at step 0 for the timed region
+    crop_graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    run_steps(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    us_token = ms_step * 1000.0
+    committed = [P0 + (i % NSTEP) for i in range(args.steps)]
+    bytes_per_call = float(np.mean([layer_bytes(H, 16, 8, 128, [L], 1) for L in committed]))
+    us_call = us_token / NL
+    achieved = bytes_per_call / (us_call * 1e-6) / 1e9
+    lens_ok = all(int(kv.lens.item()) == P0 + (args.steps % NSTEP) for kv in kvs)
+    status_ok = all(int(kv.status.item()) == 0 for kv in kvs)
+    print(f"[bench] bs1: {us_token:.1f} us/token, {us_call:.2f} us/layer-token, {achieved:.0f} GB/s "
+          f"(lens ok {lens_ok}, status ok {status_ok})", file=sys.stderr, flush=True)
+
+    result = {
+        "metric": "attn-block us/token (28 layers, bs1) + batched tok/s; % HBM roofline",
+        "value": round(us_token, 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (fp32 math)",
+        "data": "synthetic (seeded N(0,1) activations and cache, N(0,0.02) weights, gains 1+N(0,0.02))",
+        "config": {"workload": "28-layer decoder attention, bs1, fp16, hidden 1024, 16q/8kv, head_dim 128, "
+                               "KV 795->925 over 130 steps",
+                   "layers": NL, "batch": 1, "hidden": H, "prefill": P0, "decode_steps": NSTEP,
+                   "us_per_layer_token": round(us_call, 3), "dispatch": args.dispatch},
+        "roofline": {"bound": "hbm", "kernel": "layer call (all phases of one layer)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": round(bytes_per_call), "us_per_launch": round(us_call, 3)},
+    }
+
+    # ------------------------------------------------------------ batch-64 workload
+    if not args.no_batched:
+        result["batched"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream, layer_bytes)
+        del graphs
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, layer_bytes):
+    c4 = si.CONFIGS[4]
+    H, NL, B, dtype = c4["hidden"], c4["layers"], c4["batch"], c4["dtype"]
+    lens = si.kv_lengths(4, B, *c4["kv_len"])
+    cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch)
+    t0 = time.time()
+    weights, kvs = [], []
+    for l in range(NL):
+        wb = si.layer_weights(4, l, H, dtype)
+        weights.append(ga.Weights(*(to_dev(wb[n], dtype) for n in
+                                    ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o"))))
+        kv = ga.KVLayer.empty(B, 8, CAP_B64, dtype=torch.bfloat16, device=dev)
+        rows = si.kv_rows_many(4, l, list(range(B)), lens.tolist(), dtype)
+        for s, (kb, vb) in enumerate(rows):
+            kv.k[s, :, : lens[s]] = to_dev(kb, dtype)
+            kv.v[s, :, : lens[s]] = to_dev(vb, dtype)
+        kv.lens.copy_(torch.from_numpy(lens))
+        kvs.append(kv)
+    xs = torch.stack([to_dev(si.activations(4, l, 0, B, H, dtype), dtype) for l in range(NL)])
+    outs = torch.empty((NL, B, H), dtype=torch.float32, device=dev)
+    ws = ga.alloc_workspace(cfg, B, CAP_B64, device=dev)
+    base = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    torch.cuda.synchronize()
+    print(f"[bench] batch-64 inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    hl = lens.tolist()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(NL):
+            ga.layer_decode(cfg, weights[l], kvs[l], xs[l], outs[l], ws, host_lens=hl)
+        ga.kv_crop(kvs, base)
+    ga.kv_crop(kvs, base)
+    for _ in range(max(2, args.warmup // 4)):
+        g.replay()
+    torch.cuda.synchronize()
+    n = max(10, args.steps // 4)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(n):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / n
+    tok_s = B / (ms_step * 1e-3)
+    bytes_step = NL * layer_bytes(H, 16, 8, 128, lens.tolist(), B)
+    achieved = bytes_step / (ms_step * 1e-3) / 1e9
+    ok = all(int(kv.status.item()) == 0 for kv in kvs) and all(
+        torch.equal(kv.lens, base) for kv in kvs)
+    print(f"[bench] batch-64: {ms_step * 1000:.1f} us/step, {tok_s:.0f} tok/s, {achieved:.0f} GB/s (ok {ok})",
+          file=sys.stderr, flush=True)
+    return {"workload": "28-layer ragged batched decode, 64 seqs, bf16, hidden 1024, KV U{200..1500}",
+            "value": round(tok_s, 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4), "steps": n,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_step": bytes_step}}
+
+
+def cpu_baseline(budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the bs1 workload: layers 0..27 of
+    steps 0, 1, ... until the budget is spent; reported in microseconds per token."""
+    import numpy as np
+    import oracle
+    from synth import inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    H, dtype, P0 = 1024, si.F16, 795
+    ocfg = oracle.BlockConfig(hidden=H, dtype=dtype)
+    layers = []
+    for l in range(28):
+        w = oracle.LayerWeights.from_bits(si.layer_weights(2, l, H, dtype), dtype)
+        kb, vb = si.kv_rows(2, l, 0, P0, dtype)
+        c = oracle.KVCache.empty(1, 8, CAP_BS1, 128, dtype)
+        c.k[0, :, :P0], c.v[0, :, :P0], c.lens[0] = kb, vb, P0
+        xs = [si.activations(2, l, s, 1, H, dtype) for s in range(8)]
+        layers.append((w, c, xs))
+    calls = 0
+    t0 = time.perf_counter()
+    step = 0
+    while True:
+        for l in range(28):
+            w, c, xs = layers[l]
+            oracle.decode(ocfg, w, c, xs[step % len(xs)])
+            calls += 1
+        step += 1
+        if time.perf_counter() - t0 > budget_s or step >= 8:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(dt / calls * 28 * 1e6, 1), "unit": "us/token", "cores": cores, "kind": "oracle",
+            "sample": f"{step} decode steps x 28 layers of the bs1 workload (KV 795..{795 + step - 1}), "
+                      f"fp64 NumPy, {calls} layer calls in {dt:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,67 @@
+// Internal interface between the C ABI (api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "asr_attn.h"
+
+namespace asr {
+
+constexpr int kHeadDim = 128;          // the only head size this build supports
+constexpr int kMaxChunks = 64;        // split-KV chunks per (row, kv head)
+constexpr int kMinSplit = 16;         // keys per chunk, lower bound
+constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
+constexpr int kMaxVerifyK = 32;
+constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
+constexpr int kSyncWords = 1024;      // fused-dispatch counters (uint32)
+constexpr uint32_t kStatusBadSlot = 8u;  // slot index outside [0, batch_cap)
+
+// Everything a layer kernel needs, passed by value.
+struct LayerArgs {
+  // inputs
+  const uint16_t *x;          // [rows][H]
+  const uint16_t *residual;   // [rows][H] or null
+  const uint16_t *g_in;       // [H]
+  const uint16_t *w_qkv;      // [nqkv][H]
+  const uint16_t *g_q;        // [d]
+  const uint16_t *g_k;        // [d]
+  const uint16_t *w_o;        // [H][nq d]
+  const int32_t *slots;       // [B] or null
+  const int32_t *positions;   // [B] or null
+  // cache
+  uint16_t *kc, *vc;          // [batch_cap][nkv][capacity][d]
+  int32_t *lens;              // [batch_cap]
+  uint32_t *status;           // or null
+  // output
+  void *out;                  // [rows][H] fp32 or 16-bit
+  // workspace
+  float *qkv;                 // [rows][nqkv]
+  float *qn;                  // [rows][nq][d] normalised, rotated, pre-scaled q
+  float *att;                 // [rows][nq][d] attention output
+  float *part;                // [rows][nkv][kMaxChunks][group][kPartStride]
+  uint32_t *sync;             // [kSyncWords]
+  // shape
+  int B, n, rows;             // sequences, rows per sequence (1 decode, k verify), B * n
+  int H, nq, nkv, group, nqkv;
+  int batch_cap, capacity;
+  int split;                  // keys per chunk
+  float eps, theta;
+  int out_f32;
+};
+
+struct WorkspaceLayout {
+  size_t qkv, qn, att, part, sync, total;
+};
+
+WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);
+
+// launchers; return hipSuccess or the launch error
+hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s);
+hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
+                            const int32_t *slots, int B, int n, hipStream_t s);
+hipError_t launch_kv_crop(const asr_kv_layer *layers, int n_layers, const int32_t *new_lens,
+                          hipStream_t s);
+
+}  // namespace asr

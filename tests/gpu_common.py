@@ -1,0 +1,79 @@
+"""Helpers of the GPU parity tests: seeded layers on the device and in the oracle.
+
+Both sides read the same 16-bit bit patterns from ``synth.inputs``; the GPU
+side goes through the C ABI only.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import gqa_decode_attention_amd as ga
+import oracle
+from synth import inputs as si
+
+TOL = {si.F16: 2e-3, si.BF16: 8e-3}   # max |err| / RMS(oracle output) per call
+
+
+def tdt(dtype: str) -> torch.dtype:
+    return torch.float16 if dtype == si.F16 else torch.bfloat16
+
+
+def to_dev(bits: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt(dtype)).to(device)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def rel_err(got: np.ndarray, want: np.ndarray) -> float:
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return float(np.max(np.abs(got - want)) / np.sqrt(np.mean(want * want)))
+
+
+def ulp_dist(a_bits: np.ndarray, b_bits: np.ndarray) -> int:
+    """Largest distance in units of the last place between 16-bit patterns (same-sign ordering)."""
+    def key(u):
+        u = u.astype(np.int32)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return int(np.max(np.abs(key(a_bits) - key(b_bits)))) if a_bits.size else 0
+
+
+class SeededLayer:
+    """One layer's weights (device + oracle) from the seeded generator."""
+
+    def __init__(self, cfg_id, layer, hidden, dtype, nq=16, nkv=8, gain_mean=1.0):
+        self.dtype = dtype
+        self.bits = si.layer_weights(cfg_id, layer, hidden, dtype, nq=nq, nkv=nkv, gain_mean=gain_mean)
+        self.dev = ga.Weights(*(to_dev(self.bits[n], dtype) for n in
+                                ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o")))
+        self.ref = oracle.LayerWeights.from_bits(self.bits, dtype)
+        self.ocfg = oracle.BlockConfig(hidden=hidden, n_q_heads=nq, n_kv_heads=nkv, dtype=dtype)
+
+
+def fill_cache(cfg_id, layer, lens, capacity, dtype, nkv=8, seqs=None):
+    """Host cache bits [batch_cap][nkv][capacity][128] with seeded rows below each length."""
+    B = len(lens)
+    k = np.zeros((B, nkv, capacity, 128), np.uint16)
+    v = np.zeros_like(k)
+    seqs = range(B) if seqs is None else seqs
+    rows = si.kv_rows_many(cfg_id, layer, list(seqs), [int(lens[s]) for s in seqs], dtype, nkv=nkv)
+    for s, (kb, vb) in zip(seqs, rows):
+        k[s, :, : lens[s]] = kb
+        v[s, :, : lens[s]] = vb
+    return k, v
+
+
+def device_cache(kbits, vbits, lens, dtype) -> ga.KVLayer:
+    return ga.KVLayer(to_dev(kbits, dtype), to_dev(vbits, dtype),
+                      torch.tensor(np.asarray(lens, np.int32), device="cuda"),
+                      torch.zeros(1, dtype=torch.int32, device="cuda"))
+
+
+def oracle_cache(kbits, vbits, lens, dtype, seqs=None) -> oracle.KVCache:
+    """Oracle cache holding the given sequences (all by default), slot order kept."""
+    seqs = list(range(len(lens))) if seqs is None else list(seqs)
+    c = oracle.KVCache(kbits[seqs].copy(), vbits[seqs].copy(), np.asarray(lens, np.int64)[seqs].copy(), dtype)
+    return c

@@ -1,0 +1,273 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Small and mid-size cases that span several split-KV chunks with ragged tails,
+every dtype, verify block sizes, crop and append, error paths on the device.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_decode_attention_amd as ga
+import oracle
+from synth import inputs as si
+
+from gpu_common import (TOL, SeededLayer, device_cache, fill_cache, oracle_cache, rel_err, tdt, to_bits,
+                        to_dev, ulp_dist)
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(cfg_id, layer, step, shape, dtype):
+    rows = int(np.prod(shape[:-1]))
+    return si.activations(cfg_id, layer, step, rows, shape[-1], dtype).reshape(shape)
+
+
+def _run_decode(L, cfg, kv, xb, dtype, slots=None, positions=None, residual=None, host_lens=None, ws=None):
+    B, H = xb.shape
+    out = torch.empty((B, H), dtype=torch.float32 if cfg.out_dtype == ga.F32 else tdt(dtype), device="cuda")
+    ws = ga.alloc_workspace(cfg, B, kv.c.capacity) if ws is None else ws
+    ga.layer_decode(cfg, L.dev, kv, to_dev(xb, dtype), out, ws,
+                    slots=None if slots is None else torch.tensor(slots, dtype=torch.int32, device="cuda"),
+                    positions=None if positions is None else torch.tensor(positions, dtype=torch.int32, device="cuda"),
+                    residual=None if residual is None else to_dev(residual, dtype), host_lens=host_lens)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def test_cfg1_single_layer_decode():
+    """Single layer, bs1, fp16, hidden 1024, KV 64, new token at position 64."""
+    dtype, cap = si.F16, 128
+    L = SeededLayer(1, 0, 1024, dtype)
+    kb, vb = fill_cache(1, 0, [64], cap, dtype)
+    kv = device_cache(kb, vb, [64], dtype)
+    ref = oracle_cache(kb, vb, [64], dtype)
+    xb = _x(1, 0, 0, (1, 1024), dtype)
+    got = _run_decode(L, ga.config(dtype="f16"), kv, xb, dtype)
+    want = oracle.decode(L.ocfg, L.ref, ref, xb)
+    err = rel_err(got, want)
+    print(f"cfg1 max|err|/rms = {err:.3e}")
+    assert err < TOL[dtype]
+    assert int(kv.lens.item()) == 65 and int(kv.status.item()) == 0
+    kg, vg = to_bits(kv.k), to_bits(kv.v)
+    assert ulp_dist(kg[0, :, 64], ref.k[0, :, 64]) <= 1 and ulp_dist(vg[0, :, 64], ref.v[0, :, 64]) <= 1
+    untouched = np.ones(kg.shape, bool)
+    untouched[0, :, 64] = False
+    assert np.array_equal(kg[untouched], kb[untouched]) and np.array_equal(vg[untouched], vb[untouched])
+
+
+@pytest.mark.parametrize("dtype", [si.F16, si.BF16])
+@pytest.mark.parametrize("split", [0, 16, 48, 1024])
+def test_ragged_decode_vs_oracle(dtype, split):
+    lens = [0, 1, 17, 100, 333, 64]
+    cap = 400
+    slots = [3, 0, 5, 4, 1, 2]
+    L = SeededLayer(2, 1, 1024, dtype)
+    kb, vb = fill_cache(2, 1, lens, cap, dtype)
+    kv = device_cache(kb, vb, lens, dtype)
+    ref = oracle_cache(kb, vb, lens, dtype)
+    xb = _x(2, 1, 3, (6, 1024), dtype)
+    got = _run_decode(L, ga.config(dtype=dtype, kv_split=split), kv, xb, dtype, slots=slots)
+    want = oracle.decode(L.ocfg, L.ref, ref, xb, slots=slots)
+    err = rel_err(got, want)
+    print(f"ragged {dtype} split={split}: {err:.3e}")
+    assert err < TOL[dtype]
+    assert kv.lens.cpu().tolist() == [l + 1 for l in lens]
+    kg = to_bits(kv.k)
+    for s in range(6):
+        assert ulp_dist(kg[s, :, lens[s]], ref.k[s, :, lens[s]]) <= 1
+
+
+@pytest.mark.parametrize("dtype", [si.F16, si.BF16])
+def test_positions_residual_and_16bit_out(dtype):
+    lens = [10, 250]
+    L = SeededLayer(2, 2, 2048, dtype)
+    kb, vb = fill_cache(2, 2, lens, 300, dtype)
+    xb = _x(2, 2, 0, (2, 2048), dtype)
+    res = si.residual(2, 2, 0, 2, 2048, dtype)
+    pos = [1000, 3]
+    for out_dt in ("f32", dtype):
+        kv = device_cache(kb, vb, lens, dtype)
+        ref = oracle_cache(kb, vb, lens, dtype)
+        got = _run_decode(L, ga.config(hidden=2048, dtype=dtype, out_dtype=out_dt), kv, xb, dtype,
+                          positions=pos, residual=res, host_lens=lens)
+        want = oracle.decode(L.ocfg, L.ref, ref, xb, positions=pos, residual_bits=res)
+        err = rel_err(got, want)
+        print(f"pos/res {dtype} out={out_dt}: {err:.3e}")
+        assert err < TOL[dtype]
+
+
+def test_group_sizes_and_shapes():
+    """q heads per kv head 1, 2, 4, 8 (the index map i // group) at hidden 512 and 1536."""
+    dtype = si.F16
+    for hidden, nq, nkv in [(512, 4, 4), (1536, 8, 4), (1024, 16, 4), (1024, 16, 2)]:
+        L = SeededLayer(9, nq * 10 + nkv, hidden, dtype, nq=nq, nkv=nkv)
+        lens = [7, 130]
+        kb, vb = fill_cache(9, nq, lens, 160, dtype, nkv=nkv)
+        kv = device_cache(kb, vb, lens, dtype)
+        ref = oracle_cache(kb, vb, lens, dtype)
+        xb = _x(9, nq, 0, (2, hidden), dtype)
+        got = _run_decode(L, ga.config(hidden=hidden, n_q_heads=nq, n_kv_heads=nkv), kv, xb, dtype)
+        want = oracle.decode(L.ocfg, L.ref, ref, xb)
+        err = rel_err(got, want)
+        print(f"H={hidden} nq={nq} nkv={nkv}: {err:.3e}")
+        assert err < TOL[dtype]
+
+
+def test_determinism_and_split_invariance():
+    dtype = si.BF16
+    lens = [900, 37, 512]
+    L = SeededLayer(3, 0, 1024, dtype)
+    kb, vb = fill_cache(3, 0, lens, 1024, dtype)
+    xb = _x(3, 0, 0, (3, 1024), dtype)
+    outs = {}
+    for split, rep in [(16, 0), (16, 1), (64, 0), (256, 0)]:
+        kv = device_cache(kb, vb, lens, dtype)
+        outs[(split, rep)] = _run_decode(L, ga.config(dtype=dtype, kv_split=split), kv, xb, dtype)
+    assert np.array_equal(outs[(16, 0)], outs[(16, 1)])
+    for split in (64, 256):
+        assert rel_err(outs[(split, 0)], outs[(16, 0)]) < 1e-4
+
+
+def _run_verify(L, cfg, kv, xb, dtype, slots=None, positions=None, ws=None):
+    B, k, H = xb.shape
+    out = torch.empty((B, k, H), dtype=torch.float32, device="cuda")
+    ws = ga.alloc_workspace(cfg, B * k, kv.c.capacity) if ws is None else ws
+    ga.layer_verify(cfg, L.dev, kv, to_dev(xb, dtype), out, ws,
+                    slots=None if slots is None else torch.tensor(slots, dtype=torch.int32, device="cuda"),
+                    positions=None if positions is None else torch.tensor(positions, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("k", [1, 3, 8, 16, 32])
+@pytest.mark.parametrize("dtype", [si.F16, si.BF16])
+def test_verify_vs_oracle(k, dtype):
+    lens = [5, 64, 200]
+    slots = [2, 0, 1]
+    L = SeededLayer(3, 1, 1024, dtype)
+    kb, vb = fill_cache(3, 1, lens, 256, dtype)
+    kv = device_cache(kb, vb, lens, dtype)
+    ref = oracle_cache(kb, vb, lens, dtype)
+    xb = _x(3, 1, k, (3, k, 1024), dtype)
+    got = _run_verify(L, ga.config(dtype=dtype), kv, xb, dtype, slots=slots)
+    want = oracle.verify(L.ocfg, L.ref, ref, xb, slots=slots)
+    err = rel_err(got, want)
+    print(f"verify k={k} {dtype}: {err:.3e}")
+    assert err < TOL[dtype]
+    assert kv.lens.cpu().tolist() == [l + k for l in lens]
+    kg = to_bits(kv.k)
+    for b, s in enumerate(slots):
+        assert ulp_dist(kg[s, :, lens[s]:lens[s] + k], ref.k[s, :, lens[s]:lens[s] + k]) <= 1
+
+
+@pytest.mark.parametrize("k", [4, 8])
+def test_verify_rows_equal_sequential_decode_rows(k):
+    """With the same chunking, a verify block and k single-token steps give identical bits."""
+    dtype = si.F16
+    lens = [795, 40]
+    L = SeededLayer(3, 2, 1024, dtype)
+    kb, vb = fill_cache(3, 2, lens, 832, dtype)
+    xb = _x(3, 2, 0, (2, k, 1024), dtype)
+    cfg = ga.config(dtype=dtype, kv_split=32)
+    kv1 = device_cache(kb, vb, lens, dtype)
+    ov = _run_verify(L, cfg, kv1, xb, dtype)
+    kv2 = device_cache(kb, vb, lens, dtype)
+    od = np.stack([_run_decode(L, cfg, kv2, xb[:, r, :], dtype) for r in range(k)], axis=1)
+    assert np.array_equal(ov, od)
+    assert np.array_equal(to_bits(kv1.k), to_bits(kv2.k)) and np.array_equal(to_bits(kv1.v), to_bits(kv2.v))
+    # the automatic chunking may differ between the two; then they agree to rounding
+    kv3 = device_cache(kb, vb, lens, dtype)
+    ov3 = _run_verify(L, ga.config(dtype=dtype), kv3, xb, dtype)
+    assert rel_err(ov3, od) < 1e-4
+
+
+@pytest.mark.parametrize("a", [0, 1, 5, 8])
+def test_crop_after_rejection_equals_never_appended(a):
+    """Verify k = 8, crop to the accepted prefix, poison the dropped rows with NaN: the next
+    decode is bit-identical to a cache that only ever received the accepted rows."""
+    dtype, k = si.F16, 8
+    lens = [795]
+    L = SeededLayer(3, 3, 1024, dtype)
+    kb, vb = fill_cache(3, 3, lens, 832, dtype)
+    xs = _x(3, 3, 1, (1, k, 1024), dtype)
+    xn = _x(3, 3, 2, (1, 1024), dtype)
+    cfg = ga.config(dtype=dtype, kv_split=64)
+    spec = device_cache(kb, vb, lens, dtype)
+    _run_verify(L, cfg, spec, xs, dtype)
+    ga.kv_crop([spec], torch.tensor([795 + a], dtype=torch.int32, device="cuda"))
+    spec.k[0, :, 795 + a:] = float("nan")
+    spec.v[0, :, 795 + a:] = float("nan")
+    ref = device_cache(kb, vb, lens, dtype)
+    if a:
+        _run_verify(L, cfg, ref, xs[:, :a, :], dtype)
+    o_spec = _run_decode(L, cfg, spec, xn, dtype)
+    o_ref = _run_decode(L, cfg, ref, xn, dtype)
+    assert np.all(np.isfinite(o_spec))
+    assert np.array_equal(o_spec, o_ref)
+    assert spec.lens.item() == ref.lens.item() == 795 + a + 1 and spec.status.item() == 0
+
+
+def test_kv_append_and_crop_bit_exact():
+    dtype = si.BF16
+    cap, nkv = 40, 8
+    lens0 = np.array([3, 0, 10, 38], np.int32)
+    g = np.random.default_rng(5)
+    kb = g.integers(0, 2 ** 16, (4, nkv, cap, 128)).astype(np.uint16)
+    vb = g.integers(0, 2 ** 16, (4, nkv, cap, 128)).astype(np.uint16)
+    layers = [device_cache(kb, vb, lens0, dtype) for _ in range(3)]
+    kn = g.integers(0, 2 ** 16, (3, 5, nkv, 128)).astype(np.uint16)
+    vn = g.integers(0, 2 ** 16, (3, 5, nkv, 128)).astype(np.uint16)
+    slots = [2, 0, 3]                      # slot 3 (length 38) overflows capacity 40 with 5 rows
+    ga.kv_append(layers[0], to_dev(kn, dtype), to_dev(vn, dtype),
+                 slots=torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.KVCache(kb.copy(), vb.copy(), lens0.astype(np.int64), dtype)
+    oracle.kv_append(ref, kn, vn, slots=slots)
+    assert np.array_equal(to_bits(layers[0].k), ref.k) and np.array_equal(to_bits(layers[0].v), ref.v)
+    assert layers[0].lens.cpu().tolist() == ref.lens.tolist() == [8, 0, 15, 38]
+    assert layers[0].status.item() == ga.STATUS_CAPACITY == ref.status
+    # crop all three layers in one call; layer 0 grew, the others still have lens0
+    new = torch.tensor([2, 0, 12, 38], dtype=torch.int32, device="cuda")
+    ga.kv_crop(layers, new)
+    torch.cuda.synchronize()
+    assert layers[0].lens.cpu().tolist() == [2, 0, 12, 38]
+    assert layers[1].lens.cpu().tolist() == [2, 0, 10, 38] and layers[1].status.item() == ga.STATUS_CROP_GROW
+    assert np.array_equal(to_bits(layers[0].k), ref.k)          # crop never touches data
+
+
+def test_device_side_errors_write_nan_and_set_status():
+    dtype = si.F16
+    lens = [16, 5, 16]
+    L = SeededLayer(4, 0, 1024, dtype)
+    kb, vb = fill_cache(4, 0, lens, 16, dtype)
+    kv = device_cache(kb, vb, lens, dtype)
+    xb = _x(4, 0, 0, (3, 1024), dtype)
+    got = _run_decode(L, ga.config(dtype=dtype), kv, xb, dtype)
+    assert np.all(np.isnan(got[0])) and np.all(np.isnan(got[2])) and np.all(np.isfinite(got[1]))
+    assert kv.lens.cpu().tolist() == [16, 6, 16] and kv.status.item() == ga.STATUS_CAPACITY
+    # a slot outside [0, batch_cap)
+    kv2 = device_cache(kb, vb, lens, dtype)
+    got = _run_decode(L, ga.config(dtype=dtype), kv2, xb[:2], dtype, slots=[1, 7])
+    assert np.all(np.isfinite(got[0])) and np.all(np.isnan(got[1]))
+    assert kv2.status.item() == ga.STATUS_BAD_SLOT
+
+
+def test_host_side_validation():
+    dtype = si.F16
+    L = SeededLayer(4, 1, 1024, dtype)
+    kb, vb = fill_cache(4, 1, [4], 8, dtype)
+    kv = device_cache(kb, vb, [4], dtype)
+    x = to_dev(_x(4, 1, 0, (1, 1024), dtype), dtype)
+    out = torch.empty((1, 1024), dtype=torch.float32, device="cuda")
+    cfg = ga.config()
+    ws = ga.alloc_workspace(cfg, 1, 8)
+    with pytest.raises(ga.AsrError) as e:
+        ga.layer_decode(cfg, L.dev, kv, x, out, ws, host_lens=[8])
+    assert e.value.code == -3
+    with pytest.raises(ga.AsrError) as e:
+        ga.layer_decode(cfg, L.dev, kv, x, out, ws[:100])
+    assert e.value.code == -4
+    with pytest.raises(ga.AsrError) as e:
+        ga.layer_decode(ga.config(head_dim=64), L.dev, kv, x, out, ws)
+    assert e.value.code == -2
+    assert kv.lens.item() == 4     # nothing was enqueued

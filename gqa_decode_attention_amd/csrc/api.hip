@@ -3,6 +3,7 @@
 // memory back.
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 #include "internal.h"
 
@@ -46,6 +47,13 @@ int check_kv(const asr_kv_layer *kv, const asr_attn_config *c) {
     if (kv->n_kv_heads != c->n_kv_heads || kv->dtype != c->dtype) return ASR_EINVAL;
   }
   return ASR_OK;
+}
+
+// Workgroups per CU of the fused dispatch (a tuning knob; 1 by default).
+int fused_blocks_per_cu() {
+  const char *v = getenv("ASR_ATTN_FUSED_BLOCKS_PER_CU");
+  const int n = v ? atoi(v) : 1;
+  return n >= 1 && n <= 8 ? n : 1;
 }
 
 int device_cus() {
@@ -99,7 +107,6 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
     for (int b = 0; b < B; ++b)
       if (host_lens[b] < 0 || (long long)host_lens[b] + n > kv->capacity) return ASR_ECAPACITY;
   }
-  if (cfg->dispatch == ASR_DISPATCH_FUSED) return ASR_EUNSUPPORTED;
 
   const int cus = device_cus();
   LayerArgs a;
@@ -119,10 +126,11 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.out = out;
   char *base = static_cast<char *>(ws);
   a.qkv = reinterpret_cast<float *>(base + lay.qkv);
-  a.qn = reinterpret_cast<float *>(base + lay.qn);
   a.att = reinterpret_cast<float *>(base + lay.att);
   a.part = reinterpret_cast<float *>(base + lay.part);
-  a.sync = reinterpret_cast<uint32_t *>(base + lay.sync);
+  a.bar = reinterpret_cast<uint32_t *>(base + lay.bar);
+  a.mctr = reinterpret_cast<uint32_t *>(base + lay.mctr);
+  a.rowtab = reinterpret_cast<int4 *>(base + lay.rowtab);
   a.B = B;
   a.n = n;
   a.rows = rows;
@@ -148,8 +156,18 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   const long long cap_grid = 16LL * cus;
   const int attn_grid = (int)(bound < 1 ? 1 : (bound > cap_grid ? cap_grid : bound));
 
-  if (launch_layer_multi(a, cfg->dtype, attn_grid, stream) != hipSuccess) return ASR_EHIP;
-  return ASR_OK;
+  bool fused = false;
+  int fused_grid = 0;
+  if (cfg->dispatch != ASR_DISPATCH_MULTI && layer_fused_supported(a)) {
+    fused_grid = fused_max_grid(cfg->dtype, a.H, layer_dyn_smem(a), cus);
+    const long long want = (long long)cus * fused_blocks_per_cu();
+    if (fused_grid > want) fused_grid = (int)want;
+    fused = fused_grid > 0;
+  }
+  if (cfg->dispatch == ASR_DISPATCH_FUSED && !fused) return ASR_EUNSUPPORTED;
+  const hipError_t e = fused ? launch_layer_fused(a, cfg->dtype, fused_grid, stream)
+                             : launch_layer_multi(a, cfg->dtype, attn_grid, stream);
+  return e == hipSuccess ? ASR_OK : ASR_EHIP;
 }
 
 }  // namespace
@@ -160,12 +178,14 @@ WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity)
   WorkspaceLayout l;
   const size_t nqkv = (size_t)(nq + 2 * nkv) * kHeadDim;
   size_t off = 0;
-  l.sync = off;
-  off = align_up(off + kSyncWords * sizeof(uint32_t));
+  l.bar = off;
+  off = align_up(off + 2 * sizeof(uint32_t));
+  l.mctr = off;
+  off = align_up(off + (size_t)rows * nkv * sizeof(uint32_t));
+  l.rowtab = off;
+  off = align_up(off + (size_t)rows * 4 * sizeof(int));
   l.qkv = off;
   off = align_up(off + (size_t)rows * nqkv * sizeof(float));
-  l.qn = off;
-  off = align_up(off + (size_t)rows * nq * kHeadDim * sizeof(float));
   l.att = off;
   off = align_up(off + (size_t)rows * nq * kHeadDim * sizeof(float));
   l.part = off;

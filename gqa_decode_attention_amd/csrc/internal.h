@@ -15,7 +15,6 @@ constexpr int kMinSplit = 16;         // keys per chunk, lower bound
 constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
 constexpr int kMaxVerifyK = 32;
 constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
-constexpr int kSyncWords = 1024;      // fused-dispatch counters (uint32)
 constexpr uint32_t kStatusBadSlot = 8u;  // slot index outside [0, batch_cap)
 
 // Everything a layer kernel needs, passed by value.
@@ -36,12 +35,13 @@ struct LayerArgs {
   uint32_t *status;           // or null
   // output
   void *out;                  // [rows][H] fp32 or 16-bit
-  // workspace
+  // workspace (zero-filled once by the caller; every call leaves the counters at zero)
   float *qkv;                 // [rows][nqkv]
-  float *qn;                  // [rows][nq][d] normalised, rotated, pre-scaled q
   float *att;                 // [rows][nq][d] attention output
   float *part;                // [rows][nkv][kMaxChunks][group][kPartStride]
-  uint32_t *sync;             // [kSyncWords]
+  uint32_t *bar;              // [2] grid barrier: arrival count, generation
+  uint32_t *mctr;             // [rows][nkv] finished chunks per (row, kv head)
+  int4 *rowtab;               // [rows] {ok, L, slot, slot_ok} as seen before the call
   // shape
   int B, n, rows;             // sequences, rows per sequence (1 decode, k verify), B * n
   int H, nq, nkv, group, nqkv;
@@ -52,13 +52,17 @@ struct LayerArgs {
 };
 
 struct WorkspaceLayout {
-  size_t qkv, qn, att, part, sync, total;
+  size_t bar, mctr, rowtab, qkv, att, part, total;
 };
 
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);
 
 // launchers; return hipSuccess or the launch error
 hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s);
+bool layer_fused_supported(const LayerArgs &a);
+hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream_t s);
+int fused_max_grid(int dtype, int H, size_t dyn_smem, int cus);
+size_t layer_dyn_smem(const LayerArgs &a);
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
                             const int32_t *slots, int B, int n, hipStream_t s);
 hipError_t launch_kv_crop(const asr_kv_layer *layers, int n_layers, const int32_t *new_lens,

@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--dispatch", type=int, default=0, help="0 auto, 1 one kernel per phase, 2 fused")
+    p.add_argument("--kv-split", type=int, default=0, help="keys per split-KV chunk (0: automatic)")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="run only this many bs1 steps eagerly (for profilers) and exit")
     return p.parse_args()
@@ -82,7 +83,7 @@ def main():
     c2 = si.CONFIGS[2]
     H, NL, dtype = c2["hidden"], c2["layers"], c2["dtype"]
     P0, NSTEP = 795, 130
-    cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch)
+    cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch, kv_split=args.kv_split)
     t0 = time.time()
     weights, kvs = [], []
     for l in range(NL):
@@ -193,7 +194,7 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, layer_bytes):
     c4 = si.CONFIGS[4]
     H, NL, B, dtype = c4["hidden"], c4["layers"], c4["batch"], c4["dtype"]
     lens = si.kv_lengths(4, B, *c4["kv_len"])
-    cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch)
+    cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch, kv_split=args.kv_split)
     t0 = time.time()
     weights, kvs = [], []
     for l in range(NL):

@@ -126,6 +126,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.out = out;
   char *base = static_cast<char *>(ws);
   a.qkv = reinterpret_cast<float *>(base + lay.qkv);
+  a.ssq = reinterpret_cast<float *>(base + lay.ssq);
   a.att = reinterpret_cast<float *>(base + lay.att);
   a.part = reinterpret_cast<float *>(base + lay.part);
   a.bar = reinterpret_cast<uint32_t *>(base + lay.bar);
@@ -186,6 +187,8 @@ WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity)
   off = align_up(off + (size_t)rows * 4 * sizeof(int));
   l.qkv = off;
   off = align_up(off + (size_t)rows * nqkv * sizeof(float));
+  l.ssq = off;
+  off = align_up(off + (size_t)rows * (nq + nkv) * 8 * sizeof(float));
   l.att = off;
   off = align_up(off + (size_t)rows * nq * kHeadDim * sizeof(float));
   l.part = off;

@@ -1,17 +1,23 @@
 // One attention-block layer call (decode or k-token verify) on gfx950.
 //
-// Three phases; every phase is a loop over independent work items, written as
-// device functions that both dispatch modes share:
-//   A. QKV tiles     input RMSNorm fused into the q/k/v projection (GEMV over rows)
-//   C. attention     one item per (row, kv head g, chunk of keys): per-head RMSNorm
-//                    and rotary of q (and of the new k rows the chunk holds), KV
-//                    append, single-pass online-softmax attention of all q heads of
-//                    g over the chunk, a partial (m, l, acc) per q head; the last
-//                    item of a (row, g) to finish merges its chunks (log-sum-exp)
-//   D. o_proj tiles  output projection (+ residual); lengths advanced
-// ASR_DISPATCH_MULTI runs A, C, D as three kernels in stream order.
+// Phases; each is a loop over independent work items, written as device
+// functions shared by both dispatch modes:
+//   A. QKV tiles   input RMSNorm fused into the q/k/v projection (16 output rows
+//                  per tile, all input rows).  The last tile of each head to
+//                  finish completes the head for every row: RMSNorm and rotary of
+//                  q (kept in fp32, pre-scaled) and k, and the rounded append of
+//                  k and v to the cache.
+//   C. attention   one item per (row, kv head g, chunk of keys): all q heads of g
+//                  share every K/V row of the chunk; single-pass online softmax;
+//                  a partial (m, l, acc) per q head.
+//                  The last item of a (row, g) to finish merges the chunks
+//                  (log-sum-exp, chunk order) into the attention output.
+//   D. o_proj      output projection (+ residual); lengths advanced.
+// ASR_DISPATCH_MULTI runs the phases as kernels in stream order; a kernel
+// boundary makes each phase's results visible to the next.
 // ASR_DISPATCH_FUSED runs them in one persistent kernel whose workgroups meet at
-// a grid barrier between phases (two per call).
+// a grid barrier between phases; data crossing workgroups inside it go through
+// device-coherent accesses (st_dev / ld_dev).
 //
 // The operation list follows "Qwen3-ASR -- Latency & Bottleneck Analysis",
 // section 07 (q/k/v projections, GQA repeat_kv, QK^T, fp32 softmax, AV, o_proj)
@@ -27,7 +33,29 @@ namespace asr {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr long long kBarrierTimeoutTicks = 50000000;   // wall clock ticks (about 0.5 s at 100 MHz)
+constexpr long long kBarrierTimeoutTicks = 50000000;   // wall clock ticks (0.05 s at 1 GHz)
+constexpr int kRpwA = 4;                              // phase A rows per wave: tiles of 16 rows
+constexpr int kTilesPerHead = kHeadDim / (4 * kRpwA); // 8
+constexpr int kRpwD = 1;                              // phase D rows per wave: tiles of 4 rows
+
+// ---------------------------------------------------------------- coherence-selected accesses
+template <bool COH> __device__ __forceinline__ float ldx(const float *p) {
+  if constexpr (COH) return ld_dev(p); else return *p;
+}
+template <bool COH> __device__ __forceinline__ void stx(float *p, float v) {
+  if constexpr (COH) st_dev(p, v); else *p = v;
+}
+template <bool COH> __device__ __forceinline__ void stx16(uint16_t *p, uint16_t v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); else *p = v;
+}
+template <bool COH> __device__ __forceinline__ uint4 ldx16B(const uint16_t *p) {
+  if constexpr (COH) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+    return make_uint4(ld_dev(q), ld_dev(q + 1), ld_dev(q + 2), ld_dev(q + 3));
+  } else {
+    return ld16_stream(p);
+  }
+}
 
 struct RowInfo {
   int slot, L, pos, nvis, r;
@@ -52,37 +80,86 @@ __device__ __forceinline__ RowInfo row_info(const LayerArgs &A, int row) {
 
 __device__ __forceinline__ int chunks_of(int nvis, int split) { return (nvis + split - 1) / split; }
 
-// rotary angle of pair t at position pos: pos * theta^(-2t/d), formed in fp64
-__device__ __forceinline__ void rope_cs(int pos, int t, float theta, float &c, float &s) {
-  const double omega = exp2(-(2.0 * t / kHeadDim) * log2((double)theta));
-  double sn, cs;
-  sincos((double)pos * omega, &sn, &cs);
-  c = (float)cs;
-  s = (float)sn;
+// Row table for phases M and D (which must not read lens: lengths change in D).
+template <bool COH>
+__device__ void write_row_table(const LayerArgs &A) {
+  for (int row = threadIdx.x; row < A.rows; row += blockDim.x) {
+    const RowInfo ri = row_info(A, row);
+    int *rec = reinterpret_cast<int *>(A.rowtab + row);
+    if constexpr (COH) {
+      st_dev(rec + 0, (int)ri.ok);
+      st_dev(rec + 1, ri.L);
+      st_dev(rec + 2, ri.slot);
+      st_dev(rec + 3, (int)ri.slot_ok);
+    } else {
+      A.rowtab[row] = make_int4(ri.ok, ri.L, ri.slot, ri.slot_ok);
+    }
+  }
+}
+
+template <bool COH>
+__device__ __forceinline__ int4 read_row_table(const LayerArgs &A, int row) {
+  if constexpr (COH) {
+    const int *rec = reinterpret_cast<const int *>(A.rowtab + row);
+    return make_int4(ld_dev(rec), ld_dev(rec + 1), ld_dev(rec + 2), ld_dev(rec + 3));
+  } else {
+    return A.rowtab[row];
+  }
 }
 
 // ---------------------------------------------------------------- phase A: QKV projection
 //
-// Wave w of tile t owns RPW consecutive output rows; their weights stay in
-// registers while the wave walks over the input rows RB at a time.  Lane l
-// covers columns (v * 64 + l) * 8 .. + 7 for v < KV, so every wave-wide load
-// reads 1 KB contiguously.  RMSNorm: h = x * g / sqrt(mean(x^2) + eps).
-template <int DT, int KV, int RB, int RPW>
-__device__ void qkv_tile(const LayerArgs &A, int tile) {
+// RMSNorm of q and k is a per-head scalar, so rotary can act before it:
+// rotate(g * q / rms) = rotate(g * q) / rms.  A tile therefore owns whole rotary
+// pairs: tile j of head h holds pair indices t in [8 jj, 8 jj + 8) (jj = j % 8),
+// i.e. the output rows h*128 + t and h*128 + 64 + t; wave w takes two pairs.
+// For q and k heads the tile stores u = rotate(gain * qk_raw) and the partial sum
+// of squares of its raw rows; the consumer finishes with u / sqrt(sum/d + eps).
+// v heads are stored raw.  Rotary: pair t at position pos turns by
+// pos * theta^(-2t/d); the angle and its cosine and sine are formed in fp64.
+//
+// Lane l covers input columns (v * 64 + l) * 8 .. + 7 for v < KV, so every
+// wave-wide load reads 1 KB contiguously; the wave's four weight rows stay in
+// registers while it walks over the input rows RB at a time.
+// Input RMSNorm: h = x * g_in / sqrt(mean(x^2) + eps).
+template <int DT, int KV, int RB, bool COH>
+__device__ void qkv_tile(const LayerArgs &A, int tile, float (*s_ssq)[4]) {
   const int wave = wave_id(), lane = lane_id();
-  const int o0 = (tile * 4 + wave) * RPW;
+  const int head = tile / kTilesPerHead, jj = tile % kTilesPerHead;
+  const int ta = 8 * jj + 2 * wave, tb = ta + 1;
+  const int orow[4] = {head * kHeadDim + ta, head * kHeadDim + ta + 64, head * kHeadDim + tb, head * kHeadDim + tb + 64};
+  const bool rot = head < A.nq + A.nkv;
   const int H = A.H;
-  uint4 wr[RPW][KV];
+  uint4 wr[4][KV];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int v = 0; v < KV; ++v)
-      wr[i][v] = ld16_stream(A.w_qkv + (size_t)(o0 + i) * H + (v * 64 + lane) * 8);
+      wr[i][v] = ld16_stream(A.w_qkv + (size_t)orow[i] * H + (v * 64 + lane) * 8);
   float g[KV * 8];
 #pragma unroll
   for (int v = 0; v < KV; ++v) unpack8<DT>(ld16(A.g_in + (v * 64 + lane) * 8), g + v * 8);
+  float gq[4] = {1.f, 1.f, 1.f, 1.f};
+  if (rot) {
+    const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;
+    gq[0] = cvt16<DT>(gp[ta]);
+    gq[1] = cvt16<DT>(gp[ta + 64]);
+    gq[2] = cvt16<DT>(gp[tb]);
+    gq[3] = cvt16<DT>(gp[tb + 64]);
+  }
+  const double om_a = exp2(-(2.0 * ta / kHeadDim) * log2((double)A.theta));
+  const double om_b = exp2(-(2.0 * tb / kHeadDim) * log2((double)A.theta));
 
   for (int rb = 0; rb < A.rows; rb += RB) {
+    // cos/sin for the RB rows: lane 2r computes pair ta of row rb + r, lane 2r + 1 pair tb
+    float cs_c = 1.f, cs_s = 0.f;
+    if (rot && lane < 2 * RB && rb + lane / 2 < A.rows) {
+      const RowInfo ri = row_info(A, rb + lane / 2);
+      double sn, cs;
+      sincos((double)ri.pos * ((lane & 1) ? om_b : om_a), &sn, &cs);
+      cs_c = (float)cs;
+      cs_s = (float)sn;
+    }
     float x[RB][KV * 8];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -102,9 +179,9 @@ __device__ void qkv_tile(const LayerArgs &A, int tile) {
 #pragma unroll
       for (int e = 0; e < KV * 8; ++e) x[r][e] *= g[e] * inv;
     }
-    float acc[RPW][RB];
+    float acc[4][RB];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < RB; ++r) acc[i][r] = 0.f;
 #pragma unroll
@@ -118,53 +195,70 @@ __device__ void qkv_tile(const LayerArgs &A, int tile) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < RPW; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < RB; ++r) acc[i][r] = wave_sum(acc[i][r]);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int row = rb + r;
-      if (row < A.rows && lane < RPW) {
-        float val = acc[0][r];
-#pragma unroll
-        for (int i = 1; i < RPW; ++i)
-          if (lane == i) val = acc[i][r];
-        A.qkv[(size_t)row * A.nqkv + o0 + lane] = val;
+      if (row >= A.rows) continue;
+      float o[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      if (rot) {
+        const float ca = readlane(cs_c, 2 * r), sa = readlane(cs_s, 2 * r);
+        const float cb = readlane(cs_c, 2 * r + 1), sb = readlane(cs_s, 2 * r + 1);
+        const float ssq = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+        const float u0 = gq[0] * o[0], u1 = gq[1] * o[1], u2 = gq[2] * o[2], u3 = gq[3] * o[3];
+        o[0] = u0 * ca - u1 * sa;
+        o[1] = u1 * ca + u0 * sa;
+        o[2] = u2 * cb - u3 * sb;
+        o[3] = u3 * cb + u2 * sb;
+        if (lane == 0) s_ssq[r][wave] = ssq;
       }
+      if (lane < 4) {
+        float val = o[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+          if (lane == i) val = o[i];
+        stx<COH>(A.qkv + (size_t)row * A.nqkv + orow[lane], val);
+      }
+    }
+    if (rot) {
+      __syncthreads();
+      if (threadIdx.x < RB && rb + (int)threadIdx.x < A.rows) {
+        const int r = threadIdx.x;
+        stx<COH>(A.ssq + ((size_t)(rb + r) * (A.nq + A.nkv) + head) * kTilesPerHead + jj,
+                 s_ssq[r][0] + s_ssq[r][1] + s_ssq[r][2] + s_ssq[r][3]);
+      }
+      __syncthreads();
     }
   }
 }
 
-// Row table for phase D (which must not read lens: lengths change there).
-__device__ void write_row_table(const LayerArgs &A) {
-  for (int row = threadIdx.x; row < A.rows; row += blockDim.x) {
-    const RowInfo ri = row_info(A, row);
-    int4 rec;
-    rec.x = ri.ok;
-    rec.y = ri.L;
-    rec.z = ri.slot;
-    rec.w = ri.slot_ok;
-    A.rowtab[row] = rec;
-  }
+// 1 / sqrt(mean of squares + eps) of head `head` of row `row` from the tile partials
+template <bool COH>
+__device__ __forceinline__ float head_inv_rms(const LayerArgs &A, int row, int head) {
+  const float *p = A.ssq + ((size_t)row * (A.nq + A.nkv) + head) * kTilesPerHead;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTilesPerHead; ++j) s += ldx<COH>(p + j);
+  return 1.0f / sqrtf(s / (float)kHeadDim + A.eps);
 }
 
 // ---------------------------------------------------------------- phase C: attention
 //
 // Items are (row, kv head g, chunk c) for every chunk of `split` keys that holds
 // a visible key of the row.  A block-wide prefix sum over the rows' chunk counts
-// (from lens, on the device: no host readback) maps a flat item id to its
-// (row, g, c).
+// (from lens, on the device: no host readback) maps a flat item id to (row, g, c).
 //
 // Lane layout: groups of 8 lanes; a group owns one key row (8 lanes x 16 dims =
 // 128 dims, 256 contiguous bytes); a wave takes 8 keys per step, the block 32.
 // Each wave keeps a running max and sum per q head (online softmax), so K and
-// V stream once with no score buffer; the 4 waves are combined in LDS at the
-// end of the item.
+// V stream once; the 4 waves are combined in LDS at the end of the item.
 template <int GROUP>
 struct AttnShared {
-  float q[GROUP][kHeadDim];
   float acc[4][GROUP][kHeadDim];
   float m[4][GROUP], l[4][GROUP];
+  float w[GROUP][kMaxChunks];     // merge weights 2^(m_c - M) / sum
   float mc[GROUP][kMaxChunks], lc[GROUP][kMaxChunks];
   int wsum[4];
   int flag;
@@ -197,87 +291,90 @@ __device__ void build_item_prefix(const LayerArgs &A, int *pre, int *wsum) {
   __syncthreads();
 }
 
-// one wave: per-head RMSNorm (gain gp) and rotary of a 128-vector held as the
-// pairs (u0, u1) = (t, t + 64) of lane t
-template <int DT>
-__device__ __forceinline__ void norm_rope(float &u0, float &u1, const uint16_t *gp, float eps, int pos,
-                                          float theta, int lane) {
-  const float ss = wave_sum(u0 * u0 + u1 * u1);
-  const float inv = 1.0f / sqrtf(ss / (float)kHeadDim + eps);
-  u0 *= cvt16<DT>(gp[lane]) * inv;
-  u1 *= cvt16<DT>(gp[lane + 64]) * inv;
-  float c, s;
-  rope_cs(pos, lane, theta, c, s);
-  const float r0 = u0 * c - u1 * s;
-  const float r1 = u1 * c + u0 * s;
-  u0 = r0;
-  u1 = r1;
-}
+struct Item {
+  int row, g, c, nch;
+};
 
-template <int DT, int GROUP>
-__device__ void attn_item(const LayerArgs &A, int item, const int *pre, uint16_t *knew, uint16_t *vnew,
-                          AttnShared<GROUP> &S) {
-  const int wave = wave_id(), lane = lane_id();
-  const int kl = lane & 7, kr = lane >> 3;
+__device__ __forceinline__ Item decode_item(const LayerArgs &A, int item, const int *pre) {
   int lo = 0, hi = A.rows;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (pre[mid] <= item) lo = mid; else hi = mid;
   }
-  const int row = lo;
-  const int nch = (pre[row + 1] - pre[row]) / A.nkv;
-  const int rem = item - pre[row];
-  const int g = rem / nch, c = rem - g * nch;
+  Item it;
+  it.row = lo;
+  it.nch = (pre[lo + 1] - pre[lo]) / A.nkv;
+  const int rem = item - pre[lo];
+  it.g = rem / it.nch;
+  it.c = rem - it.g * it.nch;
+  return it;
+}
+
+template <int DT, int GROUP, bool COH>
+__device__ void attn_item(const LayerArgs &A, const Item &it, uint16_t *knew, uint16_t *vnew, AttnShared<GROUP> &S) {
+  const int wave = wave_id(), lane = lane_id();
+  const int kl = lane & 7, kr = lane >> 3;
+  const int row = it.row, g = it.g, c = it.c;
   const RowInfo ri = row_info(A, row);
   const int L = ri.L;
   const int t0 = c * A.split, t1 = min(t0 + A.split, ri.nvis);
   const int nb = max(t0, L);            // first appended position inside the chunk
   const int n_new = max(0, t1 - nb);    // appended rows this chunk sees
-  const bool writer = (ri.r == A.n - 1);
+  const size_t kvrow0 = ((size_t)ri.slot * A.nkv + g) * A.capacity;
+  const uint16_t *Kp = A.kc + kvrow0 * kHeadDim + kl * 16;
+  const uint16_t *Vp = A.vc + kvrow0 * kHeadDim + kl * 16;
 
-  // q of the GROUP heads: norm, rotate, pre-scale by log2(e)/sqrt(d)
-  for (int j = wave; j < GROUP; j += 4) {
-    const float *src = A.qkv + (size_t)row * A.nqkv + (g * GROUP + j) * kHeadDim;
-    float u0 = src[lane], u1 = src[lane + 64];
-    norm_rope<DT>(u0, u1, A.g_q, A.eps, ri.pos, A.theta, lane);
-    const float qs = kLog2e * rsqrtf((float)kHeadDim);
-    S.q[j][lane] = u0 * qs;
-    S.q[j][lane + 64] = u1 * qs;
-  }
-  // new K/V rows at positions nb .. t1-1 (rows r' = p - L of this sequence): rounded
-  // as the cache stores them; the last row's item also writes them to the cache
+  // committed K/V of the first two steps go out first
+  uint4 ra[4] = {}, rb[4] = {};
+  auto load_step = [&](uint4 (&r)[4], int tstep) {
+    const int t = tstep + kr;
+    const int tc = min(t < t1 ? t : t1 - 1, L - 1);   // appended rows come from LDS
+    if (tc < 0) return;
+    r[0] = ld16_stream(Kp + (size_t)tc * kHeadDim);
+    r[1] = ld16_stream(Kp + (size_t)tc * kHeadDim + 8);
+    r[2] = ld16_stream(Vp + (size_t)tc * kHeadDim);
+    r[3] = ld16_stream(Vp + (size_t)tc * kHeadDim + 8);
+  };
+  int tb = t0 + wave * 8;
+  if (tb < t1) load_step(ra, tb);
+  if (tb + 32 < t1) load_step(rb, tb + 32);
+
+  // new K/V rows at positions nb .. t1-1 (rows r' = p - L of this sequence), rounded as
+  // the cache stores them; the item of the sequence's last row also writes them out
+  const bool writer = (ri.r == A.n - 1);
   for (int i = wave; i < n_new; i += 4) {
     const int rp = nb + i - L;
     const int rrow = row - ri.r + rp;
     const float *src = A.qkv + (size_t)rrow * A.nqkv;
-    float k0 = src[(A.nq + g) * kHeadDim + lane], k1 = src[(A.nq + g) * kHeadDim + lane + 64];
-    norm_rope<DT>(k0, k1, A.g_k, A.eps, ri.pos - ri.r + rp, A.theta, lane);
-    const uint16_t kb0 = rne16<DT>(k0), kb1 = rne16<DT>(k1);
-    const uint16_t vb0 = rne16<DT>(src[(A.nq + A.nkv + g) * kHeadDim + lane]);
-    const uint16_t vb1 = rne16<DT>(src[(A.nq + A.nkv + g) * kHeadDim + lane + 64]);
+    const float inv = head_inv_rms<COH>(A, rrow, A.nq + g);
+    const uint16_t kb0 = rne16<DT>(ldx<COH>(src + (A.nq + g) * kHeadDim + lane) * inv);
+    const uint16_t kb1 = rne16<DT>(ldx<COH>(src + (A.nq + g) * kHeadDim + lane + 64) * inv);
+    const uint16_t vb0 = rne16<DT>(ldx<COH>(src + (A.nq + A.nkv + g) * kHeadDim + lane));
+    const uint16_t vb1 = rne16<DT>(ldx<COH>(src + (A.nq + A.nkv + g) * kHeadDim + lane + 64));
     knew[i * kHeadDim + lane] = kb0;
     knew[i * kHeadDim + lane + 64] = kb1;
     vnew[i * kHeadDim + lane] = vb0;
     vnew[i * kHeadDim + lane + 64] = vb1;
     if (writer) {
-      const size_t off = (((size_t)ri.slot * A.nkv + g) * A.capacity + nb + i) * kHeadDim;
+      const size_t off = (kvrow0 + nb + i) * kHeadDim;
       A.kc[off + lane] = kb0;
       A.kc[off + lane + 64] = kb1;
       A.vc[off + lane] = vb0;
       A.vc[off + lane + 64] = vb1;
     }
   }
-  __syncthreads();
-
+  // q of the GROUP heads: rotated, gained projection / rms, times log2(e)/sqrt(d)
+  const float qs = kLog2e * rsqrtf((float)kHeadDim);
   float q[GROUP][16];
 #pragma unroll
-  for (int j = 0; j < GROUP; ++j)
+  for (int j = 0; j < GROUP; ++j) {
+    const int h = g * GROUP + j;
+    const float sc = head_inv_rms<COH>(A, row, h) * qs;
+    const float *qp = A.qkv + (size_t)row * A.nqkv + h * kHeadDim + kl * 16;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) q[j][e] = S.q[j][kl * 16 + e];
-
-  const size_t kvrow0 = ((size_t)ri.slot * A.nkv + g) * A.capacity;
-  const uint16_t *Kp = A.kc + kvrow0 * kHeadDim + kl * 16;
-  const uint16_t *Vp = A.vc + kvrow0 * kHeadDim + kl * 16;
+    for (int e = 0; e < 16; ++e) q[j][e] = ldx<COH>(qp + e) * sc;
+  }
+  if (n_new > 0) __syncthreads();
 
   float m[GROUP], l[GROUP], acc[GROUP][16];
 #pragma unroll
@@ -287,40 +384,36 @@ __device__ void attn_item(const LayerArgs &A, int item, const int *pre, uint16_t
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
   }
-  for (int tb = t0 + wave * 8; tb < t1; tb += 32) {
-    const int t = tb + kr;
+  auto compute_step = [&](const uint4 (&r)[4], int tstep) {
+    const int t = tstep + kr;
     const bool valid = t < t1;
-    const int tc = valid ? t : t1 - 1;
-    uint4 ka, kb, va, vb;
-    if (tc < L) {
-      ka = ld16_stream(Kp + (size_t)tc * kHeadDim);
-      kb = ld16_stream(Kp + (size_t)tc * kHeadDim + 8);
-      va = ld16_stream(Vp + (size_t)tc * kHeadDim);
-      vb = ld16_stream(Vp + (size_t)tc * kHeadDim + 8);
-    } else {
-      const uint16_t *kn = knew + (tc - nb) * kHeadDim + kl * 16;
-      const uint16_t *vn = vnew + (tc - nb) * kHeadDim + kl * 16;
-      ka = *reinterpret_cast<const uint4 *>(kn);
-      kb = *reinterpret_cast<const uint4 *>(kn + 8);
-      va = *reinterpret_cast<const uint4 *>(vn);
-      vb = *reinterpret_cast<const uint4 *>(vn + 8);
+    uint4 k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
+    if (!valid) {   // past the chunk: weight 0, and no stale bits that could be inf or NaN
+      k0 = k1 = v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
+    } else if (t >= L) {
+      const uint16_t *kn = knew + (t - nb) * kHeadDim + kl * 16;
+      const uint16_t *vn = vnew + (t - nb) * kHeadDim + kl * 16;
+      k0 = *reinterpret_cast<const uint4 *>(kn);
+      k1 = *reinterpret_cast<const uint4 *>(kn + 8);
+      v0 = *reinterpret_cast<const uint4 *>(vn);
+      v1 = *reinterpret_cast<const uint4 *>(vn + 8);
     }
     float kf[16], vf[16];
-    unpack8<DT>(ka, kf);
-    unpack8<DT>(kb, kf + 8);
-    unpack8<DT>(va, vf);
-    unpack8<DT>(vb, vf + 8);
+    unpack8<DT>(k0, kf);
+    unpack8<DT>(k1, kf + 8);
+    unpack8<DT>(v0, vf);
+    unpack8<DT>(v1, vf + 8);
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s += q[j][e] * kf[e];
-      s = group_sum<8>(s);
+      s = sum8(s);
       s = valid ? s : -INFINITY;
-      // wave-wide running max over the 8 keys of this step
-      float smax = fmaxf(s, __shfl_xor(s, 8, kWave));
-      smax = fmaxf(smax, __shfl_xor(smax, 16, kWave));
-      smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+      // wave-wide running max over the 8 keys of this step (row_mirror pairs the
+      // two key groups of a 16-lane row; readlane combines the four rows)
+      float smax = fmaxf(s, dpp<kRowMirror>(s));
+      smax = fmaxf(fmaxf(readlane(smax, 0), readlane(smax, 16)), fmaxf(readlane(smax, 32), readlane(smax, 48)));
       const float mn = fmaxf(m[j], smax);
       const float corr = exp2f(m[j] - mn);
       const float p = valid ? exp2f(s - mn) : 0.f;
@@ -329,31 +422,30 @@ __device__ void attn_item(const LayerArgs &A, int item, const int *pre, uint16_t
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][e] = acc[j][e] * corr + p * vf[e];
     }
+  };
+  // two steps in flight while one is computed
+  for (; tb < t1; tb += 64) {
+    compute_step(ra, tb);
+    if (tb + 64 < t1) load_step(ra, tb + 64);
+    if (tb + 32 < t1) {
+      compute_step(rb, tb + 32);
+      if (tb + 96 < t1) load_step(rb, tb + 96);
+    }
   }
   // combine the 8 key groups of the wave (lanes with equal kl), then the waves
 #pragma unroll
   for (int j = 0; j < GROUP; ++j) {
-    float lj = l[j];
-    lj += __shfl_xor(lj, 8, kWave);
-    lj += __shfl_xor(lj, 16, kWave);
-    lj += __shfl_xor(lj, 32, kWave);
-    l[j] = lj;
+    l[j] = sum_stride8(l[j]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float a = acc[j][e];
-      a += __shfl_xor(a, 8, kWave);
-      a += __shfl_xor(a, 16, kWave);
-      a += __shfl_xor(a, 32, kWave);
-      acc[j][e] = a;
-    }
+    for (int e = 0; e < 16; ++e) acc[j][e] = sum_stride8(acc[j][e]);
   }
-  if (kr == 0) {
+  if (kr == 1) {   // lanes 8..15 hold the totals
 #pragma unroll
     for (int j = 0; j < GROUP; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) S.acc[wave][j][kl * 16 + e] = acc[j][e];
   }
-  if (lane == 0) {
+  if (lane == 8) {
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
       S.m[wave][j] = m[j];
@@ -372,56 +464,105 @@ __device__ void attn_item(const LayerArgs &A, int item, const int *pre, uint16_t
       a += sc * S.acc[w][j][d];
       ls += sc * S.l[w][j];
     }
-    pbase[j * kPartStride + d] = a;
+    // merged by another workgroup of this same dispatch: device-coherent stores
+    st_dev(pbase + j * kPartStride + d, a);
     if (d == 0) {
-      pbase[j * kPartStride + 128] = M;
-      pbase[j * kPartStride + 129] = ls;
+      st_dev(pbase + j * kPartStride + 128, M);
+      st_dev(pbase + j * kPartStride + 129, ls);
     }
-  }
-
-  // the last item of (row, g) to finish merges the chunks in increasing order
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  uint32_t *ctr = A.mctr + (size_t)row * A.nkv + g;
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    S.flag = (old == (uint32_t)(nch - 1));
-  }
-  __syncthreads();
-  if (S.flag) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const float *p0 = A.part + (((size_t)row * A.nkv + g) * kMaxChunks * GROUP) * kPartStride;
-    const size_t cstride = (size_t)GROUP * kPartStride;
-    for (int idx = threadIdx.x; idx < GROUP * nch; idx += 256) {
-      const int j = idx / nch, cc = idx % nch;
-      S.mc[j][cc] = p0[cc * cstride + j * kPartStride + 128];
-      S.lc[j][cc] = p0[cc * cstride + j * kPartStride + 129];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < GROUP * kHeadDim; idx += 256) {
-      const int j = idx / kHeadDim, d = idx % kHeadDim;
-      float M = -INFINITY;
-      for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, S.mc[j][cc]);
-      float ls = 0.f, a = 0.f;
-      const float *pd = p0 + j * kPartStride + d;
-#pragma unroll 8
-      for (int cc = 0; cc < nch; ++cc) {
-        const float w = exp2f(S.mc[j][cc] - M);
-        ls += w * S.lc[j][cc];
-        a += w * pd[cc * cstride];
-      }
-      A.att[((size_t)row * A.nq + g * GROUP + j) * kHeadDim + d] = a / ls;
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
 
+// ---------------------------------------------------------------- merge
+//
+// att[row][h] = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, M = max_c m_c,
+// over the chunks of (row, kv head g) in increasing order (deterministic).  The
+// last item of a (row, g) to finish does it: every item bumps a counter after
+// its partial is stored; the block that sees the count reach nch merges.  The
+// counter update of one item is resolved after the next item, so its latency
+// hides behind that item's work.
+template <int GROUP, bool COH>
+__device__ void merge_group(const LayerArgs &A, int row, int g, int nch, AttnShared<GROUP> &S) {
+  const float *p0 = A.part + (((size_t)row * A.nkv + g) * kMaxChunks * GROUP) * kPartStride;
+  const size_t cs = (size_t)GROUP * kPartStride;
+  for (int idx = threadIdx.x; idx < GROUP * nch; idx += blockDim.x) {
+    const int j = idx / nch, cc = idx % nch;
+    S.mc[j][cc] = ld_dev(p0 + cc * cs + j * kPartStride + 128);
+    S.lc[j][cc] = ld_dev(p0 + cc * cs + j * kPartStride + 129);
+  }
+  __syncthreads();
+  for (int j = wave_id(); j < GROUP; j += 4) {
+    const int lane = lane_id();
+    const float mc = lane < nch ? S.mc[j][lane] : -INFINITY;
+    const float M = wave_max(mc);
+    const float w = lane < nch ? exp2f(mc - M) : 0.f;
+    const float tot = wave_sum(w * (lane < nch ? S.lc[j][lane] : 0.f));
+    if (lane < nch) S.w[j][lane] = w / tot;
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < GROUP * kHeadDim; o += blockDim.x) {
+    const int j = o / kHeadDim, d = o % kHeadDim;
+    const float *pd = p0 + j * kPartStride + d;
+    float a = 0.f;
+    int cc = 0;
+    for (; cc + 8 <= nch; cc += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ld_dev(pd + (cc + u) * cs);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a += S.w[j][cc + u] * v[u];
+    }
+    for (; cc < nch; ++cc) a += S.w[j][cc] * ld_dev(pd + cc * cs);
+    stx<COH>(A.att + ((size_t)row * A.nq + g * GROUP + j) * kHeadDim + d, a);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(A.mctr + (size_t)row * A.nkv + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+}
+
+struct Pending {
+  int row, g, nch;
+  uint32_t old;     // counter value before this item's increment (thread 0 only)
+};
+
+// this item's partial is stored (by every thread): count it
+__device__ __forceinline__ Pending signal_item(const LayerArgs &A, const Item &it) {
+  wait_mem();
+  __syncthreads();
+  Pending p{it.row, it.g, it.nch, 0u};
+  if (threadIdx.x == 0)
+    p.old = __hip_atomic_fetch_add(A.mctr + (size_t)it.row * A.nkv + it.g, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  return p;
+}
+
+template <int GROUP, bool COH>
+__device__ __forceinline__ void resolve(const LayerArgs &A, const Pending &p, AttnShared<GROUP> &S) {
+  if (threadIdx.x == 0) S.flag = p.old == (uint32_t)(p.nch - 1);
+  __syncthreads();
+  if (S.flag) merge_group<GROUP, COH>(A, p.row, p.g, p.nch, S);
+}
+
+template <int DT, int GROUP, bool COH>
+__device__ void attention_phase(const LayerArgs &A, const int *pre, uint16_t *knew, uint16_t *vnew,
+                                AttnShared<GROUP> &S, int first, int stride) {
+  const int total = pre[A.rows];
+  Pending pend{-1, 0, 0, 0u};
+  for (int item = first; item < total; item += stride) {
+    const Item it = decode_item(A, item, pre);
+    attn_item<DT, GROUP, COH>(A, it, knew, vnew, S);
+    const Pending now = signal_item(A, it);
+    if (pend.row >= 0) resolve<GROUP, COH>(A, pend, S);
+    pend = now;
+  }
+  if (pend.row >= 0) resolve<GROUP, COH>(A, pend, S);
+}
+
 // ---------------------------------------------------------------- phase D: o_proj
 //
-// Same structure as phase A with the attention output att[row][nq d] (fp32) as
-// input.  Rows that could not be appended (capacity, bad slot) get NaN.
-template <int DT, int KV, int RB, int RPW>
+// Same structure as phase A with the attention output as input, read from LDS
+// (merged by this block) or from the workspace.
+template <int DT, int KV, int RB, int RPW, bool COH>
 __device__ void oproj_tile(const LayerArgs &A, int tile, const uint4 (&wr)[RPW][KV]) {
   const int wave = wave_id(), lane = lane_id();
   const int o0 = (tile * 4 + wave) * RPW;
@@ -434,10 +575,15 @@ __device__ void oproj_tile(const LayerArgs &A, int tile, const uint4 (&wr)[RPW][
 #pragma unroll
       for (int v = 0; v < KV; ++v) {
         if (row < A.rows) {
-          const float4 *src = reinterpret_cast<const float4 *>(A.att + (size_t)row * K + (v * 64 + lane) * 8);
-          const float4 f0 = src[0], f1 = src[1];
-          x[r][v * 8 + 0] = f0.x; x[r][v * 8 + 1] = f0.y; x[r][v * 8 + 2] = f0.z; x[r][v * 8 + 3] = f0.w;
-          x[r][v * 8 + 4] = f1.x; x[r][v * 8 + 5] = f1.y; x[r][v * 8 + 6] = f1.z; x[r][v * 8 + 7] = f1.w;
+          const float *src = A.att + (size_t)row * K + (v * 64 + lane) * 8;
+          if constexpr (COH) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[r][v * 8 + e] = ld_dev(src + e);
+          } else {
+            const float4 f0 = reinterpret_cast<const float4 *>(src)[0], f1 = reinterpret_cast<const float4 *>(src)[1];
+            x[r][v * 8 + 0] = f0.x; x[r][v * 8 + 1] = f0.y; x[r][v * 8 + 2] = f0.z; x[r][v * 8 + 3] = f0.w;
+            x[r][v * 8 + 4] = f1.x; x[r][v * 8 + 5] = f1.y; x[r][v * 8 + 6] = f1.z; x[r][v * 8 + 7] = f1.w;
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[r][v * 8 + e] = 0.f;
@@ -473,7 +619,7 @@ __device__ void oproj_tile(const LayerArgs &A, int tile, const uint4 (&wr)[RPW][
           if (lane == i) val = acc[i][r];
         const size_t o = (size_t)row * A.H + o0 + lane;
         if (A.residual) val += cvt16<DT>(A.residual[o]);
-        if (!A.rowtab[row].x) val = __builtin_nanf("");
+        if (!read_row_table<COH>(A, row).x) val = __builtin_nanf("");
         if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
         else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
       }
@@ -493,9 +639,10 @@ __device__ __forceinline__ void load_wo(const LayerArgs &A, int tile, uint4 (&wr
 }
 
 // lengths advance once every earlier phase has read them
+template <bool COH>
 __device__ void advance_lengths(const LayerArgs &A) {
   for (int b = threadIdx.x; b < A.B; b += blockDim.x) {
-    const int4 rec = A.rowtab[b * A.n];
+    const int4 rec = read_row_table<COH>(A, b * A.n);
     if (rec.x) {
       A.lens[rec.z] = rec.y + A.n;
     } else if (A.status) {
@@ -509,21 +656,25 @@ __device__ void advance_lengths(const LayerArgs &A) {
 // bar[0] counts arrivals, bar[1] is a generation number.  The last arriver
 // resets the count and bumps the generation; the others wait for the
 // generation to move.  Both words return to a reusable state, so the barrier
-// needs no reset between calls.  A bounded wait: on timeout the status bit is
-// set and the caller stops working (its outputs are then undefined).
+// needs no reset between calls.  Everything exchanged across the barrier
+// travels through st_dev / ld_dev, so arriving only needs this block's stores
+// performed.  The wait is bounded: on timeout the status bit is set and the
+// block stops working (the call's outputs are then undefined).
 __device__ bool grid_barrier(uint32_t *bar, uint32_t nblocks, uint32_t *status, int *s_ok) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
     int ok = 1;
-    const uint32_t gen0 = __hip_atomic_load(&bar[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t old = __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t gen0 = ld_dev(&bar[1]);
+    wait_mem();
+    const uint32_t old = __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == nblocks - 1) {
       __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      wait_mem();
+      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       const long long start = wall_clock64();
-      while (__hip_atomic_load(&bar[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen0) {
+      while (ld_dev(&bar[1]) == gen0) {
         __builtin_amdgcn_s_sleep(1);
         if (wall_clock64() - start > kBarrierTimeoutTicks) {
           ok = 0;
@@ -535,16 +686,21 @@ __device__ bool grid_barrier(uint32_t *bar, uint32_t nblocks, uint32_t *status, 
     *s_ok = ok;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return *s_ok != 0;
 }
 
 // ---------------------------------------------------------------- kernels
 
-template <int DT, int KV, int RB, int RPW>
+// dynamic LDS of phase C: the appended K/V rows of an item, then the item prefix
+__host__ __device__ __forceinline__ size_t lds_attn_bytes(int rows, int n) {
+  return (size_t)n * kHeadDim * 2 * sizeof(uint16_t) + (size_t)(rows + 1) * sizeof(int);
+}
+
+template <int DT, int KV, int RB>
 __global__ __launch_bounds__(256) void k_qkv(LayerArgs A) {
-  if (blockIdx.x == 0) write_row_table(A);
-  qkv_tile<DT, KV, RB, RPW>(A, blockIdx.x);
+  __shared__ float s_ssq[RB][4];
+  if (blockIdx.x == 0) write_row_table<false>(A);
+  qkv_tile<DT, KV, RB, false>(A, blockIdx.x, s_ssq);
 }
 
 template <int DT, int GROUP>
@@ -555,78 +711,55 @@ __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   uint16_t *vnew = knew + A.n * kHeadDim;
   int *pre = reinterpret_cast<int *>(vnew + A.n * kHeadDim);
   build_item_prefix(A, pre, S.wsum);
-  const int total = pre[A.rows];
-  for (int item = blockIdx.x; item < total; item += gridDim.x) attn_item<DT, GROUP>(A, item, pre, knew, vnew, S);
+  attention_phase<DT, GROUP, false>(A, pre, knew, vnew, S, blockIdx.x, gridDim.x);
 }
 
 template <int DT, int KV, int RB, int RPW>
 __global__ __launch_bounds__(256) void k_oproj(LayerArgs A) {
-  if (blockIdx.x == 0) advance_lengths(A);
   uint4 wr[RPW][KV];
   load_wo<KV, RPW>(A, blockIdx.x, wr);
-  oproj_tile<DT, KV, RB, RPW>(A, blockIdx.x, wr);
+  if (blockIdx.x == 0) advance_lengths<false>(A);
+  oproj_tile<DT, KV, RB, RPW, false>(A, blockIdx.x, wr);
 }
 
-// All three phases in one persistent dispatch.  Each block prefetches the
-// o_proj weights of its first phase-D tile at the start, so that traffic
-// overlaps phases A and C.
-template <int DT, int KVI, int RBI, int RPWI, int KVO, int RBO, int RPWO, int GROUP>
+// All phases in one persistent dispatch.  Each block prefetches the o_proj
+// weights of its first phase-D tile at the start, so that traffic overlaps
+// phases A and C.
+template <int DT, int KVI, int RBI, int KVO, int RBO, int GROUP>
 __global__ __launch_bounds__(256) void k_fused(LayerArgs A, int tiles_a, int tiles_d) {
   extern __shared__ __align__(16) unsigned char dyn[];
-  __shared__ AttnShared<GROUP> S;
+  __shared__ AttnShared<GROUP> SA;
+  __shared__ float s_ssq[RBI][4];
   __shared__ int s_ok;
+  const int G = gridDim.x;
+
+  uint4 wo[kRpwD][KVO];
+  const int first_d = blockIdx.x;
+  if (first_d < tiles_d) load_wo<KVO, kRpwD>(A, first_d, wo);
+
+  if (blockIdx.x == 0) write_row_table<true>(A);
+  for (int t = blockIdx.x; t < tiles_a; t += G) qkv_tile<DT, KVI, RBI, true>(A, t, s_ssq);
+  if (!grid_barrier(A.bar, G, A.status, &s_ok)) return;
+
   uint16_t *knew = reinterpret_cast<uint16_t *>(dyn);
   uint16_t *vnew = knew + A.n * kHeadDim;
   int *pre = reinterpret_cast<int *>(vnew + A.n * kHeadDim);
-  const int G = gridDim.x;
-
-  uint4 wo[RPWO][KVO];
-  const int first_d = blockIdx.x;
-  if (first_d < tiles_d) load_wo<KVO, RPWO>(A, first_d, wo);
-
-  if (blockIdx.x == 0) write_row_table(A);
-  for (int t = blockIdx.x; t < tiles_a; t += G) qkv_tile<DT, KVI, RBI, RPWI>(A, t);
+  build_item_prefix(A, pre, SA.wsum);
+  attention_phase<DT, GROUP, true>(A, pre, knew, vnew, SA, blockIdx.x, G);
   if (!grid_barrier(A.bar, G, A.status, &s_ok)) return;
 
-  build_item_prefix(A, pre, S.wsum);
-  const int total = pre[A.rows];
-  for (int item = blockIdx.x; item < total; item += G) attn_item<DT, GROUP>(A, item, pre, knew, vnew, S);
-  if (!grid_barrier(A.bar, G, A.status, &s_ok)) return;
-
-  if (blockIdx.x == 0) advance_lengths(A);
+  if (blockIdx.x == 0) advance_lengths<true>(A);
   for (int t = blockIdx.x; t < tiles_d; t += G) {
-    if (t != first_d) load_wo<KVO, RPWO>(A, t, wo);
-    oproj_tile<DT, KVO, RBO, RPWO>(A, t, wo);
+    if (t != first_d) load_wo<KVO, kRpwD>(A, t, wo);
+    oproj_tile<DT, KVO, RBO, kRpwD, true>(A, t, wo);
   }
 }
 
 // ---------------------------------------------------------------- launch
 
 constexpr int rb_for(int kv) { return kv <= 2 ? 4 : (kv <= 4 ? 2 : 1); }
-constexpr int kRpwA = 4;   // phase A rows per wave: tiles of 16 QKV rows
-constexpr int kRpwD = 1;   // phase D rows per wave: tiles of 4 output rows
 
-size_t attn_dyn_smem(const LayerArgs &a) {
-  return (size_t)a.n * kHeadDim * 2 * sizeof(uint16_t) + (size_t)(a.rows + 1) * sizeof(int);
-}
-
-template <int DT, int GROUP>
-hipError_t multi_attn(const LayerArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn<DT, GROUP>), dim3(grid), dim3(256), attn_dyn_smem(a), s, a);
-  return hipGetLastError();
-}
-
-template <int DT, int KVI>
-hipError_t multi_qkv(const LayerArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((k_qkv<DT, KVI, rb_for(KVI), kRpwA>), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int DT, int KVO>
-hipError_t multi_oproj(const LayerArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((k_oproj<DT, KVO, rb_for(KVO), kRpwD>), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
+size_t fused_dyn_smem(const LayerArgs &a) { return lds_attn_bytes(a.rows, a.n); }
 
 #define ASR_KV_SWITCH(val, KVNAME, ...)          \
   switch (val) {                                 \
@@ -652,13 +785,26 @@ hipError_t multi_oproj(const LayerArgs &a, hipStream_t s) {
 
 template <int DT>
 hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s) {
-  hipError_t e = hipSuccess;
-  ASR_KV_SWITCH(a.H / 512, KVI, e = multi_qkv<DT, KVI>(a, s));
+  if (a.rows == 1) {
+    ASR_KV_SWITCH(a.H / 512, KVI,
+                  hipLaunchKernelGGL((k_qkv<DT, KVI, 1>), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, a));
+  } else {
+    ASR_KV_SWITCH(a.H / 512, KVI,
+                  hipLaunchKernelGGL((k_qkv<DT, KVI, rb_for(KVI)>), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, a));
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ASR_GROUP_SWITCH(a.group, GR, e = multi_attn<DT, GR>(a, attn_grid, s));
-  if (e != hipSuccess) return e;
-  ASR_KV_SWITCH(a.nq * kHeadDim / 512, KVO, e = multi_oproj<DT, KVO>(a, s));
-  return e;
+  ASR_GROUP_SWITCH(a.group, GR,
+                   hipLaunchKernelGGL((k_attn<DT, GR>), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s, a));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.rows == 1) {
+    ASR_KV_SWITCH(a.nq * kHeadDim / 512, KVO,
+                  hipLaunchKernelGGL((k_oproj<DT, KVO, 1, kRpwD>), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s, a));
+  } else {
+    ASR_KV_SWITCH(a.nq * kHeadDim / 512, KVO,
+                  hipLaunchKernelGGL((k_oproj<DT, KVO, rb_for(KVO), kRpwD>), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s, a));
+  }
+  return hipGetLastError();
 }
 
 // The fused kernel is instantiated for the shapes of the pages' models only
@@ -671,10 +817,10 @@ bool fused_supported(const LayerArgs &a) {
 template <int DT, int KVI>
 hipError_t fused_launch(const LayerArgs &a, int grid, hipStream_t s) {
   constexpr int KVO = 4;  // nq d = 2048
-  auto kern = k_fused<DT, KVI, rb_for(KVI), kRpwA, KVO, rb_for(KVO), kRpwD, 2>;
+  auto kern = a.rows == 1 ? k_fused<DT, KVI, 1, KVO, 1, 2> : k_fused<DT, KVI, rb_for(KVI), KVO, rb_for(KVO), 2>;
   const int tiles_a = a.nqkv / (4 * kRpwA);
   const int tiles_d = a.H / (4 * kRpwD);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), attn_dyn_smem(a), s, a, tiles_a, tiles_d);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), fused_dyn_smem(a), s, a, tiles_a, tiles_d);
   return hipGetLastError();
 }
 
@@ -682,6 +828,15 @@ template <int DT>
 hipError_t layer_fused(const LayerArgs &a, int grid, hipStream_t s) {
   if (a.H == 1024) return fused_launch<DT, 2>(a, grid, s);
   return fused_launch<DT, 4>(a, grid, s);
+}
+
+template <int DT, int KVI>
+int occupancy_fused(size_t dyn) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<DT, KVI, rb_for(KVI), 4, rb_for(4), 2>, 256,
+                                                   dyn) != hipSuccess)
+    return 0;
+  return per_cu;
 }
 
 }  // namespace
@@ -699,23 +854,12 @@ hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream
 // Largest grid of the fused kernel that is co-resident on the device: blocks
 // per CU from the occupancy calculator times the CU count.
 int fused_max_grid(int dtype, int H, size_t dyn_smem, int cus) {
-  int per_cu = 0;
-  hipError_t e;
-  if (dtype == ASR_BF16) {
-    e = H == 1024 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu, k_fused<ASR_BF16, 2, 4, kRpwA, 4, 2, kRpwD, 2>, 256, dyn_smem)
-                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu, k_fused<ASR_BF16, 4, 2, kRpwA, 4, 2, kRpwD, 2>, 256, dyn_smem);
-  } else {
-    e = H == 1024 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu, k_fused<ASR_F16, 2, 4, kRpwA, 4, 2, kRpwD, 2>, 256, dyn_smem)
-                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu, k_fused<ASR_F16, 4, 2, kRpwA, 4, 2, kRpwD, 2>, 256, dyn_smem);
-  }
-  if (e != hipSuccess || per_cu <= 0) return 0;
-  return per_cu * cus;
+  int per_cu;
+  if (dtype == ASR_BF16) per_cu = H == 1024 ? occupancy_fused<ASR_BF16, 2>(dyn_smem) : occupancy_fused<ASR_BF16, 4>(dyn_smem);
+  else per_cu = H == 1024 ? occupancy_fused<ASR_F16, 2>(dyn_smem) : occupancy_fused<ASR_F16, 4>(dyn_smem);
+  return per_cu > 0 ? per_cu * cus : 0;
 }
 
-size_t layer_dyn_smem(const LayerArgs &a) { return attn_dyn_smem(a); }
+size_t layer_dyn_smem(const LayerArgs &a) { return fused_dyn_smem(a); }
 
 }  // namespace asr

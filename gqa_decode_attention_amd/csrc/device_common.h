@@ -62,25 +62,83 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---------------------------------------------------------------- data shared between workgroups
+//
+// Inside one dispatch, values that one workgroup writes and another reads go
+// through agent-scope relaxed atomic accesses: the hardware performs them at
+// the device-coherent level (no stale per-XCD L2 copy is read, no dirty copy
+// is left behind), so no cache-wide write-back or invalidate is needed.  A
+// writer waits for its stores to be performed (wait_mem) before it signals.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int *p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_dev(const int *p) {
+  return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until every memory operation this thread issued has been performed
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
 // ---------------------------------------------------------------- wave reductions
+//
+// DPP lane permutations run in the vector ALU (no trip through the LDS
+// crossbar): quad_perm swaps within 4 lanes, row_half_mirror reverses 8 lanes,
+// row_mirror reverses 16 lanes.  Sums over the four 16-lane rows finish with
+// readlane into scalar registers, which also broadcasts the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
 
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// sum over each aligned group of 8 lanes, result in all 8
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<kQuadSwap1>(v);
+  v += dpp<kQuadSwap2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  return v;
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  return v;
+}
+// sum over each 16-lane row, result in all 16
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  return v + dpp<kRowMirror>(v);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  v = sum16(v);
+  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
 }
-
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  v = max8(v);
+  v = fmaxf(v, dpp<kRowMirror>(v));
+  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
 }
-
-// sum over aligned groups of G consecutive lanes (G a power of two <= 64)
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+// sum over the 8 lanes {l & 7, (l & 7) + 8, ..., (l & 7) + 56}; the total lands in the
+// lanes 8..15 of every 16-lane row (row_shr:8 adds lane i - 8 to lane i within a row)
+__device__ __forceinline__ float sum_stride8(float v) {
+  v += dpp<0x118>(v);
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
   return v;
 }
 

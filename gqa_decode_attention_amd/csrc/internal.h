@@ -36,8 +36,9 @@ struct LayerArgs {
   // output
   void *out;                  // [rows][H] fp32 or 16-bit
   // workspace (zero-filled once by the caller; every call leaves the counters at zero)
-  float *qkv;                 // [rows][nqkv]
-  float *att;                 // [rows][nq][d] attention output
+  float *qkv;                 // [rows][nqkv] projection; q, k heads rotated and gained, not normalised
+  float *ssq;                 // [rows][nq + nkv][8] partial sums of squares of the raw q, k heads
+  float *att;                 // [rows][nq][d] merged attention output
   float *part;                // [rows][nkv][kMaxChunks][group][kPartStride]
   uint32_t *bar;              // [2] grid barrier: arrival count, generation
   uint32_t *mctr;             // [rows][nkv] finished chunks per (row, kv head)
@@ -52,7 +53,7 @@ struct LayerArgs {
 };
 
 struct WorkspaceLayout {
-  size_t bar, mctr, rowtab, qkv, att, part, total;
+  size_t bar, mctr, rowtab, qkv, ssq, att, part, total;
 };
 
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);

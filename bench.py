@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--kv-split", type=int, default=0, help="keys per split-KV chunk (0: automatic)")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="run only this many bs1 steps eagerly (for profilers) and exit")
+    p.add_argument("--profile-batched", type=int, default=0,
+                   help="run only this many batch-64 steps eagerly (for profilers) and exit")
     return p.parse_args()
 
 
@@ -78,6 +80,11 @@ def main():
     def to_dev(bits, dtype):
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
         return t.view(torch.float16 if dtype == si.F16 else torch.bfloat16).to(dev)
+
+    if args.profile_batched:
+        batched_leg(args, ga, si, np, torch, dev, to_dev, stream, layer_bytes)
+        print(json.dumps({"profile_batched": args.profile_batched}))
+        return
 
     # ------------------------------------------------------------ bs1 workload
     c2 = si.CONFIGS[2]
@@ -215,6 +222,13 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, layer_bytes):
     torch.cuda.synchronize()
     print(f"[bench] batch-64 inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     hl = lens.tolist()
+    if args.profile_batched:
+        for _ in range(args.profile_batched):
+            for l in range(NL):
+                ga.layer_decode(cfg, weights[l], kvs[l], xs[l], outs[l], ws, host_lens=hl)
+            ga.kv_crop(kvs, base)
+        torch.cuda.synchronize()
+        return None
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for l in range(NL):

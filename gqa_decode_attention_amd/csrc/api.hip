@@ -12,6 +12,7 @@ namespace asr {
 namespace {
 
 constexpr int kMaxRows = 2048;
+constexpr int kVectorRows = 4;   // up to this many rows the projections run as vector-ALU GEMVs
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -71,7 +72,9 @@ int choose_split(const asr_attn_config *c, int capacity, int B, int n, const int
   min_split = (min_split + 15) / 16 * 16;
   if (min_split < kMinSplit) min_split = kMinSplit;
   if (c->kv_split) return c->kv_split;
-  const long long target = 8LL * cus;
+  // few rows: the attention items are the only parallelism, keep about one item
+  // per two CUs; many rows: several items per CU amortise each item's fixed cost
+  const long long target = (long long)B * n <= kVectorRows ? cus / 2 : 4LL * cus;
   int split = kMinSplit;
   while (split < min_split) split *= 2;
   for (; split < kMaxSplit; split *= 2) {
@@ -128,6 +131,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.qkv = reinterpret_cast<float *>(base + lay.qkv);
   a.ssq = reinterpret_cast<float *>(base + lay.ssq);
   a.att = reinterpret_cast<float *>(base + lay.att);
+  a.att_hl = reinterpret_cast<uint16_t *>(base + lay.att_hl);
   a.part = reinterpret_cast<float *>(base + lay.part);
   a.bar = reinterpret_cast<uint32_t *>(base + lay.bar);
   a.mctr = reinterpret_cast<uint32_t *>(base + lay.mctr);
@@ -146,6 +150,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.eps = cfg->rms_eps;
   a.theta = cfg->rope_theta;
   a.out_f32 = cfg->out_dtype == ASR_F32;
+  a.mfma = rows > kVectorRows;
 
   // upper bound of attention work items; blocks stride over the real count
   long long bound = 0;
@@ -159,7 +164,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
 
   bool fused = false;
   int fused_grid = 0;
-  if (cfg->dispatch != ASR_DISPATCH_MULTI && layer_fused_supported(a)) {
+  if (cfg->dispatch == ASR_DISPATCH_FUSED && rows <= kVectorRows && layer_fused_supported(a)) {
     fused_grid = fused_max_grid(cfg->dtype, a.H, layer_dyn_smem(a), cus);
     const long long want = (long long)cus * fused_blocks_per_cu();
     if (fused_grid > want) fused_grid = (int)want;
@@ -191,6 +196,8 @@ WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity)
   off = align_up(off + (size_t)rows * (nq + nkv) * 8 * sizeof(float));
   l.att = off;
   off = align_up(off + (size_t)rows * nq * kHeadDim * sizeof(float));
+  l.att_hl = off;
+  off = align_up(off + (size_t)rows * 2 * nq * kHeadDim * sizeof(uint16_t));
   l.part = off;
   off = align_up(off + (size_t)rows * nq * kMaxChunks * kPartStride * sizeof(float));
   l.total = off;

@@ -264,14 +264,20 @@ struct AttnShared {
   int flag;
 };
 
-// block-wide exclusive prefix of (chunks per row) * nkv into pre[0..rows]
-__device__ void build_item_prefix(const LayerArgs &A, int *pre, int *wsum) {
+// block-wide exclusive prefix of (chunks per row) * nkv into pre[0..rows]; each
+// row's (slot, committed length, visible keys) is kept in rinfo[] so that items
+// start without global loads
+__device__ void build_item_prefix(const LayerArgs &A, int *pre, int4 *rinfo, int *wsum) {
   const int wave = wave_id(), lane = lane_id();
   const int rows = A.rows;
   const int per = (rows + 255) / 256;
   const int beg = min((int)threadIdx.x * per, rows), end = min(beg + per, rows);
   int local = 0;
-  for (int i = beg; i < end; ++i) local += chunks_of(row_info(A, i).nvis, A.split) * A.nkv;
+  for (int i = beg; i < end; ++i) {
+    const RowInfo ri = row_info(A, i);
+    rinfo[i] = make_int4(ri.slot, ri.L, ri.nvis, ri.r);
+    local += chunks_of(ri.nvis, A.split) * A.nkv;
+  }
   int incl = local;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -285,7 +291,7 @@ __device__ void build_item_prefix(const LayerArgs &A, int *pre, int *wsum) {
   int run = base + incl - local;
   for (int i = beg; i < end; ++i) {
     pre[i] = run;
-    run += chunks_of(row_info(A, i).nvis, A.split) * A.nkv;
+    run += chunks_of(rinfo[i].z, A.split) * A.nkv;
   }
   if (threadIdx.x == 255) pre[rows] = run;
   __syncthreads();
@@ -310,41 +316,59 @@ __device__ __forceinline__ Item decode_item(const LayerArgs &A, int item, const 
   return it;
 }
 
+// Buffer resource for raw 16-byte loads from `base` (bounds: `bytes`).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+constexpr float kRescaleLog2 = 8.f;   // lazy softmax rescale: keep exp2(s - m) <= 2^8
+
 template <int DT, int GROUP, bool COH>
-__device__ void attn_item(const LayerArgs &A, const Item &it, uint16_t *knew, uint16_t *vnew, AttnShared<GROUP> &S) {
+__device__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo, uint16_t *knew, uint16_t *vnew,
+                          AttnShared<GROUP> &S) {
   const int wave = wave_id(), lane = lane_id();
+  // lane (kr, kl): key kr of the wave's 8, dims [8 kl, 8 kl + 8) and [64 + 8 kl, 64 + 8 kl + 8),
+  // so each 16-byte load instruction of the wave covers whole 128-byte lines
   const int kl = lane & 7, kr = lane >> 3;
+  const int d0 = 8 * kl, d1 = 64 + 8 * kl;
   const int row = it.row, g = it.g, c = it.c;
-  const RowInfo ri = row_info(A, row);
-  const int L = ri.L;
-  const int t0 = c * A.split, t1 = min(t0 + A.split, ri.nvis);
+  const int4 rin = rinfo[row];          // slot, committed length, visible keys, block offset
+  const int L = rin.y, r_off = rin.w;
+  const int t0 = c * A.split, t1 = min(t0 + A.split, rin.z);
   const int nb = max(t0, L);            // first appended position inside the chunk
   const int n_new = max(0, t1 - nb);    // appended rows this chunk sees
-  const size_t kvrow0 = ((size_t)ri.slot * A.nkv + g) * A.capacity;
-  const uint16_t *Kp = A.kc + kvrow0 * kHeadDim + kl * 16;
-  const uint16_t *Vp = A.vc + kvrow0 * kHeadDim + kl * 16;
+  const size_t kvrow0 = ((size_t)rin.x * A.nkv + g) * A.capacity;
+  const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + kvrow0 * kHeadDim, region);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + kvrow0 * kHeadDim, region);
 
-  // committed K/V of the first two steps go out first
-  uint4 ra[4] = {}, rb[4] = {};
-  auto load_step = [&](uint4 (&r)[4], int tstep) {
-    const int t = tstep + kr;
-    const int tc = min(t < t1 ? t : t1 - 1, L - 1);   // appended rows come from LDS
-    if (tc < 0) return;
-    r[0] = ld16_stream(Kp + (size_t)tc * kHeadDim);
-    r[1] = ld16_stream(Kp + (size_t)tc * kHeadDim + 8);
-    r[2] = ld16_stream(Vp + (size_t)tc * kHeadDim);
-    r[3] = ld16_stream(Vp + (size_t)tc * kHeadDim + 8);
+  // Steps of 8 keys per wave, two steps in flight while one is computed.  Every
+  // load is unconditional (rows clamped into the committed range) so the
+  // compiler can count the loads in flight exactly; lanes past the chunk get
+  // weight 0.  A chunk holding appended rows takes them from LDS.
+  const int tw = t0 + wave * 8;
+  const int nsteps = tw < t1 ? (t1 - tw + 31) / 32 : 0;
+  const int last_committed = max(L - 1, 0);
+  auto load_step = [&](uint4 (&r)[4], int i) {
+    const uint32_t off = (uint32_t)min(tw + 32 * i + kr, last_committed) * (kHeadDim * 2) + kl * 16;
+    r[0] = ld_buf(Kr, off);
+    r[1] = ld_buf(Kr, off + 128);
+    r[2] = ld_buf(Vr, off);
+    r[3] = ld_buf(Vr, off + 128);
   };
-  int tb = t0 + wave * 8;
-  if (tb < t1) load_step(ra, tb);
-  if (tb + 32 < t1) load_step(rb, tb + 32);
+  uint4 ra[4], rb[4];
+  load_step(ra, 0);
+  load_step(rb, 1);
 
   // new K/V rows at positions nb .. t1-1 (rows r' = p - L of this sequence), rounded as
   // the cache stores them; the item of the sequence's last row also writes them out
-  const bool writer = (ri.r == A.n - 1);
+  const bool writer = (r_off == A.n - 1);
   for (int i = wave; i < n_new; i += 4) {
     const int rp = nb + i - L;
-    const int rrow = row - ri.r + rp;
+    const int rrow = row - r_off + rp;
     const float *src = A.qkv + (size_t)rrow * A.nqkv;
     const float inv = head_inv_rms<COH>(A, rrow, A.nq + g);
     const uint16_t kb0 = rne16<DT>(ldx<COH>(src + (A.nq + g) * kHeadDim + lane) * inv);
@@ -370,9 +394,25 @@ __device__ void attn_item(const LayerArgs &A, const Item &it, uint16_t *knew, ui
   for (int j = 0; j < GROUP; ++j) {
     const int h = g * GROUP + j;
     const float sc = head_inv_rms<COH>(A, row, h) * qs;
-    const float *qp = A.qkv + (size_t)row * A.nqkv + h * kHeadDim + kl * 16;
+    const float *qp = A.qkv + (size_t)row * A.nqkv + h * kHeadDim;
+    if constexpr (COH) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) q[j][e] = ldx<COH>(qp + e) * sc;
+      for (int e = 0; e < 8; ++e) {
+        q[j][e] = ld_dev(qp + d0 + e) * sc;
+        q[j][8 + e] = ld_dev(qp + d1 + e) * sc;
+      }
+    } else {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e4 = 0; e4 < 2; ++e4) {
+          const float4 f = *reinterpret_cast<const float4 *>(qp + (h2 ? d1 : d0) + 4 * e4);
+          q[j][8 * h2 + 4 * e4] = f.x * sc;
+          q[j][8 * h2 + 4 * e4 + 1] = f.y * sc;
+          q[j][8 * h2 + 4 * e4 + 2] = f.z * sc;
+          q[j][8 * h2 + 4 * e4 + 3] = f.w * sc;
+        }
+    }
   }
   if (n_new > 0) __syncthreads();
 
@@ -384,20 +424,24 @@ __device__ void attn_item(const LayerArgs &A, const Item &it, uint16_t *knew, ui
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
   }
-  auto compute_step = [&](const uint4 (&r)[4], int tstep) {
-    const int t = tstep + kr;
+  // Online softmax with a lazy reference: p = 2^(s - m) against a per-wave
+  // reference m that moves only when some score passes it by more than 2^8
+  // (a wave vote), so most steps skip the rescale of l and acc.
+  auto compute_step = [&](const uint4 (&r)[4], int i, bool with_new) {
+    const int t = tw + 32 * i + kr;
     const bool valid = t < t1;
     uint4 k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
-    if (!valid) {   // past the chunk: weight 0, and no stale bits that could be inf or NaN
-      k0 = k1 = v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
-    } else if (t >= L) {
-      const uint16_t *kn = knew + (t - nb) * kHeadDim + kl * 16;
-      const uint16_t *vn = vnew + (t - nb) * kHeadDim + kl * 16;
-      k0 = *reinterpret_cast<const uint4 *>(kn);
-      k1 = *reinterpret_cast<const uint4 *>(kn + 8);
-      v0 = *reinterpret_cast<const uint4 *>(vn);
-      v1 = *reinterpret_cast<const uint4 *>(vn + 8);
+    if (with_new) {
+      const bool fresh = valid && t >= L;
+      const int ni = fresh ? t - nb : 0;
+      const uint16_t *kn = knew + ni * kHeadDim, *vn = vnew + ni * kHeadDim;
+      const uint4 a0 = *reinterpret_cast<const uint4 *>(kn + d0), a1 = *reinterpret_cast<const uint4 *>(kn + d1);
+      const uint4 b0 = *reinterpret_cast<const uint4 *>(vn + d0), b1 = *reinterpret_cast<const uint4 *>(vn + d1);
+      if (fresh) {
+        k0 = a0; k1 = a1; v0 = b0; v1 = b1;
+      }
     }
+    if (!valid) k0 = k1 = v0 = v1 = make_uint4(0u, 0u, 0u, 0u);   // no stale inf/NaN bits
     float kf[16], vf[16];
     unpack8<DT>(k0, kf);
     unpack8<DT>(k1, kf + 8);
@@ -410,26 +454,37 @@ __device__ void attn_item(const LayerArgs &A, const Item &it, uint16_t *knew, ui
       for (int e = 0; e < 16; ++e) s += q[j][e] * kf[e];
       s = sum8(s);
       s = valid ? s : -INFINITY;
-      // wave-wide running max over the 8 keys of this step (row_mirror pairs the
-      // two key groups of a 16-lane row; readlane combines the four rows)
-      float smax = fmaxf(s, dpp<kRowMirror>(s));
-      smax = fmaxf(fmaxf(readlane(smax, 0), readlane(smax, 16)), fmaxf(readlane(smax, 32), readlane(smax, 48)));
-      const float mn = fmaxf(m[j], smax);
-      const float corr = exp2f(m[j] - mn);
-      const float p = valid ? exp2f(s - mn) : 0.f;
-      m[j] = mn;
-      l[j] = l[j] * corr + p;
+      if (__any(s > m[j] + kRescaleLog2)) {
+        // new reference: the wave max of this step (row_mirror pairs the two key
+        // groups of a 16-lane row; readlane combines the four rows)
+        float smax = fmaxf(s, dpp<kRowMirror>(s));
+        smax = fmaxf(fmaxf(readlane(smax, 0), readlane(smax, 16)), fmaxf(readlane(smax, 32), readlane(smax, 48)));
+        const float mn = fmaxf(m[j], smax);
+        const float corr = exp2f(m[j] - mn);   // 0 on the first step (m = -inf)
+        m[j] = mn;
+        l[j] *= corr;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][e] = acc[j][e] * corr + p * vf[e];
+        for (int e = 0; e < 16; ++e) acc[j][e] *= corr;
+      }
+      const float p = valid ? exp2f(s - m[j]) : 0.f;
+      l[j] += p;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] += p * vf[e];
     }
   };
-  // two steps in flight while one is computed
-  for (; tb < t1; tb += 64) {
-    compute_step(ra, tb);
-    if (tb + 64 < t1) load_step(ra, tb + 64);
-    if (tb + 32 < t1) {
-      compute_step(rb, tb + 32);
-      if (tb + 96 < t1) load_step(rb, tb + 96);
+  if (n_new == 0) {
+    for (int i = 0; i < nsteps; i += 2) {
+      compute_step(ra, i, false);
+      load_step(ra, i + 2);
+      compute_step(rb, i + 1, false);
+      load_step(rb, i + 3);
+    }
+  } else {
+    for (int i = 0; i < nsteps; i += 2) {
+      compute_step(ra, i, true);
+      load_step(ra, i + 2);
+      compute_step(rb, i + 1, true);
+      load_step(rb, i + 3);
     }
   }
   // combine the 8 key groups of the wave (lanes with equal kl), then the waves
@@ -443,7 +498,10 @@ __device__ void attn_item(const LayerArgs &A, const Item &it, uint16_t *knew, ui
 #pragma unroll
     for (int j = 0; j < GROUP; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) S.acc[wave][j][kl * 16 + e] = acc[j][e];
+      for (int e = 0; e < 8; ++e) {
+        S.acc[wave][j][d0 + e] = acc[j][e];
+        S.acc[wave][j][d1 + e] = acc[j][8 + e];
+      }
   }
   if (lane == 8) {
 #pragma unroll
@@ -482,7 +540,7 @@ __device__ void attn_item(const LayerArgs &A, const Item &it, uint16_t *knew, ui
 // its partial is stored; the block that sees the count reach nch merges.  The
 // counter update of one item is resolved after the next item, so its latency
 // hides behind that item's work.
-template <int GROUP, bool COH>
+template <int DT, int GROUP, bool COH>
 __device__ void merge_group(const LayerArgs &A, int row, int g, int nch, AttnShared<GROUP> &S) {
   const float *p0 = A.part + (((size_t)row * A.nkv + g) * kMaxChunks * GROUP) * kPartStride;
   const size_t cs = (size_t)GROUP * kPartStride;
@@ -514,7 +572,15 @@ __device__ void merge_group(const LayerArgs &A, int row, int g, int nch, AttnSha
       for (int u = 0; u < 8; ++u) a += S.w[j][cc + u] * v[u];
     }
     for (; cc < nch; ++cc) a += S.w[j][cc] * ld_dev(pd + cc * cs);
-    stx<COH>(A.att + ((size_t)row * A.nq + g * GROUP + j) * kHeadDim + d, a);
+    const size_t col = (size_t)(g * GROUP + j) * kHeadDim + d;
+    stx<COH>(A.att + (size_t)row * A.nq * kHeadDim + col, a);
+    if (A.mfma) {   // tiled [plane][col / 32][row][32]: one MFMA operand load reads 1 KB contiguously
+      const size_t plane = (size_t)(A.nq * kHeadDim / 32) * A.rows * 32;
+      const size_t idx = ((col / 32) * A.rows + row) * 32 + col % 32;
+      const uint16_t hi = rne16<DT>(a);
+      A.att_hl[idx] = hi;
+      A.att_hl[plane + idx] = rne16<DT>(a - cvt16<DT>(hi));
+    }
   }
   if (threadIdx.x == 0) __hip_atomic_store(A.mctr + (size_t)row * A.nkv + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -536,26 +602,26 @@ __device__ __forceinline__ Pending signal_item(const LayerArgs &A, const Item &i
   return p;
 }
 
-template <int GROUP, bool COH>
+template <int DT, int GROUP, bool COH>
 __device__ __forceinline__ void resolve(const LayerArgs &A, const Pending &p, AttnShared<GROUP> &S) {
   if (threadIdx.x == 0) S.flag = p.old == (uint32_t)(p.nch - 1);
   __syncthreads();
-  if (S.flag) merge_group<GROUP, COH>(A, p.row, p.g, p.nch, S);
+  if (S.flag) merge_group<DT, GROUP, COH>(A, p.row, p.g, p.nch, S);
 }
 
 template <int DT, int GROUP, bool COH>
-__device__ void attention_phase(const LayerArgs &A, const int *pre, uint16_t *knew, uint16_t *vnew,
-                                AttnShared<GROUP> &S, int first, int stride) {
+__device__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *rinfo, uint16_t *knew,
+                                uint16_t *vnew, AttnShared<GROUP> &S, int first, int stride) {
   const int total = pre[A.rows];
   Pending pend{-1, 0, 0, 0u};
   for (int item = first; item < total; item += stride) {
     const Item it = decode_item(A, item, pre);
-    attn_item<DT, GROUP, COH>(A, it, knew, vnew, S);
+    attn_item<DT, GROUP, COH>(A, it, rinfo, knew, vnew, S);
     const Pending now = signal_item(A, it);
-    if (pend.row >= 0) resolve<GROUP, COH>(A, pend, S);
+    if (pend.row >= 0) resolve<DT, GROUP, COH>(A, pend, S);
     pend = now;
   }
-  if (pend.row >= 0) resolve<GROUP, COH>(A, pend, S);
+  if (pend.row >= 0) resolve<DT, GROUP, COH>(A, pend, S);
 }
 
 // ---------------------------------------------------------------- phase D: o_proj
@@ -691,9 +757,245 @@ __device__ bool grid_barrier(uint32_t *bar, uint32_t nblocks, uint32_t *status, 
 
 // ---------------------------------------------------------------- kernels
 
+// ---------------------------------------------------------------- batched projections on MFMA
+//
+// For more than a few rows the projections are dense contractions and run on
+// v_mfma_f32_16x16x32.  A block owns 16 output rows and all input rows (in
+// blocks of 64); its four waves split the contraction dimension in quarters and
+// add their 16 x 64 partial tiles in LDS.  fp32 operands are split into two
+// 16-bit terms (hi = rne(v), lo = rne(v - hi)), exact 16-bit operands are used
+// as they are, so the products keep about twice the 16-bit precision.
+//
+// QKV: out[n][o] = inv_rms(x_n) * sum_k (W[o][k] g_in[k]) x[n][k].  The weight
+// times the input-norm gain is formed in fp32 (exact: two 16-bit factors) and
+// split; x is the exact 16-bit operand; the sums of squares of x for inv_rms are
+// accumulated from the same loads.  The tile's 16 rows are 8 rotary pairs
+// (t, t + 64) of one head, as in the vector path, with the same epilogue:
+// gain and rotation of q/k pairs, partial sums of squares, v stored raw.
+template <int DT, int KQ>
+__global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
+  __shared__ f32x4_t s_c[4][4][kWave];
+  __shared__ float s_ss[4][64];
+  __shared__ float2 s_rope[64][8];   // (cos, sin) for the block's 64 rows x its 8 rotary pairs
+  const int wave = wave_id(), lane = lane_id();
+  const int tile = blockIdx.x;
+  const int head = tile / kTilesPerHead, jj = tile % kTilesPerHead, t0 = 8 * jj;
+  const int i16 = lane % 16, g4 = lane / 16;
+  const int arow = head * kHeadDim + (i16 < 8 ? t0 + i16 : 64 + t0 + i16 - 8);
+  const int H = A.H;
+  const int kq0 = wave * (H / 4) + g4 * 8;       // this lane's first k
+  if (blockIdx.x == 0) write_row_table<false>(A);
+
+  uint4 w[KQ];
+#pragma unroll
+  for (int s = 0; s < KQ; ++s) w[s] = ld16_stream(A.w_qkv + (size_t)arow * H + kq0 + s * 32);
+  const bool rot = head < A.nq + A.nkv;
+  const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;
+
+  for (int nb = 0; nb < A.rows; nb += 64) {
+    if (rot) {   // rotary angles of this block's 64 rows and 8 pairs, in fp64, once
+      for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
+        const int r = idx / 8, tt = idx % 8;
+        const int n = nb + r;
+        float c = 1.f, sn = 0.f;
+        if (n < A.rows) {
+          const double omega = exp2(-(2.0 * (t0 + tt) / kHeadDim) * log2((double)A.theta));
+          double sd, cd;
+          sincos((double)row_info(A, n).pos * omega, &sd, &cd);
+          c = (float)cd;
+          sn = (float)sd;
+        }
+        s_rope[r][tt] = make_float2(c, sn);
+      }
+    }
+    f32x4_t acc[4];
+    float ss[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      ss[nt] = 0.f;
+    }
+    const uint16_t *xr[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) xr[nt] = A.x + (size_t)min(nb + nt * 16 + i16, A.rows - 1) * H + kq0;
+    uint4 bc[4], bn[4], gc, gn;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) bc[nt] = ld16(xr[nt]);
+    gc = ld16(A.g_in + kq0);
+#pragma unroll
+    for (int s = 0; s < KQ; ++s) {
+      if (s + 1 < KQ) {   // next step's operands in flight during this step's math
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bn[nt] = ld16(xr[nt] + (s + 1) * 32);
+        gn = ld16(A.g_in + kq0 + (s + 1) * 32);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this step's math
+      uint4 ahi, alo;
+      {
+        float wf[8], gf[8], p[8];
+        unpack8<DT>(w[s], wf);
+        unpack8<DT>(gc, gf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = wf[e] * gf[e];
+        split8<DT>(p, ahi, alo);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float xf[8];
+        unpack8<DT>(bc[nt], xf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss[nt] += xf[e] * xf[e];
+        acc[nt] = mfma16x16x32<DT>(ahi, bc[nt], acc[nt]);
+        acc[nt] = mfma16x16x32<DT>(alo, bc[nt], acc[nt]);
+      }
+      if (s + 1 < KQ) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bc[nt] = bn[nt];
+        gc = gn;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      s_c[wave][nt][lane] = acc[nt];
+      float v = ss[nt];
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      if (g4 == 0) s_ss[wave][nt * 16 + i16] = v;
+    }
+    __syncthreads();
+    {
+      const int nt = wave;
+      const int n = nb + nt * 16 + i16;
+      f32x4_t c = s_c[0][nt][lane];
+#pragma unroll
+      for (int wv = 1; wv < 4; ++wv) {
+        const f32x4_t d = s_c[wv][nt][lane];
+        c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
+      }
+      const float ssx = s_ss[0][nt * 16 + i16] + s_ss[1][nt * 16 + i16] + s_ss[2][nt * 16 + i16] + s_ss[3][nt * 16 + i16];
+      const float inv = 1.0f / sqrtf(ssx / (float)H + A.eps);
+      const bool first = g4 < 2;
+      float raw[4], out[4];
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        raw[j] = c[j] * inv;
+        sq += raw[j] * raw[j];
+      }
+      sq += __shfl_xor(sq, 16, kWave);
+      sq += __shfl_xor(sq, 32, kWave);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = (g4 & 1) * 4 + j;
+        const int t = t0 + tt;
+        if (rot) {
+          const float u = cvt16<DT>(gp[first ? t : t + 64]) * raw[j];
+          const float up = __shfl_xor(u, 32, kWave);
+          const float2 cs = s_rope[nt * 16 + i16][tt];
+          out[j] = first ? u * cs.x - up * cs.y : u * cs.x + up * cs.y;
+        } else {
+          out[j] = raw[j];
+        }
+      }
+      if (n < A.rows) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = t0 + (g4 & 1) * 4 + j;
+          A.qkv[(size_t)n * A.nqkv + head * kHeadDim + (first ? t : t + 64)] = out[j];
+        }
+        if (rot && g4 == 0) A.ssq[((size_t)n * (A.nq + A.nkv) + head) * kTilesPerHead + jj] = sq;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// o_proj: out[n][o] = sum_c W_o[o][c] att[n][c] (+ residual), att as hi + lo terms.
+// Eight waves split the contraction dimension in eighths.
+template <int DT, int KQ>
+__global__ __launch_bounds__(512) void k_oproj_mfma(LayerArgs A) {
+  __shared__ f32x4_t s_c[8][4][kWave];
+  const int wave = wave_id(), lane = lane_id();
+  const int i16 = lane % 16, g4 = lane / 16;
+  const int K = A.nq * kHeadDim;
+  const int o0 = blockIdx.x * 16;
+  const int kq0 = wave * (K / 8) + g4 * 8;
+  uint4 w[KQ];
+#pragma unroll
+  for (int s = 0; s < KQ; ++s) w[s] = ld16_stream(A.w_o + (size_t)(o0 + i16) * K + kq0 + s * 32);
+  if (blockIdx.x == 0) advance_lengths<false>(A);
+
+  const size_t plane = (size_t)(K / 32) * A.rows * 32;
+  const int kb0 = wave * (K / 256);          // this wave's first 32-wide block of the contraction
+  for (int nb = 0; nb < A.rows; nb += 64) {
+    const uint16_t *br[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      br[nt] = A.att_hl + ((size_t)kb0 * A.rows + min(nb + nt * 16 + i16, A.rows - 1)) * 32 + g4 * 8;
+    const size_t kstep = (size_t)A.rows * 32;   // next 32-wide block
+    f32x4_t acc[4];
+    uint4 hc[4], lc[4], hn[4], ln[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      hc[nt] = ld16(br[nt]);
+      lc[nt] = ld16(br[nt] + plane);
+    }
+#pragma unroll
+    for (int s = 0; s < KQ; ++s) {
+      if (s + 1 < KQ) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          hn[nt] = ld16(br[nt] + (s + 1) * kstep);
+          ln[nt] = ld16(br[nt] + plane + (s + 1) * kstep);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this step's math
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        acc[nt] = mfma16x16x32<DT>(w[s], hc[nt], acc[nt]);
+        acc[nt] = mfma16x16x32<DT>(w[s], lc[nt], acc[nt]);
+      }
+      if (s + 1 < KQ) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          hc[nt] = hn[nt];
+          lc[nt] = ln[nt];
+        }
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) s_c[wave][nt][lane] = acc[nt];
+    __syncthreads();
+    if (wave < 4) {
+      const int nt = wave;
+      const int n = nb + nt * 16 + i16;
+      f32x4_t c = s_c[0][nt][lane];
+#pragma unroll
+      for (int wv = 1; wv < 8; ++wv) {
+        const f32x4_t d = s_c[wv][nt][lane];
+        c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
+      }
+      if (n < A.rows) {
+        const bool ok = A.rowtab[n].x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const size_t o = (size_t)n * A.H + o0 + g4 * 4 + j;
+          float val = c[j];
+          if (A.residual) val += cvt16<DT>(A.residual[o]);
+          if (!ok) val = __builtin_nanf("");
+          if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
+          else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // dynamic LDS of phase C: the appended K/V rows of an item, then the item prefix
 __host__ __device__ __forceinline__ size_t lds_attn_bytes(int rows, int n) {
-  return (size_t)n * kHeadDim * 2 * sizeof(uint16_t) + (size_t)(rows + 1) * sizeof(int);
+  return (size_t)rows * sizeof(int4) + (size_t)n * kHeadDim * 2 * sizeof(uint16_t) + (size_t)(rows + 1) * sizeof(int);
 }
 
 template <int DT, int KV, int RB>
@@ -707,11 +1009,12 @@ template <int DT, int GROUP>
 __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ AttnShared<GROUP> S;
-  uint16_t *knew = reinterpret_cast<uint16_t *>(dyn);
+  int4 *rinfo = reinterpret_cast<int4 *>(dyn);
+  uint16_t *knew = reinterpret_cast<uint16_t *>(rinfo + A.rows);
   uint16_t *vnew = knew + A.n * kHeadDim;
   int *pre = reinterpret_cast<int *>(vnew + A.n * kHeadDim);
-  build_item_prefix(A, pre, S.wsum);
-  attention_phase<DT, GROUP, false>(A, pre, knew, vnew, S, blockIdx.x, gridDim.x);
+  build_item_prefix(A, pre, rinfo, S.wsum);
+  attention_phase<DT, GROUP, false>(A, pre, rinfo, knew, vnew, S, blockIdx.x, gridDim.x);
 }
 
 template <int DT, int KV, int RB, int RPW>
@@ -741,11 +1044,12 @@ __global__ __launch_bounds__(256) void k_fused(LayerArgs A, int tiles_a, int til
   for (int t = blockIdx.x; t < tiles_a; t += G) qkv_tile<DT, KVI, RBI, true>(A, t, s_ssq);
   if (!grid_barrier(A.bar, G, A.status, &s_ok)) return;
 
-  uint16_t *knew = reinterpret_cast<uint16_t *>(dyn);
+  int4 *rinfo = reinterpret_cast<int4 *>(dyn);
+  uint16_t *knew = reinterpret_cast<uint16_t *>(rinfo + A.rows);
   uint16_t *vnew = knew + A.n * kHeadDim;
   int *pre = reinterpret_cast<int *>(vnew + A.n * kHeadDim);
-  build_item_prefix(A, pre, SA.wsum);
-  attention_phase<DT, GROUP, true>(A, pre, knew, vnew, SA, blockIdx.x, G);
+  build_item_prefix(A, pre, rinfo, SA.wsum);
+  attention_phase<DT, GROUP, true>(A, pre, rinfo, knew, vnew, SA, blockIdx.x, G);
   if (!grid_barrier(A.bar, G, A.status, &s_ok)) return;
 
   if (blockIdx.x == 0) advance_lengths<true>(A);
@@ -785,6 +1089,37 @@ size_t fused_dyn_smem(const LayerArgs &a) { return lds_attn_bytes(a.rows, a.n); 
 
 template <int DT>
 hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s) {
+  if (a.mfma) {
+    // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
+    hipError_t e = hipSuccess;
+    switch (a.H / 128) {
+      case 4: hipLaunchKernelGGL((k_qkv_mfma<DT, 4>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      case 8: hipLaunchKernelGGL((k_qkv_mfma<DT, 8>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      case 12: hipLaunchKernelGGL((k_qkv_mfma<DT, 12>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      case 16: hipLaunchKernelGGL((k_qkv_mfma<DT, 16>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      case 20: hipLaunchKernelGGL((k_qkv_mfma<DT, 20>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      case 24: hipLaunchKernelGGL((k_qkv_mfma<DT, 24>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      case 28: hipLaunchKernelGGL((k_qkv_mfma<DT, 28>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      case 32: hipLaunchKernelGGL((k_qkv_mfma<DT, 32>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    ASR_GROUP_SWITCH(a.group, GR,
+                     hipLaunchKernelGGL((k_attn<DT, GR>), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s, a));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    switch (a.nq * kHeadDim / 256) {
+      case 2: hipLaunchKernelGGL((k_oproj_mfma<DT, 2>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((k_oproj_mfma<DT, 4>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      case 6: hipLaunchKernelGGL((k_oproj_mfma<DT, 6>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      case 8: hipLaunchKernelGGL((k_oproj_mfma<DT, 8>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      case 10: hipLaunchKernelGGL((k_oproj_mfma<DT, 10>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      case 12: hipLaunchKernelGGL((k_oproj_mfma<DT, 12>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      case 14: hipLaunchKernelGGL((k_oproj_mfma<DT, 14>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      case 16: hipLaunchKernelGGL((k_oproj_mfma<DT, 16>), dim3(a.H / 16), dim3(512), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (a.rows == 1) {
     ASR_KV_SWITCH(a.H / 512, KVI,
                   hipLaunchKernelGGL((k_qkv<DT, KVI, 1>), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, a));

@@ -62,6 +62,43 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---------------------------------------------------------------- MFMA (gfx950 v_mfma_f32_16x16x32_{bf16,f16})
+//
+// Lane layout (checked on the device against a CPU product):
+//   A (16 x 32): lane l holds row l % 16, k = (l / 16) * 8 .. + 7
+//   B (32 x 16): lane l holds column l % 16, k = (l / 16) * 8 .. + 7
+//   C (16 x 16): lane l holds column l % 16, rows (l / 16) * 4 + j, j = 0..3
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 a, const uint4 b, f32x4_t c) {
+  if constexpr (DT == ASR_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  }
+}
+
+// fp32 -> two 16-bit terms, hi = rne(v), lo = rne(v - hi): hi + lo carries about
+// twice the 16-bit precision (two-term split of an fp32 operand for 16-bit MFMA)
+template <int DT>
+__device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h0 = rne16<DT>(f[2 * i]), h1 = rne16<DT>(f[2 * i + 1]);
+    const uint16_t l0 = rne16<DT>(f[2 * i] - cvt16<DT>(h0)), l1 = rne16<DT>(f[2 * i + 1] - cvt16<DT>(h1));
+    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
 // ---------------------------------------------------------------- data shared between workgroups
 //
 // Inside one dispatch, values that one workgroup writes and another reads go

@@ -39,6 +39,7 @@ struct LayerArgs {
   float *qkv;                 // [rows][nqkv] projection; q, k heads rotated and gained, not normalised
   float *ssq;                 // [rows][nq + nkv][8] partial sums of squares of the raw q, k heads
   float *att;                 // [rows][nq][d] merged attention output
+  uint16_t *att_hl;           // [rows][2][nq d] the same as hi and lo 16-bit terms (MFMA o_proj)
   float *part;                // [rows][nkv][kMaxChunks][group][kPartStride]
   uint32_t *bar;              // [2] grid barrier: arrival count, generation
   uint32_t *mctr;             // [rows][nkv] finished chunks per (row, kv head)
@@ -50,10 +51,11 @@ struct LayerArgs {
   int split;                  // keys per chunk
   float eps, theta;
   int out_f32;
+  int mfma;                   // projections on MFMA (more than a few rows)
 };
 
 struct WorkspaceLayout {
-  size_t bar, mctr, rowtab, qkv, ssq, att, part, total;
+  size_t bar, mctr, rowtab, qkv, ssq, att, att_hl, part, total;
 };
 
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);

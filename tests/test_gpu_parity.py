@@ -59,7 +59,7 @@ def test_cfg1_single_layer_decode(dispatch):
 
 @pytest.mark.parametrize("dtype", [si.F16, si.BF16])
 @pytest.mark.parametrize("split", [0, 16, 48, 1024])
-@pytest.mark.parametrize("dispatch", [1, 2])
+@pytest.mark.parametrize("dispatch", [0, 1])
 def test_ragged_decode_vs_oracle(dtype, split, dispatch):
     lens = [0, 1, 17, 100, 333, 64]
     cap = 400
@@ -163,21 +163,25 @@ def test_verify_vs_oracle(k, dtype):
         check_rounded_rows(kg[s, :, lens[s]:lens[s] + k], ref.k[s, :, lens[s]:lens[s] + k], dtype)
 
 
-@pytest.mark.parametrize("k", [4, 8])
+@pytest.mark.parametrize("k", [2, 4, 8])
 def test_verify_rows_equal_sequential_decode_rows(k):
-    """With the same chunking, a verify block and k single-token steps give identical bits."""
+    """Verify rows agree with k single-token steps: bit for bit when both calls take the
+    same projection path (up to 4 rows: vector ALU) and chunking, else to rounding."""
     dtype = si.F16
-    lens = [795, 40]
+    lens = [795]
     L = SeededLayer(3, 2, 1024, dtype)
     kb, vb = fill_cache(3, 2, lens, 832, dtype)
-    xb = _x(3, 2, 0, (2, k, 1024), dtype)
+    xb = _x(3, 2, 0, (1, k, 1024), dtype)
     cfg = ga.config(dtype=dtype, kv_split=32)
     kv1 = device_cache(kb, vb, lens, dtype)
     ov = _run_verify(L, cfg, kv1, xb, dtype)
     kv2 = device_cache(kb, vb, lens, dtype)
     od = np.stack([_run_decode(L, cfg, kv2, xb[:, r, :], dtype) for r in range(k)], axis=1)
-    assert np.array_equal(ov, od)
-    assert np.array_equal(to_bits(kv1.k), to_bits(kv2.k)) and np.array_equal(to_bits(kv1.v), to_bits(kv2.v))
+    if k <= 4:
+        assert np.array_equal(ov, od)
+        assert np.array_equal(to_bits(kv1.k), to_bits(kv2.k)) and np.array_equal(to_bits(kv1.v), to_bits(kv2.v))
+    else:
+        assert rel_err(ov, od) < 1e-5
     # the automatic chunking may differ between the two; then they agree to rounding
     kv3 = device_cache(kb, vb, lens, dtype)
     ov3 = _run_verify(L, ga.config(dtype=dtype), kv3, xb, dtype)
@@ -186,8 +190,9 @@ def test_verify_rows_equal_sequential_decode_rows(k):
 
 @pytest.mark.parametrize("a", [0, 1, 5, 8])
 def test_crop_after_rejection_equals_never_appended(a):
-    """Verify k = 8, crop to the accepted prefix, poison the dropped rows with NaN: the next
-    decode is bit-identical to a cache that only ever received the accepted rows."""
+    """Verify k = 8, crop to the accepted prefix a, poison the dropped rows with NaN: the
+    next decode is bit-identical to a cache that only ever received the accepted rows
+    (copied bit for bit from the verify call) and no rejected one."""
     dtype, k = si.F16, 8
     lens = [795]
     L = SeededLayer(3, 3, 1024, dtype)
@@ -198,11 +203,13 @@ def test_crop_after_rejection_equals_never_appended(a):
     spec = device_cache(kb, vb, lens, dtype)
     _run_verify(L, cfg, spec, xs, dtype)
     ga.kv_crop([spec], torch.tensor([795 + a], dtype=torch.int32, device="cuda"))
+    accepted_k = spec.k[0, :, 795:795 + a].clone()
+    accepted_v = spec.v[0, :, 795:795 + a].clone()
     spec.k[0, :, 795 + a:] = float("nan")
     spec.v[0, :, 795 + a:] = float("nan")
-    ref = device_cache(kb, vb, lens, dtype)
-    if a:
-        _run_verify(L, cfg, ref, xs[:, :a, :], dtype)
+    ref = device_cache(kb, vb, [795 + a], dtype)
+    ref.k[0, :, 795:795 + a] = accepted_k
+    ref.v[0, :, 795:795 + a] = accepted_v
     o_spec = _run_decode(L, cfg, spec, xn, dtype)
     o_ref = _run_decode(L, cfg, ref, xn, dtype)
     assert np.all(np.isfinite(o_spec))
@@ -281,7 +288,7 @@ def test_fused_and_stream_ordered_dispatch_agree_bitwise(case):
     """The fused single-dispatch kernel and the three stream-ordered kernels run the same
     per-item arithmetic: identical output bits, cache bits and lengths."""
     dtype = si.F16 if case != "decode_ragged" else si.BF16
-    lens = {"decode_bs1": [795], "decode_ragged": [3, 700, 128, 1200, 0], "verify": [795, 33]}[case]
+    lens = {"decode_bs1": [795], "decode_ragged": [3, 700, 1200, 0], "verify": [795]}[case]
     cap = 1280
     L = SeededLayer(5, 1, 1024, dtype)
     kb, vb = fill_cache(5, 1, lens, cap, dtype)
@@ -290,7 +297,7 @@ def test_fused_and_stream_ordered_dispatch_agree_bitwise(case):
         kv = device_cache(kb, vb, lens, dtype)
         cfg = ga.config(dtype=dtype, dispatch=mode)
         if case == "verify":
-            out = _run_verify(L, cfg, kv, _x(5, 1, 0, (len(lens), 8, 1024), dtype), dtype)
+            out = _run_verify(L, cfg, kv, _x(5, 1, 0, (len(lens), 4, 1024), dtype), dtype)
         else:
             out = _run_decode(L, cfg, kv, _x(5, 1, 0, (len(lens), 1024), dtype), dtype)
         res[mode] = (out, to_bits(kv.k), to_bits(kv.v), kv.lens.cpu().numpy(), kv.status.item())
@@ -301,7 +308,16 @@ def test_fused_and_stream_ordered_dispatch_agree_bitwise(case):
 
 
 def test_fused_dispatch_rejects_shapes_without_an_instance():
+    """The fused dispatch exists for the pages' shapes and up to 4 rows only."""
     dtype = si.F16
+    L2 = SeededLayer(5, 2, 1024, dtype)
+    kb2, vb2 = fill_cache(5, 2, [10] * 5, 32, dtype)
+    kv2 = device_cache(kb2, vb2, [10] * 5, dtype)
+    cfg2 = ga.config(dispatch=ga.DISPATCH_FUSED)
+    with pytest.raises(ga.AsrError) as e:
+        ga.layer_decode(cfg2, L2.dev, kv2, to_dev(_x(5, 2, 0, (5, 1024), dtype), dtype),
+                        torch.empty((5, 1024), dtype=torch.float32, device="cuda"), ga.alloc_workspace(cfg2, 5, 32))
+    assert e.value.code == -2
     L = SeededLayer(9, 44, 512, dtype, nq=4, nkv=4)
     kb, vb = fill_cache(9, 4, [3], 16, dtype, nkv=4)
     kv = device_cache(kb, vb, [3], dtype)
@@ -311,3 +327,27 @@ def test_fused_dispatch_rejects_shapes_without_an_instance():
         ga.layer_decode(cfg, L.dev, kv, to_dev(_x(9, 4, 0, (1, 512), dtype), dtype), out,
                         ga.alloc_workspace(cfg, 1, 16))
     assert e.value.code == -2
+
+
+@pytest.mark.parametrize("dtype", [si.F16, si.BF16])
+@pytest.mark.parametrize("rows", [5, 16, 64, 65, 130])
+def test_matrix_core_projections_vs_oracle(dtype, rows):
+    """More than 4 rows run the projections on MFMA (two-term split of fp32 operands),
+    including ragged row counts that leave partial 16-row and 64-row blocks."""
+    lens = [int(v) for v in np.random.default_rng(rows).integers(0, 300, rows)]
+    H = 2048 if rows == 65 else 1024
+    L = SeededLayer(6, rows, H, dtype)
+    kb, vb = fill_cache(6, rows, lens, 320, dtype)
+    kv = device_cache(kb, vb, lens, dtype)
+    pick = sorted({0, rows - 1, rows // 2, 3})
+    ref = oracle_cache(kb, vb, lens, dtype, seqs=pick)
+    xb = _x(6, rows, 0, (rows, H), dtype)
+    res = si.residual(6, rows, 0, rows, H, dtype)
+    got = _run_decode(L, ga.config(hidden=H, dtype=dtype), kv, xb, dtype, residual=res)
+    want = oracle.decode(L.ocfg, L.ref, ref, xb[pick], residual_bits=res[pick])
+    err = rel_err(got[pick], want)
+    print(f"mfma rows={rows} H={H} {dtype}: {err:.3e}")
+    assert err < TOL[dtype]
+    kg = to_bits(kv.k)
+    for i, sq in enumerate(pick):
+        check_rounded_rows(kg[sq, :, lens[sq]], ref.k[i, :, lens[sq]], dtype)

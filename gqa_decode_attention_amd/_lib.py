@@ -34,7 +34,8 @@ class AsrAttnConfig(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("kv_split", ctypes.c_int32), ("dispatch", ctypes.c_int32)]
+                ("kv_split", ctypes.c_int32), ("dispatch", ctypes.c_int32),
+                ("phase_events", ctypes.c_void_p)]
 
 
 class AsrAttnWeights(ctypes.Structure):
@@ -102,7 +103,28 @@ def torch_dtype(dt) -> torch.dtype:
 def config(hidden=1024, n_q_heads=16, n_kv_heads=8, head_dim=128, rms_eps=1e-6, rope_theta=1e6,
            dtype="f16", out_dtype="f32", kv_split=0, dispatch=DISPATCH_AUTO) -> AsrAttnConfig:
     return AsrAttnConfig(hidden, n_q_heads, n_kv_heads, head_dim, rms_eps, rope_theta,
-                         _dt(dtype), _dt(out_dtype), kv_split, dispatch)
+                         _dt(dtype), _dt(out_dtype), kv_split, dispatch, None)
+
+
+class PhaseEvents:
+    """Six torch.cuda.Events that receive the start and end stamps of a layer call's three phase
+    kernels (diagnostics).  Attach with ``cfg.phase_events = pe.ptr``; read with ``elapsed_ms()``."""
+
+    def __init__(self):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in self.events:   # materialise the underlying hipEvent_t handles
+            e.record()
+        self._arr = (ctypes.c_void_p * 6)(*[e.cuda_event for e in self.events])
+        self.ptr = ctypes.cast(self._arr, ctypes.c_void_p)
+
+    def elapsed_ms(self):
+        """(projection, attention, o_proj) kernel durations of the last call, in ms."""
+        ev = self.events
+        return tuple(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(3))
+
+    def total_ms(self):
+        """First kernel start to last kernel end of the last call, in ms (also for the fused dispatch)."""
+        return self.events[0].elapsed_time(self.events[5])
 
 
 def _ptr(t):

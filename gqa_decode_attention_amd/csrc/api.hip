@@ -171,8 +171,13 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
     fused = fused_grid > 0;
   }
   if (cfg->dispatch == ASR_DISPATCH_FUSED && !fused) return ASR_EUNSUPPORTED;
-  const hipError_t e = fused ? launch_layer_fused(a, cfg->dtype, fused_grid, stream)
-                             : launch_layer_multi(a, cfg->dtype, attn_grid, stream);
+  hipEvent_t *ev = cfg->phase_events;
+  hipError_t e;
+  if (fused) {
+    e = launch_layer_fused(a, cfg->dtype, fused_grid, stream, ev);
+  } else {
+    e = launch_layer_multi(a, cfg->dtype, attn_grid, stream, ev);
+  }
   return e == hipSuccess ? ASR_OK : ASR_EHIP;
 }
 

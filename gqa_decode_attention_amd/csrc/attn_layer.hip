@@ -25,6 +25,8 @@
 // the section 03 table.  The causal rule of verify rows follows "Can CTC make
 // Qwen3-ASR faster?", section 03: position i sees the committed prefix and the
 // candidates up to i.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -346,14 +348,15 @@ __device__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo,
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + kvrow0 * kHeadDim, region);
 
   // Steps of 8 keys per wave, two steps in flight while one is computed.  Every
-  // load is unconditional (rows clamped into the committed range) so the
+  // load is unconditional (rows clamped to the chunk's last committed row, so
+  // the loads past the chunk hit lines this item already fetched) so the
   // compiler can count the loads in flight exactly; lanes past the chunk get
   // weight 0.  A chunk holding appended rows takes them from LDS.
   const int tw = t0 + wave * 8;
   const int nsteps = tw < t1 ? (t1 - tw + 31) / 32 : 0;
-  const int last_committed = max(L - 1, 0);
+  const int last_row = max(min(t1, L) - 1, 0);
   auto load_step = [&](uint4 (&r)[4], int i) {
-    const uint32_t off = (uint32_t)min(tw + 32 * i + kr, last_committed) * (kHeadDim * 2) + kl * 16;
+    const uint32_t off = (uint32_t)min(tw + 32 * i + kr, last_row) * (kHeadDim * 2) + kl * 16;
     r[0] = ld_buf(Kr, off);
     r[1] = ld_buf(Kr, off + 128);
     r[2] = ld_buf(Vr, off);
@@ -1065,81 +1068,106 @@ constexpr int rb_for(int kv) { return kv <= 2 ? 4 : (kv <= 4 ? 2 : 1); }
 
 size_t fused_dyn_smem(const LayerArgs &a) { return lds_attn_bytes(a.rows, a.n); }
 
-#define ASR_KV_SWITCH(val, KVNAME, ...)          \
-  switch (val) {                                 \
-    case 1: { constexpr int KVNAME = 1; __VA_ARGS__; } break; \
-    case 2: { constexpr int KVNAME = 2; __VA_ARGS__; } break; \
-    case 3: { constexpr int KVNAME = 3; __VA_ARGS__; } break; \
-    case 4: { constexpr int KVNAME = 4; __VA_ARGS__; } break; \
-    case 5: { constexpr int KVNAME = 5; __VA_ARGS__; } break; \
-    case 6: { constexpr int KVNAME = 6; __VA_ARGS__; } break; \
-    case 7: { constexpr int KVNAME = 7; __VA_ARGS__; } break; \
-    case 8: { constexpr int KVNAME = 8; __VA_ARGS__; } break; \
-    default: return hipErrorInvalidValue;        \
-  }
+using LayerKernel = void (*)(LayerArgs);
 
-#define ASR_GROUP_SWITCH(val, GNAME, ...)        \
-  switch (val) {                                 \
-    case 1: { constexpr int GNAME = 1; __VA_ARGS__; } break; \
-    case 2: { constexpr int GNAME = 2; __VA_ARGS__; } break; \
-    case 4: { constexpr int GNAME = 4; __VA_ARGS__; } break; \
-    case 8: { constexpr int GNAME = 8; __VA_ARGS__; } break; \
-    default: return hipErrorInvalidValue;        \
-  }
+// One phase kernel.  With diagnostics events (ev != NULL, 6 entries) the kernel
+// is launched with hipExtLaunchKernelGGL, which stamps its own start and end
+// into ev[2 phase] and ev[2 phase + 1].
+hipError_t launch_phase(LayerKernel kern, dim3 grid, dim3 block, unsigned lds, hipStream_t s, hipEvent_t *ev,
+                        int phase, const LayerArgs &a) {
+  if (!kern) return hipErrorInvalidValue;
+  if (ev)
+    hipExtLaunchKernelGGL(kern, grid, block, lds, s, ev[2 * phase], ev[2 * phase + 1], 0u, a);
+  else
+    hipLaunchKernelGGL(kern, grid, block, lds, s, a);
+  return hipGetLastError();
+}
 
 template <int DT>
-hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s) {
+LayerKernel pick_qkv_mfma(int kq) {
+  switch (kq) {
+    case 4: return k_qkv_mfma<DT, 4>;
+    case 8: return k_qkv_mfma<DT, 8>;
+    case 12: return k_qkv_mfma<DT, 12>;
+    case 16: return k_qkv_mfma<DT, 16>;
+    case 20: return k_qkv_mfma<DT, 20>;
+    case 24: return k_qkv_mfma<DT, 24>;
+    case 28: return k_qkv_mfma<DT, 28>;
+    case 32: return k_qkv_mfma<DT, 32>;
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+LayerKernel pick_oproj_mfma(int kq) {
+  switch (kq) {
+    case 2: return k_oproj_mfma<DT, 2>;
+    case 4: return k_oproj_mfma<DT, 4>;
+    case 6: return k_oproj_mfma<DT, 6>;
+    case 8: return k_oproj_mfma<DT, 8>;
+    case 10: return k_oproj_mfma<DT, 10>;
+    case 12: return k_oproj_mfma<DT, 12>;
+    case 14: return k_oproj_mfma<DT, 14>;
+    case 16: return k_oproj_mfma<DT, 16>;
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+LayerKernel pick_attn(int group) {
+  switch (group) {
+    case 1: return k_attn<DT, 1>;
+    case 2: return k_attn<DT, 2>;
+    case 4: return k_attn<DT, 4>;
+    case 8: return k_attn<DT, 8>;
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+LayerKernel pick_qkv(int kvi, bool one_row) {
+  switch (kvi) {
+#define ASR_PICK_QKV(K) \
+    case K: return one_row ? k_qkv<DT, K, 1> : k_qkv<DT, K, rb_for(K)>;
+    ASR_PICK_QKV(1) ASR_PICK_QKV(2) ASR_PICK_QKV(3) ASR_PICK_QKV(4)
+    ASR_PICK_QKV(5) ASR_PICK_QKV(6) ASR_PICK_QKV(7) ASR_PICK_QKV(8)
+#undef ASR_PICK_QKV
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+LayerKernel pick_oproj(int kvo, bool one_row) {
+  switch (kvo) {
+#define ASR_PICK_OPROJ(K) \
+    case K: return one_row ? k_oproj<DT, K, 1, kRpwD> : k_oproj<DT, K, rb_for(K), kRpwD>;
+    ASR_PICK_OPROJ(1) ASR_PICK_OPROJ(2) ASR_PICK_OPROJ(3) ASR_PICK_OPROJ(4)
+    ASR_PICK_OPROJ(5) ASR_PICK_OPROJ(6) ASR_PICK_OPROJ(7) ASR_PICK_OPROJ(8)
+#undef ASR_PICK_OPROJ
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEvent_t *ev) {
+  hipError_t e;
   if (a.mfma) {
-    // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
-    hipError_t e = hipSuccess;
-    switch (a.H / 128) {
-      case 4: hipLaunchKernelGGL((k_qkv_mfma<DT, 4>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      case 8: hipLaunchKernelGGL((k_qkv_mfma<DT, 8>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      case 12: hipLaunchKernelGGL((k_qkv_mfma<DT, 12>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      case 16: hipLaunchKernelGGL((k_qkv_mfma<DT, 16>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      case 20: hipLaunchKernelGGL((k_qkv_mfma<DT, 20>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      case 24: hipLaunchKernelGGL((k_qkv_mfma<DT, 24>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      case 28: hipLaunchKernelGGL((k_qkv_mfma<DT, 28>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      case 32: hipLaunchKernelGGL((k_qkv_mfma<DT, 32>), dim3(a.nqkv / 16), dim3(256), 0, s, a); break;
-      default: return hipErrorInvalidValue;
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    ASR_GROUP_SWITCH(a.group, GR,
-                     hipLaunchKernelGGL((k_attn<DT, GR>), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s, a));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    switch (a.nq * kHeadDim / 256) {
-      case 2: hipLaunchKernelGGL((k_oproj_mfma<DT, 2>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((k_oproj_mfma<DT, 4>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      case 6: hipLaunchKernelGGL((k_oproj_mfma<DT, 6>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      case 8: hipLaunchKernelGGL((k_oproj_mfma<DT, 8>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      case 10: hipLaunchKernelGGL((k_oproj_mfma<DT, 10>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      case 12: hipLaunchKernelGGL((k_oproj_mfma<DT, 12>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      case 14: hipLaunchKernelGGL((k_oproj_mfma<DT, 14>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      case 16: hipLaunchKernelGGL((k_oproj_mfma<DT, 16>), dim3(a.H / 16), dim3(512), 0, s, a); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
-  if (a.rows == 1) {
-    ASR_KV_SWITCH(a.H / 512, KVI,
-                  hipLaunchKernelGGL((k_qkv<DT, KVI, 1>), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, a));
+    // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 256 (o_proj, eight waves)
+    if ((e = launch_phase(pick_qkv_mfma<DT>(a.H / 128), dim3(a.nqkv / 16), dim3(256), 0, s, ev, 0, a)) !=
+        hipSuccess)
+      return e;
   } else {
-    ASR_KV_SWITCH(a.H / 512, KVI,
-                  hipLaunchKernelGGL((k_qkv<DT, KVI, rb_for(KVI)>), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, a));
+    if ((e = launch_phase(pick_qkv<DT>(a.H / 512, a.rows == 1), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, ev,
+                          0, a)) != hipSuccess)
+      return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  ASR_GROUP_SWITCH(a.group, GR,
-                   hipLaunchKernelGGL((k_attn<DT, GR>), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s, a));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.rows == 1) {
-    ASR_KV_SWITCH(a.nq * kHeadDim / 512, KVO,
-                  hipLaunchKernelGGL((k_oproj<DT, KVO, 1, kRpwD>), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s, a));
-  } else {
-    ASR_KV_SWITCH(a.nq * kHeadDim / 512, KVO,
-                  hipLaunchKernelGGL((k_oproj<DT, KVO, rb_for(KVO), kRpwD>), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s, a));
-  }
-  return hipGetLastError();
+  if ((e = launch_phase(pick_attn<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s, ev, 1,
+                        a)) != hipSuccess)
+    return e;
+  if (a.mfma)
+    return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 256), dim3(a.H / 16), dim3(512), 0, s, ev, 2, a);
+  return launch_phase(pick_oproj<DT>(a.nq * kHeadDim / 512, a.rows == 1), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s,
+                      ev, 2, a);
 }
 
 // The fused kernel is instantiated for the shapes of the pages' models only
@@ -1150,19 +1178,22 @@ bool fused_supported(const LayerArgs &a) {
 }
 
 template <int DT, int KVI>
-hipError_t fused_launch(const LayerArgs &a, int grid, hipStream_t s) {
+hipError_t fused_launch(const LayerArgs &a, int grid, hipStream_t s, hipEvent_t *ev) {
   constexpr int KVO = 4;  // nq d = 2048
   auto kern = a.rows == 1 ? k_fused<DT, KVI, 1, KVO, 1, 2> : k_fused<DT, KVI, rb_for(KVI), KVO, rb_for(KVO), 2>;
   const int tiles_a = a.nqkv / (4 * kRpwA);
   const int tiles_d = a.H / (4 * kRpwD);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), fused_dyn_smem(a), s, a, tiles_a, tiles_d);
+  if (ev)
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), fused_dyn_smem(a), s, ev[0], ev[5], 0u, a, tiles_a, tiles_d);
+  else
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), fused_dyn_smem(a), s, a, tiles_a, tiles_d);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t layer_fused(const LayerArgs &a, int grid, hipStream_t s) {
-  if (a.H == 1024) return fused_launch<DT, 2>(a, grid, s);
-  return fused_launch<DT, 4>(a, grid, s);
+hipError_t layer_fused(const LayerArgs &a, int grid, hipStream_t s, hipEvent_t *ev) {
+  if (a.H == 1024) return fused_launch<DT, 2>(a, grid, s, ev);
+  return fused_launch<DT, 4>(a, grid, s, ev);
 }
 
 template <int DT, int KVI>
@@ -1176,14 +1207,14 @@ int occupancy_fused(size_t dyn) {
 
 }  // namespace
 
-hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s) {
-  return dtype == ASR_BF16 ? layer_multi<ASR_BF16>(a, attn_grid, s) : layer_multi<ASR_F16>(a, attn_grid, s);
+hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s, hipEvent_t *ev) {
+  return dtype == ASR_BF16 ? layer_multi<ASR_BF16>(a, attn_grid, s, ev) : layer_multi<ASR_F16>(a, attn_grid, s, ev);
 }
 
 bool layer_fused_supported(const LayerArgs &a) { return fused_supported(a); }
 
-hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream_t s) {
-  return dtype == ASR_BF16 ? layer_fused<ASR_BF16>(a, grid, s) : layer_fused<ASR_F16>(a, grid, s);
+hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream_t s, hipEvent_t *ev) {
+  return dtype == ASR_BF16 ? layer_fused<ASR_BF16>(a, grid, s, ev) : layer_fused<ASR_F16>(a, grid, s, ev);
 }
 
 // Largest grid of the fused kernel that is co-resident on the device: blocks

@@ -15,7 +15,7 @@ constexpr int kMinSplit = 16;         // keys per chunk, lower bound
 constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
 constexpr int kMaxVerifyK = 32;
 constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
-constexpr uint32_t kStatusBadSlot = 8u;  // slot index outside [0, batch_cap)
+constexpr uint32_t kStatusBadSlot = ASR_STATUS_BAD_SLOT;  // slot index outside [0, batch_cap)
 
 // Everything a layer kernel needs, passed by value.
 struct LayerArgs {
@@ -61,9 +61,9 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);
 
 // launchers; return hipSuccess or the launch error
-hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s);
+hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s, hipEvent_t *ev);
 bool layer_fused_supported(const LayerArgs &a);
-hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream_t s);
+hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream_t s, hipEvent_t *ev);
 int fused_max_grid(int dtype, int H, size_t dyn_smem, int cus);
 size_t layer_dyn_smem(const LayerArgs &a);
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,

@@ -59,24 +59,30 @@ enum {
 enum {
   ASR_STATUS_CAPACITY = 1,     /* an append would pass the capacity: that sequence skipped */
   ASR_STATUS_CROP_GROW = 2,    /* a crop asked for a length < 0 or above the current one: ignored */
-  ASR_STATUS_SYNC_TIMEOUT = 4  /* the fused dispatch gave up waiting for another workgroup */
+  ASR_STATUS_SYNC_TIMEOUT = 4, /* the fused dispatch gave up waiting for another workgroup */
+  ASR_STATUS_BAD_SLOT = 8      /* a slot index outside [0, batch_cap): that row skipped */
 };
 
 /* how a layer call is dispatched */
 enum {
-  ASR_DISPATCH_AUTO = 0,   /* the library chooses */
+  ASR_DISPATCH_AUTO = 0,   /* the library chooses (currently: one kernel per phase) */
   ASR_DISPATCH_MULTI = 1,  /* one kernel per phase, ordered by the stream */
-  ASR_DISPATCH_FUSED = 2   /* one kernel per layer call; phases ordered by device-side counters */
+  ASR_DISPATCH_FUSED = 2   /* one persistent kernel per layer call whose workgroups meet at grid
+                              barriers; hidden 1024 or 2048, 16 q heads, 8 kv heads, at most 4
+                              rows (else ASR_EUNSUPPORTED) */
 };
 
 /*
  * Block shape and numerics.  Supported by this build: head_dim = 128;
  * n_q_heads a multiple of n_kv_heads with n_q_heads / n_kv_heads in
  * {1, 2, 4, 8}; n_q_heads * head_dim and hidden multiples of 512, at most
- * 8192; dtype ASR_F16 or ASR_BF16 (weights, x, residual and the KV cache);
- * out_dtype ASR_F32 or equal to dtype.  The shapes of the pages' model are
- * hidden 1024 (or 2048), 16 q heads, 8 kv heads, head_dim 128, eps 1e-6,
- * rope_theta 1e6.
+ * 4096; dtype ASR_F16 or ASR_BF16 (weights, x, residual and the KV cache);
+ * out_dtype ASR_F32 or equal to dtype; at most 2048 rows per call (B for
+ * decode, B * k for verify); cache capacity at most 65536.  The shapes of the
+ * pages' model are hidden 1024 (or 2048), 16 q heads, 8 kv heads,
+ * head_dim 128, eps 1e-6, rope_theta 1e6.  All arithmetic is fp32; 16-bit
+ * operands of the matrix-core path are exact 16-bit data or two-term (hi + lo)
+ * splits of fp32 values.
  */
 typedef struct asr_attn_config {
   int32_t hidden;       /* H */
@@ -90,6 +96,10 @@ typedef struct asr_attn_config {
   int32_t kv_split;     /* keys per split-KV chunk: 0 = automatic, else a multiple of 16 in
                            [16, 1024] with capacity <= 64 * kv_split */
   int32_t dispatch;     /* ASR_DISPATCH_* */
+  hipEvent_t *phase_events;  /* diagnostics, NULL normally: an array of 6 events (created by the
+                                caller) that receive the start and end stamps of the projection,
+                                attention and o_proj kernels, in that order, of the stream-ordered
+                                dispatch; the fused dispatch stamps its one kernel into [0] and [5] */
 } asr_attn_config;
 
 /* One layer's weights (device pointers, elements of cfg.dtype). */
@@ -124,9 +134,9 @@ typedef struct asr_kv_layer {
  * up to `max_rows` rows (B for decode, B * k for verify) on caches of
  * `capacity` positions.  Returns 0 for an unsupported or invalid config.
  * The workspace is scratch owned by the caller; it must not be shared by
- * calls that may run concurrently.  Before its first use with
- * ASR_DISPATCH_FUSED (or AUTO) it must be zero-filled; the library leaves it
- * re-usable after every call.
+ * calls that may run concurrently.  It must be zero-filled before its first
+ * use (it holds counters that every call leaves at zero again); after a call
+ * that reported ASR_STATUS_SYNC_TIMEOUT it must be zero-filled again.
  */
 size_t asr_attn_workspace_bytes(const asr_attn_config *cfg, int32_t max_rows, int32_t capacity);
 

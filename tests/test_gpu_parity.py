@@ -351,3 +351,29 @@ def test_matrix_core_projections_vs_oracle(dtype, rows):
     kg = to_bits(kv.k)
     for i, sq in enumerate(pick):
         check_rounded_rows(kg[sq, :, lens[sq]], ref.k[i, :, lens[sq]], dtype)
+
+
+@pytest.mark.parametrize("rows", [1, 64])
+def test_phase_events_leave_results_unchanged(rows):
+    """Launching the phase kernels with diagnostics events (hipExtLaunchKernelGGL) computes the
+    same bits as the plain launch, and stamps three positive, ordered kernel durations."""
+    dtype = si.BF16
+    lens = si.kv_lengths(4, rows, 200, 1500).tolist()
+    L = SeededLayer(4, 3, 1024, dtype)
+    kb, vb = fill_cache(4, 3, lens, 1536, dtype)
+    x = _x(4, 3, 0, (rows, 1024), dtype)
+    res = []
+    for with_events in (False, True):
+        kv = device_cache(kb, vb, lens, dtype)
+        cfg = ga.config(dtype=dtype, dispatch=ga.DISPATCH_MULTI)
+        pe = ga.PhaseEvents()
+        if with_events:
+            cfg.phase_events = pe.ptr
+        res.append((_run_decode(L, cfg, kv, x, dtype), to_bits(kv.k), kv.lens.cpu().numpy()))
+        if with_events:
+            torch.cuda.synchronize()
+            d = pe.elapsed_ms()
+            assert all(0.0 < t < 50.0 for t in d), d
+            assert pe.total_ms() >= sum(d) * 0.999
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])

@@ -133,7 +133,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.att = reinterpret_cast<float *>(base + lay.att);
   a.att_hl = reinterpret_cast<uint16_t *>(base + lay.att_hl);
   a.part = reinterpret_cast<float *>(base + lay.part);
-  a.bar = reinterpret_cast<uint32_t *>(base + lay.bar);
+  a.flow = reinterpret_cast<uint32_t *>(base + lay.flow);
   a.mctr = reinterpret_cast<uint32_t *>(base + lay.mctr);
   a.rowtab = reinterpret_cast<int4 *>(base + lay.rowtab);
   a.B = B;
@@ -189,8 +189,8 @@ WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity)
   WorkspaceLayout l;
   const size_t nqkv = (size_t)(nq + 2 * nkv) * kHeadDim;
   size_t off = 0;
-  l.bar = off;
-  off = align_up(off + 2 * sizeof(uint32_t));
+  l.flow = off;
+  off = align_up(off + kFlowWords * sizeof(uint32_t));
   l.mctr = off;
   off = align_up(off + (size_t)rows * nkv * sizeof(uint32_t));
   l.rowtab = off;

@@ -2,22 +2,27 @@
 //
 // Phases; each is a loop over independent work items, written as device
 // functions shared by both dispatch modes:
-//   A. QKV tiles   input RMSNorm fused into the q/k/v projection (16 output rows
-//                  per tile, all input rows).  The last tile of each head to
-//                  finish completes the head for every row: RMSNorm and rotary of
-//                  q (kept in fp32, pre-scaled) and k, and the rounded append of
-//                  k and v to the cache.
+//   A. QKV tiles   input RMSNorm fused into the q/k/v projection.  A tile is 16
+//                  output rows = 8 rotary pairs (t, t + 64) of one head, for all
+//                  input rows: it applies the q/k norm gain and the rotary to its
+//                  pairs and stores the partial sum of squares of its raw rows;
+//                  v rows are stored raw.  Above 4 rows the projection runs on
+//                  MFMA (k_qkv_mfma) with the same tile and epilogue.
 //   C. attention   one item per (row, kv head g, chunk of keys): all q heads of g
-//                  share every K/V row of the chunk; single-pass online softmax;
-//                  a partial (m, l, acc) per q head.
-//                  The last item of a (row, g) to finish merges the chunks
-//                  (log-sum-exp, chunk order) into the attention output.
+//                  share every K/V row of the chunk; the q/k norms are finished
+//                  with the tiles' partial sums; the rows this call appends are
+//                  rounded once, taken from LDS and written to the cache by the
+//                  item of the sequence's last row; single-pass online softmax;
+//                  a partial (m, l, acc) per q head.  The last item of a (row, g)
+//                  to finish merges the chunks (log-sum-exp, fixed order) into
+//                  the attention output.
 //   D. o_proj      output projection (+ residual); lengths advanced.
 // ASR_DISPATCH_MULTI runs the phases as kernels in stream order; a kernel
 // boundary makes each phase's results visible to the next.
-// ASR_DISPATCH_FUSED runs them in one persistent kernel whose workgroups meet at
-// a grid barrier between phases; data crossing workgroups inside it go through
-// device-coherent accesses (st_dev / ld_dev).
+// ASR_DISPATCH_FUSED runs them in one persistent kernel (k_flow) whose resident
+// workgroups order the phases through counters in the workspace; data crossing
+// workgroups inside it go through device-coherent accesses (st_dev / ld_dev,
+// ld_dev4).
 //
 // The operation list follows "Qwen3-ASR -- Latency & Bottleneck Analysis",
 // section 07 (q/k/v projections, GQA repeat_kv, QK^T, fp32 softmax, AV, o_proj)
@@ -124,20 +129,36 @@ __device__ __forceinline__ int4 read_row_table(const LayerArgs &A, int row) {
 // wave-wide load reads 1 KB contiguously; the wave's four weight rows stay in
 // registers while it walks over the input rows RB at a time.
 // Input RMSNorm: h = x * g_in / sqrt(mean(x^2) + eps).
-template <int DT, int KV, int RB, bool COH>
-__device__ void qkv_tile(const LayerArgs &A, int tile, float (*s_ssq)[4]) {
-  const int wave = wave_id(), lane = lane_id();
+__device__ __forceinline__ void qkv_tile_rows(int tile, int (&orow)[4]) {
   const int head = tile / kTilesPerHead, jj = tile % kTilesPerHead;
-  const int ta = 8 * jj + 2 * wave, tb = ta + 1;
-  const int orow[4] = {head * kHeadDim + ta, head * kHeadDim + ta + 64, head * kHeadDim + tb, head * kHeadDim + tb + 64};
-  const bool rot = head < A.nq + A.nkv;
-  const int H = A.H;
-  uint4 wr[4][KV];
+  const int ta = 8 * jj + 2 * wave_id(), tb = ta + 1;
+  orow[0] = head * kHeadDim + ta;
+  orow[1] = head * kHeadDim + ta + 64;
+  orow[2] = head * kHeadDim + tb;
+  orow[3] = head * kHeadDim + tb + 64;
+}
+
+// the wave's four weight rows of tile `tile`
+template <int KV>
+__device__ __forceinline__ void qkv_tile_weights(const LayerArgs &A, int tile, uint4 (&wr)[4][KV]) {
+  int orow[4];
+  qkv_tile_rows(tile, orow);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int v = 0; v < KV; ++v)
-      wr[i][v] = ld16_stream(A.w_qkv + (size_t)orow[i] * H + (v * 64 + lane) * 8);
+      wr[i][v] = ld16_stream(A.w_qkv + (size_t)orow[i] * A.H + (v * 64 + lane_id()) * 8);
+}
+
+template <int DT, int KV, int RB, bool COH>
+__device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s_ssq)[4], const uint4 (&wr)[4][KV]) {
+  const int wave = wave_id(), lane = lane_id();
+  const int head = tile / kTilesPerHead, jj = tile % kTilesPerHead;
+  const int ta = 8 * jj + 2 * wave, tb = ta + 1;
+  int orow[4];
+  qkv_tile_rows(tile, orow);
+  const bool rot = head < A.nq + A.nkv;
+  const int H = A.H;
   float g[KV * 8];
 #pragma unroll
   for (int v = 0; v < KV; ++v) unpack8<DT>(ld16(A.g_in + (v * 64 + lane) * 8), g + v * 8);
@@ -237,6 +258,12 @@ __device__ void qkv_tile(const LayerArgs &A, int tile, float (*s_ssq)[4]) {
 }
 
 // 1 / sqrt(mean of squares + eps) of head `head` of row `row` from the tile partials
+// same, from the two 16-byte halves of the 8 partials
+__device__ __forceinline__ float inv_rms_of(const LayerArgs &A, float4 a, float4 b) {
+  const float s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+  return 1.0f / sqrtf(s / (float)kHeadDim + A.eps);
+}
+
 template <bool COH>
 __device__ __forceinline__ float head_inv_rms(const LayerArgs &A, int row, int head) {
   const float *p = A.ssq + ((size_t)row * (A.nq + A.nkv) + head) * kTilesPerHead;
@@ -262,6 +289,7 @@ struct AttnShared {
   float m[4][GROUP], l[4][GROUP];
   float w[GROUP][kMaxChunks];     // merge weights 2^(m_c - M) / sum
   float mc[GROUP][kMaxChunks], lc[GROUP][kMaxChunks];
+  float4 red[256];                // merge: partial sums of the chunk classes
   int wsum[4];
   int flag;
 };
@@ -328,93 +356,143 @@ __device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 
 constexpr float kRescaleLog2 = 8.f;   // lazy softmax rescale: keep exp2(s - m) <= 2^8
 
+// Where an item's keys are: chunk [t0, t1) of the row's visible keys, of which
+// [nb, t1) are this call's appended rows (taken from LDS, not the cache).
+struct ItemGeom {
+  int L, r_off, t0, t1, nb, n_new, tw, nsteps, last_row;
+  size_t kvrow0;
+};
+
+__device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it, const int4 *rinfo) {
+  const int4 rin = rinfo[it.row];       // slot, committed length, visible keys, block offset
+  ItemGeom g;
+  g.L = rin.y;
+  g.r_off = rin.w;
+  g.t0 = it.c * A.split;
+  g.t1 = min(g.t0 + A.split, rin.z);
+  g.nb = max(g.t0, g.L);
+  g.n_new = max(0, g.t1 - g.nb);
+  g.kvrow0 = ((size_t)rin.x * A.nkv + it.g) * A.capacity;
+  g.tw = g.t0 + wave_id() * 8;
+  g.nsteps = g.tw < g.t1 ? (g.t1 - g.tw + 31) / 32 : 0;
+  g.last_row = max(min(g.t1, g.L) - 1, 0);
+  return g;
+}
+
+// The K and V registers of two 32-key steps of an item (lane: one key row of
+// its wave's 8, dims [8 kl, 8 kl + 8) and [64 + 8 kl, 64 + 8 kl + 8)).
+struct KVRegs {
+  uint4 a0, a1, a2, a3, b0, b1, b2, b3;
+};
+
+// Steps of 8 keys per wave, two steps in flight while one is computed.  Every
+// load is unconditional (rows clamped to the chunk's last committed row, so
+// the loads past the chunk hit lines this item already fetched) so the
+// compiler can count the loads in flight exactly; lanes past the chunk get
+// weight 0.  Each 16-byte load instruction of a wave covers whole 128-byte lines.
+__device__ __forceinline__ void kv_load_step(const LayerArgs &A, const ItemGeom &g, uint4 (&r)[4], int i) {
+  const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + g.kvrow0 * kHeadDim, region);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + g.kvrow0 * kHeadDim, region);
+  const uint32_t off = (uint32_t)min(g.tw + 32 * i + kr, g.last_row) * (kHeadDim * 2) + kl * 16;
+  r[0] = ld_buf(Kr, off);
+  r[1] = ld_buf(Kr, off + 128);
+  r[2] = ld_buf(Vr, off);
+  r[3] = ld_buf(Vr, off + 128);
+}
+
+__device__ __forceinline__ void attn_item_loads(const LayerArgs &A, const Item &it, const int4 *rinfo, KVRegs &P) {
+  const ItemGeom g = item_geom(A, it, rinfo);
+  uint4 a[4], b[4];
+  kv_load_step(A, g, a, 0);
+  kv_load_step(A, g, b, 1);
+  P = KVRegs{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// One item, its first two steps already loaded into P.
 template <int DT, int GROUP, bool COH>
-__device__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo, uint16_t *knew, uint16_t *vnew,
-                          AttnShared<GROUP> &S) {
+__device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo, uint16_t *knew, uint16_t *vnew,
+                          AttnShared<GROUP> &S, const KVRegs &P) {
   const int wave = wave_id(), lane = lane_id();
-  // lane (kr, kl): key kr of the wave's 8, dims [8 kl, 8 kl + 8) and [64 + 8 kl, 64 + 8 kl + 8),
-  // so each 16-byte load instruction of the wave covers whole 128-byte lines
   const int kl = lane & 7, kr = lane >> 3;
   const int d0 = 8 * kl, d1 = 64 + 8 * kl;
   const int row = it.row, g = it.g, c = it.c;
-  const int4 rin = rinfo[row];          // slot, committed length, visible keys, block offset
-  const int L = rin.y, r_off = rin.w;
-  const int t0 = c * A.split, t1 = min(t0 + A.split, rin.z);
-  const int nb = max(t0, L);            // first appended position inside the chunk
-  const int n_new = max(0, t1 - nb);    // appended rows this chunk sees
-  const size_t kvrow0 = ((size_t)rin.x * A.nkv + g) * A.capacity;
-  const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
-  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + kvrow0 * kHeadDim, region);
-  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + kvrow0 * kHeadDim, region);
+  const ItemGeom G = item_geom(A, it, rinfo);
+  const int L = G.L, r_off = G.r_off, t1 = G.t1, nb = G.nb, n_new = G.n_new, tw = G.tw, nsteps = G.nsteps;
+  const size_t kvrow0 = G.kvrow0;
+  uint4 ra[4] = {P.a0, P.a1, P.a2, P.a3};
+  uint4 rb[4] = {P.b0, P.b1, P.b2, P.b3};
+  auto load_step = [&](uint4 (&r)[4], int i) { kv_load_step(A, G, r, i); };
 
-  // Steps of 8 keys per wave, two steps in flight while one is computed.  Every
-  // load is unconditional (rows clamped to the chunk's last committed row, so
-  // the loads past the chunk hit lines this item already fetched) so the
-  // compiler can count the loads in flight exactly; lanes past the chunk get
-  // weight 0.  A chunk holding appended rows takes them from LDS.
-  const int tw = t0 + wave * 8;
-  const int nsteps = tw < t1 ? (t1 - tw + 31) / 32 : 0;
-  const int last_row = max(min(t1, L) - 1, 0);
-  auto load_step = [&](uint4 (&r)[4], int i) {
-    const uint32_t off = (uint32_t)min(tw + 32 * i + kr, last_row) * (kHeadDim * 2) + kl * 16;
-    r[0] = ld_buf(Kr, off);
-    r[1] = ld_buf(Kr, off + 128);
-    r[2] = ld_buf(Vr, off);
-    r[3] = ld_buf(Vr, off + 128);
-  };
-  uint4 ra[4], rb[4];
-  load_step(ra, 0);
-  load_step(rb, 1);
-
-  // new K/V rows at positions nb .. t1-1 (rows r' = p - L of this sequence), rounded as
-  // the cache stores them; the item of the sequence's last row also writes them out
-  const bool writer = (r_off == A.n - 1);
-  for (int i = wave; i < n_new; i += 4) {
-    const int rp = nb + i - L;
-    const int rrow = row - r_off + rp;
-    const float *src = A.qkv + (size_t)rrow * A.nqkv;
-    const float inv = head_inv_rms<COH>(A, rrow, A.nq + g);
-    const uint16_t kb0 = rne16<DT>(ldx<COH>(src + (A.nq + g) * kHeadDim + lane) * inv);
-    const uint16_t kb1 = rne16<DT>(ldx<COH>(src + (A.nq + g) * kHeadDim + lane + 64) * inv);
-    const uint16_t vb0 = rne16<DT>(ldx<COH>(src + (A.nq + A.nkv + g) * kHeadDim + lane));
-    const uint16_t vb1 = rne16<DT>(ldx<COH>(src + (A.nq + A.nkv + g) * kHeadDim + lane + 64));
-    knew[i * kHeadDim + lane] = kb0;
-    knew[i * kHeadDim + lane + 64] = kb1;
-    vnew[i * kHeadDim + lane] = vb0;
-    vnew[i * kHeadDim + lane + 64] = vb1;
-    if (writer) {
-      const size_t off = (kvrow0 + nb + i) * kHeadDim;
-      A.kc[off + lane] = kb0;
-      A.kc[off + lane + 64] = kb1;
-      A.vc[off + lane] = vb0;
-      A.vc[off + lane + 64] = vb1;
+  // Everything the item reads from this call's projection is loaded up front in
+  // one batch: its GROUP q vectors (this lane's 16 dims each), their norm
+  // partials, and for a chunk holding appended rows the k/v rows and k partials.
+  const float qs = kLog2e * rsqrtf((float)kHeadDim);
+  const uint32_t row_bytes = (uint32_t)A.nqkv * 4;
+  const __amdgpu_buffer_rsrc_t Qr = rsrc_of(A.qkv + (size_t)row * A.nqkv, row_bytes);
+  const __amdgpu_buffer_rsrc_t Sr = rsrc_of(A.ssq + (size_t)row * (A.nq + A.nkv) * kTilesPerHead,
+                                            (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4);
+  float4 qv[GROUP][4], qp[GROUP][2];
+#pragma unroll
+  for (int j = 0; j < GROUP; ++j) {
+    const uint32_t h = g * GROUP + j;
+    qv[j][0] = ld_dev4(Qr, (h * kHeadDim + d0) * 4);
+    qv[j][1] = ld_dev4(Qr, (h * kHeadDim + d0 + 4) * 4);
+    qv[j][2] = ld_dev4(Qr, (h * kHeadDim + d1) * 4);
+    qv[j][3] = ld_dev4(Qr, (h * kHeadDim + d1 + 4) * 4);
+    qp[j][0] = ld_dev4(Sr, h * kTilesPerHead * 4);
+    qp[j][1] = ld_dev4(Sr, (h * kTilesPerHead + 4) * 4);
+  }
+  // appended rows (positions nb .. t1-1 = rows nb - L .. of this sequence): wave w
+  // takes rows w, w + 4, ...; lane l holds dims 2l, 2l + 1
+  const int n_mine = n_new > wave ? (n_new - wave + 3) / 4 : 0;
+  for (int i0 = 0; i0 < n_mine; i0 += 2) {
+    float2 kx[2], vx[2];
+    float4 kp[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = wave + 4 * (i0 + u);
+      const int rrow = row - r_off + (nb + min(i, n_new - 1) - L);
+      const float *src = A.qkv + (size_t)rrow * A.nqkv;
+      const __amdgpu_buffer_rsrc_t Rr = rsrc_of(src, row_bytes);
+      const float4 k4 = ld_dev4(Rr, ((A.nq + g) * kHeadDim + 2 * (lane & ~1)) * 4);
+      const float4 v4 = ld_dev4(Rr, ((A.nq + A.nkv + g) * kHeadDim + 2 * (lane & ~1)) * 4);
+      kx[u] = (lane & 1) ? make_float2(k4.z, k4.w) : make_float2(k4.x, k4.y);
+      vx[u] = (lane & 1) ? make_float2(v4.z, v4.w) : make_float2(v4.x, v4.y);
+      const __amdgpu_buffer_rsrc_t Pr = rsrc_of(A.ssq + (size_t)rrow * (A.nq + A.nkv) * kTilesPerHead,
+                                                (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4);
+      kp[u][0] = ld_dev4(Pr, (A.nq + g) * kTilesPerHead * 4);
+      kp[u][1] = ld_dev4(Pr, ((A.nq + g) * kTilesPerHead + 4) * 4);
+    }
+    const bool writer = (r_off == A.n - 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = wave + 4 * (i0 + u);
+      if (i >= n_new) break;
+      const float inv = inv_rms_of(A, kp[u][0], kp[u][1]);
+      const uint32_t kb = (uint32_t)rne16<DT>(kx[u].x * inv) | ((uint32_t)rne16<DT>(kx[u].y * inv) << 16);
+      const uint32_t vb = (uint32_t)rne16<DT>(vx[u].x) | ((uint32_t)rne16<DT>(vx[u].y) << 16);
+      reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
+      reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
+      if (writer) {   // the item of the sequence's last row also stores them in the cache
+        const size_t off = (kvrow0 + nb + i) * kHeadDim;
+        reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
+        reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+      }
     }
   }
   // q of the GROUP heads: rotated, gained projection / rms, times log2(e)/sqrt(d)
-  const float qs = kLog2e * rsqrtf((float)kHeadDim);
   float q[GROUP][16];
 #pragma unroll
   for (int j = 0; j < GROUP; ++j) {
-    const int h = g * GROUP + j;
-    const float sc = head_inv_rms<COH>(A, row, h) * qs;
-    const float *qp = A.qkv + (size_t)row * A.nqkv + h * kHeadDim;
-    if constexpr (COH) {
+    const float sc = inv_rms_of(A, qp[j][0], qp[j][1]) * qs;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        q[j][e] = ld_dev(qp + d0 + e) * sc;
-        q[j][8 + e] = ld_dev(qp + d1 + e) * sc;
-      }
-    } else {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e4 = 0; e4 < 2; ++e4) {
-          const float4 f = *reinterpret_cast<const float4 *>(qp + (h2 ? d1 : d0) + 4 * e4);
-          q[j][8 * h2 + 4 * e4] = f.x * sc;
-          q[j][8 * h2 + 4 * e4 + 1] = f.y * sc;
-          q[j][8 * h2 + 4 * e4 + 2] = f.z * sc;
-          q[j][8 * h2 + 4 * e4 + 3] = f.w * sc;
-        }
+    for (int h2 = 0; h2 < 4; ++h2) {
+      q[j][4 * h2 + 0] = qv[j][h2].x * sc;
+      q[j][4 * h2 + 1] = qv[j][h2].y * sc;
+      q[j][4 * h2 + 2] = qv[j][h2].z * sc;
+      q[j][4 * h2 + 3] = qv[j][h2].w * sc;
     }
   }
   if (n_new > 0) __syncthreads();
@@ -538,51 +616,81 @@ __device__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo,
 // ---------------------------------------------------------------- merge
 //
 // att[row][h] = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, M = max_c m_c,
-// over the chunks of (row, kv head g) in increasing order (deterministic).  The
+// over the chunks of (row, kv head g) in a fixed order that depends only on the
+// chunk count, never on which item finished first (deterministic).  The
 // last item of a (row, g) to finish does it: every item bumps a counter after
 // its partial is stored; the block that sees the count reach nch merges.  The
 // counter update of one item is resolved after the next item, so its latency
 // hides behind that item's work.
 template <int DT, int GROUP, bool COH>
 __device__ void merge_group(const LayerArgs &A, int row, int g, int nch, AttnShared<GROUP> &S) {
+  // thread t: float4 column o4 = t % (GROUP * 32) of the GROUP x 128 outputs and
+  // chunks c = t / (GROUP * 32) + NCL * i.  The (m, l) pairs and the first 8 chunk
+  // vectors of every thread are requested in one batch; chunks past nch read
+  // zeros (outside the buffer range).
+  constexpr int NO4 = GROUP * 32, NCL = 256 / NO4, BATCH = 8;
+  const int t = threadIdx.x, o4 = t % NO4, cl = t / NO4, j = o4 / 32, d = (o4 % 32) * 4;
   const float *p0 = A.part + (((size_t)row * A.nkv + g) * kMaxChunks * GROUP) * kPartStride;
-  const size_t cs = (size_t)GROUP * kPartStride;
-  for (int idx = threadIdx.x; idx < GROUP * nch; idx += blockDim.x) {
-    const int j = idx / nch, cc = idx % nch;
-    S.mc[j][cc] = ld_dev(p0 + cc * cs + j * kPartStride + 128);
-    S.lc[j][cc] = ld_dev(p0 + cc * cs + j * kPartStride + 129);
+  const uint32_t cs = (uint32_t)GROUP * kPartStride * 4;                 // bytes per chunk
+  const __amdgpu_buffer_rsrc_t R = rsrc_of(p0, (uint32_t)nch * cs);
+  for (int idx = t; idx < GROUP * kMaxChunks; idx += 256) {
+    const int mj = idx / kMaxChunks, mc = idx % kMaxChunks;
+    const float4 v = ld_dev4(R, mc * cs + (mj * kPartStride + 128) * 4);   // m, l (zeros past nch)
+    S.mc[mj][mc] = mc < nch ? v.x : -INFINITY;
+    S.lc[mj][mc] = v.y;
   }
+  float4 v[BATCH];
+#pragma unroll
+  for (int u = 0; u < BATCH; ++u) v[u] = ld_dev4(R, (cl + NCL * u) * cs + (j * kPartStride + d) * 4);
   __syncthreads();
-  for (int j = wave_id(); j < GROUP; j += 4) {
+  for (int jj = wave_id(); jj < GROUP; jj += 4) {
     const int lane = lane_id();
-    const float mc = lane < nch ? S.mc[j][lane] : -INFINITY;
-    const float M = wave_max(mc);
-    const float w = lane < nch ? exp2f(mc - M) : 0.f;
-    const float tot = wave_sum(w * (lane < nch ? S.lc[j][lane] : 0.f));
-    if (lane < nch) S.w[j][lane] = w / tot;
+    const float m = S.mc[jj][lane];
+    const float M = wave_max(m);
+    const float w = lane < nch ? exp2f(m - M) : 0.f;
+    const float tot = wave_sum(w * S.lc[jj][lane]);
+    S.w[jj][lane] = w / tot;
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < GROUP * kHeadDim; o += blockDim.x) {
-    const int j = o / kHeadDim, d = o % kHeadDim;
-    const float *pd = p0 + j * kPartStride + d;
-    float a = 0.f;
-    int cc = 0;
-    for (; cc + 8 <= nch; cc += 8) {
-      float v[8];
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0;; i0 += BATCH) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = ld_dev(pd + (cc + u) * cs);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) a += S.w[j][cc + u] * v[u];
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = cl + NCL * (i0 + u);
+      const float w = c < nch ? S.w[j][c] : 0.f;
+      a.x += w * v[u].x;
+      a.y += w * v[u].y;
+      a.z += w * v[u].z;
+      a.w += w * v[u].w;
     }
-    for (; cc < nch; ++cc) a += S.w[j][cc] * ld_dev(pd + cc * cs);
+    if (cl + NCL * (i0 + BATCH) >= nch) break;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) v[u] = ld_dev4(R, (cl + NCL * (i0 + BATCH + u)) * cs + (j * kPartStride + d) * 4);
+  }
+  // the NCL chunk classes of a column meet in LDS
+  S.red[cl * NO4 + o4] = a;
+  __syncthreads();
+  if (cl == 0) {
+    for (int k = 1; k < NCL; ++k) {
+      const float4 b = S.red[k * NO4 + o4];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
     const size_t col = (size_t)(g * GROUP + j) * kHeadDim + d;
-    stx<COH>(A.att + (size_t)row * A.nq * kHeadDim + col, a);
+    const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) stx<COH>(A.att + (size_t)row * A.nq * kHeadDim + col + e, av[e]);
     if (A.mfma) {   // tiled [plane][col / 32][row][32]: one MFMA operand load reads 1 KB contiguously
       const size_t plane = (size_t)(A.nq * kHeadDim / 32) * A.rows * 32;
-      const size_t idx = ((col / 32) * A.rows + row) * 32 + col % 32;
-      const uint16_t hi = rne16<DT>(a);
-      A.att_hl[idx] = hi;
-      A.att_hl[plane + idx] = rne16<DT>(a - cvt16<DT>(hi));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const size_t idx = (((col + e) / 32) * A.rows + row) * 32 + (col + e) % 32;
+        const uint16_t hi = rne16<DT>(av[e]);
+        A.att_hl[idx] = hi;
+        A.att_hl[plane + idx] = rne16<DT>(av[e] - cvt16<DT>(hi));
+      }
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(A.mctr + (size_t)row * A.nkv + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -619,7 +727,9 @@ __device__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *
   Pending pend{-1, 0, 0, 0u};
   for (int item = first; item < total; item += stride) {
     const Item it = decode_item(A, item, pre);
-    attn_item<DT, GROUP, COH>(A, it, rinfo, knew, vnew, S);
+    KVRegs P;
+    attn_item_loads(A, it, rinfo, P);
+    attn_item<DT, GROUP, COH>(A, it, rinfo, knew, vnew, S, P);
     const Pending now = signal_item(A, it);
     if (pend.row >= 0) resolve<DT, GROUP, COH>(A, pend, S);
     pend = now;
@@ -631,8 +741,10 @@ __device__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *
 //
 // Same structure as phase A with the attention output as input, read from LDS
 // (merged by this block) or from the workspace.
+// rinfo: the rows' (slot, length, visible keys, offset) in LDS, or NULL to read
+// the row table in the workspace
 template <int DT, int KV, int RB, int RPW, bool COH>
-__device__ void oproj_tile(const LayerArgs &A, int tile, const uint4 (&wr)[RPW][KV]) {
+__device__ __forceinline__ void oproj_tile(const LayerArgs &A, int tile, const uint4 (&wr)[RPW][KV], const int4 *rinfo) {
   const int wave = wave_id(), lane = lane_id();
   const int o0 = (tile * 4 + wave) * RPW;
   const int K = A.nq * kHeadDim;
@@ -646,8 +758,10 @@ __device__ void oproj_tile(const LayerArgs &A, int tile, const uint4 (&wr)[RPW][
         if (row < A.rows) {
           const float *src = A.att + (size_t)row * K + (v * 64 + lane) * 8;
           if constexpr (COH) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[r][v * 8 + e] = ld_dev(src + e);
+            const __amdgpu_buffer_rsrc_t R = rsrc_of(A.att + (size_t)row * K, (uint32_t)K * 4);
+            const float4 f0 = ld_dev4(R, (v * 64 + lane) * 32), f1 = ld_dev4(R, (v * 64 + lane) * 32 + 16);
+            x[r][v * 8 + 0] = f0.x; x[r][v * 8 + 1] = f0.y; x[r][v * 8 + 2] = f0.z; x[r][v * 8 + 3] = f0.w;
+            x[r][v * 8 + 4] = f1.x; x[r][v * 8 + 5] = f1.y; x[r][v * 8 + 6] = f1.z; x[r][v * 8 + 7] = f1.w;
           } else {
             const float4 f0 = reinterpret_cast<const float4 *>(src)[0], f1 = reinterpret_cast<const float4 *>(src)[1];
             x[r][v * 8 + 0] = f0.x; x[r][v * 8 + 1] = f0.y; x[r][v * 8 + 2] = f0.z; x[r][v * 8 + 3] = f0.w;
@@ -688,7 +802,8 @@ __device__ void oproj_tile(const LayerArgs &A, int tile, const uint4 (&wr)[RPW][
           if (lane == i) val = acc[i][r];
         const size_t o = (size_t)row * A.H + o0 + lane;
         if (A.residual) val += cvt16<DT>(A.residual[o]);
-        if (!read_row_table<COH>(A, row).x) val = __builtin_nanf("");
+        const bool row_ok = rinfo ? rinfo[row].z > 0 : read_row_table<COH>(A, row).x != 0;
+        if (!row_ok) val = __builtin_nanf("");
         if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
         else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
       }
@@ -720,38 +835,77 @@ __device__ void advance_lengths(const LayerArgs &A) {
   }
 }
 
-// ---------------------------------------------------------------- grid barrier (fused dispatch)
+// ---------------------------------------------------------------- dataflow counters (one-dispatch path)
 //
-// bar[0] counts arrivals, bar[1] is a generation number.  The last arriver
-// resets the count and bumps the generation; the others wait for the
-// generation to move.  Both words return to a reusable state, so the barrier
-// needs no reset between calls.  Everything exchanged across the barrier
-// travels through st_dev / ld_dev, so arriving only needs this block's stores
-// performed.  The wait is bounded: on timeout the status bit is set and the
-// block stops working (the call's outputs are then undefined).
-__device__ bool grid_barrier(uint32_t *bar, uint32_t nblocks, uint32_t *status, int *s_ok) {
+// The one-dispatch path orders its phases with counters in the workspace
+// instead of grid barriers: a consumer waits only for the producers it reads.
+//   flow[h]             projection tiles of head h (q heads, k heads, v heads) stored
+//   flow[kFlowMerged]   (row, kv head) pairs merged into the attention output
+//   flow[kFlowStarted]  workgroups started (their tickets give the call's epoch)
+//   flow[kFlowLensRead] workgroups that have read the lengths
+// Counters are never reset: every call adds the same amount to each of them
+// (kTilesPerHead per head, kFlowMergeUnit merges, kFlowStartUnit starts and
+// reads; the
+// shortfall of a call is added up front by workgroup 0), so the call's epoch e,
+// taken from a workgroup's own ticket on flow[kFlowStarted], gives every target:
+// counter == (e + 1) * unit in the low bits that e determines.  Producers store
+// with st_dev, wait for their stores, then bump the counter; consumers poll
+// with ld_dev.  Every wait is bounded: on timeout the status bit is set and the
+// workgroup stops (the call's outputs are then undefined and the workspace must
+// be zeroed again).
+constexpr int kFlowMerged = 120, kFlowStarted = 121, kFlowLensRead = 122;
+constexpr uint32_t kFlowStartShift = 12;                    // unit 4096 >= any grid
+constexpr uint32_t kFlowStartUnit = 1u << kFlowStartShift;
+constexpr uint32_t kFlowMergeUnit = 32;                     // >= rows * nkv of the path (4 x 8)
+constexpr uint32_t kFlowEpochBits = 32 - kFlowStartShift;   // epochs are known modulo 2^20
+
+// target of a counter with `unit` per call at the end of epoch e, and the bits it determines
+struct FlowTarget {
+  uint32_t value, mask;
+};
+__device__ __forceinline__ FlowTarget flow_target(uint32_t e, uint32_t unit) {
+  const uint32_t mask = (uint32_t)(((unsigned long long)unit << kFlowEpochBits) - 1);
+  return FlowTarget{((e + 1) * unit) & mask, mask};
+}
+
+// thread 0 only
+__device__ bool spin_until(const LayerArgs &A, const uint32_t *c, FlowTarget t) {
+  if ((ld_dev(c) & t.mask) == t.value) return true;
+  const long long start = wall_clock64();
+  while ((ld_dev(c) & t.mask) != t.value) {
+    __builtin_amdgcn_s_sleep(1);
+    if (wall_clock64() - start > kBarrierTimeoutTicks) {
+      if (A.status) atomicOr(A.status, (uint32_t)ASR_STATUS_SYNC_TIMEOUT);
+      return false;
+    }
+  }
+  return true;
+}
+
+__device__ bool wait_count(const LayerArgs &A, const uint32_t *c, FlowTarget t, int *s_ok) {
+  if (threadIdx.x == 0) *s_ok = spin_until(A, c, t);
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// every thread's stores of this workgroup are performed: count them
+__device__ __forceinline__ void signal_count(uint32_t *c) {
   wait_mem();
   __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// an item reads the q heads of its kv group and, when its chunk holds this
+// call's rows, their k and v heads
+__device__ bool wait_item_inputs(const LayerArgs &A, const Item &it, const int4 *rinfo, int group, uint32_t e,
+                                 int *s_ok) {
   if (threadIdx.x == 0) {
-    int ok = 1;
-    const uint32_t gen0 = ld_dev(&bar[1]);
-    wait_mem();
-    const uint32_t old = __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == nblocks - 1) {
-      __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_mem();
-      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const long long start = wall_clock64();
-      while (ld_dev(&bar[1]) == gen0) {
-        __builtin_amdgcn_s_sleep(1);
-        if (wall_clock64() - start > kBarrierTimeoutTicks) {
-          ok = 0;
-          if (status) atomicOr(status, (uint32_t)ASR_STATUS_SYNC_TIMEOUT);
-          break;
-        }
-      }
-    }
+    const FlowTarget t = flow_target(e, kTilesPerHead);
+    bool ok = true;
+    for (int j = 0; j < group && ok; ++j) ok = spin_until(A, A.flow + it.g * group + j, t);
+    const ItemGeom g = item_geom(A, it, rinfo);
+    if (ok && g.n_new > 0)
+      ok = spin_until(A, A.flow + A.nq + it.g, t) && spin_until(A, A.flow + A.nq + A.nkv + it.g, t);
     *s_ok = ok;
   }
   __syncthreads();
@@ -1004,8 +1158,10 @@ __host__ __device__ __forceinline__ size_t lds_attn_bytes(int rows, int n) {
 template <int DT, int KV, int RB>
 __global__ __launch_bounds__(256) void k_qkv(LayerArgs A) {
   __shared__ float s_ssq[RB][4];
+  uint4 wr[4][KV];
+  qkv_tile_weights<KV>(A, blockIdx.x, wr);
   if (blockIdx.x == 0) write_row_table<false>(A);
-  qkv_tile<DT, KV, RB, false>(A, blockIdx.x, s_ssq);
+  qkv_tile<DT, KV, RB, false>(A, blockIdx.x, s_ssq, wr);
 }
 
 template <int DT, int GROUP>
@@ -1025,41 +1181,138 @@ __global__ __launch_bounds__(256) void k_oproj(LayerArgs A) {
   uint4 wr[RPW][KV];
   load_wo<KV, RPW>(A, blockIdx.x, wr);
   if (blockIdx.x == 0) advance_lengths<false>(A);
-  oproj_tile<DT, KV, RB, RPW, false>(A, blockIdx.x, wr);
+  oproj_tile<DT, KV, RB, RPW, false>(A, blockIdx.x, wr, nullptr);
 }
 
-// All phases in one persistent dispatch.  Each block prefetches the o_proj
-// weights of its first phase-D tile at the start, so that traffic overlaps
-// phases A and C.
+// lengths advance once every workgroup has read them (rows from LDS)
+__device__ void advance_lengths_lds(const LayerArgs &A, const int4 *rinfo) {
+  for (int b = threadIdx.x; b < A.B; b += blockDim.x) {
+    const int4 ri = rinfo[b * A.n];
+    if (ri.z > 0) {
+      A.lens[ri.x] = ri.y + A.n;
+    } else if (A.status) {
+      atomicOr(A.status, (ri.x >= 0 && ri.x < A.batch_cap) ? (uint32_t)ASR_STATUS_CAPACITY : kStatusBadSlot);
+    }
+  }
+}
+
+template <int DT, int GROUP>
+__device__ __forceinline__ void resolve_flow(const LayerArgs &A, const Pending &p, AttnShared<GROUP> &S) {
+  if (threadIdx.x == 0) S.flag = p.old == (uint32_t)(p.nch - 1);
+  __syncthreads();
+  if (S.flag) {
+    merge_group<DT, GROUP, true>(A, p.row, p.g, p.nch, S);
+    signal_count(A.flow + kFlowMerged);
+  }
+}
+
+// All phases of a layer call in one persistent dispatch whose workgroups are
+// all resident.  Workgroup w takes projection tile w, attention item w and
+// o_proj tile w (and every G-th after them).  The weights of its projection
+// tile are its first loads; the K/V of its first item and its W_o rows are
+// requested as soon as its projection results are stored, so they travel
+// while the phases wait only for the data they consume: an item for the
+// projection tiles of its heads, o_proj for the merged attention output.
+// (A poll returns only after every load its wave issued before it, so no
+// prefetch is issued ahead of the projection's own inputs or its signal.)
+// Diagnostics build only (-DASR_FLOW_TRACE): thread 0 of each workgroup stamps
+// the wall clock at numbered points of k_flow into 16 slots per workgroup just
+// past the split-KV partials (the caller then allocates that much more workspace).
+#ifdef ASR_FLOW_TRACE
+#define FLOW_TRACE(i)                                                                          \
+  do {                                                                                         \
+    if (threadIdx.x == 0)                                                                      \
+      reinterpret_cast<unsigned long long *>(A.part + (size_t)A.rows * A.nkv * kMaxChunks * GROUP * \
+                                             kPartStride)[blockIdx.x * 16 + (i)] = wall_clock64(); \
+  } while (0)
+#else
+#define FLOW_TRACE(i) \
+  do {                \
+  } while (0)
+#endif
+
 template <int DT, int KVI, int RBI, int KVO, int RBO, int GROUP>
-__global__ __launch_bounds__(256) void k_fused(LayerArgs A, int tiles_a, int tiles_d) {
+__global__ __launch_bounds__(256) void k_flow(LayerArgs A, int tiles_a, int tiles_d) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ AttnShared<GROUP> SA;
   __shared__ float s_ssq[RBI][4];
   __shared__ int s_ok;
-  const int G = gridDim.x;
-
-  uint4 wo[kRpwD][KVO];
-  const int first_d = blockIdx.x;
-  if (first_d < tiles_d) load_wo<KVO, kRpwD>(A, first_d, wo);
-
-  if (blockIdx.x == 0) write_row_table<true>(A);
-  for (int t = blockIdx.x; t < tiles_a; t += G) qkv_tile<DT, KVI, RBI, true>(A, t, s_ssq);
-  if (!grid_barrier(A.bar, G, A.status, &s_ok)) return;
-
+  const int G = gridDim.x, w = blockIdx.x;
   int4 *rinfo = reinterpret_cast<int4 *>(dyn);
   uint16_t *knew = reinterpret_cast<uint16_t *>(rinfo + A.rows);
   uint16_t *vnew = knew + A.n * kHeadDim;
   int *pre = reinterpret_cast<int *>(vnew + A.n * kHeadDim);
-  build_item_prefix(A, pre, rinfo, SA.wsum);
-  attention_phase<DT, GROUP, true>(A, pre, rinfo, knew, vnew, SA, blockIdx.x, G);
-  if (!grid_barrier(A.bar, G, A.status, &s_ok)) return;
 
-  if (blockIdx.x == 0) advance_lengths<true>(A);
-  for (int t = blockIdx.x; t < tiles_d; t += G) {
-    if (t != first_d) load_wo<KVO, kRpwD>(A, t, wo);
-    oproj_tile<DT, KVO, RBO, kRpwD, true>(A, t, wo);
+  FLOW_TRACE(0);
+  __shared__ uint32_t s_epoch;
+  // weights of the first projection tile: the first loads of the dispatch
+  uint4 wq[4][KVI];
+  if (w < tiles_a) qkv_tile_weights<KVI>(A, w, wq);
+  // this call's epoch from the workgroup's start ticket (workgroup 0 also adds the
+  // shortfall of the start and merge units)
+  uint32_t merged = 0;
+  if (threadIdx.x == 0) {
+    const uint32_t add = w == 0 ? kFlowStartUnit - (uint32_t)G + 1u : 1u;
+    s_epoch = __hip_atomic_fetch_add(A.flow + kFlowStarted, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >>
+              kFlowStartShift;
   }
+  build_item_prefix(A, pre, rinfo, SA.wsum);
+  FLOW_TRACE(1);
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(A.flow + kFlowLensRead, w == 0 ? kFlowStartUnit - (uint32_t)G + 1u : 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  for (int r = 0; r < A.rows; ++r) merged += rinfo[r].z > 0 ? (uint32_t)A.nkv : 0u;
+  if (w == 0 && threadIdx.x == 0 && merged < kFlowMergeUnit)
+    __hip_atomic_fetch_add(A.flow + kFlowMerged, kFlowMergeUnit - merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t e = s_epoch;
+  const int total = pre[A.rows];
+
+  // projection
+  for (int t = w; t < tiles_a; t += G) {
+    if (t != w) qkv_tile_weights<KVI>(A, t, wq);
+    qkv_tile<DT, KVI, RBI, true>(A, t, s_ssq, wq);
+    FLOW_TRACE(2);
+    signal_count(A.flow + t / kTilesPerHead);
+    FLOW_TRACE(3);
+  }
+  // K/V of the first item and W_o of the first o_proj tile, in flight while the
+  // projection results travel
+  KVRegs P;
+  Item it0{0, 0, 0, 1};
+  if (w < total) {
+    it0 = decode_item(A, w, pre);
+    attn_item_loads(A, it0, rinfo, P);
+  }
+  uint4 wo[kRpwD][KVO];
+  if (w < tiles_d) load_wo<KVO, kRpwD>(A, w, wo);
+  // attention
+  Pending pend{-1, 0, 0, 0u};
+  for (int item = w; item < total; item += G) {
+    const Item it = item == w ? it0 : decode_item(A, item, pre);
+    if (item != w) attn_item_loads(A, it, rinfo, P);
+    if (!wait_item_inputs(A, it, rinfo, GROUP, e, &s_ok)) return;
+    FLOW_TRACE(4);
+    attn_item<DT, GROUP, true>(A, it, rinfo, knew, vnew, SA, P);
+    FLOW_TRACE(5);
+    const Pending now = signal_item(A, it);
+    if (pend.row >= 0) resolve_flow<DT, GROUP>(A, pend, SA);
+    pend = now;
+  }
+  if (pend.row >= 0) resolve_flow<DT, GROUP>(A, pend, SA);
+  FLOW_TRACE(6);
+  // o_proj, once every (row, kv head) with visible keys is merged
+  if (!wait_count(A, A.flow + kFlowMerged, flow_target(e, kFlowMergeUnit), &s_ok)) return;
+  FLOW_TRACE(7);
+  if (w == 0) {   // lengths advance once every workgroup has read them
+    if (!wait_count(A, A.flow + kFlowLensRead, flow_target(e, kFlowStartUnit), &s_ok)) return;
+    advance_lengths_lds(A, rinfo);
+  }
+  for (int t = w; t < tiles_d; t += G) {
+    if (t != w) load_wo<KVO, kRpwD>(A, t, wo);
+    oproj_tile<DT, KVO, RBO, kRpwD, true>(A, t, wo, rinfo);
+  }
+  FLOW_TRACE(8);
+  FLOW_TRACE(9);
 }
 
 // ---------------------------------------------------------------- launch
@@ -1180,7 +1433,7 @@ bool fused_supported(const LayerArgs &a) {
 template <int DT, int KVI>
 hipError_t fused_launch(const LayerArgs &a, int grid, hipStream_t s, hipEvent_t *ev) {
   constexpr int KVO = 4;  // nq d = 2048
-  auto kern = a.rows == 1 ? k_fused<DT, KVI, 1, KVO, 1, 2> : k_fused<DT, KVI, rb_for(KVI), KVO, rb_for(KVO), 2>;
+  auto kern = a.rows == 1 ? k_flow<DT, KVI, 1, KVO, 1, 2> : k_flow<DT, KVI, rb_for(KVI), KVO, rb_for(KVO), 2>;
   const int tiles_a = a.nqkv / (4 * kRpwA);
   const int tiles_d = a.H / (4 * kRpwD);
   if (ev)
@@ -1199,7 +1452,7 @@ hipError_t layer_fused(const LayerArgs &a, int grid, hipStream_t s, hipEvent_t *
 template <int DT, int KVI>
 int occupancy_fused(size_t dyn) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<DT, KVI, rb_for(KVI), 4, rb_for(4), 2>, 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_flow<DT, KVI, rb_for(KVI), 4, rb_for(4), 2>, 256,
                                                    dyn) != hipSuccess)
     return 0;
   return per_cu;

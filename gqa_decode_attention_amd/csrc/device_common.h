@@ -124,6 +124,21 @@ __device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
 // wait until every memory operation this thread issued has been performed
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// 16-byte accesses with the same device-coherent cache policy (sc1) through a
+// buffer resource: a workgroup-uniform base and `bytes` of range; a lane's
+// offset past the range reads zeros and writes nothing.
+constexpr int kCachePolicyCoherent = 16;   // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyCoherent));
+}
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                         off, 0, kCachePolicyCoherent);
+}
+
 // ---------------------------------------------------------------- wave reductions
 //
 // DPP lane permutations run in the vector ALU (no trip through the LDS
@@ -179,7 +194,8 @@ __device__ __forceinline__ float sum_stride8(float v) {
   return v;
 }
 
-__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+// wave index in the workgroup, as a uniform (scalar) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x % kWave; }
 
 }  // namespace asr

@@ -14,6 +14,7 @@ constexpr int kMaxChunks = 64;        // split-KV chunks per (row, kv head)
 constexpr int kMinSplit = 16;         // keys per chunk, lower bound
 constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
 constexpr int kMaxVerifyK = 32;
+constexpr int kFlowWords = 128;      // counters of the one-dispatch path (heads + 4 totals)
 constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
 constexpr uint32_t kStatusBadSlot = ASR_STATUS_BAD_SLOT;  // slot index outside [0, batch_cap)
 
@@ -41,7 +42,7 @@ struct LayerArgs {
   float *att;                 // [rows][nq][d] merged attention output
   uint16_t *att_hl;           // [rows][2][nq d] the same as hi and lo 16-bit terms (MFMA o_proj)
   float *part;                // [rows][nkv][kMaxChunks][group][kPartStride]
-  uint32_t *bar;              // [2] grid barrier: arrival count, generation
+  uint32_t *flow;             // [kFlowWords] counters of the one-dispatch path (zero between calls)
   uint32_t *mctr;             // [rows][nkv] finished chunks per (row, kv head)
   int4 *rowtab;               // [rows] {ok, L, slot, slot_ok} as seen before the call
   // shape
@@ -55,7 +56,7 @@ struct LayerArgs {
 };
 
 struct WorkspaceLayout {
-  size_t bar, mctr, rowtab, qkv, ssq, att, att_hl, part, total;
+  size_t flow, mctr, rowtab, qkv, ssq, att, att_hl, part, total;
 };
 
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);

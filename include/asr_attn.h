@@ -67,9 +67,11 @@ enum {
 enum {
   ASR_DISPATCH_AUTO = 0,   /* the library chooses (currently: one kernel per phase) */
   ASR_DISPATCH_MULTI = 1,  /* one kernel per phase, ordered by the stream */
-  ASR_DISPATCH_FUSED = 2   /* one persistent kernel per layer call whose workgroups meet at grid
-                              barriers; hidden 1024 or 2048, 16 q heads, 8 kv heads, at most 4
-                              rows (else ASR_EUNSUPPORTED) */
+  ASR_DISPATCH_FUSED = 2   /* one persistent kernel per layer call whose resident workgroups
+                              order the phases through counters in the workspace (a phase waits
+                              only for the producers it reads); hidden 1024 or 2048, 16 q heads,
+                              8 kv heads, at most 4 rows (else ASR_EUNSUPPORTED); needs the whole
+                              device (no concurrent kernels), else it may time out */
 };
 
 /*

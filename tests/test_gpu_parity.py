@@ -377,3 +377,67 @@ def test_phase_events_leave_results_unchanged(rows):
             assert pe.total_ms() >= sum(d) * 0.999
     assert np.array_equal(res[0][0], res[1][0])
     assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
+
+
+@pytest.mark.parametrize("case", ["bs1", "rows3_with_overflow", "verify2x2"])
+def test_fused_dispatch_reuses_its_workspace(case):
+    """Several one-dispatch calls in a row on one workspace (its counters must return to zero
+    after every call) give the bits of the stream-ordered kernels, including rows whose append
+    overflows the capacity (NaN out, length kept, status bit)."""
+    dtype = si.F16 if case != "verify2x2" else si.BF16
+    lens = {"bs1": [300], "rows3_with_overflow": [40, 64, 7], "verify2x2": [100, 33]}[case]
+    n = 2 if case == "verify2x2" else 1
+    cap = {"bs1": 320, "rows3_with_overflow": 64, "verify2x2": 128}[case]
+    L = SeededLayer(6, 2, 1024, dtype)
+    kb, vb = fill_cache(6, 2, lens, cap, dtype)
+    res = {}
+    for mode in (ga.DISPATCH_MULTI, ga.DISPATCH_FUSED):
+        kv = device_cache(kb, vb, lens, dtype)
+        cfg = ga.config(dtype=dtype, dispatch=mode, kv_split=32)
+        ws = ga.alloc_workspace(cfg, len(lens) * n, cap)
+        outs = []
+        for step in range(3):
+            if n == 1:
+                outs.append(_run_decode(L, cfg, kv, _x(6, 2, step, (len(lens), 1024), dtype), dtype, ws=ws))
+            else:
+                outs.append(_run_verify(L, cfg, kv, _x(6, 2, step, (len(lens), n, 1024), dtype), dtype, ws=ws))
+        res[mode] = (outs, to_bits(kv.k), to_bits(kv.v), kv.lens.cpu().numpy(), kv.status.item())
+    a, b = res[ga.DISPATCH_MULTI], res[ga.DISPATCH_FUSED]
+    for oa, ob in zip(a[0], b[0]):
+        assert np.array_equal(oa, ob, equal_nan=True)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    assert np.array_equal(a[3], b[3]) and a[4] == b[4]
+    if case == "rows3_with_overflow":
+        assert b[4] == ga.STATUS_CAPACITY and np.all(np.isnan(b[0][0][1])) and b[3][1] == 64
+    else:
+        assert b[4] == 0
+
+
+def test_fused_dispatch_workspace_across_changing_shapes():
+    """One workspace serves one-dispatch calls of 1, 3, 2 and 4 rows (decode and verify) in turn:
+    the counters' per-call epochs stay consistent; each call matches the stream-ordered kernels."""
+    dtype = si.F16
+    lens = [50, 90, 20, 70]
+    cap = 128
+    L = SeededLayer(6, 4, 1024, dtype)
+    kb, vb = fill_cache(6, 4, lens, cap, dtype)
+    plan = [("decode", [0]), ("decode", [1, 2, 3]), ("verify", [2]), ("decode", [3, 0]), ("verify", [1, 3]),
+            ("decode", [0, 1, 2, 3]), ("decode", [2])]
+    res = {}
+    for mode in (ga.DISPATCH_MULTI, ga.DISPATCH_FUSED):
+        kv = device_cache(kb, vb, lens, dtype)
+        cfg = ga.config(dtype=dtype, dispatch=mode, kv_split=16)
+        ws = ga.alloc_workspace(cfg, 4, cap)
+        outs = []
+        for step, (kind, slots) in enumerate(plan):
+            if kind == "decode":
+                outs.append(_run_decode(L, cfg, kv, _x(6, 4, step, (len(slots), 1024), dtype), dtype, slots=slots,
+                                        ws=ws))
+            else:
+                outs.append(_run_verify(L, cfg, kv, _x(6, 4, step, (len(slots), 2, 1024), dtype), dtype, slots=slots,
+                                        ws=ws))
+        res[mode] = (outs, to_bits(kv.k), kv.lens.cpu().numpy(), kv.status.item())
+    a, b = res[ga.DISPATCH_MULTI], res[ga.DISPATCH_FUSED]
+    for oa, ob in zip(a[0], b[0]):
+        assert np.array_equal(oa, ob)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and a[3] == b[3] == 0

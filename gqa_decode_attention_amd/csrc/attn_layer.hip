@@ -917,81 +917,100 @@ __device__ bool wait_item_inputs(const LayerArgs &A, const Item &it, const int4 
 // ---------------------------------------------------------------- batched projections on MFMA
 //
 // For more than a few rows the projections are dense contractions and run on
-// v_mfma_f32_16x16x32.  A block owns 16 output rows and all input rows (in
-// blocks of 64); its four waves split the contraction dimension in quarters and
-// add their 16 x 64 partial tiles in LDS.  fp32 operands are split into two
-// 16-bit terms (hi = rne(v), lo = rne(v - hi)), exact 16-bit operands are used
-// as they are, so the products keep about twice the 16-bit precision.
+// v_mfma_f32_16x16x32.  A block owns 16 output features and 16 (o_proj) or 64
+// (QKV) input rows; its four waves split the contraction dimension in
+// quarters, request every operand of their quarter at once (one memory round
+// trip, no step-by-step dependence) and add their partial tiles in LDS.  fp32
+// operands are split into two 16-bit terms (hi = rne(v), lo = rne(v - hi)),
+// exact 16-bit operands are used as they are, so the products keep about twice
+// the 16-bit precision.
 //
+// Blocks of one output-feature tile are placed on one XCD (workgroups go to the
+// XCDs round-robin): the weight tile they share is fetched into that XCD's L2
+// once.  The number of feature tiles is a multiple of 8.
+struct TileMap {
+  int col, row;   // feature tile, row tile
+};
+__device__ __forceinline__ TileMap tile_of(int b, int rtiles) {
+  const int q = b / (8 * rtiles), rem = b - q * 8 * rtiles;
+  return TileMap{q * 8 + rem % 8, rem / 8};
+}
+
+// o_proj steps per operand batch: all of a wave's quarter up to 16 steps, else an even split
+constexpr int chunk_steps(int kq) {
+  return kq <= 16 ? kq : (kq % 16 == 0 ? 16 : (kq % 12 == 0 ? 12 : (kq % 14 == 0 ? 14 : (kq % 10 == 0 ? 10 : 4))));
+}
+
 // QKV: out[n][o] = inv_rms(x_n) * sum_k (W[o][k] g_in[k]) x[n][k].  The weight
 // times the input-norm gain is formed in fp32 (exact: two 16-bit factors) and
 // split; x is the exact 16-bit operand; the sums of squares of x for inv_rms are
-// accumulated from the same loads.  The tile's 16 rows are 8 rotary pairs
-// (t, t + 64) of one head, as in the vector path, with the same epilogue:
-// gain and rotation of q/k pairs, partial sums of squares, v stored raw.
+// accumulated from the same loads.  A block owns 16 features x 64 rows (four
+// row tiles share each split weight step); the 16 features are 8 rotary pairs
+// (t, t + 64) of one head, as in the vector path, with the same epilogue: gain
+// and rotation of q/k pairs, partial sums of squares, v stored raw.
 template <int DT, int KQ>
 __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
+  constexpr int KC = KQ < 8 ? KQ : 8;   // steps per operand batch (x of four row tiles)
   __shared__ f32x4_t s_c[4][4][kWave];
   __shared__ float s_ss[4][64];
   __shared__ float2 s_rope[64][8];   // (cos, sin) for the block's 64 rows x its 8 rotary pairs
   const int wave = wave_id(), lane = lane_id();
-  const int tile = blockIdx.x;
+  const int rtiles = (A.rows + 63) / 64;
+  const TileMap tm = tile_of(blockIdx.x, rtiles);
+  const int tile = tm.col, nb = tm.row * 64;
   const int head = tile / kTilesPerHead, jj = tile % kTilesPerHead, t0 = 8 * jj;
   const int i16 = lane % 16, g4 = lane / 16;
   const int arow = head * kHeadDim + (i16 < 8 ? t0 + i16 : 64 + t0 + i16 - 8);
   const int H = A.H;
   const int kq0 = wave * (H / 4) + g4 * 8;       // this lane's first k
-  if (blockIdx.x == 0) write_row_table<false>(A);
-
-  uint4 w[KQ];
+  const uint16_t *wp = A.w_qkv + (size_t)arow * H + kq0;
+  const uint16_t *xr[4];
 #pragma unroll
-  for (int s = 0; s < KQ; ++s) w[s] = ld16_stream(A.w_qkv + (size_t)arow * H + kq0 + s * 32);
+  for (int nt = 0; nt < 4; ++nt) xr[nt] = A.x + (size_t)min(nb + nt * 16 + i16, A.rows - 1) * H + kq0;
+  if (blockIdx.x == 0) write_row_table<false>(A);
   const bool rot = head < A.nq + A.nkv;
   const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;
 
-  for (int nb = 0; nb < A.rows; nb += 64) {
-    if (rot) {   // rotary angles of this block's 64 rows and 8 pairs, in fp64, once
+  f32x4_t acc[4];
+  float ss[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    ss[nt] = 0.f;
+  }
+#pragma unroll 1
+  for (int c0 = 0; c0 < KQ; c0 += KC) {
+    uint4 w[KC], g[KC], x[4][KC];
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+      w[s] = ld16_stream(wp + (c0 + s) * 32);
+      g[s] = ld16(A.g_in + kq0 + (c0 + s) * 32);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) x[nt][s] = ld16(xr[nt] + (c0 + s) * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
+    if (c0 == 0 && rot) {   // rotary angles of the 64 rows x 8 pairs in fp64 while the operands travel
       for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
         const int r = idx / 8, tt = idx % 8;
         const int n = nb + r;
-        float c = 1.f, sn = 0.f;
+        float cs = 1.f, sn = 0.f;
         if (n < A.rows) {
           const double omega = exp2(-(2.0 * (t0 + tt) / kHeadDim) * log2((double)A.theta));
           double sd, cd;
           sincos((double)row_info(A, n).pos * omega, &sd, &cd);
-          c = (float)cd;
+          cs = (float)cd;
           sn = (float)sd;
         }
-        s_rope[r][tt] = make_float2(c, sn);
+        s_rope[r][tt] = make_float2(cs, sn);
       }
     }
-    f32x4_t acc[4];
-    float ss[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      ss[nt] = 0.f;
-    }
-    const uint16_t *xr[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) xr[nt] = A.x + (size_t)min(nb + nt * 16 + i16, A.rows - 1) * H + kq0;
-    uint4 bc[4], bn[4], gc, gn;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bc[nt] = ld16(xr[nt]);
-    gc = ld16(A.g_in + kq0);
-#pragma unroll
-    for (int s = 0; s < KQ; ++s) {
-      if (s + 1 < KQ) {   // next step's operands in flight during this step's math
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) bn[nt] = ld16(xr[nt] + (s + 1) * 32);
-        gn = ld16(A.g_in + kq0 + (s + 1) * 32);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this step's math
+    for (int s = 0; s < KC; ++s) {
       uint4 ahi, alo;
       {
         float wf[8], gf[8], p[8];
         unpack8<DT>(w[s], wf);
-        unpack8<DT>(gc, gf);
+        unpack8<DT>(g[s], gf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = wf[e] * gf[e];
         split8<DT>(p, ahi, alo);
@@ -999,154 +1018,126 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float xf[8];
-        unpack8<DT>(bc[nt], xf);
+        unpack8<DT>(x[nt][s], xf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss[nt] += xf[e] * xf[e];
-        acc[nt] = mfma16x16x32<DT>(ahi, bc[nt], acc[nt]);
-        acc[nt] = mfma16x16x32<DT>(alo, bc[nt], acc[nt]);
-      }
-      if (s + 1 < KQ) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) bc[nt] = bn[nt];
-        gc = gn;
+        acc[nt] = mfma16x16x32<DT>(ahi, x[nt][s], acc[nt]);
+        acc[nt] = mfma16x16x32<DT>(alo, x[nt][s], acc[nt]);
       }
     }
+  }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      s_c[wave][nt][lane] = acc[nt];
-      float v = ss[nt];
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      if (g4 == 0) s_ss[wave][nt * 16 + i16] = v;
+  for (int nt = 0; nt < 4; ++nt) {
+    s_c[wave][nt][lane] = acc[nt];
+    float v = ss[nt];
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    if (g4 == 0) s_ss[wave][nt * 16 + i16] = v;
+  }
+  __syncthreads();
+  {
+    const int nt = wave;
+    const int n = nb + nt * 16 + i16;
+    f32x4_t c = s_c[0][nt][lane];
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) {
+      const f32x4_t d = s_c[wv][nt][lane];
+      c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
     }
-    __syncthreads();
-    {
-      const int nt = wave;
-      const int n = nb + nt * 16 + i16;
-      f32x4_t c = s_c[0][nt][lane];
+    const float ssx = s_ss[0][nt * 16 + i16] + s_ss[1][nt * 16 + i16] + s_ss[2][nt * 16 + i16] + s_ss[3][nt * 16 + i16];
+    const float inv = 1.0f / sqrtf(ssx / (float)H + A.eps);
+    const bool first = g4 < 2;
+    float raw[4], out[4];
+    float sq = 0.f;
 #pragma unroll
-      for (int wv = 1; wv < 4; ++wv) {
-        const f32x4_t d = s_c[wv][nt][lane];
-        c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
+    for (int j = 0; j < 4; ++j) {
+      raw[j] = c[j] * inv;
+      sq += raw[j] * raw[j];
+    }
+    sq += __shfl_xor(sq, 16, kWave);
+    sq += __shfl_xor(sq, 32, kWave);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = (g4 & 1) * 4 + j;
+      const int t = t0 + tt;
+      if (rot) {
+        const float u = cvt16<DT>(gp[first ? t : t + 64]) * raw[j];
+        const float up = __shfl_xor(u, 32, kWave);
+        const float2 cs = s_rope[nt * 16 + i16][tt];
+        out[j] = first ? u * cs.x - up * cs.y : u * cs.x + up * cs.y;
+      } else {
+        out[j] = raw[j];
       }
-      const float ssx = s_ss[0][nt * 16 + i16] + s_ss[1][nt * 16 + i16] + s_ss[2][nt * 16 + i16] + s_ss[3][nt * 16 + i16];
-      const float inv = 1.0f / sqrtf(ssx / (float)H + A.eps);
-      const bool first = g4 < 2;
-      float raw[4], out[4];
-      float sq = 0.f;
+    }
+    if (n < A.rows) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        raw[j] = c[j] * inv;
-        sq += raw[j] * raw[j];
+        const int t = t0 + (g4 & 1) * 4 + j;
+        A.qkv[(size_t)n * A.nqkv + head * kHeadDim + (first ? t : t + 64)] = out[j];
       }
-      sq += __shfl_xor(sq, 16, kWave);
-      sq += __shfl_xor(sq, 32, kWave);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tt = (g4 & 1) * 4 + j;
-        const int t = t0 + tt;
-        if (rot) {
-          const float u = cvt16<DT>(gp[first ? t : t + 64]) * raw[j];
-          const float up = __shfl_xor(u, 32, kWave);
-          const float2 cs = s_rope[nt * 16 + i16][tt];
-          out[j] = first ? u * cs.x - up * cs.y : u * cs.x + up * cs.y;
-        } else {
-          out[j] = raw[j];
-        }
-      }
-      if (n < A.rows) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = t0 + (g4 & 1) * 4 + j;
-          A.qkv[(size_t)n * A.nqkv + head * kHeadDim + (first ? t : t + 64)] = out[j];
-        }
-        if (rot && g4 == 0) A.ssq[((size_t)n * (A.nq + A.nkv) + head) * kTilesPerHead + jj] = sq;
-      }
+      if (rot && g4 == 0) A.ssq[((size_t)n * (A.nq + A.nkv) + head) * kTilesPerHead + jj] = sq;
     }
-    __syncthreads();
   }
 }
 
-// o_proj: out[n][o] = sum_c W_o[o][c] att[n][c] (+ residual), att as hi + lo terms.
-// Eight waves split the contraction dimension in eighths.
+// o_proj: out[n][o] = sum_c W_o[o][c] att[n][c] (+ residual), att as hi + lo terms
+// read from its tiled copy [plane][c / 32][row][32].
 template <int DT, int KQ>
-__global__ __launch_bounds__(512) void k_oproj_mfma(LayerArgs A) {
-  __shared__ f32x4_t s_c[8][4][kWave];
+__global__ __launch_bounds__(256) void k_oproj_mfma(LayerArgs A) {
+  constexpr int KC = chunk_steps(KQ);
+  __shared__ f32x4_t s_c[4][kWave];
   const int wave = wave_id(), lane = lane_id();
   const int i16 = lane % 16, g4 = lane / 16;
   const int K = A.nq * kHeadDim;
-  const int o0 = blockIdx.x * 16;
-  const int kq0 = wave * (K / 8) + g4 * 8;
-  uint4 w[KQ];
-#pragma unroll
-  for (int s = 0; s < KQ; ++s) w[s] = ld16_stream(A.w_o + (size_t)(o0 + i16) * K + kq0 + s * 32);
+  const int rtiles = (A.rows + 15) / 16;
+  const TileMap tm = tile_of(blockIdx.x, rtiles);
+  const int o0 = tm.col * 16, nb = tm.row * 16;
+  const int kq0 = wave * (K / 4) + g4 * 8;
+  const uint16_t *wp = A.w_o + (size_t)(o0 + i16) * K + kq0;
+  const size_t plane = (size_t)(K / 32) * A.rows * 32;
+  const size_t kstep = (size_t)A.rows * 32;   // next 32-wide block of the contraction
+  const uint16_t *bp = A.att_hl + ((size_t)(wave * (K / 128)) * A.rows + min(nb + i16, A.rows - 1)) * 32 + g4 * 8;
   if (blockIdx.x == 0) advance_lengths<false>(A);
 
-  const size_t plane = (size_t)(K / 32) * A.rows * 32;
-  const int kb0 = wave * (K / 256);          // this wave's first 32-wide block of the contraction
-  for (int nb = 0; nb < A.rows; nb += 64) {
-    const uint16_t *br[4];
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int c0 = 0; c0 < KQ; c0 += KC) {
+    uint4 w[KC], hi[KC], lo[KC];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      br[nt] = A.att_hl + ((size_t)kb0 * A.rows + min(nb + nt * 16 + i16, A.rows - 1)) * 32 + g4 * 8;
-    const size_t kstep = (size_t)A.rows * 32;   // next 32-wide block
-    f32x4_t acc[4];
-    uint4 hc[4], lc[4], hn[4], ln[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      hc[nt] = ld16(br[nt]);
-      lc[nt] = ld16(br[nt] + plane);
+    for (int s = 0; s < KC; ++s) {
+      w[s] = ld16_stream(wp + (c0 + s) * 32);
+      hi[s] = ld16(bp + (c0 + s) * kstep);
+      lo[s] = ld16(bp + plane + (c0 + s) * kstep);
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
 #pragma unroll
-    for (int s = 0; s < KQ; ++s) {
-      if (s + 1 < KQ) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          hn[nt] = ld16(br[nt] + (s + 1) * kstep);
-          ln[nt] = ld16(br[nt] + plane + (s + 1) * kstep);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this step's math
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        acc[nt] = mfma16x16x32<DT>(w[s], hc[nt], acc[nt]);
-        acc[nt] = mfma16x16x32<DT>(w[s], lc[nt], acc[nt]);
-      }
-      if (s + 1 < KQ) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          hc[nt] = hn[nt];
-          lc[nt] = ln[nt];
-        }
-      }
+    for (int s = 0; s < KC; ++s) {
+      acc = mfma16x16x32<DT>(w[s], hi[s], acc);
+      acc = mfma16x16x32<DT>(w[s], lo[s], acc);
     }
+  }
+  s_c[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    const int n = nb + i16;
+    f32x4_t c = s_c[0][lane];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) s_c[wave][nt][lane] = acc[nt];
-    __syncthreads();
-    if (wave < 4) {
-      const int nt = wave;
-      const int n = nb + nt * 16 + i16;
-      f32x4_t c = s_c[0][nt][lane];
+    for (int wv = 1; wv < 4; ++wv) {
+      const f32x4_t d = s_c[wv][lane];
+      c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
+    }
+    if (n < A.rows) {
+      const bool ok = A.rowtab[n].x;
 #pragma unroll
-      for (int wv = 1; wv < 8; ++wv) {
-        const f32x4_t d = s_c[wv][nt][lane];
-        c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
-      }
-      if (n < A.rows) {
-        const bool ok = A.rowtab[n].x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const size_t o = (size_t)n * A.H + o0 + g4 * 4 + j;
-          float val = c[j];
-          if (A.residual) val += cvt16<DT>(A.residual[o]);
-          if (!ok) val = __builtin_nanf("");
-          if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
-          else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const size_t o = (size_t)n * A.H + o0 + g4 * 4 + j;
+        float val = c[j];
+        if (A.residual) val += cvt16<DT>(A.residual[o]);
+        if (!ok) val = __builtin_nanf("");
+        if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
+        else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -1354,14 +1345,14 @@ LayerKernel pick_qkv_mfma(int kq) {
 template <int DT>
 LayerKernel pick_oproj_mfma(int kq) {
   switch (kq) {
-    case 2: return k_oproj_mfma<DT, 2>;
     case 4: return k_oproj_mfma<DT, 4>;
-    case 6: return k_oproj_mfma<DT, 6>;
     case 8: return k_oproj_mfma<DT, 8>;
-    case 10: return k_oproj_mfma<DT, 10>;
     case 12: return k_oproj_mfma<DT, 12>;
-    case 14: return k_oproj_mfma<DT, 14>;
     case 16: return k_oproj_mfma<DT, 16>;
+    case 20: return k_oproj_mfma<DT, 20>;
+    case 24: return k_oproj_mfma<DT, 24>;
+    case 28: return k_oproj_mfma<DT, 28>;
+    case 32: return k_oproj_mfma<DT, 32>;
     default: return nullptr;
   }
 }
@@ -1405,8 +1396,9 @@ template <int DT>
 hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEvent_t *ev) {
   hipError_t e;
   if (a.mfma) {
-    // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 256 (o_proj, eight waves)
-    if ((e = launch_phase(pick_qkv_mfma<DT>(a.H / 128), dim3(a.nqkv / 16), dim3(256), 0, s, ev, 0, a)) !=
+    // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
+    const int rtiles = (a.rows + 63) / 64;
+    if ((e = launch_phase(pick_qkv_mfma<DT>(a.H / 128), dim3(a.nqkv / 16 * rtiles), dim3(256), 0, s, ev, 0, a)) !=
         hipSuccess)
       return e;
   } else {
@@ -1418,7 +1410,8 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                         a)) != hipSuccess)
     return e;
   if (a.mfma)
-    return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 256), dim3(a.H / 16), dim3(512), 0, s, ev, 2, a);
+    return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 128), dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(256),
+                        0, s, ev, 2, a);
   return launch_phase(pick_oproj<DT>(a.nq * kHeadDim / 512, a.rows == 1), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s,
                       ev, 2, a);
 }

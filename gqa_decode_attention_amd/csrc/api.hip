@@ -11,7 +11,8 @@ namespace asr {
 
 namespace {
 
-constexpr int kMaxRows = 2048;
+constexpr int kMaxRows = kMaxLayerRows;
+constexpr int kMinShare = 64;    // least keys per wave share of the many-row attention
 constexpr int kVectorRows = 4;   // up to this many rows the projections run as vector-ALU GEMVs
 constexpr size_t kAlign = 256;
 
@@ -160,7 +161,16 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   }
   bound *= a.nkv;
   const long long cap_grid = 16LL * cus;
-  const int attn_grid = (int)(bound < 1 ? 1 : (bound > cap_grid ? cap_grid : bound));
+  int attn_grid = (int)(bound < 1 ? 1 : (bound > cap_grid ? cap_grid : bound));
+  if (attn_waves_used(a)) {
+    // many rows: one equal key share per wave of a resident grid; a (row, kv
+    // head) spans at most capacity / share + 2 <= kMaxChunks shares
+    attn_grid = attn_waves_grid(cfg->dtype, a.group, cus);
+    if (attn_grid <= 0) return ASR_EHIP;
+    int share = cfg->kv_split ? cfg->kv_split : kMinShare;
+    const int least = (kv->capacity + kMaxChunks - 2) / (kMaxChunks - 1);
+    a.split = share > least ? share : least;
+  }
 
   bool fused = false;
   int fused_grid = 0;

@@ -294,9 +294,10 @@ struct AttnShared {
   int flag;
 };
 
-// block-wide exclusive prefix of (chunks per row) * nkv into pre[0..rows]; each
-// row's (slot, committed length, visible keys) is kept in rinfo[] so that items
-// start without global loads
+// block-wide exclusive prefix of (chunks per row) * nkv (KEYS: visible keys per
+// row * nkv) into pre[0..rows]; each row's (slot, committed length, visible
+// keys, block offset) is kept in rinfo[] so that work starts without global loads
+template <bool KEYS = false>
 __device__ void build_item_prefix(const LayerArgs &A, int *pre, int4 *rinfo, int *wsum) {
   const int wave = wave_id(), lane = lane_id();
   const int rows = A.rows;
@@ -306,7 +307,7 @@ __device__ void build_item_prefix(const LayerArgs &A, int *pre, int4 *rinfo, int
   for (int i = beg; i < end; ++i) {
     const RowInfo ri = row_info(A, i);
     rinfo[i] = make_int4(ri.slot, ri.L, ri.nvis, ri.r);
-    local += chunks_of(ri.nvis, A.split) * A.nkv;
+    local += (KEYS ? ri.nvis : chunks_of(ri.nvis, A.split)) * A.nkv;
   }
   int incl = local;
 #pragma unroll
@@ -321,7 +322,7 @@ __device__ void build_item_prefix(const LayerArgs &A, int *pre, int4 *rinfo, int
   int run = base + incl - local;
   for (int i = beg; i < end; ++i) {
     pre[i] = run;
-    run += chunks_of(rinfo[i].z, A.split) * A.nkv;
+    run += (KEYS ? rinfo[i].z : chunks_of(rinfo[i].z, A.split)) * A.nkv;
   }
   if (threadIdx.x == 255) pre[rows] = run;
   __syncthreads();
@@ -735,6 +736,408 @@ __device__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *
     pend = now;
   }
   if (pend.row >= 0) resolve<DT, GROUP, COH>(A, pend, S);
+}
+
+// ---------------------------------------------------------------- phase C for many rows: equal key shares
+//
+// With many rows the attention work is the committed K/V stream.  The visible
+// keys of all (row, kv head) pairs, concatenated in (row, g) order, are cut
+// into equal shares, one per wave of a resident grid, so every wave streams
+// the same number of keys whatever the length mix (no tail of long chunks).  A
+// share holds one or more pieces (runs of keys of one (row, g)); a piece ends
+// in a partial (m, l, acc) stored at slot (share index - share index of the
+// (row, g)'s first key).  Waves work alone: no LDS traffic and no barrier after
+// the prologue.  The loads run two 8-key steps ahead of the arithmetic, across
+// piece boundaries.  Keys at or past the committed length are this call's
+// appended rows: their k/v come from the projection (k normalised, both
+// rounded to 16 bits as the cache stores them), and the piece of the
+// sequence's last row writes them to the cache.  The last piece of a (row, g)
+// to be counted merges the partials in slot order (deterministic).
+
+// wave-uniform position of a wave's load or arithmetic stream
+struct WCur {
+  int row, g, t, te, grem;   // step keys [t, t + 8) of the piece [., te) of (row, g); keys of the share after te
+  int P;                     // global index of key 0 of (row, g)
+  int slot, L, nvis, roff;
+};
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ void wcur_enter(WCur &c, const LayerArgs &A, const int *pre, const int4 *rinfo, int row,
+                                           int g, int a, int keys) {
+  const int4 ri = rinfo[row];
+  c.row = row;
+  c.g = g;
+  c.t = a;
+  c.slot = rfl(ri.x);
+  c.L = rfl(ri.y);
+  c.nvis = rfl(ri.z);
+  c.roff = rfl(ri.w);
+  c.P = rfl(pre[row]) + g * c.nvis;
+  const int len = min(c.nvis - a, keys);
+  c.te = a + len;
+  c.grem = keys - len;
+}
+
+// next step: 1 in the same piece, 2 in a new piece, 0 past the share (unchanged)
+__device__ __forceinline__ int wcur_next(WCur &c, const LayerArgs &A, const int *pre, const int4 *rinfo) {
+  if (c.t + 8 < c.te) {
+    c.t += 8;
+    return 1;
+  }
+  if (c.grem == 0) return 0;
+  int row = c.row, g = c.g + 1;
+  if (g == A.nkv) {
+    g = 0;
+    do {
+      ++row;
+    } while (row < A.rows - 1 && rfl(rinfo[row].z) == 0);
+    if (rfl(rinfo[row].z) == 0) return 0;   // (no keys left: the share ends)
+  }
+  wcur_enter(c, A, pre, rinfo, row, g, 0, c.grem);
+  return 2;
+}
+
+// K and V of one step: lane = key t + (lane >> 3), dims [8 kl, 8 kl + 8) and [64 + 8 kl, ..)
+// (kl = lane & 7); rows clamped to the piece's last committed key, so past
+// the piece the loads hit lines already fetched.
+__device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, uint4 (&r)[4]) {
+  const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  const size_t base = ((size_t)c.slot * A.nkv + c.g) * A.capacity * kHeadDim;
+  const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + base, region);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + base, region);
+  const int last = max(min(c.te, c.L) - 1, 0);
+  const uint32_t off = (uint32_t)min(c.t + kr, last) * (kHeadDim * 2) + kl * 16;
+  r[0] = ld_buf(Kr, off);
+  r[1] = ld_buf(Kr, off + 128);
+  r[2] = ld_buf(Vr, off);
+  r[3] = ld_buf(Vr, off + 128);
+}
+
+// One lane's 8 dims of an appended row, 16-bit as stored: k normalised with
+// its head's partial sums, v raw.
+template <int DT>
+__device__ __forceinline__ uint4 round8(float4 a, float4 b, float sc) {
+  uint4 u;
+  u.x = (uint32_t)rne16<DT>(a.x * sc) | ((uint32_t)rne16<DT>(a.y * sc) << 16);
+  u.y = (uint32_t)rne16<DT>(a.z * sc) | ((uint32_t)rne16<DT>(a.w * sc) << 16);
+  u.z = (uint32_t)rne16<DT>(b.x * sc) | ((uint32_t)rne16<DT>(b.y * sc) << 16);
+  u.w = (uint32_t)rne16<DT>(b.z * sc) | ((uint32_t)rne16<DT>(b.w * sc) << 16);
+  return u;
+}
+template <int DT>
+__device__ __forceinline__ uint4 round8(float4 a, float4 b) {
+  uint4 u;
+  u.x = (uint32_t)rne16<DT>(a.x) | ((uint32_t)rne16<DT>(a.y) << 16);
+  u.y = (uint32_t)rne16<DT>(a.z) | ((uint32_t)rne16<DT>(a.w) << 16);
+  u.z = (uint32_t)rne16<DT>(b.x) | ((uint32_t)rne16<DT>(b.y) << 16);
+  u.w = (uint32_t)rne16<DT>(b.z) | ((uint32_t)rne16<DT>(b.w) << 16);
+  return u;
+}
+
+// lane-pair exchange across lanes l ^ MASK
+template <int MASK>
+__device__ __forceinline__ float xswap(float v) {
+  if constexpr (MASK == 8) return dpp<0x128>(v);   // row_ror:8 within 16-lane rows
+  else return __shfl_xor(v, MASK, kWave);
+}
+
+// Reduce-scatter over the lanes l ^ MASK: lanes with the MASK bit clear keep
+// the low half of the values, the others the high half, each summed with its
+// partner's copy.
+template <int N, int MASK>
+__device__ __forceinline__ void rs_half(const float (&in)[N], float (&out)[N / 2]) {
+  const bool hi = (lane_id() & MASK) != 0;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = hi ? in[N / 2 + i] : in[i];
+    const float send = hi ? in[i] : in[N / 2 + i];
+    out[i] = keep + xswap<MASK>(send);
+  }
+}
+
+// counted partial of a piece whose merge check waits for a later point
+struct WPending {
+  int row, g, np;
+  uint32_t old;   // counter before this piece's increment (lane 0)
+};
+
+// Merge of the np partials of (row, g) by one wave: weights 2^(m_c - M) / sum,
+// chunks in slot order.  Lane c < np holds piece c's (m, l); lane l's outputs
+// are the float4 columns o = l + 64 q of the GROUP x 128 result.
+template <int DT, int GROUP>
+__device__ void merge_wave(const LayerArgs &A, int row, int g, int np) {
+  constexpr int NPL = GROUP / 2;   // float4 outputs per lane
+  const int lane = lane_id();
+  const float *p0 = A.part + (((size_t)row * A.nkv + g) * kMaxChunks * GROUP) * kPartStride;
+  const uint32_t cs = (uint32_t)GROUP * kPartStride * 4;   // bytes per piece
+  const __amdgpu_buffer_rsrc_t R = rsrc_of(p0, (uint32_t)np * cs);
+  float wn[GROUP];
+#pragma unroll
+  for (int j = 0; j < GROUP; ++j) {
+    const float4 ml = ld_dev4(R, lane * cs + (j * kPartStride + 128) * 4);   // zeros past np
+    const float m = lane < np ? ml.x : -INFINITY;
+    const float M = wave_max(m);
+    const float w = (lane < np && m != -INFINITY) ? exp2f(m - M) : 0.f;
+    const float tot = wave_sum(w * ml.y);
+    wn[j] = w / tot;
+  }
+  float4 a[NPL];
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) a[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int BATCH = 8;
+  for (int c0 = 0; c0 < np; c0 += BATCH) {
+    float4 v[BATCH][NPL];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const int o = lane + 64 * q, j = o / 32, d = (o % 32) * 4;
+        v[u][q] = ld_dev4(R, (c0 + u) * cs + (j * kPartStride + d) * 4);   // zeros past np
+      }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = min(c0 + u, kWave - 1);
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const int jl = (lane + 64 * q) / 32;   // head of this output: 2q or 2q + 1
+        const float w0 = readlane(wn[(2 * q) % GROUP], c), w1 = readlane(wn[(2 * q + 1) % GROUP], c);
+        const float w = c0 + u < np ? ((jl & 1) ? w1 : w0) : 0.f;
+        a[q].x += w * v[u][q].x;
+        a[q].y += w * v[u][q].y;
+        a[q].z += w * v[u][q].z;
+        a[q].w += w * v[u][q].w;
+      }
+    }
+  }
+  const size_t plane = (size_t)(A.nq * kHeadDim / 32) * A.rows * 32;
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) {
+    const int o = lane + 64 * q, j = o / 32, d = (o % 32) * 4;
+    const size_t col = (size_t)(g * GROUP + j) * kHeadDim + d;
+    const float av[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
+    *reinterpret_cast<float4 *>(A.att + (size_t)row * A.nq * kHeadDim + col) = a[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {   // tiled [plane][col / 32][row][32] for the MFMA o_proj
+      const size_t idx = (((col + e) / 32) * A.rows + row) * 32 + (col + e) % 32;
+      const uint16_t hi = rne16<DT>(av[e]);
+      A.att_hl[idx] = hi;
+      A.att_hl[plane + idx] = rne16<DT>(av[e] - cvt16<DT>(hi));
+    }
+  }
+  if (lane == 0) __hip_atomic_store(A.mctr + (size_t)row * A.nkv + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT, int GROUP>
+__device__ __forceinline__ void wresolve(const LayerArgs &A, const WPending &p) {
+  if (p.row < 0) return;
+  const uint32_t old = (uint32_t)__builtin_amdgcn_readlane((int)p.old, 0);
+  if (old == (uint32_t)(p.np - 1)) merge_wave<DT, GROUP>(A, p.row, p.g, p.np);
+}
+
+template <int DT, int GROUP>
+__device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *rinfo, int w, int W) {
+  const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  const int d0 = 8 * kl, d1 = 64 + 8 * kl;
+  const int T = pre[A.rows];
+  const int S = max(T / W + 1, A.split);
+  const long long s0l = (long long)w * S;
+  if (s0l >= T) return;
+  const int s0 = (int)s0l, s1 = min(s0 + S, T);
+  // the (row, g) holding key s0
+  int lo = 0, hi = A.rows;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= s0) lo = mid; else hi = mid;
+  }
+  const int off = s0 - pre[lo], nv0 = rinfo[lo].z;
+  WCur lc;
+  wcur_enter(lc, A, pre, rinfo, lo, off / nv0, off % nv0, s1 - s0);
+  WCur cc = lc;
+  uint4 ra[4], rb[4];
+  wstep_load(A, lc, ra);
+  wcur_next(lc, A, pre, rinfo);
+  wstep_load(A, lc, rb);
+  wcur_next(lc, A, pre, rinfo);
+
+  const float qs = kLog2e * rsqrtf((float)kHeadDim);
+  const uint32_t row_bytes = (uint32_t)A.nqkv * 4;
+  const uint32_t ssq_bytes = (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4;
+  float q[GROUP][16], m[GROUP], l[GROUP], acc[GROUP][16];
+  WPending pend{-1, 0, 0, 0u};
+
+  // q of the GROUP heads of (row, g): rotated, gained projection / rms, times log2(e)/sqrt(d)
+  auto begin_piece = [&]() {
+    const __amdgpu_buffer_rsrc_t Qr = rsrc_of(A.qkv + (size_t)cc.row * A.nqkv, row_bytes);
+    const __amdgpu_buffer_rsrc_t Sr = rsrc_of(A.ssq + (size_t)cc.row * (A.nq + A.nkv) * kTilesPerHead, ssq_bytes);
+    float4 qv[GROUP][4], qp[GROUP][2];
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      const uint32_t h = cc.g * GROUP + j;
+      qv[j][0] = ld_dev4(Qr, (h * kHeadDim + d0) * 4);
+      qv[j][1] = ld_dev4(Qr, (h * kHeadDim + d0 + 4) * 4);
+      qv[j][2] = ld_dev4(Qr, (h * kHeadDim + d1) * 4);
+      qv[j][3] = ld_dev4(Qr, (h * kHeadDim + d1 + 4) * 4);
+      qp[j][0] = ld_dev4(Sr, h * kTilesPerHead * 4);
+      qp[j][1] = ld_dev4(Sr, (h * kTilesPerHead + 4) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      const float sc = inv_rms_of(A, qp[j][0], qp[j][1]) * qs;
+#pragma unroll
+      for (int h2 = 0; h2 < 4; ++h2) {
+        q[j][4 * h2 + 0] = qv[j][h2].x * sc;
+        q[j][4 * h2 + 1] = qv[j][h2].y * sc;
+        q[j][4 * h2 + 2] = qv[j][h2].z * sc;
+        q[j][4 * h2 + 3] = qv[j][h2].w * sc;
+      }
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    }
+  };
+
+  // the piece of `c` is complete: partial to its slot, then count it
+  auto finish_piece = [&](const WCur &c) {
+    float v32[GROUP * 16];
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v32[j * 16 + e] = acc[j][e];
+    float v16[GROUP * 8], v8[GROUP * 4], v4[GROUP * 2];
+    rs_half<GROUP * 16, 32>(v32, v16);
+    rs_half<GROUP * 8, 16>(v16, v8);
+    rs_half<GROUP * 4, 8>(v8, v4);
+    float lt[GROUP];
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      float x = l[j];
+      x += xswap<32>(x);
+      x += xswap<16>(x);
+      x += xswap<8>(x);
+      lt[j] = x;
+    }
+    const int first = c.P / S;
+    const int pc = w - first;
+    const int np = (c.P + c.nvis - 1) / S - first + 1;
+    float *pb = A.part + ((((size_t)c.row * A.nkv + c.g) * kMaxChunks + pc) * GROUP) * kPartStride;
+    const __amdgpu_buffer_rsrc_t R = rsrc_of(pb, (uint32_t)GROUP * kPartStride * 4);
+    // this lane's values: v4[4 u .. 4 u + 3] = list entries base + 4 u, base from lane bits 5, 4, 3
+    const int base = ((lane >> 5) & 1) * (GROUP * 8) + ((lane >> 4) & 1) * (GROUP * 4) + ((lane >> 3) & 1) * (GROUP * 2);
+#pragma unroll
+    for (int u = 0; u < GROUP / 2; ++u) {
+      const int i = base + 4 * u, j = i / 16, e = i % 16;
+      const int d = e < 8 ? d0 + e : d1 + e - 8;
+      st_dev4(R, (j * kPartStride + d) * 4, make_float4(v4[4 * u], v4[4 * u + 1], v4[4 * u + 2], v4[4 * u + 3]));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < GROUP; ++j) st_dev4(R, (j * kPartStride + 128) * 4, make_float4(m[j], lt[j], 0.f, 0.f));
+    }
+    wait_mem();   // the partial is performed before it is counted
+    const WPending prev = pend;
+    pend.row = c.row;
+    pend.g = c.g;
+    pend.np = np;
+    pend.old = 0u;
+    if (lane == 0)
+      pend.old = __hip_atomic_fetch_add(A.mctr + (size_t)c.row * A.nkv + c.g, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    wresolve<DT, GROUP>(A, prev);
+  };
+
+  // one 8-key step of the arithmetic stream (online softmax with a lazy reference
+  // as in the chunked path: rescale only when a score passes it by 2^8)
+  auto step = [&](const uint4 (&r)[4]) {
+    const int t = cc.t + kr;
+    const bool valid = t < cc.te;
+    uint4 k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
+    if (cc.t + 8 > cc.L && cc.t < cc.te) {   // the step holds appended rows
+      if (valid && t >= cc.L) {
+        const int rrow = cc.row - cc.roff + (t - cc.L);
+        const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)rrow * A.nqkv, row_bytes);
+        const __amdgpu_buffer_rsrc_t Pr = rsrc_of(A.ssq + (size_t)rrow * (A.nq + A.nkv) * kTilesPerHead, ssq_bytes);
+        const uint32_t kh = (A.nq + cc.g) * kHeadDim, vh = (A.nq + A.nkv + cc.g) * kHeadDim;
+        const float4 ka = ld_dev4(Rr, (kh + d0) * 4), kb = ld_dev4(Rr, (kh + d0 + 4) * 4);
+        const float4 kc = ld_dev4(Rr, (kh + d1) * 4), kd = ld_dev4(Rr, (kh + d1 + 4) * 4);
+        const float4 va = ld_dev4(Rr, (vh + d0) * 4), vb = ld_dev4(Rr, (vh + d0 + 4) * 4);
+        const float4 vc = ld_dev4(Rr, (vh + d1) * 4), vd = ld_dev4(Rr, (vh + d1 + 4) * 4);
+        const float4 p0 = ld_dev4(Pr, (A.nq + cc.g) * kTilesPerHead * 4);
+        const float4 p1 = ld_dev4(Pr, ((A.nq + cc.g) * kTilesPerHead + 4) * 4);
+        const float inv = inv_rms_of(A, p0, p1);
+        k0 = round8<DT>(ka, kb, inv);
+        k1 = round8<DT>(kc, kd, inv);
+        v0 = round8<DT>(va, vb);
+        v1 = round8<DT>(vc, vd);
+        if (cc.roff == A.n - 1) {   // the sequence's last row stores the appended rows
+          const size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
+          *reinterpret_cast<uint4 *>(A.kc + ro + d0) = k0;
+          *reinterpret_cast<uint4 *>(A.kc + ro + d1) = k1;
+          *reinterpret_cast<uint4 *>(A.vc + ro + d0) = v0;
+          *reinterpret_cast<uint4 *>(A.vc + ro + d1) = v1;
+        }
+      }
+    }
+    if (!valid) k0 = k1 = v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
+    float kf[16], vf[16];
+    unpack8<DT>(k0, kf);
+    unpack8<DT>(k1, kf + 8);
+    unpack8<DT>(v0, vf);
+    unpack8<DT>(v1, vf + 8);
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += q[j][e] * kf[e];
+      s = sum8(s);
+      s = valid ? s : -INFINITY;
+      if (__any(s > m[j] + kRescaleLog2)) {
+        float smax = fmaxf(s, dpp<kRowMirror>(s));
+        smax = fmaxf(fmaxf(readlane(smax, 0), readlane(smax, 16)), fmaxf(readlane(smax, 32), readlane(smax, 48)));
+        const float mn = fmaxf(m[j], smax);
+        const float corr = exp2f(m[j] - mn);
+        m[j] = mn;
+        l[j] *= corr;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] *= corr;
+      }
+      const float p = valid ? exp2f(s - m[j]) : 0.f;
+      l[j] += p;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] += p * vf[e];
+    }
+  };
+
+  begin_piece();
+  for (;;) {
+    step(ra);
+    wstep_load(A, lc, ra);
+    wcur_next(lc, A, pre, rinfo);
+    {
+      const WCur old = cc;
+      const int st = wcur_next(cc, A, pre, rinfo);
+      if (st != 1) {
+        finish_piece(old);
+        if (st == 0) break;
+        begin_piece();
+      }
+    }
+    step(rb);
+    wstep_load(A, lc, rb);
+    wcur_next(lc, A, pre, rinfo);
+    {
+      const WCur old = cc;
+      const int st = wcur_next(cc, A, pre, rinfo);
+      if (st != 1) {
+        finish_piece(old);
+        if (st == 0) break;
+        begin_piece();
+      }
+    }
+  }
+  wresolve<DT, GROUP>(A, pend);
 }
 
 // ---------------------------------------------------------------- phase D: o_proj
@@ -1167,6 +1570,21 @@ __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   attention_phase<DT, GROUP, false>(A, pre, rinfo, knew, vnew, S, blockIdx.x, gridDim.x);
 }
 
+// many rows: equal key shares per wave of a resident grid
+template <int DT, int GROUP>
+__global__ __launch_bounds__(256) void k_attn_waves(LayerArgs A) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ int wsum[4];
+  int4 *rinfo = reinterpret_cast<int4 *>(dyn);
+  int *pre = reinterpret_cast<int *>(rinfo + A.rows);
+  build_item_prefix<true>(A, pre, rinfo, wsum);
+  attention_waves<DT, GROUP>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
+}
+
+__host__ __device__ __forceinline__ size_t lds_attn_waves_bytes(int rows) {
+  return (size_t)rows * sizeof(int4) + (size_t)(rows + 1) * sizeof(int);
+}
+
 template <int DT, int KV, int RB, int RPW>
 __global__ __launch_bounds__(256) void k_oproj(LayerArgs A) {
   uint4 wr[RPW][KV];
@@ -1369,6 +1787,15 @@ LayerKernel pick_attn(int group) {
 }
 
 template <int DT>
+LayerKernel pick_attn_waves(int group) {
+  switch (group) {
+    case 2: return k_attn_waves<DT, 2>;
+    case 4: return k_attn_waves<DT, 4>;
+    default: return nullptr;
+  }
+}
+
+template <int DT>
 LayerKernel pick_qkv(int kvi, bool one_row) {
   switch (kvi) {
 #define ASR_PICK_QKV(K) \
@@ -1406,9 +1833,14 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                           0, a)) != hipSuccess)
       return e;
   }
-  if ((e = launch_phase(pick_attn<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s, ev, 1,
-                        a)) != hipSuccess)
+  if (attn_waves_used(a)) {
+    if ((e = launch_phase(pick_attn_waves<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
+                          ev, 1, a)) != hipSuccess)
+      return e;
+  } else if ((e = launch_phase(pick_attn<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
+                               ev, 1, a)) != hipSuccess) {
     return e;
+  }
   if (a.mfma)
     return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 128), dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(256),
                         0, s, ev, 2, a);
@@ -1473,5 +1905,25 @@ int fused_max_grid(int dtype, int H, size_t dyn_smem, int cus) {
 }
 
 size_t layer_dyn_smem(const LayerArgs &a) { return fused_dyn_smem(a); }
+
+// (group 8 would hold its 8 q vectors and accumulators past the register file)
+bool attn_waves_used(const LayerArgs &a) { return a.mfma && (a.group == 2 || a.group == 4); }
+
+// Resident grid of the equal-share attention kernel: blocks per CU from the
+// occupancy calculator (at the largest row table) times the CU count.
+int attn_waves_grid(int dtype, int group, int cus) {
+  static int cached[2][9];
+  const int di = dtype == ASR_BF16 ? 1 : 0;
+  if (group != 2 && group != 4) return 0;
+  int per_cu = cached[di][group];
+  if (per_cu <= 0) {
+    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group) : pick_attn_waves<ASR_F16>(group);
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_attn_waves_bytes(kMaxLayerRows)) !=
+                  hipSuccess || per_cu <= 0)
+      return 0;
+    cached[di][group] = per_cu;
+  }
+  return per_cu * cus;
+}
 
 }  // namespace asr

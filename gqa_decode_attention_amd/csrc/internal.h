@@ -14,6 +14,7 @@ constexpr int kMaxChunks = 64;        // split-KV chunks per (row, kv head)
 constexpr int kMinSplit = 16;         // keys per chunk, lower bound
 constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
 constexpr int kMaxVerifyK = 32;
+constexpr int kMaxLayerRows = 2048;   // rows (B k) per layer call
 constexpr int kFlowWords = 128;      // counters of the one-dispatch path (heads + 4 totals)
 constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
 constexpr uint32_t kStatusBadSlot = ASR_STATUS_BAD_SLOT;  // slot index outside [0, batch_cap)
@@ -49,7 +50,7 @@ struct LayerArgs {
   int B, n, rows;             // sequences, rows per sequence (1 decode, k verify), B * n
   int H, nq, nkv, group, nqkv;
   int batch_cap, capacity;
-  int split;                  // keys per chunk
+  int split;                  // keys per chunk (few rows); least keys per wave share (many rows)
   float eps, theta;
   int out_f32;
   int mfma;                   // projections on MFMA (more than a few rows)
@@ -67,6 +68,8 @@ bool layer_fused_supported(const LayerArgs &a);
 hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream_t s, hipEvent_t *ev);
 int fused_max_grid(int dtype, int H, size_t dyn_smem, int cus);
 size_t layer_dyn_smem(const LayerArgs &a);
+bool attn_waves_used(const LayerArgs &a);
+int attn_waves_grid(int dtype, int group, int cus);
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
                             const int32_t *slots, int B, int n, hipStream_t s);
 hipError_t launch_kv_crop(const asr_kv_layer *layers, int n_layers, const int32_t *new_lens,

@@ -803,12 +803,13 @@ __device__ __forceinline__ int wcur_next(WCur &c, const LayerArgs &A, const int 
 // the piece the loads hit lines already fetched.
 __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, uint4 (&r)[4]) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
-  const size_t base = ((size_t)c.slot * A.nkv + c.g) * A.capacity * kHeadDim;
+  // (the cursor is wave-uniform; readfirstlane keeps the resources in scalar registers)
+  const size_t base = ((size_t)rfl(c.slot) * A.nkv + rfl(c.g)) * A.capacity * kHeadDim;
   const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + base, region);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + base, region);
-  const int last = max(min(c.te, c.L) - 1, 0);
-  const uint32_t off = (uint32_t)min(c.t + kr, last) * (kHeadDim * 2) + kl * 16;
+  const int last = max(min(rfl(c.te), rfl(c.L)) - 1, 0);
+  const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * (kHeadDim * 2) + kl * 16;
   r[0] = ld_buf(Kr, off);
   r[1] = ld_buf(Kr, off + 128);
   r[2] = ld_buf(Vr, off);
@@ -955,7 +956,9 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   WCur lc;
   wcur_enter(lc, A, pre, rinfo, lo, off / nv0, off % nv0, s1 - s0);
   WCur cc = lc;
-  uint4 ra[4], rb[4];
+  // three register sets in rotation: the loads of step i + 2 are issued before
+  // the arithmetic of step i, into the set step i - 1 has released
+  uint4 ra[4], rb[4], rc[4];
   wstep_load(A, lc, ra);
   wcur_next(lc, A, pre, rinfo);
   wstep_load(A, lc, rb);
@@ -969,12 +972,13 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
 
   // q of the GROUP heads of (row, g): rotated, gained projection / rms, times log2(e)/sqrt(d)
   auto begin_piece = [&]() {
-    const __amdgpu_buffer_rsrc_t Qr = rsrc_of(A.qkv + (size_t)cc.row * A.nqkv, row_bytes);
-    const __amdgpu_buffer_rsrc_t Sr = rsrc_of(A.ssq + (size_t)cc.row * (A.nq + A.nkv) * kTilesPerHead, ssq_bytes);
+    const int crow = rfl(cc.row), cg = rfl(cc.g);
+    const __amdgpu_buffer_rsrc_t Qr = rsrc_of(A.qkv + (size_t)crow * A.nqkv, row_bytes);
+    const __amdgpu_buffer_rsrc_t Sr = rsrc_of(A.ssq + (size_t)crow * (A.nq + A.nkv) * kTilesPerHead, ssq_bytes);
     float4 qv[GROUP][4], qp[GROUP][2];
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
-      const uint32_t h = cc.g * GROUP + j;
+      const uint32_t h = cg * GROUP + j;
       qv[j][0] = ld_dev4(Qr, (h * kHeadDim + d0) * 4);
       qv[j][1] = ld_dev4(Qr, (h * kHeadDim + d0 + 4) * 4);
       qv[j][2] = ld_dev4(Qr, (h * kHeadDim + d1) * 4);
@@ -1056,16 +1060,19 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
     uint4 k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
     if (cc.t + 8 > cc.L && cc.t < cc.te) {   // the step holds appended rows
       if (valid && t >= cc.L) {
-        const int rrow = cc.row - cc.roff + (t - cc.L);
-        const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)rrow * A.nqkv, row_bytes);
-        const __amdgpu_buffer_rsrc_t Pr = rsrc_of(A.ssq + (size_t)rrow * (A.nq + A.nkv) * kTilesPerHead, ssq_bytes);
-        const uint32_t kh = (A.nq + cc.g) * kHeadDim, vh = (A.nq + A.nkv + cc.g) * kHeadDim;
-        const float4 ka = ld_dev4(Rr, (kh + d0) * 4), kb = ld_dev4(Rr, (kh + d0 + 4) * 4);
-        const float4 kc = ld_dev4(Rr, (kh + d1) * 4), kd = ld_dev4(Rr, (kh + d1 + 4) * 4);
-        const float4 va = ld_dev4(Rr, (vh + d0) * 4), vb = ld_dev4(Rr, (vh + d0 + 4) * 4);
-        const float4 vc = ld_dev4(Rr, (vh + d1) * 4), vd = ld_dev4(Rr, (vh + d1 + 4) * 4);
-        const float4 p0 = ld_dev4(Pr, (A.nq + cc.g) * kTilesPerHead * 4);
-        const float4 p1 = ld_dev4(Pr, ((A.nq + cc.g) * kTilesPerHead + 4) * 4);
+        // resources at the sequence's first row (wave-uniform), the appended row by offset
+        const int row0 = rfl(cc.row) - rfl(cc.roff), i = t - rfl(cc.L), cg = rfl(cc.g);
+        const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)row0 * A.nqkv, (uint32_t)A.n * row_bytes);
+        const __amdgpu_buffer_rsrc_t Pr =
+            rsrc_of(A.ssq + (size_t)row0 * (A.nq + A.nkv) * kTilesPerHead, (uint32_t)A.n * ssq_bytes);
+        const uint32_t kh = i * row_bytes + (A.nq + cg) * kHeadDim * 4, vh = i * row_bytes + (A.nq + A.nkv + cg) * kHeadDim * 4;
+        const uint32_t ph = i * ssq_bytes + (A.nq + cg) * kTilesPerHead * 4;
+        const float4 ka = ld_dev4(Rr, kh + d0 * 4), kb = ld_dev4(Rr, kh + (d0 + 4) * 4);
+        const float4 kc = ld_dev4(Rr, kh + d1 * 4), kd = ld_dev4(Rr, kh + (d1 + 4) * 4);
+        const float4 va = ld_dev4(Rr, vh + d0 * 4), vb = ld_dev4(Rr, vh + (d0 + 4) * 4);
+        const float4 vc = ld_dev4(Rr, vh + d1 * 4), vd = ld_dev4(Rr, vh + (d1 + 4) * 4);
+        const float4 p0 = ld_dev4(Pr, ph);
+        const float4 p1 = ld_dev4(Pr, ph + 16);
         const float inv = inv_rms_of(A, p0, p1);
         k0 = round8<DT>(ka, kb, inv);
         k1 = round8<DT>(kc, kd, inv);
@@ -1080,7 +1087,12 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
         }
       }
     }
-    if (!valid) k0 = k1 = v0 = v1 = make_uint4(0u, 0u, 0u, 0u);
+    {   // invalid lanes: score -inf (a select below) and v zeroed with a mask, not a
+        // branch, so the loads of later steps stay in flight
+      const uint32_t vm = valid ? 0xffffffffu : 0u;
+      v0 = make_uint4(v0.x & vm, v0.y & vm, v0.z & vm, v0.w & vm);
+      v1 = make_uint4(v1.x & vm, v1.y & vm, v1.z & vm, v1.w & vm);
+    }
     float kf[16], vf[16];
     unpack8<DT>(k0, kf);
     unpack8<DT>(k1, kf + 8);
@@ -1110,32 +1122,29 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
     }
   };
 
+  auto issue = [&](uint4 (&r)[4]) {
+    wstep_load(A, lc, r);
+    wcur_next(lc, A, pre, rinfo);
+  };
+  // arithmetic of cc's step, then advance cc: false past the share
+  auto advance = [&](const uint4 (&r)[4]) -> bool {
+    step(r);
+    const WCur old = cc;
+    const int st = wcur_next(cc, A, pre, rinfo);
+    if (st == 1) return true;
+    finish_piece(old);
+    if (st == 0) return false;
+    begin_piece();
+    return true;
+  };
   begin_piece();
   for (;;) {
-    step(ra);
-    wstep_load(A, lc, ra);
-    wcur_next(lc, A, pre, rinfo);
-    {
-      const WCur old = cc;
-      const int st = wcur_next(cc, A, pre, rinfo);
-      if (st != 1) {
-        finish_piece(old);
-        if (st == 0) break;
-        begin_piece();
-      }
-    }
-    step(rb);
-    wstep_load(A, lc, rb);
-    wcur_next(lc, A, pre, rinfo);
-    {
-      const WCur old = cc;
-      const int st = wcur_next(cc, A, pre, rinfo);
-      if (st != 1) {
-        finish_piece(old);
-        if (st == 0) break;
-        begin_piece();
-      }
-    }
+    issue(rc);
+    if (!advance(ra)) break;
+    issue(ra);
+    if (!advance(rb)) break;
+    issue(rb);
+    if (!advance(rc)) break;
   }
   wresolve<DT, GROUP>(A, pend);
 }

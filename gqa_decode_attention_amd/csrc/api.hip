@@ -73,11 +73,22 @@ int choose_split(const asr_attn_config *c, int capacity, int B, int n, const int
   min_split = (min_split + 15) / 16 * 16;
   if (min_split < kMinSplit) min_split = kMinSplit;
   if (c->kv_split) return c->kv_split;
-  // few rows: the attention items are the only parallelism, keep about one item
-  // per two CUs; many rows: several items per CU amortise each item's fixed cost
-  const long long target = (long long)B * n <= kVectorRows ? cus / 2 : 4LL * cus;
   int split = kMinSplit;
   while (split < min_split) split *= 2;
+  if ((long long)B * n <= kVectorRows) {
+    // few rows: every o_proj workgroup merges all chunks of a row, so keep about
+    // 8 chunks per row, and chunks of at least 64 keys (one step per wave)
+    int nvis = 1;
+    for (int b = 0; b < B; ++b) {
+      const int L = host_lens ? host_lens[b] : capacity - n;
+      if (L + n > nvis) nvis = L + n;
+    }
+    if (split < 64) split = 64;
+    while (split < kMaxSplit && 8LL * split < nvis) split *= 2;
+    return split;
+  }
+  // many rows: several items per CU amortise each item's fixed cost
+  const long long target = 4LL * cus;
   for (; split < kMaxSplit; split *= 2) {
     long long items = 0;
     for (int b = 0; b < B; ++b) {
@@ -153,11 +164,17 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.out_f32 = cfg->out_dtype == ASR_F32;
   a.mfma = rows > kVectorRows;
 
-  // upper bound of attention work items; blocks stride over the real count
+  // upper bound of attention work items; blocks stride over the real count.
+  // nch_host: the most chunks of any row, by the host's view of the lengths
   long long bound = 0;
+  a.nch_host = 1;
   for (int b = 0; b < B; ++b) {
     const int L = host_lens ? host_lens[b] : kv->capacity - n;
-    for (int r = 0; r < n; ++r) bound += (L + r + 1 + a.split - 1) / a.split;
+    for (int r = 0; r < n; ++r) {
+      const int c = (L + r + 1 + a.split - 1) / a.split;
+      bound += c;
+      if (c > a.nch_host) a.nch_host = c;
+    }
   }
   bound *= a.nkv;
   const long long cap_grid = 16LL * cus;

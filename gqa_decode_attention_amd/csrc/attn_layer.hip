@@ -287,9 +287,6 @@ template <int GROUP>
 struct AttnShared {
   float acc[4][GROUP][kHeadDim];
   float m[4][GROUP], l[4][GROUP];
-  float w[GROUP][kMaxChunks];     // merge weights 2^(m_c - M) / sum
-  float mc[GROUP][kMaxChunks], lc[GROUP][kMaxChunks];
-  float4 red[256];                // merge: partial sums of the chunk classes
   int wsum[4];
   int flag;
 };
@@ -355,6 +352,13 @@ __device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16 bytes from LDS through an LDS-typed pointer
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_ld16(const uint16_t *p) {
+  const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 constexpr float kRescaleLog2 = 8.f;   // lazy softmax rescale: keep exp2(s - m) <= 2^8
 
 // Where an item's keys are: chunk [t0, t1) of the row's visible keys, of which
@@ -364,8 +368,8 @@ struct ItemGeom {
   size_t kvrow0;
 };
 
-__device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it, const int4 *rinfo) {
-  const int4 rin = rinfo[it.row];       // slot, committed length, visible keys, block offset
+__device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it, int4 rin) {
+  // rin: slot, committed length, visible keys, block offset
   ItemGeom g;
   g.L = rin.y;
   g.r_off = rin.w;
@@ -378,6 +382,9 @@ __device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it
   g.nsteps = g.tw < g.t1 ? (g.t1 - g.tw + 31) / 32 : 0;
   g.last_row = max(min(g.t1, g.L) - 1, 0);
   return g;
+}
+__device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it, const int4 *rinfo) {
+  return item_geom(A, it, rinfo[it.row]);
 }
 
 // The K and V registers of two 32-key steps of an item (lane: one key row of
@@ -411,92 +418,78 @@ __device__ __forceinline__ void attn_item_loads(const LayerArgs &A, const Item &
   P = KVRegs{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// One item, its first two steps already loaded into P.
-template <int DT, int GROUP, bool COH>
-__device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo, uint16_t *knew, uint16_t *vnew,
-                          AttnShared<GROUP> &S, const KVRegs &P) {
-  const int wave = wave_id(), lane = lane_id();
-  const int kl = lane & 7, kr = lane >> 3;
-  const int d0 = 8 * kl, d1 = 64 + 8 * kl;
-  const int row = it.row, g = it.g, c = it.c;
-  const ItemGeom G = item_geom(A, it, rinfo);
-  const int L = G.L, r_off = G.r_off, t1 = G.t1, nb = G.nb, n_new = G.n_new, tw = G.tw, nsteps = G.nsteps;
-  const size_t kvrow0 = G.kvrow0;
-  uint4 ra[4] = {P.a0, P.a1, P.a2, P.a3};
-  uint4 rb[4] = {P.b0, P.b1, P.b2, P.b3};
-  auto load_step = [&](uint4 (&r)[4], int i) { kv_load_step(A, G, r, i); };
+// The q vectors an item reads from this call's projection: its GROUP q heads
+// (this lane's 16 dims of each) and their norm partials; requested, not waited for.
+template <int GROUP>
+struct QLoads {
+  float4 v[GROUP][4], p[GROUP][2];
+};
 
-  // Everything the item reads from this call's projection is loaded up front in
-  // one batch: its GROUP q vectors (this lane's 16 dims each), their norm
-  // partials, and for a chunk holding appended rows the k/v rows and k partials.
-  const float qs = kLog2e * rsqrtf((float)kHeadDim);
-  const uint32_t row_bytes = (uint32_t)A.nqkv * 4;
-  const __amdgpu_buffer_rsrc_t Qr = rsrc_of(A.qkv + (size_t)row * A.nqkv, row_bytes);
+template <int GROUP>
+__device__ __forceinline__ void q_loads(const LayerArgs &A, int row, int g, QLoads<GROUP> &Q) {
+  const int kl = lane_id() & 7;
+  const int d0 = 8 * kl, d1 = 64 + 8 * kl;
+  const __amdgpu_buffer_rsrc_t Qr = rsrc_of(A.qkv + (size_t)row * A.nqkv, (uint32_t)A.nqkv * 4);
   const __amdgpu_buffer_rsrc_t Sr = rsrc_of(A.ssq + (size_t)row * (A.nq + A.nkv) * kTilesPerHead,
                                             (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4);
-  float4 qv[GROUP][4], qp[GROUP][2];
 #pragma unroll
   for (int j = 0; j < GROUP; ++j) {
     const uint32_t h = g * GROUP + j;
-    qv[j][0] = ld_dev4(Qr, (h * kHeadDim + d0) * 4);
-    qv[j][1] = ld_dev4(Qr, (h * kHeadDim + d0 + 4) * 4);
-    qv[j][2] = ld_dev4(Qr, (h * kHeadDim + d1) * 4);
-    qv[j][3] = ld_dev4(Qr, (h * kHeadDim + d1 + 4) * 4);
-    qp[j][0] = ld_dev4(Sr, h * kTilesPerHead * 4);
-    qp[j][1] = ld_dev4(Sr, (h * kTilesPerHead + 4) * 4);
+    Q.v[j][0] = ld_dev4(Qr, (h * kHeadDim + d0) * 4);
+    Q.v[j][1] = ld_dev4(Qr, (h * kHeadDim + d0 + 4) * 4);
+    Q.v[j][2] = ld_dev4(Qr, (h * kHeadDim + d1) * 4);
+    Q.v[j][3] = ld_dev4(Qr, (h * kHeadDim + d1 + 4) * 4);
+    Q.p[j][0] = ld_dev4(Sr, h * kTilesPerHead * 4);
+    Q.p[j][1] = ld_dev4(Sr, (h * kTilesPerHead + 4) * 4);
   }
-  // appended rows (positions nb .. t1-1 = rows nb - L .. of this sequence): wave w
-  // takes rows w, w + 4, ...; lane l holds dims 2l, 2l + 1
-  const int n_mine = n_new > wave ? (n_new - wave + 3) / 4 : 0;
-  for (int i0 = 0; i0 < n_mine; i0 += 2) {
-    float2 kx[2], vx[2];
-    float4 kp[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = wave + 4 * (i0 + u);
-      const int rrow = row - r_off + (nb + min(i, n_new - 1) - L);
-      const float *src = A.qkv + (size_t)rrow * A.nqkv;
-      const __amdgpu_buffer_rsrc_t Rr = rsrc_of(src, row_bytes);
-      const float4 k4 = ld_dev4(Rr, ((A.nq + g) * kHeadDim + 2 * (lane & ~1)) * 4);
-      const float4 v4 = ld_dev4(Rr, ((A.nq + A.nkv + g) * kHeadDim + 2 * (lane & ~1)) * 4);
-      kx[u] = (lane & 1) ? make_float2(k4.z, k4.w) : make_float2(k4.x, k4.y);
-      vx[u] = (lane & 1) ? make_float2(v4.z, v4.w) : make_float2(v4.x, v4.y);
-      const __amdgpu_buffer_rsrc_t Pr = rsrc_of(A.ssq + (size_t)rrow * (A.nq + A.nkv) * kTilesPerHead,
-                                                (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4);
-      kp[u][0] = ld_dev4(Pr, (A.nq + g) * kTilesPerHead * 4);
-      kp[u][1] = ld_dev4(Pr, ((A.nq + g) * kTilesPerHead + 4) * 4);
-    }
-    const bool writer = (r_off == A.n - 1);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = wave + 4 * (i0 + u);
-      if (i >= n_new) break;
-      const float inv = inv_rms_of(A, kp[u][0], kp[u][1]);
-      const uint32_t kb = (uint32_t)rne16<DT>(kx[u].x * inv) | ((uint32_t)rne16<DT>(kx[u].y * inv) << 16);
-      const uint32_t vb = (uint32_t)rne16<DT>(vx[u].x) | ((uint32_t)rne16<DT>(vx[u].y) << 16);
-      reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
-      reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
-      if (writer) {   // the item of the sequence's last row also stores them in the cache
-        const size_t off = (kvrow0 + nb + i) * kHeadDim;
-        reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
-        reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
-      }
-    }
-  }
-  // q of the GROUP heads: rotated, gained projection / rms, times log2(e)/sqrt(d)
-  float q[GROUP][16];
+}
+
+// q of the GROUP heads: rotated, gained projection / rms, times log2(e)/sqrt(d)
+template <int GROUP>
+__device__ __forceinline__ void q_scale(const LayerArgs &A, const QLoads<GROUP> &Q, float (&q)[GROUP][16]) {
+  const float qs = kLog2e * rsqrtf((float)kHeadDim);
 #pragma unroll
   for (int j = 0; j < GROUP; ++j) {
-    const float sc = inv_rms_of(A, qp[j][0], qp[j][1]) * qs;
+    const float sc = inv_rms_of(A, Q.p[j][0], Q.p[j][1]) * qs;
 #pragma unroll
     for (int h2 = 0; h2 < 4; ++h2) {
-      q[j][4 * h2 + 0] = qv[j][h2].x * sc;
-      q[j][4 * h2 + 1] = qv[j][h2].y * sc;
-      q[j][4 * h2 + 2] = qv[j][h2].z * sc;
-      q[j][4 * h2 + 3] = qv[j][h2].w * sc;
+      q[j][4 * h2 + 0] = Q.v[j][h2].x * sc;
+      q[j][4 * h2 + 1] = Q.v[j][h2].y * sc;
+      q[j][4 * h2 + 2] = Q.v[j][h2].z * sc;
+      q[j][4 * h2 + 3] = Q.v[j][h2].w * sc;
     }
   }
-  if (n_new > 0) __syncthreads();
+}
+
+// One lane's two dims of an appended row as the cache stores them: k
+// normalised with its head's partial sums, v raw, both rounded to 16 bits.
+template <int DT>
+__device__ __forceinline__ void fresh_pair(const LayerArgs &A, float4 k4, float4 v4, float4 kp0, float4 kp1,
+                                           uint32_t &kb, uint32_t &vb) {
+  const int lane = lane_id();
+  const float2 kx = (lane & 1) ? make_float2(k4.z, k4.w) : make_float2(k4.x, k4.y);
+  const float2 vx = (lane & 1) ? make_float2(v4.z, v4.w) : make_float2(v4.x, v4.y);
+  const float inv = inv_rms_of(A, kp0, kp1);
+  kb = (uint32_t)rne16<DT>(kx.x * inv) | ((uint32_t)rne16<DT>(kx.y * inv) << 16);
+  vb = (uint32_t)rne16<DT>(vx.x) | ((uint32_t)rne16<DT>(vx.y) << 16);
+}
+
+// The key stream of an item whose first two steps are in ra, rb (the rest are
+// loaded here) and whose appended rows, if any, are in knew/vnew: online
+// softmax per wave, the 4 waves combined in LDS, the partial (m, l, acc) of
+// each q head stored (device-coherent when COH: merged within the dispatch).
+template <int DT, int GROUP, bool COH, int NP>
+__device__ __forceinline__ void attn_stream(const LayerArgs &A, const ItemGeom &G, int row, int g, int c,
+                                            const float (&q)[GROUP][16], const uint16_t *knew,
+                                            const uint16_t *vnew, AttnShared<GROUP> &S, uint4 (&r)[NP][4]) {
+  static_assert(NP == 2 || NP == 4, "two or four steps loaded ahead");
+  uint4 (&ra)[4] = r[0];
+  uint4 (&rb)[4] = r[1];
+  const int wave = wave_id(), lane = lane_id();
+  const int kl = lane & 7, kr = lane >> 3;
+  const int d0 = 8 * kl, d1 = 64 + 8 * kl;
+  const int L = G.L, t1 = G.t1, nb = G.nb, tw = G.tw, nsteps = G.nsteps;
+  auto load_step = [&](uint4 (&r)[4], int i) __attribute__((always_inline)) { kv_load_step(A, G, r, i); };
 
   float m[GROUP], l[GROUP], acc[GROUP][16];
 #pragma unroll
@@ -509,16 +502,17 @@ __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, co
   // Online softmax with a lazy reference: p = 2^(s - m) against a per-wave
   // reference m that moves only when some score passes it by more than 2^8
   // (a wave vote), so most steps skip the rescale of l and acc.
-  auto compute_step = [&](const uint4 (&r)[4], int i, bool with_new) {
+  auto compute_step = [&](const uint4 (&r)[4], int i, bool with_new) __attribute__((always_inline)) {
     const int t = tw + 32 * i + kr;
     const bool valid = t < t1;
     uint4 k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
     if (with_new) {
       const bool fresh = valid && t >= L;
       const int ni = fresh ? t - nb : 0;
+      // LDS-typed reads: a select between them and the registers stays a value select
       const uint16_t *kn = knew + ni * kHeadDim, *vn = vnew + ni * kHeadDim;
-      const uint4 a0 = *reinterpret_cast<const uint4 *>(kn + d0), a1 = *reinterpret_cast<const uint4 *>(kn + d1);
-      const uint4 b0 = *reinterpret_cast<const uint4 *>(vn + d0), b1 = *reinterpret_cast<const uint4 *>(vn + d1);
+      const uint4 a0 = lds_ld16(kn + d0), a1 = lds_ld16(kn + d1);
+      const uint4 b0 = lds_ld16(vn + d0), b1 = lds_ld16(vn + d1);
       if (fresh) {
         k0 = a0; k1 = a1; v0 = b0; v1 = b1;
       }
@@ -554,21 +548,31 @@ __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, co
       for (int e = 0; e < 16; ++e) acc[j][e] += p * vf[e];
     }
   };
-  if (n_new == 0) {
-    for (int i = 0; i < nsteps; i += 2) {
-      compute_step(ra, i, false);
+  // The NP steps loaded by the caller first; after them two steps in flight
+  // while one is computed.  No load is issued for a step past the item but the
+  // odd one of the last pair (an outstanding load would hold the barrier below).
+  auto run = [&](bool with_new) __attribute__((always_inline)) {
+    int i = 0;
+    if constexpr (NP == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < nsteps) compute_step(r[k], k, with_new);
+      if (nsteps <= 4) return;
+      i = 4;
+      load_step(ra, 4);
+      load_step(rb, 5);
+    }
+    for (; i + 2 < nsteps; i += 2) {
+      compute_step(ra, i, with_new);
       load_step(ra, i + 2);
-      compute_step(rb, i + 1, false);
+      compute_step(rb, i + 1, with_new);
       load_step(rb, i + 3);
     }
-  } else {
-    for (int i = 0; i < nsteps; i += 2) {
-      compute_step(ra, i, true);
-      load_step(ra, i + 2);
-      compute_step(rb, i + 1, true);
-      load_step(rb, i + 3);
-    }
-  }
+    if (i < nsteps) compute_step(ra, i, with_new);
+    if (i + 1 < nsteps) compute_step(rb, i + 1, with_new);
+  };
+  if (G.n_new == 0) run(false);
+  else run(true);
   // combine the 8 key groups of the wave (lanes with equal kl), then the waves
 #pragma unroll
   for (int j = 0; j < GROUP; ++j) {
@@ -604,93 +608,163 @@ __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, co
       a += sc * S.acc[w][j][d];
       ls += sc * S.l[w][j];
     }
-    // merged by another workgroup of this same dispatch: device-coherent stores
-    st_dev(pbase + j * kPartStride + d, a);
+    stx<COH>(pbase + j * kPartStride + d, a);
     if (d == 0) {
-      st_dev(pbase + j * kPartStride + 128, M);
-      st_dev(pbase + j * kPartStride + 129, ls);
+      stx<COH>(pbase + j * kPartStride + 128, M);
+      stx<COH>(pbase + j * kPartStride + 129, ls);
     }
   }
   __syncthreads();
 }
 
+// One item, its first two steps already loaded into P; its partial is merged by
+// another workgroup of this same dispatch.
+template <int DT, int GROUP, bool COH>
+__device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo, uint16_t *knew, uint16_t *vnew,
+                          AttnShared<GROUP> &S, const KVRegs &P) {
+  const int wave = wave_id(), lane = lane_id();
+  const int row = it.row, g = it.g;
+  const ItemGeom G = item_geom(A, it, rinfo);
+  const int L = G.L, r_off = G.r_off, nb = G.nb, n_new = G.n_new;
+  uint4 rr[2][4] = {{P.a0, P.a1, P.a2, P.a3}, {P.b0, P.b1, P.b2, P.b3}};
+
+  // Everything the item reads from this call's projection is loaded up front in
+  // one batch: its q heads, their norm partials, and for a chunk holding
+  // appended rows the k/v rows and k partials.
+  const uint32_t row_bytes = (uint32_t)A.nqkv * 4;
+  QLoads<GROUP> Q;
+  q_loads<GROUP>(A, row, g, Q);
+  // appended rows (positions nb .. t1-1 = rows nb - L .. of this sequence): wave w
+  // takes rows w, w + 4, ...; lane l holds dims 2l, 2l + 1
+  const int n_mine = n_new > wave ? (n_new - wave + 3) / 4 : 0;
+  for (int i0 = 0; i0 < n_mine; i0 += 2) {
+    float4 k4[2], v4[2], kp[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = wave + 4 * (i0 + u);
+      const int rrow = row - r_off + (nb + min(i, n_new - 1) - L);
+      const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)rrow * A.nqkv, row_bytes);
+      k4[u] = ld_dev4(Rr, ((A.nq + g) * kHeadDim + 2 * (lane & ~1)) * 4);
+      v4[u] = ld_dev4(Rr, ((A.nq + A.nkv + g) * kHeadDim + 2 * (lane & ~1)) * 4);
+      const __amdgpu_buffer_rsrc_t Pr = rsrc_of(A.ssq + (size_t)rrow * (A.nq + A.nkv) * kTilesPerHead,
+                                                (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4);
+      kp[u][0] = ld_dev4(Pr, (A.nq + g) * kTilesPerHead * 4);
+      kp[u][1] = ld_dev4(Pr, ((A.nq + g) * kTilesPerHead + 4) * 4);
+    }
+    const bool writer = (r_off == A.n - 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = wave + 4 * (i0 + u);
+      if (i >= n_new) break;
+      uint32_t kb, vb;
+      fresh_pair<DT>(A, k4[u], v4[u], kp[u][0], kp[u][1], kb, vb);
+      reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
+      reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
+      if (writer) {   // the item of the sequence's last row also stores them in the cache
+        const size_t off = (G.kvrow0 + nb + i) * kHeadDim;
+        reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
+        reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+      }
+    }
+  }
+  float q[GROUP][16];
+  q_scale<GROUP>(A, Q, q);
+  if (n_new > 0) __syncthreads();
+  attn_stream<DT, GROUP, true, 2>(A, G, row, g, it.c, q, knew, vnew, S, rr);
+}
+
 // ---------------------------------------------------------------- merge
 //
 // att[row][h] = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, M = max_c m_c,
-// over the chunks of (row, kv head g) in a fixed order that depends only on the
-// chunk count, never on which item finished first (deterministic).  The
-// last item of a (row, g) to finish does it: every item bumps a counter after
-// its partial is stored; the block that sees the count reach nch merges.  The
-// counter update of one item is resolved after the next item, so its latency
-// hides behind that item's work.
+// summed in chunk order (deterministic: never in the order the chunks
+// finished).  Both merge sites (the last item of a (row, g) within the
+// attention dispatch, or the o_proj kernel of the few-row path) run
+// merge_column on the same partials, so every dispatch mode gives the same bits.
+
+// Partial (m, l) and acc of chunk c of one float4 column: P(c, ml, av).
+// ml0/av0 hold chunks [0, CB), requested by the caller; later chunks are
+// requested here CB at a time.
+template <int CB, class P>
+__device__ __forceinline__ float4 merge_column(int nch, const float2 (&ml0)[CB], const float4 (&av0)[CB], P part) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+    if (c < nch) M = fmaxf(M, ml0[c].x);
+  for (int c0 = CB; c0 < nch; c0 += CB) {
+    float2 ml[CB];
+    float4 av;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) part(c0 + u, ml[u], av, false);
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (c0 + u < nch) M = fmaxf(M, ml[u].x);
+  }
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  auto add = [&](float2 ml, float4 av) __attribute__((always_inline)) {
+    const float w = exp2f(ml.x - M);
+    den += w * ml.y;
+    num.x += w * av.x;
+    num.y += w * av.y;
+    num.z += w * av.z;
+    num.w += w * av.w;
+  };
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+    if (c < nch) add(ml0[c], av0[c]);
+  for (int c0 = CB; c0 < nch; c0 += CB) {
+    float2 ml[CB];
+    float4 av[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) part(c0 + u, ml[u], av[u], true);
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (c0 + u < nch) add(ml[u], av[u]);
+  }
+  const float inv = 1.0f / den;
+  return make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+}
+
+// chunk partials of one column read device-coherently (stored by other
+// workgroups of this dispatch); past nch the buffer range reads zeros
+struct PartCoherent {
+  __amdgpu_buffer_rsrc_t R;
+  uint32_t cs, col;   // bytes per chunk, byte offset of the column
+  __device__ __forceinline__ void operator()(int c, float2 &ml, float4 &av, bool with_av) const {
+    const float4 v = ld_dev4(R, c * cs + 128 * 4);
+    ml = make_float2(v.x, v.y);
+    if (with_av) av = ld_dev4(R, c * cs + col);
+  }
+};
+
+// The last item of (row, g) to finish merges its GROUP heads: thread t <
+// GROUP * 32 takes float4 column t of the GROUP x 128 outputs.
 template <int DT, int GROUP, bool COH>
 __device__ void merge_group(const LayerArgs &A, int row, int g, int nch, AttnShared<GROUP> &S) {
-  // thread t: float4 column o4 = t % (GROUP * 32) of the GROUP x 128 outputs and
-  // chunks c = t / (GROUP * 32) + NCL * i.  The (m, l) pairs and the first 8 chunk
-  // vectors of every thread are requested in one batch; chunks past nch read
-  // zeros (outside the buffer range).
-  constexpr int NO4 = GROUP * 32, NCL = 256 / NO4, BATCH = 8;
-  const int t = threadIdx.x, o4 = t % NO4, cl = t / NO4, j = o4 / 32, d = (o4 % 32) * 4;
-  const float *p0 = A.part + (((size_t)row * A.nkv + g) * kMaxChunks * GROUP) * kPartStride;
-  const uint32_t cs = (uint32_t)GROUP * kPartStride * 4;                 // bytes per chunk
-  const __amdgpu_buffer_rsrc_t R = rsrc_of(p0, (uint32_t)nch * cs);
-  for (int idx = t; idx < GROUP * kMaxChunks; idx += 256) {
-    const int mj = idx / kMaxChunks, mc = idx % kMaxChunks;
-    const float4 v = ld_dev4(R, mc * cs + (mj * kPartStride + 128) * 4);   // m, l (zeros past nch)
-    S.mc[mj][mc] = mc < nch ? v.x : -INFINITY;
-    S.lc[mj][mc] = v.y;
-  }
-  float4 v[BATCH];
+  constexpr int CB = 8;
+  const int t = threadIdx.x;
+  if (t < GROUP * 32) {
+    const int j = t / 32, d = (t % 32) * 4;
+    const float *p0 = A.part + ((((size_t)row * A.nkv + g) * kMaxChunks) * GROUP + j) * kPartStride;
+    const uint32_t cs = (uint32_t)GROUP * kPartStride * 4;
+    const PartCoherent P{rsrc_of(p0, (uint32_t)nch * cs), cs, (uint32_t)d * 4};
+    float2 ml[CB];
+    float4 av[CB];
 #pragma unroll
-  for (int u = 0; u < BATCH; ++u) v[u] = ld_dev4(R, (cl + NCL * u) * cs + (j * kPartStride + d) * 4);
-  __syncthreads();
-  for (int jj = wave_id(); jj < GROUP; jj += 4) {
-    const int lane = lane_id();
-    const float m = S.mc[jj][lane];
-    const float M = wave_max(m);
-    const float w = lane < nch ? exp2f(m - M) : 0.f;
-    const float tot = wave_sum(w * S.lc[jj][lane]);
-    S.w[jj][lane] = w / tot;
-  }
-  __syncthreads();
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0;; i0 += BATCH) {
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int c = cl + NCL * (i0 + u);
-      const float w = c < nch ? S.w[j][c] : 0.f;
-      a.x += w * v[u].x;
-      a.y += w * v[u].y;
-      a.z += w * v[u].z;
-      a.w += w * v[u].w;
-    }
-    if (cl + NCL * (i0 + BATCH) >= nch) break;
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) v[u] = ld_dev4(R, (cl + NCL * (i0 + BATCH + u)) * cs + (j * kPartStride + d) * 4);
-  }
-  // the NCL chunk classes of a column meet in LDS
-  S.red[cl * NO4 + o4] = a;
-  __syncthreads();
-  if (cl == 0) {
-    for (int k = 1; k < NCL; ++k) {
-      const float4 b = S.red[k * NO4 + o4];
-      a.x += b.x;
-      a.y += b.y;
-      a.z += b.z;
-      a.w += b.w;
-    }
+    for (int u = 0; u < CB; ++u) P(u, ml[u], av[u], true);
+    const float4 o = merge_column<CB>(nch, ml, av, P);
     const size_t col = (size_t)(g * GROUP + j) * kHeadDim + d;
-    const float av[4] = {a.x, a.y, a.z, a.w};
+    const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) stx<COH>(A.att + (size_t)row * A.nq * kHeadDim + col + e, av[e]);
+    for (int e = 0; e < 4; ++e) stx<COH>(A.att + (size_t)row * A.nq * kHeadDim + col + e, ov[e]);
     if (A.mfma) {   // tiled [plane][col / 32][row][32]: one MFMA operand load reads 1 KB contiguously
       const size_t plane = (size_t)(A.nq * kHeadDim / 32) * A.rows * 32;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const size_t idx = (((col + e) / 32) * A.rows + row) * 32 + (col + e) % 32;
-        const uint16_t hi = rne16<DT>(av[e]);
+        const uint16_t hi = rne16<DT>(ov[e]);
         A.att_hl[idx] = hi;
-        A.att_hl[plane + idx] = rne16<DT>(av[e] - cvt16<DT>(hi));
+        A.att_hl[plane + idx] = rne16<DT>(ov[e] - cvt16<DT>(hi));
       }
     }
   }
@@ -837,24 +911,22 @@ __device__ __forceinline__ uint4 round8(float4 a, float4 b) {
   return u;
 }
 
-// lane-pair exchange across lanes l ^ MASK
-template <int MASK>
-__device__ __forceinline__ float xswap(float v) {
-  if constexpr (MASK == 8) return dpp<0x128>(v);   // row_ror:8 within 16-lane rows
-  else return __shfl_xor(v, MASK, kWave);
-}
-
 // Reduce-scatter over the lanes l ^ MASK: lanes with the MASK bit clear keep
 // the low half of the values, the others the high half, each summed with its
 // partner's copy.
 template <int N, int MASK>
 __device__ __forceinline__ void rs_half(const float (&in)[N], float (&out)[N / 2]) {
-  const bool hi = (lane_id() & MASK) != 0;
+  if constexpr (MASK == 8) {
+    const bool hi = (lane_id() & MASK) != 0;
 #pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    const float keep = hi ? in[N / 2 + i] : in[i];
-    const float send = hi ? in[i] : in[N / 2 + i];
-    out[i] = keep + xswap<MASK>(send);
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = hi ? in[N / 2 + i] : in[i];
+      const float send = hi ? in[i] : in[N / 2 + i];
+      out[i] = keep + dpp<0x128>(send);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) out[i] = swap_sum<MASK>(in[i], in[N / 2 + i]);
   }
 }
 
@@ -1018,9 +1090,9 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
       float x = l[j];
-      x += xswap<32>(x);
-      x += xswap<16>(x);
-      x += xswap<8>(x);
+      x = xsum<32>(x);
+      x = xsum<16>(x);
+      x = xsum<8>(x);
       lt[j] = x;
     }
     const int first = c.P / S;
@@ -1579,6 +1651,295 @@ __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   attention_phase<DT, GROUP, false>(A, pre, rinfo, knew, vnew, S, blockIdx.x, gridDim.x);
 }
 
+// ---------------------------------------------------------------- phase C for a few rows
+//
+// With a few rows (bs1 decode, short verify) the attention is a chain of
+// latencies, not a stream, so nothing in it waits for another workgroup.
+// Workgroup (row, g, c0) of a grid sized from the host's view of the lengths
+// (A.nch_host chunks per row) takes chunk c0 of (row, g), and every
+// nch_host-th after it should the device lengths exceed that view.  NW waves
+// share a chunk: wave w takes keys t0 + 8 (NW i + w) + (0..7) at step i, one
+// key row per group of 8 lanes.  The first NP steps of every wave, its q heads
+// and the appended rows it may see are requested at once, before the row's
+// length is known: the K/V rows are clamped into the cache, so the loads are in
+// bounds for any length, and keys found to be past the visible ones are
+// masked.  Wave w < n holds the sequence's appended row w (n <= 4 here).
+// Softmax over the loaded steps as one block: all scores, one maximum per
+// head, then the weights (steps past NP, if any, continue online).  The waves'
+// sums are reduce-scattered over their key groups, combined in LDS, and the
+// partial (m, l, acc) is the output; the o_proj kernel merges the partials of
+// a row as it reads them (k_oproj_merge).
+template <int NW, int GROUP>
+struct FewShared {
+  float acc[NW][GROUP][kHeadDim];
+  float m[NW][GROUP], l[NW][GROUP];
+};
+
+struct FewGeom {
+  int L, t0, t1, nb, n_new, tw, nsteps, last_row;
+  size_t kvrow0;
+};
+
+template <int NW>
+__device__ __forceinline__ FewGeom few_geom(const LayerArgs &A, int slot, int g, int L, int nvis, int c) {
+  FewGeom G;
+  G.L = L;
+  G.t0 = c * A.split;
+  G.t1 = min(G.t0 + A.split, nvis);
+  G.nb = max(G.t0, L);
+  G.n_new = max(0, G.t1 - G.nb);
+  G.kvrow0 = ((size_t)slot * A.nkv + g) * A.capacity;
+  G.tw = G.t0 + wave_id() * 8;
+  G.nsteps = G.tw < G.t1 ? (G.t1 - G.tw + NW * 8 - 1) / (NW * 8) : 0;
+  G.last_row = max(min(G.t1, L) - 1, 0);
+  return G;
+}
+
+template <int NW>
+__device__ __forceinline__ void few_load_step(const LayerArgs &A, const FewGeom &G, uint4 (&r)[4], int i) {
+  const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + G.kvrow0 * kHeadDim, region);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + G.kvrow0 * kHeadDim, region);
+  const uint32_t off = (uint32_t)min(G.tw + NW * 8 * i + kr, G.last_row) * (kHeadDim * 2) + kl * 16;
+  r[0] = ld_buf(Kr, off);
+  r[1] = ld_buf(Kr, off + 128);
+  r[2] = ld_buf(Vr, off);
+  r[3] = ld_buf(Vr, off + 128);
+}
+
+template <int DT, int GROUP, int NW, int NP>
+__device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G, int row, int g, int c,
+                                           const float (&q)[GROUP][16], const uint16_t *knew, const uint16_t *vnew,
+                                           FewShared<NW, GROUP> &S, uint4 (&r)[NP][4]) {
+  static_assert(NP >= 2, "two register sets at least");
+  const int wave = wave_id(), lane = lane_id();
+  const int kl = lane & 7, kr = lane >> 3;
+  const int d0 = 8 * kl, d1 = 64 + 8 * kl;
+  const int nsteps = G.nsteps;
+  // K (h = 0) or V (h = 1) of step i as the cache holds it: appended keys from LDS, keys past the chunk zero
+  auto operand = [&](const uint4 (&rr)[4], int i, int h, bool with_new, uint4 &x0, uint4 &x1) __attribute__((always_inline)) {
+    const int t = G.tw + NW * 8 * i + kr;
+    const bool valid = t < G.t1;
+    x0 = rr[2 * h];
+    x1 = rr[2 * h + 1];
+    if (with_new) {
+      const bool fresh = valid && t >= G.L;
+      const uint16_t *src = (h == 0 ? knew : vnew) + (fresh ? t - G.nb : 0) * kHeadDim;
+      const uint4 a0 = lds_ld16(src + d0), a1 = lds_ld16(src + d1);
+      if (fresh) {
+        x0 = a0;
+        x1 = a1;
+      }
+    }
+    const uint32_t vm = valid ? 0xffffffffu : 0u;   // no stale inf/NaN bits
+    x0 = make_uint4(x0.x & vm, x0.y & vm, x0.z & vm, x0.w & vm);
+    x1 = make_uint4(x1.x & vm, x1.y & vm, x1.z & vm, x1.w & vm);
+    return valid;
+  };
+  auto score = [&](const uint4 (&rr)[4], int i, bool with_new, float (&s)[GROUP]) __attribute__((always_inline)) {
+    uint4 k0, k1;
+    const bool valid = operand(rr, i, 0, with_new, k0, k1);
+    float kf[16];
+    unpack8<DT>(k0, kf);
+    unpack8<DT>(k1, kf + 8);
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x += q[j][e] * kf[e];
+      x = sum8(x);
+      s[j] = valid ? x : -INFINITY;
+    }
+  };
+  float m[GROUP], l[GROUP], acc[GROUP][16];
+  auto weigh = [&](const uint4 (&rr)[4], int i, bool with_new, const float (&s)[GROUP]) __attribute__((always_inline)) {
+    uint4 v0, v1;
+    operand(rr, i, 1, with_new, v0, v1);
+    float vf[16];
+    unpack8<DT>(v0, vf);
+    unpack8<DT>(v1, vf + 8);
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      const float p = s[j] == -INFINITY ? 0.f : exp2f(s[j] - m[j]);
+      l[j] += p;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] += p * vf[e];
+    }
+  };
+  auto run = [&](bool with_new) __attribute__((always_inline)) {
+    // the NP loaded steps as one block
+    float sc[NP][GROUP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      if (k < nsteps) score(r[k], k, with_new, sc[k]);
+      else
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) sc[k][j] = -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      float x = sc[0][j];
+#pragma unroll
+      for (int k = 1; k < NP; ++k) x = fmaxf(x, sc[k][j]);
+      x = fmaxf(x, dpp<kRowMirror>(x));   // the two key groups of a 16-lane row, then the four rows
+      m[j] = fmaxf(fmaxf(readlane(x, 0), readlane(x, 16)), fmaxf(readlane(x, 32), readlane(x, 48)));
+      l[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+      if (k < nsteps) weigh(r[k], k, with_new, sc[k]);
+    // further steps (device lengths beyond the host's view): online, two in flight
+    if (nsteps > NP) {
+      uint4 (&ra)[4] = r[0];
+      uint4 (&rb)[4] = r[NP - 1];
+      few_load_step<NW>(A, G, ra, NP);
+      few_load_step<NW>(A, G, rb, NP + 1);
+      auto online = [&](const uint4 (&rr)[4], int i) __attribute__((always_inline)) {
+        float s[GROUP];
+        score(rr, i, with_new, s);
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) {
+          float x = fmaxf(s[j], dpp<kRowMirror>(s[j]));
+          x = fmaxf(fmaxf(readlane(x, 0), readlane(x, 16)), fmaxf(readlane(x, 32), readlane(x, 48)));
+          if (x > m[j]) {   // wave-uniform
+            const float corr = exp2f(m[j] - x);   // 0 while m = -inf
+            m[j] = x;
+            l[j] *= corr;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][e] *= corr;
+          }
+        }
+        weigh(rr, i, with_new, s);
+      };
+      int i = NP;
+      for (; i + 2 < nsteps; i += 2) {
+        online(ra, i);
+        few_load_step<NW>(A, G, ra, i + 2);
+        online(rb, i + 1);
+        few_load_step<NW>(A, G, rb, i + 3);
+      }
+      if (i < nsteps) online(ra, i);
+      if (i + 1 < nsteps) online(rb, i + 1);
+    }
+  };
+  if (G.n_new == 0) run(false);
+  else run(true);
+
+  // sum over the wave's 8 key groups: reduce-scatter over lane bits 5, 4, 3
+  constexpr int N = GROUP * 16;
+  float v1[N], v2[N / 2], v3[N / 4], v4[N / 8];
+#pragma unroll
+  for (int j = 0; j < GROUP; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v1[j * 16 + e] = acc[j][e];
+  rs_half<N, 32>(v1, v2);
+  rs_half<N / 2, 16>(v2, v3);
+  rs_half<N / 4, 8>(v3, v4);
+  const int base = ((lane >> 5) & 1) * (N / 2) + ((lane >> 4) & 1) * (N / 4) + ((lane >> 3) & 1) * (N / 8);
+#pragma unroll
+  for (int u = 0; u < N / 8; ++u) {
+    const int i = base + u, j = i / 16, e = i % 16;
+    S.acc[wave][j][e < 8 ? d0 + e : d1 + e - 8] = v4[u];
+  }
+#pragma unroll
+  for (int j = 0; j < GROUP; ++j) {
+    float x = l[j];
+    x = xsum<32>(x);
+    x = xsum<16>(x);
+    x = xsum<8>(x);
+    if (lane == 0) {
+      S.m[wave][j] = m[j];
+      S.l[wave][j] = x;
+    }
+  }
+  __syncthreads();
+  float *pbase = A.part + ((((size_t)row * A.nkv + g) * kMaxChunks + c) * GROUP) * kPartStride;
+  for (int idx = threadIdx.x; idx < GROUP * kHeadDim; idx += NW * kWave) {
+    const int j = idx / kHeadDim, d = idx % kHeadDim;
+    float M = S.m[0][j];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, S.m[w][j]);
+    float a = 0.f, ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = S.m[w][j] == -INFINITY ? 0.f : exp2f(S.m[w][j] - M);
+      a += sc * S.acc[w][j][d];
+      ls += sc * S.l[w][j];
+    }
+    pbase[j * kPartStride + d] = a;
+    if (d == 0) {
+      pbase[j * kPartStride + 128] = M;
+      pbase[j * kPartStride + 129] = ls;
+    }
+  }
+  __syncthreads();
+}
+
+template <int DT, int GROUP, int NW, int NP>
+__global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ FewShared<NW, GROUP> S;
+  uint16_t *knew = reinterpret_cast<uint16_t *>(dyn);
+  uint16_t *vnew = knew + A.n * kHeadDim;
+  const int C = A.nch_host;
+  const int row = blockIdx.x / (A.nkv * C), g = (blockIdx.x / C) % A.nkv, c0 = blockIdx.x % C;
+  const int wave = wave_id(), lane = lane_id();
+  const int b = row / A.n, r_off = row - b * A.n;
+  // the slot as far as the loads need it: a sequence's own without a slot
+  // table, else its entry clamped into the cache (rows of a bad slot are masked)
+  const int slot = A.slots ? min(max(A.slots[b], 0), A.batch_cap - 1) : b;
+  FewGeom G0 = few_geom<NW>(A, slot, g, A.capacity, A.capacity, c0);
+  G0.last_row = A.capacity - 1;
+  uint4 rr[NP][4];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) few_load_step<NW>(A, G0, rr[k], k);
+  QLoads<GROUP> Q;
+  q_loads<GROUP>(A, row, g, Q);
+  const bool has_fresh = wave <= r_off;   // sequence row `wave`, position L + wave, is visible to `row`
+  float4 fk = make_float4(0.f, 0.f, 0.f, 0.f), fv = fk, fp0 = fk, fp1 = fk;
+  if (has_fresh) {
+    const int rrow = b * A.n + wave;
+    const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)rrow * A.nqkv, (uint32_t)A.nqkv * 4);
+    fk = ld_dev4(Rr, ((A.nq + g) * kHeadDim + 2 * (lane & ~1)) * 4);
+    fv = ld_dev4(Rr, ((A.nq + A.nkv + g) * kHeadDim + 2 * (lane & ~1)) * 4);
+    const __amdgpu_buffer_rsrc_t Pr = rsrc_of(A.ssq + (size_t)rrow * (A.nq + A.nkv) * kTilesPerHead,
+                                              (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4);
+    fp0 = ld_dev4(Pr, (A.nq + g) * kTilesPerHead * 4);
+    fp1 = ld_dev4(Pr, ((A.nq + g) * kTilesPerHead + 4) * 4);
+  }
+  const RowInfo ri = row_info(A, row);
+  const int nch = chunks_of(ri.nvis, A.split);   // 0 for a row in error
+  if (c0 >= nch) return;                          // uniform over the workgroup
+  float q[GROUP][16];
+  q_scale<GROUP>(A, Q, q);
+  for (int c = c0; c < nch; c += C) {
+    const FewGeom G = few_geom<NW>(A, ri.slot, g, ri.L, ri.nvis, c);
+    if (c != c0) {
+#pragma unroll
+      for (int k = 0; k < NP; ++k) few_load_step<NW>(A, G, rr[k], k);
+    }
+    if (G.n_new > 0) {
+      const int i = ri.L + wave - G.nb;   // this wave's row among the chunk's appended ones
+      if (has_fresh && i >= 0 && i < G.n_new) {
+        uint32_t kb, vb;
+        fresh_pair<DT>(A, fk, fv, fp0, fp1, kb, vb);
+        reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
+        reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
+        if (r_off == A.n - 1) {   // the sequence's last row also stores them in the cache
+          const size_t off = (G.kvrow0 + ri.L + wave) * kHeadDim;
+          reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
+          reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+        }
+      }
+      __syncthreads();
+    }
+    few_stream<DT, GROUP, NW, NP>(A, G, row, g, c, q, knew, vnew, S, rr);
+  }
+}
+
 // many rows: equal key shares per wave of a resident grid
 template <int DT, int GROUP>
 __global__ __launch_bounds__(256) void k_attn_waves(LayerArgs A) {
@@ -1600,6 +1961,94 @@ __global__ __launch_bounds__(256) void k_oproj(LayerArgs A) {
   load_wo<KV, RPW>(A, blockIdx.x, wr);
   if (blockIdx.x == 0) advance_lengths<false>(A);
   oproj_tile<DT, KV, RB, RPW, false>(A, blockIdx.x, wr, nullptr);
+}
+
+// chunk partials of one column after the kernel boundary (plain loads); chunk
+// indices clamp to the last slot (its values are never weighted then)
+struct PartPlain {
+  const float *p;   // chunk 0 of the column's head
+  int cs, col;      // floats per chunk, float offset of the column
+  __device__ __forceinline__ void operator()(int c, float2 &ml, float4 &av, bool with_av) const {
+    const float *pc = p + (size_t)min(c, kMaxChunks - 1) * cs;
+    ml = *reinterpret_cast<const float2 *>(pc + 128);
+    if (with_av) av = *reinterpret_cast<const float4 *>(pc + col);
+  }
+};
+
+// o_proj for a few rows, merging the attention partials on the way in:
+// att[row][h] = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c over the chunks
+// of (row, h) in chunk order, M the largest m_c (deterministic).  Every
+// workgroup merges all rows into LDS: thread t takes the float4 columns t,
+// t + 256, ... of the attention output; the partials of the first CB chunks
+// are requested with the W_o rows and the row table, before the row's chunk
+// count is known, and the chunks past it are skipped (never weighted: their
+// slots hold an older call's values).
+template <int DT, int KV, int RPW, int CB>
+__global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  float *xs = reinterpret_cast<float *>(dyn);   // [rows][nq d]
+  constexpr int NS = (KV + 1) / 2;              // float4 columns per thread (nq d = 512 KV)
+  const int K = A.nq * kHeadDim, K4 = K / 4;
+  uint4 wr[RPW][KV];
+  load_wo<KV, RPW>(A, blockIdx.x, wr);
+  if (blockIdx.x == 0) advance_lengths<false>(A);
+  const int t = threadIdx.x;
+  for (int row = 0; row < A.rows; ++row) {
+    const int4 rt = A.rowtab[row];
+    const float *prow = A.part + (size_t)row * A.nkv * kMaxChunks * A.group * kPartStride;
+    float2 ml[NS][CB];
+    float4 av[NS][CB];
+    PartPlain P[NS];
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int q4 = min(t + 256 * s2, K4 - 1);
+      const int h = q4 / 32, g = h / A.group, j = h - g * A.group;
+      P[s2] = PartPlain{prow + ((size_t)g * kMaxChunks * A.group + j) * kPartStride, A.group * kPartStride, (q4 % 32) * 4};
+#pragma unroll
+      for (int c = 0; c < CB; ++c) P[s2](c, ml[s2][c], av[s2][c], true);
+    }
+    const int nch = chunks_of(rt.x ? rt.y + row % A.n + 1 : 0, A.split);
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int q4 = t + 256 * s2;
+      const float4 o = merge_column<CB>(nch, ml[s2], av[s2], P[s2]);
+      if (q4 < K4) reinterpret_cast<float4 *>(xs + (size_t)row * K)[q4] = o;
+    }
+  }
+  __syncthreads();
+  const int wave = wave_id(), lane = lane_id();
+  const int o0 = (blockIdx.x * 4 + wave) * RPW;
+  for (int row = 0; row < A.rows; ++row) {
+    float acc[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const float4 *xp = reinterpret_cast<const float4 *>(xs + (size_t)row * K + (v * 64 + lane) * 8);
+      const float4 f0 = xp[0], f1 = xp[1];
+      const float x8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        float wf[8];
+        unpack8<DT>(wr[i][v], wf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i] += wf[e] * x8[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) acc[i] = wave_sum(acc[i]);
+    if (lane < RPW) {
+      float val = acc[0];
+#pragma unroll
+      for (int i = 1; i < RPW; ++i)
+        if (lane == i) val = acc[i];
+      const size_t o = (size_t)row * A.H + o0 + lane;
+      if (A.residual) val += cvt16<DT>(A.residual[o]);
+      if (!A.rowtab[row].x) val = __builtin_nanf("");
+      if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
+      else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
+    }
+  }
 }
 
 // lengths advance once every workgroup has read them (rows from LDS)
@@ -1796,6 +2245,39 @@ LayerKernel pick_attn(int group) {
 }
 
 template <int DT>
+LayerKernel pick_attn_few(int group) {
+  // eight waves (two per SIMD) while the registers of a group allow, else four;
+  // two steps of every wave requested before any arithmetic
+  switch (group) {
+    case 1: return k_attn_few<DT, 1, 8, 2>;
+    case 2: return k_attn_few<DT, 2, 8, 2>;
+    case 4: return k_attn_few<DT, 4, 4, 2>;
+    case 8: return k_attn_few<DT, 8, 4, 2>;
+    default: return nullptr;
+  }
+}
+
+int few_waves(int group) { return group <= 2 ? 8 : 4; }
+
+// the partials of as many chunks as the host expects (4, 8, or 16 while two
+// float4 columns per thread keep that within registers) requested at once
+template <int DT>
+LayerKernel pick_oproj_merge(int kvo, int nch_host) {
+  const int cb = nch_host <= 4 ? 4 : (nch_host > 8 && kvo <= 4 ? 16 : 8);
+  switch (kvo) {
+#define ASR_PICK_OPROJ_MERGE(K) \
+    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4> : cb == 16 ? k_oproj_merge<DT, K, kRpwD, 16> : k_oproj_merge<DT, K, kRpwD, 8>;
+#define ASR_PICK_OPROJ_MERGE8(K) \
+    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4> : k_oproj_merge<DT, K, kRpwD, 8>;
+    ASR_PICK_OPROJ_MERGE(1) ASR_PICK_OPROJ_MERGE(2) ASR_PICK_OPROJ_MERGE(3) ASR_PICK_OPROJ_MERGE(4)
+    ASR_PICK_OPROJ_MERGE8(5) ASR_PICK_OPROJ_MERGE8(6) ASR_PICK_OPROJ_MERGE8(7) ASR_PICK_OPROJ_MERGE8(8)
+#undef ASR_PICK_OPROJ_MERGE
+#undef ASR_PICK_OPROJ_MERGE8
+    default: return nullptr;
+  }
+}
+
+template <int DT>
 LayerKernel pick_attn_waves(int group) {
   switch (group) {
     case 2: return k_attn_waves<DT, 2>;
@@ -1841,6 +2323,16 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
     if ((e = launch_phase(pick_qkv<DT>(a.H / 512, a.rows == 1), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, ev,
                           0, a)) != hipSuccess)
       return e;
+  }
+  if (!a.mfma) {
+    // a few rows: partials only, merged by the o_proj kernel
+    const unsigned lds_kv = (unsigned)(a.n * kHeadDim * 2 * sizeof(uint16_t));
+    if ((e = launch_phase(pick_attn_few<DT>(a.group), dim3(a.rows * a.nkv * a.nch_host), dim3(few_waves(a.group) * kWave),
+                          lds_kv, s, ev, 1, a)) != hipSuccess)
+      return e;
+    const unsigned lds_x = (unsigned)(a.rows * a.nq * kHeadDim * sizeof(float));
+    return launch_phase(pick_oproj_merge<DT>(a.nq * kHeadDim / 512, a.nch_host), dim3(a.H / (4 * kRpwD)), dim3(256),
+                        lds_x, s, ev, 2, a);
   }
   if (attn_waves_used(a)) {
     if ((e = launch_phase(pick_attn_waves<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,

@@ -185,12 +185,38 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<kRowMirror>(v));
   return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
 }
+// Lane swaps of gfx950 (VALU, no LDS round trip).  permlane32_swap(a, b)
+// returns (a[0..31] b[0..31], a[32..63] b[32..63]); permlane16_swap(a, b)
+// returns (rows a0 b0 a2 b2, rows a1 b1 a3 b3) for 16-lane rows.  With
+// (a, b) = (low value, high value) of every lane, the sum of the two results
+// holds, in lanes with the MASK bit clear, low + low of lane l ^ MASK, and in
+// the others high + high of lane l ^ MASK.
+template <int MASK>
+__device__ __forceinline__ float swap_sum(float lo, float hi) {
+  static_assert(MASK == 16 || MASK == 32, "lane masks 16 and 32");
+  const unsigned a = __builtin_bit_cast(unsigned, lo), b = __builtin_bit_cast(unsigned, hi);
+  if constexpr (MASK == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+}
+
+// v plus v of lane l ^ MASK, in every lane
+template <int MASK>
+__device__ __forceinline__ float xsum(float v) {
+  if constexpr (MASK == 8) return v + dpp<0x128>(v);   // row_ror:8 within 16-lane rows
+  else return swap_sum<MASK>(v, v);
+}
+
 // sum over the 8 lanes {l & 7, (l & 7) + 8, ..., (l & 7) + 56}; the total lands in the
 // lanes 8..15 of every 16-lane row (row_shr:8 adds lane i - 8 to lane i within a row)
 __device__ __forceinline__ float sum_stride8(float v) {
   v += dpp<0x118>(v);
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
+  v = xsum<16>(v);
+  v = xsum<32>(v);
   return v;
 }
 

@@ -51,6 +51,7 @@ struct LayerArgs {
   int H, nq, nkv, group, nqkv;
   int batch_cap, capacity;
   int split;                  // keys per chunk (few rows); least keys per wave share (many rows)
+  int nch_host;               // chunks per row the launch was sized for (few rows)
   float eps, theta;
   int out_f32;
   int mfma;                   // projections on MFMA (more than a few rows)

@@ -359,6 +359,10 @@ __device__ __forceinline__ uint4 lds_ld16(const uint16_t *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 2^x for the softmax weights (x <= 0 or -inf): the hardware exponential;
+// results below 2^-126 flush to zero
+__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
+
 constexpr float kRescaleLog2 = 8.f;   // lazy softmax rescale: keep exp2(s - m) <= 2^8
 
 // Where an item's keys are: chunk [t0, t1) of the row's visible keys, of which
@@ -536,13 +540,13 @@ __device__ __forceinline__ void attn_stream(const LayerArgs &A, const ItemGeom &
         float smax = fmaxf(s, dpp<kRowMirror>(s));
         smax = fmaxf(fmaxf(readlane(smax, 0), readlane(smax, 16)), fmaxf(readlane(smax, 32), readlane(smax, 48)));
         const float mn = fmaxf(m[j], smax);
-        const float corr = exp2f(m[j] - mn);   // 0 on the first step (m = -inf)
+        const float corr = exp2_neg(m[j] - mn);   // 0 on the first step (m = -inf)
         m[j] = mn;
         l[j] *= corr;
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[j][e] *= corr;
       }
-      const float p = valid ? exp2f(s - m[j]) : 0.f;
+      const float p = valid ? exp2_neg(s - m[j]) : 0.f;
       l[j] += p;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][e] += p * vf[e];
@@ -604,7 +608,7 @@ __device__ __forceinline__ void attn_stream(const LayerArgs &A, const ItemGeom &
     for (int w = 1; w < 4; ++w) M = fmaxf(M, S.m[w][j]);
     float a = 0.f, ls = 0.f;
     for (int w = 0; w < 4; ++w) {
-      const float sc = S.m[w][j] == -INFINITY ? 0.f : exp2f(S.m[w][j] - M);
+      const float sc = S.m[w][j] == -INFINITY ? 0.f : exp2_neg(S.m[w][j] - M);
       a += sc * S.acc[w][j][d];
       ls += sc * S.l[w][j];
     }
@@ -686,40 +690,47 @@ __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, co
 // requested here CB at a time.
 template <int CB, class P>
 __device__ __forceinline__ float4 merge_column(int nch, const float2 (&ml0)[CB], const float4 (&av0)[CB], P part) {
-  float M = -INFINITY;
+  // chunks past nch weigh nothing, by selects rather than branches (their slots
+  // may hold an older call's values), so the terms of a batch schedule freely
+  auto batch_max = [&](const float2 (&ml)[CB], int c0) __attribute__((always_inline)) {
+    float x[CB];
 #pragma unroll
-  for (int c = 0; c < CB; ++c)
-    if (c < nch) M = fmaxf(M, ml0[c].x);
+    for (int c = 0; c < CB; ++c) x[c] = c0 + c < nch ? ml[c].x : -INFINITY;
+#pragma unroll
+    for (int w = 1; w < CB; w *= 2)
+#pragma unroll
+      for (int c = 0; c + w < CB; c += 2 * w) x[c] = fmaxf(x[c], x[c + w]);
+    return x[0];
+  };
+  float M = batch_max(ml0, 0);
   for (int c0 = CB; c0 < nch; c0 += CB) {
     float2 ml[CB];
     float4 av;
 #pragma unroll
     for (int u = 0; u < CB; ++u) part(c0 + u, ml[u], av, false);
-#pragma unroll
-    for (int u = 0; u < CB; ++u)
-      if (c0 + u < nch) M = fmaxf(M, ml[u].x);
+    M = fmaxf(M, batch_max(ml, c0));
   }
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
-  auto add = [&](float2 ml, float4 av) __attribute__((always_inline)) {
-    const float w = exp2f(ml.x - M);
-    den += w * ml.y;
-    num.x += w * av.x;
-    num.y += w * av.y;
-    num.z += w * av.z;
-    num.w += w * av.w;
+  auto add = [&](float2 ml, float4 av, bool ok) __attribute__((always_inline)) {
+    const float w = ok ? exp2_neg(ml.x - M) : 0.f;
+    const float l = ok ? ml.y : 0.f;
+    const float4 a = ok ? av : make_float4(0.f, 0.f, 0.f, 0.f);
+    den += w * l;
+    num.x += w * a.x;
+    num.y += w * a.y;
+    num.z += w * a.z;
+    num.w += w * a.w;
   };
 #pragma unroll
-  for (int c = 0; c < CB; ++c)
-    if (c < nch) add(ml0[c], av0[c]);
+  for (int c = 0; c < CB; ++c) add(ml0[c], av0[c], c < nch);
   for (int c0 = CB; c0 < nch; c0 += CB) {
     float2 ml[CB];
     float4 av[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) part(c0 + u, ml[u], av[u], true);
 #pragma unroll
-    for (int u = 0; u < CB; ++u)
-      if (c0 + u < nch) add(ml[u], av[u]);
+    for (int u = 0; u < CB; ++u) add(ml[u], av[u], c0 + u < nch);
   }
   const float inv = 1.0f / den;
   return make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
@@ -952,7 +963,7 @@ __device__ void merge_wave(const LayerArgs &A, int row, int g, int np) {
     const float4 ml = ld_dev4(R, lane * cs + (j * kPartStride + 128) * 4);   // zeros past np
     const float m = lane < np ? ml.x : -INFINITY;
     const float M = wave_max(m);
-    const float w = (lane < np && m != -INFINITY) ? exp2f(m - M) : 0.f;
+    const float w = (lane < np && m != -INFINITY) ? exp2_neg(m - M) : 0.f;
     const float tot = wave_sum(w * ml.y);
     wn[j] = w / tot;
   }
@@ -1181,13 +1192,13 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
         float smax = fmaxf(s, dpp<kRowMirror>(s));
         smax = fmaxf(fmaxf(readlane(smax, 0), readlane(smax, 16)), fmaxf(readlane(smax, 32), readlane(smax, 48)));
         const float mn = fmaxf(m[j], smax);
-        const float corr = exp2f(m[j] - mn);
+        const float corr = exp2_neg(m[j] - mn);
         m[j] = mn;
         l[j] *= corr;
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[j][e] *= corr;
       }
-      const float p = valid ? exp2f(s - m[j]) : 0.f;
+      const float p = valid ? exp2_neg(s - m[j]) : 0.f;
       l[j] += p;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][e] += p * vf[e];
@@ -1432,11 +1443,12 @@ constexpr int chunk_steps(int kq) {
 // row tiles share each split weight step); the 16 features are 8 rotary pairs
 // (t, t + 64) of one head, as in the vector path, with the same epilogue: gain
 // and rotation of q/k pairs, partial sums of squares, v stored raw.
-template <int DT, int KQ>
-__global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
-  constexpr int KC = KQ < 8 ? KQ : 8;   // steps per operand batch (x of four row tiles)
-  __shared__ f32x4_t s_c[4][4][kWave];
-  __shared__ float s_ss[4][64];
+template <int DT, int KQ, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
+  constexpr int KW = KQ * 4 / NWV;      // 32-wide steps of this wave's share of the contraction
+  constexpr int KC = KW < 8 ? KW : 8;   // steps per operand batch (x of four row tiles)
+  __shared__ f32x4_t s_c[NWV][4][kWave];
+  __shared__ float s_ss[NWV][64];
   __shared__ float2 s_rope[64][8];   // (cos, sin) for the block's 64 rows x its 8 rotary pairs
   const int wave = wave_id(), lane = lane_id();
   const int rtiles = (A.rows + 63) / 64;
@@ -1446,7 +1458,7 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
   const int i16 = lane % 16, g4 = lane / 16;
   const int arow = head * kHeadDim + (i16 < 8 ? t0 + i16 : 64 + t0 + i16 - 8);
   const int H = A.H;
-  const int kq0 = wave * (H / 4) + g4 * 8;       // this lane's first k
+  const int kq0 = wave * (H / NWV) + g4 * 8;     // this lane's first k
   const uint16_t *wp = A.w_qkv + (size_t)arow * H + kq0;
   const uint16_t *xr[4];
 #pragma unroll
@@ -1454,6 +1466,12 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
   if (blockIdx.x == 0) write_row_table<false>(A);
   const bool rot = head < A.nq + A.nkv;
   const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;
+  // the q/k norm gains of this lane's four outputs, requested ahead of the operands
+  float gq4[4] = {1.f, 1.f, 1.f, 1.f};
+  if (rot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gq4[j] = cvt16<DT>(gp[t0 + (g4 & 1) * 4 + j + (g4 < 2 ? 0 : 64)]);
+  }
 
   f32x4_t acc[4];
   float ss[4];
@@ -1463,7 +1481,7 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
     ss[nt] = 0.f;
   }
 #pragma unroll 1
-  for (int c0 = 0; c0 < KQ; c0 += KC) {
+  for (int c0 = 0; c0 < KW; c0 += KC) {
     uint4 w[KC], g[KC], x[4][KC];
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
@@ -1474,7 +1492,7 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
     if (c0 == 0 && rot) {   // rotary angles of the 64 rows x 8 pairs in fp64 while the operands travel
-      for (int idx = threadIdx.x; idx < 64 * 8; idx += 256) {
+      for (int idx = threadIdx.x; idx < 64 * 8; idx += NWV * 64) {
         const int r = idx / 8, tt = idx % 8;
         const int n = nb + r;
         float cs = 1.f, sn = 0.f;
@@ -1514,21 +1532,22 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
   for (int nt = 0; nt < 4; ++nt) {
     s_c[wave][nt][lane] = acc[nt];
     float v = ss[nt];
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
+    v = xsum<16>(v);
+    v = xsum<32>(v);
     if (g4 == 0) s_ss[wave][nt * 16 + i16] = v;
   }
   __syncthreads();
-  {
+  if (wave < 4) {   // wave nt finishes row tile nt
     const int nt = wave;
     const int n = nb + nt * 16 + i16;
     f32x4_t c = s_c[0][nt][lane];
+    float ssx = s_ss[0][nt * 16 + i16];
 #pragma unroll
-    for (int wv = 1; wv < 4; ++wv) {
+    for (int wv = 1; wv < NWV; ++wv) {
       const f32x4_t d = s_c[wv][nt][lane];
       c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
+      ssx += s_ss[wv][nt * 16 + i16];
     }
-    const float ssx = s_ss[0][nt * 16 + i16] + s_ss[1][nt * 16 + i16] + s_ss[2][nt * 16 + i16] + s_ss[3][nt * 16 + i16];
     const float inv = 1.0f / sqrtf(ssx / (float)H + A.eps);
     const bool first = g4 < 2;
     float raw[4], out[4];
@@ -1538,15 +1557,14 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
       raw[j] = c[j] * inv;
       sq += raw[j] * raw[j];
     }
-    sq += __shfl_xor(sq, 16, kWave);
-    sq += __shfl_xor(sq, 32, kWave);
+    sq = xsum<16>(sq);
+    sq = xsum<32>(sq);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tt = (g4 & 1) * 4 + j;
-      const int t = t0 + tt;
       if (rot) {
-        const float u = cvt16<DT>(gp[first ? t : t + 64]) * raw[j];
-        const float up = __shfl_xor(u, 32, kWave);
+        const float u = gq4[j] * raw[j];
+        const float up = xpartner32(u);
         const float2 cs = s_rope[nt * 16 + i16][tt];
         out[j] = first ? u * cs.x - up * cs.y : u * cs.x + up * cs.y;
       } else {
@@ -1554,11 +1572,9 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
       }
     }
     if (n < A.rows) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t0 + (g4 & 1) * 4 + j;
-        A.qkv[(size_t)n * A.nqkv + head * kHeadDim + (first ? t : t + 64)] = out[j];
-      }
+      const int t = t0 + (g4 & 1) * 4;   // four consecutive outputs: one 16-byte store
+      *reinterpret_cast<float4 *>(A.qkv + (size_t)n * A.nqkv + head * kHeadDim + (first ? t : t + 64)) =
+          make_float4(out[0], out[1], out[2], out[3]);
       if (rot && g4 == 0) A.ssq[((size_t)n * (A.nq + A.nkv) + head) * kTilesPerHead + jj] = sq;
     }
   }
@@ -1566,26 +1582,38 @@ __global__ __launch_bounds__(256) void k_qkv_mfma(LayerArgs A) {
 
 // o_proj: out[n][o] = sum_c W_o[o][c] att[n][c] (+ residual), att as hi + lo terms
 // read from its tiled copy [plane][c / 32][row][32].
-template <int DT, int KQ>
-__global__ __launch_bounds__(256) void k_oproj_mfma(LayerArgs A) {
-  constexpr int KC = chunk_steps(KQ);
-  __shared__ f32x4_t s_c[4][kWave];
+template <int DT, int KQ, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_oproj_mfma(LayerArgs A) {
+  constexpr int KW = KQ * 4 / NWV;   // 32-wide steps of this wave's share of the contraction
+  constexpr int KC = chunk_steps(KW);
+  __shared__ f32x4_t s_c[NWV][kWave];
   const int wave = wave_id(), lane = lane_id();
   const int i16 = lane % 16, g4 = lane / 16;
   const int K = A.nq * kHeadDim;
   const int rtiles = (A.rows + 15) / 16;
   const TileMap tm = tile_of(blockIdx.x, rtiles);
   const int o0 = tm.col * 16, nb = tm.row * 16;
-  const int kq0 = wave * (K / 4) + g4 * 8;
+  const int kq0 = wave * (K / NWV) + g4 * 8;
   const uint16_t *wp = A.w_o + (size_t)(o0 + i16) * K + kq0;
   const size_t plane = (size_t)(K / 32) * A.rows * 32;
   const size_t kstep = (size_t)A.rows * 32;   // next 32-wide block of the contraction
-  const uint16_t *bp = A.att_hl + ((size_t)(wave * (K / 128)) * A.rows + min(nb + i16, A.rows - 1)) * 32 + g4 * 8;
+  const uint16_t *bp = A.att_hl + ((size_t)(wave * (K / (32 * NWV))) * A.rows + min(nb + i16, A.rows - 1)) * 32 + g4 * 8;
+  // what the epilogue reads besides the products, requested first (wave 0 writes the tile)
+  const int n_out = nb + i16;
+  bool row_ok = false;
+  float res4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (wave == 0 && n_out < A.rows) {
+    row_ok = A.rowtab[n_out].x != 0;
+    if (A.residual) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) res4[j] = cvt16<DT>(A.residual[(size_t)n_out * A.H + o0 + g4 * 4 + j]);
+    }
+  }
   if (blockIdx.x == 0) advance_lengths<false>(A);
 
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-  for (int c0 = 0; c0 < KQ; c0 += KC) {
+  for (int c0 = 0; c0 < KW; c0 += KC) {
     uint4 w[KC], hi[KC], lo[KC];
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
@@ -1606,18 +1634,17 @@ __global__ __launch_bounds__(256) void k_oproj_mfma(LayerArgs A) {
     const int n = nb + i16;
     f32x4_t c = s_c[0][lane];
 #pragma unroll
-    for (int wv = 1; wv < 4; ++wv) {
+    for (int wv = 1; wv < NWV; ++wv) {
       const f32x4_t d = s_c[wv][lane];
       c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
     }
     if (n < A.rows) {
-      const bool ok = A.rowtab[n].x;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const size_t o = (size_t)n * A.H + o0 + g4 * 4 + j;
         float val = c[j];
-        if (A.residual) val += cvt16<DT>(A.residual[o]);
-        if (!ok) val = __builtin_nanf("");
+        if (A.residual) val += res4[j];
+        if (!row_ok) val = __builtin_nanf("");
         if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
         else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
       }
@@ -1761,7 +1788,7 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
     unpack8<DT>(v1, vf + 8);
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
-      const float p = s[j] == -INFINITY ? 0.f : exp2f(s[j] - m[j]);
+      const float p = s[j] == -INFINITY ? 0.f : exp2_neg(s[j] - m[j]);
       l[j] += p;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][e] += p * vf[e];
@@ -1805,7 +1832,7 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
           float x = fmaxf(s[j], dpp<kRowMirror>(s[j]));
           x = fmaxf(fmaxf(readlane(x, 0), readlane(x, 16)), fmaxf(readlane(x, 32), readlane(x, 48)));
           if (x > m[j]) {   // wave-uniform
-            const float corr = exp2f(m[j] - x);   // 0 while m = -inf
+            const float corr = exp2_neg(m[j] - x);   // 0 while m = -inf
             m[j] = x;
             l[j] *= corr;
 #pragma unroll
@@ -1865,7 +1892,7 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
     float a = 0.f, ls = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float sc = S.m[w][j] == -INFINITY ? 0.f : exp2f(S.m[w][j] - M);
+      const float sc = S.m[w][j] == -INFINITY ? 0.f : exp2_neg(S.m[w][j] - M);
       a += sc * S.acc[w][j][d];
       ls += sc * S.l[w][j];
     }
@@ -2203,17 +2230,21 @@ hipError_t launch_phase(LayerKernel kern, dim3 grid, dim3 block, unsigned lds, h
   return hipGetLastError();
 }
 
+// eight waves (two per SIMD: twice the loads in flight per CU) while a wave's
+// operand batch fits its registers, else four
+int qkv_mfma_waves(int kq) { return kq <= 16 ? 8 : 4; }
+
 template <int DT>
 LayerKernel pick_qkv_mfma(int kq) {
   switch (kq) {
-    case 4: return k_qkv_mfma<DT, 4>;
-    case 8: return k_qkv_mfma<DT, 8>;
-    case 12: return k_qkv_mfma<DT, 12>;
-    case 16: return k_qkv_mfma<DT, 16>;
-    case 20: return k_qkv_mfma<DT, 20>;
-    case 24: return k_qkv_mfma<DT, 24>;
-    case 28: return k_qkv_mfma<DT, 28>;
-    case 32: return k_qkv_mfma<DT, 32>;
+    case 4: return k_qkv_mfma<DT, 4, 8>;
+    case 8: return k_qkv_mfma<DT, 8, 8>;
+    case 12: return k_qkv_mfma<DT, 12, 8>;
+    case 16: return k_qkv_mfma<DT, 16, 8>;
+    case 20: return k_qkv_mfma<DT, 20, 4>;
+    case 24: return k_qkv_mfma<DT, 24, 4>;
+    case 28: return k_qkv_mfma<DT, 28, 4>;
+    case 32: return k_qkv_mfma<DT, 32, 4>;
     default: return nullptr;
   }
 }
@@ -2221,14 +2252,14 @@ LayerKernel pick_qkv_mfma(int kq) {
 template <int DT>
 LayerKernel pick_oproj_mfma(int kq) {
   switch (kq) {
-    case 4: return k_oproj_mfma<DT, 4>;
-    case 8: return k_oproj_mfma<DT, 8>;
-    case 12: return k_oproj_mfma<DT, 12>;
-    case 16: return k_oproj_mfma<DT, 16>;
-    case 20: return k_oproj_mfma<DT, 20>;
-    case 24: return k_oproj_mfma<DT, 24>;
-    case 28: return k_oproj_mfma<DT, 28>;
-    case 32: return k_oproj_mfma<DT, 32>;
+    case 4: return k_oproj_mfma<DT, 4, 8>;
+    case 8: return k_oproj_mfma<DT, 8, 8>;
+    case 12: return k_oproj_mfma<DT, 12, 8>;
+    case 16: return k_oproj_mfma<DT, 16, 8>;
+    case 20: return k_oproj_mfma<DT, 20, 8>;
+    case 24: return k_oproj_mfma<DT, 24, 8>;
+    case 28: return k_oproj_mfma<DT, 28, 8>;
+    case 32: return k_oproj_mfma<DT, 32, 8>;
     default: return nullptr;
   }
 }
@@ -2316,7 +2347,8 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
   if (a.mfma) {
     // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
     const int rtiles = (a.rows + 63) / 64;
-    if ((e = launch_phase(pick_qkv_mfma<DT>(a.H / 128), dim3(a.nqkv / 16 * rtiles), dim3(256), 0, s, ev, 0, a)) !=
+    if ((e = launch_phase(pick_qkv_mfma<DT>(a.H / 128), dim3(a.nqkv / 16 * rtiles), dim3(qkv_mfma_waves(a.H / 128) * kWave),
+                          0, s, ev, 0, a)) !=
         hipSuccess)
       return e;
   } else {
@@ -2343,7 +2375,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
     return e;
   }
   if (a.mfma)
-    return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 128), dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(256),
+    return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 128), dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(512),
                         0, s, ev, 2, a);
   return launch_phase(pick_oproj<DT>(a.nq * kHeadDim / 512, a.rows == 1), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s,
                       ev, 2, a);

@@ -204,6 +204,13 @@ __device__ __forceinline__ float swap_sum(float lo, float hi) {
   }
 }
 
+// v of lane l ^ 32 (the halves of the wave exchanged)
+__device__ __forceinline__ float xpartner32(float v) {
+  const unsigned a = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
+}
+
 // v plus v of lane l ^ MASK, in every lane
 template <int MASK>
 __device__ __forceinline__ float xsum(float v) {

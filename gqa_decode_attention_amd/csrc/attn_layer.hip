@@ -2002,45 +2002,108 @@ struct PartPlain {
   }
 };
 
+// max and sum over aligned groups of CB lanes (CB = 4, 8 or 16), result in all of them
+template <int CB>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v));
+  if constexpr (CB >= 8) v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  if constexpr (CB >= 16) v = fmaxf(v, dpp<kRowMirror>(v));
+  return v;
+}
+template <int CB>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<kQuadSwap1>(v);
+  v += dpp<kQuadSwap2>(v);
+  if constexpr (CB >= 8) v += dpp<kRowHalfMirror>(v);
+  if constexpr (CB >= 16) v += dpp<kRowMirror>(v);
+  return v;
+}
+
 // o_proj for a few rows, merging the attention partials on the way in:
-// att[row][h] = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c over the chunks
-// of (row, h) in chunk order, M the largest m_c (deterministic).  Every
-// workgroup merges all rows into LDS: thread t takes the float4 columns t,
-// t + 256, ... of the attention output; the partials of the first CB chunks
-// are requested with the W_o rows and the row table, before the row's chunk
-// count is known, and the chunks past it are skipped (never weighted: their
-// slots hold an older call's values).
+// att[row][h] = sum_c w_c acc_c, w_c = 2^(m_c - M) / sum_c 2^(m_c - M) l_c over
+// the chunks of (row, h), M the largest m_c, summed in chunk order
+// (deterministic).  Every workgroup merges all rows into LDS.  The weights
+// first: thread t < nq CB takes head t / CB and chunks t % CB + CB i, the CB
+// lanes of a head combine maxima and sums with lane operations, and the
+// normalised weights go to LDS.  Then thread t sums the float4 columns t, t +
+// 256, ... of the output.  The partials of the first CB chunks are requested
+// with the W_o rows and the row table, before the row's chunk count is known;
+// the chunks past it weigh zero and their values are never used (their slots
+// hold an older call's values).
 template <int DT, int KV, int RPW, int CB>
 __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   float *xs = reinterpret_cast<float *>(dyn);   // [rows][nq d]
+  __shared__ float s_w[32][kMaxChunks];          // merge weights [head][chunk] (nq <= 32)
   constexpr int NS = (KV + 1) / 2;              // float4 columns per thread (nq d = 512 KV)
   const int K = A.nq * kHeadDim, K4 = K / 4;
   uint4 wr[RPW][KV];
   load_wo<KV, RPW>(A, blockIdx.x, wr);
   if (blockIdx.x == 0) advance_lengths<false>(A);
   const int t = threadIdx.x;
+  const int cs = A.group * kPartStride;         // floats per chunk of a kv head
+  // partial of head h, chunk c of `row` (chunk index clamped into the slots)
+  auto part_of = [&](int row, int h, int c) __attribute__((always_inline)) {
+    const int g = h / A.group, j = h - g * A.group;
+    return A.part + (((size_t)row * A.nkv + g) * kMaxChunks * A.group + j) * kPartStride +
+           (size_t)min(c, kMaxChunks - 1) * cs;
+  };
+  const int hq = min(t / CB, A.nq - 1), cq = t % CB;   // weights: head and first chunk of this thread
+  const bool wt = t < A.nq * CB;
   for (int row = 0; row < A.rows; ++row) {
     const int4 rt = A.rowtab[row];
-    const float *prow = A.part + (size_t)row * A.nkv * kMaxChunks * A.group * kPartStride;
-    float2 ml[NS][CB];
+    const float2 ml0 = *reinterpret_cast<const float2 *>(part_of(row, hq, cq) + 128);
     float4 av[NS][CB];
-    PartPlain P[NS];
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       const int q4 = min(t + 256 * s2, K4 - 1);
-      const int h = q4 / 32, g = h / A.group, j = h - g * A.group;
-      P[s2] = PartPlain{prow + ((size_t)g * kMaxChunks * A.group + j) * kPartStride, A.group * kPartStride, (q4 % 32) * 4};
 #pragma unroll
-      for (int c = 0; c < CB; ++c) P[s2](c, ml[s2][c], av[s2][c], true);
+      for (int c = 0; c < CB; ++c)
+        av[s2][c] = *reinterpret_cast<const float4 *>(part_of(row, q4 / 32, c) + (q4 % 32) * 4);
     }
     const int nch = chunks_of(rt.x ? rt.y + row % A.n + 1 : 0, A.split);
+    // weights
+    float mx = cq < nch ? ml0.x : -INFINITY;
+    for (int c = cq + CB; c < nch; c += CB) mx = fmaxf(mx, part_of(row, hq, c)[128]);
+    const float M = group_max<CB>(mx);
+    const float w0 = cq < nch ? exp2_neg(ml0.x - M) : 0.f;
+    float den = w0 * (cq < nch ? ml0.y : 0.f);
+    for (int c = cq + CB; c < nch; c += CB) {
+      const float2 v = *reinterpret_cast<const float2 *>(part_of(row, hq, c) + 128);
+      den += exp2_neg(v.x - M) * v.y;
+    }
+    const float inv = 1.0f / group_sum<CB>(den);
+    if (wt) {
+      s_w[hq][cq] = w0 * inv;
+      for (int c = cq + CB; c < nch; c += CB) s_w[hq][c] = exp2_neg(part_of(row, hq, c)[128] - M) * inv;
+    }
+    __syncthreads();
+    // columns
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
-      const int q4 = t + 256 * s2;
-      const float4 o = merge_column<CB>(nch, ml[s2], av[s2], P[s2]);
-      if (q4 < K4) reinterpret_cast<float4 *>(xs + (size_t)row * K)[q4] = o;
+      const int q4 = t + 256 * s2, h = min(q4, K4 - 1) / 32;
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const bool ok = c < nch;
+        const float w = s_w[h][c];   // zero past nch
+        num.x += w * (ok ? av[s2][c].x : 0.f);
+        num.y += w * (ok ? av[s2][c].y : 0.f);
+        num.z += w * (ok ? av[s2][c].z : 0.f);
+        num.w += w * (ok ? av[s2][c].w : 0.f);
+      }
+      for (int c = CB; c < nch; ++c) {
+        const float w = s_w[h][c];
+        const float4 v = *reinterpret_cast<const float4 *>(part_of(row, h, c) + (q4 % 32) * 4);
+        num.x += w * v.x;
+        num.y += w * v.y;
+        num.z += w * v.z;
+        num.w += w * v.w;
+      }
+      if (q4 < K4) reinterpret_cast<float4 *>(xs + (size_t)row * K)[q4] = num;
     }
+    __syncthreads();   // s_w is reused by the next row
   }
   __syncthreads();
   const int wave = wave_id(), lane = lane_id();

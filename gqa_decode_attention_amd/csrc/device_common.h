@@ -204,12 +204,20 @@ __device__ __forceinline__ float swap_sum(float lo, float hi) {
   }
 }
 
-// v of lane l ^ 32 (the halves of the wave exchanged)
-__device__ __forceinline__ float xpartner32(float v) {
+// v of lane l ^ MASK (MASK 16 or 32)
+template <int MASK>
+__device__ __forceinline__ float xpart(float v) {
+  static_assert(MASK == 16 || MASK == 32, "lane masks 16 and 32");
   const unsigned a = __builtin_bit_cast(unsigned, v);
-  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
-  return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
+  if constexpr (MASK == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 32) ? r[0] : r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    return __builtin_bit_cast(float, (unsigned)((threadIdx.x & 16) ? r[0] : r[1]));
+  }
 }
+__device__ __forceinline__ float xpartner32(float v) { return xpart<32>(v); }
 
 // v plus v of lane l ^ MASK, in every lane
 template <int MASK>

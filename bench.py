@@ -47,9 +47,9 @@ PAGES_US_PER_TOKEN = 9033.0
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99994, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "54d1b6131f37819ed6e4be3ebd104f9709626f6c03ebb8e309f5d8462b8e62a9",
-    "bs1": {"qkv_projection": 8568780, "attention": 3908085, "o_proj": 4309068},
-    "b64": {"qkv_projection": 11120350, "attention": 229570559, "o_proj": 8717263},
+    "sources_sha256": "2d02b1f14c106c00457fc96ef5f80dfdb816bb8a50d85aede147b11df9b28f3f",
+    "bs1": {"qkv_projection": 8570624, "attention": 4069665, "o_proj": 4845423},
+    "b64": {"qkv_projection": 11063007, "attention": 229552947, "o_proj": 8712143},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",

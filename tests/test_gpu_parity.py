@@ -86,6 +86,47 @@ def test_ragged_decode_vs_oracle(dtype, split, dispatch):
 
 
 @pytest.mark.parametrize("dtype", [si.F16, si.BF16])
+@pytest.mark.parametrize("split", [0, 32, 512])
+def test_few_rows_stale_host_lengths(dtype, split):
+    """Up to 4 rows, the host's copy of the lengths far below the device's: the launch is sized
+    for fewer chunks than the rows have, so workgroups take several chunks each and the o_proj
+    merge reads past its first batch of partials; chunks of 512 keys take steps past the loaded
+    ones.  Results follow the device lengths (the truth), decode and verify."""
+    lens = [700, 33, 250]
+    host = [100, 10, 20]
+    cap = 800
+    L = SeededLayer(2, 3, 1024, dtype)
+    kb, vb = fill_cache(2, 3, lens, cap, dtype)
+    cfg = ga.config(dtype=dtype, kv_split=split)
+    kv = device_cache(kb, vb, lens, dtype)
+    ref = oracle_cache(kb, vb, lens, dtype)
+    xb = _x(2, 3, 0, (3, 1024), dtype)
+    got = _run_decode(L, cfg, kv, xb, dtype, host_lens=host)
+    want = oracle.decode(L.ocfg, L.ref, ref, xb)
+    err = rel_err(got, want)
+    print(f"stale host lens decode {dtype} split={split}: {err:.3e}")
+    assert err < TOL[dtype]
+    assert kv.lens.cpu().tolist() == [l + 1 for l in lens]
+    kg = to_bits(kv.k)
+    for s in range(3):
+        check_rounded_rows(kg[s, :, lens[s]], ref.k[s, :, lens[s]], dtype)
+    # verify: 2 sequences x 2 rows, host copy stale
+    kv2 = device_cache(kb[:2], vb[:2], lens[:2], dtype)
+    ref2 = oracle_cache(kb[:2], vb[:2], lens[:2], dtype)
+    xv = _x(2, 3, 1, (2, 2, 1024), dtype)
+    out = torch.empty((2, 2, 1024), dtype=torch.float32, device="cuda")
+    ws = ga.alloc_workspace(cfg, 4, cap)
+    ga.layer_verify(cfg, L.dev, kv2, to_dev(xv, dtype), out, ws, host_lens=host[:2])
+    torch.cuda.synchronize()
+    gotv = out.cpu().numpy().astype(np.float64)
+    wantv = oracle.verify(L.ocfg, L.ref, ref2, xv)
+    errv = rel_err(gotv, wantv)
+    print(f"stale host lens verify {dtype} split={split}: {errv:.3e}")
+    assert errv < TOL[dtype]
+    assert kv2.lens.cpu().tolist() == [l + 2 for l in lens[:2]]
+
+
+@pytest.mark.parametrize("dtype", [si.F16, si.BF16])
 @pytest.mark.parametrize("B", [2, 6])
 def test_positions_residual_and_16bit_out(dtype, B):
     """Explicit positions, a residual and 16-bit output; B = 6 takes the many-row kernels."""

@@ -150,8 +150,21 @@ __device__ __forceinline__ void qkv_tile_weights(const LayerArgs &A, int tile, u
       wr[i][v] = ld16_stream(A.w_qkv + (size_t)orow[i] * A.H + (v * 64 + lane_id()) * 8);
 }
 
-template <int DT, int KV, int RB, bool COH>
-__device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s_ssq)[4], const uint4 (&wr)[4][KV]) {
+// fp64 rotary angle of pair t at position pos, as (cos, sin)
+__device__ __forceinline__ float2 rope_cs(int pos, double omega) {
+  double sn, cs;
+  sincos((double)pos * omega, &sn, &cs);
+  return make_float2((float)cs, (float)sn);
+}
+
+// LOADW: the tile requests its weight rows itself and, right behind them and
+// before any wait, its small inputs (x of the first RB rows, the input-norm
+// gain, the q/k gains), so that all of them travel together (a wait on a load
+// waits on every load issued before it: a small load issued only after a
+// first wait would add a round trip).  Else the caller has requested the
+// weights into wr.
+template <int DT, int KV, int RB, bool COH, bool LOADW = false>
+__device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s_ssq)[4], uint4 (&wr)[4][KV]) {
   const int wave = wave_id(), lane = lane_id();
   const int head = tile / kTilesPerHead, jj = tile % kTilesPerHead;
   const int ta = 8 * jj + 2 * wave, tb = ta + 1;
@@ -159,30 +172,54 @@ __device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s
   qkv_tile_rows(tile, orow);
   const bool rot = head < A.nq + A.nkv;
   const int H = A.H;
-  float g[KV * 8];
+  const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;   // v heads: unused
+  if constexpr (LOADW) qkv_tile_weights<KV>(A, tile, wr);
+  uint4 x0[RB][KV], g16[KV];
+  uint32_t gq16[4];
 #pragma unroll
-  for (int v = 0; v < KV; ++v) unpack8<DT>(ld16(A.g_in + (v * 64 + lane) * 8), g + v * 8);
-  float gq[4] = {1.f, 1.f, 1.f, 1.f};
-  if (rot) {
-    const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;
-    gq[0] = cvt16<DT>(gp[ta]);
-    gq[1] = cvt16<DT>(gp[ta + 64]);
-    gq[2] = cvt16<DT>(gp[tb]);
-    gq[3] = cvt16<DT>(gp[tb + 64]);
-  }
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int v = 0; v < KV; ++v) x0[r][v] = ld16(A.x + (size_t)min(r, A.rows - 1) * H + (v * 64 + lane) * 8);
+#pragma unroll
+  for (int v = 0; v < KV; ++v) g16[v] = ld16(A.g_in + (v * 64 + lane) * 8);
+  gq16[0] = gp[ta];
+  gq16[1] = gp[ta + 64];
+  gq16[2] = gp[tb];
+  gq16[3] = gp[tb + 64];
+  // rotary angles of the first row block while the loads travel: the rows'
+  // positions come through scalar loads, which do not wait on vector loads.
+  // Lane 2r computes pair ta of row rb + r, lane 2r + 1 pair tb.
   const double om_a = exp2(-(2.0 * ta / kHeadDim) * log2((double)A.theta));
   const double om_b = exp2(-(2.0 * tb / kHeadDim) * log2((double)A.theta));
+  auto angles = [&](int rb, float &cs_c, float &cs_s) __attribute__((always_inline)) {
+    cs_c = 1.f;
+    cs_s = 0.f;
+    if (rot) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (rb + r < A.rows && lane / 2 == r) {
+          const float2 c = rope_cs(row_info(A, rb + r).pos, (lane & 1) ? om_b : om_a);
+          cs_c = c.x;
+          cs_s = c.y;
+        }
+      }
+    }
+  };
+  float cs_c0, cs_s0;
+  angles(0, cs_c0, cs_s0);
+  __builtin_amdgcn_sched_barrier(0);   // loads and angles before the first use of a loaded value
+  float g[KV * 8];
+#pragma unroll
+  for (int v = 0; v < KV; ++v) unpack8<DT>(g16[v], g + v * 8);
+  float gq[4] = {1.f, 1.f, 1.f, 1.f};
+  if (rot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gq[i] = cvt16<DT>((uint16_t)gq16[i]);
+  }
 
   for (int rb = 0; rb < A.rows; rb += RB) {
-    // cos/sin for the RB rows: lane 2r computes pair ta of row rb + r, lane 2r + 1 pair tb
-    float cs_c = 1.f, cs_s = 0.f;
-    if (rot && lane < 2 * RB && rb + lane / 2 < A.rows) {
-      const RowInfo ri = row_info(A, rb + lane / 2);
-      double sn, cs;
-      sincos((double)ri.pos * ((lane & 1) ? om_b : om_a), &sn, &cs);
-      cs_c = (float)cs;
-      cs_s = (float)sn;
-    }
+    float cs_c = cs_c0, cs_s = cs_s0;
+    if (rb > 0) angles(rb, cs_c, cs_s);
     float x[RB][KV * 8];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -190,7 +227,8 @@ __device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s
       float ss = 0.f;
       if (row < A.rows) {
 #pragma unroll
-        for (int v = 0; v < KV; ++v) unpack8<DT>(ld16(A.x + (size_t)row * H + (v * 64 + lane) * 8), x[r] + v * 8);
+        for (int v = 0; v < KV; ++v)
+          unpack8<DT>(rb == 0 ? x0[r][v] : ld16(A.x + (size_t)row * H + (v * 64 + lane) * 8), x[r] + v * 8);
 #pragma unroll
         for (int e = 0; e < KV * 8; ++e) ss += x[r][e] * x[r][e];
       } else {
@@ -1661,9 +1699,8 @@ template <int DT, int KV, int RB>
 __global__ __launch_bounds__(256) void k_qkv(LayerArgs A) {
   __shared__ float s_ssq[RB][4];
   uint4 wr[4][KV];
-  qkv_tile_weights<KV>(A, blockIdx.x, wr);
+  qkv_tile<DT, KV, RB, false, true>(A, blockIdx.x, s_ssq, wr);
   if (blockIdx.x == 0) write_row_table<false>(A);
-  qkv_tile<DT, KV, RB, false>(A, blockIdx.x, s_ssq, wr);
 }
 
 template <int DT, int GROUP>
@@ -2038,9 +2075,6 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   __shared__ float s_w[32][kMaxChunks];          // merge weights [head][chunk] (nq <= 32)
   constexpr int NS = (KV + 1) / 2;              // float4 columns per thread (nq d = 512 KV)
   const int K = A.nq * kHeadDim, K4 = K / 4;
-  uint4 wr[RPW][KV];
-  load_wo<KV, RPW>(A, blockIdx.x, wr);
-  if (blockIdx.x == 0) advance_lengths<false>(A);
   const int t = threadIdx.x;
   const int cs = A.group * kPartStride;         // floats per chunk of a kv head
   // partial of head h, chunk c of `row` (chunk index clamped into the slots)
@@ -2051,10 +2085,10 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   };
   const int hq = min(t / CB, A.nq - 1), cq = t % CB;   // weights: head and first chunk of this thread
   const bool wt = t < A.nq * CB;
-  for (int row = 0; row < A.rows; ++row) {
-    const int4 rt = A.rowtab[row];
-    const float2 ml0 = *reinterpret_cast<const float2 *>(part_of(row, hq, cq) + 128);
-    float4 av[NS][CB];
+  // a row's merge inputs: its table record, this thread's (m, l) and the columns of the first CB chunks
+  auto merge_loads = [&](int row, int4 &rt, float2 &ml0, float4 (&av)[NS][CB]) __attribute__((always_inline)) {
+    rt = A.rowtab[row];
+    ml0 = *reinterpret_cast<const float2 *>(part_of(row, hq, cq) + 128);
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       const int q4 = min(t + 256 * s2, K4 - 1);
@@ -2062,6 +2096,25 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       for (int c = 0; c < CB; ++c)
         av[s2][c] = *reinterpret_cast<const float4 *>(part_of(row, q4 / 32, c) + (q4 % 32) * 4);
     }
+  };
+  // The first row's merge inputs are requested before the W_o rows: a wait on a
+  // load waits on every load issued before it, so the merge runs while W_o travels.
+  int4 rt_0;
+  float2 ml0_0;
+  float4 av_0[NS][CB];
+  merge_loads(0, rt_0, ml0_0, av_0);
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wr[RPW][KV];
+  load_wo<KV, RPW>(A, blockIdx.x, wr);
+  for (int row = 0; row < A.rows; ++row) {
+    int4 rt = rt_0;
+    float2 ml0 = ml0_0;
+    float4 av[NS][CB];
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+      for (int c = 0; c < CB; ++c) av[s2][c] = av_0[s2][c];
+    if (row > 0) merge_loads(row, rt, ml0, av);
     const int nch = chunks_of(rt.x ? rt.y + row % A.n + 1 : 0, A.split);
     // weights
     float mx = cq < nch ? ml0.x : -INFINITY;
@@ -2139,6 +2192,7 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
     }
   }
+  if (blockIdx.x == 0) advance_lengths<false>(A);
 }
 
 // lengths advance once every workgroup has read them (rows from LDS)

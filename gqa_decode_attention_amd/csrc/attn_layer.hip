@@ -1796,9 +1796,14 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
         x1 = a1;
       }
     }
-    const uint32_t vm = valid ? 0xffffffffu : 0u;   // no stale inf/NaN bits
-    x0 = make_uint4(x0.x & vm, x0.y & vm, x0.z & vm, x0.w & vm);
-    x1 = make_uint4(x1.x & vm, x1.y & vm, x1.z & vm, x1.w & vm);
+    // V rows past the chunk are zeroed (their weight is 0, but 0 * inf is not);
+    // K rows need not be: their scores are replaced by -inf.  A step whose
+    // keys are all visible (wave-uniform) skips the masking.
+    if (h == 1 && G.tw + NW * 8 * i + 7 >= G.t1) {
+      const uint32_t vm = valid ? 0xffffffffu : 0u;
+      x0 = make_uint4(x0.x & vm, x0.y & vm, x0.z & vm, x0.w & vm);
+      x1 = make_uint4(x1.x & vm, x1.y & vm, x1.z & vm, x1.w & vm);
+    }
     return valid;
   };
   auto score = [&](const uint4 (&rr)[4], int i, bool with_new, float (&s)[GROUP]) __attribute__((always_inline)) {
@@ -1809,10 +1814,10 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
     unpack8<DT>(k1, kf + 8);
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
-      float x = 0.f;
+      float xp[4] = {0.f, 0.f, 0.f, 0.f};   // four independent chains
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x += q[j][e] * kf[e];
-      x = sum8(x);
+      for (int e = 0; e < 16; ++e) xp[e & 3] += q[j][e] * kf[e];
+      const float x = sum8((xp[0] + xp[1]) + (xp[2] + xp[3]));
       s[j] = valid ? x : -INFINITY;
     }
   };

@@ -255,33 +255,37 @@ __device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s
           for (int e = 0; e < 8; ++e) acc[i][r] += wf[e] * x[r][v * 8 + e];
       }
     }
+    // Sums over the wave: reduce-scatter over lane bits 5 and 4 (the 16-lane row
+    // q = lane >> 4 keeps output row q of the wave), then a sum over the 16 lanes.
+    constexpr int N = 4 * RB;
+    float v1[N], v2[N / 2], v3[N / 4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < RB; ++r) acc[i][r] = wave_sum(acc[i][r]);
+      for (int r = 0; r < RB; ++r) v1[i * RB + r] = acc[i][r];
+    rs_half<N, 32>(v1, v2);
+    rs_half<N / 2, 16>(v2, v3);
+    const int q = lane >> 4;   // output row orow[q]: rotary pair a (rows 0, 1) or b (rows 2, 3)
+    const float gqq = q == 0 ? gq[0] : q == 1 ? gq[1] : q == 2 ? gq[2] : gq[3];
+    const int oq = q == 0 ? orow[0] : q == 1 ? orow[1] : q == 2 ? orow[2] : orow[3];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int row = rb + r;
       if (row >= A.rows) continue;
-      float o[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      float o = sum16(v3[r]);
       if (rot) {
         const float ca = readlane(cs_c, 2 * r), sa = readlane(cs_s, 2 * r);
         const float cb = readlane(cs_c, 2 * r + 1), sb = readlane(cs_s, 2 * r + 1);
-        const float ssq = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-        const float u0 = gq[0] * o[0], u1 = gq[1] * o[1], u2 = gq[2] * o[2], u3 = gq[3] * o[3];
-        o[0] = u0 * ca - u1 * sa;
-        o[1] = u1 * ca + u0 * sa;
-        o[2] = u2 * cb - u3 * sb;
-        o[3] = u3 * cb + u2 * sb;
+        const float c = (q >> 1) ? cb : ca, sn = (q >> 1) ? sb : sa;
+        float ssq = o * o;
+        ssq = xsum<16>(ssq);
+        ssq = xsum<32>(ssq);
+        const float u = gqq * o;
+        const float up = xpart<16>(u);   // the other row of the pair
+        o = (q & 1) ? u * c + up * sn : u * c - up * sn;
         if (lane == 0) s_ssq[r][wave] = ssq;
       }
-      if (lane < 4) {
-        float val = o[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i)
-          if (lane == i) val = o[i];
-        stx<COH>(A.qkv + (size_t)row * A.nqkv + orow[lane], val);
-      }
+      if ((lane & 15) == 0) stx<COH>(A.qkv + (size_t)row * A.nqkv + oq, o);
     }
     if (rot) {
       __syncthreads();
@@ -958,25 +962,6 @@ __device__ __forceinline__ uint4 round8(float4 a, float4 b) {
   u.z = (uint32_t)rne16<DT>(b.x) | ((uint32_t)rne16<DT>(b.y) << 16);
   u.w = (uint32_t)rne16<DT>(b.z) | ((uint32_t)rne16<DT>(b.w) << 16);
   return u;
-}
-
-// Reduce-scatter over the lanes l ^ MASK: lanes with the MASK bit clear keep
-// the low half of the values, the others the high half, each summed with its
-// partner's copy.
-template <int N, int MASK>
-__device__ __forceinline__ void rs_half(const float (&in)[N], float (&out)[N / 2]) {
-  if constexpr (MASK == 8) {
-    const bool hi = (lane_id() & MASK) != 0;
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      const float keep = hi ? in[N / 2 + i] : in[i];
-      const float send = hi ? in[i] : in[N / 2 + i];
-      out[i] = keep + dpp<0x128>(send);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) out[i] = swap_sum<MASK>(in[i], in[N / 2 + i]);
-  }
 }
 
 // counted partial of a piece whose merge check waits for a later point

@@ -239,4 +239,23 @@ __device__ __forceinline__ float sum_stride8(float v) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x % kWave; }
 
+// Reduce-scatter over the lanes l ^ MASK: lanes with the MASK bit clear keep
+// the low half of the values, the others the high half, each summed with its
+// partner's copy.
+template <int N, int MASK>
+__device__ __forceinline__ void rs_half(const float (&in)[N], float (&out)[N / 2]) {
+  if constexpr (MASK == 8) {
+    const bool hi = (lane_id() & MASK) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = hi ? in[N / 2 + i] : in[i];
+      const float send = hi ? in[i] : in[N / 2 + i];
+      out[i] = keep + dpp<0x128>(send);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) out[i] = swap_sum<MASK>(in[i], in[N / 2 + i]);
+  }
+}
+
 }  // namespace asr

@@ -393,6 +393,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 __device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// the same with the nontemporal hint: a stream read once, kept out of the caches' way
+constexpr int kCachePolicyStream = 2;   // nt
+__device__ __forceinline__ uint4 ld_buf_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyStream));
+}
 
 // 16 bytes from LDS through an LDS-typed pointer
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -937,10 +942,10 @@ __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, ui
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + base, region);
   const int last = max(min(rfl(c.te), rfl(c.L)) - 1, 0);
   const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * (kHeadDim * 2) + kl * 16;
-  r[0] = ld_buf(Kr, off);
-  r[1] = ld_buf(Kr, off + 128);
-  r[2] = ld_buf(Vr, off);
-  r[3] = ld_buf(Vr, off + 128);
+  r[0] = ld_buf_nt(Kr, off);
+  r[1] = ld_buf_nt(Kr, off + 128);
+  r[2] = ld_buf_nt(Vr, off);
+  r[3] = ld_buf_nt(Vr, off + 128);
 }
 
 // One lane's 8 dims of an appended row, 16-bit as stored: k normalised with

@@ -47,9 +47,9 @@ PAGES_US_PER_TOKEN = 9033.0
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99994, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "88d0a019f6ed3b4da16290c8b10025a9bda5c01124186b146fc49b8f59e3477c",
-    "bs1": {"qkv_projection": 8574908, "attention": 4071911, "o_proj": 4858930},
-    "b64": {"qkv_projection": 11062990, "attention": 229526930, "o_proj": 8703936},
+    "sources_sha256": "df0366de3dbd9aacf0e95188ea214b63fe9be76d1ea6d033f53938f1e054ca88",
+    "bs1": {"qkv_projection": 8574910, "attention": 4071911, "o_proj": 4858931},
+    "b64": {"qkv_projection": 11063196, "attention": 230240269, "o_proj": 8703938},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",

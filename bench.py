@@ -47,7 +47,7 @@ PAGES_US_PER_TOKEN = 9033.0
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99994, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "df0366de3dbd9aacf0e95188ea214b63fe9be76d1ea6d033f53938f1e054ca88",
+    "sources_sha256": "c1f97e12c1fd1c0c6c3ec05e14321de967ec877d84c7a2f4d5e6b15a13be2cb7",
     "bs1": {"qkv_projection": 8574910, "attention": 4071911, "o_proj": 4858931},
     "b64": {"qkv_projection": 11063196, "attention": 230240269, "o_proj": 8703938},
 }
@@ -151,21 +151,21 @@ def main():
         return
 
     # ------------------------------------------------------------ bs1 workload
-    c2 = si.CONFIGS[2]
-    H, NL, dtype = c2["hidden"], c2["layers"], c2["dtype"]
+    wl = si.WORKLOADS["decode_bs1_28layers_kv795"]
+    H, NL, dtype, sid = wl["hidden"], wl["layers"], wl["dtype"], wl["stream"]
     P0, NSTEP = 795, 130
     cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch, kv_split=args.kv_split)
     t0 = time.time()
     weights, kvs = [], []
     for l in range(NL):
-        wb = si.layer_weights(2, l, H, dtype)
+        wb = si.layer_weights(sid, l, H, dtype)
         weights.append(ga.Weights(*(to_dev(wb[n], dtype) for n in
                                     ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o"))))
-        kb, vb = si.kv_rows(2, l, 0, P0, dtype)
+        kb, vb = si.kv_rows(sid, l, 0, P0, dtype)
         kv = ga.KVLayer.empty(1, 8, CAP_BS1, dtype=torch.float16, device=dev)
         ga.kv_append(kv, to_dev(kb.transpose(1, 0, 2)[None], dtype), to_dev(vb.transpose(1, 0, 2)[None], dtype))
         kvs.append(kv)
-    xs = torch.stack([torch.stack([to_dev(si.activations(2, l, s, 1, H, dtype), dtype) for l in range(NL)])
+    xs = torch.stack([torch.stack([to_dev(si.activations(sid, l, s, 1, H, dtype), dtype) for l in range(NL)])
                       for s in range(NSTEP)])                      # [step][layer][1][H]
     outs = torch.empty((NL, 1, H), dtype=torch.float32, device=dev)
     ws = ga.alloc_workspace(cfg, 1, CAP_BS1, device=dev)
@@ -281,24 +281,24 @@ def main():
 
 
 def batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
-    c4 = si.CONFIGS[4]
-    H, NL, B, dtype = c4["hidden"], c4["layers"], c4["batch"], c4["dtype"]
-    lens = si.kv_lengths(4, B, *c4["kv_len"])
+    wl = si.WORKLOADS["ragged_batch64_h1024"]
+    H, NL, B, dtype, sid = wl["hidden"], wl["layers"], wl["batch"], wl["dtype"], wl["stream"]
+    lens = si.kv_lengths(sid, B, *wl["kv_len"])
     cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch, kv_split=args.kv_split)
     t0 = time.time()
     weights, kvs = [], []
     for l in range(NL):
-        wb = si.layer_weights(4, l, H, dtype)
+        wb = si.layer_weights(sid, l, H, dtype)
         weights.append(ga.Weights(*(to_dev(wb[n], dtype) for n in
                                     ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o"))))
         kv = ga.KVLayer.empty(B, 8, CAP_B64, dtype=torch.bfloat16, device=dev)
-        rows = si.kv_rows_many(4, l, list(range(B)), lens.tolist(), dtype)
+        rows = si.kv_rows_many(sid, l, list(range(B)), lens.tolist(), dtype)
         for s, (kb, vb) in enumerate(rows):
             kv.k[s, :, : lens[s]] = to_dev(kb, dtype)
             kv.v[s, :, : lens[s]] = to_dev(vb, dtype)
         kv.lens.copy_(torch.from_numpy(lens))
         kvs.append(kv)
-    xs = torch.stack([to_dev(si.activations(4, l, 0, B, H, dtype), dtype) for l in range(NL)])
+    xs = torch.stack([to_dev(si.activations(sid, l, 0, B, H, dtype), dtype) for l in range(NL)])
     outs = torch.empty((NL, B, H), dtype=torch.float32, device=dev)
     ws = ga.alloc_workspace(cfg, B, CAP_B64, device=dev)
     base = torch.from_numpy(lens.astype(np.int32)).to(dev)
@@ -372,12 +372,13 @@ def cpu_baseline(budget_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    H, dtype, P0, max_steps = 1024, si.F16, 795, 130
+    wl = si.WORKLOADS["decode_bs1_28layers_kv795"]
+    H, dtype, sid, P0, max_steps = wl["hidden"], wl["dtype"], wl["stream"], 795, 130
     ocfg = oracle.BlockConfig(hidden=H, dtype=dtype)
     layers = []
     for l in range(28):
-        w = oracle.LayerWeights.from_bits(si.layer_weights(2, l, H, dtype), dtype)
-        kb, vb = si.kv_rows(2, l, 0, P0, dtype)
+        w = oracle.LayerWeights.from_bits(si.layer_weights(sid, l, H, dtype), dtype)
+        kb, vb = si.kv_rows(sid, l, 0, P0, dtype)
         c = oracle.KVCache.empty(1, 8, CAP_BS1, 128, dtype)
         c.k[0, :, :P0], c.v[0, :, :P0], c.lens[0] = kb, vb, P0
         layers.append((w, c))
@@ -386,7 +387,7 @@ def cpu_baseline(budget_s):
     while step < max_steps:
         for l in range(28):
             w, c = layers[l]
-            oracle.decode(ocfg, w, c, si.activations(2, l, step, 1, H, dtype))
+            oracle.decode(ocfg, w, c, si.activations(sid, l, step, 1, H, dtype))
             calls += 1
         step += 1
         if time.perf_counter() - t0 > budget_s:

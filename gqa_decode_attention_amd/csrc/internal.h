@@ -9,7 +9,7 @@
 
 namespace asr {
 
-constexpr int kHeadDim = 128;          // the only head size this build supports
+constexpr int kHeadDim = 128;          // the only head size the kernels support
 constexpr int kMaxChunks = 64;        // split-KV chunks per (row, kv head)
 constexpr int kMinSplit = 16;         // keys per chunk, lower bound
 constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound

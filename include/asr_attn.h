@@ -49,7 +49,7 @@ enum { ASR_F16 = 0, ASR_BF16 = 1, ASR_F32 = 2 };
 enum {
   ASR_OK = 0,
   ASR_EINVAL = -1,        /* null pointer, negative size, inconsistent shapes, k out of range */
-  ASR_EUNSUPPORTED = -2,  /* a shape or type this build has no kernel for (see asr_attn_config) */
+  ASR_EUNSUPPORTED = -2,  /* a shape or type the library has no kernel for (see asr_attn_config) */
   ASR_ECAPACITY = -3,     /* host_lens given and some lens + n > capacity */
   ASR_EWORKSPACE = -4,    /* workspace NULL or smaller than asr_attn_workspace_bytes() */
   ASR_EHIP = -5           /* the HIP runtime refused a launch */
@@ -75,7 +75,7 @@ enum {
 };
 
 /*
- * Block shape and numerics.  Supported by this build: head_dim = 128;
+ * Block shape and numerics.  Supported by the library: head_dim = 128;
  * n_q_heads a multiple of n_kv_heads with n_q_heads / n_kv_heads in
  * {1, 2, 4, 8}; n_q_heads * head_dim and hidden multiples of 512, at most
  * 4096; dtype ASR_F16 or ASR_BF16 (weights, x, residual and the KV cache);

@@ -15,10 +15,11 @@ version 0"), and batched serving of 30 s windows at 64 concurrent requests
 and "Throughput results").
 
 Random streams: every tensor has its own NumPy PCG64 stream keyed by
-``(1000 + config id, layer, tensor id, extra)``, so any tensor can be
+``(1000 + stream, layer, tensor id, extra)``, the stream being a small
+integer per workload or test family,, so any tensor can be
 regenerated on its own.  Draws are fp64 ``standard_normal`` scaled to the
 stated distribution, then rounded once, to nearest with ties to even, into the
-config's 16-bit type.
+workload's 16-bit type.
 """
 from __future__ import annotations
 
@@ -40,32 +41,35 @@ HEAD_DIM = 128
 RMS_EPS = 1e-6
 ROPE_THETA = 1e6
 
-# The five workloads.  Lengths are committed KV lengths before the step.
-CONFIGS = {
-    1: dict(name="single layer decode, bs1, fp16, KV 64", layers=1, batch=1,
-            dtype=F16, hidden=1024, kv_len=(64, 64), steps=1),
-    2: dict(name="28-layer decode, bs1, fp16, KV 795->925 over 130 steps",
-            layers=28, batch=1, dtype=F16, hidden=1024, kv_len=(795, 795),
-            steps=130),
-    3: dict(name="28-layer verify k in {4,8,16}, bs1, fp16, committed 795",
-            layers=28, batch=1, dtype=F16, hidden=1024, kv_len=(795, 795),
-            verify_k=(4, 8, 16)),
-    4: dict(name="28-layer ragged batched decode, 64 seqs, bf16, hidden 1024, KV U{200..1500}",
-            layers=28, batch=64, dtype=BF16, hidden=1024, kv_len=(200, 1500),
-            steps=1),
-    5: dict(name="28-layer ragged batched decode, 64 seqs, bf16, hidden 2048, KV U{1024..4096}"
-                 " + verify k=8 on 8 seqs",
-            layers=28, batch=64, dtype=BF16, hidden=2048, kv_len=(1024, 4096),
-            steps=1, verify_k=(8,), verify_seqs=8),
+# The five workloads, by name.  Lengths are committed KV lengths before the
+# step; "stream" keys the workload's random streams.
+WORKLOADS = {
+    "decode_bs1_1layer_kv64": dict(
+        stream=1, name="single layer decode, bs1, fp16, KV 64", layers=1, batch=1,
+        dtype=F16, hidden=1024, kv_len=(64, 64), steps=1),
+    "decode_bs1_28layers_kv795": dict(
+        stream=2, name="28-layer decode, bs1, fp16, KV 795->925 over 130 steps",
+        layers=28, batch=1, dtype=F16, hidden=1024, kv_len=(795, 795), steps=130),
+    "verify_bs1_28layers_kv795": dict(
+        stream=3, name="28-layer verify k in {4,8,16}, bs1, fp16, committed 795",
+        layers=28, batch=1, dtype=F16, hidden=1024, kv_len=(795, 795), verify_k=(4, 8, 16)),
+    "ragged_batch64_h1024": dict(
+        stream=4, name="28-layer ragged batched decode, 64 seqs, bf16, hidden 1024, KV U{200..1500}",
+        layers=28, batch=64, dtype=BF16, hidden=1024, kv_len=(200, 1500), steps=1),
+    "ragged_batch64_h2048": dict(
+        stream=5, name="28-layer ragged batched decode, 64 seqs, bf16, hidden 2048, KV U{1024..4096}"
+                       " + verify k=8 on 8 seqs",
+        layers=28, batch=64, dtype=BF16, hidden=2048, kv_len=(1024, 4096),
+        steps=1, verify_k=(8,), verify_seqs=8),
 }
 
 
-def seed_of(cfg_id: int) -> int:
-    return 1000 + int(cfg_id)
+def seed_of(stream: int) -> int:
+    return 1000 + int(stream)
 
 
-def rng_for(cfg_id: int, layer: int, tensor_id: int, extra: int = 0) -> np.random.Generator:
-    return np.random.default_rng([seed_of(cfg_id), int(layer), int(tensor_id), int(extra)])
+def rng_for(stream: int, layer: int, tensor_id: int, extra: int = 0) -> np.random.Generator:
+    return np.random.default_rng([seed_of(stream), int(layer), int(tensor_id), int(extra)])
 
 
 def _f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -95,12 +99,12 @@ def to_bits(a: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown 16-bit dtype {dtype!r}")
 
 
-def normal_bits(cfg_id, layer, tensor_id, extra, shape, std=1.0, mean=0.0, dtype=F16):
-    g = rng_for(cfg_id, layer, tensor_id, extra)
+def normal_bits(stream, layer, tensor_id, extra, shape, std=1.0, mean=0.0, dtype=F16):
+    g = rng_for(stream, layer, tensor_id, extra)
     return to_bits(mean + std * g.standard_normal(shape), dtype)
 
 
-def layer_weights(cfg_id: int, layer: int, hidden: int, dtype: str,
+def layer_weights(stream: int, layer: int, hidden: int, dtype: str,
                   nq: int = N_Q_HEADS, nkv: int = N_KV_HEADS, d: int = HEAD_DIM,
                   gain_std: float = 0.02, gain_mean: float = 1.0, w_std: float = 0.02) -> dict:
     """Weights of one layer as bit patterns.
@@ -111,49 +115,49 @@ def layer_weights(cfg_id: int, layer: int, hidden: int, dtype: str,
     """
     nqkv = (nq + 2 * nkv) * d
     return dict(
-        input_norm_w=normal_bits(cfg_id, layer, T_GAMMA_IN, 0, (hidden,), gain_std, gain_mean, dtype),
-        w_qkv=normal_bits(cfg_id, layer, T_WQKV, 0, (nqkv, hidden), w_std, 0.0, dtype),
-        q_norm_w=normal_bits(cfg_id, layer, T_GAMMA_Q, 0, (d,), gain_std, gain_mean, dtype),
-        k_norm_w=normal_bits(cfg_id, layer, T_GAMMA_K, 0, (d,), gain_std, gain_mean, dtype),
-        w_o=normal_bits(cfg_id, layer, T_WO, 0, (hidden, nq * d), w_std, 0.0, dtype),
+        input_norm_w=normal_bits(stream, layer, T_GAMMA_IN, 0, (hidden,), gain_std, gain_mean, dtype),
+        w_qkv=normal_bits(stream, layer, T_WQKV, 0, (nqkv, hidden), w_std, 0.0, dtype),
+        q_norm_w=normal_bits(stream, layer, T_GAMMA_Q, 0, (d,), gain_std, gain_mean, dtype),
+        k_norm_w=normal_bits(stream, layer, T_GAMMA_K, 0, (d,), gain_std, gain_mean, dtype),
+        w_o=normal_bits(stream, layer, T_WO, 0, (hidden, nq * d), w_std, 0.0, dtype),
     )
 
 
-def kv_rows(cfg_id: int, layer: int, seq: int, length: int, dtype: str,
+def kv_rows(stream: int, layer: int, seq: int, length: int, dtype: str,
             nkv: int = N_KV_HEADS, d: int = HEAD_DIM):
     """Committed cache rows of one sequence: K, V bits, each [nkv][length][d], N(0, 1)."""
-    k = normal_bits(cfg_id, layer, T_KCACHE, seq, (nkv, length, d), 1.0, 0.0, dtype)
-    v = normal_bits(cfg_id, layer, T_VCACHE, seq, (nkv, length, d), 1.0, 0.0, dtype)
+    k = normal_bits(stream, layer, T_KCACHE, seq, (nkv, length, d), 1.0, 0.0, dtype)
+    v = normal_bits(stream, layer, T_VCACHE, seq, (nkv, length, d), 1.0, 0.0, dtype)
     return k, v
 
 
-def kv_rows_many(cfg_id, layer, seqs, lengths, dtype, nkv=N_KV_HEADS, d=HEAD_DIM, threads=None):
+def kv_rows_many(stream, layer, seqs, lengths, dtype, nkv=N_KV_HEADS, d=HEAD_DIM, threads=None):
     """kv_rows for several sequences on a thread pool (NumPy releases the GIL)."""
     threads = threads or min(16, len(os.sched_getaffinity(0)))
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        return list(ex.map(lambda sl: kv_rows(cfg_id, layer, sl[0], sl[1], dtype, nkv, d),
+        return list(ex.map(lambda sl: kv_rows(stream, layer, sl[0], sl[1], dtype, nkv, d),
                            zip(seqs, lengths)))
 
 
-def activations(cfg_id: int, layer: int, step: int, rows: int, hidden: int, dtype: str):
+def activations(stream: int, layer: int, step: int, rows: int, hidden: int, dtype: str):
     """Hidden states entering the block at (layer, step): [rows][hidden], N(0, 1)."""
-    return normal_bits(cfg_id, layer, T_X, step, (rows, hidden), 1.0, 0.0, dtype)
+    return normal_bits(stream, layer, T_X, step, (rows, hidden), 1.0, 0.0, dtype)
 
 
-def residual(cfg_id: int, layer: int, step: int, rows: int, hidden: int, dtype: str):
-    return normal_bits(cfg_id, layer, T_RESID, step, (rows, hidden), 1.0, 0.0, dtype)
+def residual(stream: int, layer: int, step: int, rows: int, hidden: int, dtype: str):
+    return normal_bits(stream, layer, T_RESID, step, (rows, hidden), 1.0, 0.0, dtype)
 
 
-def kv_lengths(cfg_id: int, batch: int, lo: int, hi: int) -> np.ndarray:
+def kv_lengths(stream: int, batch: int, lo: int, hi: int) -> np.ndarray:
     """Committed lengths, uniform integers in [lo, hi] inclusive."""
-    return rng_for(cfg_id, 0, T_LENS, 0).integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+    return rng_for(stream, 0, T_LENS, 0).integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
 
 
-def accepted_prefix(cfg_id: int, k: int, draw: int = 0) -> int:
+def accepted_prefix(stream: int, k: int, draw: int = 0) -> int:
     """Accepted draft prefix length, uniform in [0, k] inclusive."""
-    return int(rng_for(cfg_id, 0, T_ACCEPT, k * 1000 + draw).integers(0, k, endpoint=True))
+    return int(rng_for(stream, 0, T_ACCEPT, k * 1000 + draw).integers(0, k, endpoint=True))
 
 
-def verify_choice(cfg_id: int, batch: int, n: int) -> np.ndarray:
+def verify_choice(stream: int, batch: int, n: int) -> np.ndarray:
     """n distinct sequences of the batch, drawn without replacement."""
-    return np.sort(rng_for(cfg_id, 0, T_VCHOICE, 0).choice(batch, size=n, replace=False)).astype(np.int32)
+    return np.sort(rng_for(stream, 0, T_VCHOICE, 0).choice(batch, size=n, replace=False)).astype(np.int32)

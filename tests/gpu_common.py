@@ -57,22 +57,22 @@ def check_rounded_rows(got_bits: np.ndarray, want_bits: np.ndarray, dtype: str, 
 class SeededLayer:
     """One layer's weights (device + oracle) from the seeded generator."""
 
-    def __init__(self, cfg_id, layer, hidden, dtype, nq=16, nkv=8, gain_mean=1.0):
+    def __init__(self, stream, layer, hidden, dtype, nq=16, nkv=8, gain_mean=1.0):
         self.dtype = dtype
-        self.bits = si.layer_weights(cfg_id, layer, hidden, dtype, nq=nq, nkv=nkv, gain_mean=gain_mean)
+        self.bits = si.layer_weights(stream, layer, hidden, dtype, nq=nq, nkv=nkv, gain_mean=gain_mean)
         self.dev = ga.Weights(*(to_dev(self.bits[n], dtype) for n in
                                 ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o")))
         self.ref = oracle.LayerWeights.from_bits(self.bits, dtype)
         self.ocfg = oracle.BlockConfig(hidden=hidden, n_q_heads=nq, n_kv_heads=nkv, dtype=dtype)
 
 
-def fill_cache(cfg_id, layer, lens, capacity, dtype, nkv=8, seqs=None):
+def fill_cache(stream, layer, lens, capacity, dtype, nkv=8, seqs=None):
     """Host cache bits [batch_cap][nkv][capacity][128] with seeded rows below each length."""
     B = len(lens)
     k = np.zeros((B, nkv, capacity, 128), np.uint16)
     v = np.zeros_like(k)
     seqs = range(B) if seqs is None else seqs
-    rows = si.kv_rows_many(cfg_id, layer, list(seqs), [int(lens[s]) for s in seqs], dtype, nkv=nkv)
+    rows = si.kv_rows_many(stream, layer, list(seqs), [int(lens[s]) for s in seqs], dtype, nkv=nkv)
     for s, (kb, vb) in zip(seqs, rows):
         k[s, :, : lens[s]] = kb
         v[s, :, : lens[s]] = vb

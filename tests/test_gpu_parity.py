@@ -17,9 +17,9 @@ from gpu_common import (TOL, SeededLayer, device_cache, fill_cache, oracle_cache
 pytestmark = pytest.mark.gpu
 
 
-def _x(cfg_id, layer, step, shape, dtype):
+def _x(stream, layer, step, shape, dtype):
     rows = int(np.prod(shape[:-1]))
-    return si.activations(cfg_id, layer, step, rows, shape[-1], dtype).reshape(shape)
+    return si.activations(stream, layer, step, rows, shape[-1], dtype).reshape(shape)
 
 
 # Agreement of two dispatch modes: the same fp32 arithmetic summed in a different order
@@ -40,7 +40,7 @@ def _run_decode(L, cfg, kv, xb, dtype, slots=None, positions=None, residual=None
 
 
 @pytest.mark.parametrize("dispatch", [0, 1, 2])
-def test_cfg1_single_layer_decode(dispatch):
+def test_single_layer_decode_bs1_kv64(dispatch):
     """Single layer, bs1, fp16, hidden 1024, KV 64, new token at position 64."""
     dtype, cap = si.F16, 128
     L = SeededLayer(1, 0, 1024, dtype)
@@ -51,7 +51,7 @@ def test_cfg1_single_layer_decode(dispatch):
     got = _run_decode(L, ga.config(dtype="f16", dispatch=dispatch), kv, xb, dtype)
     want = oracle.decode(L.ocfg, L.ref, ref, xb)
     err = rel_err(got, want)
-    print(f"cfg1 dispatch={dispatch} max|err|/rms = {err:.3e}")
+    print(f"single layer bs1 dispatch={dispatch} max|err|/rms = {err:.3e}")
     assert err < TOL[dtype]
     assert int(kv.lens.item()) == 65 and int(kv.status.item()) == 0
     kg, vg = to_bits(kv.k), to_bits(kv.v)
@@ -416,10 +416,10 @@ def test_fused_dispatch_rejects_shapes_without_an_instance():
     L2 = SeededLayer(5, 2, 1024, dtype)
     kb2, vb2 = fill_cache(5, 2, [10] * 5, 32, dtype)
     kv2 = device_cache(kb2, vb2, [10] * 5, dtype)
-    cfg2 = ga.config(dispatch=ga.DISPATCH_FUSED)
+    cfg_fused = ga.config(dispatch=ga.DISPATCH_FUSED)
     with pytest.raises(ga.AsrError) as e:
-        ga.layer_decode(cfg2, L2.dev, kv2, to_dev(_x(5, 2, 0, (5, 1024), dtype), dtype),
-                        torch.empty((5, 1024), dtype=torch.float32, device="cuda"), ga.alloc_workspace(cfg2, 5, 32))
+        ga.layer_decode(cfg_fused, L2.dev, kv2, to_dev(_x(5, 2, 0, (5, 1024), dtype), dtype),
+                        torch.empty((5, 1024), dtype=torch.float32, device="cuda"), ga.alloc_workspace(cfg_fused, 5, 32))
     assert e.value.code == -2
     L = SeededLayer(9, 44, 512, dtype, nq=4, nkv=4)
     kb, vb = fill_cache(9, 4, [3], 16, dtype, nkv=4)

@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 CAP_BS1 = 928                  # cache capacity of the bs1 workload (>= 925, multiple of 16)
 CAP_B64 = 1536                 # cache capacity of the batch-64 workload (>= 1501)
+CAP_W64 = 4112                 # cache capacity of the hidden-2048 batch-64 workload (>= 4096 + 1 + 8)
 PHASES = ("qkv_projection", "attention", "o_proj")
 # the pages' figure for the same workload on another machine (context, not a target): 28 decoder
 # attention layers at bs1 over the 795 -> 925 clip, RTX 3050 Laptop, HF eager, in us per token
@@ -74,7 +75,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=130)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--no-batched", action="store_true", help="skip the batch-64 workload")
+    p.add_argument("--no-batched", action="store_true", help="skip the batch-64 workloads")
+    p.add_argument("--no-verify", action="store_true", help="skip the bs1 verify blocks")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--dispatch", type=int, default=0, help="0 auto, 1 one kernel per phase, 2 fused")
@@ -250,6 +252,9 @@ def main():
     print("[bench] bs1 phases (us): " + ", ".join(f"{k} {mean_us[k]:.2f}" for k in PHASES),
           file=sys.stderr, flush=True)
 
+    verify = None if args.no_verify else verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs,
+                                                    base_lens, H, NL, dtype, sid, P0)
+
     result = {
         "metric": "attn-block us/token (28 layers, bs1) + batched tok/s; % HBM roofline",
         "value": round(us_token, 3),
@@ -273,8 +278,11 @@ def main():
         "roofline": roofline(mean_us, bphase, measured_traffic("bs1")),
     }
 
+    if verify is not None:
+        result["verify"] = verify
     if not args.no_batched:
         result["batched"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
+        result["batched_h2048"] = wide_batched_leg(args, ga, si, np, torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -360,6 +368,136 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
             "value": round(tok_s, 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4), "steps": n,
             "step_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
             "roofline": roofline(mean_us, bphase, measured_traffic("b64"))}
+
+
+def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_lens, H, NL, dtype, sid, P0):
+    """k-token verify blocks at bs1 from the committed 795: 28 layer_verify calls captured in one
+    graph, replayed with a crop back to 795 after each (the crop outside the timed events)."""
+    out = {"workload": "28-layer verify block, bs1, fp16, hidden 1024, committed KV 795, k candidates",
+           "unit": "us per 28-layer block"}
+    ws_v = ga.alloc_workspace(cfg, 16, CAP_BS1, device=dev)
+    for k in (4, 8, 16):
+        xv = torch.stack([to_dev(si.activations(sid, l, 1000 + k, k, H, dtype).reshape(1, k, H), dtype)
+                          for l in range(NL)])
+        ov = torch.empty((NL, 1, k, H), dtype=torch.float32, device=dev)
+        ga.kv_crop(kvs, base_lens)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(NL):
+                ga.layer_verify(cfg, weights[l], kvs[l], xv[l], ov[l], ws_v, host_lens=[P0])
+        crop = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(crop):
+            ga.kv_crop(kvs, base_lens)
+        for _ in range(5):
+            g.replay()
+            crop.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(40)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            crop.replay()
+        torch.cuda.synchronize()
+        us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1000.0
+        g.replay()
+        torch.cuda.synchronize()
+        ok = all(int(kv.lens.item()) == P0 + k and int(kv.status.item()) == 0 for kv in kvs)
+        crop.replay()
+        torch.cuda.synchronize()
+        del g, crop
+        out[f"k{k}"] = {"us_per_block": round(us, 2), "us_per_layer_block": round(us / NL, 3),
+                        "us_per_candidate_token": round(us / k, 2), "ok": ok}
+        print(f"[bench] verify bs1 k={k}: {us:.1f} us per 28-layer block, {us / NL:.2f} us per layer, "
+              f"{us / k:.1f} us per candidate token (ok {ok})", file=sys.stderr, flush=True)
+    return out
+
+
+def wide_batched_leg(args, ga, si, np, torch, dev, stream):
+    """Ragged batched decode at hidden 2048 (64 sequences, bf16, lengths uniform in [1024, 4096])
+    and a k = 8 verify on 8 of them.  Weights and caches are drawn on the device from a seeded
+    torch generator (the host generator would take minutes for 18 GB of caches); lengths and the
+    verify choice come from the shared generator."""
+    wl = si.WORKLOADS["ragged_batch64_h2048"]
+    H, NL, B, dtype, sid = wl["hidden"], wl["layers"], wl["batch"], wl["dtype"], wl["stream"]
+    k, nseq = wl["verify_k"][0], wl["verify_seqs"]
+    lens = si.kv_lengths(sid, B, *wl["kv_len"])
+    tdt = torch.bfloat16
+    t0 = time.time()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + sid)
+    nqkv = (16 + 2 * 8) * 128
+
+    def randn(shape, std=1.0, mean=0.0):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std + mean).to(tdt)
+
+    weights, kvs = [], []
+    for _ in range(NL):
+        weights.append(ga.Weights(randn((H,), 0.02, 1.0), randn((nqkv, H), 0.02), randn((128,), 0.02, 1.0),
+                                  randn((128,), 0.02, 1.0), randn((H, 16 * 128), 0.02)))
+        kv = ga.KVLayer(randn((B, 8, CAP_W64, 128)), randn((B, 8, CAP_W64, 128)),
+                        torch.from_numpy(lens.astype(np.int32)).to(dev), torch.zeros(1, dtype=torch.int32, device=dev))
+        kvs.append(kv)
+    xs = randn((NL, B, H))
+    xv = randn((NL, nseq, k, H))
+    outs = torch.empty((NL, B, H), dtype=torch.float32, device=dev)
+    outv = torch.empty((NL, nseq, k, H), dtype=torch.float32, device=dev)
+    cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch, kv_split=args.kv_split)
+    ws = ga.alloc_workspace(cfg, B, CAP_W64, device=dev)
+    wsv = ga.alloc_workspace(cfg, nseq * k, CAP_W64, device=dev)
+    base = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    chosen = si.verify_choice(sid, B, nseq)
+    slots = torch.from_numpy(chosen).to(dev)
+    hl, hlv = lens.tolist(), lens[chosen].tolist()
+    torch.cuda.synchronize()
+    print(f"[bench] batch-64 hidden 2048 inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def timed(calls, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        crop = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(crop):
+            ga.kv_crop(kvs, base)
+        for _ in range(3):
+            g.replay()
+            crop.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            crop.replay()
+        torch.cuda.synchronize()
+        ok = all(int(kv.status.item()) == 0 for kv in kvs) and all(torch.equal(kv.lens, base) for kv in kvs)
+        del g, crop
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])), ok
+
+    def decode_calls():
+        for l in range(NL):
+            ga.layer_decode(cfg, weights[l], kvs[l], xs[l], outs[l], ws, host_lens=hl)
+
+    def verify_calls():
+        for l in range(NL):
+            ga.layer_verify(cfg, weights[l], kvs[l], xv[l], outv[l], wsv, slots=slots, host_lens=hlv)
+
+    ms_dec, ok_d = timed(decode_calls, max(10, args.steps // 8))
+    ms_ver, ok_v = timed(verify_calls, max(10, args.steps // 8))
+    bytes_step = NL * layer_bytes(H, 16, 8, 128, lens.tolist(), B)
+    tok_s = B / (ms_dec * 1e-3)
+    gbs = bytes_step / (ms_dec * 1e-3) / 1e9
+    print(f"[bench] batch-64 hidden 2048: {ms_dec * 1000:.1f} us/step, {tok_s:.0f} tok/s, {gbs:.0f} GB/s (ok {ok_d}); "
+          f"verify k={k} on {nseq} seqs: {ms_ver * 1000:.1f} us per 28-layer block (ok {ok_v})",
+          file=sys.stderr, flush=True)
+    del kvs, weights
+    torch.cuda.empty_cache()
+    return {"workload": "28-layer ragged batched decode, 64 seqs, bf16, hidden 2048, KV U{1024..4096}",
+            "value": round(tok_s, 1), "unit": "tokens/s", "ms_per_step": round(ms_dec, 4),
+            "step_gbs": round(gbs, 1), "step_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ok": ok_d,
+            "verify": {"k": k, "sequences": nseq, "us_per_block": round(ms_ver * 1000, 1),
+                       "us_per_layer_block": round(ms_ver * 1000 / NL, 2), "ok": ok_v}}
 
 
 def cpu_baseline(budget_s):

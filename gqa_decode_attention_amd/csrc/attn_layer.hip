@@ -932,7 +932,11 @@ __device__ __forceinline__ int wcur_next(WCur &c, const LayerArgs &A, const int 
 
 // K and V of one step: lane = key t + (lane >> 3), dims [8 kl, 8 kl + 8) and [64 + 8 kl, ..)
 // (kl = lane & 7); rows clamped to the piece's last committed key, so past
-// the piece the loads hit lines already fetched.
+// the piece the loads hit lines already fetched.  NT: the call reads each
+// cached row once (one row per sequence), so the stream carries the
+// nontemporal hint; rows of a verify block read their sequence's rows again
+// and keep plain loads.
+template <bool NT>
 __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, uint4 (&r)[4]) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
   // (the cursor is wave-uniform; readfirstlane keeps the resources in scalar registers)
@@ -942,10 +946,10 @@ __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, ui
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + base, region);
   const int last = max(min(rfl(c.te), rfl(c.L)) - 1, 0);
   const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * (kHeadDim * 2) + kl * 16;
-  r[0] = ld_buf_nt(Kr, off);
-  r[1] = ld_buf_nt(Kr, off + 128);
-  r[2] = ld_buf_nt(Vr, off);
-  r[3] = ld_buf_nt(Vr, off + 128);
+  r[0] = NT ? ld_buf_nt(Kr, off) : ld_buf(Kr, off);
+  r[1] = NT ? ld_buf_nt(Kr, off + 128) : ld_buf(Kr, off + 128);
+  r[2] = NT ? ld_buf_nt(Vr, off) : ld_buf(Vr, off);
+  r[3] = NT ? ld_buf_nt(Vr, off + 128) : ld_buf(Vr, off + 128);
 }
 
 // One lane's 8 dims of an appended row, 16-bit as stored: k normalised with
@@ -1048,7 +1052,7 @@ __device__ __forceinline__ void wresolve(const LayerArgs &A, const WPending &p) 
   if (old == (uint32_t)(p.np - 1)) merge_wave<DT, GROUP>(A, p.row, p.g, p.np);
 }
 
-template <int DT, int GROUP>
+template <int DT, int GROUP, bool NT>
 __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *rinfo, int w, int W) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
   const int d0 = 8 * kl, d1 = 64 + 8 * kl;
@@ -1070,9 +1074,9 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   // three register sets in rotation: the loads of step i + 2 are issued before
   // the arithmetic of step i, into the set step i - 1 has released
   uint4 ra[4], rb[4], rc[4];
-  wstep_load(A, lc, ra);
+  wstep_load<NT>(A, lc, ra);
   wcur_next(lc, A, pre, rinfo);
-  wstep_load(A, lc, rb);
+  wstep_load<NT>(A, lc, rb);
   wcur_next(lc, A, pre, rinfo);
 
   const float qs = kLog2e * rsqrtf((float)kHeadDim);
@@ -1234,7 +1238,7 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   };
 
   auto issue = [&](uint4 (&r)[4]) {
-    wstep_load(A, lc, r);
+    wstep_load<NT>(A, lc, r);
     wcur_next(lc, A, pre, rinfo);
   };
   // arithmetic of cc's step, then advance cc: false past the share
@@ -2000,14 +2004,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
 }
 
 // many rows: equal key shares per wave of a resident grid
-template <int DT, int GROUP>
+template <int DT, int GROUP, bool NT>
 __global__ __launch_bounds__(256) void k_attn_waves(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ int wsum[4];
   int4 *rinfo = reinterpret_cast<int4 *>(dyn);
   int *pre = reinterpret_cast<int *>(rinfo + A.rows);
   build_item_prefix<true>(A, pre, rinfo, wsum);
-  attention_waves<DT, GROUP>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
+  attention_waves<DT, GROUP, NT>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
 }
 
 __host__ __device__ __forceinline__ size_t lds_attn_waves_bytes(int rows) {
@@ -2421,10 +2425,10 @@ LayerKernel pick_oproj_merge(int kvo, int nch_host) {
 }
 
 template <int DT>
-LayerKernel pick_attn_waves(int group) {
+LayerKernel pick_attn_waves(int group, bool nt) {
   switch (group) {
-    case 2: return k_attn_waves<DT, 2>;
-    case 4: return k_attn_waves<DT, 4>;
+    case 2: return nt ? k_attn_waves<DT, 2, true> : k_attn_waves<DT, 2, false>;
+    case 4: return nt ? k_attn_waves<DT, 4, true> : k_attn_waves<DT, 4, false>;
     default: return nullptr;
   }
 }
@@ -2479,7 +2483,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                         lds_x, s, ev, 2, a);
   }
   if (attn_waves_used(a)) {
-    if ((e = launch_phase(pick_attn_waves<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
+    if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
                           ev, 1, a)) != hipSuccess)
       return e;
   } else if ((e = launch_phase(pick_attn<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
@@ -2562,7 +2566,7 @@ int attn_waves_grid(int dtype, int group, int cus) {
   if (group != 2 && group != 4) return 0;
   int per_cu = cached[di][group];
   if (per_cu <= 0) {
-    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group) : pick_attn_waves<ASR_F16>(group);
+    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, true) : pick_attn_waves<ASR_F16>(group, true);
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_attn_waves_bytes(kMaxLayerRows)) !=
                   hipSuccess || per_cu <= 0)
       return 0;

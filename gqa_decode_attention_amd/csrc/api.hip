@@ -163,6 +163,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.theta = cfg->rope_theta;
   a.out_f32 = cfg->out_dtype == ASR_F32;
   a.mfma = rows > kVectorRows;
+  a.oproj_split = 0;
 
   // upper bound of attention work items; blocks stride over the real count.
   // nch_host: the most chunks of any row, by the host's view of the lengths
@@ -198,6 +199,9 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
     fused = fused_grid > 0;
   }
   if (cfg->dispatch == ASR_DISPATCH_FUSED && !fused) return ASR_EUNSUPPORTED;
+  // few rows with an fp32 output: o_proj in two head halves, each workgroup
+  // reading half the chunk partials (the projection kernel zeroes the output)
+  if (!fused && !a.mfma && a.out_f32 && a.nq % 8 == 0 && a.H % 64 == 0) a.oproj_split = 1;
   hipEvent_t *ev = cfg->phase_events;
   hipError_t e;
   if (fused) {

@@ -1695,6 +1695,11 @@ __global__ __launch_bounds__(256) void k_qkv(LayerArgs A) {
   uint4 wr[4][KV];
   qkv_tile<DT, KV, RB, false, true>(A, blockIdx.x, s_ssq, wr);
   if (blockIdx.x == 0) write_row_table<false>(A);
+  if (A.oproj_split) {   // the fp32 output that the two o_proj halves add into
+    const int n4 = A.rows * A.H / 4;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x)
+      reinterpret_cast<float4 *>(A.out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 }
 
 template <int DT, int GROUP>
@@ -2067,13 +2072,24 @@ __device__ __forceinline__ float group_sum(float v) {
 // with the W_o rows and the row table, before the row's chunk count is known;
 // the chunks past it weigh zero and their values are never used (their slots
 // hold an older call's values).
-template <int DT, int KV, int RPW, int CB>
+// SPLIT: two workgroups share output rows: each merges and contracts one half
+// of the heads, and both add into the fp32 output that the projection kernel
+// zeroed (two terms onto zero: the sum is the same in either order); the
+// residual comes with the first half.  The pair is b and b + 8 in each group
+// of 16 workgroups, so both run on the same XCD (workgroups go round-robin
+// over the 8 XCDs).
+template <int DT, int KV, int RPW, int CB, bool SPLIT>
 __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
-  float *xs = reinterpret_cast<float *>(dyn);   // [rows][nq d]
+  float *xs = reinterpret_cast<float *>(dyn);   // [rows][this workgroup's heads x d]
   __shared__ float s_w[32][kMaxChunks];          // merge weights [head][chunk] (nq <= 32)
   constexpr int NS = (KV + 1) / 2;              // float4 columns per thread (nq d = 512 KV)
-  const int K = A.nq * kHeadDim, K4 = K / 4;
+  const int b = blockIdx.x;
+  const int hh = SPLIT ? (b >> 3) & 1 : 0;                            // head half
+  const int tile = SPLIT ? (b & 7) | ((b >> 4) << 3) : b;             // output rows
+  const int nqb = SPLIT ? A.nq / 2 : A.nq, h0 = hh * nqb;              // heads of this workgroup
+  const int K = nqb * kHeadDim, K4 = K / 4;
+  const int Kw = A.nq * kHeadDim;                                      // W_o row length
   const int t = threadIdx.x;
   const int cs = A.group * kPartStride;         // floats per chunk of a kv head
   // partial of head h, chunk c of `row` (chunk index clamped into the slots)
@@ -2082,18 +2098,18 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
     return A.part + (((size_t)row * A.nkv + g) * kMaxChunks * A.group + j) * kPartStride +
            (size_t)min(c, kMaxChunks - 1) * cs;
   };
-  const int hq = min(t / CB, A.nq - 1), cq = t % CB;   // weights: head and first chunk of this thread
-  const bool wt = t < A.nq * CB;
+  const int hq = min(t / CB, nqb - 1), cq = t % CB;   // weights: (local) head and first chunk of this thread
+  const bool wt = t < nqb * CB;
   // a row's merge inputs: its table record, this thread's (m, l) and the columns of the first CB chunks
   auto merge_loads = [&](int row, int4 &rt, float2 &ml0, float4 (&av)[NS][CB]) __attribute__((always_inline)) {
     rt = A.rowtab[row];
-    ml0 = *reinterpret_cast<const float2 *>(part_of(row, hq, cq) + 128);
+    ml0 = *reinterpret_cast<const float2 *>(part_of(row, h0 + hq, cq) + 128);
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       const int q4 = min(t + 256 * s2, K4 - 1);
 #pragma unroll
       for (int c = 0; c < CB; ++c)
-        av[s2][c] = *reinterpret_cast<const float4 *>(part_of(row, q4 / 32, c) + (q4 % 32) * 4);
+        av[s2][c] = *reinterpret_cast<const float4 *>(part_of(row, h0 + q4 / 32, c) + (q4 % 32) * 4);
     }
   };
   // The first row's merge inputs are requested before the W_o rows: a wait on a
@@ -2104,7 +2120,14 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   merge_loads(0, rt_0, ml0_0, av_0);
   __builtin_amdgcn_sched_barrier(0);
   uint4 wr[RPW][KV];
-  load_wo<KV, RPW>(A, blockIdx.x, wr);
+  {
+    const int o0 = (tile * 4 + wave_id()) * RPW;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int v = 0; v < KV; ++v)
+        wr[i][v] = ld16_stream(A.w_o + (size_t)(o0 + i) * Kw + hh * K + (v * 64 + lane_id()) * 8);
+  }
   for (int row = 0; row < A.rows; ++row) {
     int4 rt = rt_0;
     float2 ml0 = ml0_0;
@@ -2117,18 +2140,18 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
     const int nch = chunks_of(rt.x ? rt.y + row % A.n + 1 : 0, A.split);
     // weights
     float mx = cq < nch ? ml0.x : -INFINITY;
-    for (int c = cq + CB; c < nch; c += CB) mx = fmaxf(mx, part_of(row, hq, c)[128]);
+    for (int c = cq + CB; c < nch; c += CB) mx = fmaxf(mx, part_of(row, h0 + hq, c)[128]);
     const float M = group_max<CB>(mx);
     const float w0 = cq < nch ? exp2_neg(ml0.x - M) : 0.f;
     float den = w0 * (cq < nch ? ml0.y : 0.f);
     for (int c = cq + CB; c < nch; c += CB) {
-      const float2 v = *reinterpret_cast<const float2 *>(part_of(row, hq, c) + 128);
+      const float2 v = *reinterpret_cast<const float2 *>(part_of(row, h0 + hq, c) + 128);
       den += exp2_neg(v.x - M) * v.y;
     }
     const float inv = 1.0f / group_sum<CB>(den);
     if (wt) {
       s_w[hq][cq] = w0 * inv;
-      for (int c = cq + CB; c < nch; c += CB) s_w[hq][c] = exp2_neg(part_of(row, hq, c)[128] - M) * inv;
+      for (int c = cq + CB; c < nch; c += CB) s_w[hq][c] = exp2_neg(part_of(row, h0 + hq, c)[128] - M) * inv;
     }
     __syncthreads();
     // columns
@@ -2147,7 +2170,7 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       }
       for (int c = CB; c < nch; ++c) {
         const float w = s_w[h][c];
-        const float4 v = *reinterpret_cast<const float4 *>(part_of(row, h, c) + (q4 % 32) * 4);
+        const float4 v = *reinterpret_cast<const float4 *>(part_of(row, h0 + h, c) + (q4 % 32) * 4);
         num.x += w * v.x;
         num.y += w * v.y;
         num.z += w * v.z;
@@ -2159,7 +2182,7 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   }
   __syncthreads();
   const int wave = wave_id(), lane = lane_id();
-  const int o0 = (blockIdx.x * 4 + wave) * RPW;
+  const int o0 = (tile * 4 + wave) * RPW;
   for (int row = 0; row < A.rows; ++row) {
     float acc[RPW];
 #pragma unroll
@@ -2185,9 +2208,10 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       for (int i = 1; i < RPW; ++i)
         if (lane == i) val = acc[i];
       const size_t o = (size_t)row * A.H + o0 + lane;
-      if (A.residual) val += cvt16<DT>(A.residual[o]);
+      if (A.residual && hh == 0) val += cvt16<DT>(A.residual[o]);
       if (!A.rowtab[row].x) val = __builtin_nanf("");
-      if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
+      if (SPLIT) __hip_atomic_fetch_add(reinterpret_cast<float *>(A.out) + o, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
       else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
     }
   }
@@ -2409,13 +2433,22 @@ int few_waves(int group) { return group <= 2 ? 8 : 4; }
 // the partials of as many chunks as the host expects (4, 8, or 16 while two
 // float4 columns per thread keep that within registers) requested at once
 template <int DT>
-LayerKernel pick_oproj_merge(int kvo, int nch_host) {
+LayerKernel pick_oproj_merge(int kvo, int nch_host, bool split) {
   const int cb = nch_host <= 4 ? 4 : (nch_host > 8 && kvo <= 4 ? 16 : 8);
+  if (split) {   // each workgroup: half the heads (kvo / 2 float8 columns per lane), two output rows per wave
+    switch (kvo / 2) {
+#define ASR_PICK_OPROJ_HALF(K) \
+      case K: return cb == 4 ? k_oproj_merge<DT, K, 2, 4, true> : k_oproj_merge<DT, K, 2, 8, true>;
+      ASR_PICK_OPROJ_HALF(1) ASR_PICK_OPROJ_HALF(2) ASR_PICK_OPROJ_HALF(3) ASR_PICK_OPROJ_HALF(4)
+#undef ASR_PICK_OPROJ_HALF
+      default: return nullptr;
+    }
+  }
   switch (kvo) {
 #define ASR_PICK_OPROJ_MERGE(K) \
-    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4> : cb == 16 ? k_oproj_merge<DT, K, kRpwD, 16> : k_oproj_merge<DT, K, kRpwD, 8>;
+    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4, false> : cb == 16 ? k_oproj_merge<DT, K, kRpwD, 16, false> : k_oproj_merge<DT, K, kRpwD, 8, false>;
 #define ASR_PICK_OPROJ_MERGE8(K) \
-    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4> : k_oproj_merge<DT, K, kRpwD, 8>;
+    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4, false> : k_oproj_merge<DT, K, kRpwD, 8, false>;
     ASR_PICK_OPROJ_MERGE(1) ASR_PICK_OPROJ_MERGE(2) ASR_PICK_OPROJ_MERGE(3) ASR_PICK_OPROJ_MERGE(4)
     ASR_PICK_OPROJ_MERGE8(5) ASR_PICK_OPROJ_MERGE8(6) ASR_PICK_OPROJ_MERGE8(7) ASR_PICK_OPROJ_MERGE8(8)
 #undef ASR_PICK_OPROJ_MERGE
@@ -2478,9 +2511,10 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
     if ((e = launch_phase(pick_attn_few<DT>(a.group), dim3(a.rows * a.nkv * a.nch_host), dim3(few_waves(a.group) * kWave),
                           lds_kv, s, ev, 1, a)) != hipSuccess)
       return e;
-    const unsigned lds_x = (unsigned)(a.rows * a.nq * kHeadDim * sizeof(float));
-    return launch_phase(pick_oproj_merge<DT>(a.nq * kHeadDim / 512, a.nch_host), dim3(a.H / (4 * kRpwD)), dim3(256),
-                        lds_x, s, ev, 2, a);
+    const int halves = a.oproj_split ? 2 : 1, rpw = a.oproj_split ? 2 : kRpwD;
+    const unsigned lds_x = (unsigned)(a.rows * a.nq / halves * kHeadDim * sizeof(float));
+    return launch_phase(pick_oproj_merge<DT>(a.nq * kHeadDim / 512, a.nch_host, a.oproj_split != 0),
+                        dim3(a.H / (4 * rpw) * halves), dim3(256), lds_x, s, ev, 2, a);
   }
   if (attn_waves_used(a)) {
     if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,

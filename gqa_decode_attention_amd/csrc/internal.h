@@ -55,6 +55,7 @@ struct LayerArgs {
   float eps, theta;
   int out_f32;
   int mfma;                   // projections on MFMA (more than a few rows)
+  int oproj_split;            // few rows, fp32 out: o_proj in two head halves adding into the zeroed output
 };
 
 struct WorkspaceLayout {

@@ -156,6 +156,9 @@ size_t asr_attn_workspace_bytes(const asr_attn_config *cfg, int32_t max_rows, in
  *   host_lens  HOST [B] or NULL: the caller's copy of lens[slots[i]], used only
  *            to size the launch and for the ASR_ECAPACITY check; the device
  *            lengths remain the truth.
+ * out must not overlap x, residual, the cache or the workspace: with an fp32
+ * out and a few rows it is zeroed by the call's first kernel and accumulated
+ * by its last.
  */
 int asr_attn_layer_decode(const asr_attn_config *cfg, const asr_attn_weights *w,
                           const asr_kv_layer *kv, const void *x, const int32_t *slots,

@@ -1475,13 +1475,24 @@ constexpr int chunk_steps(int kq) {
 // row tiles share each split weight step); the 16 features are 8 rotary pairs
 // (t, t + 64) of one head, as in the vector path, with the same epilogue: gain
 // and rotation of q/k pairs, partial sums of squares, v stored raw.
-template <int DT, int KQ, int NWV>
+// LX (hidden 1024, eight waves): each wave loads its 64 rows x 256 bytes of x
+// as whole 128-byte lines (four rows per instruction) into its own LDS region
+// and reads the operand layout back from there: the operand layout touches 16
+// rows per load, half a line each, and a CU keeps only so many lines in flight.
+template <int DT, int KQ, int NWV, bool LX>
 __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
   constexpr int KW = KQ * 4 / NWV;      // 32-wide steps of this wave's share of the contraction
   constexpr int KC = KW < 8 ? KW : 8;   // steps per operand batch (x of four row tiles)
-  __shared__ f32x4_t s_c[NWV][4][kWave];
+  static_assert(!LX || (KQ == 8 && NWV == 8), "x staging: 16 KB per wave");
+  extern __shared__ __align__(16) unsigned char dyn[];   // LX: [NWV][64 rows][256 B] x, then the wave's sums
+  __shared__ f32x4_t s_cs[LX ? 1 : NWV][4][kWave];
   __shared__ float s_ss[NWV][64];
   __shared__ float2 s_rope[64][8];   // (cos, sin) for the block's 64 rows x its 8 rotary pairs
+  // the waves' sums: LX in each wave's own staging region (its x is read by then)
+  auto s_c_at = [&](int wv, int nt) __attribute__((always_inline)) -> f32x4_t * {
+    if constexpr (LX) return reinterpret_cast<f32x4_t *>(dyn + wv * 16384) + nt * kWave;
+    else return &s_cs[wv][nt][0];
+  };
   const int wave = wave_id(), lane = lane_id();
   const int rtiles = (A.rows + 63) / 64;
   const TileMap tm = tile_of(blockIdx.x, rtiles);
@@ -1515,12 +1526,22 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
 #pragma unroll 1
   for (int c0 = 0; c0 < KW; c0 += KC) {
     uint4 w[KC], g[KC], x[4][KC];
+    uint4 xl[LX ? 16 : 1];
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
       w[s] = ld16_stream(wp + (c0 + s) * 32);
       g[s] = ld16(A.g_in + kq0 + (c0 + s) * 32);
+      if constexpr (!LX) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) x[nt][s] = ld16(xr[nt] + (c0 + s) * 32);
+        for (int nt = 0; nt < 4; ++nt) x[nt][s] = ld16(xr[nt] + (c0 + s) * 32);
+      }
+    }
+    if constexpr (LX) {   // instruction j: rows 4 j .. 4 j + 3, sixteen 16-byte chunks each
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int f = j * 64 + lane, r = f >> 4, ch = f & 15;
+        xl[j] = ld16(A.x + (size_t)min(nb + r, A.rows - 1) * H + wave * (H / NWV) + ch * 8);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
     if (c0 == 0 && rot) {   // rotary angles of the 64 rows x 8 pairs in fp64 while the operands travel
@@ -1537,6 +1558,21 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
         }
         s_rope[r][tt] = make_float2(cs, sn);
       }
+    }
+    if constexpr (LX) {   // own region, chunk ch of row r at chunk ch ^ (r & 15): both patterns conflict-free
+      unsigned char *xw = dyn + wave * 16384;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int f = j * 64 + lane, r = f >> 4, ch = f & 15;
+        *reinterpret_cast<uint4 *>(xw + r * 256 + ((ch ^ (r & 15)) << 4)) = xl[j];
+      }
+#pragma unroll
+      for (int s = 0; s < KC; ++s)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int r = nt * 16 + i16, ch = s * 4 + g4;
+          x[nt][s] = lds_ld16(reinterpret_cast<const uint16_t *>(xw + r * 256 + ((ch ^ (r & 15)) << 4)));
+        }
     }
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
@@ -1562,7 +1598,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
   }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    s_c[wave][nt][lane] = acc[nt];
+    s_c_at(wave, nt)[lane] = acc[nt];
     float v = ss[nt];
     v = xsum<16>(v);
     v = xsum<32>(v);
@@ -1572,11 +1608,11 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
   if (wave < 4) {   // wave nt finishes row tile nt
     const int nt = wave;
     const int n = nb + nt * 16 + i16;
-    f32x4_t c = s_c[0][nt][lane];
+    f32x4_t c = s_c_at(0, nt)[lane];
     float ssx = s_ss[0][nt * 16 + i16];
 #pragma unroll
     for (int wv = 1; wv < NWV; ++wv) {
-      const f32x4_t d = s_c[wv][nt][lane];
+      const f32x4_t d = s_c_at(wv, nt)[lane];
       c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
       ssx += s_ss[wv][nt * 16 + i16];
     }
@@ -2377,14 +2413,14 @@ int qkv_mfma_waves(int kq) { return kq <= 16 ? 8 : 4; }
 template <int DT>
 LayerKernel pick_qkv_mfma(int kq) {
   switch (kq) {
-    case 4: return k_qkv_mfma<DT, 4, 8>;
-    case 8: return k_qkv_mfma<DT, 8, 8>;
-    case 12: return k_qkv_mfma<DT, 12, 8>;
-    case 16: return k_qkv_mfma<DT, 16, 8>;
-    case 20: return k_qkv_mfma<DT, 20, 4>;
-    case 24: return k_qkv_mfma<DT, 24, 4>;
-    case 28: return k_qkv_mfma<DT, 28, 4>;
-    case 32: return k_qkv_mfma<DT, 32, 4>;
+    case 4: return k_qkv_mfma<DT, 4, 8, false>;
+    case 8: return k_qkv_mfma<DT, 8, 8, true>;
+    case 12: return k_qkv_mfma<DT, 12, 8, false>;
+    case 16: return k_qkv_mfma<DT, 16, 8, false>;
+    case 20: return k_qkv_mfma<DT, 20, 4, false>;
+    case 24: return k_qkv_mfma<DT, 24, 4, false>;
+    case 28: return k_qkv_mfma<DT, 28, 4, false>;
+    case 32: return k_qkv_mfma<DT, 32, 4, false>;
     default: return nullptr;
   }
 }
@@ -2497,7 +2533,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
     // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
     const int rtiles = (a.rows + 63) / 64;
     if ((e = launch_phase(pick_qkv_mfma<DT>(a.H / 128), dim3(a.nqkv / 16 * rtiles), dim3(qkv_mfma_waves(a.H / 128) * kWave),
-                          0, s, ev, 0, a)) !=
+                          a.H / 128 == 8 ? 8 * 16384 : 0, s, ev, 0, a)) !=
         hipSuccess)
       return e;
   } else {

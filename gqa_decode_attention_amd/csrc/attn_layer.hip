@@ -1650,10 +1650,15 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
 
 // o_proj: out[n][o] = sum_c W_o[o][c] att[n][c] (+ residual), att as hi + lo terms
 // read from its tiled copy [plane][c / 32][row][32].
-template <int DT, int KQ, int NWV>
+// LW (nq d = 2048, eight waves): each wave loads its 16 W_o rows x 512 bytes
+// as whole lines (two rows per instruction) into its own 8 KB of LDS and reads
+// the operand layout back (chunk c of row r stored at chunk c ^ (r mod 16)).
+template <int DT, int KQ, int NWV, bool LW>
 __global__ __launch_bounds__(NWV * 64) void k_oproj_mfma(LayerArgs A) {
   constexpr int KW = KQ * 4 / NWV;   // 32-wide steps of this wave's share of the contraction
   constexpr int KC = chunk_steps(KW);
+  static_assert(!LW || (KQ == 16 && NWV == 8 && KC == 8), "W staging: 8 KB per wave, one batch");
+  extern __shared__ __align__(16) unsigned char dyn[];   // LW: [NWV][16 rows][512 B] of W_o
   __shared__ f32x4_t s_c[NWV][kWave];
   const int wave = wave_id(), lane = lane_id();
   const int i16 = lane % 16, g4 = lane / 16;
@@ -1685,11 +1690,29 @@ __global__ __launch_bounds__(NWV * 64) void k_oproj_mfma(LayerArgs A) {
     uint4 w[KC], hi[KC], lo[KC];
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
-      w[s] = ld16_stream(wp + (c0 + s) * 32);
+      if constexpr (LW) {   // instruction s: rows 2 s, 2 s + 1, thirty-two 16-byte chunks each
+        const int f = s * 64 + lane, r = f >> 5, ch = f & 31;
+        w[s] = ld16_stream(A.w_o + (size_t)(o0 + r) * K + wave * (K / NWV) + ch * 8);
+      } else {
+        w[s] = ld16_stream(wp + (c0 + s) * 32);
+      }
       hi[s] = ld16(bp + (c0 + s) * kstep);
       lo[s] = ld16(bp + plane + (c0 + s) * kstep);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
+    if constexpr (LW) {
+      unsigned char *ww = dyn + wave * 8192;
+#pragma unroll
+      for (int s = 0; s < KC; ++s) {
+        const int f = s * 64 + lane, r = f >> 5, ch = f & 31;
+        *reinterpret_cast<uint4 *>(ww + r * 512 + ((ch ^ (r & 15)) << 4)) = w[s];
+      }
+#pragma unroll
+      for (int s = 0; s < KC; ++s) {
+        const int ch = s * 4 + g4;
+        w[s] = lds_ld16(reinterpret_cast<const uint16_t *>(ww + i16 * 512 + ((ch ^ i16) << 4)));
+      }
+    }
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
       acc = mfma16x16x32<DT>(w[s], hi[s], acc);
@@ -2428,14 +2451,14 @@ LayerKernel pick_qkv_mfma(int kq) {
 template <int DT>
 LayerKernel pick_oproj_mfma(int kq) {
   switch (kq) {
-    case 4: return k_oproj_mfma<DT, 4, 8>;
-    case 8: return k_oproj_mfma<DT, 8, 8>;
-    case 12: return k_oproj_mfma<DT, 12, 8>;
-    case 16: return k_oproj_mfma<DT, 16, 8>;
-    case 20: return k_oproj_mfma<DT, 20, 8>;
-    case 24: return k_oproj_mfma<DT, 24, 8>;
-    case 28: return k_oproj_mfma<DT, 28, 8>;
-    case 32: return k_oproj_mfma<DT, 32, 8>;
+    case 4: return k_oproj_mfma<DT, 4, 8, false>;
+    case 8: return k_oproj_mfma<DT, 8, 8, false>;
+    case 12: return k_oproj_mfma<DT, 12, 8, false>;
+    case 16: return k_oproj_mfma<DT, 16, 8, true>;
+    case 20: return k_oproj_mfma<DT, 20, 8, false>;
+    case 24: return k_oproj_mfma<DT, 24, 8, false>;
+    case 28: return k_oproj_mfma<DT, 28, 8, false>;
+    case 32: return k_oproj_mfma<DT, 32, 8, false>;
     default: return nullptr;
   }
 }
@@ -2562,7 +2585,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
   }
   if (a.mfma)
     return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 128), dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(512),
-                        0, s, ev, 2, a);
+                        a.nq * kHeadDim == 2048 ? 8 * 8192 : 0, s, ev, 2, a);
   return launch_phase(pick_oproj<DT>(a.nq * kHeadDim / 512, a.rows == 1), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s,
                       ev, 2, a);
 }

@@ -1529,7 +1529,13 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
     uint4 xl[LX ? 16 : 1];
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
-      w[s] = ld16_stream(wp + (c0 + s) * 32);
+      if constexpr (LX) {   // W too as whole lines: instruction s, rows 4 s .. 4 s + 3 of the tile
+        const int f = s * 64 + lane, r = f >> 4, ch = f & 15;
+        const int wrow = head * kHeadDim + (r < 8 ? t0 + r : 64 + t0 + r - 8);
+        w[s] = ld16_stream(A.w_qkv + (size_t)wrow * H + wave * (H / NWV) + ch * 8);
+      } else {
+        w[s] = ld16_stream(wp + (c0 + s) * 32);
+      }
       g[s] = ld16(A.g_in + kq0 + (c0 + s) * 32);
       if constexpr (!LX) {
 #pragma unroll
@@ -1573,6 +1579,17 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
           const int r = nt * 16 + i16, ch = s * 4 + g4;
           x[nt][s] = lds_ld16(reinterpret_cast<const uint16_t *>(xw + r * 256 + ((ch ^ (r & 15)) << 4)));
         }
+      // then W's 16 rows x 256 B through the first 4 KB of the same region (its x is in registers now)
+#pragma unroll
+      for (int s = 0; s < KC; ++s) {
+        const int f = s * 64 + lane, r = f >> 4, ch = f & 15;
+        *reinterpret_cast<uint4 *>(xw + r * 256 + ((ch ^ r) << 4)) = w[s];
+      }
+#pragma unroll
+      for (int s = 0; s < KC; ++s) {
+        const int ch = s * 4 + g4;
+        w[s] = lds_ld16(reinterpret_cast<const uint16_t *>(xw + i16 * 256 + ((ch ^ i16) << 4)));
+      }
     }
 #pragma unroll
     for (int s = 0; s < KC; ++s) {

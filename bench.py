@@ -48,9 +48,9 @@ PAGES_US_PER_TOKEN = 9033.0
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99994, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "1601054210a0355ba0f7652d04bd9c44e667dfdf39b0347e96d026a73657f916",
-    "bs1": {"qkv_projection": 8583097, "attention": 4048358, "o_proj": 4862001},
-    "b64": {"qkv_projection": 11063191, "attention": 230249765, "o_proj": 8700042},
+    "sources_sha256": "86b4dc98ed0c9ee0282ed4551f3c80a463875caaa6a1570833e4c8467d5b1b77",
+    "bs1": {"qkv_projection": 8583097, "attention": 4048563, "o_proj": 4862001},
+    "b64": {"qkv_projection": 11077731, "attention": 230242802, "o_proj": 8722569},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",

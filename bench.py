@@ -13,6 +13,9 @@ timed region (the static one-token step of that page's section 08, step 2).
 Second workload (``--no-batched`` skips it): ragged batched decode of 64
 sequences in bf16, committed lengths uniform in [200, 1500]; one step = 28
 layer calls + the crop back to the committed lengths, reported in tokens/s.
+Also reported: the bs1 verify block for k = 4, 8, 16 (``--no-verify``) and
+the hidden-2048 batch-64 decode with a k = 8 verify on 8 sequences
+(``--no-wide``).
 
 Roofline: a second timed region replays the same calls eagerly with HIP
 events that the library has the runtime stamp at the start and end of each

@@ -32,6 +32,8 @@
 // candidates up to i.
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -40,7 +42,8 @@ namespace asr {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr long long kBarrierTimeoutTicks = 50000000;   // wall clock ticks (0.05 s at 1 GHz)
+constexpr long long kBarrierTimeoutTicks = 50000000;   // wall clock ticks: 0.5 s at the 100 MHz constant clock
+                                                      // gfx9 parts report (hipDeviceAttributeWallClockRate)
 constexpr int kRpwA = 4;                              // phase A rows per wave: tiles of 16 rows
 constexpr int kTilesPerHead = kHeadDim / (4 * kRpwA); // 8
 constexpr int kRpwD = 1;                              // phase D rows per wave: tiles of 4 rows
@@ -1567,11 +1570,13 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
     }
     if constexpr (LX) {   // own region, chunk ch of row r at chunk ch ^ (r & 15): both patterns conflict-free
       unsigned char *xw = dyn + wave * 16384;
+      wave_lds_sync();   // the previous batch's reads of the region are done
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int f = j * 64 + lane, r = f >> 4, ch = f & 15;
         *reinterpret_cast<uint4 *>(xw + r * 256 + ((ch ^ (r & 15)) << 4)) = xl[j];
       }
+      wave_lds_sync();   // x stored by every lane before any lane reads the operand layout
 #pragma unroll
       for (int s = 0; s < KC; ++s)
 #pragma unroll
@@ -1580,11 +1585,13 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
           x[nt][s] = lds_ld16(reinterpret_cast<const uint16_t *>(xw + r * 256 + ((ch ^ (r & 15)) << 4)));
         }
       // then W's 16 rows x 256 B through the first 4 KB of the same region (its x is in registers now)
+      wave_lds_sync();   // every lane's x reads done before W overwrites them
 #pragma unroll
       for (int s = 0; s < KC; ++s) {
         const int f = s * 64 + lane, r = f >> 4, ch = f & 15;
         *reinterpret_cast<uint4 *>(xw + r * 256 + ((ch ^ r) << 4)) = w[s];
       }
+      wave_lds_sync();   // W stored before the operand-layout reads
 #pragma unroll
       for (int s = 0; s < KC; ++s) {
         const int ch = s * 4 + g4;
@@ -1613,6 +1620,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
       }
     }
   }
+  if constexpr (LX) wave_lds_sync();   // W reads done before the sums overwrite the region
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     s_c_at(wave, nt)[lane] = acc[nt];
@@ -1719,11 +1727,13 @@ __global__ __launch_bounds__(NWV * 64) void k_oproj_mfma(LayerArgs A) {
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
     if constexpr (LW) {
       unsigned char *ww = dyn + wave * 8192;
+      wave_lds_sync();   // the previous batch's reads of the region are done
 #pragma unroll
       for (int s = 0; s < KC; ++s) {
         const int f = s * 64 + lane, r = f >> 5, ch = f & 31;
         *reinterpret_cast<uint4 *>(ww + r * 512 + ((ch ^ (r & 15)) << 4)) = w[s];
       }
+      wave_lds_sync();   // W_o stored by every lane before the operand-layout reads
 #pragma unroll
       for (int s = 0; s < KC; ++s) {
         const int ch = s * 4 + g4;
@@ -2450,33 +2460,41 @@ hipError_t launch_phase(LayerKernel kern, dim3 grid, dim3 block, unsigned lds, h
 // operand batch fits its registers, else four
 int qkv_mfma_waves(int kq) { return kq <= 16 ? 8 : 4; }
 
+// a matrix-core projection kernel and the dynamic LDS bytes it is launched with
+struct MfmaKernel {
+  LayerKernel fn;
+  unsigned lds;
+};
+
+// LX / LW instances stage each wave's operand lines through LDS: 16 KB (x, then
+// W) or 8 KB (W_o) per wave
 template <int DT>
-LayerKernel pick_qkv_mfma(int kq) {
+MfmaKernel pick_qkv_mfma(int kq) {
   switch (kq) {
-    case 4: return k_qkv_mfma<DT, 4, 8, false>;
-    case 8: return k_qkv_mfma<DT, 8, 8, true>;
-    case 12: return k_qkv_mfma<DT, 12, 8, false>;
-    case 16: return k_qkv_mfma<DT, 16, 8, false>;
-    case 20: return k_qkv_mfma<DT, 20, 4, false>;
-    case 24: return k_qkv_mfma<DT, 24, 4, false>;
-    case 28: return k_qkv_mfma<DT, 28, 4, false>;
-    case 32: return k_qkv_mfma<DT, 32, 4, false>;
-    default: return nullptr;
+    case 4: return {k_qkv_mfma<DT, 4, 8, false>, 0};
+    case 8: return {k_qkv_mfma<DT, 8, 8, true>, 8 * 16384};
+    case 12: return {k_qkv_mfma<DT, 12, 8, false>, 0};
+    case 16: return {k_qkv_mfma<DT, 16, 8, false>, 0};
+    case 20: return {k_qkv_mfma<DT, 20, 4, false>, 0};
+    case 24: return {k_qkv_mfma<DT, 24, 4, false>, 0};
+    case 28: return {k_qkv_mfma<DT, 28, 4, false>, 0};
+    case 32: return {k_qkv_mfma<DT, 32, 4, false>, 0};
+    default: return {nullptr, 0};
   }
 }
 
 template <int DT>
-LayerKernel pick_oproj_mfma(int kq) {
+MfmaKernel pick_oproj_mfma(int kq) {
   switch (kq) {
-    case 4: return k_oproj_mfma<DT, 4, 8, false>;
-    case 8: return k_oproj_mfma<DT, 8, 8, false>;
-    case 12: return k_oproj_mfma<DT, 12, 8, false>;
-    case 16: return k_oproj_mfma<DT, 16, 8, true>;
-    case 20: return k_oproj_mfma<DT, 20, 8, false>;
-    case 24: return k_oproj_mfma<DT, 24, 8, false>;
-    case 28: return k_oproj_mfma<DT, 28, 8, false>;
-    case 32: return k_oproj_mfma<DT, 32, 8, false>;
-    default: return nullptr;
+    case 4: return {k_oproj_mfma<DT, 4, 8, false>, 0};
+    case 8: return {k_oproj_mfma<DT, 8, 8, false>, 0};
+    case 12: return {k_oproj_mfma<DT, 12, 8, false>, 0};
+    case 16: return {k_oproj_mfma<DT, 16, 8, true>, 8 * 8192};
+    case 20: return {k_oproj_mfma<DT, 20, 8, false>, 0};
+    case 24: return {k_oproj_mfma<DT, 24, 8, false>, 0};
+    case 28: return {k_oproj_mfma<DT, 28, 8, false>, 0};
+    case 32: return {k_oproj_mfma<DT, 32, 8, false>, 0};
+    default: return {nullptr, 0};
   }
 }
 
@@ -2572,9 +2590,9 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
   if (a.mfma) {
     // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
     const int rtiles = (a.rows + 63) / 64;
-    if ((e = launch_phase(pick_qkv_mfma<DT>(a.H / 128), dim3(a.nqkv / 16 * rtiles), dim3(qkv_mfma_waves(a.H / 128) * kWave),
-                          a.H / 128 == 8 ? 8 * 16384 : 0, s, ev, 0, a)) !=
-        hipSuccess)
+    const MfmaKernel kq = pick_qkv_mfma<DT>(a.H / 128);
+    if ((e = launch_phase(kq.fn, dim3(a.nqkv / 16 * rtiles), dim3(qkv_mfma_waves(a.H / 128) * kWave), kq.lds, s, ev,
+                          0, a)) != hipSuccess)
       return e;
   } else {
     if ((e = launch_phase(pick_qkv<DT>(a.H / 512, a.rows == 1), dim3(a.nqkv / (4 * kRpwA)), dim3(256), 0, s, ev,
@@ -2600,9 +2618,10 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                                ev, 1, a)) != hipSuccess) {
     return e;
   }
-  if (a.mfma)
-    return launch_phase(pick_oproj_mfma<DT>(a.nq * kHeadDim / 128), dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(512),
-                        a.nq * kHeadDim == 2048 ? 8 * 8192 : 0, s, ev, 2, a);
+  if (a.mfma) {
+    const MfmaKernel ko = pick_oproj_mfma<DT>(a.nq * kHeadDim / 128);
+    return launch_phase(ko.fn, dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(512), ko.lds, s, ev, 2, a);
+  }
   return launch_phase(pick_oproj<DT>(a.nq * kHeadDim / 512, a.rows == 1), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s,
                       ev, 2, a);
 }
@@ -2671,16 +2690,18 @@ bool attn_waves_used(const LayerArgs &a) { return a.mfma && (a.group == 2 || a.g
 // Resident grid of the equal-share attention kernel: blocks per CU from the
 // occupancy calculator (at the largest row table) times the CU count.
 int attn_waves_grid(int dtype, int group, int cus) {
-  static int cached[2][9];
+  // occupancy per (dtype, group), computed once per process; calls from several
+  // threads may each compute it, they store the same value
+  static std::atomic<int> cached[2][9];
   const int di = dtype == ASR_BF16 ? 1 : 0;
   if (group != 2 && group != 4) return 0;
-  int per_cu = cached[di][group];
+  int per_cu = cached[di][group].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, true) : pick_attn_waves<ASR_F16>(group, true);
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_attn_waves_bytes(kMaxLayerRows)) !=
                   hipSuccess || per_cu <= 0)
       return 0;
-    cached[di][group] = per_cu;
+    cached[di][group].store(per_cu, std::memory_order_relaxed);
   }
   return per_cu * cus;
 }

@@ -239,6 +239,16 @@ __device__ __forceinline__ float sum_stride8(float v) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x % kWave; }
 
+// Order one wave's LDS accesses across its lanes: the stores (or reads) before
+// this point complete before the reads (or overwrites) after it by any lane of
+// the wave.  The hardware runs a wave's LDS instructions in order, so this only
+// keeps the compiler from moving accesses across it (it emits no instruction).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Reduce-scatter over the lanes l ^ MASK: lanes with the MASK bit clear keep
 // the low half of the values, the others the high half, each summed with its
 // partner's copy.

@@ -18,7 +18,9 @@
  *  - All tensor arguments are DEVICE pointers unless a comment says "host".
  *    The caller owns all memory.  The library never allocates, never
  *    synchronises the stream, never copies device data back to the host and
- *    keeps no pointer after it returns.  Work is enqueued on `stream` in
+ *    keeps no pointer after it returns.  Its only state between calls is a
+ *    per-process cache of kernel occupancies (computed on first use, the
+ *    same value whichever thread stores it).  Work is enqueued on `stream` in
  *    stream order; calls are safe to capture in a HIP graph.
  *  - Return value: ASR_OK (0) or a negative ASR_E* code for a synchronous,
  *    host-side validation failure (nothing is enqueued then).  Conditions that
@@ -185,7 +187,10 @@ int asr_attn_layer_verify(const asr_attn_config *cfg, const asr_attn_weights *w,
                           void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Bit-exact copy of given K/V rows into one layer's cache (a prefill filler).
+ * Bit-exact copy of given K/V rows into one layer's cache: the prefill filler
+ * ("Can CTC make Qwen3-ASR faster?", section 11 Phase D: build the prompt KV
+ * once, then verify blocks against it; the faster-qwen-asr GB10 record's
+ * configuration writes prefill straight into a static cache).
  * k_new, v_new are [B][n][n_kv_heads][head_dim] elements of kv->dtype; the n
  * rows of sequence b go to positions lens[s] .. lens[s] + n - 1 of slot
  * s = slots[b] (NULL: b), then lens[s] grows by n.  A sequence whose rows

@@ -362,3 +362,70 @@ def test_capacity_overflow_and_crop_growth_set_status():
     assert c.status == STATUS_CAPACITY and c.lens.tolist() == [8, 3]
     kv_crop([c], [9, 1])
     assert c.lens.tolist() == [8, 1] and c.status == STATUS_CAPACITY | STATUS_CROP_GROW
+
+
+# ---------------------------------------------------------------- verify's own branches
+
+def _verify_fixture(seed, lens, k, capacity=32):
+    cfg = BlockConfig(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=16)
+    w = LayerWeights.from_bits(rand_weights(cfg, seed), F16)
+    c = rand_cache(cfg, seed + 1, lens, capacity=capacity)
+    g = np.random.default_rng(seed + 2)
+    x = f16_bits(g.standard_normal((len(lens), k, cfg.hidden)))
+    r = f16_bits(g.standard_normal((len(lens), k, cfg.hidden)))
+    return cfg, w, c, x, r
+
+
+@pytest.mark.parametrize("k", [1, 3, 5])
+def test_verify_explicit_positions_equal_decode_at_p_plus_r(k):
+    """Row r of sequence b turns by positions[b] + r: the same rows as k decode steps given the
+    positions p_b + r explicitly (decode's explicit positions are pinned by brute force).  The
+    positions differ per sequence, so indexing them by slot instead of by sequence fails."""
+    lens = [3, 0, 7]
+    slots = [2, 0, 1]
+    pos = [40, 5, 1000]
+    cfg, w, c1, x, _ = _verify_fixture(160 + k, lens, k)
+    c2 = c1.copy()
+    ov = verify(cfg, w, c1, x, slots=slots, positions=pos)
+    for r in range(k):
+        od = decode(cfg, w, c2, x[:, r, :], slots=slots, positions=[p + r for p in pos])
+        assert rel_err(ov[:, r, :], od) < 1e-12
+    assert np.array_equal(c1.k, c2.k) and np.array_equal(c1.v, c2.v)
+    # and the positions matter: the default positions (the lengths) give other rows
+    c3 = rand_cache(cfg, 161 + k, lens, capacity=32)
+    assert rel_err(verify(cfg, w, c3, x, slots=slots), ov) > 1e-3
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_verify_residual_rows_match_decode_with_the_same_residual_rows(k):
+    """The residual is [B][k][H]: row r of sequence b gets residual[b][r].  Checked against k
+    decode steps each given residual[:, r] (decode's residual is pinned above), and against the
+    verify output without residual plus the widened residual."""
+    lens = [4, 9]
+    cfg, w, c1, x, res = _verify_fixture(170 + k, lens, k)
+    c2, c3 = c1.copy(), c1.copy()
+    ov = verify(cfg, w, c1, x, residual_bits=res)
+    for r in range(k):
+        od = decode(cfg, w, c2, x[:, r, :], residual_bits=res[:, r, :])
+        assert rel_err(ov[:, r, :], od) < 1e-12
+    plain = verify(cfg, w, c3, x)
+    assert np.allclose(ov - plain, widen(res, F16), atol=1e-12)
+
+
+def test_verify_capacity_overflow_skips_that_sequence_only():
+    """One sequence whose block would pass the capacity: its k rows are NaN, its length and
+    cache rows stay, the capacity bit is set; the other sequences equal a call without it."""
+    k, cap = 4, 12
+    lens = [5, 9, 8]           # 9 + 4 = 13 > 12 by one row; 8 + 4 = 12 fits exactly
+    cfg, w, c, x, _ = _verify_fixture(180, lens, k, capacity=cap)
+    before = c.copy()
+    out = verify(cfg, w, c, x)
+    assert np.all(np.isnan(out[1])) and np.all(np.isfinite(out[[0, 2]]))
+    assert c.status == STATUS_CAPACITY
+    assert c.lens.tolist() == [9, 9, 12]
+    assert np.array_equal(c.k[1], before.k[1]) and np.array_equal(c.v[1], before.v[1])
+    keep = [0, 2]
+    sub = KVCache(before.k[keep].copy(), before.v[keep].copy(), before.lens[keep].copy(), F16)
+    want = verify(cfg, w, sub, x[keep])
+    assert np.array_equal(out[keep], want) and sub.status == 0
+    assert np.array_equal(c.k[keep], sub.k) and np.array_equal(c.v[keep], sub.v)

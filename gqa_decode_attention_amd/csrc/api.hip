@@ -222,8 +222,11 @@ WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity)
   size_t off = 0;
   l.flow = off;
   off = align_up(off + kFlowWords * sizeof(uint32_t));
+  // the counters sit at the same offsets whatever the call's row count and
+  // head count, so a workspace shared by calls of different shapes never finds
+  // another call's data where its counters are (every call leaves them at zero)
   l.mctr = off;
-  off = align_up(off + (size_t)rows * nkv * sizeof(uint32_t));
+  off = align_up(off + (size_t)kMaxRows * kMaxKvHeads * sizeof(uint32_t));
   l.rowtab = off;
   off = align_up(off + (size_t)rows * 4 * sizeof(int));
   l.qkv = off;

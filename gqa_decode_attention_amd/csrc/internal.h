@@ -15,6 +15,7 @@ constexpr int kMinSplit = 16;         // keys per chunk, lower bound
 constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
 constexpr int kMaxVerifyK = 32;
 constexpr int kMaxLayerRows = 2048;   // rows (B k) per layer call
+constexpr int kMaxKvHeads = 32;       // n_q_heads * head_dim <= 4096 bounds both head counts
 constexpr int kFlowWords = 128;      // counters of the one-dispatch path (heads + 4 totals)
 constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
 constexpr uint32_t kStatusBadSlot = ASR_STATUS_BAD_SLOT;  // slot index outside [0, batch_cap)
@@ -63,6 +64,7 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);
+
 
 // launchers; return hipSuccess or the launch error
 hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s, hipEvent_t *ev);

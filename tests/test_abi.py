@@ -84,3 +84,14 @@ def test_host_validation_without_gpu():
     assert lib.asr_kv_crop(None, 1, fake, None) == -1
     assert lib.asr_kv_crop(None, 0, None, None) == 0
     assert lib.asr_kv_append(ctypes.byref(kv), fake, fake, None, 0, 3, None) == 0
+
+
+def test_workspace_counters_sit_at_fixed_offsets():
+    """Calls of different row counts may share one workspace: the counters every call leaves at
+    zero come first, so a workspace sized for many rows holds a small call's data only after
+    them (the bytes needed grow with the rows by the per-row regions alone)."""
+    ga, _ = _lib()
+    cfg = ga.config()
+    n1, n2, n3 = (ga.workspace_bytes(cfg, r, 1024) for r in (1, 2, 3))
+    assert n1 > 2048 * 32 * 4            # the counter block of the largest call is always there
+    assert abs((n3 - n2) - (n2 - n1)) <= 8 * 256   # per-row regions only (256-byte alignment)

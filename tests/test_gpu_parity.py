@@ -605,3 +605,29 @@ def test_fused_dispatch_workspace_across_changing_shapes():
     for oa, ob in zip(a[0], b[0]):
         assert np.max(np.abs(oa - ob)) <= AGREE * np.sqrt(np.mean(oa ** 2))
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and a[3] == b[3] == 0
+
+
+def test_one_workspace_for_calls_of_different_row_counts():
+    """One workspace serves calls of 4, 64, 6 and 2 rows in turn (few-row kernels, then the
+    equal-share attention whose merge counters sit where a smaller call's row table and
+    projection were): every call equals the same call on a fresh zeroed workspace, bit for bit."""
+    dtype = si.BF16
+    lens = [int(v) for v in si.kv_lengths(9, 64, 200, 1500)]
+    cap = 1536
+    L = SeededLayer(9, 7, 1024, dtype)
+    kb, vb = fill_cache(9, 7, lens, cap, dtype)
+    plan = [[3, 9, 27, 40], list(range(64)), [1, 2, 3, 4, 5, 6], [60, 0]]
+    cfg = ga.config(dtype=dtype)
+    res = {}
+    for shared in (True, False):
+        kv = device_cache(kb, vb, lens, dtype)
+        ws_shared = ga.alloc_workspace(cfg, 64, cap)
+        outs = []
+        for step, sl in enumerate(plan):
+            ws = ws_shared if shared else ga.alloc_workspace(cfg, 64, cap)
+            outs.append(_run_decode(L, cfg, kv, _x(9, 7, step, (len(sl), 1024), dtype), dtype, slots=sl, ws=ws))
+        res[shared] = (outs, to_bits(kv.k), kv.lens.cpu().numpy(), kv.status.item())
+    a, b = res[True], res[False]
+    for oa, ob in zip(a[0], b[0]):
+        assert np.all(np.isfinite(oa)) and np.array_equal(oa, ob)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and a[3] == b[3] == 0

@@ -20,10 +20,11 @@ DISPATCH_AUTO, DISPATCH_MULTI, DISPATCH_FUSED = 0, 1, 2
 STATUS_CAPACITY, STATUS_CROP_GROW, STATUS_SYNC_TIMEOUT, STATUS_BAD_SLOT = 1, 2, 4, 8
 
 ERRORS = {0: "ASR_OK", -1: "ASR_EINVAL", -2: "ASR_EUNSUPPORTED", -3: "ASR_ECAPACITY",
-          -4: "ASR_EWORKSPACE", -5: "ASR_EHIP"}
+          -4: "ASR_EWORKSPACE", -5: "ASR_EHIP", -6: "ASR_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 40 << 20
 
-EXPORTED = ["asr_attn_workspace_bytes", "asr_attn_layer_decode", "asr_attn_layer_verify",
-            "asr_kv_append", "asr_kv_crop", "asr_strerror"]
+EXPORTED = ["asr_attn_workspace_bytes", "asr_attn_layer_decode", "asr_attn_layer_decode_noalloc",
+            "asr_attn_layer_verify", "asr_kv_append", "asr_kv_crop", "asr_strerror"]
 
 _TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
 _DT_NAME = {"f16": F16, "bf16": BF16, "f32": F32}
@@ -67,6 +68,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.asr_attn_layer_decode.argtypes = [ctypes.POINTER(AsrAttnConfig), ctypes.POINTER(AsrAttnWeights),
                                           ctypes.POINTER(AsrKvLayer), P, P, P, I32, P, P, P, P, SZ, P]
     lib.asr_attn_layer_decode.restype = ctypes.c_int
+    lib.asr_attn_layer_decode_noalloc.argtypes = [ctypes.POINTER(AsrAttnConfig), ctypes.POINTER(AsrAttnWeights),
+                                                  ctypes.POINTER(AsrKvLayer), P, P, P, I32, P, P, P, P]
+    lib.asr_attn_layer_decode_noalloc.restype = ctypes.c_int
     lib.asr_attn_layer_verify.argtypes = [ctypes.POINTER(AsrAttnConfig), ctypes.POINTER(AsrAttnWeights),
                                           ctypes.POINTER(AsrKvLayer), P, P, P, I32, I32, P, P, P, P, SZ, P]
     lib.asr_attn_layer_verify.restype = ctypes.c_int
@@ -191,6 +195,18 @@ def layer_decode(cfg, w: Weights, kv: KVLayer, x, out, workspace, slots=None, po
                                         _ptr(slots), _ptr(positions), B, hl, _ptr(residual), _ptr(out),
                                         _ptr(workspace), workspace.numel(), _stream(stream)),
            "asr_attn_layer_decode")
+    del keep
+
+
+def layer_decode_noalloc(cfg, w: Weights, kv: KVLayer, x, out, slots=None, positions=None,
+                         host_lens=None, residual=None, stream=None) -> None:
+    """layer_decode with the library's static per-GPU scratch instead of a workspace."""
+    keep, hl = _host_lens(host_lens)
+    B = x.shape[0]
+    _check(load().asr_attn_layer_decode_noalloc(ctypes.byref(cfg), ctypes.byref(w.c), ctypes.byref(kv.c), _ptr(x),
+                                                _ptr(slots), _ptr(positions), B, hl, _ptr(residual), _ptr(out),
+                                                _stream(stream)),
+           "asr_attn_layer_decode_noalloc")
     del keep
 
 

@@ -101,6 +101,8 @@ int choose_split(const asr_attn_config *c, int capacity, int B, int n, const int
   return split < kMaxSplit ? split : kMaxSplit;
 }
 
+}  // namespace
+
 int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_kv_layer *kv,
               const void *x, const int32_t *slots, const int32_t *positions, int B, int n,
               const int32_t *host_lens, const void *residual, void *out, void *ws, size_t ws_bytes,
@@ -212,8 +214,6 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   return e == hipSuccess ? ASR_OK : ASR_EHIP;
 }
 
-}  // namespace
-
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity) {
   (void)H;
   (void)capacity;
@@ -302,6 +302,7 @@ const char *asr_strerror(int code) {
     case ASR_ECAPACITY: return "cache capacity exceeded (host lengths)";
     case ASR_EWORKSPACE: return "workspace missing or too small";
     case ASR_EHIP: return "HIP launch failed";
+    case ASR_ESCRATCH: return "call needs more scratch than the library's static scratch holds";
   }
   return "unknown error";
 }

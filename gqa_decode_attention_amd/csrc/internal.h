@@ -65,6 +65,11 @@ struct WorkspaceLayout {
 
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);
 
+// validation, workspace carving and launch of one layer call (decode: n = 1;
+// verify: n = k); the workspace is any device buffer of ws_bytes
+int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_kv_layer *kv, const void *x,
+              const int32_t *slots, const int32_t *positions, int B, int n, const int32_t *host_lens,
+              const void *residual, void *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 // launchers; return hipSuccess or the launch error
 hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s, hipEvent_t *ev);

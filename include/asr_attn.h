@@ -54,7 +54,9 @@ enum {
   ASR_EUNSUPPORTED = -2,  /* a shape or type the library has no kernel for (see asr_attn_config) */
   ASR_ECAPACITY = -3,     /* host_lens given and some lens + n > capacity */
   ASR_EWORKSPACE = -4,    /* workspace NULL or smaller than asr_attn_workspace_bytes() */
-  ASR_EHIP = -5           /* the HIP runtime refused a launch */
+  ASR_EHIP = -5,          /* the HIP runtime refused a launch */
+  ASR_ESCRATCH = -6       /* asr_attn_layer_decode_noalloc: the call needs more than
+                             ASR_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /* bits of the sticky device status word */
@@ -167,6 +169,35 @@ int asr_attn_layer_decode(const asr_attn_config *cfg, const asr_attn_weights *w,
                           const int32_t *positions, int32_t B, const int32_t *host_lens,
                           const void *residual, void *out, void *workspace, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * Bytes of the library's static device scratch used by
+ * asr_attn_layer_decode_noalloc: 40 MiB, which holds one decode call of up to
+ * 64 rows at the pages' shapes (16 q / 8 kv heads: about 575 KB per row, most
+ * of it split-KV partials).  Every GPU the entry point runs on holds one such
+ * array from its first call until the process ends.
+ */
+#define ASR_NOALLOC_SCRATCH_BYTES (40u << 20)
+
+/*
+ * asr_attn_layer_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what
+ * asr_attn_layer_decode computes, with the same kernels, using a file-scope
+ * device array of ASR_NOALLOC_SCRATCH_BYTES as the workspace; it calls no
+ * allocating routine.  The first call on a device looks up that device's
+ * array and enqueues one small kernel that zeroes its counters.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one
+ * GPU (concurrent streams, threads) race and must be serialised by the caller.
+ * Returns ASR_ESCRATCH (nothing enqueued) when the call's workspace
+ * (asr_attn_workspace_bytes for B rows and the cache capacity) exceeds the
+ * array, ASR_EHIP if the array's address cannot be obtained; otherwise as
+ * asr_attn_layer_decode.
+ */
+int asr_attn_layer_decode_noalloc(const asr_attn_config *cfg, const asr_attn_weights *w,
+                                  const asr_kv_layer *kv, const void *x, const int32_t *slots,
+                                  const int32_t *positions, int32_t B, const int32_t *host_lens,
+                                  const void *residual, void *out, hipStream_t stream);
 
 /*
  * k-token causal verification block ("Can CTC make Qwen3-ASR faster?",

@@ -86,6 +86,26 @@ def test_host_validation_without_gpu():
     assert lib.asr_kv_append(ctypes.byref(kv), fake, fake, None, 0, 3, None) == 0
 
 
+def test_noalloc_entry_validates_on_the_host():
+    """The workspace-free decode rejects, before touching a GPU, a call whose workspace would
+    exceed its static scratch (ASR_ESCRATCH), and answers like the decode entry otherwise."""
+    ga, lib = _lib()
+    fake = ctypes.c_void_p(0x1000)
+    w = ga._lib.AsrAttnWeights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    kv = ga._lib.AsrKvLayer(0x1000, 0x1000, 0x1000, None, 128, 1536, 8, 128, ga.BF16)
+    cfg = ga.config(dtype="bf16")
+    dec = lib.asr_attn_layer_decode_noalloc
+    args = lambda c, B: (ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), fake, None, None, B, None, None, fake,
+                         None)
+    assert ga.workspace_bytes(cfg, 64, 1536) <= ga.NOALLOC_SCRATCH_BYTES < ga.workspace_bytes(cfg, 80, 1536)
+    assert dec(*args(cfg, 80)) == -6
+    assert lib.asr_strerror(-6).startswith(b"call needs more scratch")
+    assert dec(*args(cfg, 0)) == 0
+    assert dec(*args(cfg, -1)) == -1
+    assert dec(*args(ga.config(hidden=1000, dtype="bf16"), 1)) == -2
+    assert dec(*args(ga.config(head_dim=64, dtype="bf16"), 1)) == -2
+
+
 def test_workspace_counters_sit_at_fixed_offsets():
     """Calls of different row counts may share one workspace: the counters every call leaves at
     zero come first, so a workspace sized for many rows holds a small call's data only after

@@ -166,6 +166,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.out_f32 = cfg->out_dtype == ASR_F32;
   a.mfma = rows > kVectorRows;
   a.oproj_split = 0;
+  a.vm_items = 0;
 
   // upper bound of attention work items; blocks stride over the real count.
   // nch_host: the most chunks of any row, by the host's view of the lengths
@@ -182,7 +183,41 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   bound *= a.nkv;
   const long long cap_grid = 16LL * cus;
   int attn_grid = (int)(bound < 1 ? 1 : (bound > cap_grid ? cap_grid : bound));
-  if (attn_waves_used(a)) {
+  if (attn_vmfma_used(a)) {
+    // verify blocks on the matrix cores: items (sequence, kv head, chunk of
+    // `split` keys, a multiple of the four waves' 32-key steps), enough of them
+    // for a few per CU; at most kMaxChunks chunks per sequence
+    int split = 128;
+    while (split < kMaxSplit && (long long)split * kMaxChunks < kv->capacity) split += 128;
+    auto items = [&](int sp) {
+      long long t = 0;
+      for (int b = 0; b < B; ++b) {
+        const int L = host_lens ? host_lens[b] : kv->capacity - n;
+        t += (L + n + sp - 1) / sp;
+      }
+      return t * a.nkv;
+    };
+    if (!cfg->kv_split) {
+      while (split < kMaxSplit && items(split) > 3LL * cus) split *= 2;
+    } else {
+      split = cfg->kv_split < split ? split : (cfg->kv_split + 127) / 128 * 128;
+    }
+    a.split = split < kMaxSplit ? split : kMaxSplit;
+    const int grid = attn_vmfma_grid(cfg->dtype, a.group, n, B, cus);
+    if (grid <= 0) return ASR_EHIP;
+    const long long want = items(a.split);
+    attn_grid = (int)(want < 1 ? 1 : (want < grid ? want : grid));
+    if (B <= kVmMaxSeqs) {   // the host lays the items out: the kernel starts without reading the lengths
+      int run = 0;
+      for (int b = 0; b < B; ++b) {
+        a.vm_pre[b] = run;
+        const int L = host_lens ? host_lens[b] : kv->capacity - n;
+        run += (L + n + a.split - 1) / a.split * a.nkv;
+      }
+      a.vm_pre[B] = run;
+      a.vm_items = run;
+    }
+  } else if (attn_waves_used(a)) {
     // many rows: one equal key share per wave of a resident grid; a (row, kv
     // head) spans at most capacity / share + 2 <= kMaxChunks shares
     attn_grid = attn_waves_grid(cfg->dtype, a.group, cus);

@@ -2109,6 +2109,486 @@ __host__ __device__ __forceinline__ size_t lds_attn_waves_bytes(int rows) {
   return (size_t)rows * sizeof(int4) + (size_t)(rows + 1) * sizeof(int);
 }
 
+// ---------------------------------------------------------------- phase C for verify blocks on the matrix cores
+//
+// The k rows of a verify block all read their sequence's cache, so here one
+// work item streams each (sequence, kv head g, chunk of keys) once for all
+// M = GROUP * k query rows of g (query row m = r * GROUP + h: block row r, q
+// head g * GROUP + h), in tiles of 16 rows.  Per 32-key step of a wave:
+//   S^T = K Q^T    v_mfma_f32_16x16x32, A = 16 keys x 32 dims of K (exact
+//                  16-bit), B = the same dims of Q (two 16-bit terms, hi + lo)
+//   O^T += V^T P^T A = 16 dims x 32 keys of V, B = the weights P (hi + lo)
+// A lane of the score tile holds 4 keys of one query row, which is exactly its
+// share of the B operand of the next product (the 32 keys are contracted in
+// the order {4j..4j+3, 16+4j..16+4j+3} for lane group j, and V is read in the
+// same order), so the weights never leave the registers.  K and V of a step
+// arrive as whole 128-byte lines (four keys per load instruction) and pass
+// through the wave's LDS region: K rows with chunk c at c ^ (key & 15) for the
+// A-operand reads, V rows with chunk c at c ^ 2 (key & 7) for the transposing
+// reads (ds_read_b64_tr_b16: lane p of each 16-lane group receives element
+// p % 4 of the lanes 4 e + p / 4, e = 0..3, i.e. four keys of one dim).
+// Online softmax per query row in base 2 (Q carries log2(e) / sqrt(d)); the
+// four waves of an item combine in LDS into one partial per (row, q head) in
+// the split-KV layout; the last item of a (sequence, g) to be counted merges
+// the partials of all its rows in chunk order (deterministic).  Keys at or past
+// the committed length are this call's rows, taken from the projection (k
+// normalised, both rounded to 16 bits as stored) and written to the cache by
+// the one step that holds them.
+
+constexpr int kVmWaves = 4;    // waves per workgroup
+constexpr int kVmStep = 32;    // keys per wave step
+constexpr int kVmStage = 8192; // LDS bytes of one 32-key K (or V) stage
+constexpr int kVmRow = 132;    // floats per query row of the combine buffer (padded against bank conflicts)
+
+// dynamic LDS: per wave a K and a V stage (reused by the combine), then the
+// sequences' item prefix and (slot, L, nvis, ok)
+__host__ __device__ __forceinline__ size_t lds_vmfma_bytes(int B) {
+  return (size_t)kVmWaves * 2 * kVmStage + (size_t)B * sizeof(int4) + (size_t)(B + 1) * sizeof(int);
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_ld8_tr16(const unsigned char *p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t *)((__attribute__((address_space(3))) unsigned char *)p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// block-wide exclusive prefix of the items (chunks x kv heads) of every sequence
+__device__ void build_seq_prefix(const LayerArgs &A, int *pre, int4 *sinfo, int *wsum) {
+  const int wave = wave_id(), lane = lane_id();
+  const int B = A.B;
+  const int per = (B + 255) / 256;
+  const int beg = min((int)threadIdx.x * per, B), end = min(beg + per, B);
+  int local = 0;
+  for (int b = beg; b < end; ++b) {
+    const RowInfo ri = row_info(A, b * A.n);
+    const int nvis = ri.ok ? ri.L + A.n : 0;
+    sinfo[b] = make_int4(ri.slot, ri.L, nvis, (int)ri.ok);
+    local += chunks_of(nvis, A.split) * A.nkv;
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  int run = base + incl - local;
+  for (int b = beg; b < end; ++b) {
+    pre[b] = run;
+    run += chunks_of(sinfo[b].z, A.split) * A.nkv;
+  }
+  if (threadIdx.x == 255) pre[B] = run;
+  __syncthreads();
+}
+
+// Merge of the np chunk partials of every (row r < k, head h) of one
+// (sequence, kv head g) by the whole workgroup at once: the (m, l) of all
+// chunks into LDS, one thread per (r, h) turns them into weights
+// 2^(m_c - M) / sum_c 2^(m_c - M) l_c, then every thread sums float4 columns
+// over the chunks in chunk order (deterministic) and writes the attention
+// output and its hi / lo tiles.  `ws` is LDS scratch of 2 * k * GROUP * np floats.
+// Merge of the np chunk partials of every (row r < k, head h) of one
+// (sequence, kv head g) by the whole workgroup at once, in one memory round
+// trip: every (m, l) and the first eight chunks of every output column are
+// requested together.  Wave w turns the (m, l) of the pairs rh = w, w + 4, ...
+// (rh = r * GROUP + h; lane c holds chunk c) into the weights
+// 2^(m_c - M) / sum_c 2^(m_c - M) l_c by wave reductions and leaves them in
+// LDS; then every thread sums its float4 columns over the chunks in chunk
+// order (deterministic) and writes the attention output and its hi / lo
+// tiles.  `ws`: LDS scratch of 32 * 64 floats; k * GROUP <= 32, np <= 64.
+template <int DT, int GROUP>
+__device__ void merge_block_vm(const LayerArgs &A, int row0, int k, int g, int np, float *ws) {
+  constexpr int CPT = 4, BATCH = 8, PPW = 32 / kVmWaves;   // columns per thread, chunks per load batch, pairs per wave
+  const int pairs = k * GROUP;
+  const int wave = wave_id(), lane = lane_id();
+  const uint32_t pstride = (uint32_t)kMaxChunks * GROUP * kPartStride;   // floats per (row, kv head)
+  // one workgroup-uniform resource over the block's partials; per-lane offsets
+  const __amdgpu_buffer_rsrc_t R =
+      rsrc_of(A.part + ((size_t)row0 * A.nkv + g) * pstride, (uint32_t)((k - 1) * A.nkv + 1) * pstride * 4);
+  auto at = [&](int rh, int c) -> uint32_t {   // byte offset of the partial of pair rh, chunk c
+    return ((uint32_t)(rh / GROUP) * A.nkv * pstride + ((uint32_t)c * GROUP + rh % GROUP) * kPartStride) * 4;
+  };
+  float4 ml[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) ml[i] = ld_dev4(R, at(min(wave + kVmWaves * i, pairs - 1), min(lane, np - 1)) + 128 * 4);
+  float4 v[CPT][BATCH];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int f = min((int)threadIdx.x + q * (int)blockDim.x, pairs * 32 - 1), rh = f / 32, d = (f % 32) * 4;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) v[q][u] = ld_dev4(R, at(rh, min(u, np - 1)) + d * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int rh = wave + kVmWaves * i;
+    if (rh < pairs) {
+      const float m = lane < np ? ml[i].x : -INFINITY;
+      const float M = wave_max(m);
+      const float w = (lane < np && m != -INFINITY) ? exp2_neg(m - M) : 0.f;
+      const float tot = wave_sum(w * ml[i].y);
+      ws[rh * kWave + lane] = w / tot;
+    }
+  }
+  __syncthreads();
+  const size_t plane = (size_t)(A.nq * kHeadDim / 32) * A.rows * 32;
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int f = threadIdx.x + q * blockDim.x;
+    if (f >= pairs * 32) break;
+    const int rh = f / 32, d = (f % 32) * 4, r = rh / GROUP, h = rh % GROUP;
+    const float *wv = ws + rh * kWave;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = 0; c0 < np; c0 += BATCH) {
+      if (c0 > 0) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) v[q][u] = ld_dev4(R, at(rh, min(c0 + u, np - 1)) + d * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const float w = c0 + u < np ? wv[c0 + u] : 0.f;
+        a.x += w * v[q][u].x;
+        a.y += w * v[q][u].y;
+        a.z += w * v[q][u].z;
+        a.w += w * v[q][u].w;
+      }
+    }
+    const int row = row0 + r;
+    const size_t col = (size_t)(g * GROUP + h) * kHeadDim + d;
+    *reinterpret_cast<float4 *>(A.att + (size_t)row * A.nq * kHeadDim + col) = a;
+    uint16_t hv[4], lv[4];
+    const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hv[e] = rne16<DT>(av[e]);
+      lv[e] = rne16<DT>(av[e] - cvt16<DT>(hv[e]));
+    }
+    // tiled [plane][col / 32][row][32] for the MFMA o_proj: the four values are adjacent
+    const size_t idx = ((col / 32) * A.rows + row) * 32 + col % 32;
+    *reinterpret_cast<uint2 *>(A.att_hl + idx) =
+        make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+    *reinterpret_cast<uint2 *>(A.att_hl + plane + idx) =
+        make_uint2((uint32_t)lv[0] | ((uint32_t)lv[1] << 16), (uint32_t)lv[2] | ((uint32_t)lv[3] << 16));
+  }
+}
+
+template <int DT, int GROUP, int QT>
+__global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ int wsum[4];
+  __shared__ float s_ml[kVmWaves][2][16];   // a wave's (m, l) per query row of the tile being combined
+  __shared__ uint32_t s_old;
+  const bool hostmap = A.vm_items > 0;   // items laid out by the host from its copy of the lengths
+  int4 *sinfo = reinterpret_cast<int4 *>(dyn + kVmWaves * 2 * kVmStage);
+  int *pre = reinterpret_cast<int *>(sinfo + A.B);
+  if (!hostmap) build_seq_prefix(A, pre, sinfo, wsum);
+  const int total = hostmap ? A.vm_items : pre[A.B];
+  const int wave = wave_id(), lane = lane_id();
+  const int n16 = lane & 15, j4 = lane >> 4;
+  unsigned char *stk = dyn + wave * 2 * kVmStage, *stv = stk + kVmStage;
+  const float qs = kLog2e * rsqrtf((float)kHeadDim);
+  const int k = A.n;
+  const uint32_t row_bytes = (uint32_t)A.nqkv * 4;
+  const uint32_t ssq_bytes = (uint32_t)(A.nq + A.nkv) * kTilesPerHead * 4;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // (sequence b, kv head g, first chunk) of the item; with the host's layout the
+    // item of a sequence's last host chunk also takes the chunks past the host's view
+    const int *ip = hostmap ? A.vm_pre : pre;
+    int lo = 0, hi = A.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ip[mid] <= item) lo = mid; else hi = mid;
+    }
+    const int b = lo, row0 = b * k;
+    const int nch_i = (ip[b + 1] - ip[b]) / A.nkv;   // chunks per kv head in the item layout
+    const int rem = item - ip[b];
+    const int g = rem / nch_i, c_first = rem - g * nch_i;
+    int slot, L, nvis;
+    if (hostmap) {
+      slot = A.slots ? A.slots[b] : b;
+    } else {
+      const int4 si = sinfo[b];
+      slot = si.x;
+      L = si.y;
+      nvis = si.z;
+    }
+    // a slot outside the cache reads slot 0's lines (its rows are skipped below)
+    const int lslot = (slot >= 0 && slot < A.batch_cap) ? slot : 0;
+    const size_t kvbase = ((size_t)lslot * A.nkv + g) * A.capacity * kHeadDim;
+    const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + kvbase, (uint32_t)A.capacity * kHeadDim * 2);
+    const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + kvbase, (uint32_t)A.capacity * kHeadDim * 2);
+
+    uint4 lk[8], lv[8];
+    int tclamp = 0;   // loads stay at or below this key (lines the item fetches anyway)
+    auto issue = [&](int ts) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = min(ts + 4 * i + j4, tclamp);
+        const uint32_t off = (uint32_t)t * (kHeadDim * 2) + n16 * 16;
+        lk[i] = ld_buf(Kr, off);
+        lv[i] = ld_buf(Vr, off);
+      }
+    };
+    // the wave's first step of the first chunk, requested before the length arrives
+    // (with the host layout): rows clamped into the chunk and the cache
+    tclamp = min(c_first * A.split + A.split, A.capacity) - 1;
+    if (hostmap || c_first * A.split + wave * kVmStep < nvis) issue(c_first * A.split + wave * kVmStep);
+    // Q of the tile rows, requested with the K/V lines and before the length (a wait
+    // on a vector load waits on every load issued before it)
+    float4 qv[QT][4][2], qp[QT][2];
+    {
+      const __amdgpu_buffer_rsrc_t Qr = make_rsrc(A.qkv + (size_t)row0 * A.nqkv, (uint32_t)k * row_bytes);
+      const __amdgpu_buffer_rsrc_t Sr =
+          make_rsrc(A.ssq + (size_t)row0 * (A.nq + A.nkv) * kTilesPerHead, (uint32_t)k * ssq_bytes);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int m = qt * 16 + n16, r = m / GROUP, h = m % GROUP;
+        const uint32_t rr = (uint32_t)min(r, k - 1);   // rows past the block: zero weight below
+        const uint32_t head = (uint32_t)(g * GROUP + h);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t o = rr * row_bytes + (head * kHeadDim + 32 * s + 8 * j4) * 4;
+          qv[qt][s][0] = __builtin_bit_cast(float4, ld_buf(Qr, o));
+          qv[qt][s][1] = __builtin_bit_cast(float4, ld_buf(Qr, o + 16));
+        }
+        qp[qt][0] = __builtin_bit_cast(float4, ld_buf(Sr, rr * ssq_bytes + head * kTilesPerHead * 4));
+        qp[qt][1] = __builtin_bit_cast(float4, ld_buf(Sr, rr * ssq_bytes + head * kTilesPerHead * 4 + 16));
+      }
+    }
+    if (hostmap) {
+      const RowInfo ri = row_info(A, row0);
+      L = ri.L;
+      nvis = ri.ok ? ri.L + k : 0;
+    }
+    const int nch = chunks_of(nvis, A.split);
+    const int c_last = (hostmap && c_first == nch_i - 1) ? max(nch, nch_i) - 1 : c_first;
+
+    // Q as B operands: lane (query row n16 of tile qt, dims 32 s + 8 j4 .. + 7), two 16-bit terms
+    uint4 qh[QT][4], ql[QT][4];
+    {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int m = qt * 16 + n16;
+        const float sc = (m / GROUP < k) ? inv_rms_of(A, qp[qt][0], qp[qt][1]) * qs : 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float f[8] = {qv[qt][s][0].x * sc, qv[qt][s][0].y * sc, qv[qt][s][0].z * sc, qv[qt][s][0].w * sc,
+                              qv[qt][s][1].x * sc, qv[qt][s][1].y * sc, qv[qt][s][1].z * sc, qv[qt][s][1].w * sc};
+          split8<DT>(f, qh[qt][s], ql[qt][s]);
+        }
+      }
+    }
+
+    for (int c = c_first; c <= c_last; ++c) {
+    if (c >= nch) break;   // past the sequence's visible keys (the length shrank since the launch)
+    const int cbeg = c * A.split, cend = min(cbeg + A.split, nvis);
+    int t0 = cbeg + wave * kVmStep;
+    tclamp = max(min(cend, L) - 1, 0);
+    if (c > c_first && t0 < cend) issue(t0);
+    float mrun[QT], lrun[QT];
+    f32x4_t o[QT][8];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      mrun[qt] = -INFINITY;
+      lrun[qt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (; t0 < cend; t0 += kVmWaves * kVmStep) {
+      wave_lds_sync();   // the previous step's operand reads are done
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kl = 4 * i + j4;
+        *reinterpret_cast<uint4 *>(stk + kl * 256 + ((n16 ^ (kl & 15)) << 4)) = lk[i];
+        *reinterpret_cast<uint4 *>(stv + kl * 256 + ((n16 ^ ((kl & 7) << 1)) << 4)) = lv[i];
+      }
+      if (t0 + kVmStep > L || t0 + kVmStep > cend) {
+        // this call's rows (keys L .. L + k - 1) replace what was loaded for them: taken from the
+        // projection as the cache stores them (k normalised, both rounded) and written to the
+        // cache here, by the one step that holds them; keys past the chunk become zeros
+        wave_lds_sync();
+        const __amdgpu_buffer_rsrc_t Rr = make_rsrc(A.qkv + (size_t)row0 * A.nqkv, (uint32_t)k * row_bytes);
+        const __amdgpu_buffer_rsrc_t Pr =
+            make_rsrc(A.ssq + (size_t)row0 * (A.nq + A.nkv) * kTilesPerHead, (uint32_t)k * ssq_bytes);
+#pragma unroll 1
+        for (int pc = lane; pc < kVmStep * 16; pc += kWave) {
+          const int kl = pc >> 4, ch = pc & 15, t = t0 + kl;
+          if (t < L) continue;
+          uint4 kq = make_uint4(0u, 0u, 0u, 0u), vq = kq;
+          if (t < cend) {
+            const uint32_t rr = (uint32_t)(t - L);
+            const uint32_t kh = rr * row_bytes + ((A.nq + g) * kHeadDim + 8 * ch) * 4;
+            const uint32_t vh = rr * row_bytes + ((A.nq + A.nkv + g) * kHeadDim + 8 * ch) * 4;
+            const uint32_t ph = rr * ssq_bytes + (A.nq + g) * kTilesPerHead * 4;
+            const float4 ka = __builtin_bit_cast(float4, ld_buf(Rr, kh));
+            const float4 kb = __builtin_bit_cast(float4, ld_buf(Rr, kh + 16));
+            const float4 va = __builtin_bit_cast(float4, ld_buf(Rr, vh));
+            const float4 vb = __builtin_bit_cast(float4, ld_buf(Rr, vh + 16));
+            const float4 p0 = __builtin_bit_cast(float4, ld_buf(Pr, ph));
+            const float4 p1 = __builtin_bit_cast(float4, ld_buf(Pr, ph + 16));
+            kq = round8<DT>(ka, kb, inv_rms_of(A, p0, p1));
+            vq = round8<DT>(va, vb);
+            const size_t ro = kvbase + (size_t)t * kHeadDim + 8 * ch;
+            *reinterpret_cast<uint4 *>(A.kc + ro) = kq;
+            *reinterpret_cast<uint4 *>(A.vc + ro) = vq;
+          }
+          *reinterpret_cast<uint4 *>(stk + kl * 256 + ((ch ^ (kl & 15)) << 4)) = kq;
+          *reinterpret_cast<uint4 *>(stv + kl * 256 + ((ch ^ ((kl & 7) << 1)) << 4)) = vq;
+        }
+      }
+      wave_lds_sync();   // the stage is complete before any lane reads it
+      const int tn = t0 + kVmWaves * kVmStep;
+      if (tn < cend) issue(tn);   // the next step's lines travel during this step's arithmetic
+
+      // scores: two 16-key tiles per query tile
+      uint4 ka[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int kl = kt * 16 + n16, ch = 4 * s + j4;
+          ka[kt][s] = lds_ld16(reinterpret_cast<const uint16_t *>(stk + kl * 256 + ((ch ^ (kl & 15)) << 4)));
+        }
+      f32x4_t sc[QT][2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            a = mfma16x16x32<DT>(ka[kt][s], qh[qt][s], a);
+            a = mfma16x16x32<DT>(ka[kt][s], ql[qt][s], a);
+          }
+          sc[qt][kt] = a;
+        }
+      // V^T operands: dims 16 dt + n16, keys {4 j4 .. 4 j4 + 3, 16 + 4 j4 .. 16 + 4 j4 + 3}
+      uint4 va[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint2 h2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int kl = hh * 16 + 4 * j4 + (n16 >> 2), cq = n16 & 3;
+          const int ch = 2 * dt + (cq >> 1);
+          h2[hh] = lds_ld8_tr16(stv + kl * 256 + ((ch ^ ((kl & 7) << 1)) << 4) + 8 * (cq & 1));
+        }
+        va[dt] = make_uint4(h2[0].x, h2[0].y, h2[1].x, h2[1].y);
+      }
+      // online softmax per query row, then the weighted values
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int m = qt * 16 + n16, r = m / GROUP;
+        const int tmax = r < k ? min(cend, L + r + 1) : 0;   // keys [.., tmax) visible to this row
+        float p[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = t0 + kt * 16 + 4 * j4 + e;
+            const float v = t < tmax ? sc[qt][kt][e] : -INFINITY;
+            p[kt * 4 + e] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, xpart<16>(mx));
+        mx = fmaxf(mx, xpart<32>(mx));
+        const float mn = fmaxf(mrun[qt], mx);
+        if (__any(mn > mrun[qt])) {
+          const float corr = mn > mrun[qt] ? exp2_neg(mrun[qt] - mn) : 1.f;
+          lrun[qt] *= corr;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            o[qt][dt][0] *= corr;
+            o[qt][dt][1] *= corr;
+            o[qt][dt][2] *= corr;
+            o[qt][dt][3] *= corr;
+          }
+        }
+        mrun[qt] = mn;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = p[e] == -INFINITY ? 0.f : exp2_neg(p[e] - mn);
+          lrun[qt] += p[e];
+        }
+        uint4 ph, pl;
+        split8<DT>(p, ph, pl);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          o[qt][dt] = mfma16x16x32<DT>(va[dt], ph, o[qt][dt]);
+          o[qt][dt] = mfma16x16x32<DT>(va[dt], pl, o[qt][dt]);
+        }
+      }
+    }
+
+    // the four waves' (m, l, O) of each query tile combined into the item's partials
+    float *cbuf = reinterpret_cast<float *>(dyn);   // [wave][16 rows][kVmRow]
+    const int prow = threadIdx.x >> 4, pcol = (threadIdx.x & 15) * 8;   // combine: one row, 8 dims per thread
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float l = lrun[qt];
+      l = xsum<16>(l);
+      l = xsum<32>(l);
+      __syncthreads();   // the stages (or the previous tile's combine) are no longer read
+      float *cw = cbuf + (size_t)wave * 16 * kVmRow;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4_t *>(cw + n16 * kVmRow + dt * 16 + 4 * j4) = o[qt][dt];
+      if (j4 == 0) {
+        s_ml[wave][0][n16] = mrun[qt];
+        s_ml[wave][1][n16] = l;
+      }
+      __syncthreads();
+      const int m = qt * 16 + prow, r = m / GROUP, h = m % GROUP;
+      if (r < k) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kVmWaves; ++w) M = fmaxf(M, s_ml[w][0][prow]);
+        float f[kVmWaves], lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < kVmWaves; ++w) {
+          const float mw = s_ml[w][0][prow];
+          f[w] = mw == -INFINITY ? 0.f : exp2_neg(mw - M);
+          lt += f[w] * s_ml[w][1][prow];
+        }
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kVmWaves; ++w) {
+          const float *src = cbuf + ((size_t)w * 16 + prow) * kVmRow + pcol;
+          const float4 a0 = *reinterpret_cast<const float4 *>(src), a1 = *reinterpret_cast<const float4 *>(src + 4);
+          acc[0] += f[w] * a0.x; acc[1] += f[w] * a0.y; acc[2] += f[w] * a0.z; acc[3] += f[w] * a0.w;
+          acc[4] += f[w] * a1.x; acc[5] += f[w] * a1.y; acc[6] += f[w] * a1.z; acc[7] += f[w] * a1.w;
+        }
+        // one workgroup-uniform resource over the item's partials (rows of the block, chunk c)
+        const uint32_t pstride = (uint32_t)kMaxChunks * GROUP * kPartStride;
+        const __amdgpu_buffer_rsrc_t R = rsrc_of(A.part + ((size_t)row0 * A.nkv + g) * pstride,
+                                                 (uint32_t)((k - 1) * A.nkv + 1) * pstride * 4);
+        const uint32_t pb = ((uint32_t)r * A.nkv * pstride + ((uint32_t)c * GROUP + h) * kPartStride) * 4;
+        st_dev4(R, pb + pcol * 4, make_float4(acc[0], acc[1], acc[2], acc[3]));
+        st_dev4(R, pb + (pcol + 4) * 4, make_float4(acc[4], acc[5], acc[6], acc[7]));
+        if (pcol == 0) st_dev4(R, pb + 128 * 4, make_float4(M, lt, 0.f, 0.f));
+      }
+    }
+    }   // chunks of the item
+    wait_mem();   // this thread's partial stores are performed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_old = __hip_atomic_fetch_add(A.mctr + (size_t)row0 * A.nkv + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_old == (uint32_t)(nch_i - 1)) {   // the last item of (sequence, g): merge every row of the block
+      if (nch > 0) merge_block_vm<DT, GROUP>(A, row0, k, g, nch, reinterpret_cast<float *>(dyn));
+      if (threadIdx.x == 0)
+        __hip_atomic_store(A.mctr + (size_t)row0 * A.nkv + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();   // LDS (stages, s_old) reused by the next item
+  }
+}
+
 template <int DT, int KV, int RB, int RPW>
 __global__ __launch_bounds__(256) void k_oproj(LayerArgs A) {
   uint4 wr[RPW][KV];
@@ -2560,6 +3040,23 @@ LayerKernel pick_attn_waves(int group, bool nt) {
   }
 }
 
+// query tiles of 16 rows for GROUP * k query rows per (sequence, kv head); 0: no instance
+int vmfma_tiles(int group, int n) {
+  const int m = group * n;
+  return m <= 16 ? 1 : (m <= 32 ? 2 : 0);
+}
+
+template <int DT>
+LayerKernel pick_attn_vmfma(int group, int qt) {
+#define ASR_PICK_VMFMA(G) \
+  case G: return qt == 1 ? k_attn_vmfma<DT, G, 1> : (qt == 2 ? k_attn_vmfma<DT, G, 2> : nullptr);
+  switch (group) {
+    ASR_PICK_VMFMA(2) ASR_PICK_VMFMA(4) ASR_PICK_VMFMA(8)
+    default: return nullptr;
+  }
+#undef ASR_PICK_VMFMA
+}
+
 template <int DT>
 LayerKernel pick_qkv(int kvi, bool one_row) {
   switch (kvi) {
@@ -2610,7 +3107,11 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
     return launch_phase(pick_oproj_merge<DT>(a.nq * kHeadDim / 512, a.nch_host, a.oproj_split != 0),
                         dim3(a.H / (4 * rpw) * halves), dim3(256), lds_x, s, ev, 2, a);
   }
-  if (attn_waves_used(a)) {
+  if (attn_vmfma_used(a)) {
+    if ((e = launch_phase(pick_attn_vmfma<DT>(a.group, vmfma_tiles(a.group, a.n)), dim3(attn_grid), dim3(kVmWaves * kWave),
+                          lds_vmfma_bytes(a.B), s, ev, 1, a)) != hipSuccess)
+      return e;
+  } else if (attn_waves_used(a)) {
     if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
                           ev, 1, a)) != hipSuccess)
       return e;
@@ -2683,6 +3184,25 @@ int fused_max_grid(int dtype, int H, size_t dyn_smem, int cus) {
 }
 
 size_t layer_dyn_smem(const LayerArgs &a) { return fused_dyn_smem(a); }
+
+// verify blocks of more than a few rows whose query rows per kv head fit two
+// tiles: one K/V stream per (sequence, kv head) on the matrix cores (the
+// per-row merge takes two or more q heads per kv head)
+bool attn_vmfma_used(const LayerArgs &a) {
+  return a.mfma && a.n > 1 && a.group >= 2 && vmfma_tiles(a.group, a.n) > 0;
+}
+
+// Resident workgroups of the verify attention kernel for B sequences (blocks per
+// CU from the occupancy calculator times the CU count).
+int attn_vmfma_grid(int dtype, int group, int n, int B, int cus) {
+  const int qt = vmfma_tiles(group, n);
+  const LayerKernel k = dtype == ASR_BF16 ? pick_attn_vmfma<ASR_BF16>(group, qt) : pick_attn_vmfma<ASR_F16>(group, qt);
+  int per_cu = 0;
+  if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kVmWaves * kWave, lds_vmfma_bytes(B)) != hipSuccess ||
+      per_cu <= 0)
+    return 0;
+  return per_cu * cus;
+}
 
 // (group 8 would hold its 8 q vectors and accumulators past the register file)
 bool attn_waves_used(const LayerArgs &a) { return a.mfma && (a.group == 2 || a.group == 4); }

@@ -16,6 +16,7 @@ constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
 constexpr int kMaxVerifyK = 32;
 constexpr int kMaxLayerRows = 2048;   // rows (B k) per layer call
 constexpr int kMaxKvHeads = 32;       // n_q_heads * head_dim <= 4096 bounds both head counts
+constexpr int kVmMaxSeqs = 64;        // sequences of a verify call whose work items the host lays out
 constexpr int kFlowWords = 128;      // counters of the one-dispatch path (heads + 4 totals)
 constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
 constexpr uint32_t kStatusBadSlot = ASR_STATUS_BAD_SLOT;  // slot index outside [0, batch_cap)
@@ -57,6 +58,11 @@ struct LayerArgs {
   int out_f32;
   int mfma;                   // projections on MFMA (more than a few rows)
   int oproj_split;            // few rows, fp32 out: o_proj in two head halves adding into the zeroed output
+  // verify attention on the matrix cores: work items (sequence, kv head, chunk) laid out by the host
+  // from its copy of the lengths (vm_items > 0; vm_pre[b] = first item of sequence b), else by the
+  // device from the lengths (vm_items = 0)
+  int vm_items;
+  int vm_pre[kVmMaxSeqs + 1];
 };
 
 struct WorkspaceLayout {
@@ -78,6 +84,8 @@ hipError_t launch_layer_fused(const LayerArgs &a, int dtype, int grid, hipStream
 int fused_max_grid(int dtype, int H, size_t dyn_smem, int cus);
 size_t layer_dyn_smem(const LayerArgs &a);
 bool attn_waves_used(const LayerArgs &a);
+bool attn_vmfma_used(const LayerArgs &a);
+int attn_vmfma_grid(int dtype, int group, int n, int B, int cus);
 int attn_waves_grid(int dtype, int group, int cus);
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
                             const int32_t *slots, int B, int n, hipStream_t s);

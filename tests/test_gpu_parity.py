@@ -631,3 +631,34 @@ def test_one_workspace_for_calls_of_different_row_counts():
     for oa, ob in zip(a[0], b[0]):
         assert np.all(np.isfinite(oa)) and np.array_equal(oa, ob)
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and a[3] == b[3] == 0
+
+
+@pytest.mark.parametrize("nq,nkv,k", [(16, 8, 8), (16, 8, 16), (16, 4, 4), (16, 4, 8), (16, 2, 4), (16, 2, 2)])
+@pytest.mark.parametrize("split", [0, 128])
+def test_verify_matrix_core_attention_groups_and_chunk_edges(nq, nkv, k, split):
+    """Verify blocks on the matrix-core attention (one K/V stream per sequence and kv head) for
+    2, 4 and 8 q heads per kv head: an empty cache, lengths whose appended rows straddle a
+    128-key chunk boundary, one chunk ending exactly at the committed length, long ragged tails."""
+    dtype = si.BF16 if k % 4 == 0 else si.F16
+    lens = [0, 120, 128, 3, 517, 255][: max(2, 16 // k + 1)]
+    cap = 640
+    L = SeededLayer(11, nq * 100 + nkv * 10 + k, 1024, dtype, nq=nq, nkv=nkv)
+    kb, vb = fill_cache(11, nkv * 10 + k, lens, cap, dtype, nkv=nkv)
+    B = len(lens)
+    slots = list(range(B))[::-1]
+    kv = device_cache(kb, vb, lens, dtype)
+    ref = oracle_cache(kb, vb, lens, dtype)
+    xb = _x(11, nkv * 10 + k, 0, (B, k, 1024), dtype)
+    cfg = ga.config(dtype=dtype, n_q_heads=nq, n_kv_heads=nkv, kv_split=split)
+    got = _run_verify(L, cfg, kv, xb, dtype, slots=slots)
+    want = oracle.verify(L.ocfg, L.ref, ref, xb, slots=slots)
+    err = rel_err(got, want)
+    print(f"verify mfma attention nq={nq} nkv={nkv} k={k} split={split} B={B}: {err:.3e}")
+    assert err < TOL[dtype]
+    assert kv.lens.cpu().tolist() == [l + k for l in lens] and kv.status.item() == 0
+    kg, vg = to_bits(kv.k), to_bits(kv.v)
+    for s in range(B):
+        check_rounded_rows(kg[s, :, lens[s]:lens[s] + k], ref.k[s, :, lens[s]:lens[s] + k], dtype)
+        check_rounded_rows(vg[s, :, lens[s]:lens[s] + k], ref.v[s, :, lens[s]:lens[s] + k], dtype)
+        assert np.array_equal(kg[s, :, :lens[s]], kb[s, :, :lens[s]])
+        assert np.array_equal(kg[s, :, lens[s] + k:], kb[s, :, lens[s] + k:])

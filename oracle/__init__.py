@@ -1,4 +1,4 @@
 """fp64 CPU oracle of the decoder attention block (test infrastructure only)."""
-from .attn_block import (BF16, F16, STATUS_CAPACITY, STATUS_CROP_GROW, BlockConfig, KVCache,
+from .attn_block import (BF16, E4M3, E4M3_MAX, F16, e4m3_value, rne_e4m3, STATUS_CAPACITY, STATUS_CROP_GROW, BlockConfig, KVCache,
                          LayerWeights, decode, kv_append, kv_crop, rms_norm, rne16, rope,
                          rope_frequencies, verify, widen)

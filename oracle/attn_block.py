@@ -34,6 +34,16 @@ x * g / sqrt(mean(x^2) + eps) with the same eps for all norms; no biases.
 
 Inputs are 16-bit bit patterns (``uint16``) widened exactly to fp64; every
 intermediate stays in fp64, and the only rounding is the one into the cache.
+
+The cache may also hold FP8 codes (E4M3: 1 sign, 4 exponent bits with bias 7,
+3 mantissa bits, no infinities, one NaN pattern per sign) with one fp32 scale
+per kv head for K and one for V: a cached value is scale * decode(code), and a
+row enters the cache as the code nearest to value / scale, ties to the even
+code, magnitudes past the largest finite value (448) saturating to it.  This
+follows "Baseten optimizes Qwen3-ASR 1.7B", section "KV cache quantization"
+(the cache in FP8, the attention arithmetic at full precision); the E4M3
+layout and the saturating conversion are the readings taken where that page
+is silent.
 """
 from __future__ import annotations
 
@@ -44,6 +54,7 @@ import numpy as np
 
 F16 = "f16"
 BF16 = "bf16"
+E4M3 = "e4m3"
 
 STATUS_CAPACITY = 1   # an append would pass the cache capacity: rows skipped, output NaN
 STATUS_CROP_GROW = 2  # a crop asked for a length above the current one: ignored
@@ -110,6 +121,46 @@ def rne16(a: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# FP8 E4M3 codes
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of E4M3 codes (uint8): sign bit 7, exponent bits 6..3
+    (bias 7), mantissa bits 2..0; exponent 0 is the subnormal range
+    m * 2^-9; exponent 15 with mantissa 7 is NaN (no infinities)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def rne_e4m3(a: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of fp64 values, ties to the even code; magnitudes past
+    448 saturate to 448 (there is no infinity to round to); NaN to the NaN code.
+
+    Works from the ascending table of the 127 non-negative finite codes, as
+    ``rne16`` does for the 16-bit formats.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    pats = np.arange(0, 0x7F, dtype=np.uint8)          # 0x00 .. 0x7E: 0 .. 448 ascending
+    vals = e4m3_value(pats)
+    mag = np.minimum(np.abs(a), E4M3_MAX)
+    hi = np.clip(np.searchsorted(vals, mag, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_lo = mag - vals[lo]
+    d_hi = vals[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (pats[hi] % 2 == 0))
+    out = np.where(pick_hi, pats[hi], pats[lo]).astype(np.uint8)
+    out = np.where(np.signbit(a), out | np.uint8(0x80), out).astype(np.uint8)
+    return np.where(np.isnan(a), np.uint8(0x7F), out).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
 # configuration, weights, cache
 
 @dataclass(frozen=True)
@@ -140,25 +191,49 @@ class LayerWeights:
 
 @dataclass
 class KVCache:
-    """One layer's cache: K and V as 16-bit patterns [batch_cap][nkv][capacity][d]."""
+    """One layer's cache: K and V as codes [batch_cap][nkv][capacity][d].
+
+    16-bit caches hold ``uint16`` bit patterns of ``dtype``; FP8 caches
+    (``dtype`` E4M3) hold ``uint8`` codes and the per-kv-head scales
+    ``k_scale``, ``v_scale`` (fp32 values)."""
     k: np.ndarray
     v: np.ndarray
     lens: np.ndarray           # [batch_cap] committed lengths
     dtype: str
     status: int = 0
+    k_scale: np.ndarray = None   # [nkv], E4M3 caches only
+    v_scale: np.ndarray = None
 
     @classmethod
-    def empty(cls, batch_cap, n_kv_heads, capacity, head_dim, dtype):
+    def empty(cls, batch_cap, n_kv_heads, capacity, head_dim, dtype, k_scale=None, v_scale=None):
         shape = (batch_cap, n_kv_heads, capacity, head_dim)
-        return cls(np.zeros(shape, np.uint16), np.zeros(shape, np.uint16),
-                   np.zeros(batch_cap, np.int64), dtype)
+        ct = np.uint8 if dtype == E4M3 else np.uint16
+        return cls(np.zeros(shape, ct), np.zeros(shape, ct), np.zeros(batch_cap, np.int64), dtype, 0,
+                   None if k_scale is None else np.asarray(k_scale, np.float64),
+                   None if v_scale is None else np.asarray(v_scale, np.float64))
 
     @property
     def capacity(self) -> int:
         return self.k.shape[2]
 
     def copy(self) -> "KVCache":
-        return KVCache(self.k.copy(), self.v.copy(), self.lens.copy(), self.dtype, self.status)
+        return KVCache(self.k.copy(), self.v.copy(), self.lens.copy(), self.dtype, self.status,
+                       self.k_scale, self.v_scale)
+
+    def encode(self, which: str, rows: np.ndarray) -> np.ndarray:
+        """Codes of rows [nkv][n][d] (or [nkv][d]) as this cache stores them."""
+        if self.dtype != E4M3:
+            return rne16(rows, self.dtype)
+        sc = self.k_scale if which == "k" else self.v_scale
+        sc = sc.reshape((-1,) + (1,) * (rows.ndim - 1))
+        return rne_e4m3(rows / sc)
+
+    def values(self, which: str, g: int, codes: np.ndarray) -> np.ndarray:
+        """fp64 values of codes of kv head g."""
+        if self.dtype != E4M3:
+            return widen(codes, self.dtype)
+        sc = self.k_scale[g] if which == "k" else self.v_scale[g]
+        return sc * e4m3_value(codes)
 
 
 # ----------------------------------------------------------------------------
@@ -235,14 +310,14 @@ def decode(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray
             cache.status |= STATUS_CAPACITY
             out[i] = np.nan
             continue
-        cache.k[s, :, L, :] = rne16(k, cache.dtype)
-        cache.v[s, :, L, :] = rne16(v, cache.dtype)
+        cache.k[s, :, L, :] = cache.encode("k", k)
+        cache.v[s, :, L, :] = cache.encode("v", v)
         n_vis = L + 1
         a = np.empty((nq, d))
         for head in range(nq):
             g = head // group
-            K = widen(cache.k[s, g, :n_vis, :], cache.dtype)
-            V = widen(cache.v[s, g, :n_vis, :], cache.dtype)
+            K = cache.values("k", g, cache.k[s, g, :n_vis, :])
+            V = cache.values("v", g, cache.v[s, g, :n_vis, :])
             wts = _softmax(K @ q[head] / math.sqrt(d))
             a[head] = wts @ V
         out[i] = w.w_o @ a.reshape(nq * d)
@@ -283,15 +358,15 @@ def verify(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray
             cache.status |= STATUS_CAPACITY
             out[b] = np.nan
             continue
-        cache.k[s, :, L:L + kk, :] = rne16(K_new.transpose(1, 0, 2), cache.dtype)
-        cache.v[s, :, L:L + kk, :] = rne16(V_new.transpose(1, 0, 2), cache.dtype)
+        cache.k[s, :, L:L + kk, :] = cache.encode("k", K_new.transpose(1, 0, 2))
+        cache.v[s, :, L:L + kk, :] = cache.encode("v", V_new.transpose(1, 0, 2))
         n_all = L + kk
         visible = np.arange(n_all)[None, :] <= (L + np.arange(kk))[:, None]   # [k][L + k]
         A = np.empty((kk, nq, d))
         for head in range(nq):
             g = head // group
-            K = widen(cache.k[s, g, :n_all, :], cache.dtype)
-            V = widen(cache.v[s, g, :n_all, :], cache.dtype)
+            K = cache.values("k", g, cache.k[s, g, :n_all, :])
+            V = cache.values("v", g, cache.v[s, g, :n_all, :])
             S = (Q[:, head, :] @ K.T) / math.sqrt(d)
             S = np.where(visible, S, -np.inf)
             A[:, head, :] = _softmax(S) @ V
@@ -303,14 +378,15 @@ def verify(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray
 
 
 def kv_append(cache: KVCache, k_bits: np.ndarray, v_bits: np.ndarray, slots=None) -> None:
-    """Copy given 16-bit rows into the cache: k_bits, v_bits are [B][n][nkv][d].
+    """Copy given rows (16-bit patterns or E4M3 codes) into the cache: k_bits, v_bits are [B][n][nkv][d].
 
     Rows of sequence b go to positions lens .. lens + n - 1 of slot
     ``slots[b]``; lens grows by n.  A sequence whose rows would pass the
     capacity is skipped and the capacity status bit set.
     """
-    k_bits = np.asarray(k_bits, np.uint16)
-    v_bits = np.asarray(v_bits, np.uint16)
+    ct = np.uint8 if cache.dtype == E4M3 else np.uint16
+    k_bits = np.asarray(k_bits, ct)
+    v_bits = np.asarray(v_bits, ct)
     B, n = k_bits.shape[:2]
     for b in range(B):
         s = int(slots[b]) if slots is not None else b

@@ -34,6 +34,7 @@ BF16 = "bf16"
 # tensor ids of the random streams
 T_GAMMA_IN, T_WQKV, T_GAMMA_Q, T_GAMMA_K, T_WO = 0, 1, 2, 3, 4
 T_KCACHE, T_VCACHE, T_X, T_LENS, T_ACCEPT, T_VCHOICE, T_RESID = 5, 6, 7, 8, 9, 10, 11
+T_KVSCALE = 12
 
 N_Q_HEADS = 16
 N_KV_HEADS = 8
@@ -99,6 +100,30 @@ def to_bits(a: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown 16-bit dtype {dtype!r}")
 
 
+def to_e4m3_codes(a: np.ndarray) -> np.ndarray:
+    """Nearest FP8 E4M3 code (ties to even, saturating at +-448) of fp64 draws, as uint8.
+
+    E4M3 keeps 4 significant bits; ``frexp`` gives a in [0.5, 1) * 2**e, so the
+    fraction times 2**4, rounded half to even, keeps them.  Below 2**-6 the
+    spacing is fixed at 2**-9.  The code is then assembled from the exponent
+    and the 3 stored mantissa bits.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    sign = np.signbit(a)
+    mag = np.minimum(np.abs(a), 448.0)
+    m, e = np.frexp(mag)
+    q = np.ldexp(np.rint(np.ldexp(m, 4)), e - 4)               # 4 significant bits
+    sub = mag < 2.0 ** -6
+    q = np.where(sub, np.ldexp(np.rint(np.ldexp(mag, 9)), -9), q)
+    q = np.minimum(q, 448.0)
+    m2, e2 = np.frexp(q)                                        # q = m2 * 2**e2, m2 in [0.5, 1)
+    exp_field = np.where(q >= 2.0 ** -6, e2 - 1 + 7, 0)
+    mant = np.where(exp_field > 0, np.rint((m2 * 2 - 1) * 8), np.rint(q * 2.0 ** 9))
+    code = (exp_field.astype(np.int64) << 3) | mant.astype(np.int64)
+    code = np.where(q == 0, 0, code)
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
 def normal_bits(stream, layer, tensor_id, extra, shape, std=1.0, mean=0.0, dtype=F16):
     g = rng_for(stream, layer, tensor_id, extra)
     return to_bits(mean + std * g.standard_normal(shape), dtype)
@@ -129,6 +154,25 @@ def kv_rows(stream: int, layer: int, seq: int, length: int, dtype: str,
     k = normal_bits(stream, layer, T_KCACHE, seq, (nkv, length, d), 1.0, 0.0, dtype)
     v = normal_bits(stream, layer, T_VCACHE, seq, (nkv, length, d), 1.0, 0.0, dtype)
     return k, v
+
+
+def kv_rows_e4m3(stream: int, layer: int, seq: int, length: int, k_scale, v_scale,
+                 nkv: int = N_KV_HEADS, d: int = HEAD_DIM):
+    """Committed FP8 cache rows of one sequence: codes of N(0, 1) draws divided by the
+    per-kv-head scales, each [nkv][length][d] uint8 (the same draws as ``kv_rows``)."""
+    ks = np.asarray(k_scale, np.float64).reshape(nkv, 1, 1)
+    vs = np.asarray(v_scale, np.float64).reshape(nkv, 1, 1)
+    k = rng_for(stream, layer, T_KCACHE, seq).standard_normal((nkv, length, d))
+    v = rng_for(stream, layer, T_VCACHE, seq).standard_normal((nkv, length, d))
+    return to_e4m3_codes(k / ks), to_e4m3_codes(v / vs)
+
+
+def kv_scales(stream: int, layer: int, nkv: int = N_KV_HEADS):
+    """Per-kv-head FP8 scales of K and V, fp32 values near 1/16 (so N(0, 1) rows use
+    about the upper two thirds of the E4M3 range): 2^-4 * (1 + 0.25 u), u uniform in [0, 1)."""
+    g = rng_for(stream, layer, T_KVSCALE, 0)
+    return ((2.0 ** -4) * (1 + 0.25 * g.random(nkv))).astype(np.float32), \
+           ((2.0 ** -4) * (1 + 0.25 * g.random(nkv))).astype(np.float32)
 
 
 def kv_rows_many(stream, layer, seqs, lengths, dtype, nkv=N_KV_HEADS, d=HEAD_DIM, threads=None):

@@ -15,7 +15,7 @@ import torch  # noqa: F401  (loads torch's HIP runtime first; the library binds 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libasr_attn.so")
 
-F16, BF16, F32 = 0, 1, 2
+F16, BF16, F32, FP8_E4M3 = 0, 1, 2, 3
 DISPATCH_AUTO, DISPATCH_MULTI, DISPATCH_FUSED = 0, 1, 2
 STATUS_CAPACITY, STATUS_CROP_GROW, STATUS_SYNC_TIMEOUT, STATUS_BAD_SLOT = 1, 2, 4, 8
 
@@ -49,7 +49,8 @@ class AsrKvLayer(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("lens", ctypes.c_void_p),
                 ("status", ctypes.c_void_p), ("batch_cap", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -150,23 +151,33 @@ class Weights:
 
 
 class KVLayer:
-    """One layer's cache: k, v [batch_cap][nkv][capacity][d], lens [batch_cap] int32, status [1] int32."""
+    """One layer's cache: k, v [batch_cap][nkv][capacity][d], lens [batch_cap] int32, status [1] int32.
 
-    def __init__(self, k, v, lens, status=None):
+    16-bit caches are float16 / bfloat16 tensors; an FP8 cache is uint8 tensors of E4M3 codes
+    with fp32 per-kv-head scales ``k_scale``, ``v_scale`` [nkv] on the device."""
+
+    def __init__(self, k, v, lens, status=None, k_scale=None, v_scale=None):
         assert k.shape == v.shape and k.dim() == 4 and k.dtype == v.dtype
         assert lens.dtype == torch.int32 and lens.numel() == k.shape[0]
         self.k, self.v, self.lens, self.status = k, v, lens, status
-        dt = {torch.float16: F16, torch.bfloat16: BF16}[k.dtype]
+        self.k_scale, self.v_scale = k_scale, v_scale
+        dt = {torch.float16: F16, torch.bfloat16: BF16, torch.uint8: FP8_E4M3}[k.dtype]
+        if dt == FP8_E4M3:
+            assert k_scale is not None and v_scale is not None
+            assert k_scale.dtype == torch.float32 and v_scale.dtype == torch.float32
         self.c = AsrKvLayer(k.data_ptr(), v.data_ptr(), lens.data_ptr(),
                             None if status is None else status.data_ptr(),
-                            k.shape[0], k.shape[2], k.shape[1], k.shape[3], dt)
+                            k.shape[0], k.shape[2], k.shape[1], k.shape[3], dt,
+                            None if k_scale is None else k_scale.data_ptr(),
+                            None if v_scale is None else v_scale.data_ptr())
 
     @classmethod
-    def empty(cls, batch_cap, n_kv_heads, capacity, head_dim=128, dtype=torch.float16, device="cuda"):
+    def empty(cls, batch_cap, n_kv_heads, capacity, head_dim=128, dtype=torch.float16, device="cuda",
+              k_scale=None, v_scale=None):
         shape = (batch_cap, n_kv_heads, capacity, head_dim)
         return cls(torch.zeros(shape, dtype=dtype, device=device), torch.zeros(shape, dtype=dtype, device=device),
                    torch.zeros(batch_cap, dtype=torch.int32, device=device),
-                   torch.zeros(1, dtype=torch.int32, device=device))
+                   torch.zeros(1, dtype=torch.int32, device=device), k_scale, v_scale)
 
 
 def workspace_bytes(cfg: AsrAttnConfig, max_rows: int, capacity: int) -> int:

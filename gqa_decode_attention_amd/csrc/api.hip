@@ -42,11 +42,13 @@ int check_kv(const asr_kv_layer *kv, const asr_attn_config *c) {
   if (!kv || !kv->k || !kv->v || !kv->lens) return ASR_EINVAL;
   if (kv->batch_cap <= 0 || kv->capacity <= 0) return ASR_EINVAL;
   if (kv->head_dim != kHeadDim) return ASR_EUNSUPPORTED;
-  if (kv->dtype != ASR_F16 && kv->dtype != ASR_BF16) return ASR_EUNSUPPORTED;
+  if (kv->dtype != ASR_F16 && kv->dtype != ASR_BF16 && kv->dtype != ASR_FP8_E4M3) return ASR_EUNSUPPORTED;
+  if (kv->dtype == ASR_FP8_E4M3 && (!kv->k_scale || !kv->v_scale)) return ASR_EINVAL;
   if (kv->n_kv_heads <= 0) return ASR_EINVAL;
   if (kv->capacity > kMaxChunks * kMaxSplit) return ASR_EUNSUPPORTED;
   if (c) {
-    if (kv->n_kv_heads != c->n_kv_heads || kv->dtype != c->dtype) return ASR_EINVAL;
+    if (kv->n_kv_heads != c->n_kv_heads) return ASR_EINVAL;
+    if (kv->dtype != c->dtype && kv->dtype != ASR_FP8_E4M3) return ASR_EINVAL;
   }
   return ASR_OK;
 }
@@ -125,6 +127,13 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
       if (host_lens[b] < 0 || (long long)host_lens[b] + n > kv->capacity) return ASR_ECAPACITY;
   }
 
+  const bool kv8 = kv->dtype == ASR_FP8_E4M3;
+  if (kv8) {
+    // FP8 caches: the many-row kernels (matrix-core projections, equal-share attention)
+    const int group = cfg->n_q_heads / cfg->n_kv_heads;
+    if (rows <= kVectorRows || (group != 2 && group != 4) || cfg->dispatch == ASR_DISPATCH_FUSED)
+      return ASR_EUNSUPPORTED;
+  }
   const int cus = device_cus();
   LayerArgs a;
   a.x = static_cast<const uint16_t *>(x);
@@ -167,6 +176,9 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.mfma = rows > kVectorRows;
   a.oproj_split = 0;
   a.vm_items = 0;
+  a.kv8 = kv8;
+  a.ksc = kv->k_scale;
+  a.vsc = kv->v_scale;
 
   // upper bound of attention work items; blocks stride over the real count.
   // nch_host: the most chunks of any row, by the host's view of the lengths

@@ -398,6 +398,11 @@ __device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 }
 // the same with the nontemporal hint: a stream read once, kept out of the caches' way
 constexpr int kCachePolicyStream = 2;   // nt
+// 8 bytes, with or without the nontemporal hint
+__device__ __forceinline__ uint2 ld_buf8(__amdgpu_buffer_rsrc_t r, uint32_t off, bool nt) {
+  return __builtin_bit_cast(uint2, nt ? __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyStream)
+                                      : __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 __device__ __forceinline__ uint4 ld_buf_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyStream));
 }
@@ -939,20 +944,33 @@ __device__ __forceinline__ int wcur_next(WCur &c, const LayerArgs &A, const int 
 // cached row once (one row per sequence), so the stream carries the
 // nontemporal hint; rows of a verify block read their sequence's rows again
 // and keep plain loads.
-template <bool NT>
+// F8: the cache holds E4M3 codes (128-byte rows); the same dims come as two
+// 8-byte loads (lanes kl = 0..7 of a key cover its row in two instructions).
+template <bool NT, bool F8>
 __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, uint4 (&r)[4]) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  constexpr uint32_t RB = F8 ? kHeadDim : kHeadDim * 2;   // bytes per cached row
   // (the cursor is wave-uniform; readfirstlane keeps the resources in scalar registers)
-  const size_t base = ((size_t)rfl(c.slot) * A.nkv + rfl(c.g)) * A.capacity * kHeadDim;
-  const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
-  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + base, region);
-  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + base, region);
+  const size_t base = ((size_t)rfl(c.slot) * A.nkv + rfl(c.g)) * A.capacity * RB;
+  const uint32_t region = (uint32_t)A.capacity * RB;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(reinterpret_cast<const unsigned char *>(A.kc) + base, region);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(reinterpret_cast<const unsigned char *>(A.vc) + base, region);
   const int last = max(min(rfl(c.te), rfl(c.L)) - 1, 0);
-  const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * (kHeadDim * 2) + kl * 16;
-  r[0] = NT ? ld_buf_nt(Kr, off) : ld_buf(Kr, off);
-  r[1] = NT ? ld_buf_nt(Kr, off + 128) : ld_buf(Kr, off + 128);
-  r[2] = NT ? ld_buf_nt(Vr, off) : ld_buf(Vr, off);
-  r[3] = NT ? ld_buf_nt(Vr, off + 128) : ld_buf(Vr, off + 128);
+  if constexpr (F8) {
+    const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * RB + kl * 8;
+    const uint2 a = ld_buf8(Kr, off, NT), b = ld_buf8(Kr, off + 64, NT);
+    const uint2 e = ld_buf8(Vr, off, NT), f = ld_buf8(Vr, off + 64, NT);
+    r[0] = make_uint4(a.x, a.y, 0u, 0u);
+    r[1] = make_uint4(b.x, b.y, 0u, 0u);
+    r[2] = make_uint4(e.x, e.y, 0u, 0u);
+    r[3] = make_uint4(f.x, f.y, 0u, 0u);
+  } else {
+    const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * RB + kl * 16;
+    r[0] = NT ? ld_buf_nt(Kr, off) : ld_buf(Kr, off);
+    r[1] = NT ? ld_buf_nt(Kr, off + 128) : ld_buf(Kr, off + 128);
+    r[2] = NT ? ld_buf_nt(Vr, off) : ld_buf(Vr, off);
+    r[3] = NT ? ld_buf_nt(Vr, off + 128) : ld_buf(Vr, off + 128);
+  }
 }
 
 // One lane's 8 dims of an appended row, 16-bit as stored: k normalised with
@@ -1055,7 +1073,7 @@ __device__ __forceinline__ void wresolve(const LayerArgs &A, const WPending &p) 
   if (old == (uint32_t)(p.np - 1)) merge_wave<DT, GROUP>(A, p.row, p.g, p.np);
 }
 
-template <int DT, int GROUP, bool NT>
+template <int DT, int GROUP, bool NT, bool F8>
 __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *rinfo, int w, int W) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
   const int d0 = 8 * kl, d1 = 64 + 8 * kl;
@@ -1077,9 +1095,9 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   // three register sets in rotation: the loads of step i + 2 are issued before
   // the arithmetic of step i, into the set step i - 1 has released
   uint4 ra[4], rb[4], rc[4];
-  wstep_load<NT>(A, lc, ra);
+  wstep_load<NT, F8>(A, lc, ra);
   wcur_next(lc, A, pre, rinfo);
-  wstep_load<NT>(A, lc, rb);
+  wstep_load<NT, F8>(A, lc, rb);
   wcur_next(lc, A, pre, rinfo);
 
   const float qs = kLog2e * rsqrtf((float)kHeadDim);
@@ -1104,9 +1122,11 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
       qp[j][0] = ld_dev4(Sr, h * kTilesPerHead * 4);
       qp[j][1] = ld_dev4(Sr, (h * kTilesPerHead + 4) * 4);
     }
+    // an FP8 cache's K scale is folded into q (scores = (s_k q) . code values)
+    const float ksc = F8 ? A.ksc[cg] : 1.f;
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
-      const float sc = inv_rms_of(A, qp[j][0], qp[j][1]) * qs;
+      const float sc = inv_rms_of(A, qp[j][0], qp[j][1]) * qs * ksc;
 #pragma unroll
       for (int h2 = 0; h2 < 4; ++h2) {
         q[j][4 * h2 + 0] = qv[j][h2].x * sc;
@@ -1123,11 +1143,13 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
 
   // the piece of `c` is complete: partial to its slot, then count it
   auto finish_piece = [&](const WCur &c) {
+    // an FP8 cache's V scale multiplies the weighted sum of code values
+    const float vsc = F8 ? A.vsc[rfl(c.g)] : 1.f;
     float v32[GROUP * 16];
 #pragma unroll
     for (int j = 0; j < GROUP; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v32[j * 16 + e] = acc[j][e];
+      for (int e = 0; e < 16; ++e) v32[j * 16 + e] = acc[j][e] * vsc;
     float v16[GROUP * 8], v8[GROUP * 4], v4[GROUP * 2];
     rs_half<GROUP * 16, 32>(v32, v16);
     rs_half<GROUP * 8, 16>(v16, v8);
@@ -1192,16 +1214,36 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
         const float4 p0 = ld_dev4(Pr, ph);
         const float4 p1 = ld_dev4(Pr, ph + 16);
         const float inv = inv_rms_of(A, p0, p1);
-        k0 = round8<DT>(ka, kb, inv);
-        k1 = round8<DT>(kc, kd, inv);
-        v0 = round8<DT>(va, vb);
-        v1 = round8<DT>(vc, vd);
-        if (cc.roff == A.n - 1) {   // the sequence's last row stores the appended rows
-          const size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
-          *reinterpret_cast<uint4 *>(A.kc + ro + d0) = k0;
-          *reinterpret_cast<uint4 *>(A.kc + ro + d1) = k1;
-          *reinterpret_cast<uint4 *>(A.vc + ro + d0) = v0;
-          *reinterpret_cast<uint4 *>(A.vc + ro + d1) = v1;
+        if constexpr (F8) {   // codes of value / scale, as the cache stores them
+          const float ik = inv / A.ksc[cg], iv = 1.f / A.vsc[cg];
+          k0 = make_uint4(pack4_e4m3(ka.x * ik, ka.y * ik, ka.z * ik, ka.w * ik),
+                          pack4_e4m3(kb.x * ik, kb.y * ik, kb.z * ik, kb.w * ik), 0u, 0u);
+          k1 = make_uint4(pack4_e4m3(kc.x * ik, kc.y * ik, kc.z * ik, kc.w * ik),
+                          pack4_e4m3(kd.x * ik, kd.y * ik, kd.z * ik, kd.w * ik), 0u, 0u);
+          v0 = make_uint4(pack4_e4m3(va.x * iv, va.y * iv, va.z * iv, va.w * iv),
+                          pack4_e4m3(vb.x * iv, vb.y * iv, vb.z * iv, vb.w * iv), 0u, 0u);
+          v1 = make_uint4(pack4_e4m3(vc.x * iv, vc.y * iv, vc.z * iv, vc.w * iv),
+                          pack4_e4m3(vd.x * iv, vd.y * iv, vd.z * iv, vd.w * iv), 0u, 0u);
+          if (cc.roff == A.n - 1) {   // the sequence's last row stores the appended rows
+            const size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
+            unsigned char *kc8 = reinterpret_cast<unsigned char *>(A.kc), *vc8 = reinterpret_cast<unsigned char *>(A.vc);
+            *reinterpret_cast<uint2 *>(kc8 + ro + d0) = make_uint2(k0.x, k0.y);
+            *reinterpret_cast<uint2 *>(kc8 + ro + d1) = make_uint2(k1.x, k1.y);
+            *reinterpret_cast<uint2 *>(vc8 + ro + d0) = make_uint2(v0.x, v0.y);
+            *reinterpret_cast<uint2 *>(vc8 + ro + d1) = make_uint2(v1.x, v1.y);
+          }
+        } else {
+          k0 = round8<DT>(ka, kb, inv);
+          k1 = round8<DT>(kc, kd, inv);
+          v0 = round8<DT>(va, vb);
+          v1 = round8<DT>(vc, vd);
+          if (cc.roff == A.n - 1) {   // the sequence's last row stores the appended rows
+            const size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
+            *reinterpret_cast<uint4 *>(A.kc + ro + d0) = k0;
+            *reinterpret_cast<uint4 *>(A.kc + ro + d1) = k1;
+            *reinterpret_cast<uint4 *>(A.vc + ro + d0) = v0;
+            *reinterpret_cast<uint4 *>(A.vc + ro + d1) = v1;
+          }
         }
       }
     }
@@ -1212,10 +1254,17 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
       v1 = make_uint4(v1.x & vm, v1.y & vm, v1.z & vm, v1.w & vm);
     }
     float kf[16], vf[16];
-    unpack8<DT>(k0, kf);
-    unpack8<DT>(k1, kf + 8);
-    unpack8<DT>(v0, vf);
-    unpack8<DT>(v1, vf + 8);
+    if constexpr (F8) {
+      unpack8_e4m3(k0.x, k0.y, kf);
+      unpack8_e4m3(k1.x, k1.y, kf + 8);
+      unpack8_e4m3(v0.x, v0.y, vf);
+      unpack8_e4m3(v1.x, v1.y, vf + 8);
+    } else {
+      unpack8<DT>(k0, kf);
+      unpack8<DT>(k1, kf + 8);
+      unpack8<DT>(v0, vf);
+      unpack8<DT>(v1, vf + 8);
+    }
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
       float s = 0.f;
@@ -1241,7 +1290,7 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   };
 
   auto issue = [&](uint4 (&r)[4]) {
-    wstep_load<NT>(A, lc, r);
+    wstep_load<NT, F8>(A, lc, r);
     wcur_next(lc, A, pre, rinfo);
   };
   // arithmetic of cc's step, then advance cc: false past the share
@@ -2095,14 +2144,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
 }
 
 // many rows: equal key shares per wave of a resident grid
-template <int DT, int GROUP, bool NT>
+template <int DT, int GROUP, bool NT, bool F8>
 __global__ __launch_bounds__(256) void k_attn_waves(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ int wsum[4];
   int4 *rinfo = reinterpret_cast<int4 *>(dyn);
   int *pre = reinterpret_cast<int *>(rinfo + A.rows);
   build_item_prefix<true>(A, pre, rinfo, wsum);
-  attention_waves<DT, GROUP, NT>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
+  attention_waves<DT, GROUP, NT, F8>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
 }
 
 __host__ __device__ __forceinline__ size_t lds_attn_waves_bytes(int rows) {
@@ -3032,12 +3081,15 @@ LayerKernel pick_oproj_merge(int kvo, int nch_host, bool split) {
 }
 
 template <int DT>
-LayerKernel pick_attn_waves(int group, bool nt) {
+LayerKernel pick_attn_waves(int group, bool nt, bool f8) {
+#define ASR_PICK_WAVES(G) \
+  case G: return f8 ? (nt ? k_attn_waves<DT, G, true, true> : k_attn_waves<DT, G, false, true>) \
+                    : (nt ? k_attn_waves<DT, G, true, false> : k_attn_waves<DT, G, false, false>);
   switch (group) {
-    case 2: return nt ? k_attn_waves<DT, 2, true> : k_attn_waves<DT, 2, false>;
-    case 4: return nt ? k_attn_waves<DT, 4, true> : k_attn_waves<DT, 4, false>;
+    ASR_PICK_WAVES(2) ASR_PICK_WAVES(4)
     default: return nullptr;
   }
+#undef ASR_PICK_WAVES
 }
 
 // query tiles of 16 rows for GROUP * k query rows per (sequence, kv head); 0: no instance
@@ -3112,7 +3164,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                           lds_vmfma_bytes(a.B), s, ev, 1, a)) != hipSuccess)
       return e;
   } else if (attn_waves_used(a)) {
-    if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
+    if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1, a.kv8 != 0), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
                           ev, 1, a)) != hipSuccess)
       return e;
   } else if ((e = launch_phase(pick_attn<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
@@ -3189,7 +3241,7 @@ size_t layer_dyn_smem(const LayerArgs &a) { return fused_dyn_smem(a); }
 // tiles: one K/V stream per (sequence, kv head) on the matrix cores (the
 // per-row merge takes two or more q heads per kv head)
 bool attn_vmfma_used(const LayerArgs &a) {
-  return a.mfma && a.n > 1 && a.group >= 2 && vmfma_tiles(a.group, a.n) > 0;
+  return a.mfma && a.n > 1 && a.group >= 2 && !a.kv8 && vmfma_tiles(a.group, a.n) > 0;
 }
 
 // Resident workgroups of the verify attention kernel for B sequences (blocks per
@@ -3217,7 +3269,7 @@ int attn_waves_grid(int dtype, int group, int cus) {
   if (group != 2 && group != 4) return 0;
   int per_cu = cached[di][group].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
-    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, true) : pick_attn_waves<ASR_F16>(group, true);
+    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, true, false) : pick_attn_waves<ASR_F16>(group, true, false);
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_attn_waves_bytes(kMaxLayerRows)) !=
                   hipSuccess || per_cu <= 0)
       return 0;

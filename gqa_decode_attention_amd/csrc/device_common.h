@@ -53,6 +53,31 @@ __device__ __forceinline__ uint16_t rne16(float f) {
   }
 }
 
+// ---------------------------------------------------------------- FP8 (E4M3) codes
+//
+// gfx950's conversions use the E4M3 layout of the cache format (bias 7,
+// largest finite 448, one NaN code per sign), rounding to nearest even; an
+// encode of a magnitude past the largest finite value gives NaN, so values are
+// clamped to +-448 first (saturating conversion).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// 8 codes (two dwords, lowest byte first) -> 8 floats
+__device__ __forceinline__ void unpack8_e4m3(uint32_t lo, uint32_t hi, float *f) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+  f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+}
+
+__device__ __forceinline__ float sat_e4m3(float v) { return v != v ? v : fminf(fmaxf(v, -448.f), 448.f); }
+
+// 4 floats -> 4 codes in one dword (lowest byte first)
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+  return (uint32_t)w;
+}
+
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 // loads of data read exactly once (KV rows, weights): keep them out of the caches' way

@@ -63,6 +63,9 @@ struct LayerArgs {
   // device from the lengths (vm_items = 0)
   int vm_items;
   int vm_pre[kVmMaxSeqs + 1];
+  // FP8 (E4M3) cache: kc / vc hold one code per element; per-kv-head scales of K and V
+  int kv8;
+  const float *ksc, *vsc;
 };
 
 struct WorkspaceLayout {

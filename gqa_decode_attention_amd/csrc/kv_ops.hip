@@ -10,9 +10,10 @@ namespace asr {
 namespace {
 
 struct AppendArgs {
-  const uint4 *k_new, *v_new;  // [B][n][nkv][d] 16-bit, d = 128 -> 16 uint4 per row
+  const uint4 *k_new, *v_new;  // [B][n][nkv][d] elements of `chunks` x 16 bytes per row (d = 128)
   const int32_t *slots;
-  uint16_t *kc, *vc;
+  unsigned char *kc, *vc;
+  int chunks;                  // 16-byte pieces per row: 16 (16-bit), 8 (E4M3 codes)
   int32_t *lens;
   uint32_t *status;
   int B, n, nkv, batch_cap, capacity;
@@ -25,11 +26,12 @@ __device__ __forceinline__ bool append_target(const AppendArgs &a, int b, int &s
   return L >= 0 && L + a.n <= a.capacity;
 }
 
-// 16 threads copy one 256-byte row of K and of V.
+// `chunks` threads copy one row of K and of V (256 bytes of 16-bit elements or
+// 128 bytes of E4M3 codes).
 __global__ __launch_bounds__(256) void k_append_rows(AppendArgs a) {
   const size_t total_rows = (size_t)a.B * a.n * a.nkv;
-  const size_t idx = (size_t)blockIdx.x * 16 + threadIdx.x / 16;
-  const int part = threadIdx.x % 16;
+  const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) / a.chunks;
+  const int part = threadIdx.x % a.chunks;
   if (idx >= total_rows) return;
   const int g = (int)(idx % a.nkv);
   const size_t br = idx / a.nkv;
@@ -37,9 +39,9 @@ __global__ __launch_bounds__(256) void k_append_rows(AppendArgs a) {
   const int b = (int)(br / a.n);
   int slot, L;
   if (!append_target(a, b, slot, L)) return;
-  const size_t dst = (((size_t)slot * a.nkv + g) * a.capacity + L + r) * kHeadDim;
-  reinterpret_cast<uint4 *>(a.kc + dst)[part] = a.k_new[idx * 16 + part];
-  reinterpret_cast<uint4 *>(a.vc + dst)[part] = a.v_new[idx * 16 + part];
+  const size_t dst = (((size_t)slot * a.nkv + g) * a.capacity + L + r) * (size_t)a.chunks * 16;
+  reinterpret_cast<uint4 *>(a.kc + dst)[part] = a.k_new[idx * a.chunks + part];
+  reinterpret_cast<uint4 *>(a.vc + dst)[part] = a.v_new[idx * a.chunks + part];
 }
 
 // Runs after k_append_rows in stream order, so every row copy has read lens.
@@ -81,13 +83,13 @@ __global__ __launch_bounds__(256) void k_crop(CropArgs a) {
 
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
                             const int32_t *slots, int B, int n, hipStream_t s) {
-  (void)dtype;  // a bit-exact copy: the element type does not matter
-  AppendArgs a;
+  AppendArgs a;   // a bit-exact copy: only the element size matters
   a.k_new = reinterpret_cast<const uint4 *>(k_new);
   a.v_new = reinterpret_cast<const uint4 *>(v_new);
   a.slots = slots;
-  a.kc = reinterpret_cast<uint16_t *>(kv.k);
-  a.vc = reinterpret_cast<uint16_t *>(kv.v);
+  a.kc = reinterpret_cast<unsigned char *>(kv.k);
+  a.vc = reinterpret_cast<unsigned char *>(kv.v);
+  a.chunks = dtype == ASR_FP8_E4M3 ? 8 : 16;
   a.lens = kv.lens;
   a.status = kv.status;
   a.B = B;
@@ -96,7 +98,7 @@ hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new
   a.batch_cap = kv.batch_cap;
   a.capacity = kv.capacity;
   const size_t rows = (size_t)B * n * kv.n_kv_heads;
-  hipLaunchKernelGGL(k_append_rows, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_append_rows, dim3((unsigned)((rows * a.chunks + 255) / 256)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_append_lens, dim3((B + 255) / 256), dim3(256), 0, s, a);

@@ -44,8 +44,8 @@
 extern "C" {
 #endif
 
-/* element types */
-enum { ASR_F16 = 0, ASR_BF16 = 1, ASR_F32 = 2 };
+/* element types (ASR_FP8_E4M3: KV caches only) */
+enum { ASR_F16 = 0, ASR_BF16 = 1, ASR_F32 = 2, ASR_FP8_E4M3 = 3 };
 
 /* return codes */
 enum {
@@ -122,6 +122,18 @@ typedef struct asr_attn_weights {
  * on a layer advances only that layer's lengths.  Position t of sequence
  * slot s, kv head g lives at k[((s * n_kv_heads + g) * capacity + t) * head_dim].
  * Positions >= lens[s] hold no committed data and are never read.
+ *
+ * An FP8 cache ("Baseten optimizes Qwen3-ASR 1.7B", section "KV cache
+ * quantization": the cache in FP8, half the bytes each step reads, the
+ * attention arithmetic at full precision) holds one E4M3 code per element
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest finite value
+ * 448, no infinities) and one fp32 scale per kv head for K and for V: the
+ * cached value of a code c of kv head g is k_scale[g] * value(c).  A row the
+ * library appends is stored as the code nearest to value / scale, ties to the
+ * even code, magnitudes past 448 saturating to 448.  The layer calls take an
+ * FP8 cache for calls of more than 4 rows (B for decode, B * k for verify) with
+ * 2 or 4 q heads per kv head and the stream-ordered dispatch; other calls on an
+ * FP8 cache return ASR_EUNSUPPORTED.
  */
 typedef struct asr_kv_layer {
   void *k;              /* [batch_cap][n_kv_heads][capacity][head_dim], elements of dtype */
@@ -132,7 +144,9 @@ typedef struct asr_kv_layer {
   int32_t capacity;
   int32_t n_kv_heads;
   int32_t head_dim;
-  int32_t dtype;        /* ASR_F16 or ASR_BF16 */
+  int32_t dtype;        /* ASR_F16 or ASR_BF16 (the layer's dtype), or ASR_FP8_E4M3 */
+  const float *k_scale; /* ASR_FP8_E4M3: [n_kv_heads] fp32 scales of K (device); else ignored */
+  const float *v_scale; /* ASR_FP8_E4M3: [n_kv_heads] fp32 scales of V (device); else ignored */
 } asr_kv_layer;
 
 /*
@@ -222,7 +236,8 @@ int asr_attn_layer_verify(const asr_attn_config *cfg, const asr_attn_weights *w,
  * ("Can CTC make Qwen3-ASR faster?", section 11 Phase D: build the prompt KV
  * once, then verify blocks against it; the faster-qwen-asr GB10 record's
  * configuration writes prefill straight into a static cache).
- * k_new, v_new are [B][n][n_kv_heads][head_dim] elements of kv->dtype; the n
+ * k_new, v_new are [B][n][n_kv_heads][head_dim] elements of kv->dtype (E4M3
+ * codes for an FP8 cache: copied as they are, the scales do not enter); the n
  * rows of sequence b go to positions lens[s] .. lens[s] + n - 1 of slot
  * s = slots[b] (NULL: b), then lens[s] grows by n.  A sequence whose rows
  * would pass the capacity is skipped (ASR_STATUS_CAPACITY).  Slots distinct.

@@ -90,3 +90,47 @@ def oracle_cache(kbits, vbits, lens, dtype, seqs=None) -> oracle.KVCache:
     seqs = list(range(len(lens))) if seqs is None else list(seqs)
     c = oracle.KVCache(kbits[seqs].copy(), vbits[seqs].copy(), np.asarray(lens, np.int64)[seqs].copy(), dtype)
     return c
+
+
+def fill_cache_e4m3(stream, layer, lens, capacity, nkv=8, seqs=None):
+    """Host FP8 cache codes [batch_cap][nkv][capacity][128] and the per-kv-head scales."""
+    ks, vs = si.kv_scales(stream, layer, nkv)
+    B = len(lens)
+    k = np.zeros((B, nkv, capacity, 128), np.uint8)
+    v = np.zeros_like(k)
+    for s in (range(B) if seqs is None else seqs):
+        kc, vc = si.kv_rows_e4m3(stream, layer, s, int(lens[s]), ks, vs, nkv=nkv)
+        k[s, :, : lens[s]] = kc
+        v[s, :, : lens[s]] = vc
+    return k, v, ks, vs
+
+
+def device_cache_e4m3(kcodes, vcodes, lens, ks, vs) -> ga.KVLayer:
+    return ga.KVLayer(torch.from_numpy(kcodes).cuda(), torch.from_numpy(vcodes).cuda(),
+                      torch.tensor(np.asarray(lens, np.int32), device="cuda"),
+                      torch.zeros(1, dtype=torch.int32, device="cuda"),
+                      torch.from_numpy(np.asarray(ks, np.float32)).cuda(), torch.from_numpy(np.asarray(vs, np.float32)).cuda())
+
+
+def oracle_cache_e4m3(kcodes, vcodes, lens, ks, vs, seqs=None) -> oracle.KVCache:
+    seqs = list(range(len(lens))) if seqs is None else list(seqs)
+    return oracle.KVCache(kcodes[seqs].copy(), vcodes[seqs].copy(), np.asarray(lens, np.int64)[seqs].copy(),
+                          oracle.E4M3, 0, np.asarray(ks, np.float64), np.asarray(vs, np.float64))
+
+
+def check_codes(got, want, max_frac=0.01):
+    """Appended FP8 codes against the oracle's: the GPU quantises its fp32 value, the oracle the
+    exact one, so a code may sit one step away where the two straddle a rounding boundary
+    (codes of one sign are ordered by value, so one step is a difference of one); such
+    straddles must stay rare.  Returns the fraction that differ."""
+    got = np.asarray(got, np.uint8).astype(np.int64)
+    want = np.asarray(want, np.uint8).astype(np.int64)
+    same_sign = (got & 0x80) == (want & 0x80)
+    g7, w7 = got & 0x7F, want & 0x7F
+    # one step apart: same sign and adjacent magnitudes, or across zero (a zero code and the
+    # smallest subnormal of either sign)
+    ok = (same_sign & (np.abs(g7 - w7) <= 1)) | (~same_sign & (g7 + w7 <= 1))
+    assert ok.all(), f"{int((~ok).sum())} codes more than one step from the oracle's"
+    frac = float(np.mean(got != want)) if got.size else 0.0
+    assert frac <= max_frac, f"{frac:.3%} of the codes differ from the oracle's"
+    return frac

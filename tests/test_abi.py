@@ -115,3 +115,21 @@ def test_workspace_counters_sit_at_fixed_offsets():
     n1, n2, n3 = (ga.workspace_bytes(cfg, r, 1024) for r in (1, 2, 3))
     assert n1 > 2048 * 32 * 4            # the counter block of the largest call is always there
     assert abs((n3 - n2) - (n2 - n1)) <= 8 * 256   # per-row regions only (256-byte alignment)
+
+
+def test_fp8_cache_validation_on_the_host():
+    """An FP8 cache needs its K and V scales; it takes calls of more than 4 rows only."""
+    ga, lib = _lib()
+    fake = ctypes.c_void_p(0x1000)
+    w = ga._lib.AsrAttnWeights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cfg = ga.config(dtype="bf16")
+    no_scales = ga._lib.AsrKvLayer(0x1000, 0x1000, 0x1000, None, 8, 64, 8, 128, ga.FP8_E4M3, None, None)
+    scaled = ga._lib.AsrKvLayer(0x1000, 0x1000, 0x1000, None, 8, 64, 8, 128, ga.FP8_E4M3, 0x1000, 0x1000)
+    dec = lib.asr_attn_layer_decode
+    args = lambda kv, B, c=cfg: (ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), fake, None, None, B, None, None,
+                                 fake, fake, 1 << 30, None)
+    assert dec(*args(no_scales, 6)) == -1
+    assert dec(*args(scaled, 4)) == -2                               # few rows: no FP8 kernel
+    assert dec(*args(scaled, 6, ga.config(dtype="bf16", n_kv_heads=2)), ) == -1   # kv heads differ from the cache
+    assert dec(*args(scaled, 6, ga.config(dtype="bf16", dispatch=ga.DISPATCH_FUSED))) == -2
+    assert lib.asr_kv_append(ctypes.byref(no_scales), fake, fake, None, 1, 1, None) == -1

@@ -9,16 +9,18 @@ generated token = 28 layer calls; step s of a 130-step round uses cache
 length 795 + s, and a crop returns the caches to 795 after step 129.  Each
 step is one captured HIP graph, replayed, so host overhead stays out of the
 timed region (the static one-token step of that page's section 08, step 2).
+The timed region starts a round at step 0 and covers exactly ``--steps``
+steps; ``config.workload`` names the committed lengths it covered.
 
-Second workload (``--no-batched`` skips it): ragged batched decode of 64
-sequences in bf16, committed lengths uniform in [200, 1500]; one step = 28
-layer calls + the crop back to the committed lengths, reported in tokens/s.
-Also reported: the bs1 verify block for k = 4, 8, 16 (``--no-verify``) and
-the hidden-2048 batch-64 decode with a k = 8 verify on 8 sequences
-(``--no-wide``).
+Other legs (each can be skipped): ragged batched decode of 64 sequences in
+bf16, committed lengths uniform in [200, 1500], with a 16-bit and with an FP8
+(E4M3) cache (``--no-batched``, ``--no-fp8``); the bs1 verify block for
+k = 4, 8, 16 (``--no-verify``); the hidden-2048 batch-64 decode with a k = 8
+verify on 8 sequences (``--no-wide``).  Every leg reports its own roofline
+(algorithmic bytes over the measured time, against 8 TB/s).
 
-Roofline: a second timed region replays the same calls eagerly with HIP
-events that the library has the runtime stamp at the start and end of each
+Per-kernel roofline: a second timed region replays the same calls eagerly with
+HIP events that the library has the runtime stamp at the start and end of each
 phase kernel on the launch stream (hipExtLaunchKernelGGL), which gives each
 kernel's average duration; the dominant kernel's algorithmic bytes over that
 duration, against the 8 TB/s HBM peak, is the roofline fraction.  ``traffic``
@@ -81,6 +83,7 @@ def parse():
     p.add_argument("--no-batched", action="store_true", help="skip the batch-64 workloads")
     p.add_argument("--no-verify", action="store_true", help="skip the bs1 verify blocks")
     p.add_argument("--no-wide", action="store_true", help="skip the hidden-2048 batch-64 workload")
+    p.add_argument("--no-fp8", action="store_true", help="skip the batch-64 decode on an FP8 cache")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--dispatch", type=int, default=0, help="0 auto, 1 one kernel per phase, 2 fused")
@@ -94,19 +97,31 @@ def parse():
     return p.parse_args()
 
 
-def phase_bytes(H, nq, nkv, d, committed, rows, e_in=2, e_out=4):
+def phase_bytes(H, nq, nkv, d, committed, rows, e_in=2, e_out=4, e_kv=2):
     """Algorithmic HBM bytes of each phase of one layer call (workspace traffic not counted).
 
     qkv_projection: W_qkv, the three norm gains and x, read once.  attention: the committed K/V
-    rows read once and the appended K/V rows written.  o_proj: W_o read once, out written."""
+    rows of every sequence read once and the appended K/V rows written (``e_kv`` bytes per cached
+    element: 2, or 1 for an FP8 cache).  o_proj: W_o read once, out written."""
     qkv = ((nq + 2 * nkv) * d * H + H + 2 * d) * 2 + rows * H * e_in
-    att = sum(committed) * 2 * nkv * d * 2 + rows * 2 * nkv * d * 2
+    att = sum(committed) * 2 * nkv * d * e_kv + rows * 2 * nkv * d * e_kv
     oproj = H * nq * d * 2 + rows * H * e_out
     return {"qkv_projection": qkv, "attention": att, "o_proj": oproj}
 
 
-def layer_bytes(H, nq, nkv, d, committed, rows, e_in=2, e_out=4):
-    return sum(phase_bytes(H, nq, nkv, d, committed, rows, e_in, e_out).values())
+def layer_bytes(H, nq, nkv, d, committed, rows, e_in=2, e_out=4, e_kv=2):
+    return sum(phase_bytes(H, nq, nkv, d, committed, rows, e_in, e_out, e_kv).values())
+
+
+def step_roofline(bytes_per_step, ms_per_step):
+    """Whole-step rate: algorithmic bytes of every kernel of the step over the step's time."""
+    gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": round(bytes_per_step)}
+
+
+# kernels one layer call launches (stream-ordered dispatch: projection, attention, o_proj)
+KERNELS_PER_LAYER_CALL = 3
 
 
 def roofline(mean_us, bphase, traffic):
@@ -222,6 +237,11 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     us_token = ms_step * 1000.0
     committed = [P0 + (i % NSTEP) for i in range(args.steps)]
+    if args.steps <= NSTEP:
+        timed_kv = f"KV {P0}->{P0 + args.steps} ({args.steps} decode steps of a {NSTEP}-step round from {P0})"
+    else:
+        timed_kv = (f"KV {P0}->{P0 + NSTEP} ({args.steps} decode steps: {NSTEP}-step rounds from {P0}, "
+                    f"a crop back to {P0} after each)")
     bytes_call = float(np.mean([layer_bytes(H, 16, 8, 128, [L], 1) for L in committed]))
     us_call = us_token / NL
     lens_ok = all(int(kv.lens.item()) == P0 + (args.steps % NSTEP) for kv in kvs)
@@ -273,27 +293,34 @@ def main():
         "dtype": "f16 (fp32 arithmetic)",
         "data": "synthetic: seeded N(0,1) activations and cache, N(0,0.02) weights, norm gains 1+N(0,0.02)",
         "config": {"workload": "28-layer decoder attention, bs1, fp16, hidden 1024, 16q/8kv heads, head_dim 128, "
-                               "KV 795->925 over 130 steps",
+                               + timed_kv,
                    "layers": NL, "batch": 1, "hidden": H, "prefill": P0, "decode_steps": NSTEP,
                    "us_per_layer_token": round(us_call, 3),
                    "layer_call_gbs": round(bytes_call / us_call / 1e3, 1),
                    "layer_call_bytes": round(bytes_call),
                    "dispatch": args.dispatch, "kv_split": args.kv_split},
         "roofline": roofline(mean_us, bphase, measured_traffic("bs1")),
+        "launches_per_token": round(NL * (1 if args.dispatch == 2 else KERNELS_PER_LAYER_CALL) + 1.0 / NSTEP, 3),
+        "step_roofline": step_roofline(bytes_call * NL, ms_step),
     }
 
     if verify is not None:
         result["verify"] = verify
     if not args.no_batched:
         result["batched"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
+        if not args.no_fp8:
+            result["batched_fp8"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=True)
         if not args.no_wide:
-            result["batched_h2048"] = wide_batched_leg(args, ga, si, np, torch, dev, stream)
+            result["batched_h2048"] = wide_batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
-def batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
+def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False):
+    """Ragged batched decode of 64 sequences (bf16, hidden 1024, lengths uniform in [200, 1500]):
+    one step = 28 layer calls + the crop back to the committed lengths, graph-replayed.  With
+    ``fp8`` the caches hold E4M3 codes of the same draws with per-kv-head scales."""
     wl = si.WORKLOADS["ragged_batch64_h1024"]
     H, NL, B, dtype, sid = wl["hidden"], wl["layers"], wl["batch"], wl["dtype"], wl["stream"]
     lens = si.kv_lengths(sid, B, *wl["kv_len"])
@@ -304,11 +331,20 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
         wb = si.layer_weights(sid, l, H, dtype)
         weights.append(ga.Weights(*(to_dev(wb[n], dtype) for n in
                                     ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o"))))
-        kv = ga.KVLayer.empty(B, 8, CAP_B64, dtype=torch.bfloat16, device=dev)
-        rows = si.kv_rows_many(sid, l, list(range(B)), lens.tolist(), dtype)
-        for s, (kb, vb) in enumerate(rows):
-            kv.k[s, :, : lens[s]] = to_dev(kb, dtype)
-            kv.v[s, :, : lens[s]] = to_dev(vb, dtype)
+        if fp8:
+            ks, vs = si.kv_scales(sid, l)
+            kv = ga.KVLayer.empty(B, 8, CAP_B64, dtype=torch.uint8, device=dev,
+                                  k_scale=torch.from_numpy(ks).to(dev), v_scale=torch.from_numpy(vs).to(dev))
+            rows = si.kv_rows_e4m3_many(sid, l, list(range(B)), lens.tolist(), ks, vs)
+            for s_, (kc, vc) in enumerate(rows):
+                kv.k[s_, :, : lens[s_]] = torch.from_numpy(kc).to(dev)
+                kv.v[s_, :, : lens[s_]] = torch.from_numpy(vc).to(dev)
+        else:
+            kv = ga.KVLayer.empty(B, 8, CAP_B64, dtype=torch.bfloat16, device=dev)
+            rows = si.kv_rows_many(sid, l, list(range(B)), lens.tolist(), dtype)
+            for s_, (kb, vb) in enumerate(rows):
+                kv.k[s_, :, : lens[s_]] = to_dev(kb, dtype)
+                kv.v[s_, :, : lens[s_]] = to_dev(vb, dtype)
         kv.lens.copy_(torch.from_numpy(lens))
         kvs.append(kv)
     xs = torch.stack([to_dev(si.activations(sid, l, 0, B, H, dtype), dtype) for l in range(NL)])
@@ -316,7 +352,8 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
     ws = ga.alloc_workspace(cfg, B, CAP_B64, device=dev)
     base = torch.from_numpy(lens.astype(np.int32)).to(dev)
     torch.cuda.synchronize()
-    print(f"[bench] batch-64 inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    tag = "batch-64 fp8 cache" if fp8 else "batch-64"
+    print(f"[bench] {tag} inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     hl = lens.tolist()
     if args.profile_batched:
         for _ in range(args.profile_batched):
@@ -343,7 +380,8 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / n
     tok_s = B / (ms_step * 1e-3)
-    bytes_step = NL * layer_bytes(H, 16, 8, 128, lens.tolist(), B)
+    e_kv = 1 if fp8 else 2
+    bytes_step = NL * layer_bytes(H, 16, 8, 128, lens.tolist(), B, e_kv=e_kv)
     ok = all(int(kv.status.item()) == 0 for kv in kvs) and all(torch.equal(kv.lens, base) for kv in kvs)
     del g
 
@@ -365,14 +403,18 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
     torch.cuda.synchronize()
     durs = np.array([pe.elapsed_ms() for pe in pes]) * 1000.0
     mean_us = dict(zip(PHASES, durs.mean(axis=0).tolist()))
-    bphase = phase_bytes(H, 16, 8, 128, lens.tolist(), B)
-    step_gbs = bytes_step / (ms_step * 1e-3) / 1e9
-    print(f"[bench] batch-64: {ms_step * 1000:.1f} us/step, {tok_s:.0f} tok/s, {step_gbs:.0f} GB/s (ok {ok}); "
+    bphase = phase_bytes(H, 16, 8, 128, lens.tolist(), B, e_kv=e_kv)
+    sr = step_roofline(bytes_step, ms_step)
+    print(f"[bench] {tag}: {ms_step * 1000:.1f} us/step, {tok_s:.0f} tok/s, {sr['achieved']:.0f} GB/s (ok {ok}); "
           "phases (us): " + ", ".join(f"{k} {mean_us[k]:.2f}" for k in PHASES), file=sys.stderr, flush=True)
-    return {"workload": "28-layer ragged batched decode, 64 seqs, bf16, hidden 1024, KV U{200..1500}",
+    del kvs, weights
+    torch.cuda.empty_cache()
+    return {"workload": "28-layer ragged batched decode, 64 seqs, bf16 weights, "
+                        + ("FP8 (E4M3) cache with per-kv-head scales" if fp8 else "bf16 cache")
+                        + ", hidden 1024, KV U{200..1500}",
             "value": round(tok_s, 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4), "steps": n,
-            "step_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-            "roofline": roofline(mean_us, bphase, measured_traffic("b64"))}
+            "step_roofline": sr, "ok": ok,
+            "roofline": roofline(mean_us, bphase, None if fp8 else measured_traffic("b64"))}
 
 
 def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_lens, H, NL, dtype, sid, P0):
@@ -412,40 +454,47 @@ def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_l
         crop.replay()
         torch.cuda.synchronize()
         del g, crop
+        b_layer = layer_bytes(H, 16, 8, 128, [P0], k)
+        gbs = b_layer / (us / NL * 1e-6) / 1e9
         out[f"k{k}"] = {"us_per_block": round(us, 2), "us_per_layer_block": round(us / NL, 3),
-                        "us_per_candidate_token": round(us / k, 2), "ok": ok}
+                        "us_per_candidate_token": round(us / k, 2), "ok": ok,
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_layer_block": b_layer}}
         print(f"[bench] verify bs1 k={k}: {us:.1f} us per 28-layer block, {us / NL:.2f} us per layer, "
               f"{us / k:.1f} us per candidate token (ok {ok})", file=sys.stderr, flush=True)
     return out
 
 
-def wide_batched_leg(args, ga, si, np, torch, dev, stream):
+def wide_batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
     """Ragged batched decode at hidden 2048 (64 sequences, bf16, lengths uniform in [1024, 4096])
-    and a k = 8 verify on 8 of them.  Weights and caches are drawn on the device from a seeded
-    torch generator (the host generator would take minutes for 18 GB of caches); lengths and the
-    verify choice come from the shared generator."""
+    and a k = 8 verify on 8 of them.  Every input comes from the shared seeded generator: the
+    weights and activations of each layer, and the caches of layer 0, which the other 27 layers
+    receive as device copies (drawing 18 GB of cache rows on the host would take minutes; the
+    values do not change the work)."""
+    from concurrent.futures import ThreadPoolExecutor
     wl = si.WORKLOADS["ragged_batch64_h2048"]
     H, NL, B, dtype, sid = wl["hidden"], wl["layers"], wl["batch"], wl["dtype"], wl["stream"]
     k, nseq = wl["verify_k"][0], wl["verify_seqs"]
     lens = si.kv_lengths(sid, B, *wl["kv_len"])
-    tdt = torch.bfloat16
     t0 = time.time()
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1000 + sid)
-    nqkv = (16 + 2 * 8) * 128
-
-    def randn(shape, std=1.0, mean=0.0):
-        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std + mean).to(tdt)
-
-    weights, kvs = [], []
-    for _ in range(NL):
-        weights.append(ga.Weights(randn((H,), 0.02, 1.0), randn((nqkv, H), 0.02), randn((128,), 0.02, 1.0),
-                                  randn((128,), 0.02, 1.0), randn((H, 16 * 128), 0.02)))
-        kv = ga.KVLayer(randn((B, 8, CAP_W64, 128)), randn((B, 8, CAP_W64, 128)),
-                        torch.from_numpy(lens.astype(np.int32)).to(dev), torch.zeros(1, dtype=torch.int32, device=dev))
-        kvs.append(kv)
-    xs = randn((NL, B, H))
-    xv = randn((NL, nseq, k, H))
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        wbits = list(ex.map(lambda l: si.layer_weights(sid, l, H, dtype), range(NL)))
+    weights = [ga.Weights(*(to_dev(wb[n], dtype) for n in ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o")))
+               for wb in wbits]
+    del wbits
+    kv0 = ga.KVLayer.empty(B, 8, CAP_W64, dtype=torch.bfloat16, device=dev)
+    for s_, (kb, vb) in enumerate(si.kv_rows_many(sid, 0, list(range(B)), lens.tolist(), dtype)):
+        kv0.k[s_, :, : lens[s_]] = to_dev(kb, dtype)
+        kv0.v[s_, :, : lens[s_]] = to_dev(vb, dtype)
+    kvs = [kv0]
+    for _ in range(1, NL):
+        kvs.append(ga.KVLayer(kv0.k.clone(), kv0.v.clone(), torch.zeros(B, dtype=torch.int32, device=dev),
+                              torch.zeros(1, dtype=torch.int32, device=dev)))
+    for kv in kvs:
+        kv.lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    xs = torch.stack([to_dev(si.activations(sid, l, 0, B, H, dtype), dtype) for l in range(NL)])
+    xv = torch.stack([to_dev(si.activations(sid, l, 1, nseq * k, H, dtype).reshape(nseq, k, H), dtype)
+                      for l in range(NL)])
     outs = torch.empty((NL, B, H), dtype=torch.float32, device=dev)
     outv = torch.empty((NL, nseq, k, H), dtype=torch.float32, device=dev)
     cfg = ga.config(hidden=H, dtype=dtype, dispatch=args.dispatch, kv_split=args.kv_split)
@@ -491,6 +540,7 @@ def wide_batched_leg(args, ga, si, np, torch, dev, stream):
     ms_dec, ok_d = timed(decode_calls, max(10, args.steps // 8))
     ms_ver, ok_v = timed(verify_calls, max(10, args.steps // 8))
     bytes_step = NL * layer_bytes(H, 16, 8, 128, lens.tolist(), B)
+    bytes_ver = NL * layer_bytes(H, 16, 8, 128, lens[chosen].tolist(), nseq * k)
     tok_s = B / (ms_dec * 1e-3)
     gbs = bytes_step / (ms_dec * 1e-3) / 1e9
     print(f"[bench] batch-64 hidden 2048: {ms_dec * 1000:.1f} us/step, {tok_s:.0f} tok/s, {gbs:.0f} GB/s (ok {ok_d}); "
@@ -500,21 +550,31 @@ def wide_batched_leg(args, ga, si, np, torch, dev, stream):
     torch.cuda.empty_cache()
     return {"workload": "28-layer ragged batched decode, 64 seqs, bf16, hidden 2048, KV U{1024..4096}",
             "value": round(tok_s, 1), "unit": "tokens/s", "ms_per_step": round(ms_dec, 4),
-            "step_gbs": round(gbs, 1), "step_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ok": ok_d,
+            "step_roofline": step_roofline(bytes_step, ms_dec), "ok": ok_d,
             "verify": {"k": k, "sequences": nseq, "us_per_block": round(ms_ver * 1000, 1),
-                       "us_per_layer_block": round(ms_ver * 1000 / NL, 2), "ok": ok_v}}
+                       "us_per_layer_block": round(ms_ver * 1000 / NL, 2), "ok": ok_v,
+                       "roofline": step_roofline(bytes_ver, ms_ver)}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(budget_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the bs1 workload: the 28 layers of
-    steps 0, 1, ... until the budget is spent; reported in microseconds per token."""
+    """The fp64 oracle, as it stands, on bounded samples: the bs1 decode workload with all host
+    threads (the 28 layers of steps 0, 1, ... until the budget is spent; us per token), then with
+    one thread the single-layer KV-64 call and the 28-layer verify blocks (k = 4, 8, 16) from 795."""
     import oracle
     from synth import inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     wl = si.WORKLOADS["decode_bs1_28layers_kv795"]
     H, dtype, sid, P0, max_steps = wl["hidden"], wl["dtype"], wl["stream"], 795, 130
     ocfg = oracle.BlockConfig(hidden=H, dtype=dtype)
@@ -525,6 +585,7 @@ def cpu_baseline(budget_s):
         c = oracle.KVCache.empty(1, 8, CAP_BS1, 128, dtype)
         c.k[0, :, :P0], c.v[0, :, :P0], c.lens[0] = kb, vb, P0
         layers.append((w, c))
+    base = [c.copy() for _, c in layers]
     calls, step = 0, 0
     t0 = time.perf_counter()
     while step < max_steps:
@@ -536,9 +597,33 @@ def cpu_baseline(budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(dt / calls * 28 * 1e6, 1), "unit": "us/token", "cores": cores, "kind": "oracle",
-            "sample": f"{step} decode steps x 28 layers of the bs1 workload (KV 795..{795 + step - 1}), "
-                      f"fp64 NumPy oracle, {calls} layer calls in {dt:.1f}s"}
+    out = {"value": round(dt / calls * 28 * 1e6, 1), "unit": "us/token", "cores": cores, "kind": "oracle",
+           "cpu": cpu_model(),
+           "sample": f"{step} decode steps x 28 layers of the bs1 workload (KV 795..{795 + step - 1}), "
+                     f"fp64 NumPy oracle on {cores} threads, {calls} layer calls in {dt:.1f}s"}
+    with threadpool_limits(limits=1):
+        w1 = si.WORKLOADS["decode_bs1_1layer_kv64"]
+        s1 = w1["stream"]
+        o1 = oracle.BlockConfig(hidden=w1["hidden"], dtype=w1["dtype"])
+        wt = oracle.LayerWeights.from_bits(si.layer_weights(s1, 0, w1["hidden"], w1["dtype"]), w1["dtype"])
+        kb, vb = si.kv_rows(s1, 0, 0, 64, w1["dtype"])
+        reps, t1 = 0, time.perf_counter()
+        while reps < 20 or time.perf_counter() - t1 < 1.0:
+            c = oracle.KVCache.empty(1, 8, 128, 128, w1["dtype"])
+            c.k[0, :, :64], c.v[0, :, :64], c.lens[0] = kb, vb, 64
+            oracle.decode(o1, wt, c, si.activations(s1, 0, 0, 1, w1["hidden"], w1["dtype"]))
+            reps += 1
+        out["one_thread_single_layer_kv64_us_per_call"] = round((time.perf_counter() - t1) / reps * 1e6, 1)
+        w3 = si.WORKLOADS["verify_bs1_28layers_kv795"]
+        ver = {}
+        for k in w3["verify_k"]:
+            caches = [c.copy() for c in base]
+            t3 = time.perf_counter()
+            for l in range(28):
+                oracle.verify(ocfg, layers[l][0], caches[l], si.activations(sid, l, 1000 + k, k, H, dtype)[None])
+            ver[f"k{k}"] = round((time.perf_counter() - t3) * 1e6, 1)
+        out["one_thread_verify_28_layers_us_per_block"] = ver
+    return out
 
 
 if __name__ == "__main__":

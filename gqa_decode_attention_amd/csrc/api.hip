@@ -197,8 +197,8 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   int attn_grid = (int)(bound < 1 ? 1 : (bound > cap_grid ? cap_grid : bound));
   if (attn_vmfma_used(a)) {
     // verify blocks on the matrix cores: items (sequence, kv head, chunk of
-    // `split` keys, a multiple of the four waves' 32-key steps), enough of them
-    // for a few per CU; at most kMaxChunks chunks per sequence
+    // `split` keys, a multiple of the four waves' 32-key steps); at most
+    // kMaxChunks chunks per sequence
     int split = 128;
     while (split < kMaxSplit && (long long)split * kMaxChunks < kv->capacity) split += 128;
     auto items = [&](int sp) {
@@ -210,7 +210,9 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
       return t * a.nkv;
     };
     if (!cfg->kv_split) {
-      while (split < kMaxSplit && items(split) > 3LL * cus) split *= 2;
+      // an item's chain (loads, products, combine, count) is latency, so longer items stream
+      // better: the largest chunk that still leaves about one item per CU
+      while (split < kMaxSplit && 4 * items(2 * split) >= 3LL * cus) split *= 2;
     } else {
       split = cfg->kv_split < split ? split : (cfg->kv_split + 127) / 128 * 128;
     }

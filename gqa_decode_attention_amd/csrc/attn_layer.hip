@@ -398,11 +398,7 @@ __device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 }
 // the same with the nontemporal hint: a stream read once, kept out of the caches' way
 constexpr int kCachePolicyStream = 2;   // nt
-// 8 bytes, with or without the nontemporal hint
-__device__ __forceinline__ uint2 ld_buf8(__amdgpu_buffer_rsrc_t r, uint32_t off, bool nt) {
-  return __builtin_bit_cast(uint2, nt ? __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyStream)
-                                      : __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
+
 __device__ __forceinline__ uint4 ld_buf_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyStream));
 }
@@ -944,8 +940,8 @@ __device__ __forceinline__ int wcur_next(WCur &c, const LayerArgs &A, const int 
 // cached row once (one row per sequence), so the stream carries the
 // nontemporal hint; rows of a verify block read their sequence's rows again
 // and keep plain loads.
-// F8: the cache holds E4M3 codes (128-byte rows); the same dims come as two
-// 8-byte loads (lanes kl = 0..7 of a key cover its row in two instructions).
+// F8: the cache holds E4M3 codes (128-byte rows); lane kl takes dims
+// [16 kl, 16 kl + 16) with one 16-byte load, so a wave's load covers 8 whole lines.
 template <bool NT, bool F8>
 __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, uint4 (&r)[4]) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
@@ -956,14 +952,14 @@ __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, ui
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(reinterpret_cast<const unsigned char *>(A.kc) + base, region);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(reinterpret_cast<const unsigned char *>(A.vc) + base, region);
   const int last = max(min(rfl(c.te), rfl(c.L)) - 1, 0);
-  if constexpr (F8) {
-    const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * RB + kl * 8;
-    const uint2 a = ld_buf8(Kr, off, NT), b = ld_buf8(Kr, off + 64, NT);
-    const uint2 e = ld_buf8(Vr, off, NT), f = ld_buf8(Vr, off + 64, NT);
+  if constexpr (F8) {   // dims [16 kl, 16 kl + 16): one 16-byte load each for K and V
+    const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * RB + kl * 16;
+    const uint4 a = NT ? ld_buf_nt(Kr, off) : ld_buf(Kr, off);
+    const uint4 e = NT ? ld_buf_nt(Vr, off) : ld_buf(Vr, off);
     r[0] = make_uint4(a.x, a.y, 0u, 0u);
-    r[1] = make_uint4(b.x, b.y, 0u, 0u);
+    r[1] = make_uint4(a.z, a.w, 0u, 0u);
     r[2] = make_uint4(e.x, e.y, 0u, 0u);
-    r[3] = make_uint4(f.x, f.y, 0u, 0u);
+    r[3] = make_uint4(e.z, e.w, 0u, 0u);
   } else {
     const uint32_t off = (uint32_t)min(rfl(c.t) + kr, last) * RB + kl * 16;
     r[0] = NT ? ld_buf_nt(Kr, off) : ld_buf(Kr, off);
@@ -1076,7 +1072,9 @@ __device__ __forceinline__ void wresolve(const LayerArgs &A, const WPending &p) 
 template <int DT, int GROUP, bool NT, bool F8>
 __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *rinfo, int w, int W) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
-  const int d0 = 8 * kl, d1 = 64 + 8 * kl;
+  // a lane's 16 dims: [8 kl, 8 kl + 8) and [64 + 8 kl, ..) of a 256-byte 16-bit row (two whole
+  // lines per key across the 8 lanes), or [16 kl, 16 kl + 16) of a 128-byte FP8 row (one line)
+  const int d0 = F8 ? 16 * kl : 8 * kl, d1 = F8 ? 16 * kl + 8 : 64 + 8 * kl;
   const int T = pre[A.rows];
   const int S = max(T / W + 1, A.split);
   const long long s0l = (long long)w * S;
@@ -1092,13 +1090,16 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   WCur lc;
   wcur_enter(lc, A, pre, rinfo, lo, off / nv0, off % nv0, s1 - s0);
   WCur cc = lc;
-  // three register sets in rotation: the loads of step i + 2 are issued before
-  // the arithmetic of step i, into the set step i - 1 has released
-  uint4 ra[4], rb[4], rc[4];
-  wstep_load<NT, F8>(A, lc, ra);
-  wcur_next(lc, A, pre, rinfo);
-  wstep_load<NT, F8>(A, lc, rb);
-  wcur_next(lc, A, pre, rinfo);
+  // NS register sets in rotation: the loads of step i + NS - 1 are issued before
+  // the arithmetic of step i.  An FP8 step is half the bytes of a 16-bit one, so
+  // it keeps twice as many steps in flight (the same bytes in flight per wave).
+  constexpr int NS = F8 ? 5 : 3;
+  uint4 rs[NS][4];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) {
+    wstep_load<NT, F8>(A, lc, rs[i]);
+    wcur_next(lc, A, pre, rinfo);
+  }
 
   const float qs = kLog2e * rsqrtf((float)kHeadDim);
   const uint32_t row_bytes = (uint32_t)A.nqkv * 4;
@@ -1306,13 +1307,13 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   };
   begin_piece();
   for (;;) {
-    issue(rc);
-    if (!advance(ra)) break;
-    issue(ra);
-    if (!advance(rb)) break;
-    issue(rb);
-    if (!advance(rc)) break;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      issue(rs[(i + NS - 1) % NS]);
+      if (!advance(rs[i])) goto streamed;
+    }
   }
+streamed:
   wresolve<DT, GROUP>(A, pend);
 }
 

@@ -183,6 +183,14 @@ def kv_rows_many(stream, layer, seqs, lengths, dtype, nkv=N_KV_HEADS, d=HEAD_DIM
                            zip(seqs, lengths)))
 
 
+def kv_rows_e4m3_many(stream, layer, seqs, lengths, k_scale, v_scale, nkv=N_KV_HEADS, d=HEAD_DIM, threads=None):
+    """kv_rows_e4m3 for several sequences on a thread pool."""
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(lambda sl: kv_rows_e4m3(stream, layer, sl[0], sl[1], k_scale, v_scale, nkv, d),
+                           zip(seqs, lengths)))
+
+
 def activations(stream: int, layer: int, step: int, rows: int, hidden: int, dtype: str):
     """Hidden states entering the block at (layer, step): [rows][hidden], N(0, 1)."""
     return normal_bits(stream, layer, T_X, step, (rows, hidden), 1.0, 0.0, dtype)

@@ -57,3 +57,17 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_fp8_cache_halves_the_cache_bytes_only():
+    b = _bench()
+    p16 = b.phase_bytes(1024, 16, 8, 128, [200, 1500], 2)
+    p8 = b.phase_bytes(1024, 16, 8, 128, [200, 1500], 2, e_kv=1)
+    assert p8["attention"] * 2 == p16["attention"]
+    assert p8["qkv_projection"] == p16["qkv_projection"] and p8["o_proj"] == p16["o_proj"]
+
+
+def test_step_roofline_is_bytes_over_time():
+    b = _bench()
+    r = b.step_roofline(8e9, 1.0)        # 8 GB in 1 ms = 8000 GB/s
+    assert r["achieved"] == 8000.0 and r["frac"] == 1.0 and r["unit"] == "GB/s"

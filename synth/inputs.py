@@ -35,6 +35,7 @@ BF16 = "bf16"
 T_GAMMA_IN, T_WQKV, T_GAMMA_Q, T_GAMMA_K, T_WO = 0, 1, 2, 3, 4
 T_KCACHE, T_VCACHE, T_X, T_LENS, T_ACCEPT, T_VCHOICE, T_RESID = 5, 6, 7, 8, 9, 10, 11
 T_KVSCALE = 12
+T_GAMMA_POST, T_WGATE, T_WUP, T_WDOWN, T_HIDDEN = 13, 14, 15, 16, 17
 
 N_Q_HEADS = 16
 N_KV_HEADS = 8
@@ -146,6 +147,24 @@ def layer_weights(stream: int, layer: int, hidden: int, dtype: str,
         k_norm_w=normal_bits(stream, layer, T_GAMMA_K, 0, (d,), gain_std, gain_mean, dtype),
         w_o=normal_bits(stream, layer, T_WO, 0, (hidden, nq * d), w_std, 0.0, dtype),
     )
+
+
+def mlp_weights(stream: int, layer: int, hidden: int, intermediate: int, dtype: str,
+                gain_std: float = 0.02, gain_mean: float = 1.0, w_std: float = 0.02) -> dict:
+    """MLP weights of one layer as bit patterns: gate and up [intermediate][hidden], down
+    [hidden][intermediate], N(0, 0.02); the post-attention norm gain 1 + N(0, 0.02)."""
+    return dict(
+        post_norm_w=normal_bits(stream, layer, T_GAMMA_POST, 0, (hidden,), gain_std, gain_mean, dtype),
+        w_gate=normal_bits(stream, layer, T_WGATE, 0, (intermediate, hidden), w_std, 0.0, dtype),
+        w_up=normal_bits(stream, layer, T_WUP, 0, (intermediate, hidden), w_std, 0.0, dtype),
+        w_down=normal_bits(stream, layer, T_WDOWN, 0, (hidden, intermediate), w_std, 0.0, dtype),
+    )
+
+
+def hidden_f32(stream: int, layer: int, step: int, rows: int, hidden: int) -> np.ndarray:
+    """fp32 hidden states entering the MLP (the attention block's fp32 output): N(0, 1) draws
+    rounded to the nearest fp32."""
+    return rng_for(stream, layer, T_HIDDEN, step).standard_normal((rows, hidden)).astype(np.float32)
 
 
 def kv_rows(stream: int, layer: int, seq: int, length: int, dtype: str,

@@ -24,7 +24,9 @@ ERRORS = {0: "ASR_OK", -1: "ASR_EINVAL", -2: "ASR_EUNSUPPORTED", -3: "ASR_ECAPAC
 NOALLOC_SCRATCH_BYTES = 40 << 20
 
 EXPORTED = ["asr_attn_workspace_bytes", "asr_attn_layer_decode", "asr_attn_layer_decode_noalloc",
-            "asr_attn_layer_verify", "asr_kv_append", "asr_kv_crop", "asr_strerror"]
+            "asr_attn_layer_verify", "asr_kv_append", "asr_kv_crop", "asr_strerror",
+            "asr_mlp_workspace_bytes", "asr_mlp_layer", "asr_decoder_layer_workspace_bytes",
+            "asr_decoder_layer_decode", "asr_decoder_layer_verify"]
 
 _TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
 _DT_NAME = {"f16": F16, "bf16": BF16, "f32": F32}
@@ -53,6 +55,17 @@ class AsrKvLayer(ctypes.Structure):
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
+class AsrMlpConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("phase_events", ctypes.c_void_p)]
+
+
+class AsrMlpWeights(ctypes.Structure):
+    _fields_ = [("post_norm_w", ctypes.c_void_p), ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -79,6 +92,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.asr_kv_append.restype = ctypes.c_int
     lib.asr_kv_crop.argtypes = [ctypes.POINTER(AsrKvLayer), I32, P, P]
     lib.asr_kv_crop.restype = ctypes.c_int
+    MC, MW, AC, AW, KV = (ctypes.POINTER(AsrMlpConfig), ctypes.POINTER(AsrMlpWeights), ctypes.POINTER(AsrAttnConfig),
+                          ctypes.POINTER(AsrAttnWeights), ctypes.POINTER(AsrKvLayer))
+    lib.asr_mlp_workspace_bytes.argtypes = [MC, I32]
+    lib.asr_mlp_workspace_bytes.restype = SZ
+    lib.asr_mlp_layer.argtypes = [MC, MW, P, I32, P, P, SZ, P]
+    lib.asr_mlp_layer.restype = ctypes.c_int
+    lib.asr_decoder_layer_workspace_bytes.argtypes = [AC, MC, I32, I32]
+    lib.asr_decoder_layer_workspace_bytes.restype = SZ
+    lib.asr_decoder_layer_decode.argtypes = [AC, AW, MC, MW, KV, P, P, P, I32, P, P, P, SZ, P]
+    lib.asr_decoder_layer_decode.restype = ctypes.c_int
+    lib.asr_decoder_layer_verify.argtypes = [AC, AW, MC, MW, KV, P, P, P, I32, I32, P, P, P, SZ, P]
+    lib.asr_decoder_layer_verify.restype = ctypes.c_int
     lib.asr_strerror.argtypes = [ctypes.c_int]
     lib.asr_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -241,3 +266,55 @@ def kv_append(kv: KVLayer, k_new, v_new, slots=None, stream=None) -> None:
 def kv_crop(layers, new_lens, stream=None) -> None:
     arr = (AsrKvLayer * len(layers))(*[l.c for l in layers])
     _check(load().asr_kv_crop(arr, len(layers), _ptr(new_lens), _stream(stream)), "asr_kv_crop")
+
+
+def mlp_config(hidden=1024, intermediate=3072, rms_eps=1e-6, dtype="f16", in_dtype="f32", out_dtype="f32"):
+    return AsrMlpConfig(hidden, intermediate, rms_eps, _dt(dtype), _dt(in_dtype), _dt(out_dtype), None)
+
+
+class MlpWeights:
+    """One layer's MLP weights as device tensors (16-bit): post-norm gain [H], gate and up [I][H], down [H][I]."""
+
+    def __init__(self, post_norm_w, w_gate, w_up, w_down):
+        self.post_norm_w, self.w_gate, self.w_up, self.w_down = post_norm_w, w_gate, w_up, w_down
+        self.c = AsrMlpWeights(*(t.data_ptr() for t in (post_norm_w, w_gate, w_up, w_down)))
+
+
+def mlp_workspace_bytes(cfg: AsrMlpConfig, max_rows: int) -> int:
+    n = load().asr_mlp_workspace_bytes(ctypes.byref(cfg), max_rows)
+    if n == 0:
+        raise AsrError(-1, "asr_mlp_workspace_bytes")
+    return int(n)
+
+
+def mlp_layer(cfg, w: MlpWeights, h, out, workspace, stream=None) -> None:
+    _check(load().asr_mlp_layer(ctypes.byref(cfg), ctypes.byref(w.c), _ptr(h), h.shape[0], _ptr(out),
+                                _ptr(workspace), workspace.numel(), _stream(stream)), "asr_mlp_layer")
+
+
+def decoder_layer_workspace(acfg, mcfg, max_rows: int, capacity: int, device="cuda") -> torch.Tensor:
+    n = load().asr_decoder_layer_workspace_bytes(ctypes.byref(acfg), ctypes.byref(mcfg), max_rows, capacity)
+    if n == 0:
+        raise AsrError(-1, "asr_decoder_layer_workspace_bytes")
+    return torch.zeros(int(n), dtype=torch.uint8, device=device)
+
+
+def decoder_layer_decode(acfg, aw: Weights, mcfg, mw: MlpWeights, kv: KVLayer, x, out, workspace, slots=None,
+                         positions=None, host_lens=None, stream=None) -> None:
+    keep, hl = _host_lens(host_lens)
+    _check(load().asr_decoder_layer_decode(ctypes.byref(acfg), ctypes.byref(aw.c), ctypes.byref(mcfg),
+                                           ctypes.byref(mw.c), ctypes.byref(kv.c), _ptr(x), _ptr(slots),
+                                           _ptr(positions), x.shape[0], hl, _ptr(out), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "asr_decoder_layer_decode")
+    del keep
+
+
+def decoder_layer_verify(acfg, aw: Weights, mcfg, mw: MlpWeights, kv: KVLayer, x, out, workspace, slots=None,
+                         positions=None, host_lens=None, stream=None) -> None:
+    keep, hl = _host_lens(host_lens)
+    _check(load().asr_decoder_layer_verify(ctypes.byref(acfg), ctypes.byref(aw.c), ctypes.byref(mcfg),
+                                           ctypes.byref(mw.c), ctypes.byref(kv.c), _ptr(x), _ptr(slots),
+                                           _ptr(positions), x.shape[0], x.shape[1], hl, _ptr(out),
+                                           _ptr(workspace), workspace.numel(), _stream(stream)),
+           "asr_decoder_layer_verify")
+    del keep

@@ -294,9 +294,128 @@ WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity)
 
 }  // namespace asr
 
+namespace asr {
+namespace {
+
+int check_mlp(const asr_mlp_config *c) {
+  if (!c) return ASR_EINVAL;
+  if (c->hidden <= 0 || c->intermediate <= 0) return ASR_EINVAL;
+  if (c->hidden % 256 != 0 || c->hidden > 4096) return ASR_EUNSUPPORTED;
+  if (c->intermediate % 256 != 0 || c->intermediate > 16384) return ASR_EUNSUPPORTED;
+  if (c->dtype != ASR_F16 && c->dtype != ASR_BF16) return ASR_EUNSUPPORTED;
+  if (c->in_dtype != ASR_F32 && c->in_dtype != c->dtype) return ASR_EUNSUPPORTED;
+  if (c->out_dtype != ASR_F32 && c->out_dtype != c->dtype) return ASR_EUNSUPPORTED;
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return ASR_EINVAL;
+  return ASR_OK;
+}
+
+size_t mlp_ws_bytes(const asr_mlp_config *c, int rows) {
+  return align_up((size_t)2 * c->hidden * rows * sizeof(uint16_t)) +
+         align_up((size_t)2 * c->intermediate * rows * sizeof(uint16_t));
+}
+
+int run_mlp(const asr_mlp_config *c, const asr_mlp_weights *w, const void *h, int rows, void *out, void *ws,
+            size_t ws_bytes, hipStream_t stream) {
+  int rc = check_mlp(c);
+  if (rc) return rc;
+  if (rows < 0 || rows > kMaxRows) return ASR_EINVAL;
+  if (rows == 0) return ASR_OK;
+  if (!w || !w->post_norm_w || !w->w_gate || !w->w_up || !w->w_down || !h || !out) return ASR_EINVAL;
+  if (!ws || ws_bytes < mlp_ws_bytes(c, rows)) return ASR_EWORKSPACE;
+  MlpArgs a;
+  a.h = h;
+  a.in_f32 = c->in_dtype == ASR_F32;
+  a.g_post = static_cast<const uint16_t *>(w->post_norm_w);
+  a.w_gate = static_cast<const uint16_t *>(w->w_gate);
+  a.w_up = static_cast<const uint16_t *>(w->w_up);
+  a.w_down = static_cast<const uint16_t *>(w->w_down);
+  a.out = out;
+  a.out_f32 = c->out_dtype == ASR_F32;
+  a.y_hl = static_cast<uint16_t *>(ws);
+  a.a_hl = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) +
+                                        align_up((size_t)2 * c->hidden * rows * sizeof(uint16_t)));
+  a.rows = rows;
+  a.H = c->hidden;
+  a.I = c->intermediate;
+  a.eps = c->rms_eps;
+  return launch_mlp(a, c->dtype, stream, c->phase_events) == hipSuccess ? ASR_OK : ASR_EHIP;
+}
+
+// attention workspace, then h [rows][H] fp32, then the MLP's workspace
+size_t layer_ws_bytes(const asr_attn_config *acfg, const asr_mlp_config *mcfg, int rows, int capacity) {
+  const size_t att = asr_attn_workspace_bytes(acfg, rows, capacity);
+  if (!att || check_mlp(mcfg) != ASR_OK || mcfg->hidden != acfg->hidden) return 0;
+  return att + align_up((size_t)rows * acfg->hidden * sizeof(float)) + mlp_ws_bytes(mcfg, rows);
+}
+
+int run_decoder_layer(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
+                      const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x, const int32_t *slots,
+                      const int32_t *positions, int B, int n, const int32_t *host_lens, void *out, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  int rc = check_cfg(acfg);
+  if (rc) return rc;
+  if ((rc = check_mlp(mcfg))) return rc;
+  if (mcfg->hidden != acfg->hidden || mcfg->dtype != acfg->dtype || mcfg->in_dtype != ASR_F32) return ASR_EINVAL;
+  if (B < 0 || n < 1 || n > kMaxVerifyK || (long long)B * n > kMaxRows) return ASR_EINVAL;
+  if (B == 0) return ASR_OK;
+  if (!kv) return ASR_EINVAL;
+  const int rows = B * n;
+  const size_t att = asr_attn_workspace_bytes(acfg, rows, kv->capacity);
+  const size_t need = layer_ws_bytes(acfg, mcfg, rows, kv->capacity);
+  if (!att || !need) return ASR_EINVAL;
+  if (!ws || ws_bytes < need) return ASR_EWORKSPACE;
+  asr_attn_config ac = *acfg;
+  ac.out_dtype = ASR_F32;
+  char *base = static_cast<char *>(ws);
+  float *h = reinterpret_cast<float *>(base + att);
+  char *mws = base + att + align_up((size_t)rows * acfg->hidden * sizeof(float));
+  rc = run_layer(&ac, aw, kv, x, slots, positions, B, n, host_lens, x, h, ws, att, stream);
+  if (rc) return rc;
+  return run_mlp(mcfg, mw, h, rows, out, mws, mlp_ws_bytes(mcfg, rows), stream);
+}
+
+}  // namespace
+}  // namespace asr
+
 using namespace asr;
 
 extern "C" {
+
+size_t asr_mlp_workspace_bytes(const asr_mlp_config *cfg, int32_t max_rows) {
+  if (check_mlp(cfg) != ASR_OK || max_rows < 0 || max_rows > kMaxRows) return 0;
+  return mlp_ws_bytes(cfg, max_rows);
+}
+
+int asr_mlp_layer(const asr_mlp_config *cfg, const asr_mlp_weights *w, const void *h, int32_t rows, void *out,
+                  void *workspace, size_t ws_bytes, hipStream_t stream) {
+  return run_mlp(cfg, w, h, rows, out, workspace, ws_bytes, stream);
+}
+
+size_t asr_decoder_layer_workspace_bytes(const asr_attn_config *acfg, const asr_mlp_config *mcfg, int32_t max_rows,
+                                         int32_t capacity) {
+  if (max_rows < 0 || max_rows > kMaxRows) return 0;
+  return layer_ws_bytes(acfg, mcfg, max_rows, capacity);
+}
+
+int asr_decoder_layer_decode(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
+                             const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x,
+                             const int32_t *slots, const int32_t *positions, int32_t B,
+                             const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  return run_decoder_layer(acfg, aw, mcfg, mw, kv, x, slots, positions, B, 1, host_lens, out, workspace, ws_bytes,
+                           stream);
+}
+
+int asr_decoder_layer_verify(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
+                             const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x,
+                             const int32_t *slots, const int32_t *positions, int32_t B, int32_t k,
+                             const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  if (k < 1 || k > kMaxVerifyK) return ASR_EINVAL;
+  return run_decoder_layer(acfg, aw, mcfg, mw, kv, x, slots, positions, B, k, host_lens, out, workspace, ws_bytes,
+                           stream);
+}
+
 
 size_t asr_attn_workspace_bytes(const asr_attn_config *cfg, int32_t max_rows, int32_t capacity) {
   if (check_cfg(cfg) != ASR_OK || max_rows < 0 || max_rows > kMaxRows || capacity <= 0) return 0;

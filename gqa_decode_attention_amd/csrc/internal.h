@@ -68,6 +68,24 @@ struct LayerArgs {
   const float *ksc, *vsc;
 };
 
+// The rest of the decoder layer: post-attention RMSNorm, gated SiLU MLP, residual.
+struct MlpArgs {
+  const void *h;              // [rows][H] fp32 (in_f32) or 16-bit: the MLP's input and residual
+  int in_f32;
+  const uint16_t *g_post;     // [H]
+  const uint16_t *w_gate;     // [I][H]
+  const uint16_t *w_up;       // [I][H]
+  const uint16_t *w_down;     // [H][I]
+  void *out;                  // [rows][H] fp32 (out_f32) or 16-bit
+  int out_f32;
+  uint16_t *y_hl;             // workspace: [2][H / 32][rows][32] normalised input, hi and lo terms
+  uint16_t *a_hl;             // workspace: [2][I / 32][rows][32] silu(gate) * up, hi and lo terms
+  int rows, H, I;
+  float eps;
+};
+
+hipError_t launch_mlp(const MlpArgs &a, int dtype, hipStream_t s, hipEvent_t *ev);
+
 struct WorkspaceLayout {
   size_t flow, mctr, rowtab, qkv, ssq, att, att_hl, part, total;
 };

@@ -1,0 +1,207 @@
+// The rest of a decoder layer on gfx950: post-attention RMSNorm, the gated
+// SiLU MLP and the residual ("Qwen3-ASR -- Latency & Bottleneck Analysis",
+// section 03: the decoder MLP is 27.5% of decode and memory-bound at
+// 529 MB/token; section 07 "Norms are real money at this size").
+//
+// Three stream-ordered kernels:
+//   k_mlp_norm  y = h * g_post / sqrt(mean(h^2) + eps) per row, stored as two
+//               16-bit terms (hi = rne(y), lo = rne(y - hi)) in the matrix-core
+//               operand tiling [2][H / 32][rows][32]
+//   k_mlp_up    gate = W_gate y and up = W_up y on v_mfma_f32_16x16x32 (W exact
+//               16-bit, y as hi + lo), act = silu(gate) * up, stored as hi / lo
+//               tiles [2][I / 32][rows][32]
+//   k_mlp_down  out = h + W_down act (act as hi + lo)
+// A block owns 16 output features x 16 rows; its 8 waves split the
+// contraction, request every operand of a batch before the products, and add
+// their partial tiles in LDS.  Blocks of one feature tile sit on one XCD.
+#include <hip/hip_ext.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace asr {
+
+namespace {
+
+constexpr int kMlpWaves = 8;
+constexpr int kMlpBatch = 4;   // 32-wide contraction steps per operand batch
+
+struct MlpTile {
+  int col, row;
+};
+__device__ __forceinline__ MlpTile mlp_tile(int b, int rtiles) {
+  const int q = b / (8 * rtiles), rem = b - q * 8 * rtiles;
+  return MlpTile{q * 8 + rem % 8, rem / 8};
+}
+
+// operand-tiled index of (row n, column c) in a [H / 32][rows][32] plane
+__device__ __forceinline__ size_t tiled(int c, int n, int rows) { return ((size_t)(c / 32) * rows + n) * 32 + c % 32; }
+
+template <int DT>
+__device__ __forceinline__ float load_h(const MlpArgs &A, size_t i) {
+  return A.in_f32 ? reinterpret_cast<const float *>(A.h)[i] : cvt16<DT>(reinterpret_cast<const uint16_t *>(A.h)[i]);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_mlp_norm(MlpArgs A) {
+  __shared__ float s_sum[4];
+  const int n = blockIdx.x;
+  const int wave = wave_id(), lane = lane_id();
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < A.H; c += 256) {
+    const float v = load_h<DT>(A, (size_t)n * A.H + c);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) s_sum[wave] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3]) / (float)A.H + A.eps);
+  const size_t plane = (size_t)A.H * A.rows;
+  for (int c = threadIdx.x; c < A.H; c += 256) {
+    const float y = load_h<DT>(A, (size_t)n * A.H + c) * cvt16<DT>(A.g_post[c]) * inv;
+    const uint16_t hi = rne16<DT>(y);
+    const size_t i = tiled(c, n, A.rows);
+    A.y_hl[i] = hi;
+    A.y_hl[plane + i] = rne16<DT>(y - cvt16<DT>(hi));
+  }
+}
+
+// the wave's share [k0, k0 + kw * 32) of the contraction: A operand rows of W at
+// feature o, B operand hi / lo tiles of `hl` (plane = K * rows) at row n
+template <int DT, int NM>
+__device__ __forceinline__ void mlp_products(const uint16_t *const (&w)[NM], int K, const uint16_t *hl, int rows,
+                                             int o, int n, int k0, int kw, f32x4_t (&acc)[NM]) {
+  const int lane = lane_id(), g4 = lane / 16;
+  const size_t plane = (size_t)K * rows;
+  for (int s0 = 0; s0 < kw; s0 += kMlpBatch) {
+    uint4 wa[NM][kMlpBatch], hi[kMlpBatch], lo[kMlpBatch];
+#pragma unroll
+    for (int s = 0; s < kMlpBatch; ++s) {
+      const int kk = k0 + min(s0 + s, kw - 1) * 32;   // past the share: a repeated step, weight zero below
+#pragma unroll
+      for (int m = 0; m < NM; ++m) wa[m][s] = ld16_stream(w[m] + (size_t)o * K + kk + g4 * 8);
+      const size_t bi = ((size_t)(kk / 32) * rows + n) * 32 + g4 * 8;
+      hi[s] = ld16(hl + bi);
+      lo[s] = ld16(hl + plane + bi);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any product
+#pragma unroll
+    for (int s = 0; s < kMlpBatch; ++s) {
+      if (s0 + s >= kw) break;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        acc[m] = mfma16x16x32<DT>(wa[m][s], hi[s], acc[m]);
+        acc[m] = mfma16x16x32<DT>(wa[m][s], lo[s], acc[m]);
+      }
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_up(MlpArgs A) {
+  __shared__ f32x4_t s_c[2][kMlpWaves][kWave];
+  const int wave = wave_id(), lane = lane_id();
+  const int i16 = lane % 16, g4 = lane / 16;
+  const int rtiles = (A.rows + 15) / 16;
+  const MlpTile tm = mlp_tile(blockIdx.x, rtiles);
+  const int o0 = tm.col * 16, nb = tm.row * 16;
+  const int kw = A.H / 32 / kMlpWaves;
+  const uint16_t *const w[2] = {A.w_gate, A.w_up};
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  mlp_products<DT, 2>(w, A.H, A.y_hl, A.rows, o0 + i16, min(nb + i16, A.rows - 1), wave * kw * 32, kw, acc);
+  s_c[0][wave][lane] = acc[0];
+  s_c[1][wave][lane] = acc[1];
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t gsum = s_c[0][0][lane], usum = s_c[1][0][lane];
+#pragma unroll
+    for (int wv = 1; wv < kMlpWaves; ++wv) {
+      const f32x4_t a = s_c[0][wv][lane], b = s_c[1][wv][lane];
+      gsum[0] += a[0]; gsum[1] += a[1]; gsum[2] += a[2]; gsum[3] += a[3];
+      usum[0] += b[0]; usum[1] += b[1]; usum[2] += b[2]; usum[3] += b[3];
+    }
+    const int n = nb + i16;
+    if (n < A.rows) {
+      uint16_t hv[4], lv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gt = gsum[j];
+        const float act = gt / (1.f + __expf(-gt)) * usum[j];
+        hv[j] = rne16<DT>(act);
+        lv[j] = rne16<DT>(act - cvt16<DT>(hv[j]));
+      }
+      // features o0 + 4 g4 .. + 3 of row n: adjacent in the tiling
+      const size_t i = tiled(o0 + 4 * g4, n, A.rows), plane = (size_t)A.I * A.rows;
+      *reinterpret_cast<uint2 *>(A.a_hl + i) =
+          make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+      *reinterpret_cast<uint2 *>(A.a_hl + plane + i) =
+          make_uint2((uint32_t)lv[0] | ((uint32_t)lv[1] << 16), (uint32_t)lv[2] | ((uint32_t)lv[3] << 16));
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_down(MlpArgs A) {
+  __shared__ f32x4_t s_c[kMlpWaves][kWave];
+  const int wave = wave_id(), lane = lane_id();
+  const int i16 = lane % 16, g4 = lane / 16;
+  const int rtiles = (A.rows + 15) / 16;
+  const MlpTile tm = mlp_tile(blockIdx.x, rtiles);
+  const int o0 = tm.col * 16, nb = tm.row * 16;
+  const int n = nb + i16;
+  // the residual, requested before the products
+  float res[4] = {0.f, 0.f, 0.f, 0.f};
+  if (wave == 0 && n < A.rows) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) res[j] = load_h<DT>(A, (size_t)n * A.H + o0 + 4 * g4 + j);
+  }
+  const int kw = A.I / 32 / kMlpWaves;
+  const uint16_t *const w[1] = {A.w_down};
+  f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  mlp_products<DT, 1>(w, A.I, A.a_hl, A.rows, o0 + i16, min(n, A.rows - 1), wave * kw * 32, kw, acc);
+  s_c[wave][lane] = acc[0];
+  __syncthreads();
+  if (wave == 0 && n < A.rows) {
+    f32x4_t c = s_c[0][lane];
+#pragma unroll
+    for (int wv = 1; wv < kMlpWaves; ++wv) {
+      const f32x4_t d = s_c[wv][lane];
+      c[0] += d[0]; c[1] += d[1]; c[2] += d[2]; c[3] += d[3];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t o = (size_t)n * A.H + o0 + 4 * g4 + j;
+      const float val = c[j] + res[j];
+      if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
+      else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
+    }
+  }
+}
+
+using MlpKernel = void (*)(MlpArgs);
+
+hipError_t launch(MlpKernel k, dim3 grid, dim3 block, hipStream_t s, hipEvent_t *ev, int phase, const MlpArgs &a) {
+  if (ev)
+    hipExtLaunchKernelGGL(k, grid, block, 0, s, ev[2 * phase], ev[2 * phase + 1], 0u, a);
+  else
+    hipLaunchKernelGGL(k, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t mlp_launch(const MlpArgs &a, hipStream_t s, hipEvent_t *ev) {
+  hipError_t e;
+  const int rtiles = (a.rows + 15) / 16;
+  if ((e = launch(k_mlp_norm<DT>, dim3(a.rows), dim3(256), s, ev, 0, a)) != hipSuccess) return e;
+  if ((e = launch(k_mlp_up<DT>, dim3(a.I / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 1, a)) != hipSuccess)
+    return e;
+  return launch(k_mlp_down<DT>, dim3(a.H / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 2, a);
+}
+
+}  // namespace
+
+hipError_t launch_mlp(const MlpArgs &a, int dtype, hipStream_t s, hipEvent_t *ev) {
+  return dtype == ASR_BF16 ? mlp_launch<ASR_BF16>(a, s, ev) : mlp_launch<ASR_F16>(a, s, ev);
+}
+
+}  // namespace asr

@@ -261,6 +261,79 @@ int asr_kv_append(const asr_kv_layer *kv, const void *k_new, const void *v_new,
 int asr_kv_crop(const asr_kv_layer *layers, int32_t n_layers, const int32_t *new_lens,
                 hipStream_t stream);
 
+/*
+ * The rest of a decoder layer: post-attention RMSNorm, the gated SiLU MLP and
+ * the residual ("Qwen3-ASR -- Latency & Bottleneck Analysis", section 03: the
+ * decoder MLP, memory-bound at 529 MB per token over 28 layers; section 07
+ * "Norms are real money at this size").  For each row,
+ *   y   = h * post_norm_w / sqrt(mean(h^2) + rms_eps)
+ *   out = h + W_down (silu(W_gate y) * (W_up y)),   silu(u) = u / (1 + e^-u)
+ * All arithmetic is fp32; matrix-core operands that are fp32 values (y and
+ * silu(gate) * up) are split into two 16-bit terms.  Supported: hidden and
+ * intermediate multiples of 256 (hidden at most 4096, intermediate at most
+ * 16384), dtype ASR_F16 or ASR_BF16, 1 to 2048 rows.
+ */
+typedef struct asr_mlp_config {
+  int32_t hidden;        /* H */
+  int32_t intermediate;  /* I */
+  float rms_eps;
+  int32_t dtype;         /* ASR_F16 or ASR_BF16: the weights */
+  int32_t in_dtype;      /* h: ASR_F32 (the attention block's fp32 output) or dtype */
+  int32_t out_dtype;     /* ASR_F32 or dtype */
+  hipEvent_t *phase_events;  /* diagnostics, NULL normally: 6 caller-created events that receive the
+                                start and end stamps of the norm, gate/up and down kernels */
+} asr_mlp_config;
+
+/* One layer's MLP weights (device, elements of dtype, row-major [out][in]). */
+typedef struct asr_mlp_weights {
+  const void *post_norm_w;  /* [H] */
+  const void *w_gate;       /* [I][H] */
+  const void *w_up;         /* [I][H] */
+  const void *w_down;       /* [H][I] */
+} asr_mlp_weights;
+
+/* Workspace bytes of asr_mlp_layer for up to max_rows rows (0: invalid config). */
+size_t asr_mlp_workspace_bytes(const asr_mlp_config *cfg, int32_t max_rows);
+
+/*
+ * out[r] = h[r] + MLP(RMSNorm(h[r])) for rows r < rows.
+ *   h   [rows][H] in_dtype (device), the residual stream after the attention block
+ *   out [rows][H] out_dtype (device); must not overlap h or the workspace
+ * The workspace needs no initialisation.  Returns ASR_OK or a host-side ASR_E*
+ * code (nothing enqueued then).  rows = 0 is a no-op.
+ */
+int asr_mlp_layer(const asr_mlp_config *cfg, const asr_mlp_weights *w, const void *h, int32_t rows, void *out,
+                  void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes of asr_decoder_layer_decode / asr_decoder_layer_verify: the
+ * attention block's workspace, the fp32 residual stream h, the MLP's workspace.
+ */
+size_t asr_decoder_layer_workspace_bytes(const asr_attn_config *acfg, const asr_mlp_config *mcfg, int32_t max_rows,
+                                         int32_t capacity);
+
+/*
+ * One whole decoder layer for B one-token rows: h = x + attention(x) (the
+ * attention block of asr_attn_layer_decode with the layer input as its
+ * residual, kept in fp32 in the workspace), then out = h + MLP(RMSNorm(h)).
+ * acfg->out_dtype is ignored (h is fp32); mcfg->in_dtype must be ASR_F32 and
+ * mcfg->out_dtype gives out's type.  Arguments as asr_attn_layer_decode; the
+ * workspace (asr_decoder_layer_workspace_bytes) must be zero-filled before
+ * its first use, like the attention block's.
+ */
+int asr_decoder_layer_decode(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
+                             const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x,
+                             const int32_t *slots, const int32_t *positions, int32_t B,
+                             const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* The k-token verify block through a whole decoder layer: x, out [B][k][H]. */
+int asr_decoder_layer_verify(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
+                             const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x,
+                             const int32_t *slots, const int32_t *positions, int32_t B, int32_t k,
+                             const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Static text of an ASR_E* code. */
 const char *asr_strerror(int code);
 

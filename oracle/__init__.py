@@ -3,3 +3,5 @@ from .attn_block import (BF16, E4M3, E4M3_MAX, F16, e4m3_value, rne_e4m3, STATUS
                          LayerWeights, decode, kv_append, kv_crop, rms_norm, rne16, rope,
                          rope_frequencies, verify, widen)
 from .decoder_layer import MlpConfig, MlpWeights, decoder_layer_decode, decoder_layer_verify, mlp, silu
+from .spec_loop import (HeadConfig, TinyModel, accept_greedy, argmax_first, embed, greedy_decode, lm_head_logits,
+                        speculative_round)

@@ -26,7 +26,8 @@ NOALLOC_SCRATCH_BYTES = 40 << 20
 EXPORTED = ["asr_attn_workspace_bytes", "asr_attn_layer_decode", "asr_attn_layer_decode_noalloc",
             "asr_attn_layer_verify", "asr_kv_append", "asr_kv_crop", "asr_strerror",
             "asr_mlp_workspace_bytes", "asr_mlp_layer", "asr_decoder_layer_workspace_bytes",
-            "asr_decoder_layer_decode", "asr_decoder_layer_verify"]
+            "asr_decoder_layer_decode", "asr_decoder_layer_verify", "asr_embed", "asr_lm_head_workspace_bytes",
+            "asr_lm_head_argmax", "asr_accept_greedy"]
 
 _TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
 _DT_NAME = {"f16": F16, "bf16": BF16, "f32": F32}
@@ -64,6 +65,11 @@ class AsrMlpConfig(ctypes.Structure):
 class AsrMlpWeights(ctypes.Structure):
     _fields_ = [("post_norm_w", ctypes.c_void_p), ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p)]
+
+
+class AsrHeadConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("in_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -104,6 +110,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.asr_decoder_layer_decode.restype = ctypes.c_int
     lib.asr_decoder_layer_verify.argtypes = [AC, AW, MC, MW, KV, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.asr_decoder_layer_verify.restype = ctypes.c_int
+    HC = ctypes.POINTER(AsrHeadConfig)
+    lib.asr_embed.argtypes = [P, I32, I32, I32, P, I32, P, P]
+    lib.asr_embed.restype = ctypes.c_int
+    lib.asr_lm_head_workspace_bytes.argtypes = [HC, I32]
+    lib.asr_lm_head_workspace_bytes.restype = SZ
+    lib.asr_lm_head_argmax.argtypes = [HC, P, P, P, I32, P, P, P, SZ, P]
+    lib.asr_lm_head_argmax.restype = ctypes.c_int
+    lib.asr_accept_greedy.argtypes = [P, P, I32, I32, P, P, I32, P, P, P, P]
+    lib.asr_accept_greedy.restype = ctypes.c_int
     lib.asr_strerror.argtypes = [ctypes.c_int]
     lib.asr_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -318,3 +333,35 @@ def decoder_layer_verify(acfg, aw: Weights, mcfg, mw: MlpWeights, kv: KVLayer, x
                                            _ptr(workspace), workspace.numel(), _stream(stream)),
            "asr_decoder_layer_verify")
     del keep
+
+
+def head_config(hidden=1024, vocab=151936, rms_eps=1e-6, dtype="f16", in_dtype="f32"):
+    return AsrHeadConfig(hidden, vocab, rms_eps, _dt(dtype), _dt(in_dtype))
+
+
+def embed(table, ids, x, stream=None) -> None:
+    """x[r] = table[ids[r]]; table [V][H] 16-bit, ids int32 [rows], x [rows][H]."""
+    dt = {torch.float16: F16, torch.bfloat16: BF16}[table.dtype]
+    _check(load().asr_embed(_ptr(table), table.shape[0], table.shape[1], dt, _ptr(ids), ids.numel(), _ptr(x),
+                            _stream(stream)), "asr_embed")
+
+
+def lm_head_workspace(cfg, max_rows: int, device="cuda") -> torch.Tensor:
+    n = load().asr_lm_head_workspace_bytes(ctypes.byref(cfg), max_rows)
+    if n == 0:
+        raise AsrError(-1, "asr_lm_head_workspace_bytes")
+    return torch.empty(int(n), dtype=torch.uint8, device=device)
+
+
+def lm_head_argmax(cfg, final_norm_w, w_lm, h, ids, workspace, max_logit=None, stream=None) -> None:
+    _check(load().asr_lm_head_argmax(ctypes.byref(cfg), _ptr(final_norm_w), _ptr(w_lm), _ptr(h), h.shape[0],
+                                     _ptr(ids), _ptr(max_logit), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)), "asr_lm_head_argmax")
+
+
+def accept_greedy(draft, target, lens, accepted, next_token, new_lens, slots=None, stream=None) -> None:
+    """draft, target int32 [B][k]; lens, new_lens int32 [batch_cap]; accepted, next_token int32 [B]."""
+    B, k = draft.shape
+    _check(load().asr_accept_greedy(_ptr(draft), _ptr(target), B, k, _ptr(slots), _ptr(lens), lens.numel(),
+                                    _ptr(accepted), _ptr(next_token), _ptr(new_lens), _stream(stream)),
+           "asr_accept_greedy")

@@ -374,12 +374,97 @@ int run_decoder_layer(const asr_attn_config *acfg, const asr_attn_weights *aw, c
   return run_mlp(mcfg, mw, h, rows, out, mws, mlp_ws_bytes(mcfg, rows), stream);
 }
 
+int check_head(const asr_head_config *c) {
+  if (!c) return ASR_EINVAL;
+  if (c->hidden <= 0 || c->vocab <= 0) return ASR_EINVAL;
+  if (c->hidden % 256 != 0 || c->hidden > 4096 || c->vocab % 16 != 0) return ASR_EUNSUPPORTED;
+  if (c->dtype != ASR_F16 && c->dtype != ASR_BF16) return ASR_EUNSUPPORTED;
+  if (c->in_dtype != ASR_F32 && c->in_dtype != c->dtype) return ASR_EUNSUPPORTED;
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return ASR_EINVAL;
+  return ASR_OK;
+}
+
+int head_parts(const asr_head_config *c) { return (c->vocab + 127) / 128; }
+
+size_t head_ws_bytes(const asr_head_config *c, int rows) {
+  return align_up((size_t)2 * c->hidden * rows * sizeof(uint16_t)) +
+         2 * align_up((size_t)head_parts(c) * rows * sizeof(float));
+}
+
 }  // namespace
 }  // namespace asr
 
 using namespace asr;
 
 extern "C" {
+
+int asr_embed(const void *table, int32_t vocab, int32_t hidden, int32_t dtype, const int32_t *ids, int32_t rows,
+              void *x, hipStream_t stream) {
+  if (rows < 0 || vocab <= 0 || hidden <= 0) return ASR_EINVAL;
+  if (rows == 0) return ASR_OK;
+  if (!table || !ids || !x) return ASR_EINVAL;
+  if (hidden % 8 != 0) return ASR_EUNSUPPORTED;
+  if (dtype != ASR_F16 && dtype != ASR_BF16) return ASR_EUNSUPPORTED;
+  HeadArgs a{};
+  a.table = static_cast<const uint16_t *>(table);
+  a.ids_in = ids;
+  a.x_out = x;
+  a.rows = rows;
+  a.H = hidden;
+  a.V = vocab;
+  return launch_embed(a, dtype, stream) == hipSuccess ? ASR_OK : ASR_EHIP;
+}
+
+size_t asr_lm_head_workspace_bytes(const asr_head_config *cfg, int32_t max_rows) {
+  if (check_head(cfg) != ASR_OK || max_rows < 0 || max_rows > kMaxRows) return 0;
+  return head_ws_bytes(cfg, max_rows);
+}
+
+int asr_lm_head_argmax(const asr_head_config *cfg, const void *final_norm_w, const void *w_lm, const void *h,
+                       int32_t rows, int32_t *ids, float *max_logit, void *workspace, size_t ws_bytes,
+                       hipStream_t stream) {
+  int rc = check_head(cfg);
+  if (rc) return rc;
+  if (rows < 0 || rows > kMaxRows) return ASR_EINVAL;
+  if (rows == 0) return ASR_OK;
+  if (!final_norm_w || !w_lm || !h || !ids) return ASR_EINVAL;
+  if (!workspace || ws_bytes < head_ws_bytes(cfg, rows)) return ASR_EWORKSPACE;
+  char *base = static_cast<char *>(workspace);
+  const size_t yb = align_up((size_t)2 * cfg->hidden * rows * sizeof(uint16_t));
+  const size_t pb = align_up((size_t)head_parts(cfg) * rows * sizeof(float));
+  MlpArgs n{};
+  n.h = h;
+  n.in_f32 = cfg->in_dtype == ASR_F32;
+  n.g_post = static_cast<const uint16_t *>(final_norm_w);
+  n.y_hl = reinterpret_cast<uint16_t *>(base);
+  n.rows = rows;
+  n.H = cfg->hidden;
+  n.I = 0;
+  n.eps = cfg->rms_eps;
+  HeadArgs a{};
+  a.w_lm = static_cast<const uint16_t *>(w_lm);
+  a.y_hl = n.y_hl;
+  a.part_v = reinterpret_cast<float *>(base + yb);
+  a.part_i = reinterpret_cast<int *>(base + yb + pb);
+  a.ids_out = ids;
+  a.max_logit = max_logit;
+  a.rows = rows;
+  a.H = cfg->hidden;
+  a.V = cfg->vocab;
+  a.nparts = head_parts(cfg);
+  return launch_head(n, a, cfg->dtype, stream) == hipSuccess ? ASR_OK : ASR_EHIP;
+}
+
+int asr_accept_greedy(const int32_t *draft, const int32_t *target, int32_t B, int32_t k, const int32_t *slots,
+                      const int32_t *lens, int32_t batch_cap, int32_t *accepted, int32_t *next_token,
+                      int32_t *new_lens, hipStream_t stream) {
+  if (B < 0 || k < 1 || batch_cap <= 0) return ASR_EINVAL;
+  if (B == 0) return ASR_OK;
+  if (!draft || !target || !lens || !accepted || !next_token || !new_lens) return ASR_EINVAL;
+  if (!slots && B > batch_cap) return ASR_EINVAL;
+  AcceptArgs a{draft, target, slots, lens, accepted, next_token, new_lens, B, k, batch_cap};
+  return launch_accept(a, stream) == hipSuccess ? ASR_OK : ASR_EHIP;
+}
 
 size_t asr_mlp_workspace_bytes(const asr_mlp_config *cfg, int32_t max_rows) {
   if (check_mlp(cfg) != ASR_OK || max_rows < 0 || max_rows > kMaxRows) return 0;

@@ -86,6 +86,34 @@ struct MlpArgs {
 
 hipError_t launch_mlp(const MlpArgs &a, int dtype, hipStream_t s, hipEvent_t *ev);
 
+// The model head: embedding lookup, final norm + lm_head argmax.
+struct HeadArgs {
+  const uint16_t *table;      // [V][H] embedding (k_embed)
+  const int32_t *ids_in;      // [rows] token ids (k_embed)
+  void *x_out;                // [rows][H] 16-bit (k_embed)
+  const uint16_t *w_lm;       // [V][H] lm_head
+  const uint16_t *y_hl;       // [2][H / 32][rows][32] normalised rows (hi, lo)
+  float *part_v;              // [nparts][rows] best logit of each block of 128 ids
+  int *part_i;                // [nparts][rows] its id
+  int32_t *ids_out;           // [rows] argmax ids
+  float *max_logit;           // [rows] or null
+  int rows, H, V, nparts;
+};
+
+// Strict greedy acceptance and the lengths to crop to.
+struct AcceptArgs {
+  const int32_t *draft, *target;  // [B][k]
+  const int32_t *slots;           // [B] or null
+  const int32_t *lens;            // [batch_cap] lengths after the verify block
+  int32_t *accepted, *next_token; // [B]
+  int32_t *new_lens;              // [batch_cap]
+  int B, k, batch_cap;
+};
+
+hipError_t launch_embed(const HeadArgs &a, int dtype, hipStream_t s);
+hipError_t launch_head(const MlpArgs &norm, const HeadArgs &h, int dtype, hipStream_t s);
+hipError_t launch_accept(const AcceptArgs &a, hipStream_t s);
+
 struct WorkspaceLayout {
   size_t flow, mctr, rowtab, qkv, ssq, att, att_hl, part, total;
 };

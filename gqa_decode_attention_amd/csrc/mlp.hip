@@ -1,7 +1,9 @@
-// The rest of a decoder layer on gfx950: post-attention RMSNorm, the gated
-// SiLU MLP and the residual ("Qwen3-ASR -- Latency & Bottleneck Analysis",
-// section 03: the decoder MLP is 27.5% of decode and memory-bound at
-// 529 MB/token; section 07 "Norms are real money at this size").
+// The rest of a decoder layer and the model head on gfx950.
+//
+// Decoder layer: post-attention RMSNorm, the gated SiLU MLP and the residual
+// ("Qwen3-ASR -- Latency & Bottleneck Analysis", section 03: the decoder MLP is
+// 27.5% of decode and memory-bound at 529 MB/token; section 07 "Norms are real
+// money at this size").
 //
 // Three stream-ordered kernels:
 //   k_mlp_norm  y = h * g_post / sqrt(mean(h^2) + eps) per row, stored as two
@@ -178,6 +180,125 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_down(MlpArgs A) {
   }
 }
 
+// ---------------------------------------------------------------- model head and verify loop
+//
+// "Can CTC make Qwen3-ASR faster?", section 11 Phase A: a loop that exposes
+// one-token decode and logits; verify_block returns the target's argmax at
+// every candidate position; strict greedy acceptance; crop to the committed
+// prefix (section 03 "Greedy exactness").
+
+// embedding rows of the token ids (16-bit copies); an id outside the table gives a NaN row
+template <int DT>
+__global__ __launch_bounds__(256) void k_embed(HeadArgs A) {
+  const int n = blockIdx.x;
+  const int id = A.ids_in[n];
+  const bool ok = id >= 0 && id < A.V;
+  const uint16_t nan16 = DT == ASR_BF16 ? 0x7FC0 : 0x7E00;
+  for (int c = threadIdx.x * 8; c < A.H; c += 256 * 8) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) v = ld16(A.table + (size_t)id * A.H + c);
+    else v.x = v.y = v.z = v.w = (uint32_t)nan16 | ((uint32_t)nan16 << 16);
+    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(A.x_out) + (size_t)n * A.H + c) = v;
+  }
+}
+
+// (value, index) kept by the larger value, then the smaller index; NaN never wins
+__device__ __forceinline__ void best_of(float &v, int &i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+// Logits of 8 vocab tiles of 16 (one per wave) x 16 rows on the matrix cores
+// (W_lm exact 16-bit, the normalised rows as hi + lo), and the best (logit,
+// id) of each row over the block's 128 ids: partial [block][row].
+template <int DT>
+__global__ __launch_bounds__(kMlpWaves * 64) void k_head_argmax(HeadArgs A) {
+  __shared__ float s_v[kMlpWaves][16];
+  __shared__ int s_i[kMlpWaves][16];
+  const int wave = wave_id(), lane = lane_id();
+  const int i16 = lane % 16, g4 = lane / 16;
+  const int nb = blockIdx.y * 16, n = nb + i16;
+  const int v0 = (blockIdx.x * kMlpWaves + wave) * 16;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  if (v0 < A.V) {
+    const uint16_t *const w[1] = {A.w_lm};
+    f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    mlp_products<DT, 1>(w, A.H, A.y_hl, A.rows, v0 + i16, min(n, A.rows - 1), 0, A.H / 32, acc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) best_of(bv, bi, acc[0][j], v0 + 4 * g4 + j);
+  }
+  // over the four lane groups of a row (lanes n, n + 16, n + 32, n + 48)
+  {
+    float v2 = xpart<16>(bv);
+    int i2 = __builtin_bit_cast(int, xpart<16>(__builtin_bit_cast(float, bi)));
+    best_of(bv, bi, v2, i2);
+    v2 = xpart<32>(bv);
+    i2 = __builtin_bit_cast(int, xpart<32>(__builtin_bit_cast(float, bi)));
+    best_of(bv, bi, v2, i2);
+  }
+  if (g4 == 0) {
+    s_v[wave][i16] = bv;
+    s_i[wave][i16] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 && nb + (int)threadIdx.x < A.rows) {
+    float v = s_v[0][threadIdx.x];
+    int i = s_i[0][threadIdx.x];
+#pragma unroll
+    for (int wv = 1; wv < kMlpWaves; ++wv) best_of(v, i, s_v[wv][threadIdx.x], s_i[wv][threadIdx.x]);
+    const size_t p = (size_t)blockIdx.x * A.rows + nb + threadIdx.x;
+    A.part_v[p] = v;
+    A.part_i[p] = i;
+  }
+}
+
+// the best of a row's partials: its argmax id (-1 when no logit is a number) and logit
+__global__ __launch_bounds__(256) void k_head_reduce(HeadArgs A) {
+  __shared__ float s_v[4];
+  __shared__ int s_i[4];
+  const int n = blockIdx.x, wave = wave_id(), lane = lane_id();
+  float v = -INFINITY;
+  int i = 0x7fffffff;
+  for (int b = threadIdx.x; b < A.nparts; b += 256) best_of(v, i, A.part_v[(size_t)b * A.rows + n], A.part_i[(size_t)b * A.rows + n]);
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float v2 = __shfl_xor(v, m, kWave);
+    const int i2 = __shfl_xor(i, m, kWave);
+    best_of(v, i, v2, i2);
+  }
+  if (lane == 0) {
+    s_v[wave] = v;
+    s_i[wave] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) best_of(v, i, s_v[w], s_i[w]);
+    A.ids_out[n] = i == 0x7fffffff ? -1 : i;
+    if (A.max_logit) A.max_logit[n] = v;
+  }
+}
+
+// strict greedy acceptance of each sequence's k drafts against the target's
+// argmax of the block rows, then the lengths that keep the committed rows
+__global__ __launch_bounds__(256) void k_lens_copy(AcceptArgs A) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s < A.batch_cap) A.new_lens[s] = A.lens[s];
+}
+__global__ __launch_bounds__(256) void k_accept(AcceptArgs A) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= A.B) return;
+  const int *d = A.draft + (size_t)b * A.k, *t = A.target + (size_t)b * A.k;
+  int a = 0;
+  while (a < A.k && d[a] == t[a]) ++a;
+  const int committed = a < A.k ? a + 1 : A.k;
+  A.accepted[b] = a;
+  A.next_token[b] = a < A.k ? t[a] : d[A.k - 1];
+  const int s = A.slots ? A.slots[b] : b;
+  if (s >= 0 && s < A.batch_cap) A.new_lens[s] = max(A.lens[s] - A.k + committed, 0);
+}
+
 using MlpKernel = void (*)(MlpArgs);
 
 hipError_t launch(MlpKernel k, dim3 grid, dim3 block, hipStream_t s, hipEvent_t *ev, int phase, const MlpArgs &a) {
@@ -198,10 +319,39 @@ hipError_t mlp_launch(const MlpArgs &a, hipStream_t s, hipEvent_t *ev) {
   return launch(k_mlp_down<DT>, dim3(a.H / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 2, a);
 }
 
+template <int DT>
+hipError_t head_launch(const MlpArgs &norm, const HeadArgs &h, hipStream_t s) {
+  hipLaunchKernelGGL(k_mlp_norm<DT>, dim3(norm.rows), dim3(256), 0, s, norm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_head_argmax<DT>, dim3(h.nparts, (h.rows + 15) / 16), dim3(kMlpWaves * kWave), 0, s, h);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_head_reduce, dim3(h.rows), dim3(256), 0, s, h);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_mlp(const MlpArgs &a, int dtype, hipStream_t s, hipEvent_t *ev) {
   return dtype == ASR_BF16 ? mlp_launch<ASR_BF16>(a, s, ev) : mlp_launch<ASR_F16>(a, s, ev);
+}
+
+hipError_t launch_embed(const HeadArgs &a, int dtype, hipStream_t s) {
+  if (dtype == ASR_BF16) hipLaunchKernelGGL(k_embed<ASR_BF16>, dim3(a.rows), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_embed<ASR_F16>, dim3(a.rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head(const MlpArgs &norm, const HeadArgs &h, int dtype, hipStream_t s) {
+  return dtype == ASR_BF16 ? head_launch<ASR_BF16>(norm, h, s) : head_launch<ASR_F16>(norm, h, s);
+}
+
+hipError_t launch_accept(const AcceptArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_lens_copy, dim3((a.batch_cap + 255) / 256), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_accept, dim3((a.B + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace asr

@@ -334,6 +334,62 @@ int asr_decoder_layer_verify(const asr_attn_config *acfg, const asr_attn_weights
                              const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/*
+ * The verify loop above the decoder ("Can CTC make Qwen3-ASR faster?", section
+ * 11 Phase A: a loop exposing one-token decode and logits; verify_block returns
+ * the target's argmax at every candidate position; section 03 "Greedy
+ * exactness": accept the longest draft prefix equal to the target's argmax,
+ * emit the target's token at the first mismatch, crop the speculative cache).
+ *
+ * A round starts from the last committed token p (its K/V not yet cached) and
+ * a draft d[0..k-1]; the caller embeds the block [p, d[0], ..., d[k-2]] with
+ * asr_embed, runs asr_decoder_layer_verify on every layer, takes the argmax of
+ * every block row with asr_lm_head_argmax (row i verifies d[i]: the one-token
+ * shift of section 11 step 3), then asr_accept_greedy gives the accepted count,
+ * the next token and the lengths to crop every layer to with asr_kv_crop.
+ */
+
+/* x[r] = table[ids[r]] (16-bit rows of dtype); an id outside [0, vocab) gives a NaN row. */
+int asr_embed(const void *table, int32_t vocab, int32_t hidden, int32_t dtype, const int32_t *ids, int32_t rows,
+              void *x, hipStream_t stream);
+
+/* Final RMSNorm and lm_head: vocab a multiple of 16, hidden a multiple of 256 (at most 4096). */
+typedef struct asr_head_config {
+  int32_t hidden;    /* H */
+  int32_t vocab;     /* V */
+  float rms_eps;
+  int32_t dtype;     /* ASR_F16 or ASR_BF16: the weights */
+  int32_t in_dtype;  /* h: ASR_F32 or dtype */
+} asr_head_config;
+
+/* Workspace bytes of asr_lm_head_argmax for up to max_rows rows (0: invalid config). */
+size_t asr_lm_head_workspace_bytes(const asr_head_config *cfg, int32_t max_rows);
+
+/*
+ * ids[r] = argmax_v (W_lm RMSNorm(h[r]) * final_norm_w)[v], the smallest id
+ * among equal maxima (-1 if no logit of the row is a number); max_logit[r]
+ * (nullable) its logit.  Logits in fp32 on the matrix cores (W_lm exact, the
+ * normalised row as two 16-bit terms).  final_norm_w [H], w_lm [V][H] of dtype;
+ * h [rows][H] of in_dtype; ids, max_logit device arrays of rows entries.
+ */
+int asr_lm_head_argmax(const asr_head_config *cfg, const void *final_norm_w, const void *w_lm, const void *h,
+                       int32_t rows, int32_t *ids, float *max_logit, void *workspace, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * Strict greedy acceptance for B sequences with k drafts each (device arrays):
+ * draft, target [B][k] (target[b][i] = the target's argmax of block row i, which
+ * verifies draft[b][i]).  accepted[b] = the longest prefix with draft = target;
+ * next_token[b] = target[b][accepted] at a mismatch, else draft[b][k-1] (the
+ * last committed token, which starts the next round); new_lens[batch_cap] =
+ * lens (the lengths after the verify block) for every slot, minus the rejected
+ * rows (k - accepted - 1 at a mismatch, none otherwise) for slots[b] (NULL: b).
+ * All integer, on the device; then asr_kv_crop(layers, n, new_lens).
+ */
+int asr_accept_greedy(const int32_t *draft, const int32_t *target, int32_t B, int32_t k, const int32_t *slots,
+                      const int32_t *lens, int32_t batch_cap, int32_t *accepted, int32_t *next_token,
+                      int32_t *new_lens, hipStream_t stream);
+
 /* Static text of an ASR_E* code. */
 const char *asr_strerror(int code);
 

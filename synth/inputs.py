@@ -232,3 +232,14 @@ def accepted_prefix(stream: int, k: int, draw: int = 0) -> int:
 def verify_choice(stream: int, batch: int, n: int) -> np.ndarray:
     """n distinct sequences of the batch, drawn without replacement."""
     return np.sort(rng_for(stream, 0, T_VCHOICE, 0).choice(batch, size=n, replace=False)).astype(np.int32)
+
+
+T_EMBED, T_GAMMA_FINAL, T_WLM = 18, 19, 20
+
+
+def head_weights(stream: int, hidden: int, vocab: int, dtype: str) -> dict:
+    """Model-head weights as bit patterns: token embedding [vocab][hidden] N(0, 1), final norm
+    gain 1 + N(0, 0.02), lm_head [vocab][hidden] N(0, 0.02)."""
+    return dict(embed=normal_bits(stream, 0, T_EMBED, 0, (vocab, hidden), 1.0, 0.0, dtype),
+                final_norm_w=normal_bits(stream, 0, T_GAMMA_FINAL, 0, (hidden,), 0.02, 1.0, dtype),
+                w_lm=normal_bits(stream, 0, T_WLM, 0, (vocab, hidden), 0.02, 0.0, dtype))

@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--no-verify", action="store_true", help="skip the bs1 verify blocks")
     p.add_argument("--no-wide", action="store_true", help="skip the hidden-2048 batch-64 workload")
     p.add_argument("--no-fp8", action="store_true", help="skip the batch-64 decode on an FP8 cache")
+    p.add_argument("--no-loop", action="store_true",
+                   help="skip greedy decoding and speculative rounds on the whole decoder with the model head")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--dispatch", type=int, default=0, help="0 auto, 1 one kernel per phase, 2 fused")
@@ -306,6 +308,8 @@ def main():
 
     if verify is not None:
         result["verify"] = verify
+    if not args.no_loop:
+        result["verify_loop"] = loop_leg(args, ga, si, np, torch, dev, to_dev, stream)
     if not args.no_batched:
         result["batched"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
         if not args.no_fp8:
@@ -554,6 +558,149 @@ def wide_batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
             "verify": {"k": k, "sequences": nseq, "us_per_block": round(ms_ver * 1000, 1),
                        "us_per_layer_block": round(ms_ver * 1000 / NL, 2), "ok": ok_v,
                        "roofline": step_roofline(bytes_ver, ms_ver)}}
+
+
+def loop_leg(args, ga, si, np, torch, dev, to_dev, stream):
+    """Greedy decoding and speculative rounds with an oracle draft on the whole decoder: 28 layers
+    of attention + MLP (hidden 1024, intermediate 3072), the token embedding and the final norm +
+    lm_head argmax over 151,936 ids, bs1 fp16, a 795-token prompt ("Can CTC make Qwen3-ASR
+    faster?", section 11 Phase A steps 2-4: verify_block, the one-token shift, an oracle draft,
+    block sizes).  Greedy: one captured graph per token (embedding, 28 layer decodes, argmax fed
+    back as the next input).  Speculative: one graph per round of k (embedding of the block, 28
+    layer verifies, argmax of every row, acceptance, crop); the draft is the greedy transcript, so
+    every round commits k tokens.  Reported in microseconds per committed token."""
+    from concurrent.futures import ThreadPoolExecutor
+    H, I, V, NL, P0, dtype, sid = 1024, 3072, 151936, 28, 795, si.F16, 6
+    T = 64                                     # tokens per timed pass
+    cap = P0 + T + 16
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        wa = list(ex.map(lambda l: si.layer_weights(sid, l, H, dtype), range(NL)))
+        wm = list(ex.map(lambda l: si.mlp_weights(sid, l, H, I, dtype), range(NL)))
+        kvb = list(ex.map(lambda l: si.kv_rows(sid, l, 0, P0, dtype), range(NL)))
+    hb = si.head_weights(sid, H, V, dtype)
+    aw = [ga.Weights(*(to_dev(w[n], dtype) for n in ("input_norm_w", "w_qkv", "q_norm_w", "k_norm_w", "w_o"))) for w in wa]
+    mw = [ga.MlpWeights(*(to_dev(w[n], dtype) for n in ("post_norm_w", "w_gate", "w_up", "w_down"))) for w in wm]
+    table, gfin, wlm = to_dev(hb["embed"], dtype), to_dev(hb["final_norm_w"], dtype), to_dev(hb["w_lm"], dtype)
+    del wa, wm, hb
+    kvs = []
+    for kb, vb in kvb:
+        kv = ga.KVLayer.empty(1, 8, cap, dtype=torch.float16, device=dev)
+        kv.k[0, :, :P0], kv.v[0, :, :P0] = to_dev(kb, dtype), to_dev(vb, dtype)
+        kv.lens.fill_(P0)
+        kvs.append(kv)
+    del kvb
+    base = torch.full((1,), P0, dtype=torch.int32, device=dev)
+    acfg = ga.config(hidden=H, dtype=dtype)
+    mcfg, mlast = ga.mlp_config(hidden=H, intermediate=I, dtype=dtype, out_dtype=dtype), ga.mlp_config(hidden=H, intermediate=I, dtype=dtype)
+    hcfg = ga.head_config(hidden=H, vocab=V, dtype=dtype)
+    KMAX = 16
+    ws = ga.decoder_layer_workspace(acfg, mcfg, KMAX, cap, device=dev)
+    hws = ga.lm_head_workspace(hcfg, KMAX, device=dev)
+    xa = torch.empty((KMAX, H), dtype=torch.float16, device=dev)
+    xb = torch.empty((KMAX, H), dtype=torch.float16, device=dev)
+    hf = torch.empty((KMAX, H), dtype=torch.float32, device=dev)
+    print(f"[bench] loop model ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def forward(ids, n, L, out_ids):
+        """ids [n] -> out_ids [n]: the block through the 28 layers and the head (L = committed length)."""
+        ga.embed(table, ids, xa[:n])
+        x = xa
+        for l in range(NL):
+            last = l == NL - 1
+            o = hf if last else (xb if x is xa else xa)
+            if n == 1:
+                ga.decoder_layer_decode(acfg, aw[l], mlast if last else mcfg, mw[l], kvs[l], x[:1], o[:1], ws,
+                                        host_lens=[L])
+            else:
+                ga.decoder_layer_verify(acfg, aw[l], mlast if last else mcfg, mw[l], kvs[l], x[:n].view(1, n, H),
+                                        o[:n].view(1, n, H), ws, host_lens=[L])
+            x = o
+        ga.lm_head_argmax(hcfg, gfin, wlm, hf[:n], out_ids, hws)
+
+    # the greedy transcript (untimed), then the timed greedy graphs: the argmax feeds the next step
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    trans = []
+    for s_ in range(T):
+        forward(tok, 1, P0 + s_, tok)
+        trans.append(tok.clone())
+    trans = torch.cat(trans)
+    ga.kv_crop(kvs, base)
+    tok.zero_()
+    torch.cuda.synchronize()
+    graphs = []
+    for s_ in range(T):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            forward(tok, 1, P0 + s_, tok)
+        graphs.append(g)
+    ga.kv_crop(kvs, base)
+    torch.cuda.synchronize()
+
+    def time_graphs(gs, reps=3):
+        best = None
+        for _ in range(reps):
+            tok.zero_()
+            ga.kv_crop(kvs, base)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for g in gs:
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    ms_greedy = time_graphs(graphs)
+    # the graphs reproduce the transcript
+    tok.zero_()
+    ga.kv_crop(kvs, base)
+    replay = []
+    for g in graphs:
+        g.replay()
+        replay.append(tok.clone())
+    greedy_ok = bool(torch.equal(torch.cat(replay), trans))
+    del graphs
+    out = {"workload": "greedy decoding and speculative rounds, 28 decoder layers (attention + MLP, hidden 1024, "
+                       "intermediate 3072) + embedding + final norm + lm_head argmax (151,936 ids), bs1, fp16, "
+                       f"prompt {P0}, {T} tokens per pass, oracle draft (the greedy transcript)",
+           "unit": "us per committed token",
+           "greedy": {"us_per_token": round(ms_greedy * 1000 / T, 2), "ok": greedy_ok}}
+    print(f"[bench] loop greedy: {ms_greedy * 1000 / T:.1f} us/token (ok {greedy_ok})", file=sys.stderr, flush=True)
+    start = torch.zeros(1, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    nxt = torch.empty(1, dtype=torch.int32, device=dev)
+    new_lens = torch.empty(1, dtype=torch.int32, device=dev)
+    for k in (4, 8, 16):
+        R = T // k
+        blocks = torch.stack([torch.cat([start if j == 0 else trans[j * k - 1:j * k], trans[j * k:j * k + k - 1]])
+                              for j in range(R)]).contiguous()
+        drafts = torch.stack([trans[j * k:(j + 1) * k] for j in range(R)]).contiguous()
+        tgt = torch.empty((R, k), dtype=torch.int32, device=dev)
+        accs = torch.empty(R, dtype=torch.int32, device=dev)
+        gs = []
+        for j in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                forward(blocks[j], k, P0 + j * k, tgt[j])
+                ga.accept_greedy(drafts[j:j + 1], tgt[j:j + 1], kvs[0].lens, accs[j:j + 1], nxt, new_lens)
+                ga.kv_crop(kvs, new_lens)
+            gs.append(g)
+        ga.kv_crop(kvs, base)
+        torch.cuda.synchronize()
+        ms = time_graphs(gs)
+        ok = bool(torch.all(accs == k).item()) and int(kvs[0].lens.item()) == P0 + R * k
+        del gs
+        out[f"k{k}"] = {"us_per_committed_token": round(ms * 1000 / (R * k), 2), "us_per_round": round(ms * 1000 / R, 1),
+                        "rounds": R, "accepted_per_round": k, "ok": ok,
+                        "speedup_vs_greedy": round(ms_greedy / ms, 3)}
+        print(f"[bench] loop speculative k={k}: {ms * 1000 / (R * k):.1f} us per committed token, "
+              f"{ms * 1000 / R:.1f} us per round (ok {ok})", file=sys.stderr, flush=True)
+    del kvs, aw, mw, table, wlm
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_model():

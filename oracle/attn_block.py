@@ -172,6 +172,9 @@ class BlockConfig:
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     dtype: str = F16
+    # multi-section rotary: rotary pairs [0, s0) turn by position component 0, the next s1 by
+    # component 1, the last s2 by component 2 (s0 + s1 + s2 = head_dim / 2); () = one position
+    mrope_sections: tuple = ()
 
 
 @dataclass
@@ -251,14 +254,23 @@ def rope_frequencies(head_dim: int, theta: float) -> np.ndarray:
     return theta ** (-2.0 * t / head_dim)
 
 
-def rope(u: np.ndarray, pos, theta: float) -> np.ndarray:
+def rope(u: np.ndarray, pos, theta: float, sections=()) -> np.ndarray:
     """Rotate pairs (t, t + d/2) of the last axis by the angle pos * omega_t.
 
-    ``pos`` broadcasts against ``u.shape[:-1]``.
+    ``pos`` broadcasts against ``u.shape[:-1]``.  With ``sections`` (s0, s1, s2), ``pos`` has
+    a trailing axis of three position components and pair t turns by component c(t): 0 for
+    t < s0, 1 for t < s0 + s1, 2 after ("MRoPE" of the Latency page's section 03 table).
     """
     d = u.shape[-1]
     half = d // 2
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_frequencies(d, theta)
+    om = rope_frequencies(d, theta)
+    if sections:
+        assert sum(sections) == half
+        comp = np.repeat(np.arange(3), sections)                       # component of each pair
+        p = np.asarray(pos, dtype=np.float64)
+        ang = np.take(p, comp, axis=-1) * om                            # [..., half]
+    else:
+        ang = np.asarray(pos, dtype=np.float64)[..., None] * om
     c, s = np.cos(ang), np.sin(ang)
     a, b = u[..., :half], u[..., half:]
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
@@ -283,7 +295,8 @@ def decode(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray
     """One-token decode for B rows (each row a distinct sequence slot).
 
     Row i works on slot ``slots[i]`` (default i) at position
-    ``positions[i]`` (default the slot's length): it computes q, k, v, appends
+    ``positions[i]`` (default the slot's length; with multi-section rotary ``positions`` is
+    [3][B], the components of row i at ``positions[:, i]``): it computes q, k, v, appends
     k and v at index lens[slot], attends over lens[slot] + 1 positions and
     returns out[i] = W_o a (+ residual).  lens[slot] grows by one.  A row whose
     append would pass the capacity is skipped: NaN output, the capacity status
@@ -303,9 +316,14 @@ def decode(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray
         q, k, v = _split_qkv(w.w_qkv @ h, cfg)
         q = rms_norm(q, w.q_norm_w, cfg.rms_eps)
         k = rms_norm(k, w.k_norm_w, cfg.rms_eps)
-        p = int(positions[i]) if positions is not None else L
-        q = rope(q, p, cfg.rope_theta)
-        k = rope(k, p, cfg.rope_theta)
+        if cfg.mrope_sections:   # positions [3][B]: the row's three components
+            p = np.asarray(positions, np.int64)[:, i] if positions is not None else np.full(3, L)
+            q = rope(q, p[None, :], cfg.rope_theta, cfg.mrope_sections)
+            k = rope(k, p[None, :], cfg.rope_theta, cfg.mrope_sections)
+        else:
+            p = int(positions[i]) if positions is not None else L
+            q = rope(q, p, cfg.rope_theta)
+            k = rope(k, p, cfg.rope_theta)
         if L + 1 > cache.capacity:
             cache.status |= STATUS_CAPACITY
             out[i] = np.nan
@@ -350,10 +368,16 @@ def verify(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray
         Q, K_new, V_new = _split_qkv(Hn @ w.w_qkv.T, cfg)               # [k][heads][d]
         Q = rms_norm(Q, w.q_norm_w, cfg.rms_eps)
         K_new = rms_norm(K_new, w.k_norm_w, cfg.rms_eps)
-        p0 = int(positions[b]) if positions is not None else L
-        pos = p0 + np.arange(kk)
-        Q = rope(Q, pos[:, None], cfg.rope_theta)
-        K_new = rope(K_new, pos[:, None], cfg.rope_theta)
+        if cfg.mrope_sections:   # every component of row r advances by r
+            p0 = np.asarray(positions, np.int64)[:, b] if positions is not None else np.full(3, L)
+            pos = p0[None, :] + np.arange(kk)[:, None]                  # [k][3]
+            Q = rope(Q, pos[:, None, :], cfg.rope_theta, cfg.mrope_sections)
+            K_new = rope(K_new, pos[:, None, :], cfg.rope_theta, cfg.mrope_sections)
+        else:
+            p0 = int(positions[b]) if positions is not None else L
+            pos = p0 + np.arange(kk)
+            Q = rope(Q, pos[:, None], cfg.rope_theta)
+            K_new = rope(K_new, pos[:, None], cfg.rope_theta)
         if L + kk > cache.capacity:
             cache.status |= STATUS_CAPACITY
             out[b] = np.nan

@@ -429,3 +429,58 @@ def test_verify_capacity_overflow_skips_that_sequence_only():
     want = verify(cfg, w, sub, x[keep])
     assert np.array_equal(out[keep], want) and sub.status == 0
     assert np.array_equal(c.k[keep], sub.k) and np.array_equal(c.v[keep], sub.v)
+
+
+# ---------------------------------------------------------------- multi-section rotary
+
+SECTIONS = (16, 24, 24)
+
+
+def test_mrope_with_equal_components_is_the_one_position_rotary():
+    u = np.random.default_rng(300).standard_normal((5, 128))
+    for p in (0, 1, 77, 4095):
+        assert np.array_equal(rope(u, np.full((5, 3), p), 1e6, SECTIONS), rope(u, np.full(5, p), 1e6))
+
+
+def test_mrope_pairs_turn_by_their_own_component():
+    """Scalar loop over the pairs: pair t turns by p[c(t)] * theta^(-2t/d)."""
+    g = np.random.default_rng(301)
+    u = g.standard_normal(128)
+    p3 = np.array([5, 900, 33])
+    out = rope(u[None], p3[None], 1e6, SECTIONS)[0]
+    for t in range(64):
+        c = 0 if t < 16 else (1 if t < 40 else 2)
+        ang = p3[c] * 1e6 ** (-2.0 * t / 128)
+        assert out[t] == pytest.approx(u[t] * math.cos(ang) - u[t + 64] * math.sin(ang), abs=1e-12)
+        assert out[t + 64] == pytest.approx(u[t + 64] * math.cos(ang) + u[t] * math.sin(ang), abs=1e-12)
+    # a section of all 64 pairs is the one-position rotary of that component
+    assert np.allclose(rope(u[None], p3[None], 1e6, (64, 0, 0))[0], rope(u, 5, 1e6), atol=1e-15)
+
+
+def test_mrope_scores_depend_on_each_component_difference_only():
+    """Shifting all three components of query and key by the same per-component offsets keeps
+    q . k (each section is a rotation by the difference of its own components)."""
+    g = np.random.default_rng(302)
+    q, k = g.standard_normal(128), g.standard_normal(128)
+    m, n, delta = np.array([10, 20, 30]), np.array([3, 7, 100]), np.array([5, -9, 1000])
+    s1 = rope(q[None], m[None], 1e6, SECTIONS)[0] @ rope(k[None], n[None], 1e6, SECTIONS)[0]
+    s2 = rope(q[None], (m + delta)[None], 1e6, SECTIONS)[0] @ rope(k[None], (n + delta)[None], 1e6, SECTIONS)[0]
+    assert abs(s1 - s2) < 1e-10
+
+
+def test_mrope_verify_equals_sequential_decode():
+    cfg = BlockConfig(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=16, mrope_sections=(2, 3, 3))
+    wb = rand_weights(cfg, 310)
+    w = LayerWeights.from_bits(wb, F16)
+    c1 = rand_cache(cfg, 311, [3, 6], capacity=16)
+    c2 = c1.copy()
+    x = f16_bits(np.random.default_rng(312).standard_normal((2, 3, cfg.hidden)))
+    pos3 = np.array([[10, 4], [200, 7], [31, 9]])
+    ov = verify(cfg, w, c1, x, positions=pos3)
+    for r in range(3):
+        od = decode(cfg, w, c2, x[:, r, :], positions=pos3 + r)
+        assert rel_err(ov[:, r], od) < 1e-12
+    # and it differs from the one-position rotary at component 0
+    c3 = rand_cache(cfg, 311, [3, 6], capacity=16)
+    one = verify(BlockConfig(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=16), w, c3, x, positions=pos3[0])
+    assert rel_err(one, ov) > 1e-3

@@ -39,7 +39,7 @@ class AsrAttnConfig(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("kv_split", ctypes.c_int32), ("dispatch", ctypes.c_int32),
-                ("phase_events", ctypes.c_void_p)]
+                ("phase_events", ctypes.c_void_p), ("mrope_sections", ctypes.c_int32 * 3)]
 
 
 class AsrAttnWeights(ctypes.Structure):
@@ -146,9 +146,10 @@ def torch_dtype(dt) -> torch.dtype:
 
 
 def config(hidden=1024, n_q_heads=16, n_kv_heads=8, head_dim=128, rms_eps=1e-6, rope_theta=1e6,
-           dtype="f16", out_dtype="f32", kv_split=0, dispatch=DISPATCH_AUTO) -> AsrAttnConfig:
+           dtype="f16", out_dtype="f32", kv_split=0, dispatch=DISPATCH_AUTO, mrope_sections=(0, 0, 0)) -> AsrAttnConfig:
     return AsrAttnConfig(hidden, n_q_heads, n_kv_heads, head_dim, rms_eps, rope_theta,
-                         _dt(dtype), _dt(out_dtype), kv_split, dispatch, None)
+                         _dt(dtype), _dt(out_dtype), kv_split, dispatch, None,
+                         (ctypes.c_int32 * 3)(*mrope_sections))
 
 
 class PhaseEvents:

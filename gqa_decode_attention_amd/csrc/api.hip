@@ -35,6 +35,10 @@ int check_cfg(const asr_attn_config *c) {
   if (c->kv_split != 0 && (c->kv_split % 16 != 0 || c->kv_split < kMinSplit || c->kv_split > kMaxSplit))
     return ASR_EINVAL;
   if (c->dispatch < ASR_DISPATCH_AUTO || c->dispatch > ASR_DISPATCH_FUSED) return ASR_EINVAL;
+  const int32_t *ms = c->mrope_sections;
+  if (ms[0] || ms[1] || ms[2]) {
+    if (ms[0] < 0 || ms[1] < 0 || ms[2] < 0 || ms[0] + ms[1] + ms[2] != c->head_dim / 2) return ASR_EINVAL;
+  }
   return ASR_OK;
 }
 
@@ -179,6 +183,9 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.kv8 = kv8;
   a.ksc = kv->k_scale;
   a.vsc = kv->v_scale;
+  a.mrope = (cfg->mrope_sections[0] || cfg->mrope_sections[1] || cfg->mrope_sections[2]) ? 1 : 0;
+  a.ms0 = cfg->mrope_sections[0];
+  a.ms1 = cfg->mrope_sections[1];
 
   // upper bound of attention work items; blocks stride over the real count.
   // nch_host: the most chunks of any row, by the host's view of the lengths

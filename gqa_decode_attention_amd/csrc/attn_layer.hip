@@ -90,6 +90,16 @@ __device__ __forceinline__ RowInfo row_info(const LayerArgs &A, int row) {
 
 __device__ __forceinline__ int chunks_of(int nvis, int split) { return (nvis + split - 1) / split; }
 
+// Rotary position of pair t of row `row`: the row's position, or with
+// multi-section rotary the position component of t's section (positions
+// [3][B]; NULL: the length), plus the row's offset in its block.
+__device__ __forceinline__ int rope_pos(const LayerArgs &A, int row, int t) {
+  const RowInfo ri = row_info(A, row);
+  if (!A.mrope) return ri.pos;
+  const int c = t < A.ms0 ? 0 : (t < A.ms0 + A.ms1 ? 1 : 2);
+  return (A.positions ? A.positions[c * A.B + row / A.n] : ri.L) + ri.r;
+}
+
 // Row table for phases M and D (which must not read lens: lengths change in D).
 template <bool COH>
 __device__ void write_row_table(const LayerArgs &A) {
@@ -201,7 +211,7 @@ __device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         if (rb + r < A.rows && lane / 2 == r) {
-          const float2 c = rope_cs(row_info(A, rb + r).pos, (lane & 1) ? om_b : om_a);
+          const float2 c = rope_cs(rope_pos(A, rb + r, (lane & 1) ? tb : ta), (lane & 1) ? om_b : om_a);
           cs_c = c.x;
           cs_s = c.y;
         }
@@ -1611,7 +1621,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
         if (n < A.rows) {
           const double omega = exp2(-(2.0 * (t0 + tt) / kHeadDim) * log2((double)A.theta));
           double sd, cd;
-          sincos((double)row_info(A, n).pos * omega, &sd, &cd);
+          sincos((double)rope_pos(A, n, t0 + tt) * omega, &sd, &cd);
           cs = (float)cd;
           sn = (float)sd;
         }

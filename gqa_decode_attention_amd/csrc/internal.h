@@ -66,6 +66,9 @@ struct LayerArgs {
   // FP8 (E4M3) cache: kc / vc hold one code per element; per-kv-head scales of K and V
   int kv8;
   const float *ksc, *vsc;
+  // multi-section rotary: pairs [0, ms0) use position component 0, [ms0, ms0 + ms1) component 1,
+  // the rest component 2 (positions [3][B]); mrope = 0: one position per row
+  int mrope, ms0, ms1;
 };
 
 // The rest of the decoder layer: post-attention RMSNorm, gated SiLU MLP, residual.

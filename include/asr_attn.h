@@ -106,6 +106,13 @@ typedef struct asr_attn_config {
                                 caller) that receive the start and end stamps of the projection,
                                 attention and o_proj kernels, in that order, of the stream-ordered
                                 dispatch; the fused dispatch stamps its one kernel into [0] and [5] */
+  int32_t mrope_sections[3];  /* multi-section rotary ("MRoPE" of the Latency page's section 03
+                                 table): all zero = one position per row; else s0 + s1 + s2 =
+                                 head_dim / 2 and rotary pair t turns by position component 0 for
+                                 t < s0, 1 for t < s0 + s1, 2 after; `positions` is then [3][B]
+                                 (component c of sequence b at positions[c * B + b]; row r of a
+                                 verify block adds r to every component; NULL: every component is
+                                 the cache length) */
 } asr_attn_config;
 
 /* One layer's weights (device pointers, elements of cfg.dtype). */

@@ -662,3 +662,39 @@ def test_verify_matrix_core_attention_groups_and_chunk_edges(nq, nkv, k, split):
         check_rounded_rows(vg[s, :, lens[s]:lens[s] + k], ref.v[s, :, lens[s]:lens[s] + k], dtype)
         assert np.array_equal(kg[s, :, :lens[s]], kb[s, :, :lens[s]])
         assert np.array_equal(kg[s, :, lens[s] + k:], kb[s, :, lens[s] + k:])
+
+
+@pytest.mark.parametrize("B,k", [(1, 1), (3, 1), (6, 1), (2, 2), (2, 8)])
+def test_multi_section_rotary_vs_oracle(B, k):
+    """Three position components per sequence, rotary sections (16, 24, 24): decode (vector and
+    matrix-core projections) and verify blocks; without positions the sections reduce to the
+    one-position rotary, bit for bit."""
+    dtype = si.BF16
+    sections = (16, 24, 24)
+    lens = [30, 250, 3, 77, 129, 0][:B]
+    cap = 300
+    L = SeededLayer(12, 10 * B + k, 1024, dtype)
+    ocfg = oracle.BlockConfig(hidden=1024, dtype=dtype, mrope_sections=sections)
+    kb, vb = fill_cache(12, B, lens, cap, dtype)
+    pos3 = np.array([[100, 7, 2000, 5, 64, 0][:B], [3, 900, 11, 70, 1, 4][:B], [4000, 50, 9, 8, 300, 2][:B]], np.int32)
+    cfg = ga.config(dtype=dtype, mrope_sections=sections)
+    kv = device_cache(kb, vb, lens, dtype)
+    ref = oracle_cache(kb, vb, lens, dtype)
+    if k == 1:
+        xb = _x(12, B, 0, (B, 1024), dtype)
+        got = _run_decode(L, cfg, kv, xb, dtype, positions=pos3.ravel().tolist())
+        want = oracle.decode(ocfg, L.ref, ref, xb, positions=pos3)
+    else:
+        xb = _x(12, B, 0, (B, k, 1024), dtype)
+        got = _run_verify(L, cfg, kv, xb, dtype, positions=pos3.ravel().tolist())
+        want = oracle.verify(ocfg, L.ref, ref, xb, positions=pos3)
+    err = rel_err(got, want)
+    print(f"mrope B={B} k={k}: {err:.3e}")
+    assert err < TOL[dtype]
+    kg = to_bits(kv.k)
+    for s in range(B):
+        check_rounded_rows(kg[s, :, lens[s]:lens[s] + k], ref.k[s, :, lens[s]:lens[s] + k], dtype)
+    if k == 1:   # no positions: every component is the length, the one-position rotary
+        a = _run_decode(L, cfg, device_cache(kb, vb, lens, dtype), xb, dtype)
+        b = _run_decode(L, ga.config(dtype=dtype), device_cache(kb, vb, lens, dtype), xb, dtype)
+        assert np.array_equal(a, b)

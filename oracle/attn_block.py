@@ -401,6 +401,37 @@ def verify(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray
     return out
 
 
+def mixed(cfg: BlockConfig, w: LayerWeights, cache: KVCache, x_bits: np.ndarray, n_per_seq,
+          slots=None, positions=None, residual_bits=None) -> np.ndarray:
+    """Decode rows and verify blocks of different sizes in one call: x is [sum(n_per_seq)][H].
+
+    "Can CTC make Qwen3-ASR faster?", section 08 (Verifier, version 0) picks the
+    block length of each sequence from the draft's confidence, so the sequences
+    of one batch carry blocks of different k (k = 1: a decode step).  Sequence b
+    owns the n_per_seq[b] consecutive rows after those of sequences 0 .. b - 1,
+    and they are exactly its verify block (rows appended at lens .. lens + k - 1,
+    row r seeing positions 0 .. lens + r, rotary at positions[b] + r).
+    Positions: [B] (one per sequence), or [3][B] with multi-section rotary.
+    """
+    n_per_seq = [int(n) for n in n_per_seq]
+    x_bits = np.asarray(x_bits)
+    out = np.empty((sum(n_per_seq), cfg.hidden), np.float64)
+    row = 0
+    for b, n in enumerate(n_per_seq):
+        s = int(slots[b]) if slots is not None else b
+        if positions is None:
+            pos = None
+        elif cfg.mrope_sections:
+            pos = np.asarray(positions, np.int64)[:, b:b + 1]
+        else:
+            pos = [int(positions[b])]
+        res = residual_bits[None, row:row + n] if residual_bits is not None else None
+        out[row:row + n] = verify(cfg, w, cache, x_bits[None, row:row + n], slots=[s], positions=pos,
+                                  residual_bits=res)[0]
+        row += n
+    return out
+
+
 def kv_append(cache: KVCache, k_bits: np.ndarray, v_bits: np.ndarray, slots=None) -> None:
     """Copy given rows (16-bit patterns or E4M3 codes) into the cache: k_bits, v_bits are [B][n][nkv][d].
 

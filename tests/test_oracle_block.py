@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import (F16, STATUS_CAPACITY, STATUS_CROP_GROW, BlockConfig, KVCache, LayerWeights,
-                    decode, kv_append, kv_crop, rms_norm, rope, verify, widen)
+                    decode, kv_append, kv_crop, mixed, rms_norm, rope, verify, widen)
 
 TINY = BlockConfig(hidden=16, n_q_heads=4, n_kv_heads=2, head_dim=8, dtype=F16)
 
@@ -484,3 +484,72 @@ def test_mrope_verify_equals_sequential_decode():
     c3 = rand_cache(cfg, 311, [3, 6], capacity=16)
     one = verify(BlockConfig(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=16), w, c3, x, positions=pos3[0])
     assert rel_err(one, ov) > 1e-3
+
+
+# ---------------------------------------------------------------- mixed decode rows and verify blocks
+
+def _sequential_decode(cfg, w, cache, x, sizes, slots, positions, residual):
+    """Each sequence's block as single-token decode steps of that sequence alone."""
+    out = np.empty((sum(sizes), cfg.hidden))
+    row = 0
+    for b, n in enumerate(sizes):
+        for r in range(n):
+            if positions is None:
+                pos = None
+            elif cfg.mrope_sections:
+                pos = np.asarray(positions)[:, b:b + 1] + r
+            else:
+                pos = [positions[b] + r]
+            res = residual[row + r:row + r + 1] if residual is not None else None
+            out[row + r] = decode(cfg, w, cache, x[row + r:row + r + 1], slots=[slots[b]], positions=pos,
+                                  residual_bits=res)[0]
+        row += n
+    return out
+
+
+@pytest.mark.parametrize("sections", [(), (2, 3, 3)])
+def test_mixed_blocks_equal_sequential_decode_per_sequence(sections):
+    """Rows of every sequence in a mixed call (block sizes 1, 4, 2, 1, 3; permuted slots, explicit
+    positions and a residual) equal that sequence's tokens decoded one by one; the cache rows and
+    lengths agree too.  A wrong row offset, slot or position lookup fails it."""
+    cfg = BlockConfig(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=16, mrope_sections=sections)
+    w = LayerWeights.from_bits(rand_weights(cfg, 400), F16)
+    sizes = [1, 4, 2, 1, 3]
+    slots = [3, 0, 4, 1, 2]
+    c1 = rand_cache(cfg, 401, [5, 0, 9, 2, 11], capacity=24)
+    c2 = c1.copy()
+    rows = sum(sizes)
+    x = f16_bits(np.random.default_rng(402).standard_normal((rows, cfg.hidden)))
+    res = f16_bits(np.random.default_rng(403).standard_normal((rows, cfg.hidden)))
+    pos = np.array([[40, 7, 300, 2, 19], [8, 50, 1, 90, 3], [61, 0, 17, 4, 200]]) if sections else [40, 7, 300, 2, 19]
+    got = mixed(cfg, w, c1, x, sizes, slots=slots, positions=pos, residual_bits=res)
+    want = _sequential_decode(cfg, w, c2, x, sizes, slots, pos, res)
+    assert rel_err(got, want) < 1e-12
+    assert np.array_equal(c1.lens, c2.lens) and np.array_equal(c1.k, c2.k) and np.array_equal(c1.v, c2.v)
+    assert [int(c1.lens[slots[b]]) for b in range(5)] == [l + n for l, n in zip([2, 5, 11, 0, 9], sizes)]
+
+
+def test_mixed_blocks_of_one_row_are_a_decode_step():
+    cfg = BlockConfig(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=16)
+    w = LayerWeights.from_bits(rand_weights(cfg, 410), F16)
+    c1 = rand_cache(cfg, 411, [4, 0, 6], capacity=16)
+    c2 = c1.copy()
+    x = f16_bits(np.random.default_rng(412).standard_normal((3, cfg.hidden)))
+    got = mixed(cfg, w, c1, x, [1, 1, 1], slots=[1, 2, 0])
+    want = decode(cfg, w, c2, x, slots=[1, 2, 0])
+    assert np.array_equal(got, want)
+    assert np.array_equal(c1.k, c2.k) and np.array_equal(c1.lens, c2.lens)
+
+
+def test_mixed_capacity_overflow_skips_that_sequence_only():
+    cfg = BlockConfig(hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=16)
+    w = LayerWeights.from_bits(rand_weights(cfg, 420), F16)
+    c1 = rand_cache(cfg, 421, [3, 14, 5], capacity=16)
+    c2 = c1.copy()
+    x = f16_bits(np.random.default_rng(422).standard_normal((2 + 3 + 4, cfg.hidden)))
+    got = mixed(cfg, w, c1, x, [2, 3, 4])          # sequence 1: 14 + 3 > 16
+    assert np.all(np.isnan(got[2:5])) and np.all(np.isfinite(got[:2])) and np.all(np.isfinite(got[5:]))
+    assert c1.status == STATUS_CAPACITY and c1.lens.tolist() == [5, 14, 9]
+    assert np.array_equal(c1.k[1], c2.k[1])
+    want0 = verify(cfg, w, c2, x[None, :2], slots=[0])[0]
+    assert rel_err(got[:2], want0) < 1e-12

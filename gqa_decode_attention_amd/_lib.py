@@ -27,7 +27,7 @@ EXPORTED = ["asr_attn_workspace_bytes", "asr_attn_layer_decode", "asr_attn_layer
             "asr_attn_layer_verify", "asr_kv_append", "asr_kv_crop", "asr_strerror",
             "asr_mlp_workspace_bytes", "asr_mlp_layer", "asr_decoder_layer_workspace_bytes",
             "asr_decoder_layer_decode", "asr_decoder_layer_verify", "asr_embed", "asr_lm_head_workspace_bytes",
-            "asr_lm_head_argmax", "asr_accept_greedy"]
+            "asr_lm_head_argmax", "asr_accept_greedy", "asr_attn_layer_mixed", "asr_decoder_layer_mixed"]
 
 _TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
 _DT_NAME = {"f16": F16, "bf16": BF16, "f32": F32}
@@ -110,6 +110,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.asr_decoder_layer_decode.restype = ctypes.c_int
     lib.asr_decoder_layer_verify.argtypes = [AC, AW, MC, MW, KV, P, P, P, I32, I32, P, P, P, SZ, P]
     lib.asr_decoder_layer_verify.restype = ctypes.c_int
+    lib.asr_attn_layer_mixed.argtypes = [AC, AW, KV, P, P, P, I32, P, P, P, P, P, SZ, P]
+    lib.asr_attn_layer_mixed.restype = ctypes.c_int
+    lib.asr_decoder_layer_mixed.argtypes = [AC, AW, MC, MW, KV, P, P, P, I32, P, P, P, P, SZ, P]
+    lib.asr_decoder_layer_mixed.restype = ctypes.c_int
     HC = ctypes.POINTER(AsrHeadConfig)
     lib.asr_embed.argtypes = [P, I32, I32, I32, P, I32, P, P]
     lib.asr_embed.restype = ctypes.c_int
@@ -273,6 +277,27 @@ def layer_verify(cfg, w: Weights, kv: KVLayer, x, out, workspace, slots=None, po
     del keep
 
 
+def _block_sizes(n_per_seq):
+    """HOST int32 array of the block sizes (a sequence of ints)."""
+    sizes = [int(v) for v in n_per_seq]
+    arr = (ctypes.c_int32 * max(1, len(sizes)))(*sizes)
+    return arr, len(sizes)
+
+
+def layer_mixed(cfg, w: Weights, kv: KVLayer, x, n_per_seq, out, workspace, slots=None, positions=None,
+                host_lens=None, residual=None, stream=None) -> None:
+    """Decode rows and verify blocks of per-sequence sizes n_per_seq (host ints) in one call:
+    x, residual, out [sum(n_per_seq)][H]."""
+    keep, hl = _host_lens(host_lens)
+    nb, B = _block_sizes(n_per_seq)
+    _check(load().asr_attn_layer_mixed(ctypes.byref(cfg), ctypes.byref(w.c), ctypes.byref(kv.c), _ptr(x),
+                                       _ptr(slots), _ptr(positions), B, ctypes.cast(nb, ctypes.c_void_p), hl,
+                                       _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)),
+           "asr_attn_layer_mixed")
+    del keep, nb
+
+
 def kv_append(kv: KVLayer, k_new, v_new, slots=None, stream=None) -> None:
     B, n = k_new.shape[0], k_new.shape[1]
     _check(load().asr_kv_append(ctypes.byref(kv.c), _ptr(k_new), _ptr(v_new), _ptr(slots), B, n,
@@ -334,6 +359,18 @@ def decoder_layer_verify(acfg, aw: Weights, mcfg, mw: MlpWeights, kv: KVLayer, x
                                            _ptr(workspace), workspace.numel(), _stream(stream)),
            "asr_decoder_layer_verify")
     del keep
+
+
+def decoder_layer_mixed(acfg, aw: Weights, mcfg, mw: MlpWeights, kv: KVLayer, x, n_per_seq, out, workspace,
+                        slots=None, positions=None, host_lens=None, stream=None) -> None:
+    keep, hl = _host_lens(host_lens)
+    nb, B = _block_sizes(n_per_seq)
+    _check(load().asr_decoder_layer_mixed(ctypes.byref(acfg), ctypes.byref(aw.c), ctypes.byref(mcfg),
+                                          ctypes.byref(mw.c), ctypes.byref(kv.c), _ptr(x), _ptr(slots),
+                                          _ptr(positions), B, ctypes.cast(nb, ctypes.c_void_p), hl, _ptr(out),
+                                          _ptr(workspace), workspace.numel(), _stream(stream)),
+           "asr_decoder_layer_mixed")
+    del keep, nb
 
 
 def head_config(hidden=1024, vocab=151936, rms_eps=1e-6, dtype="f16", in_dtype="f32"):

@@ -74,20 +74,28 @@ int device_cus() {
 
 // Smallest power-of-two chunk (>= the capacity-derived minimum) whose item
 // count stays within a few items per CU.
-int choose_split(const asr_attn_config *c, int capacity, int B, int n, const int32_t *host_lens, int cus) {
+// Rows of sequence b: n, or its entry of a mixed call's block sizes.
+struct SeqRows {
+  const int32_t *nb;
+  int n;
+  int operator()(int b) const { return nb ? nb[b] : n; }
+};
+
+int choose_split(const asr_attn_config *c, int capacity, int B, SeqRows n, int rows, const int32_t *host_lens,
+                 int cus) {
   int min_split = (capacity + kMaxChunks - 1) / kMaxChunks;
   min_split = (min_split + 15) / 16 * 16;
   if (min_split < kMinSplit) min_split = kMinSplit;
   if (c->kv_split) return c->kv_split;
   int split = kMinSplit;
   while (split < min_split) split *= 2;
-  if ((long long)B * n <= kVectorRows) {
+  if (rows <= kVectorRows) {
     // few rows: every o_proj workgroup merges all chunks of a row, so keep about
     // 8 chunks per row, and chunks of at least 64 keys (one step per wave)
     int nvis = 1;
     for (int b = 0; b < B; ++b) {
-      const int L = host_lens ? host_lens[b] : capacity - n;
-      if (L + n > nvis) nvis = L + n;
+      const int L = host_lens ? host_lens[b] : capacity - n(b);
+      if (L + n(b) > nvis) nvis = L + n(b);
     }
     if (split < 64) split = 64;
     while (split < kMaxSplit && 8LL * split < nvis) split *= 2;
@@ -98,8 +106,8 @@ int choose_split(const asr_attn_config *c, int capacity, int B, int n, const int
   for (; split < kMaxSplit; split *= 2) {
     long long items = 0;
     for (int b = 0; b < B; ++b) {
-      const int L = host_lens ? host_lens[b] : capacity - n;
-      for (int r = 0; r < n; ++r) items += (L + r + 1 + split - 1) / split;
+      const int L = host_lens ? host_lens[b] : capacity - n(b);
+      for (int r = 0; r < n(b); ++r) items += (L + r + 1 + split - 1) / split;
     }
     items *= c->n_kv_heads;
     if (items <= target) break;
@@ -112,30 +120,50 @@ int choose_split(const asr_attn_config *c, int capacity, int B, int n, const int
 int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_kv_layer *kv,
               const void *x, const int32_t *slots, const int32_t *positions, int B, int n,
               const int32_t *host_lens, const void *residual, void *out, void *ws, size_t ws_bytes,
-              hipStream_t stream) {
+              hipStream_t stream, const int32_t *n_per_seq) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if ((rc = check_kv(kv, cfg))) return rc;
-  if (B < 0 || n < 1 || n > kMaxVerifyK) return ASR_EINVAL;
+  if (B < 0) return ASR_EINVAL;
+  long long total = 0;
+  if (n_per_seq) {
+    // a mixed call: per-sequence block sizes, the host lays out the rows
+    if (B > kVmMaxSeqs) return ASR_EINVAL;
+    n = 1;
+    bool uniform = true;
+    for (int b = 0; b < B; ++b) {
+      if (n_per_seq[b] < 1 || n_per_seq[b] > kMaxVerifyK) return ASR_EINVAL;
+      total += n_per_seq[b];
+      if (n_per_seq[b] > n) n = n_per_seq[b];
+      uniform = uniform && n_per_seq[b] == n_per_seq[0];
+    }
+    if (uniform) n_per_seq = nullptr;   // one block size: the verify (k = 1: decode) call itself
+  } else {
+    if (n < 1 || n > kMaxVerifyK) return ASR_EINVAL;
+    total = (long long)B * n;
+  }
   if (B == 0) return ASR_OK;
+  const SeqRows nb{n_per_seq, n};
   if (!w || !w->input_norm_w || !w->w_qkv || !w->q_norm_w || !w->k_norm_w || !w->w_o) return ASR_EINVAL;
   if (!x || !out) return ASR_EINVAL;
   if (!slots && B > kv->batch_cap) return ASR_EINVAL;
-  if ((long long)B * n > kMaxRows) return ASR_EINVAL;
-  const int rows = B * n;
+  if (total > kMaxRows) return ASR_EINVAL;
+  const int rows = (int)total;
   if (cfg->kv_split && (kv->capacity + cfg->kv_split - 1) / cfg->kv_split > kMaxChunks) return ASR_EINVAL;
   const WorkspaceLayout lay = workspace_layout(rows, cfg->hidden, cfg->n_q_heads, cfg->n_kv_heads, kv->capacity);
   if (!ws || ws_bytes < lay.total) return ASR_EWORKSPACE;
   if (host_lens) {
     for (int b = 0; b < B; ++b)
-      if (host_lens[b] < 0 || (long long)host_lens[b] + n > kv->capacity) return ASR_ECAPACITY;
+      if (host_lens[b] < 0 || (long long)host_lens[b] + nb(b) > kv->capacity) return ASR_ECAPACITY;
   }
+  if (n_per_seq && cfg->dispatch == ASR_DISPATCH_FUSED) return ASR_EUNSUPPORTED;
+  // mixed blocks run on the many-row kernels (matrix-core projections) whatever the row count
 
   const bool kv8 = kv->dtype == ASR_FP8_E4M3;
   if (kv8) {
     // FP8 caches: the many-row kernels (matrix-core projections, equal-share attention)
     const int group = cfg->n_q_heads / cfg->n_kv_heads;
-    if (rows <= kVectorRows || (group != 2 && group != 4) || cfg->dispatch == ASR_DISPATCH_FUSED)
+    if ((rows <= kVectorRows && !n_per_seq) || (group != 2 && group != 4) || cfg->dispatch == ASR_DISPATCH_FUSED)
       return ASR_EUNSUPPORTED;
   }
   const int cus = device_cus();
@@ -173,11 +201,11 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.nqkv = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * kHeadDim;
   a.batch_cap = kv->batch_cap;
   a.capacity = kv->capacity;
-  a.split = choose_split(cfg, kv->capacity, B, n, host_lens, cus);
+  a.split = choose_split(cfg, kv->capacity, B, nb, rows, host_lens, cus);
   a.eps = cfg->rms_eps;
   a.theta = cfg->rope_theta;
   a.out_f32 = cfg->out_dtype == ASR_F32;
-  a.mfma = rows > kVectorRows;
+  a.mfma = rows > kVectorRows || n_per_seq != nullptr;
   a.oproj_split = 0;
   a.vm_items = 0;
   a.kv8 = kv8;
@@ -186,14 +214,18 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.mrope = (cfg->mrope_sections[0] || cfg->mrope_sections[1] || cfg->mrope_sections[2]) ? 1 : 0;
   a.ms0 = cfg->mrope_sections[0];
   a.ms1 = cfg->mrope_sections[1];
+  a.qo_n = n_per_seq ? 1 : 0;
+  a.qo[0] = 0;
+  if (n_per_seq)
+    for (int b = 0; b < B; ++b) a.qo[b + 1] = a.qo[b] + n_per_seq[b];
 
   // upper bound of attention work items; blocks stride over the real count.
   // nch_host: the most chunks of any row, by the host's view of the lengths
   long long bound = 0;
   a.nch_host = 1;
   for (int b = 0; b < B; ++b) {
-    const int L = host_lens ? host_lens[b] : kv->capacity - n;
-    for (int r = 0; r < n; ++r) {
+    const int L = host_lens ? host_lens[b] : kv->capacity - nb(b);
+    for (int r = 0; r < nb(b); ++r) {
       const int c = (L + r + 1 + a.split - 1) / a.split;
       bound += c;
       if (c > a.nch_host) a.nch_host = c;
@@ -241,7 +273,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   } else if (attn_waves_used(a)) {
     // many rows: one equal key share per wave of a resident grid; a (row, kv
     // head) spans at most capacity / share + 2 <= kMaxChunks shares
-    attn_grid = attn_waves_grid(cfg->dtype, a.group, cus);
+    attn_grid = attn_waves_grid(cfg->dtype, a.group, cus, n_per_seq != nullptr);
     if (attn_grid <= 0) return ASR_EHIP;
     int share = cfg->kv_split ? cfg->kv_split : kMinShare;
     const int least = (kv->capacity + kMaxChunks - 2) / (kMaxChunks - 1);
@@ -358,15 +390,27 @@ size_t layer_ws_bytes(const asr_attn_config *acfg, const asr_mlp_config *mcfg, i
 int run_decoder_layer(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
                       const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x, const int32_t *slots,
                       const int32_t *positions, int B, int n, const int32_t *host_lens, void *out, void *ws,
-                      size_t ws_bytes, hipStream_t stream) {
+                      size_t ws_bytes, hipStream_t stream, const int32_t *n_per_seq = nullptr) {
   int rc = check_cfg(acfg);
   if (rc) return rc;
   if ((rc = check_mlp(mcfg))) return rc;
   if (mcfg->hidden != acfg->hidden || mcfg->dtype != acfg->dtype || mcfg->in_dtype != ASR_F32) return ASR_EINVAL;
-  if (B < 0 || n < 1 || n > kMaxVerifyK || (long long)B * n > kMaxRows) return ASR_EINVAL;
+  if (B < 0) return ASR_EINVAL;
+  long long total = (long long)B * n;
+  if (n_per_seq) {
+    if (B > kVmMaxSeqs) return ASR_EINVAL;
+    total = 0;
+    for (int b = 0; b < B; ++b) {
+      if (n_per_seq[b] < 1 || n_per_seq[b] > kMaxVerifyK) return ASR_EINVAL;
+      total += n_per_seq[b];
+    }
+  } else if (n < 1 || n > kMaxVerifyK) {
+    return ASR_EINVAL;
+  }
+  if (total > kMaxRows) return ASR_EINVAL;
   if (B == 0) return ASR_OK;
   if (!kv) return ASR_EINVAL;
-  const int rows = B * n;
+  const int rows = (int)total;
   const size_t att = asr_attn_workspace_bytes(acfg, rows, kv->capacity);
   const size_t need = layer_ws_bytes(acfg, mcfg, rows, kv->capacity);
   if (!att || !need) return ASR_EINVAL;
@@ -376,7 +420,7 @@ int run_decoder_layer(const asr_attn_config *acfg, const asr_attn_weights *aw, c
   char *base = static_cast<char *>(ws);
   float *h = reinterpret_cast<float *>(base + att);
   char *mws = base + att + align_up((size_t)rows * acfg->hidden * sizeof(float));
-  rc = run_layer(&ac, aw, kv, x, slots, positions, B, n, host_lens, x, h, ws, att, stream);
+  rc = run_layer(&ac, aw, kv, x, slots, positions, B, n, host_lens, x, h, ws, att, stream, n_per_seq);
   if (rc) return rc;
   return run_mlp(mcfg, mw, h, rows, out, mws, mlp_ws_bytes(mcfg, rows), stream);
 }
@@ -508,6 +552,15 @@ int asr_decoder_layer_verify(const asr_attn_config *acfg, const asr_attn_weights
                            stream);
 }
 
+int asr_decoder_layer_mixed(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
+                            const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x,
+                            const int32_t *slots, const int32_t *positions, int32_t B, const int32_t *n_per_seq,
+                            const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (B > 0 && !n_per_seq) return ASR_EINVAL;
+  return run_decoder_layer(acfg, aw, mcfg, mw, kv, x, slots, positions, B, 1, host_lens, out, workspace, ws_bytes,
+                           stream, n_per_seq);
+}
 
 size_t asr_attn_workspace_bytes(const asr_attn_config *cfg, int32_t max_rows, int32_t capacity) {
   if (check_cfg(cfg) != ASR_OK || max_rows < 0 || max_rows > kMaxRows || capacity <= 0) return 0;
@@ -530,6 +583,15 @@ int asr_attn_layer_verify(const asr_attn_config *cfg, const asr_attn_weights *w,
   if (k < 1 || k > kMaxVerifyK) return ASR_EINVAL;
   return run_layer(cfg, w, kv, x, slots, positions, B, k, host_lens, residual, out, workspace, ws_bytes,
                    stream);
+}
+
+int asr_attn_layer_mixed(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_kv_layer *kv,
+                         const void *x, const int32_t *slots, const int32_t *positions, int32_t B,
+                         const int32_t *n_per_seq, const int32_t *host_lens, const void *residual, void *out,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+  if (B > 0 && !n_per_seq) return ASR_EINVAL;
+  return run_layer(cfg, w, kv, x, slots, positions, B, 1, host_lens, residual, out, workspace, ws_bytes, stream,
+                   n_per_seq);
 }
 
 int asr_kv_append(const asr_kv_layer *kv, const void *k_new, const void *v_new, const int32_t *slots,

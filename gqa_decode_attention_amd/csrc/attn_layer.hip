@@ -67,22 +67,53 @@ template <bool COH> __device__ __forceinline__ uint4 ldx16B(const uint16_t *p) {
   }
 }
 
+// Rows of a call, sequence-major: sequence b owns rows [seq_row0(b), seq_row0(b) + seq_rows(b)),
+// n each, or (MIX: kernels of a mixed call) the host's block sizes.  MIX is a template argument
+// so that the kernels of uniform calls carry no trace of the mixed layout.
+template <bool MIX = false>
+__device__ __forceinline__ int seq_row0(const LayerArgs &A, int b) {
+  if constexpr (MIX) return A.qo[b];
+  else return b * A.n;
+}
+template <bool MIX = false>
+__device__ __forceinline__ int seq_rows(const LayerArgs &A, int b) {
+  if constexpr (MIX) return A.qo[b + 1] - A.qo[b];
+  else return A.n;
+}
+
+// sequence of row `row`: a division, or in a mixed call the last b with qo[b] <= row
+// (a binary search over at most kVmMaxSeqs starts)
+template <bool MIX = false>
+__device__ __forceinline__ int seq_of(const LayerArgs &A, int row) {
+  if constexpr (!MIX) {
+    return row / A.n;
+  } else {
+    int b = 0;
+#pragma unroll
+    for (int step = kVmMaxSeqs / 2; step > 0; step >>= 1)
+      if (b + step < A.B && A.qo[b + step] <= row) b += step;
+    return b;
+  }
+}
+
 struct RowInfo {
-  int slot, L, pos, nvis, r;
+  int b, slot, L, pos, nvis, r;
   bool ok, slot_ok;
 };
 
 // Row `row` = (sequence b, block offset r).  Visible keys: L + r + 1.
+template <bool MIX = false>
 __device__ __forceinline__ RowInfo row_info(const LayerArgs &A, int row) {
   RowInfo ri;
-  const int b = row / A.n;
-  ri.r = row - b * A.n;
+  const int b = seq_of<MIX>(A, row);
+  ri.b = b;
+  ri.r = row - seq_row0<MIX>(A, b);
   const int s = A.slots ? A.slots[b] : b;
   ri.slot = s;
   ri.slot_ok = (s >= 0 && s < A.batch_cap);
   const int L = ri.slot_ok ? A.lens[s] : 0;
   ri.L = L;
-  ri.ok = ri.slot_ok && L >= 0 && L + A.n <= A.capacity;
+  ri.ok = ri.slot_ok && L >= 0 && L + seq_rows<MIX>(A, b) <= A.capacity;
   ri.pos = (A.positions ? A.positions[b] : L) + ri.r;
   ri.nvis = ri.ok ? L + ri.r + 1 : 0;
   return ri;
@@ -93,18 +124,19 @@ __device__ __forceinline__ int chunks_of(int nvis, int split) { return (nvis + s
 // Rotary position of pair t of row `row`: the row's position, or with
 // multi-section rotary the position component of t's section (positions
 // [3][B]; NULL: the length), plus the row's offset in its block.
+template <bool MIX = false>
 __device__ __forceinline__ int rope_pos(const LayerArgs &A, int row, int t) {
-  const RowInfo ri = row_info(A, row);
+  const RowInfo ri = row_info<MIX>(A, row);
   if (!A.mrope) return ri.pos;
   const int c = t < A.ms0 ? 0 : (t < A.ms0 + A.ms1 ? 1 : 2);
-  return (A.positions ? A.positions[c * A.B + row / A.n] : ri.L) + ri.r;
+  return (A.positions ? A.positions[c * A.B + ri.b] : ri.L) + ri.r;
 }
 
 // Row table for phases M and D (which must not read lens: lengths change in D).
-template <bool COH>
+template <bool COH, bool MIX = false>
 __device__ void write_row_table(const LayerArgs &A) {
   for (int row = threadIdx.x; row < A.rows; row += blockDim.x) {
-    const RowInfo ri = row_info(A, row);
+    const RowInfo ri = row_info<MIX>(A, row);
     int *rec = reinterpret_cast<int *>(A.rowtab + row);
     if constexpr (COH) {
       st_dev(rec + 0, (int)ri.ok);
@@ -349,7 +381,7 @@ struct AttnShared {
 // block-wide exclusive prefix of (chunks per row) * nkv (KEYS: visible keys per
 // row * nkv) into pre[0..rows]; each row's (slot, committed length, visible
 // keys, block offset) is kept in rinfo[] so that work starts without global loads
-template <bool KEYS = false>
+template <bool KEYS = false, bool MIX = false>
 __device__ void build_item_prefix(const LayerArgs &A, int *pre, int4 *rinfo, int *wsum) {
   const int wave = wave_id(), lane = lane_id();
   const int rows = A.rows;
@@ -357,7 +389,7 @@ __device__ void build_item_prefix(const LayerArgs &A, int *pre, int4 *rinfo, int
   const int beg = min((int)threadIdx.x * per, rows), end = min(beg + per, rows);
   int local = 0;
   for (int i = beg; i < end; ++i) {
-    const RowInfo ri = row_info(A, i);
+    const RowInfo ri = row_info<MIX>(A, i);
     rinfo[i] = make_int4(ri.slot, ri.L, ri.nvis, ri.r);
     local += (KEYS ? ri.nvis : chunks_of(ri.nvis, A.split)) * A.nkv;
   }
@@ -716,7 +748,7 @@ __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, co
       kp[u][0] = ld_dev4(Pr, (A.nq + g) * kTilesPerHead * 4);
       kp[u][1] = ld_dev4(Pr, ((A.nq + g) * kTilesPerHead + 4) * 4);
     }
-    const bool writer = (r_off == A.n - 1);
+    const int own = L + r_off - nb;   // the row's own appended row (position L + r_off), if in the chunk
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = wave + 4 * (i0 + u);
@@ -725,7 +757,7 @@ __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, co
       fresh_pair<DT>(A, k4[u], v4[u], kp[u][0], kp[u][1], kb, vb);
       reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
       reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
-      if (writer) {   // the item of the sequence's last row also stores them in the cache
+      if (i == own) {   // every row also stores its own appended row in the cache
         const size_t off = (G.kvrow0 + nb + i) * kHeadDim;
         reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
         reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
@@ -1213,9 +1245,9 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
       if (valid && t >= cc.L) {
         // resources at the sequence's first row (wave-uniform), the appended row by offset
         const int row0 = rfl(cc.row) - rfl(cc.roff), i = t - rfl(cc.L), cg = rfl(cc.g);
-        const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)row0 * A.nqkv, (uint32_t)A.n * row_bytes);
+        const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)row0 * A.nqkv, (uint32_t)(rfl(cc.roff) + 1) * row_bytes);
         const __amdgpu_buffer_rsrc_t Pr =
-            rsrc_of(A.ssq + (size_t)row0 * (A.nq + A.nkv) * kTilesPerHead, (uint32_t)A.n * ssq_bytes);
+            rsrc_of(A.ssq + (size_t)row0 * (A.nq + A.nkv) * kTilesPerHead, (uint32_t)(rfl(cc.roff) + 1) * ssq_bytes);
         const uint32_t kh = i * row_bytes + (A.nq + cg) * kHeadDim * 4, vh = i * row_bytes + (A.nq + A.nkv + cg) * kHeadDim * 4;
         const uint32_t ph = i * ssq_bytes + (A.nq + cg) * kTilesPerHead * 4;
         const float4 ka = ld_dev4(Rr, kh + d0 * 4), kb = ld_dev4(Rr, kh + (d0 + 4) * 4);
@@ -1235,7 +1267,7 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
                           pack4_e4m3(vb.x * iv, vb.y * iv, vb.z * iv, vb.w * iv), 0u, 0u);
           v1 = make_uint4(pack4_e4m3(vc.x * iv, vc.y * iv, vc.z * iv, vc.w * iv),
                           pack4_e4m3(vd.x * iv, vd.y * iv, vd.z * iv, vd.w * iv), 0u, 0u);
-          if (cc.roff == A.n - 1) {   // the sequence's last row stores the appended rows
+          if (t == cc.L + cc.roff) {   // every row stores its own appended row
             const size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
             unsigned char *kc8 = reinterpret_cast<unsigned char *>(A.kc), *vc8 = reinterpret_cast<unsigned char *>(A.vc);
             *reinterpret_cast<uint2 *>(kc8 + ro + d0) = make_uint2(k0.x, k0.y);
@@ -1248,7 +1280,7 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
           k1 = round8<DT>(kc, kd, inv);
           v0 = round8<DT>(va, vb);
           v1 = round8<DT>(vc, vd);
-          if (cc.roff == A.n - 1) {   // the sequence's last row stores the appended rows
+          if (t == cc.L + cc.roff) {   // every row stores its own appended row
             const size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
             *reinterpret_cast<uint4 *>(A.kc + ro + d0) = k0;
             *reinterpret_cast<uint4 *>(A.kc + ro + d1) = k1;
@@ -1413,12 +1445,12 @@ __device__ __forceinline__ void load_wo(const LayerArgs &A, int tile, uint4 (&wr
 }
 
 // lengths advance once every earlier phase has read them
-template <bool COH>
+template <bool COH, bool MIX = false>
 __device__ void advance_lengths(const LayerArgs &A) {
   for (int b = threadIdx.x; b < A.B; b += blockDim.x) {
-    const int4 rec = read_row_table<COH>(A, b * A.n);
+    const int4 rec = read_row_table<COH>(A, seq_row0<MIX>(A, b));
     if (rec.x) {
-      A.lens[rec.z] = rec.y + A.n;
+      A.lens[rec.z] = rec.y + seq_rows<MIX>(A, b);
     } else if (A.status) {
       atomicOr(A.status, rec.w ? (uint32_t)ASR_STATUS_CAPACITY : kStatusBadSlot);
     }
@@ -1542,7 +1574,7 @@ constexpr int chunk_steps(int kq) {
 // as whole 128-byte lines (four rows per instruction) into its own LDS region
 // and reads the operand layout back from there: the operand layout touches 16
 // rows per load, half a line each, and a CU keeps only so many lines in flight.
-template <int DT, int KQ, int NWV, bool LX>
+template <int DT, int KQ, int NWV, bool LX, bool MIX = false>
 __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
   constexpr int KW = KQ * 4 / NWV;      // 32-wide steps of this wave's share of the contraction
   constexpr int KC = KW < 8 ? KW : 8;   // steps per operand batch (x of four row tiles)
@@ -1569,7 +1601,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
   const uint16_t *xr[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) xr[nt] = A.x + (size_t)min(nb + nt * 16 + i16, A.rows - 1) * H + kq0;
-  if (blockIdx.x == 0) write_row_table<false>(A);
+  if (blockIdx.x == 0) write_row_table<false, MIX>(A);
   const bool rot = head < A.nq + A.nkv;
   const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;
   // the q/k norm gains of this lane's four outputs, requested ahead of the operands
@@ -1621,7 +1653,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
         if (n < A.rows) {
           const double omega = exp2(-(2.0 * (t0 + tt) / kHeadDim) * log2((double)A.theta));
           double sd, cd;
-          sincos((double)rope_pos(A, n, t0 + tt) * omega, &sd, &cd);
+          sincos((double)rope_pos<MIX>(A, n, t0 + tt) * omega, &sd, &cd);
           cs = (float)cd;
           sn = (float)sd;
         }
@@ -1738,7 +1770,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
 // LW (nq d = 2048, eight waves): each wave loads its 16 W_o rows x 512 bytes
 // as whole lines (two rows per instruction) into its own 8 KB of LDS and reads
 // the operand layout back (chunk c of row r stored at chunk c ^ (r mod 16)).
-template <int DT, int KQ, int NWV, bool LW>
+template <int DT, int KQ, int NWV, bool LW, bool MIX = false>
 __global__ __launch_bounds__(NWV * 64) void k_oproj_mfma(LayerArgs A) {
   constexpr int KW = KQ * 4 / NWV;   // 32-wide steps of this wave's share of the contraction
   constexpr int KC = chunk_steps(KW);
@@ -1767,7 +1799,7 @@ __global__ __launch_bounds__(NWV * 64) void k_oproj_mfma(LayerArgs A) {
       for (int j = 0; j < 4; ++j) res4[j] = cvt16<DT>(A.residual[(size_t)n_out * A.H + o0 + g4 * 4 + j]);
     }
   }
-  if (blockIdx.x == 0) advance_lengths<false>(A);
+  if (blockIdx.x == 0) advance_lengths<false, MIX>(A);
 
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
@@ -1848,7 +1880,7 @@ __global__ __launch_bounds__(256) void k_qkv(LayerArgs A) {
   }
 }
 
-template <int DT, int GROUP>
+template <int DT, int GROUP, bool MIX = false>
 __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ AttnShared<GROUP> S;
@@ -1856,7 +1888,7 @@ __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   uint16_t *knew = reinterpret_cast<uint16_t *>(rinfo + A.rows);
   uint16_t *vnew = knew + A.n * kHeadDim;
   int *pre = reinterpret_cast<int *>(vnew + A.n * kHeadDim);
-  build_item_prefix(A, pre, rinfo, S.wsum);
+  build_item_prefix<false, MIX>(A, pre, rinfo, S.wsum);
   attention_phase<DT, GROUP, false>(A, pre, rinfo, knew, vnew, S, blockIdx.x, gridDim.x);
 }
 
@@ -2101,7 +2133,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
   const int C = A.nch_host;
   const int row = blockIdx.x / (A.nkv * C), g = (blockIdx.x / C) % A.nkv, c0 = blockIdx.x % C;
   const int wave = wave_id(), lane = lane_id();
-  const int b = row / A.n, r_off = row - b * A.n;
+  const int b = seq_of(A, row), r_off = row - seq_row0(A, b);
   // the slot as far as the loads need it: a sequence's own without a slot
   // table, else its entry clamped into the cache (rows of a bad slot are masked)
   const int slot = A.slots ? min(max(A.slots[b], 0), A.batch_cap - 1) : b;
@@ -2115,7 +2147,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
   const bool has_fresh = wave <= r_off;   // sequence row `wave`, position L + wave, is visible to `row`
   float4 fk = make_float4(0.f, 0.f, 0.f, 0.f), fv = fk, fp0 = fk, fp1 = fk;
   if (has_fresh) {
-    const int rrow = b * A.n + wave;
+    const int rrow = row - r_off + wave;
     const __amdgpu_buffer_rsrc_t Rr = rsrc_of(A.qkv + (size_t)rrow * A.nqkv, (uint32_t)A.nqkv * 4);
     fk = ld_dev4(Rr, ((A.nq + g) * kHeadDim + 2 * (lane & ~1)) * 4);
     fv = ld_dev4(Rr, ((A.nq + A.nkv + g) * kHeadDim + 2 * (lane & ~1)) * 4);
@@ -2142,7 +2174,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
         fresh_pair<DT>(A, fk, fv, fp0, fp1, kb, vb);
         reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
         reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
-        if (r_off == A.n - 1) {   // the sequence's last row also stores them in the cache
+        if (wave == r_off) {   // every row also stores its own appended row in the cache
           const size_t off = (G.kvrow0 + ri.L + wave) * kHeadDim;
           reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
           reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
@@ -2155,13 +2187,13 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
 }
 
 // many rows: equal key shares per wave of a resident grid
-template <int DT, int GROUP, bool NT, bool F8>
+template <int DT, int GROUP, bool NT, bool F8, bool MIX = false>
 __global__ __launch_bounds__(256) void k_attn_waves(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ int wsum[4];
   int4 *rinfo = reinterpret_cast<int4 *>(dyn);
   int *pre = reinterpret_cast<int *>(rinfo + A.rows);
-  build_item_prefix<true>(A, pre, rinfo, wsum);
+  build_item_prefix<true, MIX>(A, pre, rinfo, wsum);
   attention_waves<DT, GROUP, NT, F8>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
 }
 
@@ -2221,8 +2253,8 @@ __device__ void build_seq_prefix(const LayerArgs &A, int *pre, int4 *sinfo, int 
   const int beg = min((int)threadIdx.x * per, B), end = min(beg + per, B);
   int local = 0;
   for (int b = beg; b < end; ++b) {
-    const RowInfo ri = row_info(A, b * A.n);
-    const int nvis = ri.ok ? ri.L + A.n : 0;
+    const RowInfo ri = row_info(A, seq_row0(A, b));
+    const int nvis = ri.ok ? ri.L + seq_rows(A, b) : 0;
     sinfo[b] = make_int4(ri.slot, ri.L, nvis, (int)ri.ok);
     local += chunks_of(nvis, A.split) * A.nkv;
   }
@@ -2763,7 +2795,7 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) av[s2][c] = av_0[s2][c];
     if (row > 0) merge_loads(row, rt, ml0, av);
-    const int nch = chunks_of(rt.x ? rt.y + row % A.n + 1 : 0, A.split);
+    const int nch = chunks_of(rt.x ? rt.y + (row - seq_row0(A, seq_of(A, row))) + 1 : 0, A.split);
     // weights
     float mx = cq < nch ? ml0.x : -INFINITY;
     for (int c = cq + CB; c < nch; c += CB) mx = fmaxf(mx, part_of(row, h0 + hq, c)[128]);
@@ -2847,9 +2879,9 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
 // lengths advance once every workgroup has read them (rows from LDS)
 __device__ void advance_lengths_lds(const LayerArgs &A, const int4 *rinfo) {
   for (int b = threadIdx.x; b < A.B; b += blockDim.x) {
-    const int4 ri = rinfo[b * A.n];
+    const int4 ri = rinfo[seq_row0(A, b)];
     if (ri.z > 0) {
-      A.lens[ri.x] = ri.y + A.n;
+      A.lens[ri.x] = ri.y + seq_rows(A, b);
     } else if (A.status) {
       atomicOr(A.status, (ri.x >= 0 && ri.x < A.batch_cap) ? (uint32_t)ASR_STATUS_CAPACITY : kStatusBadSlot);
     }
@@ -3008,43 +3040,49 @@ struct MfmaKernel {
 
 // LX / LW instances stage each wave's operand lines through LDS: 16 KB (x, then
 // W) or 8 KB (W_o) per wave
-template <int DT>
-MfmaKernel pick_qkv_mfma(int kq) {
+template <int DT, bool MIX>
+MfmaKernel pick_qkv_mfma_t(int kq) {
   switch (kq) {
-    case 4: return {k_qkv_mfma<DT, 4, 8, false>, 0};
-    case 8: return {k_qkv_mfma<DT, 8, 8, true>, 8 * 16384};
-    case 12: return {k_qkv_mfma<DT, 12, 8, false>, 0};
-    case 16: return {k_qkv_mfma<DT, 16, 8, false>, 0};
-    case 20: return {k_qkv_mfma<DT, 20, 4, false>, 0};
-    case 24: return {k_qkv_mfma<DT, 24, 4, false>, 0};
-    case 28: return {k_qkv_mfma<DT, 28, 4, false>, 0};
-    case 32: return {k_qkv_mfma<DT, 32, 4, false>, 0};
+    case 4: return {k_qkv_mfma<DT, 4, 8, false, MIX>, 0};
+    case 8: return {k_qkv_mfma<DT, 8, 8, true, MIX>, 8 * 16384};
+    case 12: return {k_qkv_mfma<DT, 12, 8, false, MIX>, 0};
+    case 16: return {k_qkv_mfma<DT, 16, 8, false, MIX>, 0};
+    case 20: return {k_qkv_mfma<DT, 20, 4, false, MIX>, 0};
+    case 24: return {k_qkv_mfma<DT, 24, 4, false, MIX>, 0};
+    case 28: return {k_qkv_mfma<DT, 28, 4, false, MIX>, 0};
+    case 32: return {k_qkv_mfma<DT, 32, 4, false, MIX>, 0};
     default: return {nullptr, 0};
   }
 }
-
 template <int DT>
-MfmaKernel pick_oproj_mfma(int kq) {
+MfmaKernel pick_qkv_mfma(int kq, bool mix) { return mix ? pick_qkv_mfma_t<DT, true>(kq) : pick_qkv_mfma_t<DT, false>(kq); }
+
+template <int DT, bool MIX>
+MfmaKernel pick_oproj_mfma_t(int kq) {
   switch (kq) {
-    case 4: return {k_oproj_mfma<DT, 4, 8, false>, 0};
-    case 8: return {k_oproj_mfma<DT, 8, 8, false>, 0};
-    case 12: return {k_oproj_mfma<DT, 12, 8, false>, 0};
-    case 16: return {k_oproj_mfma<DT, 16, 8, true>, 8 * 8192};
-    case 20: return {k_oproj_mfma<DT, 20, 8, false>, 0};
-    case 24: return {k_oproj_mfma<DT, 24, 8, false>, 0};
-    case 28: return {k_oproj_mfma<DT, 28, 8, false>, 0};
-    case 32: return {k_oproj_mfma<DT, 32, 8, false>, 0};
+    case 4: return {k_oproj_mfma<DT, 4, 8, false, MIX>, 0};
+    case 8: return {k_oproj_mfma<DT, 8, 8, false, MIX>, 0};
+    case 12: return {k_oproj_mfma<DT, 12, 8, false, MIX>, 0};
+    case 16: return {k_oproj_mfma<DT, 16, 8, true, MIX>, 8 * 8192};
+    case 20: return {k_oproj_mfma<DT, 20, 8, false, MIX>, 0};
+    case 24: return {k_oproj_mfma<DT, 24, 8, false, MIX>, 0};
+    case 28: return {k_oproj_mfma<DT, 28, 8, false, MIX>, 0};
+    case 32: return {k_oproj_mfma<DT, 32, 8, false, MIX>, 0};
     default: return {nullptr, 0};
   }
 }
+template <int DT>
+MfmaKernel pick_oproj_mfma(int kq, bool mix) {
+  return mix ? pick_oproj_mfma_t<DT, true>(kq) : pick_oproj_mfma_t<DT, false>(kq);
+}
 
 template <int DT>
-LayerKernel pick_attn(int group) {
+LayerKernel pick_attn(int group, bool mix) {
   switch (group) {
-    case 1: return k_attn<DT, 1>;
-    case 2: return k_attn<DT, 2>;
-    case 4: return k_attn<DT, 4>;
-    case 8: return k_attn<DT, 8>;
+    case 1: return mix ? k_attn<DT, 1, true> : k_attn<DT, 1>;
+    case 2: return mix ? k_attn<DT, 2, true> : k_attn<DT, 2>;
+    case 4: return mix ? k_attn<DT, 4, true> : k_attn<DT, 4>;
+    case 8: return mix ? k_attn<DT, 8, true> : k_attn<DT, 8>;
     default: return nullptr;
   }
 }
@@ -3091,10 +3129,12 @@ LayerKernel pick_oproj_merge(int kvo, int nch_host, bool split) {
   }
 }
 
+// (mixed calls: never single-token-only, so no NT instance)
 template <int DT>
-LayerKernel pick_attn_waves(int group, bool nt, bool f8) {
+LayerKernel pick_attn_waves(int group, bool nt, bool f8, bool mix = false) {
 #define ASR_PICK_WAVES(G) \
-  case G: return f8 ? (nt ? k_attn_waves<DT, G, true, true> : k_attn_waves<DT, G, false, true>) \
+  case G: return mix ? (f8 ? k_attn_waves<DT, G, false, true, true> : k_attn_waves<DT, G, false, false, true>) \
+               : f8 ? (nt ? k_attn_waves<DT, G, true, true> : k_attn_waves<DT, G, false, true>) \
                     : (nt ? k_attn_waves<DT, G, true, false> : k_attn_waves<DT, G, false, false>);
   switch (group) {
     ASR_PICK_WAVES(2) ASR_PICK_WAVES(4)
@@ -3150,7 +3190,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
   if (a.mfma) {
     // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
     const int rtiles = (a.rows + 63) / 64;
-    const MfmaKernel kq = pick_qkv_mfma<DT>(a.H / 128);
+    const MfmaKernel kq = pick_qkv_mfma<DT>(a.H / 128, a.qo_n != 0);
     if ((e = launch_phase(kq.fn, dim3(a.nqkv / 16 * rtiles), dim3(qkv_mfma_waves(a.H / 128) * kWave), kq.lds, s, ev,
                           0, a)) != hipSuccess)
       return e;
@@ -3175,15 +3215,15 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                           lds_vmfma_bytes(a.B), s, ev, 1, a)) != hipSuccess)
       return e;
   } else if (attn_waves_used(a)) {
-    if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1, a.kv8 != 0), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
+    if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1, a.kv8 != 0, a.qo_n != 0), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
                           ev, 1, a)) != hipSuccess)
       return e;
-  } else if ((e = launch_phase(pick_attn<DT>(a.group), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
+  } else if ((e = launch_phase(pick_attn<DT>(a.group, a.qo_n != 0), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
                                ev, 1, a)) != hipSuccess) {
     return e;
   }
   if (a.mfma) {
-    const MfmaKernel ko = pick_oproj_mfma<DT>(a.nq * kHeadDim / 128);
+    const MfmaKernel ko = pick_oproj_mfma<DT>(a.nq * kHeadDim / 128, a.qo_n != 0);
     return launch_phase(ko.fn, dim3(a.H / 16 * ((a.rows + 15) / 16)), dim3(512), ko.lds, s, ev, 2, a);
   }
   return launch_phase(pick_oproj<DT>(a.nq * kHeadDim / 512, a.rows == 1), dim3(a.H / (4 * kRpwD)), dim3(256), 0, s,
@@ -3252,7 +3292,7 @@ size_t layer_dyn_smem(const LayerArgs &a) { return fused_dyn_smem(a); }
 // tiles: one K/V stream per (sequence, kv head) on the matrix cores (the
 // per-row merge takes two or more q heads per kv head)
 bool attn_vmfma_used(const LayerArgs &a) {
-  return a.mfma && a.n > 1 && a.group >= 2 && !a.kv8 && vmfma_tiles(a.group, a.n) > 0;
+  return a.mfma && !a.qo_n && a.n > 1 && a.group >= 2 && !a.kv8 && vmfma_tiles(a.group, a.n) > 0;
 }
 
 // Resident workgroups of the verify attention kernel for B sequences (blocks per
@@ -3272,19 +3312,20 @@ bool attn_waves_used(const LayerArgs &a) { return a.mfma && (a.group == 2 || a.g
 
 // Resident grid of the equal-share attention kernel: blocks per CU from the
 // occupancy calculator (at the largest row table) times the CU count.
-int attn_waves_grid(int dtype, int group, int cus) {
-  // occupancy per (dtype, group), computed once per process; calls from several
-  // threads may each compute it, they store the same value
-  static std::atomic<int> cached[2][9];
-  const int di = dtype == ASR_BF16 ? 1 : 0;
+int attn_waves_grid(int dtype, int group, int cus, bool mix) {
+  // occupancy per (dtype, group, mixed), computed once per process; calls from
+  // several threads may each compute it, they store the same value
+  static std::atomic<int> cached[2][9][2];
+  const int di = dtype == ASR_BF16 ? 1 : 0, mi = mix ? 1 : 0;
   if (group != 2 && group != 4) return 0;
-  int per_cu = cached[di][group].load(std::memory_order_relaxed);
+  int per_cu = cached[di][group][mi].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
-    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, true, false) : pick_attn_waves<ASR_F16>(group, true, false);
+    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, !mix, false, mix)
+                                            : pick_attn_waves<ASR_F16>(group, !mix, false, mix);
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_attn_waves_bytes(kMaxLayerRows)) !=
                   hipSuccess || per_cu <= 0)
       return 0;
-    cached[di][group].store(per_cu, std::memory_order_relaxed);
+    cached[di][group][mi].store(per_cu, std::memory_order_relaxed);
   }
   return per_cu * cus;
 }

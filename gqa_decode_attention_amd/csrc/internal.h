@@ -69,6 +69,10 @@ struct LayerArgs {
   // multi-section rotary: pairs [0, ms0) use position component 0, [ms0, ms0 + ms1) component 1,
   // the rest component 2 (positions [3][B]); mrope = 0: one position per row
   int mrope, ms0, ms1;
+  // mixed blocks (qo_n = 1): sequence b owns rows [qo[b], qo[b + 1]) with qo[B] = rows, B <= kVmMaxSeqs,
+  // and n is the largest block; qo_n = 0: every sequence owns n rows
+  int qo_n;
+  int qo[kVmMaxSeqs + 1];
 };
 
 // The rest of the decoder layer: post-attention RMSNorm, gated SiLU MLP, residual.
@@ -124,10 +128,12 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(int rows, int H, int nq, int nkv, int capacity);
 
 // validation, workspace carving and launch of one layer call (decode: n = 1;
-// verify: n = k); the workspace is any device buffer of ws_bytes
+// verify: n = k; mixed: n_per_seq, a host array of B block sizes, with n unused);
+// the workspace is any device buffer of ws_bytes
 int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_kv_layer *kv, const void *x,
               const int32_t *slots, const int32_t *positions, int B, int n, const int32_t *host_lens,
-              const void *residual, void *out, void *ws, size_t ws_bytes, hipStream_t stream);
+              const void *residual, void *out, void *ws, size_t ws_bytes, hipStream_t stream,
+              const int32_t *n_per_seq = nullptr);
 
 // launchers; return hipSuccess or the launch error
 hipError_t launch_layer_multi(const LayerArgs &a, int dtype, int attn_grid, hipStream_t s, hipEvent_t *ev);
@@ -138,7 +144,7 @@ size_t layer_dyn_smem(const LayerArgs &a);
 bool attn_waves_used(const LayerArgs &a);
 bool attn_vmfma_used(const LayerArgs &a);
 int attn_vmfma_grid(int dtype, int group, int n, int B, int cus);
-int attn_waves_grid(int dtype, int group, int cus);
+int attn_waves_grid(int dtype, int group, int cus, bool mix);
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
                             const int32_t *slots, int B, int n, hipStream_t s);
 hipError_t launch_kv_crop(const asr_kv_layer *layers, int n_layers, const int32_t *new_lens,

@@ -239,6 +239,34 @@ int asr_attn_layer_verify(const asr_attn_config *cfg, const asr_attn_weights *w,
                           void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Decode rows and verify blocks of different lengths in one call ("Can CTC
+ * make Qwen3-ASR faster?", section 08 "Verifier, version 0": the block length
+ * is chosen per sequence from the draft's confidence, so the sequences in
+ * flight carry blocks of different k; a k of 1 is a plain decode step).
+ * Sequence b owns n_per_seq[b] consecutive rows starting at row
+ * n_per_seq[0] + ... + n_per_seq[b - 1]; with L = lens[s] its rows are appended
+ * at L .. L + n_per_seq[b] - 1 and row r attends over positions 0 .. L + r, as
+ * in asr_attn_layer_verify with k = n_per_seq[b].  lens[s] becomes
+ * L + n_per_seq[b].  Rotary position of row r: positions[b] + r (NULL: L + r;
+ * multi-section rotary: positions [3][B], component c of sequence b at
+ * positions[c * B + b]).
+ *   n_per_seq HOST [B] int32, each in 1 .. 32; B <= 64; rows = sum of n_per_seq <= 2048
+ *   x, residual [rows][H] dtype, out [rows][H] out_dtype
+ * It computes what one asr_attn_layer_verify call per sequence with its own k
+ * computes (up to the order of fp32 sums: blocks of different sizes always
+ * take the many-row kernels, whatever the row count).  Blocks all of one size
+ * k are the asr_attn_layer_verify call with that k (k = 1: the decode call),
+ * bit for bit.  Blocks of different sizes are not available with
+ * ASR_DISPATCH_FUSED (ASR_EUNSUPPORTED); B > 64 or a block size outside
+ * 1 .. 32: ASR_EINVAL.  Workspace: asr_attn_workspace_bytes for `rows` rows.
+ */
+int asr_attn_layer_mixed(const asr_attn_config *cfg, const asr_attn_weights *w,
+                         const asr_kv_layer *kv, const void *x, const int32_t *slots,
+                         const int32_t *positions, int32_t B, const int32_t *n_per_seq,
+                         const int32_t *host_lens, const void *residual, void *out,
+                         void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Bit-exact copy of given K/V rows into one layer's cache: the prefill filler
  * ("Can CTC make Qwen3-ASR faster?", section 11 Phase D: build the prompt KV
  * once, then verify blocks against it; the faster-qwen-asr GB10 record's
@@ -340,6 +368,14 @@ int asr_decoder_layer_verify(const asr_attn_config *acfg, const asr_attn_weights
                              const int32_t *slots, const int32_t *positions, int32_t B, int32_t k,
                              const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
                              hipStream_t stream);
+
+/* Mixed decode rows and verify blocks (as asr_attn_layer_mixed) through a whole
+   decoder layer: x, out [rows][H], rows = sum of n_per_seq. */
+int asr_decoder_layer_mixed(const asr_attn_config *acfg, const asr_attn_weights *aw, const asr_mlp_config *mcfg,
+                            const asr_mlp_weights *mw, const asr_kv_layer *kv, const void *x,
+                            const int32_t *slots, const int32_t *positions, int32_t B, const int32_t *n_per_seq,
+                            const int32_t *host_lens, void *out, void *workspace, size_t ws_bytes,
+                            hipStream_t stream);
 
 /*
  * The verify loop above the decoder ("Can CTC make Qwen3-ASR faster?", section

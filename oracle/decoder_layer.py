@@ -27,7 +27,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .attn_block import BlockConfig, KVCache, LayerWeights, decode, rms_norm, verify, widen
+from .attn_block import BlockConfig, KVCache, LayerWeights, decode, mixed, rms_norm, verify, widen
 
 
 @dataclass(frozen=True)
@@ -78,3 +78,11 @@ def decoder_layer_verify(acfg: BlockConfig, aw: LayerWeights, mcfg: MlpConfig, m
     h = verify(acfg, aw, cache, x_bits, slots=slots, positions=positions, residual_bits=x_bits)
     B, k, H = h.shape
     return mlp(mcfg, mw, h.reshape(B * k, H)).reshape(B, k, H)
+
+
+def decoder_layer_mixed(acfg: BlockConfig, aw: LayerWeights, mcfg: MlpConfig, mw: MlpWeights, cache: KVCache,
+                        x_bits: np.ndarray, n_per_seq, slots=None, positions=None) -> np.ndarray:
+    """Decode rows and verify blocks of per-sequence sizes through a whole decoder layer:
+    x is [sum(n_per_seq)][H] (the attention block of ``mixed``, then the MLP row by row)."""
+    h = mixed(acfg, aw, cache, x_bits, n_per_seq, slots=slots, positions=positions, residual_bits=x_bits)
+    return mlp(mcfg, mw, h)

@@ -133,3 +133,30 @@ def test_fp8_cache_validation_on_the_host():
     assert dec(*args(scaled, 6, ga.config(dtype="bf16", n_kv_heads=2)), ) == -1   # kv heads differ from the cache
     assert dec(*args(scaled, 6, ga.config(dtype="bf16", dispatch=ga.DISPATCH_FUSED))) == -2
     assert lib.asr_kv_append(ctypes.byref(no_scales), fake, fake, None, 1, 1, None) == -1
+
+
+def test_mixed_entry_validates_on_the_host():
+    """Mixed calls: block sizes 1 .. 32 for at most 64 sequences, no fused dispatch, the host
+    lengths checked against each sequence's own block."""
+    ga, lib = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    w = ga._lib.AsrAttnWeights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    kv = ga._lib.AsrKvLayer(0x1000, 0x1000, 0x1000, None, 80, 64, 8, 128, ga.F16)
+    cfg = ga.config()
+    mix = lib.asr_attn_layer_mixed
+
+    def call(sizes, c=cfg, lens=None, ws=1 << 30):
+        nb = (ctypes.c_int32 * max(1, len(sizes)))(*sizes)
+        hl = None if lens is None else ctypes.cast((ctypes.c_int32 * len(lens))(*lens), P)
+        return mix(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), fake, None, None, len(sizes),
+                   ctypes.cast(nb, P), hl, None, fake, fake, ws, None)
+
+    assert call([]) == 0
+    assert mix(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), fake, None, None, 2, None, None, None, fake,
+               fake, 1 << 30, None) == -1                             # no block sizes
+    assert call([1, 0, 2]) == -1 and call([33]) == -1 and call([1] * 65) == -1
+    assert call([4, 1], ga.config(dispatch=ga.DISPATCH_FUSED)) == -2
+    assert call([4, 8], lens=[60, 57]) == -3                          # 57 + 8 > 64
+    assert call([4, 8], ws=16) == -4
+    assert call([32] * 64, ws=16) == -4                               # the largest call: 2048 rows

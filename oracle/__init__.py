@@ -5,3 +5,4 @@ from .attn_block import (BF16, E4M3, E4M3_MAX, F16, e4m3_value, rne_e4m3, STATUS
 from .decoder_layer import MlpConfig, MlpWeights, decoder_layer_decode, decoder_layer_mixed, decoder_layer_verify, mlp, silu
 from .spec_loop import (HeadConfig, TinyModel, accept_greedy, argmax_first, embed, greedy_decode, lm_head_logits,
                         speculative_round)
+from .spec_policy import next_block_len, recycle_draft, speculative_decode

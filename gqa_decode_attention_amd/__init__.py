@@ -8,4 +8,4 @@ from ._lib import (BF16, FP8_E4M3, DISPATCH_AUTO, DISPATCH_FUSED, DISPATCH_MULTI
                    AsrError, KVLayer, Weights, alloc_workspace, config, kv_append, kv_crop, layer_decode, layer_decode_noalloc, NOALLOC_SCRATCH_BYTES,
                    layer_verify, load, torch_dtype, workspace_bytes, AsrMlpConfig, MlpWeights, mlp_config,
                    mlp_workspace_bytes, mlp_layer, decoder_layer_workspace, decoder_layer_decode,
-                   decoder_layer_verify, decoder_layer_mixed, layer_mixed, head_config, embed, lm_head_workspace, lm_head_argmax, accept_greedy)
+                   decoder_layer_verify, decoder_layer_mixed, layer_mixed, head_config, embed, lm_head_workspace, lm_head_argmax, accept_greedy, accept_greedy_mixed, next_block_len, recycle_draft)

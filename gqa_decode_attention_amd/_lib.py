@@ -27,7 +27,8 @@ EXPORTED = ["asr_attn_workspace_bytes", "asr_attn_layer_decode", "asr_attn_layer
             "asr_attn_layer_verify", "asr_kv_append", "asr_kv_crop", "asr_strerror",
             "asr_mlp_workspace_bytes", "asr_mlp_layer", "asr_decoder_layer_workspace_bytes",
             "asr_decoder_layer_decode", "asr_decoder_layer_verify", "asr_embed", "asr_lm_head_workspace_bytes",
-            "asr_lm_head_argmax", "asr_accept_greedy", "asr_attn_layer_mixed", "asr_decoder_layer_mixed"]
+            "asr_lm_head_argmax", "asr_accept_greedy", "asr_attn_layer_mixed", "asr_decoder_layer_mixed",
+            "asr_accept_greedy_mixed", "asr_next_block_len", "asr_recycle_draft"]
 
 _TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
 _DT_NAME = {"f16": F16, "bf16": BF16, "f32": F32}
@@ -114,6 +115,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.asr_attn_layer_mixed.restype = ctypes.c_int
     lib.asr_decoder_layer_mixed.argtypes = [AC, AW, MC, MW, KV, P, P, P, I32, P, P, P, P, SZ, P]
     lib.asr_decoder_layer_mixed.restype = ctypes.c_int
+    lib.asr_accept_greedy_mixed.argtypes = [P, P, I32, P, P, P, I32, P, P, P, P]
+    lib.asr_accept_greedy_mixed.restype = ctypes.c_int
+    lib.asr_next_block_len.argtypes = [P, I32, ctypes.c_float, I32, I32]
+    lib.asr_next_block_len.restype = ctypes.c_int32
+    lib.asr_recycle_draft.argtypes = [P, I32, I32, I32, I32, I32, I32]
+    lib.asr_recycle_draft.restype = ctypes.c_int32
     HC = ctypes.POINTER(AsrHeadConfig)
     lib.asr_embed.argtypes = [P, I32, I32, I32, P, I32, P, P]
     lib.asr_embed.restype = ctypes.c_int
@@ -403,3 +410,33 @@ def accept_greedy(draft, target, lens, accepted, next_token, new_lens, slots=Non
     _check(load().asr_accept_greedy(_ptr(draft), _ptr(target), B, k, _ptr(slots), _ptr(lens), lens.numel(),
                                     _ptr(accepted), _ptr(next_token), _ptr(new_lens), _stream(stream)),
            "asr_accept_greedy")
+
+
+def accept_greedy_mixed(draft, target, n_per_seq, lens, accepted, next_token, new_lens, slots=None,
+                        stream=None) -> None:
+    """draft, target int32 [sum(n_per_seq)] (sequence-major blocks); n_per_seq host ints."""
+    nb, B = _block_sizes(n_per_seq)
+    _check(load().asr_accept_greedy_mixed(_ptr(draft), _ptr(target), B, ctypes.cast(nb, ctypes.c_void_p),
+                                          _ptr(slots), _ptr(lens), lens.numel(), _ptr(accepted), _ptr(next_token),
+                                          _ptr(new_lens), _stream(stream)),
+           "asr_accept_greedy_mixed")
+    del nb
+
+
+def next_block_len(uncertainty, threshold, k_min, k_max) -> int:
+    """The next block length from the host uncertainties of the remaining draft tokens."""
+    u = [float(v) for v in uncertainty]
+    arr = (ctypes.c_float * max(1, len(u)))(*u)
+    k = load().asr_next_block_len(ctypes.cast(arr, ctypes.c_void_p), len(u), float(threshold), int(k_min), int(k_max))
+    _check(min(int(k), 0), "asr_next_block_len")
+    return int(k)
+
+
+def recycle_draft(draft, pos, k, accepted, correction, window) -> int:
+    """The draft read position after a round (host token ids; correction ignored when all accepted)."""
+    d = [int(v) for v in draft]
+    arr = (ctypes.c_int32 * max(1, len(d)))(*d)
+    p = load().asr_recycle_draft(ctypes.cast(arr, ctypes.c_void_p), len(d), int(pos), int(k), int(accepted),
+                                 int(-1 if correction is None else correction), int(window))
+    _check(min(int(p), 0), "asr_recycle_draft")
+    return int(p)

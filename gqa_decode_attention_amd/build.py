@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libasr_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "attn_layer.hip", "kv_ops.hip", "mlp.hip", "noalloc.hip"]
+SOURCES = ["api.hip", "attn_layer.hip", "kv_ops.hip", "mlp.hip", "noalloc.hip", "policy.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -513,7 +513,22 @@ int asr_accept_greedy(const int32_t *draft, const int32_t *target, int32_t B, in
   if (B == 0) return ASR_OK;
   if (!draft || !target || !lens || !accepted || !next_token || !new_lens) return ASR_EINVAL;
   if (!slots && B > batch_cap) return ASR_EINVAL;
-  AcceptArgs a{draft, target, slots, lens, accepted, next_token, new_lens, B, k, batch_cap};
+  AcceptArgs a{draft, target, slots, lens, accepted, next_token, new_lens, B, k, batch_cap, 0, {0}};
+  return launch_accept(a, stream) == hipSuccess ? ASR_OK : ASR_EHIP;
+}
+
+int asr_accept_greedy_mixed(const int32_t *draft, const int32_t *target, int32_t B, const int32_t *n_per_seq,
+                            const int32_t *slots, const int32_t *lens, int32_t batch_cap, int32_t *accepted,
+                            int32_t *next_token, int32_t *new_lens, hipStream_t stream) {
+  if (B < 0 || B > kVmMaxSeqs || batch_cap <= 0) return ASR_EINVAL;
+  if (B == 0) return ASR_OK;
+  if (!n_per_seq || !draft || !target || !lens || !accepted || !next_token || !new_lens) return ASR_EINVAL;
+  if (!slots && B > batch_cap) return ASR_EINVAL;
+  AcceptArgs a{draft, target, slots, lens, accepted, next_token, new_lens, B, 1, batch_cap, 1, {0}};
+  for (int b = 0; b < B; ++b) {
+    if (n_per_seq[b] < 1 || n_per_seq[b] > kMaxVerifyK) return ASR_EINVAL;
+    a.qo[b + 1] = a.qo[b] + n_per_seq[b];
+  }
   return launch_accept(a, stream) == hipSuccess ? ASR_OK : ASR_EHIP;
 }
 

@@ -109,12 +109,15 @@ struct HeadArgs {
 
 // Strict greedy acceptance and the lengths to crop to.
 struct AcceptArgs {
-  const int32_t *draft, *target;  // [B][k]
+  const int32_t *draft, *target;  // [B][k], or the packed blocks of a mixed call
   const int32_t *slots;           // [B] or null
   const int32_t *lens;            // [batch_cap] lengths after the verify block
   int32_t *accepted, *next_token; // [B]
   int32_t *new_lens;              // [batch_cap]
   int B, k, batch_cap;
+  // blocks of per-sequence sizes (qo_n = 1): sequence b's block is entries [qo[b], qo[b + 1])
+  int qo_n;
+  int qo[kVmMaxSeqs + 1];
 };
 
 hipError_t launch_embed(const HeadArgs &a, int dtype, hipStream_t s);

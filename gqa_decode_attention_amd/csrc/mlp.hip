@@ -289,14 +289,16 @@ __global__ __launch_bounds__(256) void k_lens_copy(AcceptArgs A) {
 __global__ __launch_bounds__(256) void k_accept(AcceptArgs A) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= A.B) return;
-  const int *d = A.draft + (size_t)b * A.k, *t = A.target + (size_t)b * A.k;
+  const size_t base = A.qo_n ? (size_t)A.qo[b] : (size_t)b * A.k;
+  const int k = A.qo_n ? A.qo[b + 1] - A.qo[b] : A.k;
+  const int *d = A.draft + base, *t = A.target + base;
   int a = 0;
-  while (a < A.k && d[a] == t[a]) ++a;
-  const int committed = a < A.k ? a + 1 : A.k;
+  while (a < k && d[a] == t[a]) ++a;
+  const int committed = a < k ? a + 1 : k;
   A.accepted[b] = a;
-  A.next_token[b] = a < A.k ? t[a] : d[A.k - 1];
+  A.next_token[b] = a < k ? t[a] : d[k - 1];
   const int s = A.slots ? A.slots[b] : b;
-  if (s >= 0 && s < A.batch_cap) A.new_lens[s] = max(A.lens[s] - A.k + committed, 0);
+  if (s >= 0 && s < A.batch_cap) A.new_lens[s] = max(A.lens[s] - k + committed, 0);
 }
 
 using MlpKernel = void (*)(MlpArgs);

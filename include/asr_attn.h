@@ -433,6 +433,49 @@ int asr_accept_greedy(const int32_t *draft, const int32_t *target, int32_t B, in
                       const int32_t *lens, int32_t batch_cap, int32_t *accepted, int32_t *next_token,
                       int32_t *new_lens, hipStream_t stream);
 
+/*
+ * asr_accept_greedy for blocks of per-sequence sizes, as a mixed call lays them
+ * out: draft and target hold sequence b's n_per_seq[b] entries after those of
+ * sequences 0 .. b-1 (device arrays); n_per_seq is a HOST array of B sizes in
+ * 1 .. 32, B <= 64.  Sequence b's results as asr_accept_greedy with k =
+ * n_per_seq[b].
+ */
+int asr_accept_greedy_mixed(const int32_t *draft, const int32_t *target, int32_t B, const int32_t *n_per_seq,
+                            const int32_t *slots, const int32_t *lens, int32_t batch_cap, int32_t *accepted,
+                            int32_t *next_token, int32_t *new_lens, hipStream_t stream);
+
+/*
+ * The loop's block-length and draft-recycling policy ("Can CTC make Qwen3-ASR
+ * faster?", section 07: adaptive block length and recycling of the aligned
+ * suffix; section 08 "Verifier, version 0": at a mismatch recycle the draft
+ * suffix that realigns after the correction, and choose the next k from the
+ * draft's confidence, longer over low-entropy spans and shorter around
+ * uncertain tokens).  Host functions on host arrays; neither changes what a
+ * round commits, only how many rounds a transcript takes.
+ *
+ * asr_next_block_len: uncertainty[0..n-1] is the draft's uncertainty of each
+ * token not yet verified (for example its frame entropy).  With j the first
+ * index whose uncertainty is above threshold (n if none; NaN is never above),
+ * the block ends at that token: k = j + 1, clamped to [k_min, k_max] and to n,
+ * and at least 1 (no draft left: a greedy step).  Returns k, or ASR_EINVAL
+ * (n < 0, a NULL array with n > 0, k_min < 1, k_max < k_min or k_max > 32).
+ */
+int32_t asr_next_block_len(const float *uncertainty, int32_t n, float threshold, int32_t k_min, int32_t k_max);
+
+/*
+ * asr_recycle_draft: the read position in draft[0..n-1] (host) for the next
+ * round, after a round that verified the k tokens from position pos (tokens
+ * past n were padding) and accepted `accepted` of them.  All accepted: pos + k.
+ * Otherwise the target's correction replaces draft[pos + accepted]; if it equals
+ * one of the next `window` tokens, the tokens before the first such match were
+ * spurious and reading resumes just past the match, else draft[pos + accepted]
+ * was a wrong token in the right place and reading resumes after it.  Returns
+ * the position, or ASR_EINVAL (n < 0, NULL draft with n > 0, pos < 0, k < 1,
+ * accepted outside [0, k], window < 0).
+ */
+int32_t asr_recycle_draft(const int32_t *draft, int32_t n, int32_t pos, int32_t k, int32_t accepted,
+                          int32_t correction, int32_t window);
+
 /* Static text of an ASR_E* code. */
 const char *asr_strerror(int code);
 

@@ -39,6 +39,15 @@ int32_t asr_recycle_draft(const int32_t *draft, int32_t n, int32_t pos, int32_t 
   if (last > (int64_t)n - 1) last = (int64_t)n - 1;
   for (int64_t j = miss + 1; j <= last; ++j)
     if (draft[j] == correction) return (int32_t)(j + 1);
+  // a round that failed at its first token: the previous realignment may have
+  // skipped a token the draft had dropped; the nearest of the `window` tokens
+  // before pos equal to the correction marks where the draft resumes
+  if (accepted == 0) {
+    int64_t hi = (int64_t)pos < (int64_t)n ? (int64_t)pos : (int64_t)n;
+    const int64_t lo = (int64_t)pos - window > 0 ? (int64_t)pos - window : 0;
+    for (int64_t j = hi - 1; j >= lo; --j)
+      if (draft[j] == correction) return (int32_t)(j + 1);
+  }
   return (int32_t)(miss + 1);
 }
 

@@ -468,8 +468,11 @@ int32_t asr_next_block_len(const float *uncertainty, int32_t n, float threshold,
  * past n were padding) and accepted `accepted` of them.  All accepted: pos + k.
  * Otherwise the target's correction replaces draft[pos + accepted]; if it equals
  * one of the next `window` tokens, the tokens before the first such match were
- * spurious and reading resumes just past the match, else draft[pos + accepted]
- * was a wrong token in the right place and reading resumes after it.  Returns
+ * spurious and reading resumes just past the match; else, for a round that
+ * failed at its first token (accepted = 0), if it equals one of the `window`
+ * tokens before pos, the draft had dropped a token there and reading resumes
+ * just past the nearest such match; else draft[pos + accepted] was a wrong
+ * token in the right place and reading resumes after it.  Returns
  * the position, or ASR_EINVAL (n < 0, NULL draft with n > 0, pos < 0, k < 1,
  * accepted outside [0, k], window < 0).
  */

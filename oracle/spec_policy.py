@@ -25,9 +25,13 @@ Readings taken here (the pages give no formula):
 * Recycling: after a < k accepted tokens the target's correction c replaces
   D[pos + a].  If c equals one of the next `window` draft tokens D[pos + a + 1 ..
   pos + a + window], the draft tokens before the first such match were spurious
-  and the draft realigns after the match: reading resumes just past it.
-  Otherwise D[pos + a] was a wrong token in the right place (a substitution) and
-  reading resumes at pos + a + 1.  window = 0 is the substitution reading alone.
+  and the draft realigns after the match: reading resumes just past it.  If the
+  round failed at its first token (a = 0) and c equals one of the `window` draft
+  tokens before pos (the nearest first), the previous round's realignment
+  skipped a token the draft had dropped before it: reading resumes just past
+  that match.  Otherwise D[pos + a] was a wrong token in the right place (a
+  substitution) and reading resumes at pos + a + 1.  window = 0 is the
+  substitution reading alone.
 """
 from __future__ import annotations
 
@@ -51,9 +55,13 @@ def recycle_draft(draft, pos: int, k: int, accepted: int, correction, window: in
     if correction is None or accepted >= k:
         return pos + k
     miss = pos + accepted
-    for j in range(miss + 1, min(miss + window, len(draft) - 1) + 1):
+    for j in range(miss + 1, min(miss + window, len(draft) - 1) + 1):      # spurious draft tokens
         if int(draft[j]) == int(correction):
             return j + 1
+    if accepted == 0:                                                     # a token the draft dropped
+        for j in range(min(pos, len(draft)) - 1, max(pos - window, 0) - 1, -1):
+            if int(draft[j]) == int(correction):
+                return j + 1
     return miss + 1
 
 

@@ -38,6 +38,15 @@ def test_recycle_cases():
     assert recycle_draft(D, 2, 3, 2, 99, 4) == 5                   # a round that started at pos 2
     assert recycle_draft(D, 4, 2, 1, 15, 4) == 6                   # miss at the last-but-one token
     assert recycle_draft(D, 5, 1, 0, 7, 4) == 6                    # miss at the last token
+    # a dropped token: the draft skips t3 (D = t0 t1 t2 t4 t5 ...); the first round misses t3 and
+    # takes the substitution reading (resume at 4); the next round fails at once with t4 = draft[3]
+    drop = [20, 21, 22, 24, 25, 26, 27]
+    assert recycle_draft(drop, 0, 4, 3, 23, 2) == 4
+    assert recycle_draft(drop, 4, 4, 0, 24, 2) == 4                # realigned: resume at 25
+    assert recycle_draft(drop, 4, 4, 0, 24, 0) == 5                # window 0: substitution reading
+    assert recycle_draft(drop, 4, 4, 1, 24, 2) == 6                # only a round that failed at once
+    assert recycle_draft([5, 9, 5, 1, 2, 3], 3, 2, 0, 5, 3) == 3   # the nearest earlier match
+    assert recycle_draft([5, 9, 6, 1, 2, 3], 3, 2, 0, 5, 2) == 4   # ... within the window only
 
 
 def _edit(seq, kind, at, vocab):
@@ -99,3 +108,19 @@ def test_adaptive_blocks_stop_at_the_flagged_token():
                                         16, 16, 0)
     assert fixed[:32] == want[:32]
     assert sum(ks) < sum(ks_f)
+
+
+def test_recycling_realigns_after_a_dropped_token():
+    """A token the draft dropped: the round that misses it takes the substitution reading, the
+    next one fails at once on the token the draft holds there, and the backward match puts the
+    draft back in step; the substitution reading alone stays one token ahead and keeps missing."""
+    model, caches0 = _model(27)
+    want = greedy_decode(model, [c.copy() for c in caches0], 8, 30)
+    assert len(set(want[:10])) == 10          # no repeats near the edit: every realignment is real
+    draft = _edit(want, "del", 5, model.hcfg.vocab)
+    unc = [0.0] * len(draft)
+    got1, ks1, acc1 = speculative_decode(model, [c.copy() for c in caches0], 8, draft, unc, 24, 1.0, 4, 4, 2)
+    got0, ks0, acc0 = speculative_decode(model, [c.copy() for c in caches0], 8, draft, unc, 24, 1.0, 4, 4, 0)
+    assert got1[:24] == got0[:24] == want[:24]
+    assert acc1[:4] == [4, 1, 0, 4]
+    assert acc0[:4] == [4, 1, 0, 0] and len(ks1) < len(ks0)

@@ -49,6 +49,10 @@ PHASES = ("qkv_projection", "attention", "o_proj")
 # the pages' figure for the same workload on another machine (context, not a target): 28 decoder
 # attention layers at bs1 over the 795 -> 925 clip, RTX 3050 Laptop, HF eager, in us per token
 PAGES_US_PER_TOKEN = 9033.0
+# logit gap below which two tokens count as tied in the batched speculative check: the one-token
+# and block paths give the same logits to about 1e-3 (logits of about 3) after 28 layers whose
+# outputs are rounded to 16 bits apart
+NEAR_TIE = 5e-3
 # HBM bytes per launch of each phase kernel from the FETCH_SIZE and WRITE_SIZE counters, each
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99994, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
@@ -589,7 +593,7 @@ def loop_leg(args, ga, si, np, torch, dev, to_dev, stream):
         kv.k[0, :, :P0], kv.v[0, :, :P0] = to_dev(kb, dtype), to_dev(vb, dtype)
         kv.lens.fill_(P0)
         kvs.append(kv)
-    del kvb
+    kvb_first = kvb
     base = torch.full((1,), P0, dtype=torch.int32, device=dev)
     acfg = ga.config(hidden=H, dtype=dtype)
     mcfg, mlast = ga.mlp_config(hidden=H, intermediate=I, dtype=dtype, out_dtype=dtype), ga.mlp_config(hidden=H, intermediate=I, dtype=dtype)
@@ -698,9 +702,168 @@ def loop_leg(args, ga, si, np, torch, dev, to_dev, stream):
                         "speedup_vs_greedy": round(ms_greedy / ms, 3)}
         print(f"[bench] loop speculative k={k}: {ms * 1000 / (R * k):.1f} us per committed token, "
               f"{ms * 1000 / R:.1f} us per round (ok {ok})", file=sys.stderr, flush=True)
-    del kvs, aw, mw, table, wlm
+    del kvs
+    torch.cuda.empty_cache()
+    out["batched"] = spec_batch_leg(ga, si, np, torch, dev, to_dev, kvb_first, aw, mw, table, gfin, wlm,
+                                    H, I, V, NL, dtype, sid)
+    del aw, mw, table, wlm
     torch.cuda.empty_cache()
     return out
+
+
+def spec_batch_leg(ga, si, np, torch, dev, to_dev, prompt_rows, aw, mw, table, gfin, wlm, H, I, V, NL, dtype, sid):
+    """Batched speculative decoding with per-sequence block lengths on the whole decoder ("Can CTC
+    make Qwen3-ASR faster?", section 07 and section 08 "Verifier, version 0"; section 12's fixed
+    block sizes against entropy-adaptive ones).  16 sequences with prompts of 150 to 795 positions
+    (the first rows of each layer's bs1 prompt); drafts are each sequence's greedy transcript with
+    seeded substitutions, insertions and deletions at a rate of 1 in 12, and uncertainties that flag
+    them.  Every round: the blocks of the active sequences packed into one mixed batch (embedding,
+    28 mixed decoder layers, argmax of every row, acceptance per sequence, crop), then the host picks
+    each sequence's next block length and recycles its draft.  Device time per round is taken
+    between events while the host has already enqueued the round (the GPU spins meanwhile), so it
+    holds no host gaps; committed tokens per second of that time, against greedy batched decoding
+    timed the same way."""
+    B, T, P_hi = 16, 48, 795
+    prompts = [150 + (P_hi - 150) * s // (B - 1) for s in range(B)]
+    cap = P_hi + T + 32
+    KMAX = 16
+    kvs = []
+    for l in range(NL):
+        kv = ga.KVLayer.empty(B, 8, cap, dtype=torch.float16, device=dev)
+        kb, vb = prompt_rows[l]
+        kd, vd = to_dev(kb, dtype), to_dev(vb, dtype)
+        for s_, P in enumerate(prompts):
+            kv.k[s_, :, :P], kv.v[s_, :, :P] = kd[:, :P], vd[:, :P]
+        kv.lens.copy_(torch.tensor(prompts, dtype=torch.int32))
+        kvs.append(kv)
+    base = torch.tensor(prompts, dtype=torch.int32, device=dev)
+    acfg = ga.config(hidden=H, dtype=dtype)
+    mcfg = ga.mlp_config(hidden=H, intermediate=I, dtype=dtype, out_dtype=dtype)
+    mlast = ga.mlp_config(hidden=H, intermediate=I, dtype=dtype)
+    hcfg = ga.head_config(hidden=H, vocab=V, dtype=dtype)
+    ws = ga.decoder_layer_workspace(acfg, mcfg, B * KMAX, cap, device=dev)
+    hws = ga.lm_head_workspace(hcfg, B * KMAX, device=dev)
+    xa = torch.empty((B * KMAX, H), dtype=torch.float16, device=dev)
+    xb = torch.empty((B * KMAX, H), dtype=torch.float16, device=dev)
+    hf = torch.empty((B * KMAX, H), dtype=torch.float32, device=dev)
+    tgt = torch.empty(B * KMAX, dtype=torch.int32, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    new_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    first = [(7919 * (s_ + 1)) % V for s_ in range(B)]
+
+    def run_block(ids, sizes, slots):
+        rows = sum(sizes)
+        ga.embed(table, ids, xa[:rows])
+        x = xa
+        for l in range(NL):
+            last = l == NL - 1
+            o = hf if last else (xb if x is xa else xa)
+            ga.decoder_layer_mixed(acfg, aw[l], mlast if last else mcfg, mw[l], kvs[l], x[:rows], sizes, o[:rows], ws,
+                                   slots=slots)
+            x = o
+        ga.lm_head_argmax(hcfg, gfin, wlm, hf[:rows], tgt[:rows], hws)
+
+    def timed(enqueue):
+        """Device time of the enqueued work, free of host gaps."""
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(10_000_000)
+        e0.record()
+        enqueue()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # greedy transcripts (untimed), then greedy batched decoding timed step by step
+    ga.kv_crop(kvs, base)
+    cur = torch.tensor(first, dtype=torch.int32, device=dev)
+    allslots = torch.arange(B, dtype=torch.int32, device=dev)
+    trans, gaps = [], []
+    w32, g32 = wlm.float(), gfin.float()
+    for _ in range(T + 24):
+        run_block(cur, [1] * B, allslots)
+        cur = tgt[:B].clone()
+        trans.append(cur.cpu().tolist())
+        # the top-two logit gap of every greedy token (fp32 logits, for the check below)
+        y = hf[:B] * torch.rsqrt((hf[:B] * hf[:B]).mean(dim=1, keepdim=True) + 1e-6) * g32
+        top = torch.topk(y @ w32.t(), 2, dim=1).values
+        gaps.append((top[:, 0] - top[:, 1]).cpu().tolist())
+    del w32
+    trans = [[trans[t][s_] for t in range(T + 24)] for s_ in range(B)]
+    ga.kv_crop(kvs, base)
+    cur = torch.tensor(first, dtype=torch.int32, device=dev)
+    ms_greedy = 0.0
+    for t in range(T):
+        ms_greedy += timed(lambda: run_block(cur, [1] * B, allslots))
+        cur = tgt[:B].clone()
+    greedy_ok = all(x == trans[s_][T - 1] for s_, x in enumerate(cur.cpu().tolist()))
+    tok_greedy = B * T / (ms_greedy * 1e-3)
+    res = {"workload": f"batched speculative decoding, {B} sequences, prompts {prompts[0]}..{prompts[-1]}, "
+                       f"{T} tokens each, 28 decoder layers + head (151,936 ids), fp16; drafts: greedy transcripts "
+                       "with seeded substitutions, insertions and deletions (1 in 12) and uncertainties flagging them",
+           "unit": "committed tokens/s (device time)",
+           "greedy": {"tokens_per_s": round(tok_greedy, 1), "ms": round(ms_greedy, 3), "ok": greedy_ok}}
+    print(f"[bench] batched greedy: {tok_greedy:.0f} tok/s ({ms_greedy:.2f} ms for {B}x{T}; ok {greedy_ok})",
+          file=sys.stderr, flush=True)
+    drafts = [si.draft_with_edits(sid, s_, trans[s_], 1 / 12, V) for s_ in range(B)]
+    variants = {"fixed_k8": (8, 8, 0, 1e30), "fixed_k8_recycle2": (8, 8, 2, 1e30), "adaptive_2_16_recycle2": (2, 16, 2, 1.0)}
+    for name, (kmin, kmax, window, tau) in variants.items():
+        ga.kv_crop(kvs, base)
+        pos, last = [0] * B, list(first)
+        got = [[] for _ in range(B)]
+        done = [False] * B
+        ms, rounds, rows_total, acc_total = 0.0, 0, 0, 0
+        while not all(done):
+            act = [s_ for s_ in range(B) if not done[s_]]
+            kk = [ga.next_block_len(drafts[s_][1][pos[s_]:], tau, kmin, kmax) for s_ in act]
+            dr = [(drafts[s_][0][pos[s_]:] + [-1] * k)[:k] for s_, k in zip(act, kk)]
+            ids = torch.tensor([t for s_, d, k in zip(act, dr, kk) for t in [last[s_]] + d[:k - 1]],
+                               dtype=torch.int32, device=dev)
+            dflat = torch.tensor([t for d in dr for t in d], dtype=torch.int32, device=dev)
+            slots = torch.tensor(act, dtype=torch.int32, device=dev)
+
+            def enqueue():
+                run_block(ids, kk, slots)
+                ga.accept_greedy_mixed(dflat, tgt[:sum(kk)], kk, kvs[0].lens, acc[:len(act)], nxt[:len(act)],
+                                       new_lens, slots=slots)
+                ga.kv_crop(kvs, new_lens)
+            ms += timed(enqueue)
+            A, N = acc[:len(act)].cpu().tolist(), nxt[:len(act)].cpu().tolist()
+            for i, s_ in enumerate(act):
+                k, a = kk[i], A[i]
+                got[s_] += dr[i][:a] + ([] if a == k else [N[i]])
+                pos[s_] = ga.recycle_draft(drafts[s_][0], pos[s_], k, a, None if a == k else N[i], window)
+                last[s_] = got[s_][-1]
+                done[s_] = len(got[s_]) >= T
+            rounds += 1
+            rows_total += sum(kk)
+            acc_total += sum(A)
+        # greedy exactness: each transcript equals the greedy one, or first leaves it at a token
+        # whose two best logits lie closer than the rounding of the two computations can tell
+        # apart (the block path and the one-token path round each layer's 16-bit output apart)
+        exact, ties = 0, []
+        for s_ in range(B):
+            dv = next((t for t in range(T) if got[s_][t] != trans[s_][t]), None)
+            if dv is None:
+                exact += 1
+            else:
+                ties.append({"seq": s_, "pos": dv, "greedy_top2_gap": round(gaps[dv][s_], 6)})
+        ok = all(t["greedy_top2_gap"] < NEAR_TIE for t in ties)
+        committed = sum(len(g) for g in got)
+        tps = committed / (ms * 1e-3)
+        res[name] = {"tokens_per_s": round(tps, 1), "ms": round(ms, 3), "rounds": rounds,
+                     "committed": committed, "rows_verified": rows_total,
+                     "committed_per_row": round(committed / rows_total, 3), "ok": ok,
+                     "exact_sequences": exact, "near_tie_divergences": ties,
+                     "speedup_vs_greedy": round(tps / tok_greedy, 3)}
+        print(f"[bench] batched speculative {name}: {tps:.0f} tok/s, {rounds} rounds, "
+              f"{committed / rows_total:.2f} committed per verified row, {exact}/{B} transcripts exact, "
+              f"other divergences at near ties {[t['greedy_top2_gap'] for t in ties]} (ok {ok})",
+              file=sys.stderr, flush=True)
+    del kvs
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_model():

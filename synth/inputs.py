@@ -243,3 +243,36 @@ def head_weights(stream: int, hidden: int, vocab: int, dtype: str) -> dict:
     return dict(embed=normal_bits(stream, 0, T_EMBED, 0, (vocab, hidden), 1.0, 0.0, dtype),
                 final_norm_w=normal_bits(stream, 0, T_GAMMA_FINAL, 0, (hidden,), 0.02, 1.0, dtype),
                 w_lm=normal_bits(stream, 0, T_WLM, 0, (vocab, hidden), 0.02, 0.0, dtype))
+
+
+# ------------------------------------------------------------------ synthetic drafts
+
+T_DRAFT = 21
+
+
+def draft_with_edits(stream: int, seq: int, transcript, rate: float, vocab: int, u_low: float = 0.3,
+                     u_high: float = 3.0):
+    """A stand-in for a CTC draft of `transcript` (the target's greedy tokens): each position is
+    kept, or with probability `rate` substituted, preceded by an inserted token, or dropped (one
+    third each), seeded by (stream, seq).  The per-token uncertainty is exponential with mean
+    u_low, and u_high plus that noise at the draft token where an edit lands (the draft model
+    knows its uncertain frames).  Returns (draft ids, uncertainties) as lists."""
+    g = rng_for(stream, 0, T_DRAFT, seq)
+    draft, unc = [], []
+    for t in transcript:
+        t = int(t)
+        r = g.random()
+        noise = float(g.exponential(u_low))
+        if r < rate / 3:                         # substitution
+            draft.append((t + 1 + int(g.integers(0, vocab - 1))) % vocab)
+            unc.append(u_high + noise)
+        elif r < 2 * rate / 3:                   # an inserted token before t
+            draft += [int(g.integers(0, vocab)), t]
+            unc += [u_high + noise, float(g.exponential(u_low))]
+        elif r < rate:                           # t dropped: the next token carries the flag
+            if unc:
+                unc[-1] = max(unc[-1], u_high + noise)
+        else:
+            draft.append(t)
+            unc.append(noise)
+    return draft, unc

@@ -59,6 +59,9 @@ CASES = {
     "waves_g4": (16, 4, [3, 1, 1, 7, 2], [100, 5, 260, 33, 1]),
     "chunked_g8": (16, 2, [5, 1, 2, 9], [12, 290, 0, 140]),
     "chunked_g1": (8, 8, [1, 2, 6, 1, 1], [61, 3, 199, 0, 240]),
+    # more than 64 rows: several row tiles of the projections
+    "waves_g2_rows140": (16, 8, [9, 1, 16, 4, 12, 7, 1, 16, 3, 10, 14, 2, 8, 16, 5, 16],
+                         [150, 193, 236, 279, 0, 280, 231, 120, 100, 50, 283, 270, 17, 1, 90, 200]),
 }
 
 

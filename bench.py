@@ -54,12 +54,13 @@ PAGES_US_PER_TOKEN = 9033.0
 # outputs are rounded to 16 bits apart
 NEAR_TIE = 5e-3
 # HBM bytes per launch of each phase kernel from the FETCH_SIZE and WRITE_SIZE counters, each
-# scaled by what that counter reads for a 1 GiB device copy (fetch x1.99994, write x1.000), and
+# scaled by what that counter reads for a 1 GiB device copy (fetch x1.99995, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "86b4dc98ed0c9ee0282ed4551f3c80a463875caaa6a1570833e4c8467d5b1b77",
-    "bs1": {"qkv_projection": 8583097, "attention": 4048563, "o_proj": 4862001},
-    "b64": {"qkv_projection": 11077731, "attention": 230242802, "o_proj": 8722569},
+    "sources_sha256": "7eda89780d4af1960861499c6162c4fcfe6860d8273ca2be8cb396abdc7adc46",
+    "bs1": {"qkv_projection": 8577996, "attention": 4057708, "o_proj": 4851740},
+    "b64": {"qkv_projection": 11086773, "attention": 230490285, "o_proj": 8708341},
+    "b64_fp8": {"qkv_projection": 11086773, "attention": 120117138, "o_proj": 8708341},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",
@@ -98,6 +99,8 @@ def parse():
                    help="run only this many bs1 steps eagerly (for profilers) and exit")
     p.add_argument("--profile-batched", type=int, default=0,
                    help="run only this many batch-64 steps eagerly (for profilers) and exit")
+    p.add_argument("--profile-verify", type=int, default=0,
+                   help="run only this many bs1 verify blocks per k (and hidden-2048 verify blocks) eagerly and exit")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="only run three device-to-device copies of this many MiB (counter calibration)")
     return p.parse_args()
@@ -174,6 +177,8 @@ def main():
 
     if args.profile_batched:
         batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
+        if not args.no_fp8:
+            batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=True)
         print(json.dumps({"profile_batched": args.profile_batched}))
         return
 
@@ -203,6 +208,16 @@ def main():
     def step_calls(s):
         for l in range(NL):
             ga.layer_decode(cfg, weights[l], kvs[l], xs[s, l], outs[l], ws, host_lens=[P0 + s])
+
+    if args.profile_verify:
+        verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_lens, H, NL, dtype, sid, P0,
+                   profile=args.profile_verify)
+        if not args.no_wide:
+            del weights, kvs
+            torch.cuda.empty_cache()
+            wide_batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
+        print(json.dumps({"profile_verify": args.profile_verify}))
+        return
 
     if args.profile_steps:
         for s in range(args.profile_steps):
@@ -422,12 +437,14 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False):
                         + ", hidden 1024, KV U{200..1500}",
             "value": round(tok_s, 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4), "steps": n,
             "step_roofline": sr, "ok": ok,
-            "roofline": roofline(mean_us, bphase, None if fp8 else measured_traffic("b64"))}
+            "roofline": roofline(mean_us, bphase, measured_traffic("b64_fp8" if fp8 else "b64"))}
 
 
-def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_lens, H, NL, dtype, sid, P0):
+def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_lens, H, NL, dtype, sid, P0,
+               profile=0):
     """k-token verify blocks at bs1 from the committed 795: 28 layer_verify calls captured in one
-    graph, replayed with a crop back to 795 after each (the crop outside the timed events)."""
+    graph, replayed with a crop back to 795 after each (the crop outside the timed events).  With
+    ``profile``: that many blocks per k, eagerly, for profilers."""
     out = {"workload": "28-layer verify block, bs1, fp16, hidden 1024, committed KV 795, k candidates",
            "unit": "us per 28-layer block"}
     ws_v = ga.alloc_workspace(cfg, 16, CAP_BS1, device=dev)
@@ -437,6 +454,13 @@ def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_l
         ov = torch.empty((NL, 1, k, H), dtype=torch.float32, device=dev)
         ga.kv_crop(kvs, base_lens)
         torch.cuda.synchronize()
+        if profile:
+            for _ in range(profile):
+                for l in range(NL):
+                    ga.layer_verify(cfg, weights[l], kvs[l], xv[l], ov[l], ws_v, host_lens=[P0])
+                ga.kv_crop(kvs, base_lens)
+            torch.cuda.synchronize()
+            continue
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for l in range(NL):
@@ -545,6 +569,12 @@ def wide_batched_leg(args, ga, si, np, torch, dev, to_dev, stream):
         for l in range(NL):
             ga.layer_verify(cfg, weights[l], kvs[l], xv[l], outv[l], wsv, slots=slots, host_lens=hlv)
 
+    if args.profile_verify:
+        for _ in range(args.profile_verify):
+            verify_calls()
+            ga.kv_crop(kvs, base)
+        torch.cuda.synchronize()
+        return None
     ms_dec, ok_d = timed(decode_calls, max(10, args.steps // 8))
     ms_ver, ok_v = timed(verify_calls, max(10, args.steps // 8))
     bytes_step = NL * layer_bytes(H, 16, 8, 128, lens.tolist(), B)

@@ -339,7 +339,7 @@ namespace {
 int check_mlp(const asr_mlp_config *c) {
   if (!c) return ASR_EINVAL;
   if (c->hidden <= 0 || c->intermediate <= 0) return ASR_EINVAL;
-  if (c->hidden % 256 != 0 || c->hidden > 4096) return ASR_EUNSUPPORTED;
+  if (c->hidden % 256 != 0 || c->hidden > 2048) return ASR_EUNSUPPORTED;
   if (c->intermediate % 256 != 0 || c->intermediate > 16384) return ASR_EUNSUPPORTED;
   if (c->dtype != ASR_F16 && c->dtype != ASR_BF16) return ASR_EUNSUPPORTED;
   if (c->in_dtype != ASR_F32 && c->in_dtype != c->dtype) return ASR_EUNSUPPORTED;

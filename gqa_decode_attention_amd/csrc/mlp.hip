@@ -5,17 +5,19 @@
 // 27.5% of decode and memory-bound at 529 MB/token; section 07 "Norms are real
 // money at this size").
 //
-// Three stream-ordered kernels:
-//   k_mlp_norm  y = h * g_post / sqrt(mean(h^2) + eps) per row, stored as two
-//               16-bit terms (hi = rne(y), lo = rne(y - hi)) in the matrix-core
-//               operand tiling [2][H / 32][rows][32]
-//   k_mlp_up    gate = W_gate y and up = W_up y on v_mfma_f32_16x16x32 (W exact
-//               16-bit, y as hi + lo), act = silu(gate) * up, stored as hi / lo
-//               tiles [2][I / 32][rows][32]
+// Two stream-ordered kernels:
+//   k_mlp_up    y = h * g_post / sqrt(mean(h^2) + eps) for the block's 16 rows,
+//               formed in registers from the h slice each lane loads as its
+//               operand (the rows' sums of squares exchanged through LDS), as
+//               two 16-bit terms (hi = rne(y), lo = rne(y - hi)); gate = W_gate y
+//               and up = W_up y on v_mfma_f32_16x16x32 (W exact 16-bit);
+//               act = silu(gate) * up, stored as hi / lo tiles [2][I / 32][rows][32]
 //   k_mlp_down  out = h + W_down act (act as hi + lo)
 // A block owns 16 output features x 16 rows; its 8 waves split the
 // contraction, request every operand of a batch before the products, and add
 // their partial tiles in LDS.  Blocks of one feature tile sit on one XCD.
+// (k_mlp_norm, the same normalisation as its own pass into the operand tiling
+// [2][H / 32][rows][32], serves the model head.)
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
@@ -70,15 +72,15 @@ __global__ __launch_bounds__(256) void k_mlp_norm(MlpArgs A) {
 
 // the wave's share [k0, k0 + kw * 32) of the contraction: A operand rows of W at
 // feature o, B operand hi / lo tiles of `hl` (plane = K * rows) at row n
-template <int DT, int NM>
+template <int DT, int NM, int BATCH = kMlpBatch>
 __device__ __forceinline__ void mlp_products(const uint16_t *const (&w)[NM], int K, const uint16_t *hl, int rows,
                                              int o, int n, int k0, int kw, f32x4_t (&acc)[NM]) {
   const int lane = lane_id(), g4 = lane / 16;
   const size_t plane = (size_t)K * rows;
-  for (int s0 = 0; s0 < kw; s0 += kMlpBatch) {
-    uint4 wa[NM][kMlpBatch], hi[kMlpBatch], lo[kMlpBatch];
+  for (int s0 = 0; s0 < kw; s0 += BATCH) {
+    uint4 wa[NM][BATCH], hi[BATCH], lo[BATCH];
 #pragma unroll
-    for (int s = 0; s < kMlpBatch; ++s) {
+    for (int s = 0; s < BATCH; ++s) {
       const int kk = k0 + min(s0 + s, kw - 1) * 32;   // past the share: a repeated step, weight zero below
 #pragma unroll
       for (int m = 0; m < NM; ++m) wa[m][s] = ld16_stream(w[m] + (size_t)o * K + kk + g4 * 8);
@@ -88,29 +90,81 @@ __device__ __forceinline__ void mlp_products(const uint16_t *const (&w)[NM], int
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any product
 #pragma unroll
-    for (int s = 0; s < kMlpBatch; ++s) {
-      if (s0 + s >= kw) break;
+    for (int s = 0; s < BATCH; ++s) {
+      if (s0 + s < kw) {   // (a predicate, not a break: the batch stays unrolled, in registers)
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        acc[m] = mfma16x16x32<DT>(wa[m][s], hi[s], acc[m]);
-        acc[m] = mfma16x16x32<DT>(wa[m][s], lo[s], acc[m]);
+        for (int m = 0; m < NM; ++m) {
+          acc[m] = mfma16x16x32<DT>(wa[m][s], hi[s], acc[m]);
+          acc[m] = mfma16x16x32<DT>(wa[m][s], lo[s], acc[m]);
+        }
       }
     }
   }
 }
 
-template <int DT>
+// KW: 32-wide contraction steps per wave (H / 32 / 8: 4 at hidden 1024, 8 at 2048)
+template <int DT, int KW>
 __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_up(MlpArgs A) {
   __shared__ f32x4_t s_c[2][kMlpWaves][kWave];
+  __shared__ float s_ss[kMlpWaves][16];
   const int wave = wave_id(), lane = lane_id();
   const int i16 = lane % 16, g4 = lane / 16;
   const int rtiles = (A.rows + 15) / 16;
   const MlpTile tm = mlp_tile(blockIdx.x, rtiles);
   const int o0 = tm.col * 16, nb = tm.row * 16;
-  const int kw = A.H / 32 / kMlpWaves;
-  const uint16_t *const w[2] = {A.w_gate, A.w_up};
+  const int n = min(nb + i16, A.rows - 1);   // rows past the call repeat the last (not stored)
+  const int k0 = wave * KW * 32 + g4 * 8;    // this lane's 8 columns of each step: k0 + 32 s ..
+  // every load before any wait: the gate and up rows of feature o0 + i16, then the lane's slice
+  // of row n of h and the post-norm gains of the same columns
+  uint4 wa[2][KW], gv[KW];
+  float hv[KW][8];
+#pragma unroll
+  for (int st = 0; st < KW; ++st) {
+    wa[0][st] = ld16_stream(A.w_gate + (size_t)(o0 + i16) * A.H + k0 + 32 * st);
+    wa[1][st] = ld16_stream(A.w_up + (size_t)(o0 + i16) * A.H + k0 + 32 * st);
+  }
+#pragma unroll
+  for (int st = 0; st < KW; ++st) {
+    const size_t i = (size_t)n * A.H + k0 + 32 * st;
+    if (A.in_f32) {
+      const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(A.h) + i);
+      const float4 b = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(A.h) + i + 4);
+      hv[st][0] = a.x; hv[st][1] = a.y; hv[st][2] = a.z; hv[st][3] = a.w;
+      hv[st][4] = b.x; hv[st][5] = b.y; hv[st][6] = b.z; hv[st][7] = b.w;
+    } else {
+      unpack8<DT>(ld16(reinterpret_cast<const uint16_t *>(A.h) + i), hv[st]);
+    }
+    gv[st] = ld16(A.g_post + k0 + 32 * st);
+  }
+  // the row's sum of squares: this lane's slice, the 4 lanes of row n, then the 8 waves
+  float ss = 0.f;
+#pragma unroll
+  for (int st = 0; st < KW; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += hv[st][e] * hv[st][e];
+  ss = xsum<16>(ss);
+  ss = xsum<32>(ss);
+  if (g4 == 0) s_ss[wave][i16] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int wv = 0; wv < kMlpWaves; ++wv) tot += s_ss[wv][i16];
+  const float inv = 1.0f / sqrtf(tot / (float)A.H + A.eps);
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  mlp_products<DT, 2>(w, A.H, A.y_hl, A.rows, o0 + i16, min(nb + i16, A.rows - 1), wave * kw * 32, kw, acc);
+#pragma unroll
+  for (int st = 0; st < KW; ++st) {
+    float gf[8], y[8];
+    unpack8<DT>(gv[st], gf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = hv[st][e] * gf[e] * inv;
+    uint4 hi, lo;
+    split8<DT>(y, hi, lo);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      acc[m] = mfma16x16x32<DT>(wa[m][st], hi, acc[m]);
+      acc[m] = mfma16x16x32<DT>(wa[m][st], lo, acc[m]);
+    }
+  }
   s_c[0][wave][lane] = acc[0];
   s_c[1][wave][lane] = acc[1];
   __syncthreads();
@@ -122,22 +176,22 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_up(MlpArgs A) {
       gsum[0] += a[0]; gsum[1] += a[1]; gsum[2] += a[2]; gsum[3] += a[3];
       usum[0] += b[0]; usum[1] += b[1]; usum[2] += b[2]; usum[3] += b[3];
     }
-    const int n = nb + i16;
-    if (n < A.rows) {
-      uint16_t hv[4], lv[4];
+    const int row = nb + i16;
+    if (row < A.rows) {
+      uint16_t hv16[4], lv16[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float gt = gsum[j];
         const float act = gt / (1.f + __expf(-gt)) * usum[j];
-        hv[j] = rne16<DT>(act);
-        lv[j] = rne16<DT>(act - cvt16<DT>(hv[j]));
+        hv16[j] = rne16<DT>(act);
+        lv16[j] = rne16<DT>(act - cvt16<DT>(hv16[j]));
       }
-      // features o0 + 4 g4 .. + 3 of row n: adjacent in the tiling
-      const size_t i = tiled(o0 + 4 * g4, n, A.rows), plane = (size_t)A.I * A.rows;
+      // features o0 + 4 g4 .. + 3 of the row: adjacent in the tiling
+      const size_t i = tiled(o0 + 4 * g4, row, A.rows), plane = (size_t)A.I * A.rows;
       *reinterpret_cast<uint2 *>(A.a_hl + i) =
-          make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+          make_uint2((uint32_t)hv16[0] | ((uint32_t)hv16[1] << 16), (uint32_t)hv16[2] | ((uint32_t)hv16[3] << 16));
       *reinterpret_cast<uint2 *>(A.a_hl + plane + i) =
-          make_uint2((uint32_t)lv[0] | ((uint32_t)lv[1] << 16), (uint32_t)lv[2] | ((uint32_t)lv[3] << 16));
+          make_uint2((uint32_t)lv16[0] | ((uint32_t)lv16[1] << 16), (uint32_t)lv16[2] | ((uint32_t)lv16[3] << 16));
     }
   }
 }
@@ -160,7 +214,8 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_down(MlpArgs A) {
   const int kw = A.I / 32 / kMlpWaves;
   const uint16_t *const w[1] = {A.w_down};
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  mlp_products<DT, 1>(w, A.I, A.a_hl, A.rows, o0 + i16, min(n, A.rows - 1), wave * kw * 32, kw, acc);
+  // batches of 12 steps: the whole share at intermediate 3072, one wait per batch
+  mlp_products<DT, 1, 12>(w, A.I, A.a_hl, A.rows, o0 + i16, min(n, A.rows - 1), wave * kw * 32, kw, acc);
   s_c[wave][lane] = acc[0];
   __syncthreads();
   if (wave == 0 && n < A.rows) {
@@ -315,10 +370,20 @@ template <int DT>
 hipError_t mlp_launch(const MlpArgs &a, hipStream_t s, hipEvent_t *ev) {
   hipError_t e;
   const int rtiles = (a.rows + 15) / 16;
-  if ((e = launch(k_mlp_norm<DT>, dim3(a.rows), dim3(256), s, ev, 0, a)) != hipSuccess) return e;
-  if ((e = launch(k_mlp_up<DT>, dim3(a.I / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 1, a)) != hipSuccess)
-    return e;
-  return launch(k_mlp_down<DT>, dim3(a.H / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 2, a);
+  MlpKernel up = nullptr;
+  switch (a.H / 32 / kMlpWaves) {
+    case 1: up = k_mlp_up<DT, 1>; break;
+    case 2: up = k_mlp_up<DT, 2>; break;
+    case 3: up = k_mlp_up<DT, 3>; break;
+    case 4: up = k_mlp_up<DT, 4>; break;
+    case 5: up = k_mlp_up<DT, 5>; break;
+    case 6: up = k_mlp_up<DT, 6>; break;
+    case 7: up = k_mlp_up<DT, 7>; break;
+    case 8: up = k_mlp_up<DT, 8>; break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = launch(up, dim3(a.I / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 0, a)) != hipSuccess) return e;
+  return launch(k_mlp_down<DT>, dim3(a.H / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 1, a);
 }
 
 template <int DT>

@@ -305,7 +305,7 @@ int asr_kv_crop(const asr_kv_layer *layers, int32_t n_layers, const int32_t *new
  *   out = h + W_down (silu(W_gate y) * (W_up y)),   silu(u) = u / (1 + e^-u)
  * All arithmetic is fp32; matrix-core operands that are fp32 values (y and
  * silu(gate) * up) are split into two 16-bit terms.  Supported: hidden and
- * intermediate multiples of 256 (hidden at most 4096, intermediate at most
+ * intermediate multiples of 256 (hidden at most 2048, intermediate at most
  * 16384), dtype ASR_F16 or ASR_BF16, 1 to 2048 rows.
  */
 typedef struct asr_mlp_config {
@@ -315,8 +315,9 @@ typedef struct asr_mlp_config {
   int32_t dtype;         /* ASR_F16 or ASR_BF16: the weights */
   int32_t in_dtype;      /* h: ASR_F32 (the attention block's fp32 output) or dtype */
   int32_t out_dtype;     /* ASR_F32 or dtype */
-  hipEvent_t *phase_events;  /* diagnostics, NULL normally: 6 caller-created events that receive the
-                                start and end stamps of the norm, gate/up and down kernels */
+  hipEvent_t *phase_events;  /* diagnostics, NULL normally: 4 caller-created events that receive the
+                                start and end stamps of the normalising gate/up kernel, then of the
+                                down kernel */
 } asr_mlp_config;
 
 /* One layer's MLP weights (device, elements of dtype, row-major [out][in]). */

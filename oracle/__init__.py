@@ -6,3 +6,4 @@ from .decoder_layer import MlpConfig, MlpWeights, decoder_layer_decode, decoder_
 from .spec_loop import (HeadConfig, TinyModel, accept_greedy, argmax_first, embed, greedy_decode, lm_head_logits,
                         speculative_round)
 from .spec_policy import next_block_len, recycle_draft, speculative_decode
+from .paged_kv import STATUS_BAD_PAGE, PagedKV, on_pages

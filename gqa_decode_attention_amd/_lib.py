@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libasr_attn.so")
 
 F16, BF16, F32, FP8_E4M3 = 0, 1, 2, 3
 DISPATCH_AUTO, DISPATCH_MULTI, DISPATCH_FUSED = 0, 1, 2
-STATUS_CAPACITY, STATUS_CROP_GROW, STATUS_SYNC_TIMEOUT, STATUS_BAD_SLOT = 1, 2, 4, 8
+STATUS_CAPACITY, STATUS_CROP_GROW, STATUS_SYNC_TIMEOUT, STATUS_BAD_SLOT, STATUS_BAD_PAGE = 1, 2, 4, 8, 16
 
 ERRORS = {0: "ASR_OK", -1: "ASR_EINVAL", -2: "ASR_EUNSUPPORTED", -3: "ASR_ECAPACITY",
           -4: "ASR_EWORKSPACE", -5: "ASR_EHIP", -6: "ASR_ESCRATCH"}
@@ -54,7 +54,9 @@ class AsrKvLayer(ctypes.Structure):
                 ("status", ctypes.c_void_p), ("batch_cap", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
 class AsrMlpConfig(ctypes.Structure):
@@ -206,22 +208,41 @@ class KVLayer:
     """One layer's cache: k, v [batch_cap][nkv][capacity][d], lens [batch_cap] int32, status [1] int32.
 
     16-bit caches are float16 / bfloat16 tensors; an FP8 cache is uint8 tensors of E4M3 codes
-    with fp32 per-kv-head scales ``k_scale``, ``v_scale`` [nkv] on the device."""
+    with fp32 per-kv-head scales ``k_scale``, ``v_scale`` [nkv] on the device.  A paged cache
+    (``block_table`` [batch_cap][pages_per_seq] int32 on the device) has pools
+    k, v [num_pages][nkv][page_size][d] instead."""
 
-    def __init__(self, k, v, lens, status=None, k_scale=None, v_scale=None):
+    def __init__(self, k, v, lens, status=None, k_scale=None, v_scale=None, block_table=None):
         assert k.shape == v.shape and k.dim() == 4 and k.dtype == v.dtype
-        assert lens.dtype == torch.int32 and lens.numel() == k.shape[0]
+        assert lens.dtype == torch.int32
         self.k, self.v, self.lens, self.status = k, v, lens, status
-        self.k_scale, self.v_scale = k_scale, v_scale
+        self.k_scale, self.v_scale, self.block_table = k_scale, v_scale, block_table
         dt = {torch.float16: F16, torch.bfloat16: BF16, torch.uint8: FP8_E4M3}[k.dtype]
         if dt == FP8_E4M3:
             assert k_scale is not None and v_scale is not None
             assert k_scale.dtype == torch.float32 and v_scale.dtype == torch.float32
+        if block_table is None:
+            assert lens.numel() == k.shape[0]
+            batch_cap, capacity, paged = k.shape[0], k.shape[2], (None, 0, 0, 0)
+        else:
+            assert block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+            assert lens.numel() == block_table.shape[0]
+            batch_cap, pps = block_table.shape
+            capacity = pps * k.shape[2]
+            paged = (block_table.data_ptr(), k.shape[2], pps, k.shape[0])
         self.c = AsrKvLayer(k.data_ptr(), v.data_ptr(), lens.data_ptr(),
                             None if status is None else status.data_ptr(),
-                            k.shape[0], k.shape[2], k.shape[1], k.shape[3], dt,
+                            batch_cap, capacity, k.shape[1], k.shape[3], dt,
                             None if k_scale is None else k_scale.data_ptr(),
-                            None if v_scale is None else v_scale.data_ptr())
+                            None if v_scale is None else v_scale.data_ptr(), *paged)
+
+    @property
+    def batch_cap(self) -> int:
+        return self.c.batch_cap
+
+    @property
+    def capacity(self) -> int:
+        return self.c.capacity
 
     @classmethod
     def empty(cls, batch_cap, n_kv_heads, capacity, head_dim=128, dtype=torch.float16, device="cuda",
@@ -230,6 +251,16 @@ class KVLayer:
         return cls(torch.zeros(shape, dtype=dtype, device=device), torch.zeros(shape, dtype=dtype, device=device),
                    torch.zeros(batch_cap, dtype=torch.int32, device=device),
                    torch.zeros(1, dtype=torch.int32, device=device), k_scale, v_scale)
+
+    @classmethod
+    def paged(cls, num_pages, n_kv_heads, page_size, block_table, head_dim=128, dtype=torch.float16,
+              device="cuda"):
+        """A zeroed pool of num_pages pages and the given page table [batch_cap][pages_per_seq]."""
+        shape = (num_pages, n_kv_heads, page_size, head_dim)
+        bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
+        return cls(torch.zeros(shape, dtype=dtype, device=device), torch.zeros(shape, dtype=dtype, device=device),
+                   torch.zeros(bt.shape[0], dtype=torch.int32, device=device),
+                   torch.zeros(1, dtype=torch.int32, device=device), block_table=bt)
 
 
 def workspace_bytes(cfg: AsrAttnConfig, max_rows: int, capacity: int) -> int:

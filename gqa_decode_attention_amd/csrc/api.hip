@@ -50,6 +50,14 @@ int check_kv(const asr_kv_layer *kv, const asr_attn_config *c) {
   if (kv->dtype == ASR_FP8_E4M3 && (!kv->k_scale || !kv->v_scale)) return ASR_EINVAL;
   if (kv->n_kv_heads <= 0) return ASR_EINVAL;
   if (kv->capacity > kMaxChunks * kMaxSplit) return ASR_EUNSUPPORTED;
+  if (kv->block_table) {
+    // a paged pool: 16-bit elements, power-of-two pages of 16 .. 1024 rows
+    const int P = kv->page_size;
+    if (P < 16 || P > 1024 || (P & (P - 1)) != 0) return ASR_EUNSUPPORTED;
+    if (kv->pages_per_seq <= 0 || kv->num_pages <= 0) return ASR_EINVAL;
+    if ((long long)kv->pages_per_seq * P != kv->capacity) return ASR_EINVAL;
+    if (kv->dtype == ASR_FP8_E4M3) return ASR_EUNSUPPORTED;
+  }
   if (c) {
     if (kv->n_kv_heads != c->n_kv_heads) return ASR_EINVAL;
     if (kv->dtype != c->dtype && kv->dtype != ASR_FP8_E4M3) return ASR_EINVAL;
@@ -156,7 +164,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
     for (int b = 0; b < B; ++b)
       if (host_lens[b] < 0 || (long long)host_lens[b] + nb(b) > kv->capacity) return ASR_ECAPACITY;
   }
-  if (n_per_seq && cfg->dispatch == ASR_DISPATCH_FUSED) return ASR_EUNSUPPORTED;
+  if ((n_per_seq || kv->block_table) && cfg->dispatch == ASR_DISPATCH_FUSED) return ASR_EUNSUPPORTED;
   // mixed blocks run on the many-row kernels (matrix-core projections) whatever the row count
 
   const bool kv8 = kv->dtype == ASR_FP8_E4M3;
@@ -181,6 +189,12 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.vc = static_cast<uint16_t *>(kv->v);
   a.lens = kv->lens;
   a.status = kv->status;
+  a.ptab = kv->block_table;
+  a.pps = kv->block_table ? kv->pages_per_seq : 0;
+  a.npages = kv->block_table ? kv->num_pages : 0;
+  a.psz = kv->block_table ? kv->page_size : 0;
+  a.plog = 0;
+  while (a.psz > (1 << a.plog)) ++a.plog;
   a.out = out;
   char *base = static_cast<char *>(ws);
   a.qkv = reinterpret_cast<float *>(base + lay.qkv);
@@ -205,7 +219,8 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.eps = cfg->rms_eps;
   a.theta = cfg->rope_theta;
   a.out_f32 = cfg->out_dtype == ASR_F32;
-  a.mfma = rows > kVectorRows || n_per_seq != nullptr;
+  // mixed blocks and paged caches run on the many-row kernels whatever the row count
+  a.mfma = rows > kVectorRows || n_per_seq != nullptr || kv->block_table != nullptr;
   a.oproj_split = 0;
   a.vm_items = 0;
   a.kv8 = kv8;

@@ -460,11 +460,20 @@ constexpr float kRescaleLog2 = 8.f;   // lazy softmax rescale: keep exp2(s - m) 
 
 // Where an item's keys are: chunk [t0, t1) of the row's visible keys, of which
 // [nb, t1) are this call's appended rows (taken from LDS, not the cache).
+// PG (paged cache): the chunk's keys lie in pages t0 / psz .. (t1 - 1) / psz, at
+// most 64 of them (a chunk holds at most 1024 keys, a page at least 16); lane j
+// holds the id of the j-th (lanes past the chunk: the table row's last entry),
+// an id outside the pool replaced by page 0 so that every address stays in the
+// pool; pbad: the chunk needs such a page.  kvrow0 is then the kv head's first
+// row inside a page.
 struct ItemGeom {
   int L, r_off, t0, t1, nb, n_new, tw, nsteps, last_row;
   size_t kvrow0;
+  int slot, pg;
+  bool pbad;
 };
 
+template <bool PG = false>
 __device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it, int4 rin) {
   // rin: slot, committed length, visible keys, block offset
   ItemGeom g;
@@ -474,14 +483,28 @@ __device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it
   g.t1 = min(g.t0 + A.split, rin.z);
   g.nb = max(g.t0, g.L);
   g.n_new = max(0, g.t1 - g.nb);
-  g.kvrow0 = ((size_t)rin.x * A.nkv + it.g) * A.capacity;
+  g.slot = rin.x;
+  if constexpr (PG) {
+    const int lane = lane_id();
+    const int p0 = g.t0 >> A.plog, npg = ((g.t1 - 1) >> A.plog) - p0 + 1;
+    const int pid = A.ptab[(size_t)rin.x * A.pps + min(p0 + lane, A.pps - 1)];
+    const bool ok = (unsigned)pid < (unsigned)A.npages;
+    g.pg = ok ? pid : 0;
+    g.pbad = __any(lane < npg && !ok) != 0;
+    g.kvrow0 = (size_t)it.g * A.psz;
+  } else {
+    g.pg = 0;
+    g.pbad = false;
+    g.kvrow0 = ((size_t)rin.x * A.nkv + it.g) * A.capacity;
+  }
   g.tw = g.t0 + wave_id() * 8;
   g.nsteps = g.tw < g.t1 ? (g.t1 - g.tw + 31) / 32 : 0;
   g.last_row = max(min(g.t1, g.L) - 1, 0);
   return g;
 }
+template <bool PG = false>
 __device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it, const int4 *rinfo) {
-  return item_geom(A, it, rinfo[it.row]);
+  return item_geom<PG>(A, it, rinfo[it.row]);
 }
 
 // The K and V registers of two 32-key steps of an item (lane: one key row of
@@ -495,8 +518,23 @@ struct KVRegs {
 // the loads past the chunk hit lines this item already fetched) so the
 // compiler can count the loads in flight exactly; lanes past the chunk get
 // weight 0.  Each 16-byte load instruction of a wave covers whole 128-byte lines.
+// PG: the key row's page comes from the lane that holds it (a row clamped below
+// the chunk takes the chunk's first page: its value is never used), so every
+// address is inside the pool.
+template <bool PG = false>
 __device__ __forceinline__ void kv_load_step(const LayerArgs &A, const ItemGeom &g, uint4 (&r)[4], int i) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  if constexpr (PG) {
+    const int row = min(g.tw + 32 * i + kr, g.last_row);
+    const int j = min(max((row >> A.plog) - (g.t0 >> A.plog), 0), kWave - 1);
+    const int page = __shfl(g.pg, j, kWave);
+    const size_t e = ((size_t)page * A.nkv * A.psz + g.kvrow0 + (row & (A.psz - 1))) * kHeadDim + kl * 8;
+    r[0] = ld16(A.kc + e);
+    r[1] = ld16(A.kc + e + 64);
+    r[2] = ld16(A.vc + e);
+    r[3] = ld16(A.vc + e + 64);
+    return;
+  }
   const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + g.kvrow0 * kHeadDim, region);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + g.kvrow0 * kHeadDim, region);
@@ -507,11 +545,12 @@ __device__ __forceinline__ void kv_load_step(const LayerArgs &A, const ItemGeom 
   r[3] = ld_buf(Vr, off + 128);
 }
 
+template <bool PG = false>
 __device__ __forceinline__ void attn_item_loads(const LayerArgs &A, const Item &it, const int4 *rinfo, KVRegs &P) {
-  const ItemGeom g = item_geom(A, it, rinfo);
+  const ItemGeom g = item_geom<PG>(A, it, rinfo);
   uint4 a[4], b[4];
-  kv_load_step(A, g, a, 0);
-  kv_load_step(A, g, b, 1);
+  kv_load_step<PG>(A, g, a, 0);
+  kv_load_step<PG>(A, g, b, 1);
   P = KVRegs{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
@@ -575,7 +614,7 @@ __device__ __forceinline__ void fresh_pair(const LayerArgs &A, float4 k4, float4
 // loaded here) and whose appended rows, if any, are in knew/vnew: online
 // softmax per wave, the 4 waves combined in LDS, the partial (m, l, acc) of
 // each q head stored (device-coherent when COH: merged within the dispatch).
-template <int DT, int GROUP, bool COH, int NP>
+template <int DT, int GROUP, bool COH, int NP, bool PG = false>
 __device__ __forceinline__ void attn_stream(const LayerArgs &A, const ItemGeom &G, int row, int g, int c,
                                             const float (&q)[GROUP][16], const uint16_t *knew,
                                             const uint16_t *vnew, AttnShared<GROUP> &S, uint4 (&r)[NP][4]) {
@@ -586,7 +625,7 @@ __device__ __forceinline__ void attn_stream(const LayerArgs &A, const ItemGeom &
   const int kl = lane & 7, kr = lane >> 3;
   const int d0 = 8 * kl, d1 = 64 + 8 * kl;
   const int L = G.L, t1 = G.t1, nb = G.nb, tw = G.tw, nsteps = G.nsteps;
-  auto load_step = [&](uint4 (&r)[4], int i) __attribute__((always_inline)) { kv_load_step(A, G, r, i); };
+  auto load_step = [&](uint4 (&r)[4], int i) __attribute__((always_inline)) { kv_load_step<PG>(A, G, r, i); };
 
   float m[GROUP], l[GROUP], acc[GROUP][16];
 #pragma unroll
@@ -716,12 +755,15 @@ __device__ __forceinline__ void attn_stream(const LayerArgs &A, const ItemGeom &
 
 // One item, its first two steps already loaded into P; its partial is merged by
 // another workgroup of this same dispatch.
-template <int DT, int GROUP, bool COH>
+template <int DT, int GROUP, bool COH, bool PG = false>
 __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, const int4 *rinfo, uint16_t *knew, uint16_t *vnew,
                           AttnShared<GROUP> &S, const KVRegs &P) {
   const int wave = wave_id(), lane = lane_id();
   const int row = it.row, g = it.g;
-  const ItemGeom G = item_geom(A, it, rinfo);
+  const ItemGeom G = item_geom<PG>(A, it, rinfo);
+  if constexpr (PG) {
+    if (G.pbad && threadIdx.x == 0 && A.status) atomicOr(A.status, kStatusBadPage);
+  }
   const int L = G.L, r_off = G.r_off, nb = G.nb, n_new = G.n_new;
   uint4 rr[2][4] = {{P.a0, P.a1, P.a2, P.a3}, {P.b0, P.b1, P.b2, P.b3}};
 
@@ -758,16 +800,27 @@ __device__ __forceinline__ void attn_item(const LayerArgs &A, const Item &it, co
       reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
       reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
       if (i == own) {   // every row also stores its own appended row in the cache
-        const size_t off = (G.kvrow0 + nb + i) * kHeadDim;
-        reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
-        reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+        if constexpr (PG) {
+          // position nb + i = L + r_off: row (nb + i) % psz of the chunk's page (nb + i) / psz
+          if (!G.pbad) {
+            const int t = nb + i;
+            const int page = __shfl(G.pg, (t >> A.plog) - (G.t0 >> A.plog), kWave);
+            const size_t off = ((size_t)page * A.nkv * A.psz + G.kvrow0 + (t & (A.psz - 1))) * kHeadDim;
+            reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
+            reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+          }
+        } else {
+          const size_t off = (G.kvrow0 + nb + i) * kHeadDim;
+          reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
+          reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+        }
       }
     }
   }
   float q[GROUP][16];
   q_scale<GROUP>(A, Q, q);
   if (n_new > 0) __syncthreads();
-  attn_stream<DT, GROUP, true, 2>(A, G, row, g, it.c, q, knew, vnew, S, rr);
+  attn_stream<DT, GROUP, true, 2, PG>(A, G, row, g, it.c, q, knew, vnew, S, rr);
 }
 
 // ---------------------------------------------------------------- merge
@@ -899,7 +952,7 @@ __device__ __forceinline__ void resolve(const LayerArgs &A, const Pending &p, At
   if (S.flag) merge_group<DT, GROUP, COH>(A, p.row, p.g, p.nch, S);
 }
 
-template <int DT, int GROUP, bool COH>
+template <int DT, int GROUP, bool COH, bool PG = false>
 __device__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *rinfo, uint16_t *knew,
                                 uint16_t *vnew, AttnShared<GROUP> &S, int first, int stride) {
   const int total = pre[A.rows];
@@ -907,8 +960,8 @@ __device__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *
   for (int item = first; item < total; item += stride) {
     const Item it = decode_item(A, item, pre);
     KVRegs P;
-    attn_item_loads(A, it, rinfo, P);
-    attn_item<DT, GROUP, COH>(A, it, rinfo, knew, vnew, S, P);
+    attn_item_loads<PG>(A, it, rinfo, P);
+    attn_item<DT, GROUP, COH, PG>(A, it, rinfo, knew, vnew, S, P);
     const Pending now = signal_item(A, it);
     if (pend.row >= 0) resolve<DT, GROUP, COH>(A, pend, S);
     pend = now;
@@ -1880,7 +1933,7 @@ __global__ __launch_bounds__(256) void k_qkv(LayerArgs A) {
   }
 }
 
-template <int DT, int GROUP, bool MIX = false>
+template <int DT, int GROUP, bool MIX = false, bool PG = false>
 __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ AttnShared<GROUP> S;
@@ -1889,7 +1942,7 @@ __global__ __launch_bounds__(256) void k_attn(LayerArgs A) {
   uint16_t *vnew = knew + A.n * kHeadDim;
   int *pre = reinterpret_cast<int *>(vnew + A.n * kHeadDim);
   build_item_prefix<false, MIX>(A, pre, rinfo, S.wsum);
-  attention_phase<DT, GROUP, false>(A, pre, rinfo, knew, vnew, S, blockIdx.x, gridDim.x);
+  attention_phase<DT, GROUP, false, PG>(A, pre, rinfo, knew, vnew, S, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------- phase C for a few rows
@@ -3077,12 +3130,14 @@ MfmaKernel pick_oproj_mfma(int kq, bool mix) {
 }
 
 template <int DT>
-LayerKernel pick_attn(int group, bool mix) {
+LayerKernel pick_attn(int group, bool mix, bool paged) {
+#define ASR_PICK_ATTN(G)                                                              \
+  case G:                                                                             \
+    if (paged) return mix ? k_attn<DT, G, true, true> : k_attn<DT, G, false, true>;  \
+    return mix ? k_attn<DT, G, true> : k_attn<DT, G>;
   switch (group) {
-    case 1: return mix ? k_attn<DT, 1, true> : k_attn<DT, 1>;
-    case 2: return mix ? k_attn<DT, 2, true> : k_attn<DT, 2>;
-    case 4: return mix ? k_attn<DT, 4, true> : k_attn<DT, 4>;
-    case 8: return mix ? k_attn<DT, 8, true> : k_attn<DT, 8>;
+    ASR_PICK_ATTN(1) ASR_PICK_ATTN(2) ASR_PICK_ATTN(4) ASR_PICK_ATTN(8)
+#undef ASR_PICK_ATTN
     default: return nullptr;
   }
 }
@@ -3218,7 +3273,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
     if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1, a.kv8 != 0, a.qo_n != 0), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
                           ev, 1, a)) != hipSuccess)
       return e;
-  } else if ((e = launch_phase(pick_attn<DT>(a.group, a.qo_n != 0), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
+  } else if ((e = launch_phase(pick_attn<DT>(a.group, a.qo_n != 0, a.ptab != nullptr), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
                                ev, 1, a)) != hipSuccess) {
     return e;
   }
@@ -3292,7 +3347,7 @@ size_t layer_dyn_smem(const LayerArgs &a) { return fused_dyn_smem(a); }
 // tiles: one K/V stream per (sequence, kv head) on the matrix cores (the
 // per-row merge takes two or more q heads per kv head)
 bool attn_vmfma_used(const LayerArgs &a) {
-  return a.mfma && !a.qo_n && a.n > 1 && a.group >= 2 && !a.kv8 && vmfma_tiles(a.group, a.n) > 0;
+  return a.mfma && !a.qo_n && a.n > 1 && a.group >= 2 && !a.kv8 && !a.ptab && vmfma_tiles(a.group, a.n) > 0;
 }
 
 // Resident workgroups of the verify attention kernel for B sequences (blocks per
@@ -3308,7 +3363,8 @@ int attn_vmfma_grid(int dtype, int group, int n, int B, int cus) {
 }
 
 // (group 8 would hold its 8 q vectors and accumulators past the register file)
-bool attn_waves_used(const LayerArgs &a) { return a.mfma && (a.group == 2 || a.group == 4); }
+// (paged caches take the chunked kernel: its chunks hold the page ids of their keys)
+bool attn_waves_used(const LayerArgs &a) { return a.mfma && !a.ptab && (a.group == 2 || a.group == 4); }
 
 // Resident grid of the equal-share attention kernel: blocks per CU from the
 // occupancy calculator (at the largest row table) times the CU count.

@@ -20,6 +20,7 @@ constexpr int kVmMaxSeqs = 64;        // sequences of a verify call whose work i
 constexpr int kFlowWords = 128;      // counters of the one-dispatch path (heads + 4 totals)
 constexpr int kPartStride = 132;      // floats per (chunk, q head) partial: acc[128], m, l, pad
 constexpr uint32_t kStatusBadSlot = ASR_STATUS_BAD_SLOT;  // slot index outside [0, batch_cap)
+constexpr uint32_t kStatusBadPage = ASR_STATUS_BAD_PAGE;  // page id outside the paged cache's pool
 
 // Everything a layer kernel needs, passed by value.
 struct LayerArgs {
@@ -34,9 +35,12 @@ struct LayerArgs {
   const int32_t *slots;       // [B] or null
   const int32_t *positions;   // [B] or null
   // cache
-  uint16_t *kc, *vc;          // [batch_cap][nkv][capacity][d]
+  uint16_t *kc, *vc;          // [batch_cap][nkv][capacity][d], or paged: [npages][nkv][psz][d]
   int32_t *lens;              // [batch_cap]
   uint32_t *status;           // or null
+  // paged cache (ptab not null): position t of slot s is row t % psz of page ptab[s * pps + t / psz]
+  const int32_t *ptab;        // [batch_cap][pps]
+  int pps, npages, psz, plog; // psz = 1 << plog
   // output
   void *out;                  // [rows][H] fp32 or 16-bit
   // workspace (zero-filled once by the caller; every call leaves the counters at zero)

@@ -17,6 +17,8 @@ struct AppendArgs {
   int32_t *lens;
   uint32_t *status;
   int B, n, nkv, batch_cap, capacity;
+  const int32_t *ptab;         // paged cache: [batch_cap][pps] page ids of psz rows, or null
+  int pps, npages, psz;
 };
 
 __device__ __forceinline__ bool append_target(const AppendArgs &a, int b, int &slot, int &L) {
@@ -39,7 +41,18 @@ __global__ __launch_bounds__(256) void k_append_rows(AppendArgs a) {
   const int b = (int)(br / a.n);
   int slot, L;
   if (!append_target(a, b, slot, L)) return;
-  const size_t dst = (((size_t)slot * a.nkv + g) * a.capacity + L + r) * (size_t)a.chunks * 16;
+  size_t dst_row = ((size_t)slot * a.nkv + g) * a.capacity + L + r;
+  if (a.ptab) {
+    // position L + r: row (L + r) % psz of its page; a page id outside the pool is not written
+    const int t = L + r;
+    const int page = a.ptab[(size_t)slot * a.pps + t / a.psz];
+    if ((unsigned)page >= (unsigned)a.npages) {
+      if (a.status && part == 0) atomicOr(a.status, (uint32_t)ASR_STATUS_BAD_PAGE);
+      return;
+    }
+    dst_row = ((size_t)page * a.nkv + g) * a.psz + t % a.psz;
+  }
+  const size_t dst = dst_row * (size_t)a.chunks * 16;
   reinterpret_cast<uint4 *>(a.kc + dst)[part] = a.k_new[idx * a.chunks + part];
   reinterpret_cast<uint4 *>(a.vc + dst)[part] = a.v_new[idx * a.chunks + part];
 }
@@ -97,6 +110,10 @@ hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new
   a.nkv = kv.n_kv_heads;
   a.batch_cap = kv.batch_cap;
   a.capacity = kv.capacity;
+  a.ptab = kv.block_table;
+  a.pps = kv.pages_per_seq;
+  a.npages = kv.num_pages;
+  a.psz = kv.page_size;
   const size_t rows = (size_t)B * n * kv.n_kv_heads;
   hipLaunchKernelGGL(k_append_rows, dim3((unsigned)((rows * a.chunks + 255) / 256)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();

@@ -64,7 +64,9 @@ enum {
   ASR_STATUS_CAPACITY = 1,     /* an append would pass the capacity: that sequence skipped */
   ASR_STATUS_CROP_GROW = 2,    /* a crop asked for a length < 0 or above the current one: ignored */
   ASR_STATUS_SYNC_TIMEOUT = 4, /* the fused dispatch gave up waiting for another workgroup */
-  ASR_STATUS_BAD_SLOT = 8      /* a slot index outside [0, batch_cap): that row skipped */
+  ASR_STATUS_BAD_SLOT = 8,     /* a slot index outside [0, batch_cap): that row skipped */
+  ASR_STATUS_BAD_PAGE = 16     /* a paged cache's block table names a page outside
+                                  [0, num_pages) for a position a call needs */
 };
 
 /* how a layer call is dispatched */
@@ -141,9 +143,28 @@ typedef struct asr_attn_weights {
  * FP8 cache for calls of more than 4 rows (B for decode, B * k for verify) with
  * 2 or 4 q heads per kv head and the stream-ordered dispatch; other calls on an
  * FP8 cache return ASR_EUNSUPPORTED.
+ *
+ * A paged cache (block_table not NULL) keeps K and V in one pool of fixed-size
+ * pages shared by all slots, addressed through a page table per slot (the
+ * cache of the vLLM engine that "Baseten optimizes Qwen3-ASR 1.7B", section
+ * "Our optimized Qwen3-ASR stack", starts its serving stack from).  k and v
+ * are then [num_pages][n_kv_heads][page_size][head_dim]; position t of slot s,
+ * kv head g lives in page p = block_table[s * pages_per_seq + t / page_size]
+ * at k[((p * n_kv_heads + g) * page_size + t % page_size) * head_dim].
+ * capacity must equal pages_per_seq * page_size; page_size is a power of two
+ * in [16, 1024]; 16-bit caches only.  Slots may name the same page (a shared
+ * prompt prefix) as long as no call appends into a page that another slot
+ * still reads.  The table is read by the kernels, never by the host: a page
+ * id outside [0, num_pages) for a position a call needs sets
+ * ASR_STATUS_BAD_PAGE, and that sequence's output rows, appended rows and
+ * length are then unspecified (nothing outside the pool is read or written).
+ * Layer calls on a paged cache run the matrix-core projections and the
+ * chunked split-KV attention whatever the row count (the stream-ordered
+ * dispatch; the fused dispatch returns ASR_EUNSUPPORTED).
  */
 typedef struct asr_kv_layer {
-  void *k;              /* [batch_cap][n_kv_heads][capacity][head_dim], elements of dtype */
+  void *k;              /* [batch_cap][n_kv_heads][capacity][head_dim], elements of dtype
+                           (paged: [num_pages][n_kv_heads][page_size][head_dim]) */
   void *v;              /* same layout */
   int32_t *lens;        /* [batch_cap] committed length per slot (device) */
   uint32_t *status;     /* sticky ASR_STATUS_* word (device) or NULL */
@@ -154,6 +175,11 @@ typedef struct asr_kv_layer {
   int32_t dtype;        /* ASR_F16 or ASR_BF16 (the layer's dtype), or ASR_FP8_E4M3 */
   const float *k_scale; /* ASR_FP8_E4M3: [n_kv_heads] fp32 scales of K (device); else ignored */
   const float *v_scale; /* ASR_FP8_E4M3: [n_kv_heads] fp32 scales of V (device); else ignored */
+  const int32_t *block_table; /* paged cache: [batch_cap][pages_per_seq] page ids (device);
+                                 NULL: the contiguous layout above, and the fields below are ignored */
+  int32_t page_size;    /* paged: positions per page */
+  int32_t pages_per_seq;
+  int32_t num_pages;    /* paged: pages in the pool */
 } asr_kv_layer;
 
 /*
@@ -276,6 +302,8 @@ int asr_attn_layer_mixed(const asr_attn_config *cfg, const asr_attn_weights *w,
  * rows of sequence b go to positions lens[s] .. lens[s] + n - 1 of slot
  * s = slots[b] (NULL: b), then lens[s] grows by n.  A sequence whose rows
  * would pass the capacity is skipped (ASR_STATUS_CAPACITY).  Slots distinct.
+ * On a paged cache each row goes to the page its position maps to; a row
+ * whose page id lies outside the pool is not stored (ASR_STATUS_BAD_PAGE).
  */
 int asr_kv_append(const asr_kv_layer *kv, const void *k_new, const void *v_new,
                   const int32_t *slots, int32_t B, int32_t n, hipStream_t stream);

@@ -276,3 +276,16 @@ def draft_with_edits(stream: int, seq: int, transcript, rate: float, vocab: int,
             draft.append(t)
             unc.append(noise)
     return draft, unc
+
+
+T_PAGES = 22
+
+
+def page_table(stream: int, batch_cap: int, pages_per_seq: int, num_pages: int) -> np.ndarray:
+    """A paged cache's table [batch_cap][pages_per_seq] int32: distinct pages of a pool of
+    num_pages (>= batch_cap * pages_per_seq), in a seeded random order, so that neighbouring
+    positions of a sequence sit in unrelated pages, as in a pool whose pages were handed out
+    and returned by many requests."""
+    assert num_pages >= batch_cap * pages_per_seq
+    perm = rng_for(stream, 0, T_PAGES, num_pages).permutation(num_pages)
+    return perm[:batch_cap * pages_per_seq].reshape(batch_cap, pages_per_seq).astype(np.int32)

@@ -160,3 +160,36 @@ def test_mixed_entry_validates_on_the_host():
     assert call([4, 8], lens=[60, 57]) == -3                          # 57 + 8 > 64
     assert call([4, 8], ws=16) == -4
     assert call([32] * 64, ws=16) == -4                               # the largest call: 2048 rows
+
+
+def test_paged_cache_validation_on_the_host():
+    """A paged cache: power-of-two pages of 16 .. 1024 rows, capacity = pages_per_seq * page_size,
+    a non-empty pool, 16-bit elements, the stream-ordered dispatch; the prefill copy checks the
+    same descriptor."""
+    ga, lib = _lib()
+    fake = ctypes.c_void_p(0x1000)
+    w = ga._lib.AsrAttnWeights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cfg = ga.config()
+
+    def kv(page=16, pps=4, cap=None, num=32, dt=ga.F16, scales=(None, None)):
+        cap = page * pps if cap is None else cap
+        return ga._lib.AsrKvLayer(0x1000, 0x1000, 0x1000, None, 8, cap, 8, 128, dt, *scales, 0x1000, page, pps, num)
+
+    dec = lib.asr_attn_layer_decode
+    args = lambda c_kv, B=1, c=cfg, ws=1 << 30: (ctypes.byref(c), ctypes.byref(w), ctypes.byref(c_kv), fake, None,
+                                                 None, B, None, None, fake, fake, ws, None)
+    assert dec(*args(kv(page=24, pps=4))) == -2                    # not a power of two
+    assert dec(*args(kv(page=8, pps=8))) == -2                     # below 16 rows
+    assert dec(*args(kv(page=2048, pps=1))) == -2                  # above 1024 rows
+    assert dec(*args(kv(cap=100))) == -1                           # capacity != pages_per_seq * page_size
+    assert dec(*args(kv(num=0))) == -1
+    assert dec(*args(kv(pps=0, cap=16))) == -1
+    assert dec(*args(kv(dt=ga.FP8_E4M3, scales=(0x1000, 0x1000)), 6, ga.config(dtype="bf16"))) == -2
+    assert dec(*args(kv(), 1, ga.config(dispatch=ga.DISPATCH_FUSED))) == -2
+    assert dec(*args(kv(), 0)) == 0
+    assert dec(*args(kv(), 1, cfg, 16)) == -4                      # the workspace check still applies
+    assert lib.asr_kv_append(ctypes.byref(kv(page=48)), fake, fake, None, 1, 1, None) == -2
+    assert lib.asr_kv_append(ctypes.byref(kv()), fake, fake, None, 0, 1, None) == 0
+    # the descriptor's layout: the paged fields follow the FP8 scales
+    assert ctypes.sizeof(ga._lib.AsrKvLayer) == 96
+    assert ga._lib.AsrKvLayer.block_table.offset == 72 and ga._lib.AsrKvLayer.num_pages.offset == 88

@@ -77,7 +77,7 @@ def sources_digest():
 
 
 def measured_traffic(workload):
-    return TRAFFIC[workload] if sources_digest() == TRAFFIC["sources_sha256"] else None
+    return TRAFFIC.get(workload) if sources_digest() == TRAFFIC["sources_sha256"] else None
 
 
 def parse():
@@ -89,6 +89,8 @@ def parse():
     p.add_argument("--no-verify", action="store_true", help="skip the bs1 verify blocks")
     p.add_argument("--no-wide", action="store_true", help="skip the hidden-2048 batch-64 workload")
     p.add_argument("--no-fp8", action="store_true", help="skip the batch-64 decode on an FP8 cache")
+    p.add_argument("--no-paged", action="store_true", help="skip the batch-64 decode on a paged cache")
+    p.add_argument("--page-size", type=int, default=16, help="rows per page of the paged batch-64 cache")
     p.add_argument("--no-loop", action="store_true",
                    help="skip greedy decoding and speculative rounds on the whole decoder with the model head")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -179,6 +181,8 @@ def main():
         batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
         if not args.no_fp8:
             batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=True)
+        if not args.no_paged:
+            batched_leg(args, ga, si, np, torch, dev, to_dev, stream, page=args.page_size)
         print(json.dumps({"profile_batched": args.profile_batched}))
         return
 
@@ -333,6 +337,8 @@ def main():
         result["batched"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
         if not args.no_fp8:
             result["batched_fp8"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=True)
+        if not args.no_paged:
+            result["batched_paged"] = batched_leg(args, ga, si, np, torch, dev, to_dev, stream, page=args.page_size)
         if not args.no_wide:
             result["batched_h2048"] = wide_batched_leg(args, ga, si, np, torch, dev, to_dev, stream)
     if not args.no_cpu_baseline:
@@ -340,10 +346,12 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False):
+def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False, page=0):
     """Ragged batched decode of 64 sequences (bf16, hidden 1024, lengths uniform in [200, 1500]):
     one step = 28 layer calls + the crop back to the committed lengths, graph-replayed.  With
-    ``fp8`` the caches hold E4M3 codes of the same draws with per-kv-head scales."""
+    ``fp8`` the caches hold E4M3 codes of the same draws with per-kv-head scales; with ``page``
+    each layer's cache is a pool of pages of that many rows, every sequence's pages in a shuffled
+    order (a pool whose pages many requests have taken and returned)."""
     wl = si.WORKLOADS["ragged_batch64_h1024"]
     H, NL, B, dtype, sid = wl["hidden"], wl["layers"], wl["batch"], wl["dtype"], wl["stream"]
     lens = si.kv_lengths(sid, B, *wl["kv_len"])
@@ -362,6 +370,16 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False):
             for s_, (kc, vc) in enumerate(rows):
                 kv.k[s_, :, : lens[s_]] = torch.from_numpy(kc).to(dev)
                 kv.v[s_, :, : lens[s_]] = torch.from_numpy(vc).to(dev)
+        elif page:
+            pps = CAP_B64 // page
+            table = torch.from_numpy(si.page_table(sid, B, pps, B * pps)).to(dev)
+            kv = ga.KVLayer.paged(B * pps, 8, page, table, dtype=torch.bfloat16, device=dev)
+            rows = si.kv_rows_many(sid, l, list(range(B)), lens.tolist(), dtype)
+            for s_, (kb, vb) in enumerate(rows):
+                for which, bits, pool in (("k", kb, kv.k), ("v", vb, kv.v)):
+                    full = torch.zeros((8, CAP_B64, 128), dtype=torch.bfloat16, device=dev)
+                    full[:, : lens[s_]] = to_dev(bits, dtype)
+                    pool[table[s_].long()] = full.view(8, pps, page, 128).transpose(0, 1)
         else:
             kv = ga.KVLayer.empty(B, 8, CAP_B64, dtype=torch.bfloat16, device=dev)
             rows = si.kv_rows_many(sid, l, list(range(B)), lens.tolist(), dtype)
@@ -375,7 +393,7 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False):
     ws = ga.alloc_workspace(cfg, B, CAP_B64, device=dev)
     base = torch.from_numpy(lens.astype(np.int32)).to(dev)
     torch.cuda.synchronize()
-    tag = "batch-64 fp8 cache" if fp8 else "batch-64"
+    tag = "batch-64 fp8 cache" if fp8 else (f"batch-64 paged cache ({page}-row pages)" if page else "batch-64")
     print(f"[bench] {tag} inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     hl = lens.tolist()
     if args.profile_batched:
@@ -432,12 +450,14 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False):
           "phases (us): " + ", ".join(f"{k} {mean_us[k]:.2f}" for k in PHASES), file=sys.stderr, flush=True)
     del kvs, weights
     torch.cuda.empty_cache()
-    return {"workload": "28-layer ragged batched decode, 64 seqs, bf16 weights, "
-                        + ("FP8 (E4M3) cache with per-kv-head scales" if fp8 else "bf16 cache")
+    cache = ("FP8 (E4M3) cache with per-kv-head scales" if fp8 else
+             f"bf16 paged cache, {page}-row pages in shuffled order" if page else "bf16 cache")
+    tkey = "b64_fp8" if fp8 else ("b64_paged" if page else "b64")
+    return {"workload": "28-layer ragged batched decode, 64 seqs, bf16 weights, " + cache
                         + ", hidden 1024, KV U{200..1500}",
             "value": round(tok_s, 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4), "steps": n,
             "step_roofline": sr, "ok": ok,
-            "roofline": roofline(mean_us, bphase, measured_traffic("b64_fp8" if fp8 else "b64"))}
+            "roofline": roofline(mean_us, bphase, measured_traffic(tkey))}
 
 
 def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_lens, H, NL, dtype, sid, P0,

@@ -288,7 +288,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   } else if (attn_waves_used(a)) {
     // many rows: one equal key share per wave of a resident grid; a (row, kv
     // head) spans at most capacity / share + 2 <= kMaxChunks shares
-    attn_grid = attn_waves_grid(cfg->dtype, a.group, cus, n_per_seq != nullptr);
+    attn_grid = attn_waves_grid(cfg->dtype, a.group, cus, n_per_seq != nullptr, kv->block_table != nullptr);
     if (attn_grid <= 0) return ASR_EHIP;
     int share = cfg->kv_split ? cfg->kv_split : kMinShare;
     const int least = (kv->capacity + kMaxChunks - 2) / (kMaxChunks - 1);

@@ -1037,9 +1037,36 @@ __device__ __forceinline__ int wcur_next(WCur &c, const LayerArgs &A, const int 
 // and keep plain loads.
 // F8: the cache holds E4M3 codes (128-byte rows); lane kl takes dims
 // [16 kl, 16 kl + 16) with one 16-byte load, so a wave's load covers 8 whole lines.
-template <bool NT, bool F8>
-__device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, uint4 (&r)[4]) {
+// Entry `pidx` of slot `slot`'s page table, both wave-uniform: read through the
+// scalar cache, so that waiting for it never waits on the K/V loads in flight.
+__device__ __forceinline__ int page_entry(const LayerArgs &A, int slot, int pidx) {
+  typedef const __attribute__((address_space(4))) int32_t *ctab_t;
+  return ((ctab_t)A.ptab)[(size_t)slot * A.pps + pidx];
+}
+
+// PG (paged cache): the step's rows lie in at most two pages (a page holds at
+// least 16 rows), whose ids are read as wave-uniform values; each lane takes
+// its row's.  An id outside the pool is replaced by page 0 (the return value
+// says so), so every address stays in the pool.
+template <bool NT, bool F8, bool PG = false>
+__device__ __forceinline__ bool wstep_load(const LayerArgs &A, const WCur &c, uint4 (&r)[4]) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  if constexpr (PG) {
+    static_assert(!F8, "paged caches hold 16-bit rows");
+    const int last = max(min(rfl(c.te), rfl(c.L)) - 1, 0);
+    const int slot = rfl(c.slot), t = rfl(c.t);
+    const int ia = min(t, last) >> A.plog, ib = min(t + 7, last) >> A.plog;
+    const int pa = page_entry(A, slot, ia), pb = page_entry(A, slot, ib);
+    const bool oka = (unsigned)pa < (unsigned)A.npages, okb = (unsigned)pb < (unsigned)A.npages;
+    const int row = min(t + kr, last);
+    const int page = (row >> A.plog) == ia ? (oka ? pa : 0) : (okb ? pb : 0);
+    const size_t e = (((size_t)page * A.nkv + rfl(c.g)) * A.psz + (row & (A.psz - 1))) * kHeadDim + kl * 8;
+    r[0] = NT ? ld16_stream(A.kc + e) : ld16(A.kc + e);
+    r[1] = NT ? ld16_stream(A.kc + e + 64) : ld16(A.kc + e + 64);
+    r[2] = NT ? ld16_stream(A.vc + e) : ld16(A.vc + e);
+    r[3] = NT ? ld16_stream(A.vc + e + 64) : ld16(A.vc + e + 64);
+    return !(oka && okb);
+  }
   constexpr uint32_t RB = F8 ? kHeadDim : kHeadDim * 2;   // bytes per cached row
   // (the cursor is wave-uniform; readfirstlane keeps the resources in scalar registers)
   const size_t base = ((size_t)rfl(c.slot) * A.nkv + rfl(c.g)) * A.capacity * RB;
@@ -1062,6 +1089,7 @@ __device__ __forceinline__ void wstep_load(const LayerArgs &A, const WCur &c, ui
     r[2] = NT ? ld_buf_nt(Vr, off) : ld_buf(Vr, off);
     r[3] = NT ? ld_buf_nt(Vr, off + 128) : ld_buf(Vr, off + 128);
   }
+  return false;
 }
 
 // One lane's 8 dims of an appended row, 16-bit as stored: k normalised with
@@ -1164,7 +1192,7 @@ __device__ __forceinline__ void wresolve(const LayerArgs &A, const WPending &p) 
   if (old == (uint32_t)(p.np - 1)) merge_wave<DT, GROUP>(A, p.row, p.g, p.np);
 }
 
-template <int DT, int GROUP, bool NT, bool F8>
+template <int DT, int GROUP, bool NT, bool F8, bool PG = false>
 __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *rinfo, int w, int W) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
   // a lane's 16 dims: [8 kl, 8 kl + 8) and [64 + 8 kl, ..) of a 256-byte 16-bit row (two whole
@@ -1190,9 +1218,10 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   // it keeps twice as many steps in flight (the same bytes in flight per wave).
   constexpr int NS = F8 ? 5 : 3;
   uint4 rs[NS][4];
+  bool pbad = false;   // PG: a page id outside the pool was met (loads or this wave's appended rows)
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) {
-    wstep_load<NT, F8>(A, lc, rs[i]);
+    pbad |= wstep_load<NT, F8, PG>(A, lc, rs[i]);
     wcur_next(lc, A, pre, rinfo);
   }
 
@@ -1334,11 +1363,21 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
           v0 = round8<DT>(va, vb);
           v1 = round8<DT>(vc, vd);
           if (t == cc.L + cc.roff) {   // every row stores its own appended row
-            const size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
-            *reinterpret_cast<uint4 *>(A.kc + ro + d0) = k0;
-            *reinterpret_cast<uint4 *>(A.kc + ro + d1) = k1;
-            *reinterpret_cast<uint4 *>(A.vc + ro + d0) = v0;
-            *reinterpret_cast<uint4 *>(A.vc + ro + d1) = v1;
+            size_t ro = (((size_t)cc.slot * A.nkv + cc.g) * A.capacity + t) * kHeadDim;
+            bool store = true;
+            if constexpr (PG) {   // row t % psz of its page (skipped, and reported, for an id outside the pool)
+              const int own = rfl(cc.L) + rfl(cc.roff);
+              const int pg = page_entry(A, rfl(cc.slot), own >> A.plog);
+              store = (unsigned)pg < (unsigned)A.npages;
+              pbad |= !store;
+              ro = (((size_t)(store ? pg : 0) * A.nkv + cc.g) * A.psz + (own & (A.psz - 1))) * kHeadDim;
+            }
+            if (store) {
+              *reinterpret_cast<uint4 *>(A.kc + ro + d0) = k0;
+              *reinterpret_cast<uint4 *>(A.kc + ro + d1) = k1;
+              *reinterpret_cast<uint4 *>(A.vc + ro + d0) = v0;
+              *reinterpret_cast<uint4 *>(A.vc + ro + d1) = v1;
+            }
           }
         }
       }
@@ -1386,7 +1425,7 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   };
 
   auto issue = [&](uint4 (&r)[4]) {
-    wstep_load<NT, F8>(A, lc, r);
+    pbad |= wstep_load<NT, F8, PG>(A, lc, r);
     wcur_next(lc, A, pre, rinfo);
   };
   // arithmetic of cc's step, then advance cc: false past the share
@@ -1410,6 +1449,9 @@ __device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *
   }
 streamed:
   wresolve<DT, GROUP>(A, pend);
+  if constexpr (PG) {
+    if (__any(pbad) && lane == 0 && A.status) atomicOr(A.status, kStatusBadPage);
+  }
 }
 
 // ---------------------------------------------------------------- phase D: o_proj
@@ -2240,14 +2282,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
 }
 
 // many rows: equal key shares per wave of a resident grid
-template <int DT, int GROUP, bool NT, bool F8, bool MIX = false>
+template <int DT, int GROUP, bool NT, bool F8, bool MIX = false, bool PG = false>
 __global__ __launch_bounds__(256) void k_attn_waves(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ int wsum[4];
   int4 *rinfo = reinterpret_cast<int4 *>(dyn);
   int *pre = reinterpret_cast<int *>(rinfo + A.rows);
   build_item_prefix<true, MIX>(A, pre, rinfo, wsum);
-  attention_waves<DT, GROUP, NT, F8>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
+  attention_waves<DT, GROUP, NT, F8, PG>(A, pre, rinfo, blockIdx.x * 4 + wave_id(), gridDim.x * 4);
 }
 
 __host__ __device__ __forceinline__ size_t lds_attn_waves_bytes(int rows) {
@@ -3186,9 +3228,13 @@ LayerKernel pick_oproj_merge(int kvo, int nch_host, bool split) {
 
 // (mixed calls: never single-token-only, so no NT instance)
 template <int DT>
-LayerKernel pick_attn_waves(int group, bool nt, bool f8, bool mix = false) {
+LayerKernel pick_attn_waves(int group, bool nt, bool f8, bool mix = false, bool pg = false) {
 #define ASR_PICK_WAVES(G) \
-  case G: return mix ? (f8 ? k_attn_waves<DT, G, false, true, true> : k_attn_waves<DT, G, false, false, true>) \
+  case G: \
+    if (pg) return f8 ? nullptr : (mix ? k_attn_waves<DT, G, false, false, true, true> \
+                                       : (nt ? k_attn_waves<DT, G, true, false, false, true> \
+                                             : k_attn_waves<DT, G, false, false, false, true>)); \
+    return mix ? (f8 ? k_attn_waves<DT, G, false, true, true> : k_attn_waves<DT, G, false, false, true>) \
                : f8 ? (nt ? k_attn_waves<DT, G, true, true> : k_attn_waves<DT, G, false, true>) \
                     : (nt ? k_attn_waves<DT, G, true, false> : k_attn_waves<DT, G, false, false>);
   switch (group) {
@@ -3270,7 +3316,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                           lds_vmfma_bytes(a.B), s, ev, 1, a)) != hipSuccess)
       return e;
   } else if (attn_waves_used(a)) {
-    if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1, a.kv8 != 0, a.qo_n != 0), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
+    if ((e = launch_phase(pick_attn_waves<DT>(a.group, a.n == 1, a.kv8 != 0, a.qo_n != 0, a.ptab != nullptr), dim3(attn_grid), dim3(256), lds_attn_waves_bytes(a.rows), s,
                           ev, 1, a)) != hipSuccess)
       return e;
   } else if ((e = launch_phase(pick_attn<DT>(a.group, a.qo_n != 0, a.ptab != nullptr), dim3(attn_grid), dim3(256), lds_attn_bytes(a.rows, a.n), s,
@@ -3363,25 +3409,24 @@ int attn_vmfma_grid(int dtype, int group, int n, int B, int cus) {
 }
 
 // (group 8 would hold its 8 q vectors and accumulators past the register file)
-// (paged caches take the chunked kernel: its chunks hold the page ids of their keys)
-bool attn_waves_used(const LayerArgs &a) { return a.mfma && !a.ptab && (a.group == 2 || a.group == 4); }
+bool attn_waves_used(const LayerArgs &a) { return a.mfma && (a.group == 2 || a.group == 4); }
 
 // Resident grid of the equal-share attention kernel: blocks per CU from the
 // occupancy calculator (at the largest row table) times the CU count.
-int attn_waves_grid(int dtype, int group, int cus, bool mix) {
-  // occupancy per (dtype, group, mixed), computed once per process; calls from
+int attn_waves_grid(int dtype, int group, int cus, bool mix, bool paged) {
+  // occupancy per (dtype, group, mixed, paged), computed once per process; calls from
   // several threads may each compute it, they store the same value
-  static std::atomic<int> cached[2][9][2];
-  const int di = dtype == ASR_BF16 ? 1 : 0, mi = mix ? 1 : 0;
+  static std::atomic<int> cached[2][9][2][2];
+  const int di = dtype == ASR_BF16 ? 1 : 0, mi = mix ? 1 : 0, pi = paged ? 1 : 0;
   if (group != 2 && group != 4) return 0;
-  int per_cu = cached[di][group][mi].load(std::memory_order_relaxed);
+  int per_cu = cached[di][group][mi][pi].load(std::memory_order_relaxed);
   if (per_cu <= 0) {
-    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, !mix, false, mix)
-                                            : pick_attn_waves<ASR_F16>(group, !mix, false, mix);
+    const LayerKernel k = dtype == ASR_BF16 ? pick_attn_waves<ASR_BF16>(group, !mix, false, mix, paged)
+                                            : pick_attn_waves<ASR_F16>(group, !mix, false, mix, paged);
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, lds_attn_waves_bytes(kMaxLayerRows)) !=
                   hipSuccess || per_cu <= 0)
       return 0;
-    cached[di][group][mi].store(per_cu, std::memory_order_relaxed);
+    cached[di][group][mi][pi].store(per_cu, std::memory_order_relaxed);
   }
   return per_cu * cus;
 }

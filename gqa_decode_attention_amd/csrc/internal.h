@@ -151,7 +151,7 @@ size_t layer_dyn_smem(const LayerArgs &a);
 bool attn_waves_used(const LayerArgs &a);
 bool attn_vmfma_used(const LayerArgs &a);
 int attn_vmfma_grid(int dtype, int group, int n, int B, int cus);
-int attn_waves_grid(int dtype, int group, int cus, bool mix);
+int attn_waves_grid(int dtype, int group, int cus, bool mix, bool paged);
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
                             const int32_t *slots, int B, int n, hipStream_t s);
 hipError_t launch_kv_crop(const asr_kv_layer *layers, int n_layers, const int32_t *new_lens,

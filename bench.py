@@ -303,6 +303,8 @@ def main():
 
     verify = None if args.no_verify else verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs,
                                                     base_lens, H, NL, dtype, sid, P0)
+    paged1 = None if args.no_paged else bs1_paged_leg(args, ga, si, np, torch, dev, to_dev, stream, cfg, weights, xs,
+                                                      outs, ws, H, NL, dtype, sid, P0, NSTEP, args.page_size)
 
     result = {
         "metric": "attn-block us/token (28 layers, bs1) + batched tok/s; % HBM roofline",
@@ -331,6 +333,8 @@ def main():
 
     if verify is not None:
         result["verify"] = verify
+    if paged1 is not None:
+        result["bs1_paged"] = paged1
     if not args.no_loop:
         result["verify_loop"] = loop_leg(args, ga, si, np, torch, dev, to_dev, stream)
     if not args.no_batched:
@@ -344,6 +348,60 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bs1_paged_leg(args, ga, si, np, torch, dev, to_dev, stream, cfg, weights, xs, outs, ws, H, NL, dtype, sid, P0,
+                  NSTEP, page):
+    """The headline bs1 steps with every layer's cache a pool of `page`-row pages in shuffled
+    order (the same prompt rows, inputs and timed steps)."""
+    pps = CAP_BS1 // page
+    table = torch.from_numpy(si.page_table(sid, 1, pps, pps)).to(dev)
+    kvs = []
+    for l in range(NL):
+        kb, vb = si.kv_rows(sid, l, 0, P0, dtype)
+        kv = ga.KVLayer.paged(pps, 8, page, table, dtype=torch.float16, device=dev)
+        for bits, pool in ((kb, kv.k), (vb, kv.v)):
+            full = torch.zeros((8, CAP_BS1, 128), dtype=torch.float16, device=dev)
+            full[:, :P0] = to_dev(bits, dtype)
+            pool[table[0].long()] = full.view(8, pps, page, 128).transpose(0, 1)
+        kv.lens.fill_(P0)
+        kvs.append(kv)
+    base = torch.full((1,), P0, dtype=torch.int32, device=dev)
+    graphs = []
+    for s_ in range(NSTEP):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(NL):
+                ga.layer_decode(cfg, weights[l], kvs[l], xs[s_, l], outs[l], ws, host_lens=[P0 + s_])
+        graphs.append(g)
+    crop = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(crop):
+        ga.kv_crop(kvs, base)
+    ga.kv_crop(kvs, base)
+    torch.cuda.synchronize()
+
+    def run(n):
+        for i in range(n):
+            graphs[i % NSTEP].replay()
+            if i % NSTEP == NSTEP - 1:
+                crop.replay()
+
+    run(args.warmup)
+    crop.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    run(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_token = ev0.elapsed_time(ev1) / args.steps * 1000.0
+    ok = all(int(kv.status.item()) == 0 for kv in kvs) and all(
+        int(kv.lens.item()) == P0 + (args.steps % NSTEP) for kv in kvs)
+    del graphs, crop, kvs
+    torch.cuda.empty_cache()
+    print(f"[bench] bs1 paged cache ({page}-row pages): {us_token:.1f} us/token (ok {ok})", file=sys.stderr, flush=True)
+    return {"workload": f"the bs1 steps above on paged caches of {page}-row pages in shuffled order",
+            "value": round(us_token, 3), "unit": "us/token", "page_size": page, "ok": ok}
 
 
 def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False, page=0):

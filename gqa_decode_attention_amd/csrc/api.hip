@@ -219,8 +219,8 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.eps = cfg->rms_eps;
   a.theta = cfg->rope_theta;
   a.out_f32 = cfg->out_dtype == ASR_F32;
-  // mixed blocks and paged caches run on the many-row kernels whatever the row count
-  a.mfma = rows > kVectorRows || n_per_seq != nullptr || kv->block_table != nullptr;
+  // mixed blocks run on the many-row kernels whatever the row count
+  a.mfma = rows > kVectorRows || n_per_seq != nullptr;
   a.oproj_split = 0;
   a.vm_items = 0;
   a.kv8 = kv8;

@@ -2014,6 +2014,7 @@ struct FewShared {
 struct FewGeom {
   int L, t0, t1, nb, n_new, tw, nsteps, last_row;
   size_t kvrow0;
+  int slot, g;
 };
 
 template <int NW>
@@ -2025,15 +2026,33 @@ __device__ __forceinline__ FewGeom few_geom(const LayerArgs &A, int slot, int g,
   G.nb = max(G.t0, L);
   G.n_new = max(0, G.t1 - G.nb);
   G.kvrow0 = ((size_t)slot * A.nkv + g) * A.capacity;
+  G.slot = slot;
+  G.g = g;
   G.tw = G.t0 + wave_id() * 8;
   G.nsteps = G.tw < G.t1 ? (G.t1 - G.tw + NW * 8 - 1) / (NW * 8) : 0;
   G.last_row = max(min(G.t1, L) - 1, 0);
   return G;
 }
 
-template <int NW>
+// PG (paged cache): a step's rows, 8-aligned and clamped to the chunk's last
+// committed row, lie in one page (a page holds at least 16 rows), whose id is a
+// wave-uniform value; an id outside the pool (possible for rows requested
+// before the length is known, which are then never used) reads page 0.
+template <int NW, bool PG = false>
 __device__ __forceinline__ void few_load_step(const LayerArgs &A, const FewGeom &G, uint4 (&r)[4], int i) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
+  if constexpr (PG) {
+    const int t = G.tw + NW * 8 * i;
+    const int pid = page_entry(A, G.slot, min(t, G.last_row) >> A.plog);
+    const int page = (unsigned)pid < (unsigned)A.npages ? pid : 0;
+    const int row = min(t + kr, G.last_row);
+    const size_t e = (((size_t)page * A.nkv + G.g) * A.psz + (row & (A.psz - 1))) * kHeadDim + kl * 8;
+    r[0] = ld16(A.kc + e);
+    r[1] = ld16(A.kc + e + 64);
+    r[2] = ld16(A.vc + e);
+    r[3] = ld16(A.vc + e + 64);
+    return;
+  }
   const uint32_t region = (uint32_t)A.capacity * kHeadDim * 2;
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + G.kvrow0 * kHeadDim, region);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + G.kvrow0 * kHeadDim, region);
@@ -2044,7 +2063,7 @@ __device__ __forceinline__ void few_load_step(const LayerArgs &A, const FewGeom 
   r[3] = ld_buf(Vr, off + 128);
 }
 
-template <int DT, int GROUP, int NW, int NP>
+template <int DT, int GROUP, int NW, int NP, bool PG = false>
 __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G, int row, int g, int c,
                                            const float (&q)[GROUP][16], const uint16_t *knew, const uint16_t *vnew,
                                            FewShared<NW, GROUP> &S, uint4 (&r)[NP][4]) {
@@ -2136,8 +2155,8 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
     if (nsteps > NP) {
       uint4 (&ra)[4] = r[0];
       uint4 (&rb)[4] = r[NP - 1];
-      few_load_step<NW>(A, G, ra, NP);
-      few_load_step<NW>(A, G, rb, NP + 1);
+      few_load_step<NW, PG>(A, G, ra, NP);
+      few_load_step<NW, PG>(A, G, rb, NP + 1);
       auto online = [&](const uint4 (&rr)[4], int i) __attribute__((always_inline)) {
         float s[GROUP];
         score(rr, i, with_new, s);
@@ -2158,9 +2177,9 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
       int i = NP;
       for (; i + 2 < nsteps; i += 2) {
         online(ra, i);
-        few_load_step<NW>(A, G, ra, i + 2);
+        few_load_step<NW, PG>(A, G, ra, i + 2);
         online(rb, i + 1);
-        few_load_step<NW>(A, G, rb, i + 3);
+        few_load_step<NW, PG>(A, G, rb, i + 3);
       }
       if (i < nsteps) online(ra, i);
       if (i + 1 < nsteps) online(rb, i + 1);
@@ -2219,7 +2238,7 @@ __device__ __forceinline__ void few_stream(const LayerArgs &A, const FewGeom &G,
   __syncthreads();
 }
 
-template <int DT, int GROUP, int NW, int NP>
+template <int DT, int GROUP, int NW, int NP, bool PG = false>
 __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ FewShared<NW, GROUP> S;
@@ -2236,7 +2255,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
   G0.last_row = A.capacity - 1;
   uint4 rr[NP][4];
 #pragma unroll
-  for (int k = 0; k < NP; ++k) few_load_step<NW>(A, G0, rr[k], k);
+  for (int k = 0; k < NP; ++k) few_load_step<NW, PG>(A, G0, rr[k], k);
   QLoads<GROUP> Q;
   q_loads<GROUP>(A, row, g, Q);
   const bool has_fresh = wave <= r_off;   // sequence row `wave`, position L + wave, is visible to `row`
@@ -2260,7 +2279,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
     const FewGeom G = few_geom<NW>(A, ri.slot, g, ri.L, ri.nvis, c);
     if (c != c0) {
 #pragma unroll
-      for (int k = 0; k < NP; ++k) few_load_step<NW>(A, G, rr[k], k);
+      for (int k = 0; k < NP; ++k) few_load_step<NW, PG>(A, G, rr[k], k);
     }
     if (G.n_new > 0) {
       const int i = ri.L + wave - G.nb;   // this wave's row among the chunk's appended ones
@@ -2270,14 +2289,32 @@ __global__ __launch_bounds__(NW * 64) void k_attn_few(LayerArgs A) {
         reinterpret_cast<uint32_t *>(knew + i * kHeadDim)[lane] = kb;
         reinterpret_cast<uint32_t *>(vnew + i * kHeadDim)[lane] = vb;
         if (wave == r_off) {   // every row also stores its own appended row in the cache
-          const size_t off = (G.kvrow0 + ri.L + wave) * kHeadDim;
-          reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
-          reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+          size_t off = (G.kvrow0 + ri.L + wave) * kHeadDim;
+          bool store = true;
+          if constexpr (PG) {   // row (L + wave) % psz of its page; not stored for an id outside the pool
+            const int t = ri.L + wave;
+            const int pid = page_entry(A, ri.slot, t >> A.plog);
+            store = (unsigned)pid < (unsigned)A.npages;
+            off = (((size_t)(store ? pid : 0) * A.nkv + g) * A.psz + (t & (A.psz - 1))) * kHeadDim;
+          }
+          if (store) {
+            reinterpret_cast<uint32_t *>(A.kc + off)[lane] = kb;
+            reinterpret_cast<uint32_t *>(A.vc + off)[lane] = vb;
+          }
         }
       }
       __syncthreads();
     }
-    few_stream<DT, GROUP, NW, NP>(A, G, row, g, c, q, knew, vnew, S, rr);
+    few_stream<DT, GROUP, NW, NP, PG>(A, G, row, g, c, q, knew, vnew, S, rr);
+    if constexpr (PG) {
+      // the chunk's pages, now that its keys are known: an id outside the pool is reported
+      if (wave == 0) {
+        const int p0 = G.t0 >> A.plog, npg = ((G.t1 - 1) >> A.plog) - p0 + 1;
+        const int pid = A.ptab[(size_t)ri.slot * A.pps + min(p0 + lane, A.pps - 1)];
+        if (__any(lane < npg && (unsigned)pid >= (unsigned)A.npages) && lane == 0 && A.status)
+          atomicOr(A.status, kStatusBadPage);
+      }
+    }
   }
 }
 
@@ -3185,14 +3222,14 @@ LayerKernel pick_attn(int group, bool mix, bool paged) {
 }
 
 template <int DT>
-LayerKernel pick_attn_few(int group) {
+LayerKernel pick_attn_few(int group, bool paged) {
   // eight waves (two per SIMD) while the registers of a group allow, else four;
   // two steps of every wave requested before any arithmetic
   switch (group) {
-    case 1: return k_attn_few<DT, 1, 8, 2>;
-    case 2: return k_attn_few<DT, 2, 8, 2>;
-    case 4: return k_attn_few<DT, 4, 4, 2>;
-    case 8: return k_attn_few<DT, 8, 4, 2>;
+    case 1: return paged ? k_attn_few<DT, 1, 8, 2, true> : k_attn_few<DT, 1, 8, 2>;
+    case 2: return paged ? k_attn_few<DT, 2, 8, 2, true> : k_attn_few<DT, 2, 8, 2>;
+    case 4: return paged ? k_attn_few<DT, 4, 4, 2, true> : k_attn_few<DT, 4, 4, 2>;
+    case 8: return paged ? k_attn_few<DT, 8, 4, 2, true> : k_attn_few<DT, 8, 4, 2>;
     default: return nullptr;
   }
 }
@@ -3303,7 +3340,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
   if (!a.mfma) {
     // a few rows: partials only, merged by the o_proj kernel
     const unsigned lds_kv = (unsigned)(a.n * kHeadDim * 2 * sizeof(uint16_t));
-    if ((e = launch_phase(pick_attn_few<DT>(a.group), dim3(a.rows * a.nkv * a.nch_host), dim3(few_waves(a.group) * kWave),
+    if ((e = launch_phase(pick_attn_few<DT>(a.group, a.ptab != nullptr), dim3(a.rows * a.nkv * a.nch_host), dim3(few_waves(a.group) * kWave),
                           lds_kv, s, ev, 1, a)) != hipSuccess)
       return e;
     const int halves = a.oproj_split ? 2 : 1, rpw = a.oproj_split ? 2 : kRpwD;

@@ -158,9 +158,9 @@ typedef struct asr_attn_weights {
  * id outside [0, num_pages) for a position a call needs sets
  * ASR_STATUS_BAD_PAGE, and that sequence's output rows, appended rows and
  * length are then unspecified (nothing outside the pool is read or written).
- * Layer calls on a paged cache run the matrix-core projections and the
- * chunked split-KV attention whatever the row count (the stream-ordered
- * dispatch; the fused dispatch returns ASR_EUNSUPPORTED).
+ * Layer calls on a paged cache take the kernels they take on a contiguous
+ * cache, except that verify blocks attend on the vector units rather than the
+ * matrix cores; the fused dispatch returns ASR_EUNSUPPORTED.
  */
 typedef struct asr_kv_layer {
   void *k;              /* [batch_cap][n_kv_heads][capacity][head_dim], elements of dtype

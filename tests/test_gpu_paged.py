@@ -144,11 +144,14 @@ def test_paged_vs_oracle(case, dtype):
 
 
 @pytest.mark.parametrize("nq,nkv,sizes,P", [(16, 2, [3, 5, 1, 7], 16), (8, 8, [1] * 6, 64), (8, 8, [4] * 3, 32),
-                                            (16, 8, [1] * 6, 16), (16, 4, [2, 5, 1, 3], 64), (16, 8, [1, 1, 8], 32)])
+                                            (16, 8, [1] * 6, 16), (16, 4, [2, 5, 1, 3], 64), (16, 8, [1, 1, 8], 32),
+                                            (16, 8, [1], 64), (16, 8, [1, 1, 1], 16), (16, 2, [4], 32),
+                                            (8, 8, [2, 2], 16)])
 def test_paged_equals_the_contiguous_cache_on_the_same_kernel(nq, nkv, sizes, P):
     """The paged call runs the contiguous call's kernel with another address map (the chunked
-    kernel for GQA groups 1 and 8, the equal-share kernel for groups 2 and 4, decode and mixed
-    rows), so it gives the same bits: output and appended rows alike."""
+    kernel for GQA groups 1 and 8, the equal-share kernel for groups 2 and 4, the few-row kernel
+    for up to 4 rows; decode, verify and mixed rows), so it gives the same bits: output and
+    appended rows alike."""
     dtype = si.BF16
     B, rows = len(sizes), sum(sizes)
     lens = [300, 17, 0, 128, 64, 255][:B]

@@ -13,7 +13,6 @@ namespace {
 
 constexpr int kMaxRows = kMaxLayerRows;
 constexpr int kMinShare = 64;    // least keys per wave share of the many-row attention
-constexpr int kVectorRows = 4;   // up to this many rows the projections run as vector-ALU GEMVs
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }

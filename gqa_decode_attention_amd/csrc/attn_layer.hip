@@ -233,20 +233,26 @@ __device__ __forceinline__ void qkv_tile(const LayerArgs &A, int tile, float (*s
   gq16[3] = gp[tb + 64];
   // rotary angles of the first row block while the loads travel: the rows'
   // positions come through scalar loads, which do not wait on vector loads.
-  // Lane 2r computes pair ta of row rb + r, lane 2r + 1 pair tb.
-  const double om_a = exp2(-(2.0 * ta / kHeadDim) * log2((double)A.theta));
-  const double om_b = exp2(-(2.0 * tb / kHeadDim) * log2((double)A.theta));
+  // Lane 2r computes pair ta of row rb + r, lane 2r + 1 pair tb: each lane
+  // selects its position among the block's and takes one fp64 sincos.
+  const int tl = (lane & 1) ? tb : ta;
+  const double om = exp2(-(2.0 * tl / kHeadDim) * log2((double)A.theta));
   auto angles = [&](int rb, float &cs_c, float &cs_s) __attribute__((always_inline)) {
     cs_c = 1.f;
     cs_s = 0.f;
     if (rot) {
+      int pos = 0;
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        if (rb + r < A.rows && lane / 2 == r) {
-          const float2 c = rope_cs(rope_pos(A, rb + r, (lane & 1) ? tb : ta), (lane & 1) ? om_b : om_a);
-          cs_c = c.x;
-          cs_s = c.y;
+        if (rb + r < A.rows) {
+          const int pa = rope_pos(A, rb + r, ta), pb = rope_pos(A, rb + r, tb);
+          if (lane >> 1 == r) pos = (lane & 1) ? pb : pa;
         }
+      }
+      if ((lane >> 1) < RB && rb + (lane >> 1) < A.rows) {
+        const float2 c = rope_cs(pos, om);
+        cs_c = c.x;
+        cs_s = c.y;
       }
     }
   };
@@ -1669,33 +1675,34 @@ constexpr int chunk_steps(int kq) {
 // as whole 128-byte lines (four rows per instruction) into its own LDS region
 // and reads the operand layout back from there: the operand layout touches 16
 // rows per load, half a line each, and a CU keeps only so many lines in flight.
-template <int DT, int KQ, int NWV, bool LX, bool MIX = false>
+template <int DT, int KQ, int NWV, bool LX, bool MIX = false, int NTL = 4>
 __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
+  constexpr int BR = 16 * NTL;          // rows per block: NTL row tiles of 16
   constexpr int KW = KQ * 4 / NWV;      // 32-wide steps of this wave's share of the contraction
   constexpr int KC = KW < 8 ? KW : 8;   // steps per operand batch (x of four row tiles)
   static_assert(!LX || (KQ == 8 && NWV == 8), "x staging: 16 KB per wave");
-  extern __shared__ __align__(16) unsigned char dyn[];   // LX: [NWV][64 rows][256 B] x, then the wave's sums
-  __shared__ f32x4_t s_cs[LX ? 1 : NWV][4][kWave];
-  __shared__ float s_ss[NWV][64];
-  __shared__ float2 s_rope[64][8];   // (cos, sin) for the block's 64 rows x its 8 rotary pairs
+  extern __shared__ __align__(16) unsigned char dyn[];   // LX: [NWV][BR rows][256 B] x, then the wave's sums
+  __shared__ f32x4_t s_cs[LX ? 1 : NWV][NTL][kWave];
+  __shared__ float s_ss[NWV][BR];
+  __shared__ float2 s_rope[BR][8];   // (cos, sin) for the block's rows x its 8 rotary pairs
   // the waves' sums: LX in each wave's own staging region (its x is read by then)
   auto s_c_at = [&](int wv, int nt) __attribute__((always_inline)) -> f32x4_t * {
     if constexpr (LX) return reinterpret_cast<f32x4_t *>(dyn + wv * 16384) + nt * kWave;
     else return &s_cs[wv][nt][0];
   };
   const int wave = wave_id(), lane = lane_id();
-  const int rtiles = (A.rows + 63) / 64;
+  const int rtiles = (A.rows + BR - 1) / BR;
   const TileMap tm = tile_of(blockIdx.x, rtiles);
-  const int tile = tm.col, nb = tm.row * 64;
+  const int tile = tm.col, nb = tm.row * BR;
   const int head = tile / kTilesPerHead, jj = tile % kTilesPerHead, t0 = 8 * jj;
   const int i16 = lane % 16, g4 = lane / 16;
   const int arow = head * kHeadDim + (i16 < 8 ? t0 + i16 : 64 + t0 + i16 - 8);
   const int H = A.H;
   const int kq0 = wave * (H / NWV) + g4 * 8;     // this lane's first k
   const uint16_t *wp = A.w_qkv + (size_t)arow * H + kq0;
-  const uint16_t *xr[4];
+  const uint16_t *xr[NTL];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) xr[nt] = A.x + (size_t)min(nb + nt * 16 + i16, A.rows - 1) * H + kq0;
+  for (int nt = 0; nt < NTL; ++nt) xr[nt] = A.x + (size_t)min(nb + nt * 16 + i16, A.rows - 1) * H + kq0;
   if (blockIdx.x == 0) write_row_table<false, MIX>(A);
   const bool rot = head < A.nq + A.nkv;
   const uint16_t *gp = head < A.nq ? A.g_q : A.g_k;
@@ -1706,17 +1713,17 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
     for (int j = 0; j < 4; ++j) gq4[j] = cvt16<DT>(gp[t0 + (g4 & 1) * 4 + j + (g4 < 2 ? 0 : 64)]);
   }
 
-  f32x4_t acc[4];
-  float ss[4];
+  f32x4_t acc[NTL];
+  float ss[NTL];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NTL; ++nt) {
     acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     ss[nt] = 0.f;
   }
 #pragma unroll 1
   for (int c0 = 0; c0 < KW; c0 += KC) {
-    uint4 w[KC], g[KC], x[4][KC];
-    uint4 xl[LX ? 16 : 1];
+    uint4 w[KC], g[KC], x[NTL][KC];
+    uint4 xl[LX ? 4 * NTL : 1];
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
       if constexpr (LX) {   // W too as whole lines: instruction s, rows 4 s .. 4 s + 3 of the tile
@@ -1729,19 +1736,19 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
       g[s] = ld16(A.g_in + kq0 + (c0 + s) * 32);
       if constexpr (!LX) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) x[nt][s] = ld16(xr[nt] + (c0 + s) * 32);
+        for (int nt = 0; nt < NTL; ++nt) x[nt][s] = ld16(xr[nt] + (c0 + s) * 32);
       }
     }
     if constexpr (LX) {   // instruction j: rows 4 j .. 4 j + 3, sixteen 16-byte chunks each
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < 4 * NTL; ++j) {
         const int f = j * 64 + lane, r = f >> 4, ch = f & 15;
         xl[j] = ld16(A.x + (size_t)min(nb + r, A.rows - 1) * H + wave * (H / NWV) + ch * 8);
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
-    if (c0 == 0 && rot) {   // rotary angles of the 64 rows x 8 pairs in fp64 while the operands travel
-      for (int idx = threadIdx.x; idx < 64 * 8; idx += NWV * 64) {
+    if (c0 == 0 && rot) {   // rotary angles of the block's rows x 8 pairs in fp64 while the operands travel
+      for (int idx = threadIdx.x; idx < BR * 8; idx += NWV * 64) {
         const int r = idx / 8, tt = idx % 8;
         const int n = nb + r;
         float cs = 1.f, sn = 0.f;
@@ -1759,7 +1766,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
       unsigned char *xw = dyn + wave * 16384;
       wave_lds_sync();   // the previous batch's reads of the region are done
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < 4 * NTL; ++j) {
         const int f = j * 64 + lane, r = f >> 4, ch = f & 15;
         *reinterpret_cast<uint4 *>(xw + r * 256 + ((ch ^ (r & 15)) << 4)) = xl[j];
       }
@@ -1767,7 +1774,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
 #pragma unroll
       for (int s = 0; s < KC; ++s)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NTL; ++nt) {
           const int r = nt * 16 + i16, ch = s * 4 + g4;
           x[nt][s] = lds_ld16(reinterpret_cast<const uint16_t *>(xw + r * 256 + ((ch ^ (r & 15)) << 4)));
         }
@@ -1797,7 +1804,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
         split8<DT>(p, ahi, alo);
       }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NTL; ++nt) {
         float xf[8];
         unpack8<DT>(x[nt][s], xf);
 #pragma unroll
@@ -1809,7 +1816,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
   }
   if constexpr (LX) wave_lds_sync();   // W reads done before the sums overwrite the region
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NTL; ++nt) {
     s_c_at(wave, nt)[lane] = acc[nt];
     float v = ss[nt];
     v = xsum<16>(v);
@@ -1817,7 +1824,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
     if (g4 == 0) s_ss[wave][nt * 16 + i16] = v;
   }
   __syncthreads();
-  if (wave < 4) {   // wave nt finishes row tile nt
+  if (wave < NTL) {   // wave nt finishes row tile nt
     const int nt = wave;
     const int n = nb + nt * 16 + i16;
     f32x4_t c = s_c_at(0, nt)[lane];
@@ -2902,12 +2909,18 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
         av[s2][c] = *reinterpret_cast<const float4 *>(part_of(row, h0 + q4 / 32, c) + (q4 % 32) * 4);
     }
   };
-  // The first row's merge inputs are requested before the W_o rows: a wait on a
-  // load waits on every load issued before it, so the merge runs while W_o travels.
-  int4 rt_0;
-  float2 ml0_0;
-  float4 av_0[NS][CB];
-  merge_loads(0, rt_0, ml0_0, av_0);
+  // The merge inputs of the first RP rows (as many as 128 registers hold) are
+  // requested before the W_o rows: a wait on a load waits on every load issued
+  // before it, so they arrive in one round trip and the merges run while W_o
+  // travels; rows past RP (more chunks per row) request theirs one row at a time.
+  constexpr int RP = 128 / (NS * CB * 4) < 1 ? 1 : (128 / (NS * CB * 4) > kVectorRows ? kVectorRows
+                                                                                    : 128 / (NS * CB * 4));
+  int4 rt_p[RP];
+  float2 ml0_p[RP];
+  float4 av_p[RP][NS][CB];
+#pragma unroll
+  for (int r = 0; r < RP; ++r)
+    if (r < A.rows) merge_loads(r, rt_p[r], ml0_p[r], av_p[r]);
   __builtin_amdgcn_sched_barrier(0);
   uint4 wr[RPW][KV];
   {
@@ -2918,15 +2931,8 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       for (int v = 0; v < KV; ++v)
         wr[i][v] = ld16_stream(A.w_o + (size_t)(o0 + i) * Kw + hh * K + (v * 64 + lane_id()) * 8);
   }
-  for (int row = 0; row < A.rows; ++row) {
-    int4 rt = rt_0;
-    float2 ml0 = ml0_0;
-    float4 av[NS][CB];
-#pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2)
-#pragma unroll
-      for (int c = 0; c < CB; ++c) av[s2][c] = av_0[s2][c];
-    if (row > 0) merge_loads(row, rt, ml0, av);
+  auto merge_row = [&](int row, const int4 &rt, const float2 &ml0, const float4 (&av)[NS][CB])
+                       __attribute__((always_inline)) {
     const int nch = chunks_of(rt.x ? rt.y + (row - seq_row0(A, seq_of(A, row))) + 1 : 0, A.split);
     // weights
     float mx = cq < nch ? ml0.x : -INFINITY;
@@ -2969,6 +2975,16 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       if (q4 < K4) reinterpret_cast<float4 *>(xs + (size_t)row * K)[q4] = num;
     }
     __syncthreads();   // s_w is reused by the next row
+  };
+#pragma unroll
+  for (int r = 0; r < RP; ++r)
+    if (r < A.rows) merge_row(r, rt_p[r], ml0_p[r], av_p[r]);
+  for (int row = RP; row < A.rows; ++row) {
+    int4 rt;
+    float2 ml0;
+    float4 av[NS][CB];
+    merge_loads(row, rt, ml0, av);
+    merge_row(row, rt, ml0, av);
   }
   __syncthreads();
   const int wave = wave_id(), lane = lane_id();
@@ -3172,22 +3188,28 @@ struct MfmaKernel {
 
 // LX / LW instances stage each wave's operand lines through LDS: 16 KB (x, then
 // W) or 8 KB (W_o) per wave
-template <int DT, bool MIX>
+template <int DT, bool MIX, int NTL>
 MfmaKernel pick_qkv_mfma_t(int kq) {
   switch (kq) {
-    case 4: return {k_qkv_mfma<DT, 4, 8, false, MIX>, 0};
-    case 8: return {k_qkv_mfma<DT, 8, 8, true, MIX>, 8 * 16384};
-    case 12: return {k_qkv_mfma<DT, 12, 8, false, MIX>, 0};
-    case 16: return {k_qkv_mfma<DT, 16, 8, false, MIX>, 0};
-    case 20: return {k_qkv_mfma<DT, 20, 4, false, MIX>, 0};
-    case 24: return {k_qkv_mfma<DT, 24, 4, false, MIX>, 0};
-    case 28: return {k_qkv_mfma<DT, 28, 4, false, MIX>, 0};
-    case 32: return {k_qkv_mfma<DT, 32, 4, false, MIX>, 0};
+    case 4: return {k_qkv_mfma<DT, 4, 8, false, MIX, NTL>, 0};
+    case 8: return {k_qkv_mfma<DT, 8, 8, true, MIX, NTL>, 8 * 16384};
+    case 12: return {k_qkv_mfma<DT, 12, 8, false, MIX, NTL>, 0};
+    case 16: return {k_qkv_mfma<DT, 16, 8, false, MIX, NTL>, 0};
+    case 20: return {k_qkv_mfma<DT, 20, 4, false, MIX, NTL>, 0};
+    case 24: return {k_qkv_mfma<DT, 24, 4, false, MIX, NTL>, 0};
+    case 28: return {k_qkv_mfma<DT, 28, 4, false, MIX, NTL>, 0};
+    case 32: return {k_qkv_mfma<DT, 32, 4, false, MIX, NTL>, 0};
     default: return {nullptr, 0};
   }
 }
+// row tiles of 16 per block: one for calls of at most 16 rows (verify blocks of a
+// sequence or two), else four (the weight tile's loads shared by 64 rows)
+constexpr int qkv_row_tiles(int rows, bool mix) { return !mix && rows <= 16 ? 1 : 4; }
 template <int DT>
-MfmaKernel pick_qkv_mfma(int kq, bool mix) { return mix ? pick_qkv_mfma_t<DT, true>(kq) : pick_qkv_mfma_t<DT, false>(kq); }
+MfmaKernel pick_qkv_mfma(int kq, bool mix, int ntl) {
+  if (mix) return pick_qkv_mfma_t<DT, true, 4>(kq);
+  return ntl == 1 ? pick_qkv_mfma_t<DT, false, 1>(kq) : pick_qkv_mfma_t<DT, false, 4>(kq);
+}
 
 template <int DT, bool MIX>
 MfmaKernel pick_oproj_mfma_t(int kq) {
@@ -3327,8 +3349,9 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
   hipError_t e;
   if (a.mfma) {
     // contraction quarters of 32-wide steps: H / 128 (QKV) and nq d / 128 (o_proj)
-    const int rtiles = (a.rows + 63) / 64;
-    const MfmaKernel kq = pick_qkv_mfma<DT>(a.H / 128, a.qo_n != 0);
+    const int ntl = qkv_row_tiles(a.rows, a.qo_n != 0);
+    const int rtiles = (a.rows + 16 * ntl - 1) / (16 * ntl);
+    const MfmaKernel kq = pick_qkv_mfma<DT>(a.H / 128, a.qo_n != 0, ntl);
     if ((e = launch_phase(kq.fn, dim3(a.nqkv / 16 * rtiles), dim3(qkv_mfma_waves(a.H / 128) * kWave), kq.lds, s, ev,
                           0, a)) != hipSuccess)
       return e;

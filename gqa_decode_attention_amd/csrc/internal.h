@@ -15,6 +15,7 @@ constexpr int kMinSplit = 16;         // keys per chunk, lower bound
 constexpr int kMaxSplit = 1024;       // keys per chunk, upper bound
 constexpr int kMaxVerifyK = 32;
 constexpr int kMaxLayerRows = 2048;   // rows (B k) per layer call
+constexpr int kVectorRows = 4;        // up to this many rows the projections run as vector-ALU GEMVs
 constexpr int kMaxKvHeads = 32;       // n_q_heads * head_dim <= 4096 bounds both head counts
 constexpr int kVmMaxSeqs = 64;        // sequences of a verify call whose work items the host lays out
 constexpr int kFlowWords = 128;      // counters of the one-dispatch path (heads + 4 totals)

@@ -54,13 +54,14 @@ PAGES_US_PER_TOKEN = 9033.0
 # outputs are rounded to 16 bits apart
 NEAR_TIE = 5e-3
 # HBM bytes per launch of each phase kernel from the FETCH_SIZE and WRITE_SIZE counters, each
-# scaled by what that counter reads for a 1 GiB device copy (fetch x1.99995, write x1.000), and
+# scaled by what that counter reads for a 1 GiB device copy (fetch x1.99992, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "7eda89780d4af1960861499c6162c4fcfe6860d8273ca2be8cb396abdc7adc46",
-    "bs1": {"qkv_projection": 8577996, "attention": 4057708, "o_proj": 4851740},
-    "b64": {"qkv_projection": 11086773, "attention": 230490285, "o_proj": 8708341},
-    "b64_fp8": {"qkv_projection": 11086773, "attention": 120117138, "o_proj": 8708341},
+    "sources_sha256": "8fbaa708d02d93f7aed4e17489feca6620f0e196a845382c6f4dde756c3fba6d",
+    "bs1": {"qkv_projection": 8564587, "attention": 4071965, "o_proj": 4913255},
+    "b64": {"qkv_projection": 11078472, "attention": 230492568, "o_proj": 8708347},
+    "b64_fp8": {"qkv_projection": 11078472, "attention": 120122860, "o_proj": 8708347},
+    "b64_paged": {"qkv_projection": 11078472, "attention": 230698977, "o_proj": 8708347},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",

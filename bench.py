@@ -13,10 +13,12 @@ The timed region starts a round at step 0 and covers exactly ``--steps``
 steps; ``config.workload`` names the committed lengths it covered.
 
 Other legs (each can be skipped): ragged batched decode of 64 sequences in
-bf16, committed lengths uniform in [200, 1500], with a 16-bit and with an FP8
-(E4M3) cache (``--no-batched``, ``--no-fp8``); the bs1 verify block for
-k = 4, 8, 16 (``--no-verify``); the hidden-2048 batch-64 decode with a k = 8
-verify on 8 sequences (``--no-wide``).  Every leg reports its own roofline
+bf16, committed lengths uniform in [200, 1500], with a 16-bit, an FP8 (E4M3)
+and a paged 16-bit cache (``--no-batched``, ``--no-fp8``, ``--no-paged``); the
+bs1 steps on paged caches (``--no-paged``; ``--page-size`` rows per page); the
+bs1 verify block for k = 4, 8, 16 (``--no-verify``); the hidden-2048 batch-64
+decode with a k = 8 verify on 8 sequences (``--no-wide``); the whole decoder's
+greedy and speculative decoding (``--no-loop``).  Every leg reports its own roofline
 (algorithmic bytes over the measured time, against 8 TB/s).
 
 Per-kernel roofline: a second timed region replays the same calls eagerly with

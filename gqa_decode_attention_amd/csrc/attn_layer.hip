@@ -2875,11 +2875,11 @@ __device__ __forceinline__ float group_sum(float v) {
 // residual comes with the first half.  The pair is b and b + 8 in each group
 // of 16 workgroups, so both run on the same XCD (workgroups go round-robin
 // over the 8 XCDs).
-template <int DT, int KV, int RPW, int CB, bool SPLIT>
+template <int DT, int KV, int RPW, int CB, bool SPLIT, int MR = 1>
 __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   float *xs = reinterpret_cast<float *>(dyn);   // [rows][this workgroup's heads x d]
-  __shared__ float s_w[32][kMaxChunks];          // merge weights [head][chunk] (nq <= 32)
+  __shared__ float s_w[MR][32][kMaxChunks];   // merge weights [row][head][chunk] (nq <= 32)
   constexpr int NS = (KV + 1) / 2;              // float4 columns per thread (nq d = 512 KV)
   const int b = blockIdx.x;
   const int hh = SPLIT ? (b >> 3) & 1 : 0;                            // head half
@@ -2913,8 +2913,8 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
   // requested before the W_o rows: a wait on a load waits on every load issued
   // before it, so they arrive in one round trip and the merges run while W_o
   // travels; rows past RP (more chunks per row) request theirs one row at a time.
-  constexpr int RP = 128 / (NS * CB * 4) < 1 ? 1 : (128 / (NS * CB * 4) > kVectorRows ? kVectorRows
-                                                                                    : 128 / (NS * CB * 4));
+  // MR: the rows one pass handles (1 for single-row calls, else kVectorRows)
+  constexpr int RP = 128 / (NS * CB * 4) < 1 ? 1 : (128 / (NS * CB * 4) > MR ? MR : 128 / (NS * CB * 4));
   int4 rt_p[RP];
   float2 ml0_p[RP];
   float4 av_p[RP][NS][CB];
@@ -2931,10 +2931,11 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       for (int v = 0; v < KV; ++v)
         wr[i][v] = ld16_stream(A.w_o + (size_t)(o0 + i) * Kw + hh * K + (v * 64 + lane_id()) * 8);
   }
-  auto merge_row = [&](int row, const int4 &rt, const float2 &ml0, const float4 (&av)[NS][CB])
-                       __attribute__((always_inline)) {
+  // merge of one row in two phases, the weights (into s_w[slot]) and then the
+  // columns (into xs); the prefetched rows run each phase together, so their
+  // chains interleave and one barrier serves them all
+  auto merge_weights = [&](int slot, int row, const int4 &rt, const float2 &ml0) __attribute__((always_inline)) {
     const int nch = chunks_of(rt.x ? rt.y + (row - seq_row0(A, seq_of(A, row))) + 1 : 0, A.split);
-    // weights
     float mx = cq < nch ? ml0.x : -INFINITY;
     for (int c = cq + CB; c < nch; c += CB) mx = fmaxf(mx, part_of(row, h0 + hq, c)[128]);
     const float M = group_max<CB>(mx);
@@ -2946,11 +2947,12 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
     }
     const float inv = 1.0f / group_sum<CB>(den);
     if (wt) {
-      s_w[hq][cq] = w0 * inv;
-      for (int c = cq + CB; c < nch; c += CB) s_w[hq][c] = exp2_neg(part_of(row, h0 + hq, c)[128] - M) * inv;
+      s_w[slot][hq][cq] = w0 * inv;
+      for (int c = cq + CB; c < nch; c += CB) s_w[slot][hq][c] = exp2_neg(part_of(row, h0 + hq, c)[128] - M) * inv;
     }
-    __syncthreads();
-    // columns
+    return nch;
+  };
+  auto merge_columns = [&](int slot, int row, int nch, const float4 (&av)[NS][CB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       const int q4 = t + 256 * s2, h = min(q4, K4 - 1) / 32;
@@ -2958,14 +2960,14 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
         const bool ok = c < nch;
-        const float w = s_w[h][c];   // zero past nch
+        const float w = s_w[slot][h][c];   // zero past nch
         num.x += w * (ok ? av[s2][c].x : 0.f);
         num.y += w * (ok ? av[s2][c].y : 0.f);
         num.z += w * (ok ? av[s2][c].z : 0.f);
         num.w += w * (ok ? av[s2][c].w : 0.f);
       }
       for (int c = CB; c < nch; ++c) {
-        const float w = s_w[h][c];
+        const float w = s_w[slot][h][c];
         const float4 v = *reinterpret_cast<const float4 *>(part_of(row, h0 + h, c) + (q4 % 32) * 4);
         num.x += w * v.x;
         num.y += w * v.y;
@@ -2974,51 +2976,75 @@ __global__ __launch_bounds__(256) void k_oproj_merge(LayerArgs A) {
       }
       if (q4 < K4) reinterpret_cast<float4 *>(xs + (size_t)row * K)[q4] = num;
     }
-    __syncthreads();   // s_w is reused by the next row
   };
+  int nch_p[RP];
 #pragma unroll
   for (int r = 0; r < RP; ++r)
-    if (r < A.rows) merge_row(r, rt_p[r], ml0_p[r], av_p[r]);
+    if (r < A.rows) nch_p[r] = merge_weights(r, r, rt_p[r], ml0_p[r]);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < RP; ++r)
+    if (r < A.rows) merge_columns(r, r, nch_p[r], av_p[r]);
   for (int row = RP; row < A.rows; ++row) {
     int4 rt;
     float2 ml0;
     float4 av[NS][CB];
     merge_loads(row, rt, ml0, av);
-    merge_row(row, rt, ml0, av);
+    __syncthreads();   // the previous row's weights are read
+    const int nch = merge_weights(0, row, rt, ml0);
+    __syncthreads();
+    merge_columns(0, row, nch, av);
   }
   __syncthreads();
+  // the GEMV of MR rows at a time: W_o unpacked once, the rows' reductions interleaved
   const int wave = wave_id(), lane = lane_id();
   const int o0 = (tile * 4 + wave) * RPW;
-  for (int row = 0; row < A.rows; ++row) {
-    float acc[RPW];
+  float wf[RPW][KV * 8];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) acc[i] = 0.f;
+  for (int i = 0; i < RPW; ++i)
 #pragma unroll
-    for (int v = 0; v < KV; ++v) {
-      const float4 *xp = reinterpret_cast<const float4 *>(xs + (size_t)row * K + (v * 64 + lane) * 8);
-      const float4 f0 = xp[0], f1 = xp[1];
-      const float x8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    for (int v = 0; v < KV; ++v) unpack8<DT>(wr[i][v], wf[i] + v * 8);
+  for (int r0 = 0; r0 < A.rows; r0 += MR) {
+    float acc[MR][RPW];
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        float wf[8];
-        unpack8<DT>(wr[i][v], wf);
+    for (int rr = 0; rr < MR; ++rr) {
+      const int row = r0 + rr;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i] += wf[e] * x8[e];
+      for (int i = 0; i < RPW; ++i) acc[rr][i] = 0.f;
+      if (row < A.rows) {
+#pragma unroll
+        for (int v = 0; v < KV; ++v) {
+          const float4 *xp = reinterpret_cast<const float4 *>(xs + (size_t)row * K + (v * 64 + lane) * 8);
+          const float4 f0 = xp[0], f1 = xp[1];
+          const float x8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+          for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[rr][i] += wf[i][v * 8 + e] * x8[e];
+        }
       }
     }
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) acc[i] = wave_sum(acc[i]);
-    if (lane < RPW) {
-      float val = acc[0];
+    for (int rr = 0; rr < MR; ++rr)
+      if (r0 + rr < A.rows) {
 #pragma unroll
-      for (int i = 1; i < RPW; ++i)
-        if (lane == i) val = acc[i];
-      const size_t o = (size_t)row * A.H + o0 + lane;
-      if (A.residual && hh == 0) val += cvt16<DT>(A.residual[o]);
-      if (!A.rowtab[row].x) val = __builtin_nanf("");
-      if (SPLIT) __hip_atomic_fetch_add(reinterpret_cast<float *>(A.out) + o, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
-      else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
+        for (int i = 0; i < RPW; ++i) acc[rr][i] = wave_sum(acc[rr][i]);
+      }
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) {
+      const int row = r0 + rr;
+      if (row < A.rows && lane < RPW) {
+        float val = acc[rr][0];
+#pragma unroll
+        for (int i = 1; i < RPW; ++i)
+          if (lane == i) val = acc[rr][i];
+        const size_t o = (size_t)row * A.H + o0 + lane;
+        if (A.residual && hh == 0) val += cvt16<DT>(A.residual[o]);
+        if (!A.rowtab[row].x) val = __builtin_nanf("");
+        if (SPLIT) __hip_atomic_fetch_add(reinterpret_cast<float *>(A.out) + o, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else if (A.out_f32) reinterpret_cast<float *>(A.out)[o] = val;
+        else reinterpret_cast<uint16_t *>(A.out)[o] = rne16<DT>(val);
+      }
     }
   }
   if (blockIdx.x == 0) advance_lengths<false>(A);
@@ -3260,13 +3286,13 @@ int few_waves(int group) { return group <= 2 ? 8 : 4; }
 
 // the partials of as many chunks as the host expects (4, 8, or 16 while two
 // float4 columns per thread keep that within registers) requested at once
-template <int DT>
-LayerKernel pick_oproj_merge(int kvo, int nch_host, bool split) {
+template <int DT, int MR>
+LayerKernel pick_oproj_merge_t(int kvo, int nch_host, bool split) {
   const int cb = nch_host <= 4 ? 4 : (nch_host > 8 && kvo <= 4 ? 16 : 8);
   if (split) {   // each workgroup: half the heads (kvo / 2 float8 columns per lane), two output rows per wave
     switch (kvo / 2) {
 #define ASR_PICK_OPROJ_HALF(K) \
-      case K: return cb == 4 ? k_oproj_merge<DT, K, 2, 4, true> : k_oproj_merge<DT, K, 2, 8, true>;
+      case K: return cb == 4 ? k_oproj_merge<DT, K, 2, 4, true, MR> : k_oproj_merge<DT, K, 2, 8, true, MR>;
       ASR_PICK_OPROJ_HALF(1) ASR_PICK_OPROJ_HALF(2) ASR_PICK_OPROJ_HALF(3) ASR_PICK_OPROJ_HALF(4)
 #undef ASR_PICK_OPROJ_HALF
       default: return nullptr;
@@ -3274,15 +3300,20 @@ LayerKernel pick_oproj_merge(int kvo, int nch_host, bool split) {
   }
   switch (kvo) {
 #define ASR_PICK_OPROJ_MERGE(K) \
-    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4, false> : cb == 16 ? k_oproj_merge<DT, K, kRpwD, 16, false> : k_oproj_merge<DT, K, kRpwD, 8, false>;
+    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4, false, MR> : cb == 16 ? k_oproj_merge<DT, K, kRpwD, 16, false, MR> : k_oproj_merge<DT, K, kRpwD, 8, false, MR>;
 #define ASR_PICK_OPROJ_MERGE8(K) \
-    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4, false> : k_oproj_merge<DT, K, kRpwD, 8, false>;
+    case K: return cb == 4 ? k_oproj_merge<DT, K, kRpwD, 4, false, MR> : k_oproj_merge<DT, K, kRpwD, 8, false, MR>;
     ASR_PICK_OPROJ_MERGE(1) ASR_PICK_OPROJ_MERGE(2) ASR_PICK_OPROJ_MERGE(3) ASR_PICK_OPROJ_MERGE(4)
     ASR_PICK_OPROJ_MERGE8(5) ASR_PICK_OPROJ_MERGE8(6) ASR_PICK_OPROJ_MERGE8(7) ASR_PICK_OPROJ_MERGE8(8)
 #undef ASR_PICK_OPROJ_MERGE
 #undef ASR_PICK_OPROJ_MERGE8
     default: return nullptr;
   }
+}
+// single-row calls (bs1 decode) keep the one-row pass: its GEMV is not widened
+template <int DT>
+LayerKernel pick_oproj_merge(int kvo, int nch_host, bool split, bool one_row) {
+  return one_row ? pick_oproj_merge_t<DT, 1>(kvo, nch_host, split) : pick_oproj_merge_t<DT, kVectorRows>(kvo, nch_host, split);
 }
 
 // (mixed calls: never single-token-only, so no NT instance)
@@ -3368,7 +3399,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
       return e;
     const int halves = a.oproj_split ? 2 : 1, rpw = a.oproj_split ? 2 : kRpwD;
     const unsigned lds_x = (unsigned)(a.rows * a.nq / halves * kHeadDim * sizeof(float));
-    return launch_phase(pick_oproj_merge<DT>(a.nq * kHeadDim / 512, a.nch_host, a.oproj_split != 0),
+    return launch_phase(pick_oproj_merge<DT>(a.nq * kHeadDim / 512, a.nch_host, a.oproj_split != 0, a.rows == 1),
                         dim3(a.H / (4 * rpw) * halves), dim3(256), lds_x, s, ev, 2, a);
   }
   if (attn_vmfma_used(a)) {

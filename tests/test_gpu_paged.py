@@ -291,3 +291,65 @@ def test_paged_bad_page_id_sets_status_and_spares_the_others(bad):
     assert np.array_equal(kg2[p0, :, :16], kn[0, :16].transpose(1, 0, 2))
     rest = [p for p in range(ref.k.shape[0]) if p != p0]
     assert np.array_equal(kg2[rest], pool_k[rest])
+
+
+def test_paged_graph_replays_and_workspace_free_decode():
+    """Paged decode steps captured in a HIP graph and replayed (a crop back to the start and new
+    inputs between replays) leave the eager calls' outputs, pool bits and lengths; the
+    workspace-free decode entry gives the decode entry's bits on a paged cache (5 rows on the
+    many-row kernels, then 2 rows on the few-row ones)."""
+    dtype, P = si.BF16, 16
+    lens = [40, 300, 7, 129, 64]
+    B, pps = len(lens), 320 // 16
+    L = SeededLayer(101, 0, 1024, dtype)
+    cfg = ga.config(dtype=dtype)
+    ws = ga.alloc_workspace(cfg, B, pps * P)
+    xs = [to_dev(si.activations(101, 0, r, B, 1024, dtype), dtype) for r in range(3)]
+    x = torch.empty((B, 1024), dtype=tdt(dtype), device="cuda")
+    out = torch.empty((B, 1024), dtype=torch.float32, device="cuda")
+
+    def snapshot(kv):
+        torch.cuda.synchronize()
+        return out.cpu().numpy().copy(), to_bits(kv.k), to_bits(kv.v), kv.lens.cpu().numpy()
+
+    kv_e, _ = paged_pair(101, lens, P, pps, dtype)
+    base = kv_e.lens.clone()
+    eager = []
+    for r in range(3):
+        ga.kv_crop([kv_e], base)
+        x.copy_(xs[r])
+        ga.layer_decode(cfg, L.dev, kv_e, x, out, ws)
+        eager.append(snapshot(kv_e))
+    kv_g, _ = paged_pair(101, lens, P, pps, dtype)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ga.layer_decode(cfg, L.dev, kv_g, x, out, ws)
+    for r in range(3):
+        ga.kv_crop([kv_g], base)
+        x.copy_(xs[r])
+        g.replay()
+        got = snapshot(kv_g)
+        assert all(np.array_equal(a, b) for a, b in zip(got, eager[r])), f"replay {r}"
+        assert kv_g.status.item() == 0
+    del g
+
+    res = {}
+    for entry in ("decode", "noalloc"):
+        kv, _ = paged_pair(102, lens, P, pps, dtype)
+        outs = []
+        for rows in (B, 2):
+            xb = to_dev(si.activations(102, 0, rows, rows, 1024, dtype), dtype)
+            o = torch.empty((rows, 1024), dtype=torch.float32, device="cuda")
+            st = _i32(list(range(rows))[::-1])
+            if entry == "noalloc":
+                ga.layer_decode_noalloc(cfg, L.dev, kv, xb, o, slots=st)
+            else:
+                ga.layer_decode(cfg, L.dev, kv, xb, o, ws, slots=st)
+            torch.cuda.synchronize()
+            outs.append(o.cpu().numpy())
+        res[entry] = (outs, to_bits(kv.k), to_bits(kv.v), kv.lens.cpu().numpy(), kv.status.item())
+    a, b = res["decode"], res["noalloc"]
+    assert all(np.array_equal(p, q) for p, q in zip(a[0], b[0]))
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+    assert a[4] == b[4] == 0

@@ -59,11 +59,11 @@ NEAR_TIE = 5e-3
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99992, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "8fbaa708d02d93f7aed4e17489feca6620f0e196a845382c6f4dde756c3fba6d",
-    "bs1": {"qkv_projection": 8564587, "attention": 4071965, "o_proj": 4913255},
-    "b64": {"qkv_projection": 11078472, "attention": 230492568, "o_proj": 8708347},
-    "b64_fp8": {"qkv_projection": 11078472, "attention": 120122860, "o_proj": 8708347},
-    "b64_paged": {"qkv_projection": 11078472, "attention": 230698977, "o_proj": 8708347},
+    "sources_sha256": "8f4db6cf889f9b99acfc7ac20c858403f188833ec7760ae68f0f067d5969f719",
+    "bs1": {"qkv_projection": 8570088, "attention": 4071815, "o_proj": 4883431},
+    "b64": {"qkv_projection": 11086690, "attention": 230488121, "o_proj": 8722670},
+    "b64_fp8": {"qkv_projection": 11086690, "attention": 120120823, "o_proj": 8722670},
+    "b64_paged": {"qkv_projection": 11086690, "attention": 230722858, "o_proj": 8722670},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",

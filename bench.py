@@ -524,7 +524,7 @@ def batched_leg(args, ga, si, np, torch, dev, to_dev, stream, fp8=False, page=0)
 def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_lens, H, NL, dtype, sid, P0,
                profile=0):
     """k-token verify blocks at bs1 from the committed 795: 28 layer_verify calls captured in one
-    graph, replayed with a crop back to 795 after each (the crop outside the timed events).  With
+    graph, replayed with a crop back to 795 after each (the crop timed on its own events).  With
     ``profile``: that many blocks per k, eagerly, for profilers."""
     out = {"workload": "28-layer verify block, bs1, fp16, hidden 1024, committed KV 795, k candidates",
            "unit": "us per 28-layer block"}
@@ -554,13 +554,17 @@ def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_l
             crop.replay()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(40)]
-        for e0, e1 in evs:
+        cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(40)]
+        for (e0, e1), (c0, c1) in zip(evs, cevs):
             e0.record(stream)
             g.replay()
             e1.record(stream)
+            c0.record(stream)
             crop.replay()
+            c1.record(stream)
         torch.cuda.synchronize()
         us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1000.0
+        crop_us = float(np.mean([c0.elapsed_time(c1) for c0, c1 in cevs])) * 1000.0
         g.replay()
         torch.cuda.synchronize()
         ok = all(int(kv.lens.item()) == P0 + k and int(kv.status.item()) == 0 for kv in kvs)
@@ -571,6 +575,7 @@ def verify_leg(ga, si, np, torch, dev, to_dev, stream, cfg, weights, kvs, base_l
         gbs = b_layer / (us / NL * 1e-6) / 1e9
         out[f"k{k}"] = {"us_per_block": round(us, 2), "us_per_layer_block": round(us / NL, 3),
                         "us_per_candidate_token": round(us / k, 2), "ok": ok,
+                        "crop_us": round(crop_us, 2),   # the 28 layers' crop back to 795, one dispatch
                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_layer_block": b_layer}}
         print(f"[bench] verify bs1 k={k}: {us:.1f} us per 28-layer block, {us / NL:.2f} us per layer, "

@@ -235,6 +235,165 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_down(MlpArgs A) {
   }
 }
 
+// ---------------------------------------------------------------- a few rows on the vector units
+//
+// With at most kVectorRows rows the MLP is two GEMVs that stream the weights
+// once; the matrix-core tiles above would keep 192 and 64 blocks busy at
+// hidden 1024 and leave most CUs idle.  Here each wave owns one intermediate
+// feature (up: its gate and up rows) or one output feature (down); lane l
+// covers input columns (v * 64 + l) * 8 .. + 7, so every wave-wide load reads
+// 1 KB contiguously, and every load of a batch is requested before its first
+// wait.  act = silu(gate) * up travels in fp32 through the workspace (the
+// bytes of the hi / lo tiles of the many-row path).  R: the rows the kernel is
+// built for (1, or kVectorRows with the rows past the call skipped).
+
+// columns (v * 64 + lane) * 8 .. + 7 of a row of length len (zeros past it)
+template <int DT>
+__device__ __forceinline__ void load8(const uint16_t *row, int len, int v, float (&f)[8]) {
+  const int c = (v * 64 + lane_id()) * 8;
+  if (c < len) {
+    unpack8<DT>(ld16(row + c), f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 0.f;
+  }
+}
+
+template <int DT, int KV, int R>   // KV = ceil(H / 512)
+__global__ __launch_bounds__(256) void k_mlp_up_few(MlpArgs A) {
+  const int lane = lane_id();
+  const int f = blockIdx.x * 4 + wave_id();   // intermediate feature
+  const int H = A.H;
+  // every load first: the gate and up rows of f, the post-norm gain, the rows of h
+  uint4 wg[KV], wu[KV], gq[KV];
+#pragma unroll
+  for (int v = 0; v < KV; ++v) {
+    const int c = min((v * 64 + lane) * 8, H - 8);
+    wg[v] = ld16_stream(A.w_gate + (size_t)f * H + c);
+    wu[v] = ld16_stream(A.w_up + (size_t)f * H + c);
+    gq[v] = ld16(A.g_post + c);
+  }
+  float hv[R][KV * 8];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(r, A.rows - 1);
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int c = (v * 64 + lane) * 8;
+      const int cc = min(c, H - 8);
+      float *x = hv[r] + v * 8;
+      if (A.in_f32) {
+        const float *src = reinterpret_cast<const float *>(A.h) + (size_t)n * H + cc;
+        const float4 a = *reinterpret_cast<const float4 *>(src), b = *reinterpret_cast<const float4 *>(src + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      } else {
+        unpack8<DT>(ld16(reinterpret_cast<const uint16_t *>(A.h) + (size_t)n * H + cc), x);
+      }
+      if (c >= H) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+    }
+  }
+  float gf[KV * 8], wgf[KV * 8], wuf[KV * 8];
+#pragma unroll
+  for (int v = 0; v < KV; ++v) {
+    const bool in = (v * 64 + lane) * 8 < H;
+    unpack8<DT>(gq[v], gf + v * 8);
+    unpack8<DT>(wg[v], wgf + v * 8);
+    unpack8<DT>(wu[v], wuf + v * 8);
+    if (!in) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wgf[v * 8 + e] = wuf[v * 8 + e] = 0.f;
+    }
+  }
+  float ag[R], au[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    ag[r] = au[r] = 0.f;
+    if (r < A.rows) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < KV * 8; ++e) ss += hv[r][e] * hv[r][e];
+      ss = wave_sum(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)H + A.eps);
+#pragma unroll
+      for (int e = 0; e < KV * 8; ++e) {
+        const float y = hv[r][e] * gf[e] * inv;
+        ag[r] += wgf[e] * y;
+        au[r] += wuf[e] * y;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r < A.rows) {
+      ag[r] = wave_sum(ag[r]);
+      au[r] = wave_sum(au[r]);
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < A.rows) reinterpret_cast<float *>(A.a_hl)[(size_t)r * A.I + f] = ag[r] / (1.f + __expf(-ag[r])) * au[r];
+  }
+}
+
+template <int DT, int R>
+__global__ __launch_bounds__(256) void k_mlp_down_few(MlpArgs A) {
+  constexpr int BK = R == 1 ? 8 : 4;   // 1 KB column groups per batch (registers: W and R act rows)
+  const int lane = lane_id();
+  const int o = blockIdx.x * 4 + wave_id();   // output feature
+  const int I = A.I, KI = (I + 511) / 512;
+  const float *act = reinterpret_cast<const float *>(A.a_hl);
+  float res = 0.f;   // lane r < rows: the residual of row r
+  if (lane < R && lane < A.rows) res = load_h<DT>(A, (size_t)lane * A.H + o);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  for (int v0 = 0; v0 < KI; v0 += BK) {
+    uint4 w[BK];
+    float4 xa[R][BK][2];
+#pragma unroll
+    for (int b = 0; b < BK; ++b) {
+      const int c = min(((v0 + b) * 64 + lane) * 8, I - 8);
+      w[b] = ld16_stream(A.w_down + (size_t)o * I + c);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float *src = act + (size_t)min(r, A.rows - 1) * I + c;
+        xa[r][b][0] = *reinterpret_cast<const float4 *>(src);
+        xa[r][b][1] = *reinterpret_cast<const float4 *>(src + 4);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BK; ++b) {
+      if (((v0 + b) * 64 + lane) * 8 >= I) continue;   // past the row (and past KI)
+      float wf[8];
+      unpack8<DT>(w[b], wf);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float x8[8] = {xa[r][b][0].x, xa[r][b][0].y, xa[r][b][0].z, xa[r][b][0].w,
+                             xa[r][b][1].x, xa[r][b][1].y, xa[r][b][1].z, xa[r][b][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r] += wf[e] * x8[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r < A.rows) acc[r] = wave_sum(acc[r]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < A.rows) {
+      const float val = acc[r] + readlane(res, r);
+      if (lane == 0) {
+        const size_t i = (size_t)r * A.H + o;
+        if (A.out_f32) reinterpret_cast<float *>(A.out)[i] = val;
+        else reinterpret_cast<uint16_t *>(A.out)[i] = rne16<DT>(val);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- model head and verify loop
 //
 // "Can CTC make Qwen3-ASR faster?", section 11 Phase A: a loop that exposes
@@ -369,6 +528,19 @@ hipError_t launch(MlpKernel k, dim3 grid, dim3 block, hipStream_t s, hipEvent_t 
 template <int DT>
 hipError_t mlp_launch(const MlpArgs &a, hipStream_t s, hipEvent_t *ev) {
   hipError_t e;
+  if (a.rows <= kVectorRows) {   // the vector-unit GEMVs: one wave per feature
+    const bool one = a.rows == 1;
+    MlpKernel up = nullptr;
+    switch ((a.H + 511) / 512) {
+#define ASR_MLP_UP_FEW(K) \
+      case K: up = one ? k_mlp_up_few<DT, K, 1> : k_mlp_up_few<DT, K, kVectorRows>; break;
+      ASR_MLP_UP_FEW(1) ASR_MLP_UP_FEW(2) ASR_MLP_UP_FEW(3) ASR_MLP_UP_FEW(4)
+#undef ASR_MLP_UP_FEW
+      default: return hipErrorInvalidValue;
+    }
+    if ((e = launch(up, dim3(a.I / 4), dim3(256), s, ev, 0, a)) != hipSuccess) return e;
+    return launch(one ? k_mlp_down_few<DT, 1> : k_mlp_down_few<DT, kVectorRows>, dim3(a.H / 4), dim3(256), s, ev, 1, a);
+  }
   const int rtiles = (a.rows + 15) / 16;
   MlpKernel up = nullptr;
   switch (a.H / 32 / kMlpWaves) {

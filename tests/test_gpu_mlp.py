@@ -23,9 +23,10 @@ class SeededMlp:
 
 
 @pytest.mark.parametrize("dtype", [si.BF16, si.F16])
-@pytest.mark.parametrize("rows,hidden,inter", [(1, 1024, 3072), (5, 1024, 3072), (16, 1024, 3072), (17, 1024, 3072),
-                                               (64, 1024, 3072), (1, 2048, 6144), (17, 2048, 6144),
-                                               (64, 2048, 6144)])
+@pytest.mark.parametrize("rows,hidden,inter", [(1, 1024, 3072), (2, 1024, 3072), (4, 1024, 3072), (5, 1024, 3072),
+                                               (16, 1024, 3072), (17, 1024, 3072), (64, 1024, 3072), (1, 2048, 6144),
+                                               (3, 2048, 6144), (17, 2048, 6144), (64, 2048, 6144),
+                                               (1, 1280, 2816), (3, 768, 1280)])
 def test_mlp_vs_oracle(dtype, rows, hidden, inter):
     M = SeededMlp(30, rows, hidden, inter, dtype)
     h = si.hidden_f32(30, rows, 0, rows, hidden)
@@ -43,8 +44,9 @@ def test_mlp_vs_oracle(dtype, rows, hidden, inter):
 
 
 @pytest.mark.parametrize("dtype", [si.BF16, si.F16])
-def test_mlp_16bit_input_and_output(dtype):
-    rows, hidden, inter = 9, 1024, 3072
+@pytest.mark.parametrize("rows", [9, 3])
+def test_mlp_16bit_input_and_output(dtype, rows):
+    hidden, inter = 1024, 3072
     M = SeededMlp(31, 0, hidden, inter, dtype)
     hb = si.activations(31, 0, 0, rows, hidden, dtype)
     cfg = ga.mlp_config(hidden=hidden, intermediate=inter, dtype=dtype, in_dtype=dtype, out_dtype=dtype)

@@ -262,16 +262,16 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
       }
       return t * a.nkv;
     };
+    const int grid = attn_vmfma_grid(cfg->dtype, a.group, n, B, cus);
+    if (grid <= 0) return ASR_EHIP;
     if (!cfg->kv_split) {
-      // an item's chain (loads, products, combine, count) is latency, so longer items stream
-      // better: the largest chunk that still leaves about one item per CU
-      while (split < kMaxSplit && 4 * items(2 * split) >= 3LL * cus) split *= 2;
+      // the smallest chunk (in 128-key steps) whose items all fit the resident grid at
+      // once: a second round of items would double the kernel's time
+      while (split < kMaxSplit && items(split) > grid) split += 128;
     } else {
       split = cfg->kv_split < split ? split : (cfg->kv_split + 127) / 128 * 128;
     }
     a.split = split < kMaxSplit ? split : kMaxSplit;
-    const int grid = attn_vmfma_grid(cfg->dtype, a.group, n, B, cus);
-    if (grid <= 0) return ASR_EHIP;
     const long long want = items(a.split);
     attn_grid = (int)(want < 1 ? 1 : (want < grid ? want : grid));
     if (B <= kVmMaxSeqs) {   // the host lays the items out: the kernel starts without reading the lengths

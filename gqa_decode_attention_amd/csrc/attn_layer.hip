@@ -1671,16 +1671,19 @@ constexpr int chunk_steps(int kq) {
 // row tiles share each split weight step); the 16 features are 8 rotary pairs
 // (t, t + 64) of one head, as in the vector path, with the same epilogue: gain
 // and rotation of q/k pairs, partial sums of squares, v stored raw.
-// LX (hidden 1024, eight waves): each wave loads its 64 rows x 256 bytes of x
-// as whole 128-byte lines (four rows per instruction) into its own LDS region
-// and reads the operand layout back from there: the operand layout touches 16
-// rows per load, half a line each, and a CU keeps only so many lines in flight.
+// LX (hidden 1024 and 2048, eight waves): per batch of four 32-wide steps, each
+// wave loads its 64 rows x 256 bytes of x as whole 128-byte lines (four rows
+// per instruction) into its own 16 KB LDS region and reads the operand layout
+// back from there: the operand layout touches 16 rows per load, half a line
+// each, and a CU keeps only so many lines in flight.  At hidden 2048 a wave's
+// share takes two batches.
 template <int DT, int KQ, int NWV, bool LX, bool MIX = false, int NTL = 4>
 __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
   constexpr int BR = 16 * NTL;          // rows per block: NTL row tiles of 16
   constexpr int KW = KQ * 4 / NWV;      // 32-wide steps of this wave's share of the contraction
-  constexpr int KC = KW < 8 ? KW : 8;   // steps per operand batch (x of four row tiles)
-  static_assert(!LX || (KQ == 8 && NWV == 8), "x staging: 16 KB per wave");
+  // steps per operand batch (x of four row tiles); LX: 4 steps = 16 KB of x per wave
+  constexpr int KC = LX ? 4 : (KW < 8 ? KW : 8);
+  static_assert(!LX || (NWV == 8 && KW % 4 == 0), "x staging: 16 KB per wave and batch");
   extern __shared__ __align__(16) unsigned char dyn[];   // LX: [NWV][BR rows][256 B] x, then the wave's sums
   __shared__ f32x4_t s_cs[LX ? 1 : NWV][NTL][kWave];
   __shared__ float s_ss[NWV][BR];
@@ -1729,7 +1732,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
       if constexpr (LX) {   // W too as whole lines: instruction s, rows 4 s .. 4 s + 3 of the tile
         const int f = s * 64 + lane, r = f >> 4, ch = f & 15;
         const int wrow = head * kHeadDim + (r < 8 ? t0 + r : 64 + t0 + r - 8);
-        w[s] = ld16_stream(A.w_qkv + (size_t)wrow * H + wave * (H / NWV) + ch * 8);
+        w[s] = ld16_stream(A.w_qkv + (size_t)wrow * H + wave * (H / NWV) + c0 * 32 + ch * 8);
       } else {
         w[s] = ld16_stream(wp + (c0 + s) * 32);
       }
@@ -1743,7 +1746,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
 #pragma unroll
       for (int j = 0; j < 4 * NTL; ++j) {
         const int f = j * 64 + lane, r = f >> 4, ch = f & 15;
-        xl[j] = ld16(A.x + (size_t)min(nb + r, A.rows - 1) * H + wave * (H / NWV) + ch * 8);
+        xl[j] = ld16(A.x + (size_t)min(nb + r, A.rows - 1) * H + wave * (H / NWV) + c0 * 32 + ch * 8);
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any math
@@ -1805,10 +1808,7 @@ __global__ __launch_bounds__(NWV * 64) void k_qkv_mfma(LayerArgs A) {
       }
 #pragma unroll
       for (int nt = 0; nt < NTL; ++nt) {
-        float xf[8];
-        unpack8<DT>(x[nt][s], xf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss[nt] += xf[e] * xf[e];
+        ss[nt] = sumsq8<DT>(x[nt][s], ss[nt]);   // the row sums of squares on the packed dot
         acc[nt] = mfma16x16x32<DT>(ahi, x[nt][s], acc[nt]);
         acc[nt] = mfma16x16x32<DT>(alo, x[nt][s], acc[nt]);
       }
@@ -2506,7 +2506,7 @@ __device__ void merge_block_vm(const LayerArgs &A, int row0, int k, int g, int n
   }
 }
 
-template <int DT, int GROUP, int QT>
+template <int DT, int GROUP, int QT, bool DB>
 __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ int wsum[4];
@@ -2553,9 +2553,18 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
     const __amdgpu_buffer_rsrc_t Kr = make_rsrc(A.kc + kvbase, (uint32_t)A.capacity * kHeadDim * 2);
     const __amdgpu_buffer_rsrc_t Vr = make_rsrc(A.vc + kvbase, (uint32_t)A.capacity * kHeadDim * 2);
 
-    uint4 lk[8], lv[8];
+    // DB (chunks of several steps per wave, one query tile): two register sets of
+    // K/V lines, a wave's steps alternate between them, and the loads of step j + 2
+    // are requested as soon as step j is in LDS, so two steps are in flight while
+    // one is computed.  Every DB request is unconditional (rows clamped into the
+    // chunk, so a request past the chunk re-reads its last row): the number of
+    // loads behind each set is then fixed and a wait for one set never waits for
+    // the other.  (With two query tiles the second set would not fit the register
+    // file beside their operands.)
+    static_assert(!DB || QT == 1, "two register sets beside one query tile");
+    uint4 lk0[8], lv0[8], lk1[8], lv1[8];
     int tclamp = 0;   // loads stay at or below this key (lines the item fetches anyway)
-    auto issue = [&](int ts) {
+    auto issue = [&](uint4 (&lk)[8], uint4 (&lv)[8], int ts) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int t = min(ts + 4 * i + j4, tclamp);
@@ -2564,10 +2573,14 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
         lv[i] = ld_buf(Vr, off);
       }
     };
-    // the wave's first step of the first chunk, requested before the length arrives
+    constexpr int kRound = kVmWaves * kVmStep;   // keys of one step of all four waves
+    // the wave's first two steps of the first chunk, requested before the length arrives
     // (with the host layout): rows clamped into the chunk and the cache
     tclamp = min(c_first * A.split + A.split, A.capacity) - 1;
-    if (hostmap || c_first * A.split + wave * kVmStep < nvis) issue(c_first * A.split + wave * kVmStep);
+    if (hostmap || c_first * A.split + wave * kVmStep < nvis) {
+      issue(lk0, lv0, c_first * A.split + wave * kVmStep);
+      if (DB) issue(lk1, lv1, c_first * A.split + wave * kVmStep + kRound);
+    }
     // Q of the tile rows, requested with the K/V lines and before the length (a wait
     // on a vector load waits on every load issued before it)
     float4 qv[QT][4][2], qp[QT][2];
@@ -2619,7 +2632,10 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
     const int cbeg = c * A.split, cend = min(cbeg + A.split, nvis);
     int t0 = cbeg + wave * kVmStep;
     tclamp = max(min(cend, L) - 1, 0);
-    if (c > c_first && t0 < cend) issue(t0);
+    if (c > c_first && t0 < cend) {
+      issue(lk0, lv0, t0);
+      if (DB) issue(lk1, lv1, t0 + kRound);
+    }
     float mrun[QT], lrun[QT];
     f32x4_t o[QT][8];
 #pragma unroll
@@ -2630,7 +2646,8 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
       for (int dt = 0; dt < 8; ++dt) o[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (; t0 < cend; t0 += kVmWaves * kVmStep) {
+    // one step: set (lk, lv) holds keys [t0, t0 + 32) of this wave
+    auto vstep = [&](uint4 (&lk)[8], uint4 (&lv)[8]) __attribute__((always_inline)) {
       wave_lds_sync();   // the previous step's operand reads are done
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -2673,8 +2690,8 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
         }
       }
       wave_lds_sync();   // the stage is complete before any lane reads it
-      const int tn = t0 + kVmWaves * kVmStep;
-      if (tn < cend) issue(tn);   // the next step's lines travel during this step's arithmetic
+      if constexpr (DB) issue(lk, lv, t0 + 2 * kRound);   // the set's next step travels during two steps
+      else if (t0 + kRound < cend) issue(lk, lv, t0 + kRound);   // the next step travels during this one
 
       // scores: two 16-key tiles per query tile
       uint4 ka[2][4];
@@ -2755,6 +2772,17 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
           o[qt][dt] = mfma16x16x32<DT>(va[dt], pl, o[qt][dt]);
         }
       }
+    };
+    if constexpr (DB) {
+      for (; t0 < cend; t0 += 2 * kRound) {
+        vstep(lk0, lv0);
+        if (t0 + kRound >= cend) break;
+        t0 += kRound;
+        vstep(lk1, lv1);
+        t0 -= kRound;
+      }
+    } else {
+      for (; t0 < cend; t0 += kRound) vstep(lk0, lv0);
     }
 
     // the four waves' (m, l, O) of each query tile combined into the item's partials
@@ -3220,7 +3248,7 @@ MfmaKernel pick_qkv_mfma_t(int kq) {
     case 4: return {k_qkv_mfma<DT, 4, 8, false, MIX, NTL>, 0};
     case 8: return {k_qkv_mfma<DT, 8, 8, true, MIX, NTL>, 8 * 16384};
     case 12: return {k_qkv_mfma<DT, 12, 8, false, MIX, NTL>, 0};
-    case 16: return {k_qkv_mfma<DT, 16, 8, false, MIX, NTL>, 0};
+    case 16: return {k_qkv_mfma<DT, 16, 8, true, MIX, NTL>, 8 * 16384};
     case 20: return {k_qkv_mfma<DT, 20, 4, false, MIX, NTL>, 0};
     case 24: return {k_qkv_mfma<DT, 24, 4, false, MIX, NTL>, 0};
     case 28: return {k_qkv_mfma<DT, 28, 4, false, MIX, NTL>, 0};
@@ -3340,10 +3368,16 @@ int vmfma_tiles(int group, int n) {
   return m <= 16 ? 1 : (m <= 32 ? 2 : 0);
 }
 
+// two register sets when a chunk gives each wave more than one step (one query tile)
+bool vmfma_double_buffer(const LayerArgs &a) {
+  return vmfma_tiles(a.group, a.n) == 1 && a.split > kVmWaves * kVmStep;
+}
+
 template <int DT>
-LayerKernel pick_attn_vmfma(int group, int qt) {
+LayerKernel pick_attn_vmfma(int group, int qt, bool db) {
 #define ASR_PICK_VMFMA(G) \
-  case G: return qt == 1 ? k_attn_vmfma<DT, G, 1> : (qt == 2 ? k_attn_vmfma<DT, G, 2> : nullptr);
+  case G: return qt == 1 ? (db ? k_attn_vmfma<DT, G, 1, true> : k_attn_vmfma<DT, G, 1, false>) \
+                         : (qt == 2 ? k_attn_vmfma<DT, G, 2, false> : nullptr);
   switch (group) {
     ASR_PICK_VMFMA(2) ASR_PICK_VMFMA(4) ASR_PICK_VMFMA(8)
     default: return nullptr;
@@ -3403,7 +3437,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                         dim3(a.H / (4 * rpw) * halves), dim3(256), lds_x, s, ev, 2, a);
   }
   if (attn_vmfma_used(a)) {
-    if ((e = launch_phase(pick_attn_vmfma<DT>(a.group, vmfma_tiles(a.group, a.n)), dim3(attn_grid), dim3(kVmWaves * kWave),
+    if ((e = launch_phase(pick_attn_vmfma<DT>(a.group, vmfma_tiles(a.group, a.n), vmfma_double_buffer(a)), dim3(attn_grid), dim3(kVmWaves * kWave),
                           lds_vmfma_bytes(a.B), s, ev, 1, a)) != hipSuccess)
       return e;
   } else if (attn_waves_used(a)) {
@@ -3491,7 +3525,9 @@ bool attn_vmfma_used(const LayerArgs &a) {
 // CU from the occupancy calculator times the CU count).
 int attn_vmfma_grid(int dtype, int group, int n, int B, int cus) {
   const int qt = vmfma_tiles(group, n);
-  const LayerKernel k = dtype == ASR_BF16 ? pick_attn_vmfma<ASR_BF16>(group, qt) : pick_attn_vmfma<ASR_F16>(group, qt);
+  // (both register-set variants hold one workgroup per CU)
+  const LayerKernel k =
+      dtype == ASR_BF16 ? pick_attn_vmfma<ASR_BF16>(group, qt, false) : pick_attn_vmfma<ASR_F16>(group, qt, false);
   int per_cu = 0;
   if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kVmWaves * kWave, lds_vmfma_bytes(B)) != hipSuccess ||
       per_cu <= 0)

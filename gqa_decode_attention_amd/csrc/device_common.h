@@ -43,6 +43,24 @@ __device__ __forceinline__ void unpack8(const uint4 v, float *f) {
   cvt16x2<DT>(v.w, f[6], f[7]);
 }
 
+// sum of squares of 8 packed 16-bit values added to acc, on the packed dot
+// instructions (v_dot2_f32_bf16 / v_dot2_f32_f16: each product is exact in fp32)
+template <int DT>
+__device__ __forceinline__ float sumsq8(const uint4 v, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == ASR_BF16)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), __builtin_bit_cast(bf16x2_t, w[i]), acc,
+                                            false);
+    else
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w[i]), __builtin_bit_cast(f16x2_t, w[i]), acc, false);
+  }
+  return acc;
+}
+
 // fp32 -> 16-bit, round to nearest even (hardware conversions, no flush of subnormals)
 template <int DT>
 __device__ __forceinline__ uint16_t rne16(float f) {

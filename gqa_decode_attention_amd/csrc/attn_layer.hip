@@ -428,10 +428,12 @@ __device__ __forceinline__ Item decode_item(const LayerArgs &A, int item, const 
     const int mid = (lo + hi) >> 1;
     if (pre[mid] <= item) lo = mid; else hi = mid;
   }
+  // (an item is uniform over its workgroup: readfirstlane keeps its indices, and the
+  // buffer resources built from them, in scalar registers)
   Item it;
-  it.row = lo;
-  it.nch = (pre[lo + 1] - pre[lo]) / A.nkv;
-  const int rem = item - pre[lo];
+  it.row = __builtin_amdgcn_readfirstlane(lo);
+  it.nch = __builtin_amdgcn_readfirstlane((pre[lo + 1] - pre[lo]) / A.nkv);
+  const int rem = item - __builtin_amdgcn_readfirstlane(pre[lo]);
   it.g = rem / it.nch;
   it.c = rem - it.g * it.nch;
   return it;
@@ -481,7 +483,9 @@ struct ItemGeom {
 
 template <bool PG = false>
 __device__ __forceinline__ ItemGeom item_geom(const LayerArgs &A, const Item &it, int4 rin) {
-  // rin: slot, committed length, visible keys, block offset
+  // rin: slot, committed length, visible keys, block offset (uniform over the workgroup)
+  rin = make_int4(__builtin_amdgcn_readfirstlane(rin.x), __builtin_amdgcn_readfirstlane(rin.y),
+                  __builtin_amdgcn_readfirstlane(rin.z), __builtin_amdgcn_readfirstlane(rin.w));
   ItemGeom g;
   g.L = rin.y;
   g.r_off = rin.w;
@@ -891,12 +895,12 @@ __device__ __forceinline__ float4 merge_column(int nch, const float2 (&ml0)[CB],
 // chunk partials of one column read device-coherently (stored by other
 // workgroups of this dispatch); past nch the buffer range reads zeros
 struct PartCoherent {
-  __amdgpu_buffer_rsrc_t R;
-  uint32_t cs, col;   // bytes per chunk, byte offset of the column
+  __amdgpu_buffer_rsrc_t R;   // the (row, kv head)'s partials: uniform over the workgroup
+  uint32_t cs, head, col;     // bytes per chunk, byte offsets of the q head and of the column
   __device__ __forceinline__ void operator()(int c, float2 &ml, float4 &av, bool with_av) const {
-    const float4 v = ld_dev4(R, c * cs + 128 * 4);
+    const float4 v = ld_dev4(R, c * cs + head + 128 * 4);
     ml = make_float2(v.x, v.y);
-    if (with_av) av = ld_dev4(R, c * cs + col);
+    if (with_av) av = ld_dev4(R, c * cs + head + col);
   }
 };
 
@@ -904,13 +908,18 @@ struct PartCoherent {
 // GROUP * 32 takes float4 column t of the GROUP x 128 outputs.
 template <int DT, int GROUP, bool COH>
 __device__ void merge_group(const LayerArgs &A, int row, int g, int nch, AttnShared<GROUP> &S) {
+  // (uniform over the workgroup: scalar registers for the resources built from them)
+  row = __builtin_amdgcn_readfirstlane(row);
+  g = __builtin_amdgcn_readfirstlane(g);
+  nch = __builtin_amdgcn_readfirstlane(nch);
   constexpr int CB = 8;
   const int t = threadIdx.x;
   if (t < GROUP * 32) {
     const int j = t / 32, d = (t % 32) * 4;
-    const float *p0 = A.part + ((((size_t)row * A.nkv + g) * kMaxChunks) * GROUP + j) * kPartStride;
+    // the head j of this thread goes into the offset, so the resource stays uniform
+    const float *p0 = A.part + (((size_t)row * A.nkv + g) * kMaxChunks) * GROUP * kPartStride;
     const uint32_t cs = (uint32_t)GROUP * kPartStride * 4;
-    const PartCoherent P{rsrc_of(p0, (uint32_t)nch * cs), cs, (uint32_t)d * 4};
+    const PartCoherent P{rsrc_of(p0, (uint32_t)nch * cs), cs, (uint32_t)j * kPartStride * 4, (uint32_t)d * 4};
     float2 ml[CB];
     float4 av[CB];
 #pragma unroll
@@ -959,7 +968,7 @@ __device__ __forceinline__ void resolve(const LayerArgs &A, const Pending &p, At
 }
 
 template <int DT, int GROUP, bool COH, bool PG = false>
-__device__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *rinfo, uint16_t *knew,
+__device__ __forceinline__ void attention_phase(const LayerArgs &A, const int *pre, const int4 *rinfo, uint16_t *knew,
                                 uint16_t *vnew, AttnShared<GROUP> &S, int first, int stride) {
   const int total = pre[A.rows];
   Pending pend{-1, 0, 0, 0u};
@@ -1199,7 +1208,7 @@ __device__ __forceinline__ void wresolve(const LayerArgs &A, const WPending &p) 
 }
 
 template <int DT, int GROUP, bool NT, bool F8, bool PG = false>
-__device__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *rinfo, int w, int W) {
+__device__ __forceinline__ void attention_waves(const LayerArgs &A, const int *pre, const int4 *rinfo, int w, int W) {
   const int lane = lane_id(), kl = lane & 7, kr = lane >> 3;
   // a lane's 16 dims: [8 kl, 8 kl + 8) and [64 + 8 kl, ..) of a 256-byte 16-bit row (two whole
   // lines per key across the 8 lanes), or [16 kl, 16 kl + 16) of a 128-byte FP8 row (one line)
@@ -2534,18 +2543,21 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
       const int mid = (lo + hi) >> 1;
       if (ip[mid] <= item) lo = mid; else hi = mid;
     }
-    const int b = lo, row0 = b * k;
-    const int nch_i = (ip[b + 1] - ip[b]) / A.nkv;   // chunks per kv head in the item layout
-    const int rem = item - ip[b];
+    // the item's indices are uniform over the workgroup: readfirstlane keeps them, and
+    // the buffer resources built from them, in scalar registers (a resource the
+    // compiler cannot prove uniform costs a loop around every load)
+    const int b = rfl(lo), row0 = b * k;
+    const int nch_i = rfl((ip[b + 1] - ip[b]) / A.nkv);   // chunks per kv head in the item layout
+    const int rem = item - rfl(ip[b]);
     const int g = rem / nch_i, c_first = rem - g * nch_i;
     int slot, L, nvis;
     if (hostmap) {
-      slot = A.slots ? A.slots[b] : b;
+      slot = rfl(A.slots ? A.slots[b] : b);
     } else {
       const int4 si = sinfo[b];
-      slot = si.x;
-      L = si.y;
-      nvis = si.z;
+      slot = rfl(si.x);
+      L = rfl(si.y);
+      nvis = rfl(si.z);
     }
     // a slot outside the cache reads slot 0's lines (its rows are skipped below)
     const int lslot = (slot >= 0 && slot < A.batch_cap) ? slot : 0;
@@ -2605,8 +2617,8 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
     }
     if (hostmap) {
       const RowInfo ri = row_info(A, row0);
-      L = ri.L;
-      nvis = ri.ok ? ri.L + k : 0;
+      L = rfl(ri.L);
+      nvis = rfl(ri.ok ? ri.L + k : 0);
     }
     const int nch = chunks_of(nvis, A.split);
     const int c_last = (hostmap && c_first == nch_i - 1) ? max(nch, nch_i) - 1 : c_first;

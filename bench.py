@@ -59,11 +59,11 @@ NEAR_TIE = 5e-3
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99992, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "8f4db6cf889f9b99acfc7ac20c858403f188833ec7760ae68f0f067d5969f719",
-    "bs1": {"qkv_projection": 8570088, "attention": 4071815, "o_proj": 4883431},
-    "b64": {"qkv_projection": 11086690, "attention": 230488121, "o_proj": 8722670},
-    "b64_fp8": {"qkv_projection": 11086690, "attention": 120120823, "o_proj": 8722670},
-    "b64_paged": {"qkv_projection": 11086690, "attention": 230722858, "o_proj": 8722670},
+    "sources_sha256": "f0734952419ae31f52e1f0226b19d72b7e2a241a6df4c787377fa8ad5553cfec",
+    "bs1": {"qkv_projection": 8587107, "attention": 4058658, "o_proj": 4864994},
+    "b64": {"qkv_projection": 11070259, "attention": 230482129, "o_proj": 8722651},
+    "b64_fp8": {"qkv_projection": 11070259, "attention": 120147852, "o_proj": 8722651},
+    "b64_paged": {"qkv_projection": 11070259, "attention": 230699889, "o_proj": 8722651},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",

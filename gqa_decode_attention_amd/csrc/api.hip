@@ -222,6 +222,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
   a.mfma = rows > kVectorRows || n_per_seq != nullptr;
   a.oproj_split = 0;
   a.vm_items = 0;
+  a.vm_nt = 1;
   a.kv8 = kv8;
   a.ksc = kv->k_scale;
   a.vsc = kv->v_scale;
@@ -254,13 +255,14 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
     // kMaxChunks chunks per sequence
     int split = 128;
     while (split < kMaxSplit && (long long)split * kMaxChunks < kv->capacity) split += 128;
+    a.vm_nt = attn_vmfma_tiles(a.group, n);   // 16-row query tiles per (sequence, kv head)
     auto items = [&](int sp) {
       long long t = 0;
       for (int b = 0; b < B; ++b) {
         const int L = host_lens ? host_lens[b] : kv->capacity - n;
         t += (L + n + sp - 1) / sp;
       }
-      return t * a.nkv;
+      return t * a.nkv * a.vm_nt;
     };
     const int grid = attn_vmfma_grid(cfg->dtype, a.group, n, B, cus);
     if (grid <= 0) return ASR_EHIP;
@@ -279,7 +281,7 @@ int run_layer(const asr_attn_config *cfg, const asr_attn_weights *w, const asr_k
       for (int b = 0; b < B; ++b) {
         a.vm_pre[b] = run;
         const int L = host_lens ? host_lens[b] : kv->capacity - n;
-        run += (L + n + a.split - 1) / a.split * a.nkv;
+        run += (L + n + a.split - 1) / a.split * a.nkv * a.vm_nt;
       }
       a.vm_pre[B] = run;
       a.vm_items = run;

@@ -2352,9 +2352,12 @@ __host__ __device__ __forceinline__ size_t lds_attn_waves_bytes(int rows) {
 // ---------------------------------------------------------------- phase C for verify blocks on the matrix cores
 //
 // The k rows of a verify block all read their sequence's cache, so here one
-// work item streams each (sequence, kv head g, chunk of keys) once for all
-// M = GROUP * k query rows of g (query row m = r * GROUP + h: block row r, q
-// head g * GROUP + h), in tiles of 16 rows.  Per 32-key step of a wave:
+// work item streams each (sequence, kv head g, chunk of keys) once for a
+// 16-row tile of the M = GROUP * k query rows of g (query row m = r * GROUP + h:
+// block row r, q head g * GROUP + h); with 32 query rows the two tiles are two
+// items of the same chunk (the second stream mostly hits the caches), which
+// keeps one tile's operands per wave and leaves room for two K/V register sets.
+// Per 32-key step of a wave:
 //   S^T = K Q^T    v_mfma_f32_16x16x32, A = 16 keys x 32 dims of K (exact
 //                  16-bit), B = the same dims of Q (two 16-bit terms, hi + lo)
 //   O^T += V^T P^T A = 16 dims x 32 keys of V, B = the weights P (hi + lo)
@@ -2404,7 +2407,7 @@ __device__ void build_seq_prefix(const LayerArgs &A, int *pre, int4 *sinfo, int 
     const RowInfo ri = row_info(A, seq_row0(A, b));
     const int nvis = ri.ok ? ri.L + seq_rows(A, b) : 0;
     sinfo[b] = make_int4(ri.slot, ri.L, nvis, (int)ri.ok);
-    local += chunks_of(nvis, A.split) * A.nkv;
+    local += chunks_of(nvis, A.split) * A.nkv * A.vm_nt;
   }
   int incl = local;
 #pragma unroll
@@ -2419,7 +2422,7 @@ __device__ void build_seq_prefix(const LayerArgs &A, int *pre, int4 *sinfo, int 
   int run = base + incl - local;
   for (int b = beg; b < end; ++b) {
     pre[b] = run;
-    run += chunks_of(sinfo[b].z, A.split) * A.nkv;
+    run += chunks_of(sinfo[b].z, A.split) * A.nkv * A.vm_nt;
   }
   if (threadIdx.x == 255) pre[B] = run;
   __syncthreads();
@@ -2515,7 +2518,7 @@ __device__ void merge_block_vm(const LayerArgs &A, int row0, int k, int g, int n
   }
 }
 
-template <int DT, int GROUP, int QT, bool DB>
+template <int DT, int GROUP, int QT, bool DB, int NT>
 __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ int wsum[4];
@@ -2547,9 +2550,11 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
     // the buffer resources built from them, in scalar registers (a resource the
     // compiler cannot prove uniform costs a loop around every load)
     const int b = rfl(lo), row0 = b * k;
-    const int nch_i = rfl((ip[b + 1] - ip[b]) / A.nkv);   // chunks per kv head in the item layout
+    constexpr int nt = NT;   // query tiles (A.vm_nt): items (g, chunk, tile) of sequence b
+    const int nch_i = rfl((ip[b + 1] - ip[b]) / (A.nkv * nt));   // chunks per kv head in the item layout
     const int rem = item - rfl(ip[b]);
-    const int g = rem / nch_i, c_first = rem - g * nch_i;
+    const int g = rem / (nch_i * nt), rc = rem - g * (nch_i * nt);
+    const int c_first = rc / nt, m0 = (rc - c_first * nt) * 16 * QT;   // first query row of the item's tiles
     int slot, L, nvis;
     if (hostmap) {
       slot = rfl(A.slots ? A.slots[b] : b);
@@ -2602,7 +2607,7 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
           make_rsrc(A.ssq + (size_t)row0 * (A.nq + A.nkv) * kTilesPerHead, (uint32_t)k * ssq_bytes);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const int m = qt * 16 + n16, r = m / GROUP, h = m % GROUP;
+        const int m = m0 + qt * 16 + n16, r = m / GROUP, h = m % GROUP;
         const uint32_t rr = (uint32_t)min(r, k - 1);   // rows past the block: zero weight below
         const uint32_t head = (uint32_t)(g * GROUP + h);
 #pragma unroll
@@ -2628,7 +2633,7 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
     {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const int m = qt * 16 + n16;
+        const int m = m0 + qt * 16 + n16;
         const float sc = (m / GROUP < k) ? inv_rms_of(A, qp[qt][0], qp[qt][1]) * qs : 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -2743,7 +2748,7 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
       // online softmax per query row, then the weighted values
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const int m = qt * 16 + n16, r = m / GROUP;
+        const int m = m0 + qt * 16 + n16, r = m / GROUP;
         const int tmax = r < k ? min(cend, L + r + 1) : 0;   // keys [.., tmax) visible to this row
         float p[8];
         float mx = -INFINITY;
@@ -2815,7 +2820,7 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
         s_ml[wave][1][n16] = l;
       }
       __syncthreads();
-      const int m = qt * 16 + prow, r = m / GROUP, h = m % GROUP;
+      const int m = m0 + qt * 16 + prow, r = m / GROUP, h = m % GROUP;
       if (r < k) {
         float M = -INFINITY;
 #pragma unroll
@@ -2851,7 +2856,7 @@ __global__ __launch_bounds__(kVmWaves * 64) void k_attn_vmfma(LayerArgs A) {
     if (threadIdx.x == 0)
       s_old = __hip_atomic_fetch_add(A.mctr + (size_t)row0 * A.nkv + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (s_old == (uint32_t)(nch_i - 1)) {   // the last item of (sequence, g): merge every row of the block
+    if (s_old == (uint32_t)(nch_i * nt - 1)) {   // the last item of (sequence, g): merge every row of the block
       if (nch > 0) merge_block_vm<DT, GROUP>(A, row0, k, g, nch, reinterpret_cast<float *>(dyn));
       if (threadIdx.x == 0)
         __hip_atomic_store(A.mctr + (size_t)row0 * A.nkv + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -3380,16 +3385,17 @@ int vmfma_tiles(int group, int n) {
   return m <= 16 ? 1 : (m <= 32 ? 2 : 0);
 }
 
-// two register sets when a chunk gives each wave more than one step (one query tile)
+// two register sets when a chunk gives each wave more than one step
 bool vmfma_double_buffer(const LayerArgs &a) {
-  return vmfma_tiles(a.group, a.n) == 1 && a.split > kVmWaves * kVmStep;
+  return a.split > kVmWaves * kVmStep;
 }
 
 template <int DT>
-LayerKernel pick_attn_vmfma(int group, int qt, bool db) {
+LayerKernel pick_attn_vmfma(int group, int qt, bool db, int nt) {
 #define ASR_PICK_VMFMA(G) \
-  case G: return qt == 1 ? (db ? k_attn_vmfma<DT, G, 1, true> : k_attn_vmfma<DT, G, 1, false>) \
-                         : (qt == 2 ? k_attn_vmfma<DT, G, 2, false> : nullptr);
+  case G: return qt != 1 ? nullptr                                                                      \
+                 : nt == 1 ? (db ? k_attn_vmfma<DT, G, 1, true, 1> : k_attn_vmfma<DT, G, 1, false, 1>) \
+                           : (db ? k_attn_vmfma<DT, G, 1, true, 2> : k_attn_vmfma<DT, G, 1, false, 2>);
   switch (group) {
     ASR_PICK_VMFMA(2) ASR_PICK_VMFMA(4) ASR_PICK_VMFMA(8)
     default: return nullptr;
@@ -3449,7 +3455,7 @@ hipError_t layer_multi(const LayerArgs &a, int attn_grid, hipStream_t s, hipEven
                         dim3(a.H / (4 * rpw) * halves), dim3(256), lds_x, s, ev, 2, a);
   }
   if (attn_vmfma_used(a)) {
-    if ((e = launch_phase(pick_attn_vmfma<DT>(a.group, vmfma_tiles(a.group, a.n), vmfma_double_buffer(a)), dim3(attn_grid), dim3(kVmWaves * kWave),
+    if ((e = launch_phase(pick_attn_vmfma<DT>(a.group, 1, vmfma_double_buffer(a), a.vm_nt), dim3(attn_grid), dim3(kVmWaves * kWave),
                           lds_vmfma_bytes(a.B), s, ev, 1, a)) != hipSuccess)
       return e;
   } else if (attn_waves_used(a)) {
@@ -3529,6 +3535,8 @@ size_t layer_dyn_smem(const LayerArgs &a) { return fused_dyn_smem(a); }
 // verify blocks of more than a few rows whose query rows per kv head fit two
 // tiles: one K/V stream per (sequence, kv head) on the matrix cores (the
 // per-row merge takes two or more q heads per kv head)
+int attn_vmfma_tiles(int group, int n) { return vmfma_tiles(group, n); }
+
 bool attn_vmfma_used(const LayerArgs &a) {
   return a.mfma && !a.qo_n && a.n > 1 && a.group >= 2 && !a.kv8 && !a.ptab && vmfma_tiles(a.group, a.n) > 0;
 }
@@ -3536,10 +3544,10 @@ bool attn_vmfma_used(const LayerArgs &a) {
 // Resident workgroups of the verify attention kernel for B sequences (blocks per
 // CU from the occupancy calculator times the CU count).
 int attn_vmfma_grid(int dtype, int group, int n, int B, int cus) {
-  const int qt = vmfma_tiles(group, n);
-  // (both register-set variants hold one workgroup per CU)
+  // one query tile per work item; both register-set variants hold one workgroup per CU
+  if (vmfma_tiles(group, n) <= 0) return 0;
   const LayerKernel k =
-      dtype == ASR_BF16 ? pick_attn_vmfma<ASR_BF16>(group, qt, false) : pick_attn_vmfma<ASR_F16>(group, qt, false);
+      dtype == ASR_BF16 ? pick_attn_vmfma<ASR_BF16>(group, 1, false, 1) : pick_attn_vmfma<ASR_F16>(group, 1, false, 1);
   int per_cu = 0;
   if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kVmWaves * kWave, lds_vmfma_bytes(B)) != hipSuccess ||
       per_cu <= 0)

@@ -68,6 +68,8 @@ struct LayerArgs {
   // device from the lengths (vm_items = 0)
   int vm_items;
   int vm_pre[kVmMaxSeqs + 1];
+  // 16-row query tiles of a (sequence, kv head): one work item per (sequence, kv head, chunk, tile)
+  int vm_nt;
   // FP8 (E4M3) cache: kc / vc hold one code per element; per-kv-head scales of K and V
   int kv8;
   const float *ksc, *vsc;
@@ -152,6 +154,7 @@ size_t layer_dyn_smem(const LayerArgs &a);
 bool attn_waves_used(const LayerArgs &a);
 bool attn_vmfma_used(const LayerArgs &a);
 int attn_vmfma_grid(int dtype, int group, int n, int B, int cus);
+int attn_vmfma_tiles(int group, int n);
 int attn_waves_grid(int dtype, int group, int cus, bool mix, bool paged);
 hipError_t launch_kv_append(int dtype, const asr_kv_layer &kv, const void *k_new, const void *v_new,
                             const int32_t *slots, int B, int n, hipStream_t s);

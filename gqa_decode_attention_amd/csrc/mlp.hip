@@ -424,6 +424,59 @@ __device__ __forceinline__ void best_of(float &v, int &i, float v2, int i2) {
   }
 }
 
+// The wave's products over the whole contraction for 16 weight rows o0 .. o0 + 15
+// with W read as whole 128-byte lines: a matrix-core A operand load covers 64
+// bytes of 16 rows, and with the streaming hint (which keeps the 311 MB of the
+// model head out of the memory-side cache) the line is not kept for its other
+// half, so operand-layout loads fetched most lines twice.  Per batch of BATCH
+// steps each instruction loads 64 / (4 BATCH) rows x 4 BATCH 16-byte chunks
+// (whole lines), the rows go through the wave's LDS region (chunk c
+// of row r at c ^ (r & 15): both the stores and the operand reads are free of
+// bank conflicts), and the A operands are read back in the MFMA layout.
+// lds: the wave's BATCH x 1 KB.
+template <int DT, int BATCH>
+__device__ __forceinline__ void line_products(const uint16_t *w, int K, const uint16_t *hl, int rows, int o0, int n,
+                                              int kw, unsigned char *lds, f32x4_t &acc) {
+  constexpr int CPR = BATCH * 4;   // 16-byte chunks per row and batch
+  static_assert(64 % CPR == 0 || CPR % 8 == 0, "whole lines per load instruction");
+  const int lane = lane_id(), i16 = lane % 16, g4 = lane / 16;
+  const size_t plane = (size_t)K * rows;
+  for (int s0 = 0; s0 < kw; s0 += BATCH) {
+    uint4 wa[BATCH], hi[BATCH], lo[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {   // instruction j: chunks f = 64 j + lane, row f / CPR
+      const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
+      const int col = min(s0 + c / 4, kw - 1) * 32 + (c % 4) * 8;   // past the share: a repeated step
+      wa[j] = ld16_stream(w + (size_t)(o0 + r) * K + col);
+    }
+#pragma unroll
+    for (int s = 0; s < BATCH; ++s) {
+      const int kk = min(s0 + s, kw - 1) * 32;
+      const size_t bi = ((size_t)(kk / 32) * rows + n) * 32 + g4 * 8;
+      hi[s] = ld16(hl + bi);
+      lo[s] = ld16(hl + plane + bi);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any use
+    wave_lds_sync();                     // the previous batch's operand reads are done
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
+      *reinterpret_cast<uint4 *>(lds + r * CPR * 16 + ((c ^ (r & 15)) << 4)) = wa[j];
+    }
+    wave_lds_sync();                     // the rows are stored before any lane reads the operand layout
+#pragma unroll
+    for (int s = 0; s < BATCH; ++s)
+      wa[s] = *reinterpret_cast<const uint4 *>(lds + i16 * CPR * 16 + (((s * 4 + g4) ^ i16) << 4));
+#pragma unroll
+    for (int s = 0; s < BATCH; ++s) {
+      if (s0 + s < kw) {
+        acc = mfma16x16x32<DT>(wa[s], hi[s], acc);
+        acc = mfma16x16x32<DT>(wa[s], lo[s], acc);
+      }
+    }
+  }
+}
+
 // Logits of 8 vocab tiles of 16 (one per wave) x 16 rows on the matrix cores
 // (W_lm exact 16-bit, the normalised rows as hi + lo), and the best (logit,
 // id) of each row over the block's 128 ids: partial [block][row].
@@ -431,6 +484,7 @@ template <int DT>
 __global__ __launch_bounds__(kMlpWaves * 64) void k_head_argmax(HeadArgs A) {
   __shared__ float s_v[kMlpWaves][16];
   __shared__ int s_i[kMlpWaves][16];
+  __shared__ __align__(16) unsigned char s_w[kMlpWaves][kMlpBatch * 1024];   // each wave's W rows of a batch
   const int wave = wave_id(), lane = lane_id();
   const int i16 = lane % 16, g4 = lane / 16;
   const int nb = blockIdx.y * 16, n = nb + i16;
@@ -438,11 +492,10 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_head_argmax(HeadArgs A) {
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   if (v0 < A.V) {
-    const uint16_t *const w[1] = {A.w_lm};
-    f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    mlp_products<DT, 1>(w, A.H, A.y_hl, A.rows, v0 + i16, min(n, A.rows - 1), 0, A.H / 32, acc);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    line_products<DT, kMlpBatch>(A.w_lm, A.H, A.y_hl, A.rows, v0, min(n, A.rows - 1), A.H / 32, s_w[wave], acc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) best_of(bv, bi, acc[0][j], v0 + 4 * g4 + j);
+    for (int j = 0; j < 4; ++j) best_of(bv, bi, acc[j], v0 + 4 * g4 + j);
   }
   // over the four lane groups of a row (lanes n, n + 16, n + 32, n + 48)
   {

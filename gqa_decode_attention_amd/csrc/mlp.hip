@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kMlpWaves = 8;
 constexpr int kMlpBatch = 4;   // 32-wide contraction steps per operand batch
+constexpr int kDownBatch = 12; // steps per batch of the down projection (a wave's whole share at intermediate 3072)
 
 struct MlpTile {
   int col, row;
@@ -70,33 +71,56 @@ __global__ __launch_bounds__(256) void k_mlp_norm(MlpArgs A) {
   }
 }
 
-// the wave's share [k0, k0 + kw * 32) of the contraction: A operand rows of W at
-// feature o, B operand hi / lo tiles of `hl` (plane = K * rows) at row n
-template <int DT, int NM, int BATCH = kMlpBatch>
-__device__ __forceinline__ void mlp_products(const uint16_t *const (&w)[NM], int K, const uint16_t *hl, int rows,
-                                             int o, int n, int k0, int kw, f32x4_t (&acc)[NM]) {
-  const int lane = lane_id(), g4 = lane / 16;
+// The wave's products over its share [k0, k0 + 32 kw) of the contraction for 16
+// weight rows o0 .. o0 + 15 (B operand: the hi / lo tiles of `hl`, planes of K x rows, at row n)
+// with W read as whole 128-byte lines: a matrix-core A operand load covers 64
+// bytes of 16 rows, and with the streaming hint (which keeps the 311 MB of the
+// model head out of the memory-side cache) the line is not kept for its other
+// half, so operand-layout loads fetched most lines twice.  Per batch of BATCH
+// steps each instruction loads 64 consecutive 16-byte chunks of the batch's
+// rows (4 BATCH chunks per row, a multiple of 8: whole lines when the share
+// starts on a line), the rows go through the wave's LDS region (chunk c
+// of row r at c ^ (r & 15): both the stores and the operand reads are free of
+// bank conflicts), and the A operands are read back in the MFMA layout.
+// lds: the wave's BATCH x 1 KB.
+template <int DT, int BATCH>
+__device__ __forceinline__ void line_products(const uint16_t *w, int K, const uint16_t *hl, int rows, int o0, int n,
+                                              int k0, int kw, unsigned char *lds, f32x4_t &acc) {
+  constexpr int CPR = BATCH * 4;   // 16-byte chunks per row and batch
+  static_assert(64 % CPR == 0 || CPR % 8 == 0, "whole lines per load instruction");
+  const int lane = lane_id(), i16 = lane % 16, g4 = lane / 16;
   const size_t plane = (size_t)K * rows;
   for (int s0 = 0; s0 < kw; s0 += BATCH) {
-    uint4 wa[NM][BATCH], hi[BATCH], lo[BATCH];
+    uint4 wa[BATCH], hi[BATCH], lo[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {   // instruction j: chunks f = 64 j + lane, row f / CPR
+      const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
+      const int col = k0 + min(s0 + c / 4, kw - 1) * 32 + (c % 4) * 8;   // past the share: a repeated step
+      wa[j] = ld16_stream(w + (size_t)(o0 + r) * K + col);
+    }
 #pragma unroll
     for (int s = 0; s < BATCH; ++s) {
-      const int kk = k0 + min(s0 + s, kw - 1) * 32;   // past the share: a repeated step, weight zero below
-#pragma unroll
-      for (int m = 0; m < NM; ++m) wa[m][s] = ld16_stream(w[m] + (size_t)o * K + kk + g4 * 8);
+      const int kk = k0 + min(s0 + s, kw - 1) * 32;
       const size_t bi = ((size_t)(kk / 32) * rows + n) * 32 + g4 * 8;
       hi[s] = ld16(hl + bi);
       lo[s] = ld16(hl + plane + bi);
     }
-    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any product
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any use
+    wave_lds_sync();                     // the previous batch's operand reads are done
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
+      *reinterpret_cast<uint4 *>(lds + r * CPR * 16 + ((c ^ (r & 15)) << 4)) = wa[j];
+    }
+    wave_lds_sync();                     // the rows are stored before any lane reads the operand layout
+#pragma unroll
+    for (int s = 0; s < BATCH; ++s)
+      wa[s] = *reinterpret_cast<const uint4 *>(lds + i16 * CPR * 16 + (((s * 4 + g4) ^ i16) << 4));
 #pragma unroll
     for (int s = 0; s < BATCH; ++s) {
-      if (s0 + s < kw) {   // (a predicate, not a break: the batch stays unrolled, in registers)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          acc[m] = mfma16x16x32<DT>(wa[m][s], hi[s], acc[m]);
-          acc[m] = mfma16x16x32<DT>(wa[m][s], lo[s], acc[m]);
-        }
+      if (s0 + s < kw) {
+        acc = mfma16x16x32<DT>(wa[s], hi[s], acc);
+        acc = mfma16x16x32<DT>(wa[s], lo[s], acc);
       }
     }
   }
@@ -212,11 +236,13 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_down(MlpArgs A) {
     for (int j = 0; j < 4; ++j) res[j] = load_h<DT>(A, (size_t)n * A.H + o0 + 4 * g4 + j);
   }
   const int kw = A.I / 32 / kMlpWaves;
-  const uint16_t *const w[1] = {A.w_down};
-  f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  // batches of 12 steps: the whole share at intermediate 3072, one wait per batch
-  mlp_products<DT, 1, 12>(w, A.I, A.a_hl, A.rows, o0 + i16, min(n, A.rows - 1), wave * kw * 32, kw, acc);
-  s_c[wave][lane] = acc[0];
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // batches of 12 steps (the whole share at intermediate 3072, one wait per batch),
+  // W_down as whole lines through the wave's 12 KB of dynamic LDS
+  extern __shared__ __align__(16) unsigned char dyn[];
+  line_products<DT, kDownBatch>(A.w_down, A.I, A.a_hl, A.rows, o0, min(n, A.rows - 1), wave * kw * 32, kw,
+                                dyn + wave * kDownBatch * 1024, acc);
+  s_c[wave][lane] = acc;
   __syncthreads();
   if (wave == 0 && n < A.rows) {
     f32x4_t c = s_c[0][lane];
@@ -424,59 +450,6 @@ __device__ __forceinline__ void best_of(float &v, int &i, float v2, int i2) {
   }
 }
 
-// The wave's products over the whole contraction for 16 weight rows o0 .. o0 + 15
-// with W read as whole 128-byte lines: a matrix-core A operand load covers 64
-// bytes of 16 rows, and with the streaming hint (which keeps the 311 MB of the
-// model head out of the memory-side cache) the line is not kept for its other
-// half, so operand-layout loads fetched most lines twice.  Per batch of BATCH
-// steps each instruction loads 64 / (4 BATCH) rows x 4 BATCH 16-byte chunks
-// (whole lines), the rows go through the wave's LDS region (chunk c
-// of row r at c ^ (r & 15): both the stores and the operand reads are free of
-// bank conflicts), and the A operands are read back in the MFMA layout.
-// lds: the wave's BATCH x 1 KB.
-template <int DT, int BATCH>
-__device__ __forceinline__ void line_products(const uint16_t *w, int K, const uint16_t *hl, int rows, int o0, int n,
-                                              int kw, unsigned char *lds, f32x4_t &acc) {
-  constexpr int CPR = BATCH * 4;   // 16-byte chunks per row and batch
-  static_assert(64 % CPR == 0 || CPR % 8 == 0, "whole lines per load instruction");
-  const int lane = lane_id(), i16 = lane % 16, g4 = lane / 16;
-  const size_t plane = (size_t)K * rows;
-  for (int s0 = 0; s0 < kw; s0 += BATCH) {
-    uint4 wa[BATCH], hi[BATCH], lo[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {   // instruction j: chunks f = 64 j + lane, row f / CPR
-      const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
-      const int col = min(s0 + c / 4, kw - 1) * 32 + (c % 4) * 8;   // past the share: a repeated step
-      wa[j] = ld16_stream(w + (size_t)(o0 + r) * K + col);
-    }
-#pragma unroll
-    for (int s = 0; s < BATCH; ++s) {
-      const int kk = min(s0 + s, kw - 1) * 32;
-      const size_t bi = ((size_t)(kk / 32) * rows + n) * 32 + g4 * 8;
-      hi[s] = ld16(hl + bi);
-      lo[s] = ld16(hl + plane + bi);
-    }
-    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any use
-    wave_lds_sync();                     // the previous batch's operand reads are done
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
-      *reinterpret_cast<uint4 *>(lds + r * CPR * 16 + ((c ^ (r & 15)) << 4)) = wa[j];
-    }
-    wave_lds_sync();                     // the rows are stored before any lane reads the operand layout
-#pragma unroll
-    for (int s = 0; s < BATCH; ++s)
-      wa[s] = *reinterpret_cast<const uint4 *>(lds + i16 * CPR * 16 + (((s * 4 + g4) ^ i16) << 4));
-#pragma unroll
-    for (int s = 0; s < BATCH; ++s) {
-      if (s0 + s < kw) {
-        acc = mfma16x16x32<DT>(wa[s], hi[s], acc);
-        acc = mfma16x16x32<DT>(wa[s], lo[s], acc);
-      }
-    }
-  }
-}
-
 // Logits of 8 vocab tiles of 16 (one per wave) x 16 rows on the matrix cores
 // (W_lm exact 16-bit, the normalised rows as hi + lo), and the best (logit,
 // id) of each row over the block's 128 ids: partial [block][row].
@@ -493,7 +466,7 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_head_argmax(HeadArgs A) {
   int bi = 0x7fffffff;
   if (v0 < A.V) {
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    line_products<DT, kMlpBatch>(A.w_lm, A.H, A.y_hl, A.rows, v0, min(n, A.rows - 1), A.H / 32, s_w[wave], acc);
+    line_products<DT, kMlpBatch>(A.w_lm, A.H, A.y_hl, A.rows, v0, min(n, A.rows - 1), 0, A.H / 32, s_w[wave], acc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) best_of(bv, bi, acc[j], v0 + 4 * g4 + j);
   }
@@ -570,11 +543,12 @@ __global__ __launch_bounds__(256) void k_accept(AcceptArgs A) {
 
 using MlpKernel = void (*)(MlpArgs);
 
-hipError_t launch(MlpKernel k, dim3 grid, dim3 block, hipStream_t s, hipEvent_t *ev, int phase, const MlpArgs &a) {
+hipError_t launch(MlpKernel k, dim3 grid, dim3 block, hipStream_t s, hipEvent_t *ev, int phase, const MlpArgs &a,
+                  unsigned lds = 0) {
   if (ev)
-    hipExtLaunchKernelGGL(k, grid, block, 0, s, ev[2 * phase], ev[2 * phase + 1], 0u, a);
+    hipExtLaunchKernelGGL(k, grid, block, lds, s, ev[2 * phase], ev[2 * phase + 1], 0u, a);
   else
-    hipLaunchKernelGGL(k, grid, block, 0, s, a);
+    hipLaunchKernelGGL(k, grid, block, lds, s, a);
   return hipGetLastError();
 }
 
@@ -608,7 +582,8 @@ hipError_t mlp_launch(const MlpArgs &a, hipStream_t s, hipEvent_t *ev) {
     default: return hipErrorInvalidValue;
   }
   if ((e = launch(up, dim3(a.I / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 0, a)) != hipSuccess) return e;
-  return launch(k_mlp_down<DT>, dim3(a.H / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 1, a);
+  return launch(k_mlp_down<DT>, dim3(a.H / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 1, a,
+                kMlpWaves * kDownBatch * 1024);
 }
 
 template <int DT>

@@ -127,7 +127,9 @@ __device__ __forceinline__ void line_products(const uint16_t *w, int K, const ui
 }
 
 // KW: 32-wide contraction steps per wave (H / 32 / 8: 4 at hidden 1024, 8 at 2048)
-template <int DT, int KW>
+// LS (calls of at most 16 rows): the weight rows as whole lines through LDS; with more rows the
+// blocks of a feature tile share its lines in L2 and the 64-128 KB of LDS would cost occupancy
+template <int DT, int KW, bool LS>
 __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_up(MlpArgs A) {
   __shared__ f32x4_t s_c[2][kMlpWaves][kWave];
   __shared__ float s_ss[kMlpWaves][16];
@@ -137,15 +139,24 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_up(MlpArgs A) {
   const MlpTile tm = mlp_tile(blockIdx.x, rtiles);
   const int o0 = tm.col * 16, nb = tm.row * 16;
   const int n = min(nb + i16, A.rows - 1);   // rows past the call repeat the last (not stored)
-  const int k0 = wave * KW * 32 + g4 * 8;    // this lane's 8 columns of each step: k0 + 32 s ..
-  // every load before any wait: the gate and up rows of feature o0 + i16, then the lane's slice
-  // of row n of h and the post-norm gains of the same columns
+  const int kw0 = wave * KW * 32;            // the wave's share of the contraction: columns kw0 ..
+  const int k0 = kw0 + g4 * 8;               // this lane's 8 columns of each step: k0 + 32 s ..
+  // every load before any wait: the gate and up rows o0 .. o0 + 15 of the wave's share as whole
+  // 128-byte lines (instruction j: 16-byte chunks 64 j .. 64 j + 63, row f / CPR, chunk f % CPR),
+  // then the lane's slice of row n of h and the post-norm gains of the same columns
+  constexpr int CPR = KW * 4;   // 16-byte chunks per row of the share
   uint4 wa[2][KW], gv[KW];
   float hv[KW][8];
 #pragma unroll
-  for (int st = 0; st < KW; ++st) {
-    wa[0][st] = ld16_stream(A.w_gate + (size_t)(o0 + i16) * A.H + k0 + 32 * st);
-    wa[1][st] = ld16_stream(A.w_up + (size_t)(o0 + i16) * A.H + k0 + 32 * st);
+  for (int j = 0; j < KW; ++j) {
+    if constexpr (LS) {
+      const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
+      wa[0][j] = ld16_stream(A.w_gate + (size_t)(o0 + r) * A.H + kw0 + c * 8);
+      wa[1][j] = ld16_stream(A.w_up + (size_t)(o0 + r) * A.H + kw0 + c * 8);
+    } else {   // the operand layout directly: row i16, columns k0 + 32 j ..
+      wa[0][j] = ld16_stream(A.w_gate + (size_t)(o0 + i16) * A.H + k0 + 32 * j);
+      wa[1][j] = ld16_stream(A.w_up + (size_t)(o0 + i16) * A.H + k0 + 32 * j);
+    }
   }
 #pragma unroll
   for (int st = 0; st < KW; ++st) {
@@ -159,6 +170,25 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_up(MlpArgs A) {
       unpack8<DT>(ld16(reinterpret_cast<const uint16_t *>(A.h) + i), hv[st]);
     }
     gv[st] = ld16(A.g_post + k0 + 32 * st);
+  }
+  // the weight rows through the wave's LDS (chunk c of row r at c ^ (r & 15)) into the
+  // matrix-core operand layout (lane: row i16, chunk 4 s + g4 of step s)
+  if constexpr (LS) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    unsigned char *lw = dyn + wave * 2 * KW * 1024;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        const int f = j * 64 + lane, r = f / CPR, c = f % CPR;
+        *reinterpret_cast<uint4 *>(lw + m * KW * 1024 + r * CPR * 16 + ((c ^ (r & 15)) << 4)) = wa[m][j];
+      }
+    wave_lds_sync();   // the rows are stored before any lane reads the operand layout
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int st = 0; st < KW; ++st)
+        wa[m][st] = *reinterpret_cast<const uint4 *>(lw + m * KW * 1024 + i16 * CPR * 16 + (((st * 4 + g4) ^ i16) << 4));
   }
   // the row's sum of squares: this lane's slice, the 4 lanes of row n, then the 8 waves
   float ss = 0.f;
@@ -569,19 +599,24 @@ hipError_t mlp_launch(const MlpArgs &a, hipStream_t s, hipEvent_t *ev) {
     return launch(one ? k_mlp_down_few<DT, 1> : k_mlp_down_few<DT, kVectorRows>, dim3(a.H / 4), dim3(256), s, ev, 1, a);
   }
   const int rtiles = (a.rows + 15) / 16;
+  const bool ls = rtiles == 1;   // weight lines through LDS for calls of at most 16 rows
   MlpKernel up = nullptr;
   switch (a.H / 32 / kMlpWaves) {
-    case 1: up = k_mlp_up<DT, 1>; break;
-    case 2: up = k_mlp_up<DT, 2>; break;
-    case 3: up = k_mlp_up<DT, 3>; break;
-    case 4: up = k_mlp_up<DT, 4>; break;
-    case 5: up = k_mlp_up<DT, 5>; break;
-    case 6: up = k_mlp_up<DT, 6>; break;
-    case 7: up = k_mlp_up<DT, 7>; break;
-    case 8: up = k_mlp_up<DT, 8>; break;
+    case 1: up = ls ? k_mlp_up<DT, 1, true> : k_mlp_up<DT, 1, false>; break;
+    case 2: up = ls ? k_mlp_up<DT, 2, true> : k_mlp_up<DT, 2, false>; break;
+    case 3: up = ls ? k_mlp_up<DT, 3, true> : k_mlp_up<DT, 3, false>; break;
+    case 4: up = ls ? k_mlp_up<DT, 4, true> : k_mlp_up<DT, 4, false>; break;
+    case 5: up = ls ? k_mlp_up<DT, 5, true> : k_mlp_up<DT, 5, false>; break;
+    case 6: up = ls ? k_mlp_up<DT, 6, true> : k_mlp_up<DT, 6, false>; break;
+    case 7: up = ls ? k_mlp_up<DT, 7, true> : k_mlp_up<DT, 7, false>; break;
+    case 8: up = ls ? k_mlp_up<DT, 8, true> : k_mlp_up<DT, 8, false>; break;
     default: return hipErrorInvalidValue;
   }
-  if ((e = launch(up, dim3(a.I / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 0, a)) != hipSuccess) return e;
+  // (dynamic LDS: each wave's gate and up rows of its share, 2 matrices x 16 rows x H / 8 columns
+  // x 2 bytes = 8 H bytes per wave; 128 KB at hidden 2048)
+  if ((e = launch(up, dim3(a.I / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 0, a, ls ? kMlpWaves * 8 * a.H : 0)) !=
+      hipSuccess)
+    return e;
   return launch(k_mlp_down<DT>, dim3(a.H / 16 * rtiles), dim3(kMlpWaves * kWave), s, ev, 1, a,
                 kMlpWaves * kDownBatch * 1024);
 }

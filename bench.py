@@ -59,11 +59,11 @@ NEAR_TIE = 5e-3
 # scaled by what that counter reads for a 1 GiB device copy (fetch x1.99992, write x1.000), and
 # the digest of the kernel sources they were taken on: reported only while the sources match
 TRAFFIC = {
-    "sources_sha256": "f0734952419ae31f52e1f0226b19d72b7e2a241a6df4c787377fa8ad5553cfec",
-    "bs1": {"qkv_projection": 8587107, "attention": 4058658, "o_proj": 4864994},
-    "b64": {"qkv_projection": 11070259, "attention": 230482129, "o_proj": 8722651},
-    "b64_fp8": {"qkv_projection": 11070259, "attention": 120147852, "o_proj": 8722651},
-    "b64_paged": {"qkv_projection": 11070259, "attention": 230699889, "o_proj": 8722651},
+    "sources_sha256": "4386e2f4ea80e25e43affc393d0c09996453fb1b49c96b35cd37c3b640228d91",
+    "bs1": {"qkv_projection": 8587103, "attention": 4071800, "o_proj": 4885473},
+    "b64": {"qkv_projection": 11059060, "attention": 230482124, "o_proj": 8712441},
+    "b64_fp8": {"qkv_projection": 11059060, "attention": 120127730, "o_proj": 8712441},
+    "b64_paged": {"qkv_projection": 11059060, "attention": 230736493, "o_proj": 8712441},
 }
 KERNEL_SOURCES = ("gqa_decode_attention_amd/csrc/attn_layer.hip", "gqa_decode_attention_amd/csrc/device_common.h",
                   "gqa_decode_attention_amd/csrc/internal.h", "gqa_decode_attention_amd/csrc/api.hip",

@@ -75,8 +75,9 @@ __global__ __launch_bounds__(256) void k_mlp_norm(MlpArgs A) {
 // weight rows o0 .. o0 + 15 (B operand: the hi / lo tiles of `hl`, planes of K x rows, at row n)
 // with W read as whole 128-byte lines: a matrix-core A operand load covers 64
 // bytes of 16 rows, and with the streaming hint (which keeps the 311 MB of the
-// model head out of the memory-side cache) the line is not kept for its other
-// half, so operand-layout loads fetched most lines twice.  Per batch of BATCH
+// model head out of the memory-side cache) the line need not be kept for its
+// other half (FETCH_SIZE per head call: 531 MB for 311 MB of weights with
+// operand-layout loads, 475 MB with whole lines).  Per batch of BATCH
 // steps each instruction loads 64 consecutive 16-byte chunks of the batch's
 // rows (4 BATCH chunks per row, a multiple of 8: whole lines when the share
 // starts on a line), the rows go through the wave's LDS region (chunk c
@@ -141,9 +142,10 @@ __global__ __launch_bounds__(kMlpWaves * 64) void k_mlp_up(MlpArgs A) {
   const int n = min(nb + i16, A.rows - 1);   // rows past the call repeat the last (not stored)
   const int kw0 = wave * KW * 32;            // the wave's share of the contraction: columns kw0 ..
   const int k0 = kw0 + g4 * 8;               // this lane's 8 columns of each step: k0 + 32 s ..
-  // every load before any wait: the gate and up rows o0 .. o0 + 15 of the wave's share as whole
-  // 128-byte lines (instruction j: 16-byte chunks 64 j .. 64 j + 63, row f / CPR, chunk f % CPR),
-  // then the lane's slice of row n of h and the post-norm gains of the same columns
+  // every load before any wait: the gate and up rows o0 .. o0 + 15 of the wave's share (LS:
+  // instruction j takes 16-byte chunks 64 j .. 64 j + 63, row f / CPR, chunk f % CPR: whole
+  // 128-byte lines when CPR is a multiple of 8), then the lane's slice of row n of h and the
+  // post-norm gains of the same columns
   constexpr int CPR = KW * 4;   // 16-byte chunks per row of the share
   uint4 wa[2][KW], gv[KW];
   float hv[KW][8];
